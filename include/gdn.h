@@ -1,0 +1,143 @@
+/*
+ * gdn.h -- C ABI of the Gated DeltaNet gated-delta-rule library for MI355X
+ * (gfx950).
+ *
+ * The operation.  "Optimizing on-device inference for Apple Silicon"
+ * (Perplexity blog), section "Qwen creates three distinct workload shapes",
+ * describes the Gated DeltaNet layer.  It keeps a fixed-size recurrent state
+ * per head.  A learned gate sets how much of that state survives each token,
+ * and a delta update writes the current token in.  Per (sequence, v-head),
+ * with S a d_v x d_k fp32 matrix:
+ *
+ *     S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *     o_t = S_t q_t,          alpha_t = exp(g_t).
+ *
+ * The same section gives two ways to evaluate it.  One scans tokens directly
+ * (gdn_decode_step, one token per sequence).  The other regroups the updates
+ * into blocks of tokens that expose matrix work (gdn_prefill, blocks of
+ * `chunk` tokens).  Section "Keep the recurrent state on chip" keeps the state
+ * and its gate in fp32 and the query/key activations in bf16.  This library
+ * does the same, and reads and writes each state exactly once per call.
+ *
+ * Conventions shared by every call:
+ *   - All tensors are contiguous, in device memory, and owned by the caller.
+ *     The library never allocates, frees or synchronises.  Every call is
+ *     enqueued on `stream` (a hipStream_t; NULL = the null stream) and returns
+ *     once it is enqueued.
+ *   - q, k   [tokens, h_k, d_k]  in io_dtype (bf16 or fp32)
+ *     v      [tokens, h_v, d_v]  in io_dtype
+ *     g      [tokens, h_v]       fp32, the log of the decay (alpha = exp(g), g <= 0)
+ *     beta   [tokens, h_v]       fp32 in [0, 1], used as given (no sigmoid inside)
+ *     out    [tokens, h_v, d_v]  in out_dtype (bf16 or fp32)
+ *     state  [num_seqs, h_v, d_v, d_k] fp32, row-major: row i holds the d_k
+ *            key-side entries of value index i.
+ *   - v-head h reads q/k head h / (h_v / h_k): consecutive v-heads share one
+ *     q/k head.
+ *   - qk_l2norm = 1 normalises q and k per (token, k-head) inside the kernel,
+ *     x / sqrt(sum x^2 + 1e-6).  The query is then multiplied by `scale`.
+ *   - Supported shapes: d_k = d_v in {64, 128}; h_v % h_k == 0; chunk = 64.
+ *   - Numerics: bf16 inputs feed fp16 matrix-core operands inside the prefill.
+ *     Normalised q/k, decays and triangular factors are exact or bounded by 1.
+ *     Values, states and value-sized intermediates (|v|, |S|, and |S k| for a
+ *     unit key) must stay below 2^14 in magnitude.  fp32 inputs use fp32
+ *     matrix-core operands throughout.
+ *   - Errors: every scalar and pointer check runs on the host before anything
+ *     is enqueued.  A failed check returns GDN_ERR_INVALID_ARGUMENT or
+ *     GDN_ERR_UNSUPPORTED, and the call then has no effect.  A failed launch
+ *     returns GDN_ERR_HIP.  gdn_last_error() gives a detail string for the
+ *     calling thread.
+ *   - The library holds no state between calls.  Calls on different streams
+ *     may overlap.  They must not share output or workspace buffers.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_INVALID_ARGUMENT = 1,
+    GDN_ERR_UNSUPPORTED = 2,
+    GDN_ERR_WORKSPACE = 3,
+    GDN_ERR_HIP = 4
+} gdn_status;
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+/* Problem description.  Plain data.  The integer fields hold gdn_dtype values. */
+typedef struct {
+    int32_t num_seqs;      /* N >= 1 */
+    int64_t total_tokens;  /* prefill: packed token count T >= 0.  decode: ignored (N tokens) */
+    int32_t h_k;           /* q/k heads >= 1 */
+    int32_t h_v;           /* v-heads, a multiple of h_k */
+    int32_t d_k;           /* key width: 64 or 128 */
+    int32_t d_v;           /* value width: must equal d_k */
+    int32_t io_dtype;      /* dtype of q, k, v */
+    int32_t out_dtype;     /* dtype of out */
+    int32_t qk_l2norm;     /* 1: L2-normalise q and k per token inside the kernel */
+    float   scale;         /* multiplies the (normalised) query; 1.0 = plain rule */
+} gdn_desc;
+
+/*
+ * Bytes of device workspace gdn_prefill needs for this problem (0 when
+ * total_tokens == 0).  It depends only on the descriptor and chunk.  Returns
+ * 0 and sets gdn_last_error() for an invalid descriptor.
+ */
+size_t gdn_prefill_workspace_bytes(const gdn_desc *desc, int32_t chunk);
+
+/*
+ * Blocked ("chunked") prefill over packed sequences.  This is the block form
+ * of the rule from the workload-shapes section.
+ *
+ *   cu_seqlens  device int32 [num_seqs + 1].  Sequence n covers packed tokens
+ *               [cu[n], cu[n+1]).  The array must start at 0, never decrease,
+ *               and end at total_tokens.  The kernels clamp values that break
+ *               this, so memory stays in bounds, but the results are then
+ *               unspecified.  NULL is allowed only when num_seqs == 1.  A
+ *               zero-length sequence passes its state through unchanged.
+ *               Blocks restart at every sequence start.
+ *   state_in    initial states, or NULL for zeros.
+ *   state_out   final states, or NULL to skip them.  May equal state_in
+ *               (in place).  No other argument may alias another.
+ *   chunk       block length in tokens: 64.
+ *   workspace   device scratch of at least gdn_prefill_workspace_bytes().
+ *               Contents on entry do not matter.
+ */
+gdn_status gdn_prefill(const gdn_desc *desc,
+                       const void *q, const void *k, const void *v,
+                       const float *g, const float *beta,
+                       const float *state_in,
+                       void *out, float *state_out,
+                       const int32_t *cu_seqlens, int32_t chunk,
+                       void *workspace, size_t workspace_bytes,
+                       void *stream);
+
+/*
+ * One decode step: one new token for each of num_seqs sequences.  This is the
+ * direct token scan of the workload-shapes section, fused with the q/k
+ * normalisation and the exponential gate ("Reduce intermediate traffic and
+ * state traffic": the recurrent update is fused with its normalisation).
+ * Shapes are those above with tokens = num_seqs.  `state` is read and written
+ * in place, once each.
+ */
+gdn_status gdn_decode_step(const gdn_desc *desc,
+                           const void *q, const void *k, const void *v,
+                           const float *g, const float *beta,
+                           float *state, void *out, void *stream);
+
+/* Static, English name of a status code. */
+const char *gdn_status_str(gdn_status status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char *gdn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,248 @@
+// Host side of the C ABI declared in include/gdn.h.  It validates every
+// argument before anything is enqueued, sizes the prefill workspace, picks
+// launch shapes, and launches the kernels in decode.hip and prefill.hip.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "gdn.h"
+
+namespace gdn {
+hipError_t launch_decode(int d, bool in_bf16, bool out_bf16, const void* q, const void* k,
+                         const void* v, const float* g, const float* beta, float* state, void* out,
+                         int units, int h_k, int h_v, int l2norm, float scale, hipStream_t stream);
+size_t prefill_record_bytes(int d, bool in_bf16);
+hipError_t launch_plan(const int32_t* cu, int N, int T, int max_slots, void* info, int32_t* slot_seq,
+                       hipStream_t stream);
+hipError_t launch_prep(int d, bool in_bf16, const void* q, const void* k, const void* v,
+                       const float* g, const float* beta, const void* info, const int32_t* slot_seq,
+                       int slots, int T, int h_k, int h_v, int l2norm, float scale, void* recs,
+                       hipStream_t stream);
+hipError_t launch_scan(int d, bool in_bf16, bool out_bf16, int nw, const void* recs, const void* info,
+                       const float* s_in, float* s_out, void* out, int units, int T, int h_v,
+                       hipStream_t stream);
+}  // namespace gdn
+
+namespace {
+
+constexpr int kChunk = 64;
+constexpr int64_t kMaxTokens = (int64_t)1 << 30;
+
+thread_local char g_err[512] = "";
+
+gdn_status fail(gdn_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+size_t dtype_size(int32_t dt) { return dt == GDN_BF16 ? 2 : 4; }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Common descriptor checks for both calls.
+gdn_status check_desc(const gdn_desc* d, bool prefill) {
+    if (!d) return fail(GDN_ERR_INVALID_ARGUMENT, "desc is NULL");
+    if (d->num_seqs < 1) return fail(GDN_ERR_INVALID_ARGUMENT, "num_seqs must be >= 1 (got %d)", d->num_seqs);
+    if (d->h_k < 1 || d->h_v < 1)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "h_k and h_v must be >= 1 (got %d, %d)", d->h_k, d->h_v);
+    if (d->h_v % d->h_k != 0)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "h_v (%d) must be a multiple of h_k (%d)", d->h_v, d->h_k);
+    if (d->d_k < 1 || d->d_v < 1)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "d_k and d_v must be >= 1 (got %d, %d)", d->d_k, d->d_v);
+    if (d->d_k != d->d_v)
+        return fail(GDN_ERR_UNSUPPORTED, "d_k (%d) must equal d_v (%d)", d->d_k, d->d_v);
+    if (d->d_k != 64 && d->d_k != 128)
+        return fail(GDN_ERR_UNSUPPORTED, "head width %d not supported (64 or 128)", d->d_k);
+    if ((d->io_dtype != GDN_F32 && d->io_dtype != GDN_BF16) ||
+        (d->out_dtype != GDN_F32 && d->out_dtype != GDN_BF16))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "io_dtype/out_dtype must be GDN_F32 or GDN_BF16");
+    if (d->qk_l2norm != 0 && d->qk_l2norm != 1)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "qk_l2norm must be 0 or 1");
+    if (!std::isfinite(d->scale)) return fail(GDN_ERR_INVALID_ARGUMENT, "scale must be finite");
+    if (d->h_v > 65535) return fail(GDN_ERR_UNSUPPORTED, "h_v above 65535 not supported");
+    if ((int64_t)d->num_seqs * d->h_v * 4 > INT32_MAX)
+        return fail(GDN_ERR_UNSUPPORTED, "num_seqs * h_v too large");
+    if (prefill) {
+        if (d->total_tokens < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "total_tokens must be >= 0");
+        if (d->total_tokens > kMaxTokens)
+            return fail(GDN_ERR_UNSUPPORTED, "total_tokens above 2^30 not supported");
+        if (d->io_dtype == GDN_F32 && d->d_k == 128)
+            return fail(GDN_ERR_UNSUPPORTED, "fp32-input prefill supports head width 64 only");
+    }
+    return GDN_OK;
+}
+
+int64_t max_slots(const gdn_desc* d, bool varlen) {
+    const int64_t T = d->total_tokens;
+    if (!varlen) return (T + kChunk - 1) / kChunk;
+    return (T + (int64_t)d->num_seqs * (kChunk - 1)) / kChunk;
+}
+
+struct WsLayout {
+    size_t info_off, slot_off, rec_off, total;
+    int64_t slots;
+};
+
+WsLayout ws_layout(const gdn_desc* d, bool varlen) {
+    WsLayout w{};
+    w.slots = max_slots(d, varlen);
+    size_t plan = 0;
+    if (varlen) {
+        w.info_off = 0;
+        w.slot_off = (size_t)d->num_seqs * 16;
+        plan = align_up(w.slot_off + (size_t)w.slots * 4, 256);
+    }
+    w.rec_off = plan;
+    w.total = plan + (size_t)w.slots * d->h_v * gdn::prefill_record_bytes(d->d_k, d->io_dtype == GDN_BF16);
+    return w;
+}
+
+struct Span {
+    const char* p;
+    size_t n;
+    const char* name;
+};
+
+// Any two non-empty ranges that overlap (other than the allowed in-place state pair) are rejected.
+gdn_status check_overlaps(const Span* s, int count, const void* allow_a, const void* allow_b) {
+    for (int i = 0; i < count; ++i)
+        for (int j = i + 1; j < count; ++j) {
+            if (!s[i].p || !s[j].p || !s[i].n || !s[j].n) continue;
+            // in place: the allowed pair at exactly the same address and size
+            if (allow_a && allow_a == allow_b && s[i].p == allow_a && s[j].p == allow_a && s[i].n == s[j].n)
+                continue;
+            if (s[i].p < s[j].p + s[j].n && s[j].p < s[i].p + s[i].n)
+                return fail(GDN_ERR_INVALID_ARGUMENT, "buffers %s and %s overlap", s[i].name, s[j].name);
+        }
+    return GDN_OK;
+}
+
+int scan_waves(const gdn_desc* d) {
+    if (const char* e = getenv("GDN_SCAN_WAVES")) {
+        const int w = atoi(e);
+        if ((w == 1 || w == 2 || (w == 4 && d->d_k == 128))) return w;
+    }
+    const int64_t units = (int64_t)d->num_seqs * d->h_v;
+    const int full = d->d_k / 32;  // waves that cover a whole head
+    return units >= 256 ? full : 1;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn_status_str(gdn_status s) {
+    switch (s) {
+        case GDN_OK: return "GDN_OK";
+        case GDN_ERR_INVALID_ARGUMENT: return "GDN_ERR_INVALID_ARGUMENT";
+        case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED";
+        case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE";
+        case GDN_ERR_HIP: return "GDN_ERR_HIP";
+    }
+    return "GDN_UNKNOWN_STATUS";
+}
+
+const char* gdn_last_error(void) { return g_err; }
+
+size_t gdn_prefill_workspace_bytes(const gdn_desc* desc, int32_t chunk) {
+    g_err[0] = 0;
+    if (check_desc(desc, true) != GDN_OK) return 0;
+    if (chunk != kChunk) { fail(GDN_ERR_UNSUPPORTED, "chunk must be 64 (got %d)", chunk); return 0; }
+    // the packed-sequence layout is a superset; size for it so one query covers both uses
+    return ws_layout(desc, true).total;
+}
+
+gdn_status gdn_prefill(const gdn_desc* desc, const void* q, const void* k, const void* v,
+                       const float* g, const float* beta, const float* state_in, void* out,
+                       float* state_out, const int32_t* cu_seqlens, int32_t chunk, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    g_err[0] = 0;
+    gdn_status st = check_desc(desc, true);
+    if (st != GDN_OK) return st;
+    if (chunk != kChunk) return fail(GDN_ERR_UNSUPPORTED, "chunk must be 64 (got %d)", chunk);
+    const int64_t T = desc->total_tokens;
+    const int N = desc->num_seqs, hk = desc->h_k, hv = desc->h_v, d = desc->d_k;
+    if (!cu_seqlens && N != 1) return fail(GDN_ERR_INVALID_ARGUMENT, "cu_seqlens is NULL but num_seqs = %d", N);
+    if (T > 0 && (!q || !k || !v || !g || !beta || !out))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "q, k, v, g, beta and out must be non-NULL");
+    const bool varlen = cu_seqlens != nullptr;
+    const WsLayout ws = ws_layout(desc, varlen);
+    // the requirement is what gdn_prefill_workspace_bytes reports, whichever layout is used
+    const size_t need = ws_layout(desc, true).total;
+    if (need > 0 && !workspace) return fail(GDN_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+    if (workspace_bytes < need)
+        return fail(GDN_ERR_WORKSPACE, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
+    const size_t io = dtype_size(desc->io_dtype), os = dtype_size(desc->out_dtype);
+    const size_t sbytes = (size_t)N * hv * d * d * 4;
+    const Span spans[] = {
+        {(const char*)q, (size_t)T * hk * d * io, "q"},
+        {(const char*)k, (size_t)T * hk * d * io, "k"},
+        {(const char*)v, (size_t)T * hv * d * io, "v"},
+        {(const char*)g, (size_t)T * hv * 4, "g"},
+        {(const char*)beta, (size_t)T * hv * 4, "beta"},
+        {(const char*)out, (size_t)T * hv * d * os, "out"},
+        {(const char*)state_in, state_in ? sbytes : 0, "state_in"},
+        {(const char*)state_out, state_out ? sbytes : 0, "state_out"},
+        {(const char*)cu_seqlens, cu_seqlens ? (size_t)(N + 1) * 4 : 0, "cu_seqlens"},
+        {(const char*)workspace, ws.total, "workspace"},
+    };
+    st = check_overlaps(spans, sizeof(spans) / sizeof(spans[0]), state_in, state_out);
+    if (st != GDN_OK) return st;
+    if (!state_out && T == 0) return GDN_OK;
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const bool in_bf16 = desc->io_dtype == GDN_BF16, out_bf16 = desc->out_dtype == GDN_BF16;
+    char* wsb = reinterpret_cast<char*>(workspace);
+    void* info = varlen ? wsb + ws.info_off : nullptr;
+    int32_t* slot_seq = varlen ? reinterpret_cast<int32_t*>(wsb + ws.slot_off) : nullptr;
+    hipError_t e = hipSuccess;
+    if (varlen) {
+        e = gdn::launch_plan(cu_seqlens, N, (int)T, (int)ws.slots, info, slot_seq, s);
+        if (e != hipSuccess) return fail(GDN_ERR_HIP, "plan launch: %s", hipGetErrorString(e));
+    }
+    if (ws.slots > 0) {
+        e = gdn::launch_prep(d, in_bf16, q, k, v, g, beta, info, slot_seq, (int)ws.slots, (int)T, hk, hv,
+                             desc->qk_l2norm, desc->scale, wsb + ws.rec_off, s);
+        if (e != hipSuccess) return fail(GDN_ERR_HIP, "chunk_prep launch: %s", hipGetErrorString(e));
+    }
+    e = gdn::launch_scan(d, in_bf16, out_bf16, scan_waves(desc), wsb + ws.rec_off, info, state_in, state_out,
+                         out, N * hv, (int)T, hv, s);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "chunk_scan launch: %s", hipGetErrorString(e));
+    return GDN_OK;
+}
+
+gdn_status gdn_decode_step(const gdn_desc* desc, const void* q, const void* k, const void* v,
+                           const float* g, const float* beta, float* state, void* out, void* stream) {
+    g_err[0] = 0;
+    gdn_status st = check_desc(desc, false);
+    if (st != GDN_OK) return st;
+    if (!q || !k || !v || !g || !beta || !state || !out)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "q, k, v, g, beta, state and out must be non-NULL");
+    const int N = desc->num_seqs, hk = desc->h_k, hv = desc->h_v, d = desc->d_k;
+    const size_t io = dtype_size(desc->io_dtype), os = dtype_size(desc->out_dtype);
+    const Span spans[] = {
+        {(const char*)q, (size_t)N * hk * d * io, "q"},
+        {(const char*)k, (size_t)N * hk * d * io, "k"},
+        {(const char*)v, (size_t)N * hv * d * io, "v"},
+        {(const char*)g, (size_t)N * hv * 4, "g"},
+        {(const char*)beta, (size_t)N * hv * 4, "beta"},
+        {(const char*)out, (size_t)N * hv * d * os, "out"},
+        {(const char*)state, (size_t)N * hv * d * d * 4, "state"},
+    };
+    st = check_overlaps(spans, sizeof(spans) / sizeof(spans[0]), nullptr, nullptr);
+    if (st != GDN_OK) return st;
+    hipError_t e = gdn::launch_decode(d, desc->io_dtype == GDN_BF16, desc->out_dtype == GDN_BF16, q, k, v, g,
+                                      beta, state, out, N * hv, hk, hv, desc->qk_l2norm, desc->scale,
+                                      reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+    return GDN_OK;
+}
+
+}  // extern "C"

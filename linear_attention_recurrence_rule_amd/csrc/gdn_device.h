@@ -1,0 +1,152 @@
+// Device-side building blocks shared by the gated-delta-rule kernels (gfx950).
+//
+// Matrix-core tiles.  Every product uses 16x16 output tiles, with a
+// contraction split into blocks of 32.  A lane's operand fragment holds 8
+// elements of one row of A, or one column of B.  Lane l has row/column
+// i = l % 16 and group q = l / 16.  Element e < 4 sits at contraction index
+// 4q + e, and element e >= 4 at 16 + 4q + (e - 4).  A and B use the same
+// (lane, element) -> index map, so the instruction's own internal k order
+// does not matter.  The 16x16 fp32 accumulator gives lane l the rows
+// 4q + r (r = 0..3) of column l % 16.  Hence two vertically adjacent
+// accumulator tiles are, element for element, the B fragment of the next
+// product that contracts over those rows.  The kernels chain products this
+// way without moving data between lanes.
+//
+//   fp16 operands: one v_mfma_f32_16x16x32_f16 per 32-block.
+//   fp32 operands: eight v_mfma_f32_16x16x4_f32 per 32-block.  Instruction e
+//                  contracts the index set {4q + e'} over the lane groups.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+
+constexpr int WAVE = 64;
+constexpr int CHUNK = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// float -> bfloat16, round to nearest, ties to even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Load 4 consecutive input elements as fp32 (bf16 bit patterns or fp32).
+template <bool BF16>
+__device__ __forceinline__ void load4(const void* base, size_t idx, float x[4]) {
+    if constexpr (BF16) {
+        uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(base) + idx);
+        x[0] = __uint_as_float(w.x << 16); x[1] = __uint_as_float(w.x & 0xffff0000u);
+        x[2] = __uint_as_float(w.y << 16); x[3] = __uint_as_float(w.y & 0xffff0000u);
+    } else {
+        float4 w = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + idx);
+        x[0] = w.x; x[1] = w.y; x[2] = w.z; x[3] = w.w;
+    }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void load8(const void* base, size_t idx, float x[8]) {
+    load4<BF16>(base, idx, x);
+    load4<BF16>(base, idx + 4, x + 4);
+}
+
+template <bool BF16>
+__device__ __forceinline__ float load1(const void* base, size_t idx) {
+    if constexpr (BF16) return bf16_to_f32(reinterpret_cast<const uint16_t*>(base)[idx]);
+    else return reinterpret_cast<const float*>(base)[idx];
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store1(void* base, size_t idx, float x) {
+    if constexpr (BF16) reinterpret_cast<uint16_t*>(base)[idx] = f32_to_bf16(x);
+    else reinterpret_cast<float*>(base)[idx] = x;
+}
+
+// ---- operand fragments ----------------------------------------------------------------
+template <typename OP> struct Frag;
+template <> struct Frag<_Float16> { h8_t v; };
+template <> struct Frag<float> { f4_t lo, hi; };
+
+__device__ __forceinline__ void frag_set(Frag<_Float16>& f, int e, float x) { f.v[e] = (_Float16)x; }
+__device__ __forceinline__ void frag_set(Frag<float>& f, int e, float x) {
+    if (e < 4) f.lo[e] = x; else f.hi[e - 4] = x;
+}
+
+__device__ __forceinline__ void mma(f4_t& acc, const Frag<_Float16>& a, const Frag<_Float16>& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f4_t& acc, const Frag<float>& a, const Frag<float>& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[0], b.lo[0], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[1], b.lo[1], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[2], b.lo[2], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[3], b.lo[3], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[0], b.hi[0], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[1], b.hi[1], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[2], b.hi[2], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[3], b.hi[3], acc, 0, 0, 0);
+}
+
+// Fragment of a row-major matrix M (leading dimension ld, in elements) for the
+// 16-row block `rb` and the 32-wide contraction block `kb`.  It serves as an
+// A fragment of M, or as a B fragment of M^T.
+template <typename OP>
+__device__ __forceinline__ Frag<OP> frag_rowmajor(const OP* M, int ld, int rb, int kb, int lane) {
+    const int i = lane & 15, q = lane >> 4;
+    const OP* p = M + (size_t)(16 * rb + i) * ld + 32 * kb + 4 * q;
+    Frag<OP> f;
+    if constexpr (sizeof(OP) == 2) {
+        typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+        h4_t a = *reinterpret_cast<const h4_t*>(p);
+        h4_t b = *reinterpret_cast<const h4_t*>(p + 16);
+        f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    } else {
+        f.lo = *reinterpret_cast<const f4_t*>(p);
+        f.hi = *reinterpret_cast<const f4_t*>(p + 16);
+    }
+    return f;
+}
+
+// B fragment from two accumulator tiles stacked along the contraction:
+// `top` holds contraction rows 0..15 of the block, `bot` rows 16..31.
+template <typename OP>
+__device__ __forceinline__ Frag<OP> frag_from_acc(const f4_t& top, const f4_t& bot) {
+    Frag<OP> f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { frag_set(f, e, top[e]); frag_set(f, e + 4, bot[e]); }
+    return f;
+}
+
+// A stored fragment (fragment-major layout: 64 lanes x 8 elements, contiguous).
+template <typename OP>
+__device__ __forceinline__ Frag<OP> frag_stored(const OP* base, int frag, int lane) {
+    const OP* p = base + ((size_t)frag * WAVE + lane) * 8;
+    Frag<OP> f;
+    if constexpr (sizeof(OP) == 2) {
+        f.v = *reinterpret_cast<const h8_t*>(p);
+    } else {
+        f.lo = *reinterpret_cast<const f4_t*>(p);
+        f.hi = *reinterpret_cast<const f4_t*>(p + 4);
+    }
+    return f;
+}
+
+template <typename OP>
+__device__ __forceinline__ void frag_store(OP* base, int frag, int lane, const Frag<OP>& f) {
+    OP* p = base + ((size_t)frag * WAVE + lane) * 8;
+    if constexpr (sizeof(OP) == 2) {
+        *reinterpret_cast<h8_t*>(p) = f.v;
+    } else {
+        *reinterpret_cast<f4_t*>(p) = f.lo;
+        *reinterpret_cast<f4_t*>(p + 4) = f.hi;
+    }
+}
+
+__device__ __forceinline__ float shfl_xor(float x, int mask) { return __shfl_xor(x, mask, WAVE); }
+
+}  // namespace gdn

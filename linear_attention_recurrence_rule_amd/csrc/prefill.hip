@@ -1,0 +1,646 @@
+// Blocked ("chunked") prefill of the gated delta rule on gfx950.
+//
+// "Optimizing on-device inference for Apple Silicon", section "Qwen creates
+// three distinct workload shapes", says the recurrence can be regrouped into
+// blocks of tokens that expose matrix work.  Section "Keep the recurrent state
+// on chip" keeps the state on chip for the whole scan and writes it back once,
+// in fp32.  This file implements that blocked form with matrix-core tiles.
+//
+// Per block of n <= 64 tokens (chunk) and v-head, with block-initial state S
+// (d_v x d_k), cumulative log-decay G_i = g_1 + ... + g_i, effective keys k_i
+// and queries q_i (normalised, query scaled):
+//   A_ij = beta_i exp(G_i - G_j) k_i.k_j (i > j),  T = (I + A)^{-1} diag(beta)
+//   W = T diag(exp G) K,  Ut = T V,  P_ij = exp(G_i - G_j) q_i.k_j (i >= j)
+//   U = Ut - W S^T,  O = diag(exp G) Q S^T + P U,
+//   S' = exp(G_n) S + U^T diag(exp(G_n - G)) K.
+// Splitting O = Ot + Qt S^T with Ot = P Ut and Qt = diag(exp G) Q - P W gives
+// two phases:
+//   chunk_prep  (parallel over blocks x v-heads): everything not involving S,
+//               written to a workspace record per (block, v-head);
+//   chunk_scan  (sequential over the blocks of a sequence, parallel over
+//               sequences x v-heads x row slices of S): S lives in registers
+//               for the whole sequence and is read and written once.
+// S's rows evolve independently, so a v-head's state can be split by rows
+// over several workgroups.
+//
+// Precision.  q/k are scaled per token by a power of two (exact) and fed raw
+// to the matrix cores.  Their L2 norms become fp32 row factors c_t.  Values
+// enter as fp16 (exact for bf16 in range).  fp32 intermediates that feed the
+// matrix cores are rounded to fp16 (bf16 inputs) or stay fp32 (fp32 inputs).
+// Ut and Ot stay fp32 in the workspace.
+#include "gdn_device.h"
+
+namespace gdn {
+
+struct SeqInfo {
+    int32_t begin, len, slot_base, pad;
+};
+
+// ---- varlen plan: per-sequence token range and block-slot base, slot -> sequence ----
+// One workgroup.  cu_seqlens is clamped into a non-decreasing sequence inside
+// [0, T] so that every index stays in bounds whatever the caller passed.
+__global__ __launch_bounds__(256) void plan_kernel(const int32_t* __restrict__ cu, int N, int T,
+                                                   int max_slots, SeqInfo* __restrict__ info,
+                                                   int32_t* __restrict__ slot_seq) {
+    __shared__ int s_carry_tok, s_carry_slot;
+    __shared__ int s_scan[256];
+    const int tid = threadIdx.x;
+    if (tid == 0) { s_carry_tok = 0; s_carry_slot = 0; }
+    __syncthreads();
+    for (int base = 0; base < N; base += 256) {
+        const int n = base + tid;
+        // running max of clamped ends (prefix max over this block, seeded by the carry)
+        int end = 0;
+        if (n < N) {
+            end = cu[n + 1];
+            end = end < 0 ? 0 : (end > T ? T : end);
+        }
+        s_scan[tid] = end;
+        __syncthreads();
+        for (int off = 1; off < 256; off <<= 1) {
+            int o = (tid >= off) ? s_scan[tid - off] : 0;
+            __syncthreads();
+            s_scan[tid] = max(s_scan[tid], o);
+            __syncthreads();
+        }
+        const int carry_tok = s_carry_tok;
+        const int my_end = max(s_scan[tid], carry_tok);
+        const int my_begin = (tid == 0) ? carry_tok : max(s_scan[tid - 1], carry_tok);
+        const int len = (n < N) ? my_end - my_begin : 0;
+        const int nch = (len + CHUNK - 1) / CHUNK;
+        __syncthreads();
+        s_scan[tid] = nch;
+        __syncthreads();
+        for (int off = 1; off < 256; off <<= 1) {
+            int o = (tid >= off) ? s_scan[tid - off] : 0;
+            __syncthreads();
+            s_scan[tid] += o;
+            __syncthreads();
+        }
+        const int slot_base = s_carry_slot + s_scan[tid] - nch;
+        if (n < N) {
+            info[n] = SeqInfo{my_begin, len, slot_base, 0};
+            for (int j = 0; j < nch; ++j)
+                if (slot_base + j < max_slots) slot_seq[slot_base + j] = n;
+        }
+        __syncthreads();
+        if (tid == 255) { s_carry_tok = my_end; s_carry_slot = slot_base + nch; }
+        __syncthreads();
+    }
+    const int used = s_carry_slot;
+    for (int s = used + tid; s < max_slots; s += 256) slot_seq[s] = -1;
+}
+
+// ---- workspace record of one (block slot, v-head) ----------------------------------------
+template <int D, typename OP>
+struct Rec {
+    // fragment-major operands for chunk_scan (64 lanes x 8 elements per fragment)
+    static constexpr size_t W = 0;                                 // -W   : (C/16) x (D/32) frags
+    static constexpr size_t Q = W + (size_t)CHUNK * D * sizeof(OP);  // Qt  : same
+    static constexpr size_t K = Q + (size_t)CHUNK * D * sizeof(OP);  // K^T : (D/16) x (C/32) frags
+    static constexpr size_t U = K + (size_t)CHUNK * D * sizeof(OP);  // Ut  : (C/16)(D/16) acc tiles fp32
+    static constexpr size_t O = U + (size_t)CHUNK * D * 4;           // Ot  : same
+    static constexpr size_t S = O + (size_t)CHUNK * D * 4;           // s_t = exp(G_n - G_t) c_t, fp32[C]
+    static constexpr size_t M = S + CHUNK * 4;                       // gamma_n (fp32), pad
+    static constexpr size_t BYTES = M + 256;
+    static constexpr size_t FRAG_BYTES = 3 * (size_t)CHUNK * D * sizeof(OP) + CHUNK * 4 + 16;
+};
+
+template <int D, typename OP>
+constexpr int ldsk() { return D + 16 / (int)sizeof(OP); }  // row stride of [token][d] tiles
+template <typename OP>
+constexpr int ldt() { return CHUNK + 16 / (int)sizeof(OP); }
+constexpr int LDF = CHUNK + 4;  // fp32 64x64 tiles
+
+// LDS plan of chunk_prep.  Region r0 holds, by phase: the scaled raw keys
+// [token][d] (Gram), then X = (I+A)^{-1} in fp32 (solve), then -W^T [d][token].
+template <int D, typename OP>
+struct PrepLds {
+    static constexpr int LK = ldsk<D, OP>(), LT = ldt<OP>();
+    union R0 {
+        OP k[CHUNK * LK];
+        float x[CHUNK * LDF];
+        OP wt[D * LT];
+    } r0;
+    float a[CHUNK * LDF];  // A (fp32, strictly lower)
+    OP kt[D * LT];         // scaled raw keys transposed [d][token]
+    OP qs[CHUNK * LK];     // scaled raw queries [token][d]
+    OP vt[D * LT];         // values transposed [d][token]
+    OP t[CHUNK * LT];      // T = (I+A)^{-1} diag(beta)
+    OP p[CHUNK * LT];      // P
+    float G[CHUNK], gam[CHUNK], ck[CHUNK], cq[CHUNK], bt[CHUNK];
+};
+
+template <int D, typename OP>
+constexpr size_t prep_lds_bytes() { return sizeof(PrepLds<D, OP>); }
+
+// Per-token power-of-two scaling and norm factor for one (token, head) vector.
+// Returns the scaled elements (exact) and c such that the effective vector is
+// c * scaled.
+__device__ __forceinline__ float norm_factor(float ss_scaled, int e, int l2norm, float mul) {
+    if (!l2norm) return ldexpf(mul, e);
+    double den = ldexp((double)ss_scaled, 2 * e) + 1e-6;
+    return (float)(ldexp((double)mul, e) / sqrt(den));
+}
+
+template <int D, typename OP, bool IN_BF16>
+__global__ __launch_bounds__(256) void chunk_prep_kernel(
+    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, const SeqInfo* __restrict__ info,
+    const int32_t* __restrict__ slot_seq, int T, int h_k, int h_v, int l2norm, float scale,
+    char* __restrict__ recs) {
+    using R = Rec<D, OP>;
+    extern __shared__ __align__(16) char smem_raw[];
+    PrepLds<D, OP>& L = *reinterpret_cast<PrepLds<D, OP>*>(smem_raw);
+    constexpr int LK = PrepLds<D, OP>::LK, LT = PrepLds<D, OP>::LT;
+
+    const int slot = blockIdx.x, h = blockIdx.y;
+    int tok0, nt;
+    if (slot_seq) {
+        const int n = slot_seq[slot];
+        if (n < 0) return;
+        const SeqInfo si = info[n];
+        const int j = slot - si.slot_base;
+        tok0 = si.begin + j * CHUNK;
+        nt = min(CHUNK, si.len - j * CHUNK);
+    } else {
+        tok0 = slot * CHUNK;
+        nt = min(CHUNK, T - tok0);
+    }
+    const int hk = h / (h_v / h_k);
+    const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
+    char* rec = recs + ((size_t)slot * h_v + h) * R::BYTES;
+
+    // ---- 1. load q, k, v; per-token scaling; transposed copies --------------------------
+    constexpr int PER_TOK = D / 8;           // 8-element pieces per token row
+    constexpr int ITEMS = CHUNK * PER_TOK;   // pieces per chunk
+    for (int it = tid; it < ITEMS; it += 256) {
+        const int t = it / PER_TOK, pc = it % PER_TOK;
+        float kx[8], qx[8], vx[8];
+        const bool live = t < nt;
+        if (live) {
+            const size_t qk_off = ((size_t)(tok0 + t) * h_k + hk) * D + 8 * pc;
+            load8<IN_BF16>(k, qk_off, kx);
+            load8<IN_BF16>(q, qk_off, qx);
+            load8<IN_BF16>(v, ((size_t)(tok0 + t) * h_v + h) * D + 8 * pc, vx);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) kx[e] = qx[e] = vx[e] = 0.f;
+        }
+        float mk = 0.f, mq = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { mk = fmaxf(mk, fabsf(kx[e])); mq = fmaxf(mq, fabsf(qx[e])); }
+#pragma unroll
+        for (int m = PER_TOK / 2; m >= 1; m >>= 1) {   // the PER_TOK lanes of a token are adjacent
+            mk = fmaxf(mk, shfl_xor(mk, m));
+            mq = fmaxf(mq, shfl_xor(mq, m));
+        }
+        int ek = 0, eq = 0;
+        frexpf(mk, &ek);
+        frexpf(mq, &eq);
+        float ssk = 0.f, ssq = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            kx[e] = ldexpf(kx[e], -ek);
+            qx[e] = ldexpf(qx[e], -eq);
+            const OP kr = (OP)kx[e], qr = (OP)qx[e];
+            ssk += (float)kr * (float)kr;
+            ssq += (float)qr * (float)qr;
+            L.r0.k[t * LK + 8 * pc + e] = kr;
+            L.qs[t * LK + 8 * pc + e] = qr;
+            L.kt[(8 * pc + e) * LT + t] = kr;
+            L.vt[(8 * pc + e) * LT + t] = (OP)vx[e];
+        }
+#pragma unroll
+        for (int m = PER_TOK / 2; m >= 1; m >>= 1) {
+            ssk += shfl_xor(ssk, m);
+            ssq += shfl_xor(ssq, m);
+        }
+        if (pc == 0) {
+            L.ck[t] = live ? norm_factor(ssk, ek, l2norm, 1.0f) : 0.f;
+            L.cq[t] = live ? norm_factor(ssq, eq, l2norm, scale) : 0.f;
+        }
+    }
+    if (wave == 0) {
+        const int t = lane;
+        const bool live = t < nt;
+        float gx = live ? g[(size_t)(tok0 + t) * h_v + h] : 0.f;
+        L.bt[t] = live ? beta[(size_t)(tok0 + t) * h_v + h] : 0.f;
+        // inclusive prefix sum over the 64 tokens
+#pragma unroll
+        for (int off = 1; off < WAVE; off <<= 1) {
+            const float o = __shfl_up(gx, off, WAVE);
+            if (t >= off) gx += o;
+        }
+        L.G[t] = gx;
+        L.gam[t] = expf(gx);
+    }
+    __syncthreads();
+
+    // ---- 2. Gram products: A (fp32) and P --------------------------------------------------
+    {
+        const int mb = wave;  // token rows 16mb..16mb+15
+        for (int nb = 0; nb <= mb; ++nb) {
+            f4_t ak = {0, 0, 0, 0}, aq = {0, 0, 0, 0};
+#pragma unroll
+            for (int kb = 0; kb < D / 32; ++kb) {
+                const Frag<OP> fk = frag_rowmajor<OP>(L.r0.k, LK, nb, kb, lane);
+                mma(ak, frag_rowmajor<OP>(L.r0.k, LK, mb, kb, lane), fk);
+                mma(aq, frag_rowmajor<OP>(L.qs, LK, mb, kb, lane), fk);
+            }
+            const int j = 16 * nb + (lane & 15);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * mb + 4 * (lane >> 4) + r;
+                const float dec = (j <= i) ? expf(L.G[i] - L.G[j]) : 0.f;
+                const float kk = ak[r] * L.ck[i] * L.ck[j];
+                L.a[i * LDF + j] = (j < i) ? L.bt[i] * dec * kk : 0.f;
+                L.p[i * LT + j] = (OP)((j <= i) ? dec * aq[r] * L.cq[i] * L.ck[j] : 0.f);
+            }
+        }
+        // zero the strictly-upper blocks of P (A's upper blocks are never read)
+        for (int nb = mb + 1; nb < 4; ++nb) {
+            const int j = 16 * nb + (lane & 15);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) L.p[(16 * mb + 4 * (lane >> 4) + r) * LT + j] = (OP)0.f;
+        }
+    }
+    __syncthreads();
+
+    // ---- 3. X = (I + A)^{-1}, block forward substitution on 16x16 blocks (fp32) -----------
+    float* X = L.r0.x;  // the raw-key tile is no longer needed
+    {
+        // diagonal blocks: wave w inverts block w; lane c < 16 owns column c
+        const int b = wave;
+        if (lane < 16) {
+            float x[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float acc = (i == lane) ? 1.f : 0.f;
+#pragma unroll
+                for (int j = 0; j < i; ++j) acc -= L.a[(16 * b + i) * LDF + 16 * b + j] * x[j];
+                x[i] = acc;
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) X[(16 * b + i) * LDF + 16 * b + lane] = x[i];
+        }
+        // upper blocks of X are zero
+        for (int idx = lane; idx < 16 * 16; idx += WAVE) {
+            const int i = idx / 16, jj = idx % 16;
+            for (int cb = b + 1; cb < 4; ++cb) X[(16 * b + i) * LDF + 16 * cb + jj] = 0.f;
+        }
+    }
+    __syncthreads();
+    // off-diagonal blocks by distance: X_ij = -X_ii * sum_{m=j}^{i-1} A_im X_mj
+    for (int dist = 1; dist < 4; ++dist) {
+        const int i = wave + dist, j = wave;
+        if (i < 4) {
+            f4_t acc = {0, 0, 0, 0};
+            for (int m = j; m < i; ++m) {
+                // acc += A_im (16x16) * X_mj (16x16), fp32 matrix cores, contraction of 16
+                const int li = lane & 15, q = lane >> 4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float av = L.a[(16 * i + li) * LDF + 16 * m + 4 * q + e];
+                    const float bv = X[(16 * m + 4 * q + e) * LDF + 16 * j + li];
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
+                }
+            }
+            // X_ij = -X_ii * acc ; acc (accumulator layout) is the B operand directly
+            f4_t res = {0, 0, 0, 0};
+            const int li = lane & 15, q = lane >> 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float av = -X[(16 * i + li) * LDF + 16 * i + 4 * q + e];
+                res = __builtin_amdgcn_mfma_f32_16x16x4f32(av, acc[e], res, 0, 0, 0);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) X[(16 * i + 4 * q + r) * LDF + 16 * j + li] = res[r];
+        }
+        __syncthreads();
+    }
+    // T = X diag(beta)
+    for (int idx = tid; idx < CHUNK * CHUNK; idx += 256) {
+        const int i = idx / CHUNK, j = idx % CHUNK;
+        L.t[i * LT + j] = (OP)(X[i * LDF + j] * L.bt[j]);
+    }
+    __syncthreads();
+
+    // ---- 4. W^T = (diag(gam c) K)^T T^T : D x C, stored as -W fragments and -W^T in LDS ----
+    OP* WT = L.r0.wt;  // [d][token], stride LT; X is no longer needed
+    OP* wrec = reinterpret_cast<OP*>(rec + R::W);
+    OP* qrec = reinterpret_cast<OP*>(rec + R::Q);
+    constexpr int UNITS_PER_WAVE = D / 32;  // (d-block pair, token block) units
+    for (int uu = 0; uu < UNITS_PER_WAVE; ++uu) {
+        const int unit = wave * UNITS_PER_WAVE + uu;
+        const int kb = unit / 4, tb = unit % 4;  // d-blocks 2kb, 2kb+1; token block tb
+        f4_t acc[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            acc[s] = f4_t{0, 0, 0, 0};
+            const int mb = 2 * kb + s;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                // A: rows d = 16mb + i of (diag(gam c) K)^T, columns tokens 32kk + ...
+                Frag<OP> fa;
+                const int i = lane & 15, q = lane >> 4;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int t = 32 * kk + 4 * q + (e & 3) + 16 * (e >> 2);
+                    frag_set(fa, e, (float)L.kt[(16 * mb + i) * LT + t] * L.gam[t] * L.ck[t]);
+                }
+                mma(acc[s], fa, frag_rowmajor<OP>(L.t, LT, tb, kk, lane));
+            }
+        }
+        // acc[s] lane (j=token, q): W^T[16(2kb+s) + 4q + r][16tb + j] = W[token][d]
+        Frag<OP> fw;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { frag_set(fw, e, -acc[0][e]); frag_set(fw, e + 4, -acc[1][e]); }
+        frag_store<OP>(wrec, tb * (D / 32) + kb, lane, fw);
+        const int jt = 16 * tb + (lane & 15), q = lane >> 4;
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) WT[(16 * (2 * kb + s) + 4 * q + r) * LT + jt] = (OP)(-acc[s][r]);
+    }
+
+    // ---- 5. Ut = T V and Ot = P Ut : C x D, fp32 accumulator tiles --------------------------
+    float* urec = reinterpret_cast<float*>(rec + R::U);
+    float* orec = reinterpret_cast<float*>(rec + R::O);
+    for (int cbi = 0; cbi < D / 64; ++cbi) {
+        const int nb = wave * (D / 64) + cbi;  // d_v block
+        f4_t ut[4];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+            ut[mb] = f4_t{0, 0, 0, 0};
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+                mma(ut[mb], frag_rowmajor<OP>(L.t, LT, mb, kk, lane),
+                    frag_rowmajor<OP>(L.vt, LT, nb, kk, lane));
+            *reinterpret_cast<f4_t*>(urec + ((size_t)(mb * (D / 16) + nb) * WAVE + lane) * 4) = ut[mb];
+        }
+        const Frag<OP> fu0 = frag_from_acc<OP>(ut[0], ut[1]);
+        const Frag<OP> fu1 = frag_from_acc<OP>(ut[2], ut[3]);
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+            f4_t ot = {0, 0, 0, 0};
+            mma(ot, frag_rowmajor<OP>(L.p, LT, mb, 0, lane), fu0);
+            mma(ot, frag_rowmajor<OP>(L.p, LT, mb, 1, lane), fu1);
+            *reinterpret_cast<f4_t*>(orec + ((size_t)(mb * (D / 16) + nb) * WAVE + lane) * 4) = ot;
+        }
+    }
+    __syncthreads();  // -W^T complete in LDS
+
+    // ---- 6. Qt^T = (diag(gam cq) Q)^T + (-W^T) P^T : D x C ----------------------------------
+    for (int uu = 0; uu < UNITS_PER_WAVE; ++uu) {
+        const int unit = wave * UNITS_PER_WAVE + uu;
+        const int kb = unit / 4, tb = unit % 4;
+        f4_t acc[2];
+        const int jt = 16 * tb + (lane & 15), q = lane >> 4;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int mb = 2 * kb + s;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                acc[s][r] = (float)L.qs[jt * LK + 16 * mb + 4 * q + r] * L.gam[jt] * L.cq[jt];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+                mma(acc[s], frag_rowmajor<OP>(WT, LT, mb, kk, lane), frag_rowmajor<OP>(L.p, LT, tb, kk, lane));
+        }
+        Frag<OP> fq;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { frag_set(fq, e, acc[0][e]); frag_set(fq, e + 4, acc[1][e]); }
+        frag_store<OP>(qrec, tb * (D / 32) + kb, lane, fq);
+    }
+
+    // ---- 7. K^T fragments (A operand of the state update), s_t, gamma_n ---------------------
+    OP* krec = reinterpret_cast<OP*>(rec + R::K);
+    for (int f = wave; f < (D / 16) * 2; f += 4) {
+        const int mb = f / 2, kk = f % 2;
+        frag_store<OP>(krec, f, lane, frag_rowmajor<OP>(L.kt, LT, mb, kk, lane));
+    }
+    if (tid < CHUNK) {
+        const float Gn = L.G[nt - 1];
+        reinterpret_cast<float*>(rec + R::S)[tid] = (tid < nt) ? expf(Gn - L.G[tid]) * L.ck[tid] : 0.f;
+        if (tid == 0) reinterpret_cast<float*>(rec + R::M)[0] = expf(Gn);
+    }
+}
+
+// ---- sequential phase -------------------------------------------------------------------
+// Workgroup = NW waves; wave w owns state rows r0 = slice*32*NW + 32w .. +31 (two 16-row
+// column blocks of S^T).  S^T tiles (d-block mb, row block nb) live in registers:
+// lane (j, q) holds S[r0 + 16nb + j][16mb + 4q + 0..3].
+template <int D, typename OP>
+struct ScanLds {
+    OP frag[3 * CHUNK * D];  // -W, Qt, K^T fragments of the current block
+    float s[CHUNK];
+    float gn;
+};
+
+template <int D, typename OP, int NW, bool OUT_BF16>
+__global__ __launch_bounds__(NW * WAVE) void chunk_scan_kernel(
+    const char* __restrict__ recs, const SeqInfo* __restrict__ info, const float* __restrict__ state_in,
+    float* __restrict__ state_out, void* __restrict__ out, int T, int h_v) {
+    using R = Rec<D, OP>;
+    __shared__ __align__(16) ScanLds<D, OP> L;
+    constexpr int SLICES = D / (32 * NW);
+    const int slice = blockIdx.x % SLICES;
+    const int unit = blockIdx.x / SLICES;  // sequence * h_v + v-head
+    const int n = unit / h_v, h = unit - n * h_v;
+    const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
+    const int r0 = slice * 32 * NW + 32 * wave;
+    int begin, len, slot0;
+    if (info) {
+        const SeqInfo si = info[n];
+        begin = si.begin; len = si.len; slot0 = si.slot_base;
+    } else {
+        begin = 0; len = T; slot0 = 0;
+    }
+    const int j16 = lane & 15, q4 = lane >> 4;
+
+    f4_t S[D / 16][2];
+    const size_t sbase = (size_t)unit * D * D;
+#pragma unroll
+    for (int mb = 0; mb < D / 16; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            if (state_in) {
+                const float4 x = *reinterpret_cast<const float4*>(
+                    state_in + sbase + (size_t)(r0 + 16 * nb + j16) * D + 16 * mb + 4 * q4);
+                S[mb][nb] = f4_t{x.x, x.y, x.z, x.w};
+            } else {
+                S[mb][nb] = f4_t{0, 0, 0, 0};
+            }
+        }
+
+    const int nchunks = (len + CHUNK - 1) / CHUNK;
+    constexpr int FRAG_ELEMS = 3 * CHUNK * D;
+    constexpr int VEC = 16 / sizeof(OP);  // elements per 16-byte copy
+    for (int c = 0; c < nchunks; ++c) {
+        const char* rec = recs + ((size_t)(slot0 + c) * h_v + h) * R::BYTES;
+        // stage the shared fragments (contiguous W, Q, K regions) into LDS
+        const uint4* src = reinterpret_cast<const uint4*>(rec + R::W);
+        uint4* dst = reinterpret_cast<uint4*>(L.frag);
+        for (int i = tid; i < FRAG_ELEMS / VEC; i += NW * WAVE) dst[i] = src[i];
+        if (tid < CHUNK) L.s[tid] = reinterpret_cast<const float*>(rec + R::S)[tid];
+        if (tid == 0) L.gn = reinterpret_cast<const float*>(rec + R::M)[0];
+        // value-side accumulators for this wave's columns
+        const float* urec = reinterpret_cast<const float*>(rec + R::U);
+        const float* orec = reinterpret_cast<const float*>(rec + R::O);
+        f4_t accU[4][2], accO[4][2];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+                const int cb = (r0 >> 4) + nb;
+                accU[mb][nb] = *reinterpret_cast<const f4_t*>(urec + ((size_t)(mb * (D / 16) + cb) * WAVE + lane) * 4);
+                accO[mb][nb] = *reinterpret_cast<const f4_t*>(orec + ((size_t)(mb * (D / 16) + cb) * WAVE + lane) * 4);
+            }
+        __syncthreads();
+
+        const OP* fW = L.frag;
+        const OP* fQ = L.frag + CHUNK * D;
+        const OP* fK = L.frag + 2 * CHUNK * D;
+        // U = Ut - W S^T ; O = Ot + Qt S^T   (contraction over d_k)
+#pragma unroll
+        for (int kb = 0; kb < D / 32; ++kb) {
+            Frag<OP> bs[2];
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) bs[nb] = frag_from_acc<OP>(S[2 * kb][nb], S[2 * kb + 1][nb]);
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+                const Frag<OP> fw = frag_stored<OP>(fW, mb * (D / 32) + kb, lane);
+                const Frag<OP> fq = frag_stored<OP>(fQ, mb * (D / 32) + kb, lane);
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb) {
+                    mma(accU[mb][nb], fw, bs[nb]);
+                    mma(accO[mb][nb], fq, bs[nb]);
+                }
+            }
+        }
+        // outputs of the valid tokens
+        const int tok0 = begin + c * CHUNK;
+        const int nt = min(CHUNK, len - c * CHUNK);
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * mb + 4 * q4 + r;
+                if (t < nt) {
+                    const size_t o = ((size_t)(tok0 + t) * h_v + h) * D + r0;
+#pragma unroll
+                    for (int nb = 0; nb < 2; ++nb) store1<OUT_BF16>(out, o + 16 * nb + j16, accO[mb][nb][r]);
+                }
+            }
+        // U rows scaled by s_t, as B fragments over tokens
+        Frag<OP> bu[2][2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    frag_set(bu[kk][nb], e, accU[2 * kk][nb][e] * L.s[32 * kk + 4 * q4 + e]);
+                    frag_set(bu[kk][nb], e + 4, accU[2 * kk + 1][nb][e] * L.s[32 * kk + 16 + 4 * q4 + e]);
+                }
+            }
+        // S^T <- gamma_n S^T + K^T (diag(s) U)
+        const float gn = L.gn;
+#pragma unroll
+        for (int mb = 0; mb < D / 16; ++mb) {
+            const Frag<OP> fk0 = frag_stored<OP>(fK, mb * 2 + 0, lane);
+            const Frag<OP> fk1 = frag_stored<OP>(fK, mb * 2 + 1, lane);
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+                S[mb][nb] *= gn;
+                mma(S[mb][nb], fk0, bu[0][nb]);
+                mma(S[mb][nb], fk1, bu[1][nb]);
+            }
+        }
+        __syncthreads();  // LDS is overwritten by the next block
+    }
+
+    if (state_out) {
+#pragma unroll
+        for (int mb = 0; mb < D / 16; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+                const f4_t x = S[mb][nb];
+                *reinterpret_cast<float4*>(state_out + sbase + (size_t)(r0 + 16 * nb + j16) * D + 16 * mb + 4 * q4) =
+                    make_float4(x[0], x[1], x[2], x[3]);
+            }
+    }
+}
+
+// ---- host launchers ----------------------------------------------------------------------
+size_t prefill_record_bytes(int d, bool in_bf16) {
+    if (d == 128) return in_bf16 ? Rec<128, _Float16>::BYTES : Rec<128, float>::BYTES;
+    return in_bf16 ? Rec<64, _Float16>::BYTES : Rec<64, float>::BYTES;
+}
+
+hipError_t launch_plan(const int32_t* cu, int N, int T, int max_slots, void* info, int32_t* slot_seq,
+                       hipStream_t stream) {
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, cu, N, T, max_slots,
+                       reinterpret_cast<SeqInfo*>(info), slot_seq);
+    return hipGetLastError();
+}
+
+template <int D, typename OP, bool IB>
+static hipError_t launch_prep_t(const void* q, const void* k, const void* v, const float* g,
+                                const float* beta, const void* info, const int32_t* slot_seq,
+                                int slots, int T, int h_k, int h_v, int l2norm, float scale,
+                                char* recs, hipStream_t stream) {
+    constexpr size_t lds = prep_lds_bytes<D, OP>();
+    static_assert(lds <= 160 * 1024, "chunk_prep LDS budget");
+    auto kern = chunk_prep_kernel<D, OP, IB>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(slots, h_v), dim3(256), lds, stream, q, k, v, g, beta,
+                       reinterpret_cast<const SeqInfo*>(info), slot_seq, T, h_k, h_v, l2norm, scale,
+                       recs);
+    return hipGetLastError();
+}
+
+hipError_t launch_prep(int d, bool in_bf16, const void* q, const void* k, const void* v,
+                       const float* g, const float* beta, const void* info, const int32_t* slot_seq,
+                       int slots, int T, int h_k, int h_v, int l2norm, float scale, void* recs,
+                       hipStream_t stream) {
+    char* r = reinterpret_cast<char*>(recs);
+    if (d == 128 && in_bf16)
+        return launch_prep_t<128, _Float16, true>(q, k, v, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, stream);
+    if (d == 64 && in_bf16)
+        return launch_prep_t<64, _Float16, true>(q, k, v, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, stream);
+    if (d == 64 && !in_bf16)
+        return launch_prep_t<64, float, false>(q, k, v, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, stream);
+    return hipErrorInvalidValue;
+}
+
+template <int D, typename OP, int NW, bool OB>
+static hipError_t launch_scan_t(const void* recs, const void* info, const float* s_in, float* s_out,
+                                void* out, int units, int T, int h_v, hipStream_t stream) {
+    constexpr int SLICES = D / (32 * NW);
+    hipLaunchKernelGGL((chunk_scan_kernel<D, OP, NW, OB>), dim3(units * SLICES), dim3(NW * WAVE), 0,
+                       stream, reinterpret_cast<const char*>(recs),
+                       reinterpret_cast<const SeqInfo*>(info), s_in, s_out, out, T, h_v);
+    return hipGetLastError();
+}
+
+hipError_t launch_scan(int d, bool in_bf16, bool out_bf16, int nw, const void* recs, const void* info,
+                       const float* s_in, float* s_out, void* out, int units, int T, int h_v,
+                       hipStream_t stream) {
+#define GDN_SCAN(D, OP, IB, NW, OB)                                                               \
+    if (d == D && in_bf16 == IB && nw == NW && out_bf16 == OB)                                    \
+        return launch_scan_t<D, OP, NW, OB>(recs, info, s_in, s_out, out, units, T, h_v, stream);
+    GDN_SCAN(128, _Float16, true, 1, true) GDN_SCAN(128, _Float16, true, 1, false)
+    GDN_SCAN(128, _Float16, true, 2, true) GDN_SCAN(128, _Float16, true, 2, false)
+    GDN_SCAN(128, _Float16, true, 4, true) GDN_SCAN(128, _Float16, true, 4, false)
+    GDN_SCAN(64, _Float16, true, 1, true) GDN_SCAN(64, _Float16, true, 1, false)
+    GDN_SCAN(64, _Float16, true, 2, true) GDN_SCAN(64, _Float16, true, 2, false)
+    GDN_SCAN(64, float, false, 1, true) GDN_SCAN(64, float, false, 1, false)
+    GDN_SCAN(64, float, false, 2, true) GDN_SCAN(64, float, false, 2, false)
+#undef GDN_SCAN
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gdn

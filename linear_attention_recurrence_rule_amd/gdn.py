@@ -1,0 +1,206 @@
+"""Thin Python binding over libgdn.so (C ABI in include/gdn.h).
+
+Argument marshalling only: every step of the recurrence runs in the HIP
+kernels behind the C entry points.  PyTorch supplies device memory and the
+current stream.  The functions named like the C entry points
+(``gdn_prefill``, ``gdn_decode_step``, ``gdn_prefill_workspace_bytes``) take
+the same arguments, with torch tensors in place of raw pointers.  ``prefill``
+and ``decode_step`` also allocate the outputs.
+
+There is no fallback: if the library is missing or a call fails, an
+exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import threading
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgdn.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "gdn.h")
+
+GDN_OK, GDN_ERR_INVALID_ARGUMENT, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP = range(5)
+GDN_F32, GDN_BF16 = 0, 1
+CHUNK = 64
+
+
+class GdnDesc(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("total_tokens", ctypes.c_int64),
+                ("h_k", ctypes.c_int32), ("h_v", ctypes.c_int32),
+                ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("io_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("qk_l2norm", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status, detail):
+        self.status = status
+        super().__init__("%s: %s" % (status_str(status), detail))
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def declared_functions():
+    """Names of the functions include/gdn.h declares."""
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(gdn_[a-z_0-9]+)\s*\(", src, re.M)))
+
+
+def lib():
+    """Load libgdn.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError("libgdn.so is not built (run __graft_entry__.build() or "
+                                   "python -m linear_attention_recurrence_rule_amd.build)")
+            L = ctypes.CDLL(LIB_PATH)
+            vp, sz = ctypes.c_void_p, ctypes.c_size_t
+            dp = ctypes.POINTER(GdnDesc)
+            L.gdn_prefill_workspace_bytes.argtypes = [dp, ctypes.c_int32]
+            L.gdn_prefill_workspace_bytes.restype = sz
+            L.gdn_prefill.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32, vp, sz, vp]
+            L.gdn_prefill.restype = ctypes.c_int
+            L.gdn_decode_step.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp]
+            L.gdn_decode_step.restype = ctypes.c_int
+            L.gdn_status_str.argtypes = [ctypes.c_int]
+            L.gdn_status_str.restype = ctypes.c_char_p
+            L.gdn_last_error.argtypes = []
+            L.gdn_last_error.restype = ctypes.c_char_p
+            _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().gdn_status_str(int(status)).decode()
+
+
+def last_error() -> str:
+    return lib().gdn_last_error().decode()
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status):
+    if status != GDN_OK:
+        raise GdnError(status, last_error())
+
+
+def make_desc(*, num_seqs, total_tokens, h_k, h_v, d, io_dtype, out_dtype, qk_l2norm=True, scale=1.0):
+    return GdnDesc(int(num_seqs), int(total_tokens), int(h_k), int(h_v), int(d), int(d),
+                   int(io_dtype), int(out_dtype), int(bool(qk_l2norm)), float(scale))
+
+
+# ---- entry points with the C names -------------------------------------------------------
+
+def gdn_prefill_workspace_bytes(desc: GdnDesc, chunk: int = CHUNK) -> int:
+    n = lib().gdn_prefill_workspace_bytes(ctypes.byref(desc), int(chunk))
+    if n == 0 and desc.total_tokens > 0:
+        raise GdnError(GDN_ERR_INVALID_ARGUMENT, last_error())
+    return n
+
+
+def gdn_prefill(desc, q, k, v, g, beta, state_in, out, state_out, cu_seqlens, chunk, workspace,
+                workspace_bytes, stream=None):
+    _check(lib().gdn_prefill(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                             _ptr(state_in), _ptr(out), _ptr(state_out), _ptr(cu_seqlens), int(chunk),
+                             _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def gdn_decode_step(desc, q, k, v, g, beta, state, out, stream=None):
+    _check(lib().gdn_decode_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                 _ptr(state), _ptr(out), _stream(stream)))
+
+
+# ---- allocating wrappers ---------------------------------------------------------------
+
+_TORCH_DT = {GDN_F32: torch.float32, GDN_BF16: torch.bfloat16}
+
+
+def _io_dtype(t):
+    if t.dtype == torch.bfloat16:
+        return GDN_BF16
+    if t.dtype == torch.float32:
+        return GDN_F32
+    raise TypeError("q/k/v must be bfloat16 or float32 (got %s)" % t.dtype)
+
+
+def _need(t, name, dtype=None, device=None):
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s (got %s)" % (name, dtype, t.dtype))
+    if device is not None and t.device != device:
+        raise ValueError("%s must be on %s" % (name, device))
+
+
+def prefill(q, k, v, g, beta, *, state_in=None, cu_seqlens=None, out_dtype=None, qk_l2norm=True,
+            scale=1.0, want_state=True, workspace=None, stream=None):
+    """q, k [T, h_k, d]; v [T, h_v, d]; g, beta [T, h_v] fp32; state_in [N, h_v, d, d] fp32 or
+    None; cu_seqlens int32 [N+1] or None.  Returns (out [T, h_v, d], state_out or None)."""
+    dev = q.device
+    io = _io_dtype(q)
+    T, h_k, d = q.shape
+    h_v = v.shape[1]
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype, dev)
+    _need(g, "g", torch.float32, dev)
+    _need(beta, "beta", torch.float32, dev)
+    N = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    if state_in is not None:
+        _need(state_in, "state_in", torch.float32, dev)
+    od = io if out_dtype is None else out_dtype
+    desc = make_desc(num_seqs=N, total_tokens=T, h_k=h_k, h_v=h_v, d=d, io_dtype=io, out_dtype=od,
+                     qk_l2norm=qk_l2norm, scale=scale)
+    out = torch.empty((T, h_v, d), dtype=_TORCH_DT[od], device=dev)
+    state_out = torch.empty((N, h_v, d, d), dtype=torch.float32, device=dev) if want_state else None
+    nbytes = gdn_prefill_workspace_bytes(desc)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    gdn_prefill(desc, q, k, v, g, beta, state_in, out, state_out, cu_seqlens, CHUNK, workspace,
+                workspace.numel(), stream)
+    return out, state_out
+
+
+def decode_step(q, k, v, g, beta, state, *, out=None, out_dtype=None, qk_l2norm=True, scale=1.0,
+                stream=None):
+    """One token per sequence: q, k [N, h_k, d]; v [N, h_v, d]; g, beta [N, h_v];
+    state [N, h_v, d, d] fp32, updated in place.  Returns out [N, h_v, d]."""
+    dev = q.device
+    io = _io_dtype(q)
+    N, h_k, d = q.shape
+    h_v = v.shape[1]
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype, dev)
+    _need(g, "g", torch.float32, dev)
+    _need(beta, "beta", torch.float32, dev)
+    _need(state, "state", torch.float32, dev)
+    od = io if out_dtype is None else out_dtype
+    desc = make_desc(num_seqs=N, total_tokens=N, h_k=h_k, h_v=h_v, d=d, io_dtype=io, out_dtype=od,
+                     qk_l2norm=qk_l2norm, scale=scale)
+    if out is None:
+        out = torch.empty((N, h_v, d), dtype=_TORCH_DT[od], device=dev)
+    gdn_decode_step(desc, q, k, v, g, beta, state, out, stream)
+    return out

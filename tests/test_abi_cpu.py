@@ -1,0 +1,151 @@
+"""Boundary tests that need no GPU: the library loads, exports every function
+include/gdn.h declares, sizes workspaces, and rejects every invalid argument on
+the host before anything is enqueued (so no HIP call is reached).
+
+Only argument sets that fail validation are passed here.  As a second guard,
+the tests that pass made-up pointers are skipped wherever a GPU is visible, so
+a validation bug can never turn into a launch on bad addresses.
+"""
+import ctypes
+import os
+
+import pytest
+
+from linear_attention_recurrence_rule_amd import gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _gpu_visible():
+    import torch
+    return torch.cuda.is_available()
+
+
+fake_pointers = pytest.mark.skipif(_gpu_visible(), reason="made-up pointers are only passed where no GPU is visible")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(gdn.LIB_PATH):
+        from linear_attention_recurrence_rule_amd import build
+        build.build()
+    return gdn.lib()
+
+
+def test_exports_every_declared_function(L):
+    names = gdn.declared_functions()
+    assert set(names) == {"gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_decode_step",
+                          "gdn_status_str", "gdn_last_error"}
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_desc_layout_matches_header():
+    # int32, (pad), int64, 7 x int32, float  -> 48 bytes with 8-byte alignment
+    assert ctypes.sizeof(gdn.GdnDesc) == 48
+    assert gdn.GdnDesc.total_tokens.offset == 8
+    assert gdn.GdnDesc.scale.offset == 44
+
+
+def test_status_strings(L):
+    for s, name in enumerate(["GDN_OK", "GDN_ERR_INVALID_ARGUMENT", "GDN_ERR_UNSUPPORTED",
+                              "GDN_ERR_WORKSPACE", "GDN_ERR_HIP"]):
+        assert gdn.status_str(s) == name
+    assert gdn.status_str(99) == "GDN_UNKNOWN_STATUS"
+
+
+def desc(**kw):
+    base = dict(num_seqs=1, total_tokens=4096, h_k=16, h_v=32, d=128, io_dtype=gdn.GDN_BF16,
+                out_dtype=gdn.GDN_BF16, qk_l2norm=True, scale=1.0)
+    base.update(kw)
+    return gdn.make_desc(**base)
+
+
+def test_workspace_bytes(L):
+    # 64 blocks x 32 v-heads x record; record = 3 fp16 fragment sets + fp32 Ut, Ot + 512 B
+    rec = 3 * 64 * 128 * 2 + 2 * 64 * 128 * 4 + 256 + 256
+    plan = (1 * 16 + 64 * 4 + 255) // 256 * 256
+    assert gdn.gdn_prefill_workspace_bytes(desc()) == plan + 64 * 32 * rec
+    # packed sequences: at most T/64 + N blocks in total
+    n = gdn.gdn_prefill_workspace_bytes(desc(num_seqs=16, total_tokens=1000))
+    slots = (1000 + 16 * 63) // 64
+    assert n == (16 * 16 + slots * 4 + 255) // 256 * 256 + slots * 32 * rec
+    rec64f = 3 * 64 * 64 * 4 + 2 * 64 * 64 * 4 + 512
+    assert gdn.gdn_prefill_workspace_bytes(desc(total_tokens=256, h_k=1, h_v=1, d=64,
+                                                io_dtype=gdn.GDN_F32, out_dtype=gdn.GDN_F32)) == \
+        256 + 4 * rec64f
+    assert L.gdn_prefill_workspace_bytes(ctypes.byref(desc()), 32) == 0
+    assert "chunk" in gdn.last_error()
+
+
+FAKE = 0x1000  # never dereferenced: every case below fails validation first
+
+
+def call_prefill(d, *, q=FAKE, k=FAKE + 1 << 32, v=FAKE + 2 << 32, g=FAKE + 3 << 32, b=FAKE + 4 << 32,
+                 s_in=None, out=FAKE + 5 << 32, s_out=None, cu=None, chunk=64, ws=None, ws_bytes=0):
+    return gdn.lib().gdn_prefill(ctypes.byref(d), q, k, v, g, b, s_in, out, s_out, cu, chunk, ws,
+                                 ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_seqs=0), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(h_k=0), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(h_v=24, h_k=16), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(d=96), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(io_dtype=7), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(out_dtype=-1), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(total_tokens=-5), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(total_tokens=(1 << 30) + 1), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(io_dtype=gdn.GDN_F32), gdn.GDN_ERR_UNSUPPORTED),      # fp32 prefill at d=128
+    (dict(scale=float("inf")), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(num_seqs=3), gdn.GDN_ERR_INVALID_ARGUMENT),           # cu_seqlens NULL with N > 1
+])
+@fake_pointers
+def test_prefill_rejects_bad_descriptor(L, kw, status):
+    d = desc(**kw)
+    assert call_prefill(d) == status
+    assert gdn.last_error() != ""
+
+
+@fake_pointers
+def test_prefill_rejects_bad_pointers_and_sizes(L):
+    d = desc()
+    need = gdn.gdn_prefill_workspace_bytes(d)
+    ws = 0x7 << 40
+    assert call_prefill(d, chunk=128, ws=ws, ws_bytes=need) == gdn.GDN_ERR_UNSUPPORTED
+    assert call_prefill(d, q=None, ws=ws, ws_bytes=need) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call_prefill(d, out=None, ws=ws, ws_bytes=need) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call_prefill(d, ws=None, ws_bytes=need) == gdn.GDN_ERR_WORKSPACE
+    assert call_prefill(d, ws=ws, ws_bytes=need - 1) == gdn.GDN_ERR_WORKSPACE
+    # aliasing: out overlapping v is rejected
+    assert call_prefill(d, out=(FAKE + 2 << 32) + 64, ws=ws, ws_bytes=need) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert "overlap" in gdn.last_error()
+    # workspace overlapping q is rejected
+    assert call_prefill(d, ws=FAKE, ws_bytes=need) == gdn.GDN_ERR_INVALID_ARGUMENT
+    # state_out overlapping state_in at a different address is rejected
+    s = 0x9 << 40
+    assert call_prefill(d, s_in=s, s_out=s + 4, ws=ws, ws_bytes=need) == gdn.GDN_ERR_INVALID_ARGUMENT
+
+
+@fake_pointers
+def test_decode_rejects_bad_arguments(L):
+    lib = gdn.lib()
+    def call(d, **p):
+        a = dict(q=FAKE, k=FAKE + 1 << 32, v=FAKE + 2 << 32, g=FAKE + 3 << 32, b=FAKE + 4 << 32,
+                 s=FAKE + 5 << 32, o=FAKE + 6 << 32)
+        a.update(p)
+        return lib.gdn_decode_step(ctypes.byref(d), a["q"], a["k"], a["v"], a["g"], a["b"], a["s"],
+                                   a["o"], None)
+    assert call(desc(num_seqs=64, h_v=30)) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call(desc(num_seqs=64, d=32)) == gdn.GDN_ERR_UNSUPPORTED
+    assert call(desc(num_seqs=64), s=None) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call(desc(num_seqs=64), o=FAKE + 5 << 32) == gdn.GDN_ERR_INVALID_ARGUMENT  # out == state
+    assert call(desc(num_seqs=0)) == gdn.GDN_ERR_INVALID_ARGUMENT
+
+
+@fake_pointers
+def test_null_descriptor(L):
+    assert gdn.lib().gdn_prefill(None, None, None, None, None, None, None, None, None, None, 64,
+                                 None, 0, None) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert gdn.lib().gdn_decode_step(None, None, None, None, None, None, None, None, None) == \
+        gdn.GDN_ERR_INVALID_ARGUMENT
