@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Benchmark of the gated-delta-rule hot path on one MI355X.
+
+One step = one gdn_prefill call on the 4K-token workload (32 v-heads over 16
+q/k heads, d = 128, bf16 in and out, fp32 state, 64-token blocks), with inputs
+already resident in HBM.  ``value`` is prefill tokens/s over the K timed steps.
+The same JSON line also reports:
+  * decode: 512 consecutive gdn_decode_step launches on the decode workload
+    (64 sequences x 32 v-heads, d = 128, fp32 state);
+  * roofline of the dominant prefill kernel: algorithmic flops per launch over
+    its average HIP-event duration, against the 2.5 PFLOP/s dense fp16
+    matrix-core peak; the decode kernel's algorithmic bytes against 8 TB/s;
+  * cpu_baseline: the fp64 CPU oracle on this host, same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GDN prefill tok/s @4K (MFMA %) + decode steps/s (state GB/s, % HBM peak)"
+PEAK_FP16_TFLOPS = 2500.0     # MI355X dense fp16/bf16 matrix-core peak
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E peak
+PREFILL_WL = "prefill_t4096_hv32_hk16_d128"
+DECODE_WL = "decode_n64_hv32_hk16_d128_512steps"
+
+
+def algorithmic_prefill(T, h_v, h_k, d, C=64, out_bytes=2, io_bytes=2, state_in=False):
+    """Flops and HBM bytes the blocked method must spend (independent of this
+    implementation).  Per token and v-head: 10*C*d flops for the block-local
+    products (two Gram products, W, Ut and P.U) and 6*d^2 for the three
+    state-dependent products."""
+    flops_prep = 10.0 * C * d * T * h_v
+    flops_scan = 6.0 * d * d * T * h_v
+    nbytes = (2 * T * h_k * d * io_bytes + T * h_v * d * io_bytes + 2 * T * h_v * 4
+              + T * h_v * d * out_bytes + h_v * d * d * 4 * (2 if state_in else 1))
+    return flops_prep, flops_scan, nbytes
+
+
+def algorithmic_decode(N, h_v, h_k, d, io_bytes=2, out_bytes=2):
+    """The fp32 state read and written once, plus one token's inputs and output."""
+    return (2 * N * h_v * d * d * 4 + 2 * N * h_k * d * io_bytes + N * h_v * d * io_bytes
+            + 2 * N * h_v * 4 + N * h_v * d * out_bytes)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--decode-steps", type=int, default=512)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on exactly one GPU; --gpus %d is not supported "
+              "(the multi-GPU sharding is described in DESIGN.md, not built)." % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from linear_attention_recurrence_rule_amd import gdn, inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    L = gdn.lib()
+    dev = torch.device("cuda:0")
+
+    def to_dev(x):
+        if x is None:
+            return None
+        if x.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    # ---------------- prefill ----------------
+    w = inputs.WORKLOADS[PREFILL_WL]
+    x = inputs.workload_inputs(w)
+    T, h_k, h_v, d = w.total_tokens, w.h_k, w.h_v, w.d
+    q, k, v, g, b = (to_dev(x[n]) for n in ("q", "k", "v", "g", "beta"))
+    desc = gdn.make_desc(num_seqs=1, total_tokens=T, h_k=h_k, h_v=h_v, d=d, io_dtype=gdn.GDN_BF16,
+                         out_dtype=gdn.GDN_BF16)
+    ws_bytes = gdn.gdn_prefill_workspace_bytes(desc)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty((T, h_v, d), dtype=torch.bfloat16, device=dev)
+    s_out = torch.empty((1, h_v, d, d), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    dref = ctypes.byref(desc)
+    P = [t.data_ptr() for t in (q, k, v, g, b)]
+
+    def prefill_call():
+        st = L.gdn_prefill(dref, P[0], P[1], P[2], P[3], P[4], None, out.data_ptr(), s_out.data_ptr(),
+                           None, 64, ws.data_ptr(), ws_bytes, sp)
+        if st:
+            raise gdn.GdnError(st, gdn.last_error())
+
+    def prepare_call():
+        st = L.gdn_prefill_prepare(dref, P[0], P[1], P[2], P[3], P[4], None, 64, ws.data_ptr(), ws_bytes, sp)
+        if st:
+            raise gdn.GdnError(st, gdn.last_error())
+
+    def scan_call():
+        st = L.gdn_prefill_scan(dref, None, out.data_ptr(), s_out.data_ptr(), None, 64, ws.data_ptr(),
+                                ws_bytes, sp)
+        if st:
+            raise gdn.GdnError(st, gdn.last_error())
+
+    for _ in range(args.warmup):
+        prefill_call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        prefill_call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_step = e0.elapsed_time(e1) / args.steps
+    tok_s = T / (ms_step * 1e-3)
+
+    # per-kernel durations (events between the two launches of each call)
+    n_k = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_k)]
+    for i in range(n_k):
+        evs[i][0].record(stream)
+        prepare_call()
+        evs[i][1].record(stream)
+        scan_call()
+        evs[i][2].record(stream)
+    torch.cuda.synchronize()
+    us_prep = 1e3 * float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    us_scan = 1e3 * float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    f_prep, f_scan, nbytes = algorithmic_prefill(T, h_v, h_k, d)
+    kern = {"chunk_prep": (us_prep, f_prep), "chunk_scan": (us_scan, f_scan)}
+    dom = max(kern, key=lambda n: kern[n][0])
+    us_dom, f_dom = kern[dom]
+    ach = f_dom / (us_dom * 1e-6) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": PEAK_FP16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_FP16_TFLOPS, 4), "traffic": None,
+                "avg_launch_us": round(us_dom, 2),
+                "algorithmic_gflop_per_launch": round(f_dom / 1e9, 3)}
+    prefill_info = {
+        "tok_per_s": tok_s, "us_per_call": ms_step * 1e3,
+        "mfma_frac_whole_call": (f_prep + f_scan) / (ms_step * 1e-3) / (PEAK_FP16_TFLOPS * 1e12),
+        "hbm_frac_whole_call": nbytes / (ms_step * 1e-3) / (PEAK_HBM_GBS * 1e9),
+        "algorithmic_gflop": (f_prep + f_scan) / 1e9, "algorithmic_mib": nbytes / 2 ** 20,
+        "kernels_us": {"chunk_prep": round(us_prep, 2), "chunk_scan": round(us_scan, 2)},
+        "wall_s_timed_loop": t_wall,
+    }
+    del ws, out, q, k, v, g, b
+
+    # ---------------- decode ----------------
+    wd = inputs.WORKLOADS[DECODE_WL]
+    y = inputs.workload_inputs(wd)
+    N, dh_k, dh_v, dd, steps = wd.num_seqs, wd.h_k, wd.h_v, wd.d, min(args.decode_steps, wd.steps)
+    dq, dk, dv, dg, db = (to_dev(y[n]) for n in ("q", "k", "v", "g", "beta"))
+    state = to_dev(y["state"])
+    dout = torch.empty((N, dh_v, dd), dtype=torch.bfloat16, device=dev)
+    ddesc = gdn.make_desc(num_seqs=N, total_tokens=N, h_k=dh_k, h_v=dh_v, d=dd, io_dtype=gdn.GDN_BF16,
+                          out_dtype=gdn.GDN_BF16)
+    ddref = ctypes.byref(ddesc)
+    qs, ks, vs_, gs, bs = dq.stride(0) * 2, dk.stride(0) * 2, dv.stride(0) * 2, dg.stride(0) * 4, db.stride(0) * 4
+    base = [dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dg.data_ptr(), db.data_ptr()]
+    sptr, optr = state.data_ptr(), dout.data_ptr()
+
+    def decode_call(t):
+        st = L.gdn_decode_step(ddref, base[0] + t * qs, base[1] + t * ks, base[2] + t * vs_, base[3] + t * gs,
+                               base[4] + t * bs, sptr, optr, sp)
+        if st:
+            raise gdn.GdnError(st, gdn.last_error())
+
+    for t in range(10):
+        decode_call(t % steps)
+    torch.cuda.synchronize()
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    d0.record(stream)
+    for t in range(steps):
+        decode_call(t)
+    d1.record(stream)
+    torch.cuda.synchronize()
+    us_dec = d0.elapsed_time(d1) * 1e3 / steps
+    dbytes = algorithmic_decode(N, dh_v, dh_k, dd)
+    dec_gbs = dbytes / (us_dec * 1e-6) / 1e9
+    decode_info = {"workload": DECODE_WL, "steps_timed": steps, "us_per_step": us_dec,
+                   "steps_per_s": 1e6 / us_dec, "tok_per_s": N * 1e6 / us_dec,
+                   "algorithmic_mb_per_step": dbytes / 1e6,
+                   "roofline": {"bound": "hbm", "kernel": "decode_step", "achieved": round(dec_gbs, 1),
+                                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+                                "traffic": None}}
+    del dq, dk, dv, dg, db, state, dout
+
+    # ---------------- CPU baseline (the oracle, same 4K workload) ----------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import oracle
+        ncpu = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+        threads = max(1, min(h_v, ncpu))
+        times = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            oracle.scan(x["q"], x["k"], x["v"], x["g"], x["beta"], h_k=h_k, h_v=h_v, threads=threads)
+            times.append(time.perf_counter() - t0)
+        tc = float(np.median(times))
+        cpu = {"value": T / tc, "unit": "tok/s", "cores": threads, "kind": "oracle",
+               "sample": "the full 4096-token, 32-v-head workload, fp64 token scan, median of 3 runs "
+                         "(%.2f s each); host has %d usable cores" % (tc, ncpu)}
+
+    rec = {
+        "metric": METRIC, "value": tok_s, "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16-mfma/f32", "data": "synthetic",
+        "config": {"workload": PREFILL_WL, "total_tokens": T, "h_v": h_v, "h_k": h_k, "d": d, "chunk": 64,
+                   "io_dtype": "bf16", "out_dtype": "bf16", "state_in": "zeros"},
+        "roofline": roofline, "cpu_baseline": cpu, "prefill": prefill_info, "decode": decode_info,
+    }
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

@@ -84,9 +84,9 @@ typedef struct {
 } gdn_desc;
 
 /*
- * Bytes of device workspace gdn_prefill needs for this problem (0 when
- * total_tokens == 0).  It depends only on the descriptor and chunk.  Returns
- * 0 and sets gdn_last_error() for an invalid descriptor.
+ * Bytes of device workspace gdn_prefill needs for this problem.  It depends
+ * only on the descriptor and chunk (whether or not cu_seqlens is passed).
+ * Returns 0 and sets gdn_last_error() for an invalid descriptor.
  */
 size_t gdn_prefill_workspace_bytes(const gdn_desc *desc, int32_t chunk);
 
@@ -116,6 +116,34 @@ gdn_status gdn_prefill(const gdn_desc *desc,
                        const int32_t *cu_seqlens, int32_t chunk,
                        void *workspace, size_t workspace_bytes,
                        void *stream);
+
+/*
+ * The two phases of gdn_prefill, for callers that schedule or time them
+ * separately.  gdn_prefill is exactly gdn_prefill_prepare followed by
+ * gdn_prefill_scan on the same stream, with the same workspace.
+ *
+ * gdn_prefill_prepare: everything that does not depend on the carried state,
+ *   for all blocks at once (parallel over blocks and v-heads).  Reads q, k, v,
+ *   g, beta and cu_seqlens.  Writes only the workspace.
+ * gdn_prefill_scan: walks each sequence's blocks in order with the state held
+ *   on chip.  Reads the prepared workspace and state_in, and writes out and
+ *   state_out.  Pass the same desc, cu_seqlens (as a layout flag: NULL or
+ *   not) and workspace as the prepare call.  The workspace must not change in
+ *   between.
+ * Arguments, validation and errors are those of gdn_prefill.
+ */
+gdn_status gdn_prefill_prepare(const gdn_desc *desc,
+                               const void *q, const void *k, const void *v,
+                               const float *g, const float *beta,
+                               const int32_t *cu_seqlens, int32_t chunk,
+                               void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+gdn_status gdn_prefill_scan(const gdn_desc *desc,
+                            const float *state_in, void *out, float *state_out,
+                            const int32_t *cu_seqlens, int32_t chunk,
+                            void *workspace, size_t workspace_bytes,
+                            void *stream);
 
 /*
  * One decode step: one new token for each of num_seqs sequences.  This is the

@@ -159,10 +159,18 @@ size_t gdn_prefill_workspace_bytes(const gdn_desc* desc, int32_t chunk) {
     return ws_layout(desc, true).total;
 }
 
-gdn_status gdn_prefill(const gdn_desc* desc, const void* q, const void* k, const void* v,
-                       const float* g, const float* beta, const float* state_in, void* out,
-                       float* state_out, const int32_t* cu_seqlens, int32_t chunk, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+enum Phase { kPrepare = 1, kScan = 2, kBoth = 3 };
+
+// Validation shared by gdn_prefill and its two phases.  Pointers that a phase
+// does not use are passed as NULL and not checked.
+gdn_status prefill_call(Phase phase, const gdn_desc* desc, const void* q, const void* k, const void* v,
+                        const float* g, const float* beta, const float* state_in, void* out,
+                        float* state_out, const int32_t* cu_seqlens, int32_t chunk, void* workspace,
+                        size_t workspace_bytes, void* stream) {
     g_err[0] = 0;
     gdn_status st = check_desc(desc, true);
     if (st != GDN_OK) return st;
@@ -170,8 +178,9 @@ gdn_status gdn_prefill(const gdn_desc* desc, const void* q, const void* k, const
     const int64_t T = desc->total_tokens;
     const int N = desc->num_seqs, hk = desc->h_k, hv = desc->h_v, d = desc->d_k;
     if (!cu_seqlens && N != 1) return fail(GDN_ERR_INVALID_ARGUMENT, "cu_seqlens is NULL but num_seqs = %d", N);
-    if (T > 0 && (!q || !k || !v || !g || !beta || !out))
-        return fail(GDN_ERR_INVALID_ARGUMENT, "q, k, v, g, beta and out must be non-NULL");
+    if (T > 0 && (phase & kPrepare) && (!q || !k || !v || !g || !beta))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "q, k, v, g and beta must be non-NULL");
+    if (T > 0 && (phase & kScan) && !out) return fail(GDN_ERR_INVALID_ARGUMENT, "out must be non-NULL");
     const bool varlen = cu_seqlens != nullptr;
     const WsLayout ws = ws_layout(desc, varlen);
     // the requirement is what gdn_prefill_workspace_bytes reports, whichever layout is used
@@ -191,11 +200,10 @@ gdn_status gdn_prefill(const gdn_desc* desc, const void* q, const void* k, const
         {(const char*)state_in, state_in ? sbytes : 0, "state_in"},
         {(const char*)state_out, state_out ? sbytes : 0, "state_out"},
         {(const char*)cu_seqlens, cu_seqlens ? (size_t)(N + 1) * 4 : 0, "cu_seqlens"},
-        {(const char*)workspace, ws.total, "workspace"},
+        {(const char*)workspace, need, "workspace"},
     };
     st = check_overlaps(spans, sizeof(spans) / sizeof(spans[0]), state_in, state_out);
     if (st != GDN_OK) return st;
-    if (!state_out && T == 0) return GDN_OK;
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const bool in_bf16 = desc->io_dtype == GDN_BF16, out_bf16 = desc->out_dtype == GDN_BF16;
@@ -203,19 +211,49 @@ gdn_status gdn_prefill(const gdn_desc* desc, const void* q, const void* k, const
     void* info = varlen ? wsb + ws.info_off : nullptr;
     int32_t* slot_seq = varlen ? reinterpret_cast<int32_t*>(wsb + ws.slot_off) : nullptr;
     hipError_t e = hipSuccess;
-    if (varlen) {
-        e = gdn::launch_plan(cu_seqlens, N, (int)T, (int)ws.slots, info, slot_seq, s);
-        if (e != hipSuccess) return fail(GDN_ERR_HIP, "plan launch: %s", hipGetErrorString(e));
+    if (phase & kPrepare) {
+        if (varlen) {
+            e = gdn::launch_plan(cu_seqlens, N, (int)T, (int)ws.slots, info, slot_seq, s);
+            if (e != hipSuccess) return fail(GDN_ERR_HIP, "plan launch: %s", hipGetErrorString(e));
+        }
+        if (ws.slots > 0) {
+            e = gdn::launch_prep(d, in_bf16, q, k, v, g, beta, info, slot_seq, (int)ws.slots, (int)T, hk, hv,
+                                 desc->qk_l2norm, desc->scale, wsb + ws.rec_off, s);
+            if (e != hipSuccess) return fail(GDN_ERR_HIP, "chunk_prep launch: %s", hipGetErrorString(e));
+        }
     }
-    if (ws.slots > 0) {
-        e = gdn::launch_prep(d, in_bf16, q, k, v, g, beta, info, slot_seq, (int)ws.slots, (int)T, hk, hv,
-                             desc->qk_l2norm, desc->scale, wsb + ws.rec_off, s);
-        if (e != hipSuccess) return fail(GDN_ERR_HIP, "chunk_prep launch: %s", hipGetErrorString(e));
+    if ((phase & kScan) && (state_out || T > 0)) {
+        e = gdn::launch_scan(d, in_bf16, out_bf16, scan_waves(desc), wsb + ws.rec_off, info, state_in, state_out,
+                             out, N * hv, (int)T, hv, s);
+        if (e != hipSuccess) return fail(GDN_ERR_HIP, "chunk_scan launch: %s", hipGetErrorString(e));
     }
-    e = gdn::launch_scan(d, in_bf16, out_bf16, scan_waves(desc), wsb + ws.rec_off, info, state_in, state_out,
-                         out, N * hv, (int)T, hv, s);
-    if (e != hipSuccess) return fail(GDN_ERR_HIP, "chunk_scan launch: %s", hipGetErrorString(e));
     return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_prefill(const gdn_desc* desc, const void* q, const void* k, const void* v,
+                       const float* g, const float* beta, const float* state_in, void* out,
+                       float* state_out, const int32_t* cu_seqlens, int32_t chunk, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    return prefill_call(kBoth, desc, q, k, v, g, beta, state_in, out, state_out, cu_seqlens, chunk,
+                        workspace, workspace_bytes, stream);
+}
+
+gdn_status gdn_prefill_prepare(const gdn_desc* desc, const void* q, const void* k, const void* v,
+                               const float* g, const float* beta, const int32_t* cu_seqlens,
+                               int32_t chunk, void* workspace, size_t workspace_bytes, void* stream) {
+    return prefill_call(kPrepare, desc, q, k, v, g, beta, nullptr, nullptr, nullptr, cu_seqlens, chunk,
+                        workspace, workspace_bytes, stream);
+}
+
+gdn_status gdn_prefill_scan(const gdn_desc* desc, const float* state_in, void* out, float* state_out,
+                            const int32_t* cu_seqlens, int32_t chunk, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+    return prefill_call(kScan, desc, nullptr, nullptr, nullptr, nullptr, nullptr, state_in, out, state_out,
+                        cu_seqlens, chunk, workspace, workspace_bytes, stream);
 }
 
 gdn_status gdn_decode_step(const gdn_desc* desc, const void* q, const void* k, const void* v,

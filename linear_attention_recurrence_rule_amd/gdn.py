@@ -67,6 +67,10 @@ def lib():
             L.gdn_prefill_workspace_bytes.restype = sz
             L.gdn_prefill.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32, vp, sz, vp]
             L.gdn_prefill.restype = ctypes.c_int
+            L.gdn_prefill_prepare.argtypes = [dp, vp, vp, vp, vp, vp, vp, ctypes.c_int32, vp, sz, vp]
+            L.gdn_prefill_prepare.restype = ctypes.c_int
+            L.gdn_prefill_scan.argtypes = [dp, vp, vp, vp, vp, ctypes.c_int32, vp, sz, vp]
+            L.gdn_prefill_scan.restype = ctypes.c_int
             L.gdn_decode_step.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp]
             L.gdn_decode_step.restype = ctypes.c_int
             L.gdn_status_str.argtypes = [ctypes.c_int]
@@ -125,6 +129,20 @@ def gdn_prefill(desc, q, k, v, g, beta, state_in, out, state_out, cu_seqlens, ch
     _check(lib().gdn_prefill(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                              _ptr(state_in), _ptr(out), _ptr(state_out), _ptr(cu_seqlens), int(chunk),
                              _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def gdn_prefill_prepare(desc, q, k, v, g, beta, cu_seqlens, chunk, workspace, workspace_bytes,
+                        stream=None):
+    _check(lib().gdn_prefill_prepare(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                     _ptr(cu_seqlens), int(chunk), _ptr(workspace), int(workspace_bytes),
+                                     _stream(stream)))
+
+
+def gdn_prefill_scan(desc, state_in, out, state_out, cu_seqlens, chunk, workspace, workspace_bytes,
+                     stream=None):
+    _check(lib().gdn_prefill_scan(ctypes.byref(desc), _ptr(state_in), _ptr(out), _ptr(state_out),
+                                  _ptr(cu_seqlens), int(chunk), _ptr(workspace), int(workspace_bytes),
+                                  _stream(stream)))
 
 
 def gdn_decode_step(desc, q, k, v, g, beta, state, out, stream=None):

@@ -34,8 +34,8 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = gdn.declared_functions()
-    assert set(names) == {"gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_decode_step",
-                          "gdn_status_str", "gdn_last_error"}
+    assert set(names) == {"gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_prefill_prepare",
+                          "gdn_prefill_scan", "gdn_decode_step", "gdn_status_str", "gdn_last_error"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -125,6 +125,27 @@ def test_prefill_rejects_bad_pointers_and_sizes(L):
     # state_out overlapping state_in at a different address is rejected
     s = 0x9 << 40
     assert call_prefill(d, s_in=s, s_out=s + 4, ws=ws, ws_bytes=need) == gdn.GDN_ERR_INVALID_ARGUMENT
+
+
+@fake_pointers
+def test_prefill_phases_reject_bad_arguments(L):
+    d = desc()
+    need = gdn.gdn_prefill_workspace_bytes(d)
+    ws = 0x7 << 40
+    lib = gdn.lib()
+    by = ctypes.byref
+    # prepare: inputs required, workspace checked
+    assert lib.gdn_prefill_prepare(by(d), None, FAKE, FAKE + 2 << 32, FAKE + 3 << 32, FAKE + 4 << 32, None,
+                                   64, ws, need, None) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert lib.gdn_prefill_prepare(by(d), FAKE, FAKE + 1 << 32, FAKE + 2 << 32, FAKE + 3 << 32,
+                                   FAKE + 4 << 32, None, 64, ws, need - 1, None) == gdn.GDN_ERR_WORKSPACE
+    assert lib.gdn_prefill_prepare(by(desc(d=48)), FAKE, FAKE + 1 << 32, FAKE + 2 << 32, FAKE + 3 << 32,
+                                   FAKE + 4 << 32, None, 64, ws, need, None) == gdn.GDN_ERR_UNSUPPORTED
+    # scan: out required, aliasing checked
+    assert lib.gdn_prefill_scan(by(d), None, None, None, None, 64, ws, need, None) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert lib.gdn_prefill_scan(by(d), None, ws + 8, None, None, 64, ws, need, None) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert lib.gdn_prefill_scan(by(desc(num_seqs=2)), None, FAKE, None, None, 64, ws, need, None) == \
+        gdn.GDN_ERR_INVALID_ARGUMENT
 
 
 @fake_pointers
