@@ -22,8 +22,8 @@ hipError_t launch_prep(int d, bool in_bf16, const void* q, const void* k, const 
                        const float* g, const float* beta, const void* info, const int32_t* slot_seq,
                        int slots, int T, int h_k, int h_v, int l2norm, float scale, void* recs,
                        hipStream_t stream);
-hipError_t launch_scan(int d, bool in_bf16, bool out_bf16, int nw, const void* recs, const void* info,
-                       const float* s_in, float* s_out, void* out, int units, int T, int h_v,
+hipError_t launch_scan(int d, bool in_bf16, bool out_bf16, const void* recs, const void* info,
+                       const float* s_in, float* s_out, void* out, void* sink, int units, int T, int h_v,
                        hipStream_t stream);
 }  // namespace gdn
 
@@ -85,18 +85,23 @@ int64_t max_slots(const gdn_desc* d, bool varlen) {
     return (T + (int64_t)d->num_seqs * (kChunk - 1)) / kChunk;
 }
 
+// Workspace: [sink 1 KiB][plan: per-sequence info, slot -> sequence][block records]
+// The sink absorbs the chunk scan's stores for rows past the end of a block.
+constexpr size_t kSinkBytes = 1024;
+
 struct WsLayout {
-    size_t info_off, slot_off, rec_off, total;
+    size_t sink_off, info_off, slot_off, rec_off, total;
     int64_t slots;
 };
 
 WsLayout ws_layout(const gdn_desc* d, bool varlen) {
     WsLayout w{};
     w.slots = max_slots(d, varlen);
-    size_t plan = 0;
+    w.sink_off = 0;
+    size_t plan = kSinkBytes;
     if (varlen) {
-        w.info_off = 0;
-        w.slot_off = (size_t)d->num_seqs * 16;
+        w.info_off = plan;
+        w.slot_off = plan + (size_t)d->num_seqs * 16;
         plan = align_up(w.slot_off + (size_t)w.slots * 4, 256);
     }
     w.rec_off = plan;
@@ -110,6 +115,18 @@ struct Span {
     const char* name;
 };
 
+// Vector loads and stores need 16-byte aligned tensors (4 bytes for g, beta, cu_seqlens).
+gdn_status check_align(const Span* s, int count) {
+    for (int i = 0; i < count; ++i) {
+        if (!s[i].p || !s[i].n) continue;
+        const bool small = !strcmp(s[i].name, "g") || !strcmp(s[i].name, "beta") || !strcmp(s[i].name, "cu_seqlens");
+        const uintptr_t a = small ? 4 : (!strcmp(s[i].name, "workspace") ? 256 : 16);
+        if (reinterpret_cast<uintptr_t>(s[i].p) % a)
+            return fail(GDN_ERR_INVALID_ARGUMENT, "%s must be %zu-byte aligned", s[i].name, (size_t)a);
+    }
+    return GDN_OK;
+}
+
 // Any two non-empty ranges that overlap (other than the allowed in-place state pair) are rejected.
 gdn_status check_overlaps(const Span* s, int count, const void* allow_a, const void* allow_b) {
     for (int i = 0; i < count; ++i)
@@ -122,16 +139,6 @@ gdn_status check_overlaps(const Span* s, int count, const void* allow_a, const v
                 return fail(GDN_ERR_INVALID_ARGUMENT, "buffers %s and %s overlap", s[i].name, s[j].name);
         }
     return GDN_OK;
-}
-
-int scan_waves(const gdn_desc* d) {
-    if (const char* e = getenv("GDN_SCAN_WAVES")) {
-        const int w = atoi(e);
-        if ((w == 1 || w == 2 || (w == 4 && d->d_k == 128))) return w;
-    }
-    const int64_t units = (int64_t)d->num_seqs * d->h_v;
-    const int full = d->d_k / 32;  // waves that cover a whole head
-    return units >= 256 ? full : 1;
 }
 
 }  // namespace
@@ -202,6 +209,8 @@ gdn_status prefill_call(Phase phase, const gdn_desc* desc, const void* q, const 
         {(const char*)cu_seqlens, cu_seqlens ? (size_t)(N + 1) * 4 : 0, "cu_seqlens"},
         {(const char*)workspace, need, "workspace"},
     };
+    st = check_align(spans, sizeof(spans) / sizeof(spans[0]));
+    if (st != GDN_OK) return st;
     st = check_overlaps(spans, sizeof(spans) / sizeof(spans[0]), state_in, state_out);
     if (st != GDN_OK) return st;
 
@@ -223,8 +232,8 @@ gdn_status prefill_call(Phase phase, const gdn_desc* desc, const void* q, const 
         }
     }
     if ((phase & kScan) && (state_out || T > 0)) {
-        e = gdn::launch_scan(d, in_bf16, out_bf16, scan_waves(desc), wsb + ws.rec_off, info, state_in, state_out,
-                             out, N * hv, (int)T, hv, s);
+        e = gdn::launch_scan(d, in_bf16, out_bf16, wsb + ws.rec_off, info, state_in, state_out,
+                             out, wsb + ws.sink_off, N * hv, (int)T, hv, s);
         if (e != hipSuccess) return fail(GDN_ERR_HIP, "chunk_scan launch: %s", hipGetErrorString(e));
     }
     return GDN_OK;
@@ -274,6 +283,8 @@ gdn_status gdn_decode_step(const gdn_desc* desc, const void* q, const void* k, c
         {(const char*)out, (size_t)N * hv * d * os, "out"},
         {(const char*)state, (size_t)N * hv * d * d * 4, "state"},
     };
+    st = check_align(spans, sizeof(spans) / sizeof(spans[0]));
+    if (st != GDN_OK) return st;
     st = check_overlaps(spans, sizeof(spans) / sizeof(spans[0]), nullptr, nullptr);
     if (st != GDN_OK) return st;
     hipError_t e = gdn::launch_decode(d, desc->io_dtype == GDN_BF16, desc->out_dtype == GDN_BF16, q, k, v, g,

@@ -427,28 +427,84 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
 }
 
 // ---- sequential phase -------------------------------------------------------------------
-// Workgroup = NW waves; wave w owns state rows r0 = slice*32*NW + 32w .. +31 (two 16-row
-// column blocks of S^T).  S^T tiles (d-block mb, row block nb) live in registers:
-// lane (j, q) holds S[r0 + 16nb + j][16mb + 4q + 0..3].
+// One workgroup of 4 waves owns 32 rows of one (sequence, v-head) state, so a
+// d-wide head has d/32 workgroups.  The rows of S evolve independently.  Per
+// 64-token block:
+//   phase A (contraction over d_k): wave w forms the block's token rows
+//     16w..16w+15 of U = Ut - W S^T and O = Ot + Qt S^T for the 32 rows,
+//     reading S (as matrix-core operands) from LDS;
+//   phase B (contraction over tokens): wave w updates the d_k columns it owns,
+//     S^T <- gamma_n S^T + K^T diag(s) U, reading diag(s) U from LDS.
+// The fp32 state stays in registers for the whole sequence.  Each wave reads
+// only the operand fragments it uses, straight from the workspace into
+// registers, one block ahead of use.
 template <int D, typename OP>
-struct ScanLds {
-    OP frag[3 * CHUNK * D];  // -W, Qt, K^T fragments of the current block
-    float s[CHUNK];
-    float gn;
+struct ScanOps {
+    static constexpr int DB = D / 64;  // d_k blocks of 16 owned by a wave
+    Frag<OP> w[D / 32], q[D / 32], k[DB][2];
+    f4_t u[2], o[2];
+    f4_t s;    // s_t of this lane's 4 tokens
+    float gn;  // exp(G_n)
 };
 
-template <int D, typename OP, int NW, bool OUT_BF16>
-__global__ __launch_bounds__(NW * WAVE) void chunk_scan_kernel(
-    const char* __restrict__ recs, const SeqInfo* __restrict__ info, const float* __restrict__ state_in,
-    float* __restrict__ state_out, void* __restrict__ out, int T, int h_v) {
+template <int D, typename OP>
+__device__ __forceinline__ void load_ops(ScanOps<D, OP>& op, const char* rec, int w, int lane, int cb0) {
     using R = Rec<D, OP>;
-    __shared__ __align__(16) ScanLds<D, OP> L;
-    constexpr int SLICES = D / (32 * NW);
+    const OP* W = reinterpret_cast<const OP*>(rec + R::W);
+    const OP* Q = reinterpret_cast<const OP*>(rec + R::Q);
+    const OP* K = reinterpret_cast<const OP*>(rec + R::K);
+#pragma unroll
+    for (int kb = 0; kb < D / 32; ++kb) {
+        op.w[kb] = frag_stored<OP>(W, w * (D / 32) + kb, lane);
+        op.q[kb] = frag_stored<OP>(Q, w * (D / 32) + kb, lane);
+    }
+#pragma unroll
+    for (int i = 0; i < ScanOps<D, OP>::DB; ++i)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) op.k[i][kk] = frag_stored<OP>(K, (w * ScanOps<D, OP>::DB + i) * 2 + kk, lane);
+    const float* U = reinterpret_cast<const float*>(rec + R::U);
+    const float* O = reinterpret_cast<const float*>(rec + R::O);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+        const size_t t = ((size_t)(w * (D / 16) + cb0 + nb) * WAVE + lane) * 4;
+        op.u[nb] = *reinterpret_cast<const f4_t*>(U + t);
+        op.o[nb] = *reinterpret_cast<const f4_t*>(O + t);
+    }
+    op.s = *reinterpret_cast<const f4_t*>(reinterpret_cast<const float*>(rec + R::S) + 16 * w + 4 * (lane >> 4));
+    op.gn = reinterpret_cast<const float*>(rec + R::M)[0];
+}
+
+// Write 4 accumulator values (one lane's share of a 16x16 tile) as half of a
+// stored fragment: part 0 = elements 0..3, part 1 = elements 4..7.
+template <typename OP>
+__device__ __forceinline__ void store_part(OP* base, int frag, int part, int lane, const f4_t& x) {
+    OP* p = base + ((size_t)frag * WAVE + lane) * 8 + 4 * part;
+    if constexpr (sizeof(OP) == 2) {
+        typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+        h4_t h = {(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
+        *reinterpret_cast<h4_t*>(p) = h;
+    } else {
+        *reinterpret_cast<f4_t*>(p) = x;
+    }
+}
+
+template <int D, typename OP, bool OUT_BF16>
+__global__ __launch_bounds__(256) void chunk_scan_kernel(
+    const char* __restrict__ recs, const SeqInfo* __restrict__ info, const float* __restrict__ state_in,
+    float* __restrict__ state_out, void* __restrict__ out, char* __restrict__ sink, int T, int h_v) {
+    using R = Rec<D, OP>;
+    constexpr int SLICES = D / 32;
+    constexpr int DB = ScanOps<D, OP>::DB;
+    __shared__ __align__(16) OP sS[(D / 32) * 2 * WAVE * 8];  // S^T as B fragments (kb, row block)
+    __shared__ __align__(16) OP sU[2 * 2 * WAVE * 8];         // diag(s) U as B fragments (kk, row block)
+    constexpr int OB = OUT_BF16 ? 2 : 4;                       // bytes per output element
+    __shared__ __align__(16) char sO[4][16 * 32 * OB];         // per wave: 16 tokens x 32 outputs, row-major
     const int slice = blockIdx.x % SLICES;
     const int unit = blockIdx.x / SLICES;  // sequence * h_v + v-head
     const int n = unit / h_v, h = unit - n * h_v;
-    const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
-    const int r0 = slice * 32 * NW + 32 * wave;
+    const int tid = threadIdx.x, w = tid / WAVE, lane = tid % WAVE;
+    const int j16 = lane & 15, q4 = lane >> 4;
+    const int r0 = slice * 32, cb0 = r0 / 16;
     int begin, len, slot0;
     if (info) {
         const SeqInfo si = info[n];
@@ -456,117 +512,112 @@ __global__ __launch_bounds__(NW * WAVE) void chunk_scan_kernel(
     } else {
         begin = 0; len = T; slot0 = 0;
     }
-    const int j16 = lane & 15, q4 = lane >> 4;
 
-    f4_t S[D / 16][2];
+    // S^T tiles for the d_k blocks this wave owns: St[i][nb], lane (j, q) holds
+    // S[r0 + 16nb + j][16 mb + 4q + 0..3] with mb = w*DB + i
+    f4_t St[DB][2];
     const size_t sbase = (size_t)unit * D * D;
 #pragma unroll
-    for (int mb = 0; mb < D / 16; ++mb)
+    for (int i = 0; i < DB; ++i)
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
+            const int mb = w * DB + i;
             if (state_in) {
                 const float4 x = *reinterpret_cast<const float4*>(
                     state_in + sbase + (size_t)(r0 + 16 * nb + j16) * D + 16 * mb + 4 * q4);
-                S[mb][nb] = f4_t{x.x, x.y, x.z, x.w};
+                St[i][nb] = f4_t{x.x, x.y, x.z, x.w};
             } else {
-                S[mb][nb] = f4_t{0, 0, 0, 0};
+                St[i][nb] = f4_t{0, 0, 0, 0};
             }
+            store_part<OP>(sS, (mb / 2) * 2 + nb, mb % 2, lane, St[i][nb]);
         }
 
     const int nchunks = (len + CHUNK - 1) / CHUNK;
-    constexpr int FRAG_ELEMS = 3 * CHUNK * D;
-    constexpr int VEC = 16 / sizeof(OP);  // elements per 16-byte copy
-    for (int c = 0; c < nchunks; ++c) {
-        const char* rec = recs + ((size_t)(slot0 + c) * h_v + h) * R::BYTES;
-        // stage the shared fragments (contiguous W, Q, K regions) into LDS
-        const uint4* src = reinterpret_cast<const uint4*>(rec + R::W);
-        uint4* dst = reinterpret_cast<uint4*>(L.frag);
-        for (int i = tid; i < FRAG_ELEMS / VEC; i += NW * WAVE) dst[i] = src[i];
-        if (tid < CHUNK) L.s[tid] = reinterpret_cast<const float*>(rec + R::S)[tid];
-        if (tid == 0) L.gn = reinterpret_cast<const float*>(rec + R::M)[0];
-        // value-side accumulators for this wave's columns
-        const float* urec = reinterpret_cast<const float*>(rec + R::U);
-        const float* orec = reinterpret_cast<const float*>(rec + R::O);
-        f4_t accU[4][2], accO[4][2];
+    auto rec_of = [&](int c) { return recs + ((size_t)(slot0 + c) * h_v + h) * R::BYTES; };
+
+    auto step = [&](const ScanOps<D, OP>& op, int c) {
+        __syncthreads();  // S^T fragments of this block are complete
+        f4_t accU[2], accO[2];
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
+        for (int nb = 0; nb < 2; ++nb) { accU[nb] = op.u[nb]; accO[nb] = op.o[nb]; }
+#pragma unroll
+        for (int kb = 0; kb < D / 32; ++kb)
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb) {
-                const int cb = (r0 >> 4) + nb;
-                accU[mb][nb] = *reinterpret_cast<const f4_t*>(urec + ((size_t)(mb * (D / 16) + cb) * WAVE + lane) * 4);
-                accO[mb][nb] = *reinterpret_cast<const f4_t*>(orec + ((size_t)(mb * (D / 16) + cb) * WAVE + lane) * 4);
+                const Frag<OP> bs = frag_stored<OP>(sS, kb * 2 + nb, lane);
+                mma(accU[nb], op.w[kb], bs);
+                mma(accO[nb], op.q[kb], bs);
             }
-        __syncthreads();
-
-        const OP* fW = L.frag;
-        const OP* fQ = L.frag + CHUNK * D;
-        const OP* fK = L.frag + 2 * CHUNK * D;
-        // U = Ut - W S^T ; O = Ot + Qt S^T   (contraction over d_k)
-#pragma unroll
-        for (int kb = 0; kb < D / 32; ++kb) {
-            Frag<OP> bs[2];
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb) bs[nb] = frag_from_acc<OP>(S[2 * kb][nb], S[2 * kb + 1][nb]);
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
-                const Frag<OP> fw = frag_stored<OP>(fW, mb * (D / 32) + kb, lane);
-                const Frag<OP> fq = frag_stored<OP>(fQ, mb * (D / 32) + kb, lane);
-#pragma unroll
-                for (int nb = 0; nb < 2; ++nb) {
-                    mma(accU[mb][nb], fw, bs[nb]);
-                    mma(accO[mb][nb], fq, bs[nb]);
-                }
-            }
-        }
-        // outputs of the valid tokens
+        // outputs: transpose the wave's 16 x 32 tile through LDS, then one
+        // unconditional 16-byte store per lane (rows past the block's end go to the sink)
         const int tok0 = begin + c * CHUNK;
         const int nt = min(CHUNK, len - c * CHUNK);
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
+        for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int t = 16 * mb + 4 * q4 + r;
-                if (t < nt) {
-                    const size_t o = ((size_t)(tok0 + t) * h_v + h) * D + r0;
-#pragma unroll
-                    for (int nb = 0; nb < 2; ++nb) store1<OUT_BF16>(out, o + 16 * nb + j16, accO[mb][nb][r]);
-                }
+                const int e = (4 * q4 + r) * 32 + 16 * nb + j16;
+                if constexpr (OUT_BF16) reinterpret_cast<uint16_t*>(sO[w])[e] = f32_to_bf16(accO[nb][r]);
+                else reinterpret_cast<float*>(sO[w])[e] = accO[nb][r];
             }
-        // U rows scaled by s_t, as B fragments over tokens
-        Frag<OP> bu[2][2];
+        {
+            constexpr int LPRW = 32 * OB / 16;  // lanes per output row (16 B each)
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    frag_set(bu[kk][nb], e, accU[2 * kk][nb][e] * L.s[32 * kk + 4 * q4 + e]);
-                    frag_set(bu[kk][nb], e + 4, accU[2 * kk + 1][nb][e] * L.s[32 * kk + 16 + 4 * q4 + e]);
-                }
-            }
-        // S^T <- gamma_n S^T + K^T (diag(s) U)
-        const float gn = L.gn;
-#pragma unroll
-        for (int mb = 0; mb < D / 16; ++mb) {
-            const Frag<OP> fk0 = frag_stored<OP>(fK, mb * 2 + 0, lane);
-            const Frag<OP> fk1 = frag_stored<OP>(fK, mb * 2 + 1, lane);
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-                S[mb][nb] *= gn;
-                mma(S[mb][nb], fk0, bu[0][nb]);
-                mma(S[mb][nb], fk1, bu[1][nb]);
+            for (int part = 0; part < LPRW * 16 / WAVE; ++part) {
+                const int idx = part * WAVE + lane;
+                const int row = idx / LPRW, col16 = idx % LPRW;
+                const uint4 val = *reinterpret_cast<const uint4*>(sO[w] + row * 32 * OB + col16 * 16);
+                const int t = 16 * w + row;
+                char* dst = (t < nt) ? reinterpret_cast<char*>(out) +
+                                           (((size_t)(tok0 + t) * h_v + h) * D + r0) * OB + col16 * 16
+                                     : sink + lane * 16;
+                *reinterpret_cast<uint4*>(dst) = val;
             }
         }
-        __syncthreads();  // LDS is overwritten by the next block
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            f4_t us;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) us[r] = accU[nb][r] * op.s[r];
+            store_part<OP>(sU, (w / 2) * 2 + nb, w % 2, lane, us);
+        }
+        __syncthreads();  // diag(s) U complete; S^T fragments no longer read
+#pragma unroll
+        for (int i = 0; i < DB; ++i)
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+                St[i][nb] *= op.gn;
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) mma(St[i][nb], op.k[i][kk], frag_stored<OP>(sU, kk * 2 + nb, lane));
+                const int mb = w * DB + i;
+                store_part<OP>(sS, (mb / 2) * 2 + nb, mb % 2, lane, St[i][nb]);
+            }
+    };
+
+    // Two operand sets in flight.  Every iteration issues the same memory
+    // operations (a prefetch past the last block re-reads the last block), so
+    // the wait before each block covers exactly that block's loads.
+    if (nchunks > 0) {
+        const int last = nchunks - 1;
+        ScanOps<D, OP> opA, opB;
+        load_ops<D, OP>(opA, rec_of(0), w, lane, cb0);
+        load_ops<D, OP>(opB, rec_of(min(1, last)), w, lane, cb0);
+        for (int c = 0; c < nchunks; c += 2) {
+            step(opA, c);
+            load_ops<D, OP>(opA, rec_of(min(c + 2, last)), w, lane, cb0);
+            if (c + 1 > last) break;
+            step(opB, c + 1);
+            load_ops<D, OP>(opB, rec_of(min(c + 3, last)), w, lane, cb0);
+        }
     }
 
     if (state_out) {
 #pragma unroll
-        for (int mb = 0; mb < D / 16; ++mb)
+        for (int i = 0; i < DB; ++i)
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb) {
-                const f4_t x = S[mb][nb];
-                *reinterpret_cast<float4*>(state_out + sbase + (size_t)(r0 + 16 * nb + j16) * D + 16 * mb + 4 * q4) =
+                const f4_t x = St[i][nb];
+                *reinterpret_cast<float4*>(state_out + sbase + (size_t)(r0 + 16 * nb + j16) * D + 16 * (w * DB + i) + 4 * q4) =
                     make_float4(x[0], x[1], x[2], x[3]);
             }
     }
@@ -616,29 +667,24 @@ hipError_t launch_prep(int d, bool in_bf16, const void* q, const void* k, const 
     return hipErrorInvalidValue;
 }
 
-template <int D, typename OP, int NW, bool OB>
+template <int D, typename OP, bool OB>
 static hipError_t launch_scan_t(const void* recs, const void* info, const float* s_in, float* s_out,
-                                void* out, int units, int T, int h_v, hipStream_t stream) {
-    constexpr int SLICES = D / (32 * NW);
-    hipLaunchKernelGGL((chunk_scan_kernel<D, OP, NW, OB>), dim3(units * SLICES), dim3(NW * WAVE), 0,
-                       stream, reinterpret_cast<const char*>(recs),
-                       reinterpret_cast<const SeqInfo*>(info), s_in, s_out, out, T, h_v);
+                                void* out, void* sink, int units, int T, int h_v, hipStream_t stream) {
+    hipLaunchKernelGGL((chunk_scan_kernel<D, OP, OB>), dim3(units * (D / 32)), dim3(256), 0, stream,
+                       reinterpret_cast<const char*>(recs), reinterpret_cast<const SeqInfo*>(info), s_in,
+                       s_out, out, reinterpret_cast<char*>(sink), T, h_v);
     return hipGetLastError();
 }
 
-hipError_t launch_scan(int d, bool in_bf16, bool out_bf16, int nw, const void* recs, const void* info,
-                       const float* s_in, float* s_out, void* out, int units, int T, int h_v,
+hipError_t launch_scan(int d, bool in_bf16, bool out_bf16, const void* recs, const void* info,
+                       const float* s_in, float* s_out, void* out, void* sink, int units, int T, int h_v,
                        hipStream_t stream) {
-#define GDN_SCAN(D, OP, IB, NW, OB)                                                               \
-    if (d == D && in_bf16 == IB && nw == NW && out_bf16 == OB)                                    \
-        return launch_scan_t<D, OP, NW, OB>(recs, info, s_in, s_out, out, units, T, h_v, stream);
-    GDN_SCAN(128, _Float16, true, 1, true) GDN_SCAN(128, _Float16, true, 1, false)
-    GDN_SCAN(128, _Float16, true, 2, true) GDN_SCAN(128, _Float16, true, 2, false)
-    GDN_SCAN(128, _Float16, true, 4, true) GDN_SCAN(128, _Float16, true, 4, false)
-    GDN_SCAN(64, _Float16, true, 1, true) GDN_SCAN(64, _Float16, true, 1, false)
-    GDN_SCAN(64, _Float16, true, 2, true) GDN_SCAN(64, _Float16, true, 2, false)
-    GDN_SCAN(64, float, false, 1, true) GDN_SCAN(64, float, false, 1, false)
-    GDN_SCAN(64, float, false, 2, true) GDN_SCAN(64, float, false, 2, false)
+#define GDN_SCAN(D, OP, IB, OB)                                                                   \
+    if (d == D && in_bf16 == IB && out_bf16 == OB)                                                \
+        return launch_scan_t<D, OP, OB>(recs, info, s_in, s_out, out, sink, units, T, h_v, stream);
+    GDN_SCAN(128, _Float16, true, true) GDN_SCAN(128, _Float16, true, false)
+    GDN_SCAN(64, _Float16, true, true) GDN_SCAN(64, _Float16, true, false)
+    GDN_SCAN(64, float, false, true) GDN_SCAN(64, float, false, false)
 #undef GDN_SCAN
     return hipErrorInvalidValue;
 }

@@ -64,21 +64,21 @@ def desc(**kw):
 def test_workspace_bytes(L):
     # 64 blocks x 32 v-heads x record; record = 3 fp16 fragment sets + fp32 Ut, Ot + 512 B
     rec = 3 * 64 * 128 * 2 + 2 * 64 * 128 * 4 + 256 + 256
-    plan = (1 * 16 + 64 * 4 + 255) // 256 * 256
+    plan = (1024 + 1 * 16 + 64 * 4 + 255) // 256 * 256
     assert gdn.gdn_prefill_workspace_bytes(desc()) == plan + 64 * 32 * rec
     # packed sequences: at most T/64 + N blocks in total
     n = gdn.gdn_prefill_workspace_bytes(desc(num_seqs=16, total_tokens=1000))
     slots = (1000 + 16 * 63) // 64
-    assert n == (16 * 16 + slots * 4 + 255) // 256 * 256 + slots * 32 * rec
+    assert n == (1024 + 16 * 16 + slots * 4 + 255) // 256 * 256 + slots * 32 * rec
     rec64f = 3 * 64 * 64 * 4 + 2 * 64 * 64 * 4 + 512
     assert gdn.gdn_prefill_workspace_bytes(desc(total_tokens=256, h_k=1, h_v=1, d=64,
                                                 io_dtype=gdn.GDN_F32, out_dtype=gdn.GDN_F32)) == \
-        256 + 4 * rec64f
+        1280 + 4 * rec64f
     assert L.gdn_prefill_workspace_bytes(ctypes.byref(desc()), 32) == 0
     assert "chunk" in gdn.last_error()
 
 
-FAKE = 0x1000  # never dereferenced: every case below fails validation first
+FAKE = 0x10000  # never dereferenced: every case below fails validation first
 
 
 def call_prefill(d, *, q=FAKE, k=FAKE + 1 << 32, v=FAKE + 2 << 32, g=FAKE + 3 << 32, b=FAKE + 4 << 32,
@@ -122,6 +122,10 @@ def test_prefill_rejects_bad_pointers_and_sizes(L):
     assert "overlap" in gdn.last_error()
     # workspace overlapping q is rejected
     assert call_prefill(d, ws=FAKE, ws_bytes=need) == gdn.GDN_ERR_INVALID_ARGUMENT
+    # misaligned tensors are rejected
+    assert call_prefill(d, q=FAKE + 2, ws=ws, ws_bytes=need) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert "aligned" in gdn.last_error()
+    assert call_prefill(d, ws=ws + 16, ws_bytes=need) == gdn.GDN_ERR_INVALID_ARGUMENT
     # state_out overlapping state_in at a different address is rejected
     s = 0x9 << 40
     assert call_prefill(d, s_in=s, s_out=s + 4, ws=ws, ws_bytes=need) == gdn.GDN_ERR_INVALID_ARGUMENT
