@@ -14,7 +14,8 @@
 namespace gdn {
 hipError_t launch_decode(int d, bool in_bf16, bool out_bf16, const void* q, const void* k,
                          const void* v, const float* g, const float* beta, float* state, void* out,
-                         int units, int h_k, int h_v, int l2norm, float scale, hipStream_t stream);
+                         int units, int h_k, int h_v, int l2norm, float scale, int grid,
+                         hipStream_t stream);
 size_t prefill_record_bytes(int d, bool in_bf16);
 hipError_t launch_plan(const int32_t* cu, int N, int T, int max_slots, void* info, int32_t* slot_seq,
                        hipStream_t stream);
@@ -139,6 +140,20 @@ gdn_status check_overlaps(const Span* s, int count, const void* allow_a, const v
                 return fail(GDN_ERR_INVALID_ARGUMENT, "buffers %s and %s overlap", s[i].name, s[j].name);
         }
     return GDN_OK;
+}
+
+// Decode workgroups: a few per compute unit, each walking several (sequence,
+// v-head) units so that one unit's loads overlap the previous unit's work.
+int decode_grid(int units) {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+    }
+    int per_cu = 2;
+    if (const char* e = getenv("GDN_DECODE_WG_PER_CU")) per_cu = atoi(e);
+    const int grid = cus * (per_cu > 0 ? per_cu : 2);
+    return grid < units ? grid : units;
 }
 
 }  // namespace
@@ -289,7 +304,7 @@ gdn_status gdn_decode_step(const gdn_desc* desc, const void* q, const void* k, c
     if (st != GDN_OK) return st;
     hipError_t e = gdn::launch_decode(d, desc->io_dtype == GDN_BF16, desc->out_dtype == GDN_BF16, q, k, v, g,
                                       beta, state, out, N * hv, hk, hv, desc->qk_l2norm, desc->scale,
-                                      reinterpret_cast<hipStream_t>(stream));
+                                      decode_grid(N * hv), reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
     return GDN_OK;
 }

@@ -15,48 +15,57 @@
 // Both dot products S k^ and S q^ are taken from the state as loaded, in one
 // pass.
 //
-// Layout: one workgroup per (sequence, v-head), d/32 waves.  Each wave owns
-// 32 state rows.  A lane holds 4 consecutive entries (16 bytes) of one row,
-// so d/4 lanes cover a row, and each wave-wide load reads 1 KiB of contiguous
-// state.  The loads are issued before any other work.  The row sums are a
-// reduce-scatter across the d/4 lanes of a row.  After it, lane c of a row
-// group holds either S k^ or S q^ of one row.
+// Layout: a workgroup has d/32 waves, and each wave owns 32 state rows.  A
+// lane holds 4 consecutive entries (16 bytes) of one row, so d/4 lanes cover a
+// row, and each wave-wide load reads 1 KiB of contiguous state.  The row sums
+// are a reduce-scatter across the d/4 lanes of a row.  After it, lane c of a
+// row group holds either S k^ or S q^ of one row.  A grid of a few workgroups
+// per compute unit walks the (sequence, v-head) units.  The next unit's state
+// and token inputs are loaded while the current unit computes and stores.
 #include "gdn_device.h"
 
 namespace gdn {
 
-template <int D, bool IN_BF16, bool OUT_BF16>
-__global__ __launch_bounds__(2 * D) void decode_step_kernel(
-    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
-    const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ state,
-    void* __restrict__ out, int h_k, int h_v, int l2norm, float scale) {
-    constexpr int LPR = D / 4;      // lanes per state row
-    constexpr int RPI = WAVE / LPR;  // rows covered by one wave-wide load
-    constexpr int NL = LPR / 2;      // loads per lane (32 rows per wave)
-    static_assert(RPI * NL == 32, "each wave owns 32 rows");
+// Everything one unit needs, loaded together so the next unit's loads can be
+// in flight while the current unit computes.
+template <int D>
+struct DecodeIn {
+    float4 s[D / 8];  // this lane's state slices (D/8 = LPR/2 rows)
+    float kx[4], qx[4];
+    float v, g, b;
+};
 
-    const int unit = blockIdx.x;  // sequence * h_v + v-head
+template <int D, bool IN_BF16>
+__device__ __forceinline__ void decode_load(DecodeIn<D>& in, const float* __restrict__ state, const void* q,
+                                            const void* k, const void* v, const float* g, const float* beta,
+                                            int unit, int h_k, int h_v, int wave, int lane) {
+    constexpr int LPR = D / 4, RPI = WAVE / LPR, NL = LPR / 2;
     const int n = unit / h_v, h = unit - n * h_v;
     const int hk = h / (h_v / h_k);
-    const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
     const int c = lane % LPR, sub = lane / LPR;
-
-    float* S = state + (size_t)unit * D * D;
-    float4 s[NL];
+    const float* S = state + (size_t)unit * D * D;
 #pragma unroll
     for (int m = 0; m < NL; ++m) {
         const int row = wave * 32 + m * RPI + sub;
-        s[m] = *reinterpret_cast<const float4*>(S + (size_t)row * D + 4 * c);
+        in.s[m] = *reinterpret_cast<const float4*>(S + (size_t)row * D + 4 * c);
     }
+    load4<IN_BF16>(k, ((size_t)n * h_k + hk) * D + 4 * c, in.kx);
+    load4<IN_BF16>(q, ((size_t)n * h_k + hk) * D + 4 * c, in.qx);
+    const int mrow = (c < NL) ? c : c - NL;
+    in.v = load1<IN_BF16>(v, (size_t)unit * D + wave * 32 + mrow * RPI + sub);
+    in.g = g[unit];
+    in.b = beta[unit];
+}
 
-    float kx[4], qx[4];
-    load4<IN_BF16>(k, ((size_t)n * h_k + hk) * D + 4 * c, kx);
-    load4<IN_BF16>(q, ((size_t)n * h_k + hk) * D + 4 * c, qx);
-    const float alpha = expf(g[unit]);
-    const float bt = beta[unit];
-
-    float ssk = kx[0] * kx[0] + kx[1] * kx[1] + kx[2] * kx[2] + kx[3] * kx[3];
-    float ssq = qx[0] * qx[0] + qx[1] * qx[1] + qx[2] * qx[2] + qx[3] * qx[3];
+template <int D, bool OUT_BF16>
+__device__ __forceinline__ void decode_compute(DecodeIn<D>& in, float* __restrict__ state, void* out, int unit,
+                                               int l2norm, float scale, int wave, int lane) {
+    constexpr int LPR = D / 4, RPI = WAVE / LPR, NL = LPR / 2;
+    const int c = lane % LPR, sub = lane / LPR;
+    const float alpha = expf(in.g);
+    float ssk = 0.f, ssq = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { ssk += in.kx[e] * in.kx[e]; ssq += in.qx[e] * in.qx[e]; }
 #pragma unroll
     for (int mask = LPR / 2; mask >= 1; mask >>= 1) {
         ssk += shfl_xor(ssk, mask);
@@ -64,8 +73,9 @@ __global__ __launch_bounds__(2 * D) void decode_step_kernel(
     }
     const float rk = l2norm ? 1.0f / sqrtf(ssk + 1e-6f) : 1.0f;
     const float rq = (l2norm ? 1.0f / sqrtf(ssq + 1e-6f) : 1.0f) * scale;
+    float kx[4], qx[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) { kx[e] *= rk; qx[e] *= rq; }
+    for (int e = 0; e < 4; ++e) { kx[e] = in.kx[e] * rk; qx[e] = in.qx[e] * rq; }
     float kq = kx[0] * qx[0] + kx[1] * qx[1] + kx[2] * qx[2] + kx[3] * qx[3];
 #pragma unroll
     for (int mask = LPR / 2; mask >= 1; mask >>= 1) kq += shfl_xor(kq, mask);
@@ -74,8 +84,9 @@ __global__ __launch_bounds__(2 * D) void decode_step_kernel(
     float x[LPR];
 #pragma unroll
     for (int m = 0; m < NL; ++m) {
-        x[m] = s[m].x * kx[0] + s[m].y * kx[1] + s[m].z * kx[2] + s[m].w * kx[3];
-        x[NL + m] = s[m].x * qx[0] + s[m].y * qx[1] + s[m].z * qx[2] + s[m].w * qx[3];
+        const float4 sm = in.s[m];
+        x[m] = sm.x * kx[0] + sm.y * kx[1] + sm.z * kx[2] + sm.w * kx[3];
+        x[NL + m] = sm.x * qx[0] + sm.y * qx[1] + sm.z * qx[2] + sm.w * qx[3];
     }
     // reduce-scatter over the LPR lanes of each row group: afterwards lane c holds x[c] summed
 #pragma unroll
@@ -92,45 +103,72 @@ __global__ __launch_bounds__(2 * D) void decode_step_kernel(
     // lanes c < NL: row (c) has p = S k^ ; lanes c >= NL: row (c - NL) has S q^
     const int mrow = (c < NL) ? c : c - NL;
     const int row = wave * 32 + mrow * RPI + sub;
-    const size_t vo = ((size_t)n * h_v + h) * D + row;
     float u = 0.f;
-    if (c < NL) u = bt * (load1<IN_BF16>(v, vo) - alpha * red);
+    if (c < NL) u = in.b * (in.v - alpha * red);
     const float u_pair = shfl_xor(u, NL);
-    if (c >= NL) store1<OUT_BF16>(out, vo, alpha * red + u_pair * kq);
+    if (c >= NL) store1<OUT_BF16>(out, (size_t)unit * D + row, alpha * red + u_pair * kq);
 
     // rank-1 update; u of row m lives in lane (group base + m)
     const int base = lane - c;
+    float* S = state + (size_t)unit * D * D;
 #pragma unroll
     for (int m = 0; m < NL; ++m) {
         const float um = __shfl(u, base + m, WAVE);
-        s[m].x = alpha * s[m].x + um * kx[0];
-        s[m].y = alpha * s[m].y + um * kx[1];
-        s[m].z = alpha * s[m].z + um * kx[2];
-        s[m].w = alpha * s[m].w + um * kx[3];
-    }
-#pragma unroll
-    for (int m = 0; m < NL; ++m) {
+        float4 sm = in.s[m];
+        sm.x = alpha * sm.x + um * kx[0];
+        sm.y = alpha * sm.y + um * kx[1];
+        sm.z = alpha * sm.z + um * kx[2];
+        sm.w = alpha * sm.w + um * kx[3];
         const int r2 = wave * 32 + m * RPI + sub;
-        *reinterpret_cast<float4*>(S + (size_t)r2 * D + 4 * c) = s[m];
+        *reinterpret_cast<float4*>(S + (size_t)r2 * D + 4 * c) = sm;
+    }
+}
+
+// Each workgroup walks units blockIdx.x, blockIdx.x + gridDim.x, ... with the
+// next unit's state and token inputs loaded while the current unit computes.
+// Every iteration issues the same loads (past the end it re-reads the last
+// unit, unused), so each wait covers exactly one unit's data.
+template <int D, bool IN_BF16, bool OUT_BF16>
+__global__ __launch_bounds__(2 * D) void decode_step_kernel(
+    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ state,
+    void* __restrict__ out, int units, int h_k, int h_v, int l2norm, float scale) {
+    const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
+    const int stride = gridDim.x, last = units - 1;
+    int u = blockIdx.x;
+    if (u > last) return;
+    DecodeIn<D> A, B;
+    decode_load<D, IN_BF16>(A, state, q, k, v, g, beta, u, h_k, h_v, wave, lane);
+    for (;;) {
+        decode_load<D, IN_BF16>(B, state, q, k, v, g, beta, min(u + stride, last), h_k, h_v, wave, lane);
+        decode_compute<D, OUT_BF16>(A, state, out, u, l2norm, scale, wave, lane);
+        u += stride;
+        if (u > last) break;
+        decode_load<D, IN_BF16>(A, state, q, k, v, g, beta, min(u + stride, last), h_k, h_v, wave, lane);
+        decode_compute<D, OUT_BF16>(B, state, out, u, l2norm, scale, wave, lane);
+        u += stride;
+        if (u > last) break;
     }
 }
 
 template <int D, bool IB, bool OB>
 static hipError_t launch_decode_t(const void* q, const void* k, const void* v, const float* g,
                                   const float* beta, float* state, void* out, int units, int h_k,
-                                  int h_v, int l2norm, float scale, hipStream_t stream) {
-    hipLaunchKernelGGL((decode_step_kernel<D, IB, OB>), dim3(units), dim3(2 * D), 0, stream, q, k, v,
-                       g, beta, state, out, h_k, h_v, l2norm, scale);
+                                  int h_v, int l2norm, float scale, int grid, hipStream_t stream) {
+    hipLaunchKernelGGL((decode_step_kernel<D, IB, OB>), dim3(grid), dim3(2 * D), 0, stream, q, k, v,
+                       g, beta, state, out, units, h_k, h_v, l2norm, scale);
     return hipGetLastError();
 }
 
 hipError_t launch_decode(int d, bool in_bf16, bool out_bf16, const void* q, const void* k,
                          const void* v, const float* g, const float* beta, float* state, void* out,
-                         int units, int h_k, int h_v, int l2norm, float scale, hipStream_t stream) {
+                         int units, int h_k, int h_v, int l2norm, float scale, int grid,
+                         hipStream_t stream) {
+    if (grid < 1 || grid > units) grid = units;
 #define GDN_DEC(D, IB, OB)                                                                        \
     if (d == D && in_bf16 == IB && out_bf16 == OB)                                                \
         return launch_decode_t<D, IB, OB>(q, k, v, g, beta, state, out, units, h_k, h_v, l2norm, \
-                                          scale, stream);
+                                          scale, grid, stream);
     GDN_DEC(128, true, true) GDN_DEC(128, true, false) GDN_DEC(128, false, true)
     GDN_DEC(128, false, false) GDN_DEC(64, true, true) GDN_DEC(64, true, false)
     GDN_DEC(64, false, true) GDN_DEC(64, false, false)
