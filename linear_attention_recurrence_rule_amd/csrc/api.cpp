@@ -21,7 +21,7 @@ hipError_t launch_plan(const int32_t* cu, int N, int T, int max_slots, void* inf
                        hipStream_t stream);
 hipError_t launch_prep(int d, bool in_bf16, const void* q, const void* k, const void* v,
                        const float* g, const float* beta, const void* info, const int32_t* slot_seq,
-                       int slots, int T, int h_k, int h_v, int l2norm, float scale, void* recs,
+                       int slots, int T, int h_k, int h_v, int l2norm, float scale, void* recs, int grid,
                        hipStream_t stream);
 hipError_t launch_scan(int d, bool in_bf16, bool out_bf16, const void* recs, const void* info,
                        const float* s_in, float* s_out, void* out, void* sink, int units, int T, int h_v,
@@ -142,17 +142,28 @@ gdn_status check_overlaps(const Span* s, int count, const void* allow_a, const v
     return GDN_OK;
 }
 
-// Decode workgroups: a few per compute unit, each walking several (sequence,
-// v-head) units so that one unit's loads overlap the previous unit's work.
-int decode_grid(int units) {
+int cu_count() {
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess) {
         int v = 0;
         if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
     }
-    int per_cu = 2;
-    if (const char* e = getenv("GDN_DECODE_WG_PER_CU")) per_cu = atoi(e);
-    const int grid = cus * (per_cu > 0 ? per_cu : 2);
+    return cus;
+}
+
+int env_int(const char* name, int dflt) {
+    const char* e = getenv(name);
+    const int v = e ? atoi(e) : 0;
+    return v > 0 ? v : dflt;
+}
+
+// Persistent chunk_prep: one workgroup per compute unit (its LDS use allows one).
+int prep_per_cu() { return env_int("GDN_PREP_WG_PER_CU", 1); }
+
+// Decode workgroups: a few per compute unit, each walking several (sequence,
+// v-head) units so that one unit's loads overlap the previous unit's work.
+int decode_grid(int units) {
+    const int grid = cu_count() * env_int("GDN_DECODE_WG_PER_CU", 2);
     return grid < units ? grid : units;
 }
 
@@ -240,9 +251,9 @@ gdn_status prefill_call(Phase phase, const gdn_desc* desc, const void* q, const 
             e = gdn::launch_plan(cu_seqlens, N, (int)T, (int)ws.slots, info, slot_seq, s);
             if (e != hipSuccess) return fail(GDN_ERR_HIP, "plan launch: %s", hipGetErrorString(e));
         }
-        if (ws.slots > 0) {
+        if (ws.slots > 0 && T > 0) {  // chunk_prep clamps token indices into [0, T)
             e = gdn::launch_prep(d, in_bf16, q, k, v, g, beta, info, slot_seq, (int)ws.slots, (int)T, hk, hv,
-                                 desc->qk_l2norm, desc->scale, wsb + ws.rec_off, s);
+                                 desc->qk_l2norm, desc->scale, wsb + ws.rec_off, cu_count() * prep_per_cu(), s);
             if (e != hipSuccess) return fail(GDN_ERR_HIP, "chunk_prep launch: %s", hipGetErrorString(e));
         }
     }

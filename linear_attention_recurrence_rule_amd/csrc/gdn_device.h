@@ -78,6 +78,13 @@ __device__ __forceinline__ void frag_set(Frag<float>& f, int e, float x) {
     if (e < 4) f.lo[e] = x; else f.hi[e - 4] = x;
 }
 
+__device__ __forceinline__ void frag_set_raw(Frag<_Float16>& f, int e, _Float16 x) { f.v[e] = x; }
+__device__ __forceinline__ void frag_set_raw(Frag<float>& f, int e, float x) {
+    if (e < 4) f.lo[e] = x; else f.hi[e - 4] = x;
+}
+__device__ __forceinline__ float frag_get(const Frag<_Float16>& f, int e) { return (float)f.v[e]; }
+__device__ __forceinline__ float frag_get(const Frag<float>& f, int e) { return e < 4 ? f.lo[e] : f.hi[e - 4]; }
+
 __device__ __forceinline__ void mma(f4_t& acc, const Frag<_Float16>& a, const Frag<_Float16>& b) {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.v, b.v, acc, 0, 0, 0);
 }
@@ -109,6 +116,20 @@ __device__ __forceinline__ Frag<OP> frag_rowmajor(const OP* M, int ld, int rb, i
         f.lo = *reinterpret_cast<const f4_t*>(p);
         f.hi = *reinterpret_cast<const f4_t*>(p + 16);
     }
+    return f;
+}
+
+// Column fragment of a row-major matrix M: the contraction runs down the rows
+// 32*kb + (4q + e) for e < 4 and 32*kb + 16 + 4q + (e - 4) for e >= 4, at
+// column 16*cb + (lane % 16).  It serves as a B fragment of M, or as an A
+// fragment of M^T.
+template <typename OP>
+__device__ __forceinline__ Frag<OP> frag_colmajor(const OP* M, int ld, int cb, int kb, int lane) {
+    const int i = lane & 15, q = lane >> 4;
+    const OP* p = M + (size_t)(32 * kb + 4 * q) * ld + 16 * cb + i;
+    Frag<OP> f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) frag_set_raw(f, e, p[(size_t)((e & 3) + 16 * (e >> 2)) * ld]);
     return f;
 }
 

@@ -109,89 +109,166 @@ struct Rec {
 template <int D, typename OP>
 constexpr int ldsk() { return D + 16 / (int)sizeof(OP); }  // row stride of [token][d] tiles
 template <typename OP>
-constexpr int ldt() { return CHUNK + 16 / (int)sizeof(OP); }
-constexpr int LDF = CHUNK + 4;  // fp32 64x64 tiles
+constexpr int ldt() { return CHUNK + 16 / (int)sizeof(OP); }  // row stride of [token][token] tiles
+constexpr int LDF = CHUNK + 4;                                  // fp32 64x64 tiles
 
-// LDS plan of chunk_prep.  Region r0 holds, by phase: the scaled raw keys
-// [token][d] (Gram), then X = (I+A)^{-1} in fp32 (solve), then -W^T [d][token].
+// LDS of chunk_prep.  q/k/v are kept row-major ([token][d]).  Operands that
+// contract over tokens are read from them as column fragments, so nothing is
+// ever written transposed.  Region r0 holds A during the solve and -W after it.
 template <int D, typename OP>
 struct PrepLds {
     static constexpr int LK = ldsk<D, OP>(), LT = ldt<OP>();
+    OP k[CHUNK * LK];  // keys scaled per token by a power of two (exact)
+    OP q[CHUNK * LK];  // queries, likewise
+    OP v[CHUNK * LK];  // values
     union R0 {
-        OP k[CHUNK * LK];
-        float x[CHUNK * LDF];
-        OP wt[D * LT];
+        float a[CHUNK * LDF];  // A = diag(beta) strict_lower(D o K K^T)
+        OP w[CHUNK * LK];      // -W [token][d]
     } r0;
-    float a[CHUNK * LDF];  // A (fp32, strictly lower)
-    OP kt[D * LT];         // scaled raw keys transposed [d][token]
-    OP qs[CHUNK * LK];     // scaled raw queries [token][d]
-    OP vt[D * LT];         // values transposed [d][token]
-    OP t[CHUNK * LT];      // T = (I+A)^{-1} diag(beta)
-    OP p[CHUNK * LT];      // P
-    float G[CHUNK], gam[CHUNK], ck[CHUNK], cq[CHUNK], bt[CHUNK];
+    float x[CHUNK * LDF];  // X = (I + A)^{-1}
+    OP t[CHUNK * LT];      // T = X diag(beta)
+    OP p[CHUNK * LT];      // P = lower_incl(D o Q K^T)
+    float G[CHUNK], ck[CHUNK], cq[CHUNK], bt[CHUNK], gck[CHUNK], gcq[CHUNK];
 };
 
 template <int D, typename OP>
 constexpr size_t prep_lds_bytes() { return sizeof(PrepLds<D, OP>); }
 
-// Per-token power-of-two scaling and norm factor for one (token, head) vector.
-// Returns the scaled elements (exact) and c such that the effective vector is
-// c * scaled.
+// Norm factor c of one (token, head) vector whose elements were scaled by
+// 2^-e (exactly): the effective vector is c * scaled.
 __device__ __forceinline__ float norm_factor(float ss_scaled, int e, int l2norm, float mul) {
     if (!l2norm) return ldexpf(mul, e);
     double den = ldexp((double)ss_scaled, 2 * e) + 1e-6;
     return (float)(ldexp((double)mul, e) / sqrt(den));
 }
 
-template <int D, typename OP, bool IN_BF16>
-__global__ __launch_bounds__(256) void chunk_prep_kernel(
-    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
-    const float* __restrict__ g, const float* __restrict__ beta, const SeqInfo* __restrict__ info,
-    const int32_t* __restrict__ slot_seq, int T, int h_k, int h_v, int l2norm, float scale,
-    char* __restrict__ recs) {
-    using R = Rec<D, OP>;
-    extern __shared__ __align__(16) char smem_raw[];
-    PrepLds<D, OP>& L = *reinterpret_cast<PrepLds<D, OP>*>(smem_raw);
-    constexpr int LK = PrepLds<D, OP>::LK, LT = PrepLds<D, OP>::LT;
-
-    const int slot = blockIdx.x, h = blockIdx.y;
+// Raw inputs of one (block slot, v-head) item, held in registers so the next
+// item's loads overlap the current item's work.  Thread tid covers the 8-element
+// pieces tid, tid + 256, ... of the block's [token][d] tiles; the PER_TOK lanes of
+// a token are adjacent.
+template <int D, bool IN_BF16>
+struct PrepRaw {
+    static constexpr int PER_TOK = D / 8, NIT = CHUNK * PER_TOK / 256, W16 = IN_BF16 ? 1 : 2;
+    uint4 q[NIT][W16], k[NIT][W16], v[NIT][W16];
+    float g, b;
     int tok0, nt;
+};
+
+template <int D, bool IN_BF16>
+__device__ __forceinline__ void prep_load(PrepRaw<D, IN_BF16>& R, int item, const void* q, const void* k,
+                                          const void* v, const float* g, const float* beta,
+                                          const SeqInfo* info, const int32_t* slot_seq, int T, int h_k,
+                                          int h_v, int tid) {
+    using PR = PrepRaw<D, IN_BF16>;
+    const int slot = item / h_v, h = item - slot * h_v, hk = h / (h_v / h_k);
+    int tok0 = 0, nt = 0;
     if (slot_seq) {
         const int n = slot_seq[slot];
-        if (n < 0) return;
-        const SeqInfo si = info[n];
-        const int j = slot - si.slot_base;
-        tok0 = si.begin + j * CHUNK;
-        nt = min(CHUNK, si.len - j * CHUNK);
+        if (n >= 0) {
+            const SeqInfo si = info[n];
+            const int j = slot - si.slot_base;
+            tok0 = si.begin + j * CHUNK;
+            nt = min(CHUNK, si.len - j * CHUNK);
+        }
     } else {
         tok0 = slot * CHUNK;
         nt = min(CHUNK, T - tok0);
     }
-    const int hk = h / (h_v / h_k);
-    const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
-    char* rec = recs + ((size_t)slot * h_v + h) * R::BYTES;
-
-    // ---- 1. load q, k, v; per-token scaling; transposed copies --------------------------
-    constexpr int PER_TOK = D / 8;           // 8-element pieces per token row
-    constexpr int ITEMS = CHUNK * PER_TOK;   // pieces per chunk
-    for (int it = tid; it < ITEMS; it += 256) {
-        const int t = it / PER_TOK, pc = it % PER_TOK;
-        float kx[8], qx[8], vx[8];
-        const bool live = t < nt;
-        if (live) {
-            const size_t qk_off = ((size_t)(tok0 + t) * h_k + hk) * D + 8 * pc;
-            load8<IN_BF16>(k, qk_off, kx);
-            load8<IN_BF16>(q, qk_off, qx);
-            load8<IN_BF16>(v, ((size_t)(tok0 + t) * h_v + h) * D + 8 * pc, vx);
-        } else {
+    R.tok0 = tok0;
+    R.nt = nt;
+    // every load is issued (token indices clamped into [0, T)); data past nt is zeroed on use
+    constexpr int ES = IN_BF16 ? 2 : 4;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) kx[e] = qx[e] = vx[e] = 0.f;
+    for (int it = 0; it < PR::NIT; ++it) {
+        const int idx = tid + 256 * it, t = idx / PR::PER_TOK, pc = idx % PR::PER_TOK;
+        const size_t tok = (size_t)min(tok0 + t, T - 1);
+        const char* pq = reinterpret_cast<const char*>(q) + ((tok * h_k + hk) * D + 8 * pc) * ES;
+        const char* pk = reinterpret_cast<const char*>(k) + ((tok * h_k + hk) * D + 8 * pc) * ES;
+        const char* pv = reinterpret_cast<const char*>(v) + ((tok * h_v + h) * D + 8 * pc) * ES;
+#pragma unroll
+        for (int w = 0; w < PR::W16; ++w) {
+            R.q[it][w] = reinterpret_cast<const uint4*>(pq)[w];
+            R.k[it][w] = reinterpret_cast<const uint4*>(pk)[w];
+            R.v[it][w] = reinterpret_cast<const uint4*>(pv)[w];
         }
+    }
+    const size_t tg = (size_t)min(tok0 + (tid & 63), T - 1) * h_v + h;
+    R.g = g[tg];
+    R.b = beta[tg];
+}
+
+template <bool IN_BF16>
+__device__ __forceinline__ void unpack8(const uint4* src, float x[8]) {
+    if constexpr (IN_BF16) {
+        const uint32_t w[4] = {src[0].x, src[0].y, src[0].z, src[0].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = __uint_as_float(w[i] << 16);
+            x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            x[4 * i + 0] = __uint_as_float(src[i].x); x[4 * i + 1] = __uint_as_float(src[i].y);
+            x[4 * i + 2] = __uint_as_float(src[i].z); x[4 * i + 3] = __uint_as_float(src[i].w);
+        }
+    }
+}
+
+template <typename OP>
+__device__ __forceinline__ void store8(OP* dst, const float x[8]) {
+    if constexpr (sizeof(OP) == 2) {
+        h8_t h;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = (_Float16)x[e];
+        *reinterpret_cast<h8_t*>(dst) = h;
+    } else {
+        *reinterpret_cast<f4_t*>(dst) = f4_t{x[0], x[1], x[2], x[3]};
+        *reinterpret_cast<f4_t*>(dst + 4) = f4_t{x[4], x[5], x[6], x[7]};
+    }
+}
+
+template <typename OP>
+__device__ __forceinline__ void store4(OP* dst, const f4_t& x) {
+    if constexpr (sizeof(OP) == 2) {
+        typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+        *reinterpret_cast<h4_t*>(dst) = h4_t{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
+    } else {
+        *reinterpret_cast<f4_t*>(dst) = x;
+    }
+}
+
+// One (block slot, v-head) item: everything of the block form that does not
+// depend on the carried state.
+template <int D, typename OP, bool IN_BF16>
+__device__ __forceinline__ void prep_item(PrepLds<D, OP>& L, const PrepRaw<D, IN_BF16>& R, char* rec, int l2norm,
+                                          float scale, int tid) {
+    using PR = PrepRaw<D, IN_BF16>;
+    using RC = Rec<D, OP>;
+    constexpr int LK = PrepLds<D, OP>::LK, LT = PrepLds<D, OP>::LT;
+    const int wave = tid / WAVE, lane = tid % WAVE;
+    const int li = lane & 15, lq = lane >> 4;
+    const int nt = R.nt;
+    __syncthreads();  // the previous item is done with LDS
+
+    // ---- 1. per-token power-of-two scaling and norms; q, k, v to LDS (row-major) ----------
+#pragma unroll
+    for (int it = 0; it < PR::NIT; ++it) {
+        const int idx = tid + 256 * it, t = idx / PR::PER_TOK, pc = idx % PR::PER_TOK;
+        const bool live = t < nt;
+        float kx[8], qx[8], vx[8];
+        unpack8<IN_BF16>(R.k[it], kx);
+        unpack8<IN_BF16>(R.q[it], qx);
+        unpack8<IN_BF16>(R.v[it], vx);
         float mk = 0.f, mq = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) { mk = fmaxf(mk, fabsf(kx[e])); mq = fmaxf(mq, fabsf(qx[e])); }
+        for (int e = 0; e < 8; ++e) {
+            if (!live) { kx[e] = 0.f; qx[e] = 0.f; vx[e] = 0.f; }
+            mk = fmaxf(mk, fabsf(kx[e]));
+            mq = fmaxf(mq, fabsf(qx[e]));
+        }
 #pragma unroll
-        for (int m = PER_TOK / 2; m >= 1; m >>= 1) {   // the PER_TOK lanes of a token are adjacent
+        for (int m = PR::PER_TOK / 2; m >= 1; m >>= 1) {
             mk = fmaxf(mk, shfl_xor(mk, m));
             mq = fmaxf(mq, shfl_xor(mq, m));
         }
@@ -201,182 +278,188 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
         float ssk = 0.f, ssq = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            kx[e] = ldexpf(kx[e], -ek);
-            qx[e] = ldexpf(qx[e], -eq);
-            const OP kr = (OP)kx[e], qr = (OP)qx[e];
-            ssk += (float)kr * (float)kr;
-            ssq += (float)qr * (float)qr;
-            L.r0.k[t * LK + 8 * pc + e] = kr;
-            L.qs[t * LK + 8 * pc + e] = qr;
-            L.kt[(8 * pc + e) * LT + t] = kr;
-            L.vt[(8 * pc + e) * LT + t] = (OP)vx[e];
+            kx[e] = (float)(OP)ldexpf(kx[e], -ek);
+            qx[e] = (float)(OP)ldexpf(qx[e], -eq);
+            ssk += kx[e] * kx[e];
+            ssq += qx[e] * qx[e];
         }
 #pragma unroll
-        for (int m = PER_TOK / 2; m >= 1; m >>= 1) {
+        for (int m = PR::PER_TOK / 2; m >= 1; m >>= 1) {
             ssk += shfl_xor(ssk, m);
             ssq += shfl_xor(ssq, m);
         }
+        store8<OP>(L.k + t * LK + 8 * pc, kx);
+        store8<OP>(L.q + t * LK + 8 * pc, qx);
+        store8<OP>(L.v + t * LK + 8 * pc, vx);
         if (pc == 0) {
             L.ck[t] = live ? norm_factor(ssk, ek, l2norm, 1.0f) : 0.f;
             L.cq[t] = live ? norm_factor(ssq, eq, l2norm, scale) : 0.f;
         }
     }
+    float gam = 0.f;
     if (wave == 0) {
         const int t = lane;
         const bool live = t < nt;
-        float gx = live ? g[(size_t)(tok0 + t) * h_v + h] : 0.f;
-        L.bt[t] = live ? beta[(size_t)(tok0 + t) * h_v + h] : 0.f;
-        // inclusive prefix sum over the 64 tokens
+        float gx = live ? R.g : 0.f;
 #pragma unroll
         for (int off = 1; off < WAVE; off <<= 1) {
             const float o = __shfl_up(gx, off, WAVE);
             if (t >= off) gx += o;
         }
         L.G[t] = gx;
-        L.gam[t] = expf(gx);
+        L.bt[t] = live ? R.b : 0.f;
+        gam = expf(gx);
+    }
+    __syncthreads();
+    if (wave == 0) {
+        L.gck[lane] = gam * L.ck[lane];
+        L.gcq[lane] = gam * L.cq[lane];
+    }
+
+    // ---- 2. decay-masked Gram products: A (fp32) and P (lower 4x4 tiles, spread over waves) ----
+    for (int tl = wave; tl < 10; tl += 4) {
+        const int mb = (tl >= 6) ? 3 : (tl >= 3) ? 2 : (tl >= 1) ? 1 : 0;
+        const int nb = tl - mb * (mb + 1) / 2;
+        f4_t ak = {0, 0, 0, 0}, aq = {0, 0, 0, 0};
+#pragma unroll
+        for (int kb = 0; kb < D / 32; ++kb) {
+            const Frag<OP> fk = frag_rowmajor<OP>(L.k, LK, nb, kb, lane);
+            mma(ak, frag_rowmajor<OP>(L.k, LK, mb, kb, lane), fk);
+            mma(aq, frag_rowmajor<OP>(L.q, LK, mb, kb, lane), fk);
+        }
+        const int j = 16 * nb + li, i0 = 16 * mb + 4 * lq;
+        const float Gj = L.G[j], ckj = L.ck[j];
+        const f4_t Gi = *reinterpret_cast<const f4_t*>(&L.G[i0]);
+        const f4_t cki = *reinterpret_cast<const f4_t*>(&L.ck[i0]);
+        const f4_t cqi = *reinterpret_cast<const f4_t*>(&L.cq[i0]);
+        const f4_t bti = *reinterpret_cast<const f4_t*>(&L.bt[i0]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = i0 + r;
+            const float dec = (j <= i) ? expf(fminf(Gi[r] - Gj, 0.f)) : 0.f;
+            L.r0.a[i * LDF + j] = (j < i) ? bti[r] * dec * ak[r] * cki[r] * ckj : 0.f;
+            L.p[i * LT + j] = (OP)(dec * aq[r] * cqi[r] * ckj);
+        }
+    }
+    for (int tl = wave; tl < 6; tl += 4) {  // strictly-upper tiles of P are zero
+        const int nb = (tl >= 3) ? 3 : (tl >= 1) ? 2 : 1;
+        const int mb = tl - (nb - 1) * nb / 2;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) L.p[(16 * mb + 4 * lq + r) * LT + 16 * nb + li] = (OP)0.f;
     }
     __syncthreads();
 
-    // ---- 2. Gram products: A (fp32) and P --------------------------------------------------
+    // ---- 3. X = (I + A)^{-1}: substitution in the 16x16 diagonal blocks, then
+    //         X_ij = -X_ii sum_{m=j}^{i-1} A_im X_mj by block distance (fp32 matrix cores) -----
     {
-        const int mb = wave;  // token rows 16mb..16mb+15
-        for (int nb = 0; nb <= mb; ++nb) {
-            f4_t ak = {0, 0, 0, 0}, aq = {0, 0, 0, 0};
-#pragma unroll
-            for (int kb = 0; kb < D / 32; ++kb) {
-                const Frag<OP> fk = frag_rowmajor<OP>(L.r0.k, LK, nb, kb, lane);
-                mma(ak, frag_rowmajor<OP>(L.r0.k, LK, mb, kb, lane), fk);
-                mma(aq, frag_rowmajor<OP>(L.qs, LK, mb, kb, lane), fk);
-            }
-            const int j = 16 * nb + (lane & 15);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * mb + 4 * (lane >> 4) + r;
-                const float dec = (j <= i) ? expf(L.G[i] - L.G[j]) : 0.f;
-                const float kk = ak[r] * L.ck[i] * L.ck[j];
-                L.a[i * LDF + j] = (j < i) ? L.bt[i] * dec * kk : 0.f;
-                L.p[i * LT + j] = (OP)((j <= i) ? dec * aq[r] * L.cq[i] * L.ck[j] : 0.f);
-            }
-        }
-        // zero the strictly-upper blocks of P (A's upper blocks are never read)
-        for (int nb = mb + 1; nb < 4; ++nb) {
-            const int j = 16 * nb + (lane & 15);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) L.p[(16 * mb + 4 * (lane >> 4) + r) * LT + j] = (OP)0.f;
-        }
-    }
-    __syncthreads();
-
-    // ---- 3. X = (I + A)^{-1}, block forward substitution on 16x16 blocks (fp32) -----------
-    float* X = L.r0.x;  // the raw-key tile is no longer needed
-    {
-        // diagonal blocks: wave w inverts block w; lane c < 16 owns column c
-        const int b = wave;
+        const int bb = wave;
         if (lane < 16) {
             float x[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
+                const float* arow = &L.r0.a[(16 * bb + i) * LDF + 16 * bb];
                 float acc = (i == lane) ? 1.f : 0.f;
 #pragma unroll
-                for (int j = 0; j < i; ++j) acc -= L.a[(16 * b + i) * LDF + 16 * b + j] * x[j];
+                for (int j = 0; j < i; ++j) acc -= arow[j] * x[j];
                 x[i] = acc;
             }
 #pragma unroll
-            for (int i = 0; i < 16; ++i) X[(16 * b + i) * LDF + 16 * b + lane] = x[i];
+            for (int i = 0; i < 16; ++i) L.x[(16 * bb + i) * LDF + 16 * bb + lane] = x[i];
         }
-        // upper blocks of X are zero
-        for (int idx = lane; idx < 16 * 16; idx += WAVE) {
+        for (int idx = lane; idx < 256; idx += WAVE) {
             const int i = idx / 16, jj = idx % 16;
-            for (int cb = b + 1; cb < 4; ++cb) X[(16 * b + i) * LDF + 16 * cb + jj] = 0.f;
+            for (int cb = bb + 1; cb < 4; ++cb) L.x[(16 * bb + i) * LDF + 16 * cb + jj] = 0.f;
         }
     }
     __syncthreads();
-    // off-diagonal blocks by distance: X_ij = -X_ii * sum_{m=j}^{i-1} A_im X_mj
     for (int dist = 1; dist < 4; ++dist) {
         const int i = wave + dist, j = wave;
         if (i < 4) {
             f4_t acc = {0, 0, 0, 0};
             for (int m = j; m < i; ++m) {
-                // acc += A_im (16x16) * X_mj (16x16), fp32 matrix cores, contraction of 16
-                const int li = lane & 15, q = lane >> 4;
+                const f4_t av = *reinterpret_cast<const f4_t*>(&L.r0.a[(16 * i + li) * LDF + 16 * m + 4 * lq]);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float av = L.a[(16 * i + li) * LDF + 16 * m + 4 * q + e];
-                    const float bv = X[(16 * m + 4 * q + e) * LDF + 16 * j + li];
-                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
-                }
+                for (int e = 0; e < 4; ++e)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], L.x[(16 * m + 4 * lq + e) * LDF + 16 * j + li], acc,
+                                                              0, 0, 0);
             }
-            // X_ij = -X_ii * acc ; acc (accumulator layout) is the B operand directly
+            const f4_t xv = *reinterpret_cast<const f4_t*>(&L.x[(16 * i + li) * LDF + 16 * i + 4 * lq]);
             f4_t res = {0, 0, 0, 0};
-            const int li = lane & 15, q = lane >> 4;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float av = -X[(16 * i + li) * LDF + 16 * i + 4 * q + e];
-                res = __builtin_amdgcn_mfma_f32_16x16x4f32(av, acc[e], res, 0, 0, 0);
-            }
+            for (int e = 0; e < 4; ++e) res = __builtin_amdgcn_mfma_f32_16x16x4f32(-xv[e], acc[e], res, 0, 0, 0);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) X[(16 * i + 4 * q + r) * LDF + 16 * j + li] = res[r];
+            for (int r = 0; r < 4; ++r) L.x[(16 * i + 4 * lq + r) * LDF + 16 * j + li] = res[r];
         }
         __syncthreads();
     }
-    // T = X diag(beta)
-    for (int idx = tid; idx < CHUNK * CHUNK; idx += 256) {
-        const int i = idx / CHUNK, j = idx % CHUNK;
-        L.t[i * LT + j] = (OP)(X[i * LDF + j] * L.bt[j]);
+    for (int idx = tid; idx < CHUNK * CHUNK / 4; idx += 256) {  // T = X diag(beta)
+        const int i = idx / (CHUNK / 4), j4 = 4 * (idx % (CHUNK / 4));
+        const f4_t xv = *reinterpret_cast<const f4_t*>(&L.x[i * LDF + j4]);
+        const f4_t bv = *reinterpret_cast<const f4_t*>(&L.bt[j4]);
+        store4<OP>(L.t + i * LT + j4, xv * bv);
     }
     __syncthreads();
 
-    // ---- 4. W^T = (diag(gam c) K)^T T^T : D x C, stored as -W fragments and -W^T in LDS ----
-    OP* WT = L.r0.wt;  // [d][token], stride LT; X is no longer needed
-    OP* wrec = reinterpret_cast<OP*>(rec + R::W);
-    OP* qrec = reinterpret_cast<OP*>(rec + R::Q);
-    constexpr int UNITS_PER_WAVE = D / 32;  // (d-block pair, token block) units
-    for (int uu = 0; uu < UNITS_PER_WAVE; ++uu) {
-        const int unit = wave * UNITS_PER_WAVE + uu;
-        const int kb = unit / 4, tb = unit % 4;  // d-blocks 2kb, 2kb+1; token block tb
-        f4_t acc[2];
+    // ---- 4. K^T fragments for the scan, and W^T = (diag(gam c) K)^T T^T -------------------
+    // Units (kb, tb): d-blocks 2kb, 2kb+1 and token block tb; a wave's units share kb
+    // for d = 128.  Its accumulators are the scan's -W fragments directly.
+    OP* wrec = reinterpret_cast<OP*>(rec + RC::W);
+    OP* qrec = reinterpret_cast<OP*>(rec + RC::Q);
+    OP* krec = reinterpret_cast<OP*>(rec + RC::K);
+    constexpr int UPW = D / 32;  // units per wave
+    {
+        int cur_kb = -1;
+        Frag<OP> aw[2][2];
+        for (int uu = 0; uu < UPW; ++uu) {
+            const int unit = wave * UPW + uu, kb = unit / 4, tb = unit % 4;
+            if (kb != cur_kb) {
+                cur_kb = kb;
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            acc[s] = f4_t{0, 0, 0, 0};
-            const int mb = 2 * kb + s;
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const int mb = 2 * kb + s2;
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                // A: rows d = 16mb + i of (diag(gam c) K)^T, columns tokens 32kk + ...
-                Frag<OP> fa;
-                const int i = lane & 15, q = lane >> 4;
+                    for (int kk = 0; kk < 2; ++kk) {
+                        Frag<OP> f = frag_colmajor<OP>(L.k, LK, mb, kk, lane);
+                        // the scan's K^T fragments: each d-block written by one wave
+                        if (mb / (D / 64) == wave) frag_store<OP>(krec, mb * 2 + kk, lane, f);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int t = 32 * kk + 4 * q + (e & 3) + 16 * (e >> 2);
-                    frag_set(fa, e, (float)L.kt[(16 * mb + i) * LT + t] * L.gam[t] * L.ck[t]);
+                        for (int e = 0; e < 8; ++e)
+                            frag_set(f, e, frag_get(f, e) * L.gck[32 * kk + 4 * lq + (e & 3) + 16 * (e >> 2)]);
+                        aw[s2][kk] = f;
+                    }
                 }
-                mma(acc[s], fa, frag_rowmajor<OP>(L.t, LT, tb, kk, lane));
             }
+            f4_t acc[2];
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                acc[s2] = f4_t{0, 0, 0, 0};
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) mma(acc[s2], aw[s2][kk], frag_rowmajor<OP>(L.t, LT, tb, kk, lane));
+            }
+            // lane (j, q): acc[s2][r] = W[token 16tb + j][d 16(2kb + s2) + 4q + r]
+            Frag<OP> fw;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { frag_set(fw, e, -acc[0][e]); frag_set(fw, e + 4, -acc[1][e]); }
+            frag_store<OP>(wrec, tb * (D / 32) + kb, lane, fw);
+            const int tok = 16 * tb + li;
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) store4<OP>(L.r0.w + tok * LK + 16 * (2 * kb + s2) + 4 * lq, -acc[s2]);
         }
-        // acc[s] lane (j=token, q): W^T[16(2kb+s) + 4q + r][16tb + j] = W[token][d]
-        Frag<OP> fw;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) { frag_set(fw, e, -acc[0][e]); frag_set(fw, e + 4, -acc[1][e]); }
-        frag_store<OP>(wrec, tb * (D / 32) + kb, lane, fw);
-        const int jt = 16 * tb + (lane & 15), q = lane >> 4;
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) WT[(16 * (2 * kb + s) + 4 * q + r) * LT + jt] = (OP)(-acc[s][r]);
     }
 
-    // ---- 5. Ut = T V and Ot = P Ut : C x D, fp32 accumulator tiles --------------------------
-    float* urec = reinterpret_cast<float*>(rec + R::U);
-    float* orec = reinterpret_cast<float*>(rec + R::O);
+    // ---- 5. Ut = T V and Ot = P Ut (fp32 accumulator tiles) --------------------------------
+    float* urec = reinterpret_cast<float*>(rec + RC::U);
+    float* orec = reinterpret_cast<float*>(rec + RC::O);
     for (int cbi = 0; cbi < D / 64; ++cbi) {
-        const int nb = wave * (D / 64) + cbi;  // d_v block
+        const int nb = wave * (D / 64) + cbi;
+        const Frag<OP> fv0 = frag_colmajor<OP>(L.v, LK, nb, 0, lane);
+        const Frag<OP> fv1 = frag_colmajor<OP>(L.v, LK, nb, 1, lane);
         f4_t ut[4];
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
             ut[mb] = f4_t{0, 0, 0, 0};
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-                mma(ut[mb], frag_rowmajor<OP>(L.t, LT, mb, kk, lane),
-                    frag_rowmajor<OP>(L.vt, LT, nb, kk, lane));
+            mma(ut[mb], frag_rowmajor<OP>(L.t, LT, mb, 0, lane), fv0);
+            mma(ut[mb], frag_rowmajor<OP>(L.t, LT, mb, 1, lane), fv1);
             *reinterpret_cast<f4_t*>(urec + ((size_t)(mb * (D / 16) + nb) * WAVE + lane) * 4) = ut[mb];
         }
         const Frag<OP> fu0 = frag_from_acc<OP>(ut[0], ut[1]);
@@ -389,40 +472,73 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
             *reinterpret_cast<f4_t*>(orec + ((size_t)(mb * (D / 16) + nb) * WAVE + lane) * 4) = ot;
         }
     }
-    __syncthreads();  // -W^T complete in LDS
+    __syncthreads();  // -W complete in LDS
 
-    // ---- 6. Qt^T = (diag(gam cq) Q)^T + (-W^T) P^T : D x C ----------------------------------
-    for (int uu = 0; uu < UNITS_PER_WAVE; ++uu) {
-        const int unit = wave * UNITS_PER_WAVE + uu;
-        const int kb = unit / 4, tb = unit % 4;
-        f4_t acc[2];
-        const int jt = 16 * tb + (lane & 15), q = lane >> 4;
+    // ---- 6. Qt^T = (diag(gam cq) Q)^T + (-W)^T P^T : the scan's Qt fragments --------------
+    {
+        int cur_kb = -1;
+        Frag<OP> aw[2][2];
+        for (int uu = 0; uu < UPW; ++uu) {
+            const int unit = wave * UPW + uu, kb = unit / 4, tb = unit % 4;
+            if (kb != cur_kb) {
+                cur_kb = kb;
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int mb = 2 * kb + s;
+                for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                acc[s][r] = (float)L.qs[jt * LK + 16 * mb + 4 * q + r] * L.gam[jt] * L.cq[jt];
+                    for (int kk = 0; kk < 2; ++kk) aw[s2][kk] = frag_colmajor<OP>(L.r0.w, LK, 2 * kb + s2, kk, lane);
+            }
+            const int tok = 16 * tb + li;
+            const float gq = L.gcq[tok];
+            f4_t acc[2];
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-                mma(acc[s], frag_rowmajor<OP>(WT, LT, mb, kk, lane), frag_rowmajor<OP>(L.p, LT, tb, kk, lane));
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const OP* qr = L.q + tok * LK + 16 * (2 * kb + s2) + 4 * lq;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[s2][r] = (float)qr[r] * gq;
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) mma(acc[s2], aw[s2][kk], frag_rowmajor<OP>(L.p, LT, tb, kk, lane));
+            }
+            Frag<OP> fq;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { frag_set(fq, e, acc[0][e]); frag_set(fq, e + 4, acc[1][e]); }
+            frag_store<OP>(qrec, tb * (D / 32) + kb, lane, fq);
         }
-        Frag<OP> fq;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) { frag_set(fq, e, acc[0][e]); frag_set(fq, e + 4, acc[1][e]); }
-        frag_store<OP>(qrec, tb * (D / 32) + kb, lane, fq);
     }
 
-    // ---- 7. K^T fragments (A operand of the state update), s_t, gamma_n ---------------------
-    OP* krec = reinterpret_cast<OP*>(rec + R::K);
-    for (int f = wave; f < (D / 16) * 2; f += 4) {
-        const int mb = f / 2, kk = f % 2;
-        frag_store<OP>(krec, f, lane, frag_rowmajor<OP>(L.kt, LT, mb, kk, lane));
-    }
+    // ---- 7. s_t = exp(G_n - G_t) c_t and gamma_n -------------------------------------------
     if (tid < CHUNK) {
-        const float Gn = L.G[nt - 1];
-        reinterpret_cast<float*>(rec + R::S)[tid] = (tid < nt) ? expf(Gn - L.G[tid]) * L.ck[tid] : 0.f;
-        if (tid == 0) reinterpret_cast<float*>(rec + R::M)[0] = expf(Gn);
+        const float Gn = L.G[max(nt - 1, 0)];
+        reinterpret_cast<float*>(rec + RC::S)[tid] = (tid < nt) ? expf(Gn - L.G[tid]) * L.ck[tid] : 0.f;
+        if (tid == 0) reinterpret_cast<float*>(rec + RC::M)[0] = expf(Gn);
+    }
+}
+
+// Persistent: workgroup b handles items b, b + gridDim.x, ... (item = slot * h_v + v-head),
+// with the next item's inputs loaded while the current one is processed.  Every
+// iteration issues the same loads (past the end it re-reads the last item).
+template <int D, typename OP, bool IN_BF16>
+__global__ __launch_bounds__(256) void chunk_prep_kernel(
+    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, const SeqInfo* __restrict__ info,
+    const int32_t* __restrict__ slot_seq, int items, int T, int h_k, int h_v, int l2norm, float scale,
+    char* __restrict__ recs) {
+    using RC = Rec<D, OP>;
+    extern __shared__ __align__(16) char smem_raw[];
+    PrepLds<D, OP>& L = *reinterpret_cast<PrepLds<D, OP>*>(smem_raw);
+    const int tid = threadIdx.x, stride = gridDim.x, last = items - 1;
+    int it = blockIdx.x;
+    if (it > last) return;
+    PrepRaw<D, IN_BF16> A, B;
+    prep_load<D, IN_BF16>(A, it, q, k, v, g, beta, info, slot_seq, T, h_k, h_v, tid);
+    for (;;) {
+        prep_load<D, IN_BF16>(B, min(it + stride, last), q, k, v, g, beta, info, slot_seq, T, h_k, h_v, tid);
+        if (A.nt > 0) prep_item<D, OP, IN_BF16>(L, A, recs + (size_t)it * RC::BYTES, l2norm, scale, tid);
+        it += stride;
+        if (it > last) break;
+        prep_load<D, IN_BF16>(A, min(it + stride, last), q, k, v, g, beta, info, slot_seq, T, h_k, h_v, tid);
+        if (B.nt > 0) prep_item<D, OP, IN_BF16>(L, B, recs + (size_t)it * RC::BYTES, l2norm, scale, tid);
+        it += stride;
+        if (it > last) break;
     }
 }
 
@@ -491,7 +607,7 @@ __device__ __forceinline__ void store_part(OP* base, int frag, int part, int lan
 template <int D, typename OP, bool OUT_BF16>
 __global__ __launch_bounds__(256) void chunk_scan_kernel(
     const char* __restrict__ recs, const SeqInfo* __restrict__ info, const float* __restrict__ state_in,
-    float* __restrict__ state_out, void* __restrict__ out, char* __restrict__ sink, int T, int h_v) {
+    float* __restrict__ state_out, void* __restrict__ out, char* __restrict__ sink, int units, int T, int h_v) {
     using R = Rec<D, OP>;
     constexpr int SLICES = D / 32;
     constexpr int DB = ScanOps<D, OP>::DB;
@@ -499,8 +615,14 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(
     __shared__ __align__(16) OP sU[2 * 2 * WAVE * 8];         // diag(s) U as B fragments (kk, row block)
     constexpr int OB = OUT_BF16 ? 2 : 4;                       // bytes per output element
     __shared__ __align__(16) char sO[4][16 * 32 * OB];         // per wave: 16 tokens x 32 outputs, row-major
-    const int slice = blockIdx.x % SLICES;
-    const int unit = blockIdx.x / SLICES;  // sequence * h_v + v-head
+    // Workgroups are dispatched round-robin over the 8 XCDs (blockIdx % 8).
+    // The SLICES workgroups of one (sequence, v-head) unit are placed on the
+    // same XCD at consecutive positions, so they read each block record from
+    // that XCD's L2 instead of from HBM.
+    const int xcd = blockIdx.x % 8, m = blockIdx.x / 8;
+    const int slice = m % SLICES;
+    const int unit = (m / SLICES) * 8 + xcd;  // sequence * h_v + v-head
+    if (unit >= units) return;
     const int n = unit / h_v, h = unit - n * h_v;
     const int tid = threadIdx.x, w = tid / WAVE, lane = tid % WAVE;
     const int j16 = lane & 15, q4 = lane >> 4;
@@ -594,20 +716,26 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(
             }
     };
 
-    // Two operand sets in flight.  Every iteration issues the same memory
-    // operations (a prefetch past the last block re-reads the last block), so
-    // the wait before each block covers exactly that block's loads.
+    // Three operand sets in flight (two blocks of look-ahead).  Every
+    // iteration issues the same memory operations (a prefetch past the last
+    // block re-reads the last block), so the loads of one block are never
+    // conditional on the data of another.
     if (nchunks > 0) {
         const int last = nchunks - 1;
-        ScanOps<D, OP> opA, opB;
+        ScanOps<D, OP> opA, opB, opC;
         load_ops<D, OP>(opA, rec_of(0), w, lane, cb0);
         load_ops<D, OP>(opB, rec_of(min(1, last)), w, lane, cb0);
-        for (int c = 0; c < nchunks; c += 2) {
+        load_ops<D, OP>(opC, rec_of(min(2, last)), w, lane, cb0);
+        for (int c = 0;; c += 3) {
             step(opA, c);
-            load_ops<D, OP>(opA, rec_of(min(c + 2, last)), w, lane, cb0);
+            load_ops<D, OP>(opA, rec_of(min(c + 3, last)), w, lane, cb0);
             if (c + 1 > last) break;
             step(opB, c + 1);
-            load_ops<D, OP>(opB, rec_of(min(c + 3, last)), w, lane, cb0);
+            load_ops<D, OP>(opB, rec_of(min(c + 4, last)), w, lane, cb0);
+            if (c + 2 > last) break;
+            step(opC, c + 2);
+            load_ops<D, OP>(opC, rec_of(min(c + 5, last)), w, lane, cb0);
+            if (c + 3 > last) break;
         }
     }
 
@@ -640,39 +768,42 @@ template <int D, typename OP, bool IB>
 static hipError_t launch_prep_t(const void* q, const void* k, const void* v, const float* g,
                                 const float* beta, const void* info, const int32_t* slot_seq,
                                 int slots, int T, int h_k, int h_v, int l2norm, float scale,
-                                char* recs, hipStream_t stream) {
+                                char* recs, int grid, hipStream_t stream) {
     constexpr size_t lds = prep_lds_bytes<D, OP>();
     static_assert(lds <= 160 * 1024, "chunk_prep LDS budget");
     auto kern = chunk_prep_kernel<D, OP, IB>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(slots, h_v), dim3(256), lds, stream, q, k, v, g, beta,
-                       reinterpret_cast<const SeqInfo*>(info), slot_seq, T, h_k, h_v, l2norm, scale,
+    const int items = slots * h_v;
+    if (grid < 1 || grid > items) grid = items;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, stream, q, k, v, g, beta,
+                       reinterpret_cast<const SeqInfo*>(info), slot_seq, items, T, h_k, h_v, l2norm, scale,
                        recs);
     return hipGetLastError();
 }
 
 hipError_t launch_prep(int d, bool in_bf16, const void* q, const void* k, const void* v,
                        const float* g, const float* beta, const void* info, const int32_t* slot_seq,
-                       int slots, int T, int h_k, int h_v, int l2norm, float scale, void* recs,
+                       int slots, int T, int h_k, int h_v, int l2norm, float scale, void* recs, int grid,
                        hipStream_t stream) {
     char* r = reinterpret_cast<char*>(recs);
     if (d == 128 && in_bf16)
-        return launch_prep_t<128, _Float16, true>(q, k, v, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, stream);
+        return launch_prep_t<128, _Float16, true>(q, k, v, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, grid, stream);
     if (d == 64 && in_bf16)
-        return launch_prep_t<64, _Float16, true>(q, k, v, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, stream);
+        return launch_prep_t<64, _Float16, true>(q, k, v, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, grid, stream);
     if (d == 64 && !in_bf16)
-        return launch_prep_t<64, float, false>(q, k, v, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, stream);
+        return launch_prep_t<64, float, false>(q, k, v, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, grid, stream);
     return hipErrorInvalidValue;
 }
 
 template <int D, typename OP, bool OB>
 static hipError_t launch_scan_t(const void* recs, const void* info, const float* s_in, float* s_out,
                                 void* out, void* sink, int units, int T, int h_v, hipStream_t stream) {
-    hipLaunchKernelGGL((chunk_scan_kernel<D, OP, OB>), dim3(units * (D / 32)), dim3(256), 0, stream,
+    const int groups = (units + 7) / 8;  // see the XCD placement in chunk_scan_kernel
+    hipLaunchKernelGGL((chunk_scan_kernel<D, OP, OB>), dim3(groups * 8 * (D / 32)), dim3(256), 0, stream,
                        reinterpret_cast<const char*>(recs), reinterpret_cast<const SeqInfo*>(info), s_in,
-                       s_out, out, reinterpret_cast<char*>(sink), T, h_v);
+                       s_out, out, reinterpret_cast<char*>(sink), units, T, h_v);
     return hipGetLastError();
 }
 
