@@ -51,6 +51,41 @@ def algorithmic_decode(N, h_v, h_k, d, io_bytes=2, out_bytes=2):
             + 2 * N * h_v * 4 + N * h_v * d * out_bytes)
 
 
+def kernel_source_digest():
+    """Digest of the HIP sources; counter figures are only reported for the
+    kernels they were measured on."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "linear_attention_recurrence_rule_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE runs
+    summarised in profiles/hbm_traffic.md (already scaled by the plain-copy
+    reference), or None when the kernels changed since those runs."""
+    import json
+    import re
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
+    if not m:
+        return None
+    data = json.loads(m.group(1))
+    if data.get("source_digest") != kernel_source_digest():
+        return None
+    k = data.get("kernels", {}).get(kernel)
+    if not k:
+        return None
+    return {"fetch_bytes": k["fetch_bytes"], "write_bytes": k["write_bytes"],
+            "total_bytes": k["fetch_bytes"] + k["write_bytes"], "source": "profiles/hbm_traffic.md"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -58,6 +93,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--decode-steps", type=int, default=512)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run plain 256 MiB device copies (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on exactly one GPU; --gpus %d is not supported "
@@ -147,7 +184,7 @@ def main():
     us_dom, f_dom = kern[dom]
     ach = f_dom / (us_dom * 1e-6) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": PEAK_FP16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / PEAK_FP16_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_FP16_TFLOPS, 4), "traffic": measured_traffic(dom),
                 "avg_launch_us": round(us_dom, 2),
                 "algorithmic_gflop_per_launch": round(f_dom / 1e9, 3)}
     prefill_info = {
@@ -197,8 +234,16 @@ def main():
                    "algorithmic_mb_per_step": dbytes / 1e6,
                    "roofline": {"bound": "hbm", "kernel": "decode_step", "achieved": round(dec_gbs, 1),
                                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
-                                "traffic": None}}
+                                "traffic": measured_traffic("decode_step")}}
     del dq, dk, dv, dg, db, state, dout
+
+    if args.calibrate_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---------------- CPU baseline (the oracle, same 4K workload) ----------------
     cpu = None

@@ -21,7 +21,7 @@ hipError_t launch_plan(const int32_t* cu, int N, int T, int max_slots, void* inf
                        hipStream_t stream);
 hipError_t launch_prep(int d, bool in_bf16, const void* q, const void* k, const void* v,
                        const float* g, const float* beta, const void* info, const int32_t* slot_seq,
-                       int slots, int T, int h_k, int h_v, int l2norm, float scale, void* recs, int grid,
+                       int slots, int T, int h_k, int h_v, int l2norm, float scale, void* recs,
                        hipStream_t stream);
 hipError_t launch_scan(int d, bool in_bf16, bool out_bf16, const void* recs, const void* info,
                        const float* s_in, float* s_out, void* out, void* sink, int units, int T, int h_v,
@@ -157,9 +157,6 @@ int env_int(const char* name, int dflt) {
     return v > 0 ? v : dflt;
 }
 
-// Persistent chunk_prep: one workgroup per compute unit (its LDS use allows one).
-int prep_per_cu() { return env_int("GDN_PREP_WG_PER_CU", 1); }
-
 // Decode workgroups: a few per compute unit, each walking several (sequence,
 // v-head) units so that one unit's loads overlap the previous unit's work.
 int decode_grid(int units) {
@@ -253,7 +250,7 @@ gdn_status prefill_call(Phase phase, const gdn_desc* desc, const void* q, const 
         }
         if (ws.slots > 0 && T > 0) {  // chunk_prep clamps token indices into [0, T)
             e = gdn::launch_prep(d, in_bf16, q, k, v, g, beta, info, slot_seq, (int)ws.slots, (int)T, hk, hv,
-                                 desc->qk_l2norm, desc->scale, wsb + ws.rec_off, cu_count() * prep_per_cu(), s);
+                                 desc->qk_l2norm, desc->scale, wsb + ws.rec_off, s);
             if (e != hipSuccess) return fail(GDN_ERR_HIP, "chunk_prep launch: %s", hipGetErrorString(e));
         }
     }

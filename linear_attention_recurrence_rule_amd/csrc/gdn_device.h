@@ -170,4 +170,40 @@ __device__ __forceinline__ void frag_store(OP* base, int frag, int lane, const F
 
 __device__ __forceinline__ float shfl_xor(float x, int mask) { return __shfl_xor(x, mask, WAVE); }
 
+// Cross-lane moves inside a row of 16 lanes (DPP, no LDS round trip).
+// CTRL: quad_perm(1,0,3,2) = 0xB1, quad_perm(2,3,0,1) = 0x4E, row_ror:4 = 0x124,
+// row_ror:8 = 0x128, row_half_mirror = 0x141.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum / max over aligned groups of N lanes (N = 8 or 16), result in every lane.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+    static_assert(N == 8 || N == 16, "group of 8 or 16 lanes");
+    x += dpp<0xB1>(x);
+    x += dpp<0x4E>(x);
+    if constexpr (N == 16) {
+        x += dpp<0x124>(x);
+        x += dpp<0x128>(x);
+    } else {
+        x += dpp<0x141>(x);
+    }
+    return x;
+}
+template <int N>
+__device__ __forceinline__ float group_max(float x) {
+    static_assert(N == 8 || N == 16, "group of 8 or 16 lanes");
+    x = fmaxf(x, dpp<0xB1>(x));
+    x = fmaxf(x, dpp<0x4E>(x));
+    if constexpr (N == 16) {
+        x = fmaxf(x, dpp<0x124>(x));
+        x = fmaxf(x, dpp<0x128>(x));
+    } else {
+        x = fmaxf(x, dpp<0x141>(x));
+    }
+    return x;
+}
+
 }  // namespace gdn

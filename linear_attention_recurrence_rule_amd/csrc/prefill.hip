@@ -112,22 +112,23 @@ template <typename OP>
 constexpr int ldt() { return CHUNK + 16 / (int)sizeof(OP); }  // row stride of [token][token] tiles
 constexpr int LDF = CHUNK + 4;                                  // fp32 64x64 tiles
 
-// LDS of chunk_prep.  q/k/v are kept row-major ([token][d]).  Operands that
+// LDS of chunk_prep (about 70 KiB at d = 128, so two workgroups share a
+// compute unit).  q and k are kept row-major ([token][d]).  Operands that
 // contract over tokens are read from them as column fragments, so nothing is
-// ever written transposed.  Region r0 holds A during the solve and -W after it.
+// ever written transposed.  Region b holds, by phase: A (strictly lower) with
+// X^T = ((I + A)^{-1})^T in its upper triangle, then the values V, then -W.
 template <int D, typename OP>
 struct PrepLds {
     static constexpr int LK = ldsk<D, OP>(), LT = ldt<OP>();
     OP k[CHUNK * LK];  // keys scaled per token by a power of two (exact)
     OP q[CHUNK * LK];  // queries, likewise
-    OP v[CHUNK * LK];  // values
-    union R0 {
-        float a[CHUNK * LDF];  // A = diag(beta) strict_lower(D o K K^T)
-        OP w[CHUNK * LK];      // -W [token][d]
-    } r0;
-    float x[CHUNK * LDF];  // X = (I + A)^{-1}
-    OP t[CHUNK * LT];      // T = X diag(beta)
-    OP p[CHUNK * LT];      // P = lower_incl(D o Q K^T)
+    union B {
+        float ax[CHUNK * LDF];  // A_ij (i > j) at [i][j]; X_ij (i >= j) at [j][i]
+        OP v[CHUNK * LK];       // values [token][d]
+        OP w[CHUNK * LK];       // -W [token][d]
+    } b;
+    OP t[CHUNK * LT];  // T = X diag(beta)
+    OP p[CHUNK * LT];  // P = lower_incl(D o Q K^T)
     float G[CHUNK], ck[CHUNK], cq[CHUNK], bt[CHUNK], gck[CHUNK], gcq[CHUNK];
 };
 
@@ -135,66 +136,12 @@ template <int D, typename OP>
 constexpr size_t prep_lds_bytes() { return sizeof(PrepLds<D, OP>); }
 
 // Norm factor c of one (token, head) vector whose elements were scaled by
-// 2^-e (exactly): the effective vector is c * scaled.
+// 2^-e (exactly): the effective vector is c * scaled.  With the L2 norm,
+// c = 1 / sqrt(sum scaled^2 + 1e-6 * 2^-2e); the epsilon term underflows to 0
+// or overflows to +inf (c = 0) only where it is negligible or dominant.
 __device__ __forceinline__ float norm_factor(float ss_scaled, int e, int l2norm, float mul) {
     if (!l2norm) return ldexpf(mul, e);
-    double den = ldexp((double)ss_scaled, 2 * e) + 1e-6;
-    return (float)(ldexp((double)mul, e) / sqrt(den));
-}
-
-// Raw inputs of one (block slot, v-head) item, held in registers so the next
-// item's loads overlap the current item's work.  Thread tid covers the 8-element
-// pieces tid, tid + 256, ... of the block's [token][d] tiles; the PER_TOK lanes of
-// a token are adjacent.
-template <int D, bool IN_BF16>
-struct PrepRaw {
-    static constexpr int PER_TOK = D / 8, NIT = CHUNK * PER_TOK / 256, W16 = IN_BF16 ? 1 : 2;
-    uint4 q[NIT][W16], k[NIT][W16], v[NIT][W16];
-    float g, b;
-    int tok0, nt;
-};
-
-template <int D, bool IN_BF16>
-__device__ __forceinline__ void prep_load(PrepRaw<D, IN_BF16>& R, int item, const void* q, const void* k,
-                                          const void* v, const float* g, const float* beta,
-                                          const SeqInfo* info, const int32_t* slot_seq, int T, int h_k,
-                                          int h_v, int tid) {
-    using PR = PrepRaw<D, IN_BF16>;
-    const int slot = item / h_v, h = item - slot * h_v, hk = h / (h_v / h_k);
-    int tok0 = 0, nt = 0;
-    if (slot_seq) {
-        const int n = slot_seq[slot];
-        if (n >= 0) {
-            const SeqInfo si = info[n];
-            const int j = slot - si.slot_base;
-            tok0 = si.begin + j * CHUNK;
-            nt = min(CHUNK, si.len - j * CHUNK);
-        }
-    } else {
-        tok0 = slot * CHUNK;
-        nt = min(CHUNK, T - tok0);
-    }
-    R.tok0 = tok0;
-    R.nt = nt;
-    // every load is issued (token indices clamped into [0, T)); data past nt is zeroed on use
-    constexpr int ES = IN_BF16 ? 2 : 4;
-#pragma unroll
-    for (int it = 0; it < PR::NIT; ++it) {
-        const int idx = tid + 256 * it, t = idx / PR::PER_TOK, pc = idx % PR::PER_TOK;
-        const size_t tok = (size_t)min(tok0 + t, T - 1);
-        const char* pq = reinterpret_cast<const char*>(q) + ((tok * h_k + hk) * D + 8 * pc) * ES;
-        const char* pk = reinterpret_cast<const char*>(k) + ((tok * h_k + hk) * D + 8 * pc) * ES;
-        const char* pv = reinterpret_cast<const char*>(v) + ((tok * h_v + h) * D + 8 * pc) * ES;
-#pragma unroll
-        for (int w = 0; w < PR::W16; ++w) {
-            R.q[it][w] = reinterpret_cast<const uint4*>(pq)[w];
-            R.k[it][w] = reinterpret_cast<const uint4*>(pk)[w];
-            R.v[it][w] = reinterpret_cast<const uint4*>(pv)[w];
-        }
-    }
-    const size_t tg = (size_t)min(tok0 + (tid & 63), T - 1) * h_v + h;
-    R.g = g[tg];
-    R.b = beta[tg];
+    return mul * rsqrtf(ss_scaled + ldexpf(1e-6f, -2 * e));
 }
 
 template <bool IN_BF16>
@@ -238,40 +185,73 @@ __device__ __forceinline__ void store4(OP* dst, const f4_t& x) {
     }
 }
 
-// One (block slot, v-head) item: everything of the block form that does not
-// depend on the carried state.
+// One workgroup per (block slot, v-head): everything of the block form that
+// does not depend on the carried state.
 template <int D, typename OP, bool IN_BF16>
-__device__ __forceinline__ void prep_item(PrepLds<D, OP>& L, const PrepRaw<D, IN_BF16>& R, char* rec, int l2norm,
-                                          float scale, int tid) {
-    using PR = PrepRaw<D, IN_BF16>;
+__global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
+    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, const SeqInfo* __restrict__ info,
+    const int32_t* __restrict__ slot_seq, int T, int h_k, int h_v, int l2norm, float scale,
+    char* __restrict__ recs) {
     using RC = Rec<D, OP>;
     constexpr int LK = PrepLds<D, OP>::LK, LT = PrepLds<D, OP>::LT;
-    const int wave = tid / WAVE, lane = tid % WAVE;
+    constexpr int PER_TOK = D / 8, NIT = CHUNK * PER_TOK / 256, W16 = IN_BF16 ? 1 : 2, ES = IN_BF16 ? 2 : 4;
+    extern __shared__ __align__(16) char smem_raw[];
+    PrepLds<D, OP>& L = *reinterpret_cast<PrepLds<D, OP>*>(smem_raw);
+    const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
     const int li = lane & 15, lq = lane >> 4;
-    const int nt = R.nt;
-    __syncthreads();  // the previous item is done with LDS
 
-    // ---- 1. per-token power-of-two scaling and norms; q, k, v to LDS (row-major) ----------
+    const int slot = blockIdx.x / h_v, h = blockIdx.x - slot * h_v, hk = h / (h_v / h_k);
+    int tok0, nt;
+    if (slot_seq) {
+        const int n = slot_seq[slot];
+        if (n < 0) return;
+        const SeqInfo si = info[n];
+        const int j = slot - si.slot_base;
+        tok0 = si.begin + j * CHUNK;
+        nt = min(CHUNK, si.len - j * CHUNK);
+    } else {
+        tok0 = slot * CHUNK;
+        nt = min(CHUNK, T - tok0);
+    }
+    char* rec = recs + (size_t)blockIdx.x * RC::BYTES;
+
+    // ---- 0. issue every input load (token indices clamped; data past nt zeroed on use) ----
+    uint4 rq[NIT][W16], rk[NIT][W16], rv[NIT][W16];
 #pragma unroll
-    for (int it = 0; it < PR::NIT; ++it) {
-        const int idx = tid + 256 * it, t = idx / PR::PER_TOK, pc = idx % PR::PER_TOK;
+    for (int it = 0; it < NIT; ++it) {
+        const int idx = tid + 256 * it, t = idx / PER_TOK, pc = idx % PER_TOK;
+        const size_t tok = (size_t)min(tok0 + t, T - 1);
+        const char* pq = reinterpret_cast<const char*>(q) + ((tok * h_k + hk) * D + 8 * pc) * ES;
+        const char* pk = reinterpret_cast<const char*>(k) + ((tok * h_k + hk) * D + 8 * pc) * ES;
+        const char* pv = reinterpret_cast<const char*>(v) + ((tok * h_v + h) * D + 8 * pc) * ES;
+#pragma unroll
+        for (int w = 0; w < W16; ++w) {
+            rq[it][w] = reinterpret_cast<const uint4*>(pq)[w];
+            rk[it][w] = reinterpret_cast<const uint4*>(pk)[w];
+            rv[it][w] = reinterpret_cast<const uint4*>(pv)[w];
+        }
+    }
+    const size_t tg = (size_t)min(tok0 + lane, T - 1) * h_v + h;
+    const float rg = g[tg], rb = beta[tg];
+
+    // ---- 1. per-token power-of-two scaling and norms; q, k to LDS (row-major) ---------------
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        const int idx = tid + 256 * it, t = idx / PER_TOK, pc = idx % PER_TOK;
         const bool live = t < nt;
-        float kx[8], qx[8], vx[8];
-        unpack8<IN_BF16>(R.k[it], kx);
-        unpack8<IN_BF16>(R.q[it], qx);
-        unpack8<IN_BF16>(R.v[it], vx);
+        float kx[8], qx[8];
+        unpack8<IN_BF16>(rk[it], kx);
+        unpack8<IN_BF16>(rq[it], qx);
         float mk = 0.f, mq = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            if (!live) { kx[e] = 0.f; qx[e] = 0.f; vx[e] = 0.f; }
+            if (!live) { kx[e] = 0.f; qx[e] = 0.f; }
             mk = fmaxf(mk, fabsf(kx[e]));
             mq = fmaxf(mq, fabsf(qx[e]));
         }
-#pragma unroll
-        for (int m = PR::PER_TOK / 2; m >= 1; m >>= 1) {
-            mk = fmaxf(mk, shfl_xor(mk, m));
-            mq = fmaxf(mq, shfl_xor(mq, m));
-        }
+        mk = group_max<PER_TOK>(mk);  // the PER_TOK lanes of a token are adjacent
+        mq = group_max<PER_TOK>(mq);
         int ek = 0, eq = 0;
         frexpf(mk, &ek);
         frexpf(mq, &eq);
@@ -283,14 +263,10 @@ __device__ __forceinline__ void prep_item(PrepLds<D, OP>& L, const PrepRaw<D, IN
             ssk += kx[e] * kx[e];
             ssq += qx[e] * qx[e];
         }
-#pragma unroll
-        for (int m = PR::PER_TOK / 2; m >= 1; m >>= 1) {
-            ssk += shfl_xor(ssk, m);
-            ssq += shfl_xor(ssq, m);
-        }
+        ssk = group_sum<PER_TOK>(ssk);
+        ssq = group_sum<PER_TOK>(ssq);
         store8<OP>(L.k + t * LK + 8 * pc, kx);
         store8<OP>(L.q + t * LK + 8 * pc, qx);
-        store8<OP>(L.v + t * LK + 8 * pc, vx);
         if (pc == 0) {
             L.ck[t] = live ? norm_factor(ssk, ek, l2norm, 1.0f) : 0.f;
             L.cq[t] = live ? norm_factor(ssq, eq, l2norm, scale) : 0.f;
@@ -298,17 +274,16 @@ __device__ __forceinline__ void prep_item(PrepLds<D, OP>& L, const PrepRaw<D, IN
     }
     float gam = 0.f;
     if (wave == 0) {
-        const int t = lane;
-        const bool live = t < nt;
-        float gx = live ? R.g : 0.f;
+        const bool live = lane < nt;
+        float gx = live ? rg : 0.f;
 #pragma unroll
         for (int off = 1; off < WAVE; off <<= 1) {
             const float o = __shfl_up(gx, off, WAVE);
-            if (t >= off) gx += o;
+            if (lane >= off) gx += o;
         }
-        L.G[t] = gx;
-        L.bt[t] = live ? R.b : 0.f;
-        gam = expf(gx);
+        L.G[lane] = gx;
+        L.bt[lane] = live ? rb : 0.f;
+        gam = __expf(gx);
     }
     __syncthreads();
     if (wave == 0) {
@@ -316,7 +291,7 @@ __device__ __forceinline__ void prep_item(PrepLds<D, OP>& L, const PrepRaw<D, IN
         L.gcq[lane] = gam * L.cq[lane];
     }
 
-    // ---- 2. decay-masked Gram products: A (fp32) and P (lower 4x4 tiles, spread over waves) ----
+    // ---- 2. decay-masked Gram products: A (fp32, strictly lower) and P (lower tiles over waves) ----
     for (int tl = wave; tl < 10; tl += 4) {
         const int mb = (tl >= 6) ? 3 : (tl >= 3) ? 2 : (tl >= 1) ? 1 : 0;
         const int nb = tl - mb * (mb + 1) / 2;
@@ -336,8 +311,8 @@ __device__ __forceinline__ void prep_item(PrepLds<D, OP>& L, const PrepRaw<D, IN
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int i = i0 + r;
-            const float dec = (j <= i) ? expf(fminf(Gi[r] - Gj, 0.f)) : 0.f;
-            L.r0.a[i * LDF + j] = (j < i) ? bti[r] * dec * ak[r] * cki[r] * ckj : 0.f;
+            const float dec = (j <= i) ? __expf(fminf(Gi[r] - Gj, 0.f)) : 0.f;
+            if (j < i) L.b.ax[i * LDF + j] = bti[r] * dec * ak[r] * cki[r] * ckj;
             L.p[i * LT + j] = (OP)(dec * aq[r] * cqi[r] * ckj);
         }
     }
@@ -349,27 +324,26 @@ __device__ __forceinline__ void prep_item(PrepLds<D, OP>& L, const PrepRaw<D, IN
     }
     __syncthreads();
 
-    // ---- 3. X = (I + A)^{-1}: substitution in the 16x16 diagonal blocks, then
-    //         X_ij = -X_ii sum_{m=j}^{i-1} A_im X_mj by block distance (fp32 matrix cores) -----
-    {
+    // ---- 3. X = (I + A)^{-1}, kept transposed in the upper triangle of b.ax -----------------
+    // Diagonal 16x16 blocks by substitution (wave w, lane c < 16 owns column c of block w);
+    // X_ij = -X_ii sum_{m=j}^{i-1} A_im X_mj by block distance (fp32 matrix cores).
+    if (lane < 16) {
         const int bb = wave;
-        if (lane < 16) {
-            float x[16];
+        float x[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float* arow = &L.r0.a[(16 * bb + i) * LDF + 16 * bb];
-                float acc = (i == lane) ? 1.f : 0.f;
+        for (int i = 0; i < 16; ++i) {
+            const float* arow = &L.b.ax[(16 * bb + i) * LDF + 16 * bb];
+            float acc = (i == lane) ? 1.f : 0.f;
 #pragma unroll
-                for (int j = 0; j < i; ++j) acc -= arow[j] * x[j];
-                x[i] = acc;
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) L.x[(16 * bb + i) * LDF + 16 * bb + lane] = x[i];
+            for (int jj = 0; jj < i; ++jj) acc -= arow[jj] * x[jj];
+            x[i] = acc;
         }
-        for (int idx = lane; idx < 256; idx += WAVE) {
-            const int i = idx / 16, jj = idx % 16;
-            for (int cb = bb + 1; cb < 4; ++cb) L.x[(16 * bb + i) * LDF + 16 * cb + jj] = 0.f;
-        }
+        // X[16bb + i][16bb + lane] for i >= lane, stored at [16bb + lane][16bb + i]
+#pragma unroll
+        for (int i4 = 0; i4 < 16; i4 += 4)
+            *reinterpret_cast<f4_t*>(&L.b.ax[(16 * bb + lane) * LDF + 16 * bb + i4]) =
+                f4_t{i4 + 0 >= lane ? x[i4 + 0] : 0.f, i4 + 1 >= lane ? x[i4 + 1] : 0.f,
+                     i4 + 2 >= lane ? x[i4 + 2] : 0.f, i4 + 3 >= lane ? x[i4 + 3] : 0.f};
     }
     __syncthreads();
     for (int dist = 1; dist < 4; ++dist) {
@@ -377,83 +351,57 @@ __device__ __forceinline__ void prep_item(PrepLds<D, OP>& L, const PrepRaw<D, IN
         if (i < 4) {
             f4_t acc = {0, 0, 0, 0};
             for (int m = j; m < i; ++m) {
-                const f4_t av = *reinterpret_cast<const f4_t*>(&L.r0.a[(16 * i + li) * LDF + 16 * m + 4 * lq]);
+                // A_im (lower, row-major) as the A operand; X_mj (stored transposed) as the B operand
+                const f4_t av = *reinterpret_cast<const f4_t*>(&L.b.ax[(16 * i + li) * LDF + 16 * m + 4 * lq]);
+                const f4_t xv = *reinterpret_cast<const f4_t*>(&L.b.ax[(16 * j + li) * LDF + 16 * m + 4 * lq]);
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], L.x[(16 * m + 4 * lq + e) * LDF + 16 * j + li], acc,
-                                                              0, 0, 0);
+                for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], xv[e], acc, 0, 0, 0);
             }
-            const f4_t xv = *reinterpret_cast<const f4_t*>(&L.x[(16 * i + li) * LDF + 16 * i + 4 * lq]);
+            // res = -X_ii acc: A operand X_ii[li][4q + e] stored at [16i + 4q + e][16i + li]
             f4_t res = {0, 0, 0, 0};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) res = __builtin_amdgcn_mfma_f32_16x16x4f32(-xv[e], acc[e], res, 0, 0, 0);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) L.x[(16 * i + 4 * lq + r) * LDF + 16 * j + li] = res[r];
+            for (int e = 0; e < 4; ++e)
+                res = __builtin_amdgcn_mfma_f32_16x16x4f32(-L.b.ax[(16 * i + 4 * lq + e) * LDF + 16 * i + li], acc[e], res,
+                                                          0, 0, 0);
+            // lane (c, q): X[16i + 4q + r][16j + c] -> stored at [16j + c][16i + 4q + r]
+            *reinterpret_cast<f4_t*>(&L.b.ax[(16 * j + li) * LDF + 16 * i + 4 * lq]) = res;
         }
         __syncthreads();
     }
-    for (int idx = tid; idx < CHUNK * CHUNK / 4; idx += 256) {  // T = X diag(beta)
-        const int i = idx / (CHUNK / 4), j4 = 4 * (idx % (CHUNK / 4));
-        const f4_t xv = *reinterpret_cast<const f4_t*>(&L.x[i * LDF + j4]);
-        const f4_t bv = *reinterpret_cast<const f4_t*>(&L.bt[j4]);
-        store4<OP>(L.t + i * LT + j4, xv * bv);
+    // T = X diag(beta): T[i][j] = X[i][j] beta_j for i >= j (X_ij at [j][i]), else 0
+    for (int idx = tid; idx < CHUNK * CHUNK / 4; idx += 256) {
+        const int jj = idx / (CHUNK / 4), i4 = 4 * (idx % (CHUNK / 4));
+        const f4_t xv = *reinterpret_cast<const f4_t*>(&L.b.ax[jj * LDF + i4]);
+        const float bj = L.bt[jj];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) L.t[(i4 + r) * LT + jj] = (OP)((i4 + r >= jj) ? xv[r] * bj : 0.f);
     }
     __syncthreads();
 
-    // ---- 4. K^T fragments for the scan, and W^T = (diag(gam c) K)^T T^T -------------------
-    // Units (kb, tb): d-blocks 2kb, 2kb+1 and token block tb; a wave's units share kb
-    // for d = 128.  Its accumulators are the scan's -W fragments directly.
-    OP* wrec = reinterpret_cast<OP*>(rec + RC::W);
-    OP* qrec = reinterpret_cast<OP*>(rec + RC::Q);
+    // ---- 4. values to LDS (region b), and the scan's K^T fragments --------------------------
     OP* krec = reinterpret_cast<OP*>(rec + RC::K);
-    constexpr int UPW = D / 32;  // units per wave
-    {
-        int cur_kb = -1;
-        Frag<OP> aw[2][2];
-        for (int uu = 0; uu < UPW; ++uu) {
-            const int unit = wave * UPW + uu, kb = unit / 4, tb = unit % 4;
-            if (kb != cur_kb) {
-                cur_kb = kb;
 #pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    const int mb = 2 * kb + s2;
+    for (int it = 0; it < NIT; ++it) {
+        const int idx = tid + 256 * it, t = idx / PER_TOK, pc = idx % PER_TOK;
+        float vx[8];
+        unpack8<IN_BF16>(rv[it], vx);
+        if (t >= nt) {
 #pragma unroll
-                    for (int kk = 0; kk < 2; ++kk) {
-                        Frag<OP> f = frag_colmajor<OP>(L.k, LK, mb, kk, lane);
-                        // the scan's K^T fragments: each d-block written by one wave
-                        if (mb / (D / 64) == wave) frag_store<OP>(krec, mb * 2 + kk, lane, f);
-#pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            frag_set(f, e, frag_get(f, e) * L.gck[32 * kk + 4 * lq + (e & 3) + 16 * (e >> 2)]);
-                        aw[s2][kk] = f;
-                    }
-                }
-            }
-            f4_t acc[2];
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                acc[s2] = f4_t{0, 0, 0, 0};
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) mma(acc[s2], aw[s2][kk], frag_rowmajor<OP>(L.t, LT, tb, kk, lane));
-            }
-            // lane (j, q): acc[s2][r] = W[token 16tb + j][d 16(2kb + s2) + 4q + r]
-            Frag<OP> fw;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) { frag_set(fw, e, -acc[0][e]); frag_set(fw, e + 4, -acc[1][e]); }
-            frag_store<OP>(wrec, tb * (D / 32) + kb, lane, fw);
-            const int tok = 16 * tb + li;
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) store4<OP>(L.r0.w + tok * LK + 16 * (2 * kb + s2) + 4 * lq, -acc[s2]);
+            for (int e = 0; e < 8; ++e) vx[e] = 0.f;
         }
+        store8<OP>(L.b.v + t * LK + 8 * pc, vx);
     }
+    for (int f = wave; f < (D / 16) * 2; f += 4)
+        frag_store<OP>(krec, f, lane, frag_colmajor<OP>(L.k, LK, f / 2, f % 2, lane));
+    __syncthreads();
 
     // ---- 5. Ut = T V and Ot = P Ut (fp32 accumulator tiles) --------------------------------
     float* urec = reinterpret_cast<float*>(rec + RC::U);
     float* orec = reinterpret_cast<float*>(rec + RC::O);
     for (int cbi = 0; cbi < D / 64; ++cbi) {
         const int nb = wave * (D / 64) + cbi;
-        const Frag<OP> fv0 = frag_colmajor<OP>(L.v, LK, nb, 0, lane);
-        const Frag<OP> fv1 = frag_colmajor<OP>(L.v, LK, nb, 1, lane);
+        const Frag<OP> fv0 = frag_colmajor<OP>(L.b.v, LK, nb, 0, lane);
+        const Frag<OP> fv1 = frag_colmajor<OP>(L.b.v, LK, nb, 1, lane);
         f4_t ut[4];
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
@@ -472,9 +420,13 @@ __device__ __forceinline__ void prep_item(PrepLds<D, OP>& L, const PrepRaw<D, IN
             *reinterpret_cast<f4_t*>(orec + ((size_t)(mb * (D / 16) + nb) * WAVE + lane) * 4) = ot;
         }
     }
-    __syncthreads();  // -W complete in LDS
+    __syncthreads();  // the values are no longer read
 
-    // ---- 6. Qt^T = (diag(gam cq) Q)^T + (-W)^T P^T : the scan's Qt fragments --------------
+    // ---- 6. W^T = (diag(gam c) K)^T T^T: the scan's -W fragments, and -W row-major in LDS -----
+    // Units (kb, tb): d-blocks 2kb, 2kb+1 and token block tb; a wave's units share kb for d = 128.
+    OP* wrec = reinterpret_cast<OP*>(rec + RC::W);
+    OP* qrec = reinterpret_cast<OP*>(rec + RC::Q);
+    constexpr int UPW = D / 32;  // units per wave
     {
         int cur_kb = -1;
         Frag<OP> aw[2][2];
@@ -485,7 +437,45 @@ __device__ __forceinline__ void prep_item(PrepLds<D, OP>& L, const PrepRaw<D, IN
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-                    for (int kk = 0; kk < 2; ++kk) aw[s2][kk] = frag_colmajor<OP>(L.r0.w, LK, 2 * kb + s2, kk, lane);
+                    for (int kk = 0; kk < 2; ++kk) {
+                        Frag<OP> f = frag_colmajor<OP>(L.k, LK, 2 * kb + s2, kk, lane);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            frag_set(f, e, frag_get(f, e) * L.gck[32 * kk + 4 * lq + (e & 3) + 16 * (e >> 2)]);
+                        aw[s2][kk] = f;
+                    }
+            }
+            f4_t acc[2];
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                acc[s2] = f4_t{0, 0, 0, 0};
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) mma(acc[s2], aw[s2][kk], frag_rowmajor<OP>(L.t, LT, tb, kk, lane));
+            }
+            // lane (j, q): acc[s2][r] = W[token 16tb + j][d 16(2kb + s2) + 4q + r]
+            Frag<OP> fw;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { frag_set(fw, e, -acc[0][e]); frag_set(fw, e + 4, -acc[1][e]); }
+            frag_store<OP>(wrec, tb * (D / 32) + kb, lane, fw);
+            const int tok = 16 * tb + li;
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) store4<OP>(L.b.w + tok * LK + 16 * (2 * kb + s2) + 4 * lq, -acc[s2]);
+        }
+    }
+    __syncthreads();  // -W complete in LDS
+
+    // ---- 7. Qt^T = (diag(gam cq) Q)^T + (-W)^T P^T: the scan's Qt fragments ----------------
+    {
+        int cur_kb = -1;
+        Frag<OP> aw[2][2];
+        for (int uu = 0; uu < UPW; ++uu) {
+            const int unit = wave * UPW + uu, kb = unit / 4, tb = unit % 4;
+            if (kb != cur_kb) {
+                cur_kb = kb;
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk) aw[s2][kk] = frag_colmajor<OP>(L.b.w, LK, 2 * kb + s2, kk, lane);
             }
             const int tok = 16 * tb + li;
             const float gq = L.gcq[tok];
@@ -505,40 +495,11 @@ __device__ __forceinline__ void prep_item(PrepLds<D, OP>& L, const PrepRaw<D, IN
         }
     }
 
-    // ---- 7. s_t = exp(G_n - G_t) c_t and gamma_n -------------------------------------------
+    // ---- 8. s_t = exp(G_n - G_t) c_t and gamma_n -------------------------------------------
     if (tid < CHUNK) {
         const float Gn = L.G[max(nt - 1, 0)];
-        reinterpret_cast<float*>(rec + RC::S)[tid] = (tid < nt) ? expf(Gn - L.G[tid]) * L.ck[tid] : 0.f;
-        if (tid == 0) reinterpret_cast<float*>(rec + RC::M)[0] = expf(Gn);
-    }
-}
-
-// Persistent: workgroup b handles items b, b + gridDim.x, ... (item = slot * h_v + v-head),
-// with the next item's inputs loaded while the current one is processed.  Every
-// iteration issues the same loads (past the end it re-reads the last item).
-template <int D, typename OP, bool IN_BF16>
-__global__ __launch_bounds__(256) void chunk_prep_kernel(
-    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
-    const float* __restrict__ g, const float* __restrict__ beta, const SeqInfo* __restrict__ info,
-    const int32_t* __restrict__ slot_seq, int items, int T, int h_k, int h_v, int l2norm, float scale,
-    char* __restrict__ recs) {
-    using RC = Rec<D, OP>;
-    extern __shared__ __align__(16) char smem_raw[];
-    PrepLds<D, OP>& L = *reinterpret_cast<PrepLds<D, OP>*>(smem_raw);
-    const int tid = threadIdx.x, stride = gridDim.x, last = items - 1;
-    int it = blockIdx.x;
-    if (it > last) return;
-    PrepRaw<D, IN_BF16> A, B;
-    prep_load<D, IN_BF16>(A, it, q, k, v, g, beta, info, slot_seq, T, h_k, h_v, tid);
-    for (;;) {
-        prep_load<D, IN_BF16>(B, min(it + stride, last), q, k, v, g, beta, info, slot_seq, T, h_k, h_v, tid);
-        if (A.nt > 0) prep_item<D, OP, IN_BF16>(L, A, recs + (size_t)it * RC::BYTES, l2norm, scale, tid);
-        it += stride;
-        if (it > last) break;
-        prep_load<D, IN_BF16>(A, min(it + stride, last), q, k, v, g, beta, info, slot_seq, T, h_k, h_v, tid);
-        if (B.nt > 0) prep_item<D, OP, IN_BF16>(L, B, recs + (size_t)it * RC::BYTES, l2norm, scale, tid);
-        it += stride;
-        if (it > last) break;
+        reinterpret_cast<float*>(rec + RC::S)[tid] = (tid < nt) ? __expf(Gn - L.G[tid]) * L.ck[tid] : 0.f;
+        if (tid == 0) reinterpret_cast<float*>(rec + RC::M)[0] = __expf(Gn);
     }
 }
 
@@ -768,32 +729,29 @@ template <int D, typename OP, bool IB>
 static hipError_t launch_prep_t(const void* q, const void* k, const void* v, const float* g,
                                 const float* beta, const void* info, const int32_t* slot_seq,
                                 int slots, int T, int h_k, int h_v, int l2norm, float scale,
-                                char* recs, int grid, hipStream_t stream) {
+                                char* recs, hipStream_t stream) {
     constexpr size_t lds = prep_lds_bytes<D, OP>();
     static_assert(lds <= 160 * 1024, "chunk_prep LDS budget");
     auto kern = chunk_prep_kernel<D, OP, IB>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    const int items = slots * h_v;
-    if (grid < 1 || grid > items) grid = items;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, stream, q, k, v, g, beta,
-                       reinterpret_cast<const SeqInfo*>(info), slot_seq, items, T, h_k, h_v, l2norm, scale,
-                       recs);
+    hipLaunchKernelGGL(kern, dim3(slots * h_v), dim3(256), lds, stream, q, k, v, g, beta,
+                       reinterpret_cast<const SeqInfo*>(info), slot_seq, T, h_k, h_v, l2norm, scale, recs);
     return hipGetLastError();
 }
 
 hipError_t launch_prep(int d, bool in_bf16, const void* q, const void* k, const void* v,
                        const float* g, const float* beta, const void* info, const int32_t* slot_seq,
-                       int slots, int T, int h_k, int h_v, int l2norm, float scale, void* recs, int grid,
+                       int slots, int T, int h_k, int h_v, int l2norm, float scale, void* recs,
                        hipStream_t stream) {
     char* r = reinterpret_cast<char*>(recs);
     if (d == 128 && in_bf16)
-        return launch_prep_t<128, _Float16, true>(q, k, v, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, grid, stream);
+        return launch_prep_t<128, _Float16, true>(q, k, v, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, stream);
     if (d == 64 && in_bf16)
-        return launch_prep_t<64, _Float16, true>(q, k, v, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, grid, stream);
+        return launch_prep_t<64, _Float16, true>(q, k, v, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, stream);
     if (d == 64 && !in_bf16)
-        return launch_prep_t<64, float, false>(q, k, v, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, grid, stream);
+        return launch_prep_t<64, float, false>(q, k, v, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, stream);
     return hipErrorInvalidValue;
 }
 
