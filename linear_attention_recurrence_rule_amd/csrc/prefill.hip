@@ -185,42 +185,31 @@ __device__ __forceinline__ void store4(OP* dst, const f4_t& x) {
     }
 }
 
-// One workgroup per (block slot, v-head): everything of the block form that
-// does not depend on the carried state.
+// Workgroup size of the block-form work (8 waves).
+constexpr int PREP_THREADS = 512;
+constexpr int PREP_WAVES = PREP_THREADS / WAVE;
+
+// The block-form work of one (block, v-head) that does not depend on the
+// carried state, written as one record.  Called by a whole workgroup of
+// PREP_THREADS threads; tokens tok0 .. tok0 + nt - 1 (1 <= nt <= 64) of v-head h.
 template <int D, typename OP, bool IN_BF16>
-__global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
-    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
-    const float* __restrict__ g, const float* __restrict__ beta, const SeqInfo* __restrict__ info,
-    const int32_t* __restrict__ slot_seq, int T, int h_k, int h_v, int l2norm, float scale,
-    char* __restrict__ recs) {
+__device__ __forceinline__ void prep_block(const void* __restrict__ q, const void* __restrict__ k,
+                                           const void* __restrict__ v, const float* __restrict__ g,
+                                           const float* __restrict__ beta, int tok0, int nt, int h, int T,
+                                           int h_k, int h_v, int l2norm, float scale, char* __restrict__ rec,
+                                           PrepLds<D, OP>& L) {
     using RC = Rec<D, OP>;
     constexpr int LK = PrepLds<D, OP>::LK, LT = PrepLds<D, OP>::LT;
-    constexpr int PER_TOK = D / 8, NIT = CHUNK * PER_TOK / 256, W16 = IN_BF16 ? 1 : 2, ES = IN_BF16 ? 2 : 4;
-    extern __shared__ __align__(16) char smem_raw[];
-    PrepLds<D, OP>& L = *reinterpret_cast<PrepLds<D, OP>*>(smem_raw);
+    constexpr int PER_TOK = D / 8, NIT = CHUNK * PER_TOK / PREP_THREADS, W16 = IN_BF16 ? 1 : 2, ES = IN_BF16 ? 2 : 4;
     const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
     const int li = lane & 15, lq = lane >> 4;
-
-    const int slot = blockIdx.x / h_v, h = blockIdx.x - slot * h_v, hk = h / (h_v / h_k);
-    int tok0, nt;
-    if (slot_seq) {
-        const int n = slot_seq[slot];
-        if (n < 0) return;
-        const SeqInfo si = info[n];
-        const int j = slot - si.slot_base;
-        tok0 = si.begin + j * CHUNK;
-        nt = min(CHUNK, si.len - j * CHUNK);
-    } else {
-        tok0 = slot * CHUNK;
-        nt = min(CHUNK, T - tok0);
-    }
-    char* rec = recs + (size_t)blockIdx.x * RC::BYTES;
+    const int hk = h / (h_v / h_k);
 
     // ---- 0. issue every input load (token indices clamped; data past nt zeroed on use) ----
     uint4 rq[NIT][W16], rk[NIT][W16], rv[NIT][W16];
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
-        const int idx = tid + 256 * it, t = idx / PER_TOK, pc = idx % PER_TOK;
+        const int idx = tid + PREP_THREADS * it, t = idx / PER_TOK, pc = idx % PER_TOK;
         const size_t tok = (size_t)min(tok0 + t, T - 1);
         const char* pq = reinterpret_cast<const char*>(q) + ((tok * h_k + hk) * D + 8 * pc) * ES;
         const char* pk = reinterpret_cast<const char*>(k) + ((tok * h_k + hk) * D + 8 * pc) * ES;
@@ -238,7 +227,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
     // ---- 1. per-token power-of-two scaling and norms; q, k to LDS (row-major) ---------------
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
-        const int idx = tid + 256 * it, t = idx / PER_TOK, pc = idx % PER_TOK;
+        const int idx = tid + PREP_THREADS * it, t = idx / PER_TOK, pc = idx % PER_TOK;
         const bool live = t < nt;
         float kx[8], qx[8];
         unpack8<IN_BF16>(rk[it], kx);
@@ -258,8 +247,8 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
         float ssk = 0.f, ssq = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            kx[e] = (float)(OP)ldexpf(kx[e], -ek);
-            qx[e] = (float)(OP)ldexpf(qx[e], -eq);
+            kx[e] = ldexpf(kx[e], -ek);  // exact; representable in OP for bf16 inputs
+            qx[e] = ldexpf(qx[e], -eq);
             ssk += kx[e] * kx[e];
             ssq += qx[e] * qx[e];
         }
@@ -291,32 +280,39 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
         L.gcq[lane] = gam * L.cq[lane];
     }
 
-    // ---- 2. decay-masked Gram products: A (fp32, strictly lower) and P (lower tiles over waves) ----
-    for (int tl = wave; tl < 10; tl += 4) {
+    // ---- 2. decay-masked Gram products: A (fp32, strictly lower) and P ----------------------
+    // 20 tile-products (10 lower 16x16 tiles of K K^T and of Q K^T) over the waves.
+    for (int tp = wave; tp < 20; tp += PREP_WAVES) {
+        const int tl = tp >> 1, isq = tp & 1;
         const int mb = (tl >= 6) ? 3 : (tl >= 3) ? 2 : (tl >= 1) ? 1 : 0;
         const int nb = tl - mb * (mb + 1) / 2;
-        f4_t ak = {0, 0, 0, 0}, aq = {0, 0, 0, 0};
+        const OP* rows = isq ? L.q : L.k;
+        f4_t acc = {0, 0, 0, 0};
 #pragma unroll
-        for (int kb = 0; kb < D / 32; ++kb) {
-            const Frag<OP> fk = frag_rowmajor<OP>(L.k, LK, nb, kb, lane);
-            mma(ak, frag_rowmajor<OP>(L.k, LK, mb, kb, lane), fk);
-            mma(aq, frag_rowmajor<OP>(L.q, LK, mb, kb, lane), fk);
-        }
+        for (int kb = 0; kb < D / 32; ++kb)
+            mma(acc, frag_rowmajor<OP>(rows, LK, mb, kb, lane), frag_rowmajor<OP>(L.k, LK, nb, kb, lane));
         const int j = 16 * nb + li, i0 = 16 * mb + 4 * lq;
         const float Gj = L.G[j], ckj = L.ck[j];
         const f4_t Gi = *reinterpret_cast<const f4_t*>(&L.G[i0]);
-        const f4_t cki = *reinterpret_cast<const f4_t*>(&L.ck[i0]);
-        const f4_t cqi = *reinterpret_cast<const f4_t*>(&L.cq[i0]);
-        const f4_t bti = *reinterpret_cast<const f4_t*>(&L.bt[i0]);
+        if (!isq) {
+            const f4_t cki = *reinterpret_cast<const f4_t*>(&L.ck[i0]);
+            const f4_t bti = *reinterpret_cast<const f4_t*>(&L.bt[i0]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = i0 + r;
-            const float dec = (j <= i) ? __expf(fminf(Gi[r] - Gj, 0.f)) : 0.f;
-            if (j < i) L.b.ax[i * LDF + j] = bti[r] * dec * ak[r] * cki[r] * ckj;
-            L.p[i * LT + j] = (OP)(dec * aq[r] * cqi[r] * ckj);
+            for (int r = 0; r < 4; ++r) {
+                const int i = i0 + r;
+                if (j < i) L.b.ax[i * LDF + j] = bti[r] * __expf(Gi[r] - Gj) * acc[r] * cki[r] * ckj;
+            }
+        } else {
+            const f4_t cqi = *reinterpret_cast<const f4_t*>(&L.cq[i0]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = i0 + r;
+                const float dec = (j <= i) ? __expf(fminf(Gi[r] - Gj, 0.f)) : 0.f;
+                L.p[i * LT + j] = (OP)(dec * acc[r] * cqi[r] * ckj);
+            }
         }
     }
-    for (int tl = wave; tl < 6; tl += 4) {  // strictly-upper tiles of P are zero
+    for (int tl = wave; tl < 6; tl += PREP_WAVES) {  // strictly-upper tiles of P are zero
         const int nb = (tl >= 3) ? 3 : (tl >= 1) ? 2 : 1;
         const int mb = tl - (nb - 1) * nb / 2;
 #pragma unroll
@@ -327,7 +323,11 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
     // ---- 3. X = (I + A)^{-1}, kept transposed in the upper triangle of b.ax -----------------
     // Diagonal 16x16 blocks by substitution (wave w, lane c < 16 owns column c of block w);
     // X_ij = -X_ii sum_{m=j}^{i-1} A_im X_mj by block distance (fp32 matrix cores).
-    if (lane < 16) {
+    OP* krec = reinterpret_cast<OP*>(rec + RC::K);
+    if (wave >= 4) {  // the scan's K^T fragments, while waves 0..3 solve the diagonal blocks
+        for (int f = wave - 4; f < (D / 16) * 2; f += PREP_WAVES - 4)
+            frag_store<OP>(krec, f, lane, frag_colmajor<OP>(L.k, LK, f / 2, f % 2, lane));
+    } else if (lane < 16) {
         const int bb = wave;
         float x[16];
 #pragma unroll
@@ -369,7 +369,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
         __syncthreads();
     }
     // T = X diag(beta): T[i][j] = X[i][j] beta_j for i >= j (X_ij at [j][i]), else 0
-    for (int idx = tid; idx < CHUNK * CHUNK / 4; idx += 256) {
+    for (int idx = tid; idx < CHUNK * CHUNK / 4; idx += PREP_THREADS) {
         const int jj = idx / (CHUNK / 4), i4 = 4 * (idx % (CHUNK / 4));
         const f4_t xv = *reinterpret_cast<const f4_t*>(&L.b.ax[jj * LDF + i4]);
         const float bj = L.bt[jj];
@@ -378,11 +378,10 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
     }
     __syncthreads();
 
-    // ---- 4. values to LDS (region b), and the scan's K^T fragments --------------------------
-    OP* krec = reinterpret_cast<OP*>(rec + RC::K);
+    // ---- 4. values to LDS (region b) -------------------------------------------------------
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
-        const int idx = tid + 256 * it, t = idx / PER_TOK, pc = idx % PER_TOK;
+        const int idx = tid + PREP_THREADS * it, t = idx / PER_TOK, pc = idx % PER_TOK;
         float vx[8];
         unpack8<IN_BF16>(rv[it], vx);
         if (t >= nt) {
@@ -391,15 +390,12 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
         }
         store8<OP>(L.b.v + t * LK + 8 * pc, vx);
     }
-    for (int f = wave; f < (D / 16) * 2; f += 4)
-        frag_store<OP>(krec, f, lane, frag_colmajor<OP>(L.k, LK, f / 2, f % 2, lane));
     __syncthreads();
 
     // ---- 5. Ut = T V and Ot = P Ut (fp32 accumulator tiles) --------------------------------
     float* urec = reinterpret_cast<float*>(rec + RC::U);
     float* orec = reinterpret_cast<float*>(rec + RC::O);
-    for (int cbi = 0; cbi < D / 64; ++cbi) {
-        const int nb = wave * (D / 64) + cbi;
+    for (int nb = wave; nb < D / 16; nb += PREP_WAVES) {
         const Frag<OP> fv0 = frag_colmajor<OP>(L.b.v, LK, nb, 0, lane);
         const Frag<OP> fv1 = frag_colmajor<OP>(L.b.v, LK, nb, 1, lane);
         f4_t ut[4];
@@ -426,7 +422,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
     // Units (kb, tb): d-blocks 2kb, 2kb+1 and token block tb; a wave's units share kb for d = 128.
     OP* wrec = reinterpret_cast<OP*>(rec + RC::W);
     OP* qrec = reinterpret_cast<OP*>(rec + RC::Q);
-    constexpr int UPW = D / 32;  // units per wave
+    constexpr int UPW = (D / 32) * 4 / PREP_WAVES;  // units per wave
     {
         int cur_kb = -1;
         Frag<OP> aw[2][2];
@@ -503,53 +499,58 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(
     }
 }
 
+// One workgroup per (block slot, v-head).
+template <int D, typename OP, bool IN_BF16>
+__global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
+    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, const SeqInfo* __restrict__ info,
+    const int32_t* __restrict__ slot_seq, int T, int h_k, int h_v, int l2norm, float scale,
+    char* __restrict__ recs) {
+    extern __shared__ __align__(16) char smem_raw[];
+    PrepLds<D, OP>& L = *reinterpret_cast<PrepLds<D, OP>*>(smem_raw);
+    const int slot = blockIdx.x / h_v, h = blockIdx.x - slot * h_v;
+    int tok0, nt;
+    if (slot_seq) {
+        const int n = slot_seq[slot];
+        if (n < 0) return;
+        const SeqInfo si = info[n];
+        const int j = slot - si.slot_base;
+        tok0 = si.begin + j * CHUNK;
+        nt = min(CHUNK, si.len - j * CHUNK);
+    } else {
+        tok0 = slot * CHUNK;
+        nt = min(CHUNK, T - tok0);
+    }
+    prep_block<D, OP, IN_BF16>(q, k, v, g, beta, tok0, nt, h, T, h_k, h_v, l2norm, scale,
+                               recs + (size_t)blockIdx.x * Rec<D, OP>::BYTES, L);
+}
+
 // ---- sequential phase -------------------------------------------------------------------
-// One workgroup of 4 waves owns 32 rows of one (sequence, v-head) state, so a
-// d-wide head has d/32 workgroups.  The rows of S evolve independently.  Per
-// 64-token block:
-//   phase A (contraction over d_k): wave w forms the block's token rows
-//     16w..16w+15 of U = Ut - W S^T and O = Ot + Qt S^T for the 32 rows,
+// One workgroup owns 32 rows of one (sequence, v-head) state, so a d-wide head
+// has d/32 workgroups.  The rows of S evolve independently.  A workgroup has
+// 12 waves.  Waves 0..7 compute; per 64-token block:
+//   phase A (contraction over d_k): wave w forms the 16 x 16 tiles (token
+//     block w % 4, row block w / 4) of U = Ut - W S^T and O = Ot + Qt S^T,
 //     reading S (as matrix-core operands) from LDS;
-//   phase B (contraction over tokens): wave w updates the d_k columns it owns,
+//   phase B (contraction over tokens): wave w updates the S^T tiles it owns,
 //     S^T <- gamma_n S^T + K^T diag(s) U, reading diag(s) U from LDS.
-// The fp32 state stays in registers for the whole sequence.  Each wave reads
-// only the operand fragments it uses, straight from the workspace into
-// registers, one block ahead of use.
-template <int D, typename OP>
-struct ScanOps {
-    static constexpr int DB = D / 64;  // d_k blocks of 16 owned by a wave
-    Frag<OP> w[D / 32], q[D / 32], k[DB][2];
-    f4_t u[2], o[2];
-    f4_t s;    // s_t of this lane's 4 tokens
-    float gn;  // exp(G_n)
+// The fp32 state stays in registers for the whole sequence.  Waves 8..11 copy
+// the records into a two-slot LDS ring with direct global-to-LDS loads (no
+// registers), issued one block and a half before use; only they wait on them.
+template <int D, typename OP, bool OUT_BF16>
+struct ScanLds {
+    struct Buf {
+        OP frag[3 * CHUNK * D];          // -W, Qt, K^T fragments of the block (record order)
+        float uo[2 * 4 * 2 * WAVE * 4];  // Ut, Ot tiles of the slice: [Ut|Ot][token block][row block][lane]
+        float sg[CHUNK + 4];             // s_t, then gamma_n
+    } buf[2];
+    OP sS[(D / 32) * 2 * WAVE * 8];            // S^T as B fragments (kb, row block)
+    OP sU[2 * 2 * WAVE * 8];                   // diag(s) U as B fragments (kk, row block)
+    char sO[CHUNK * 32 * (OUT_BF16 ? 2 : 4)];  // the block's 64 x 32 outputs, row-major
 };
 
-template <int D, typename OP>
-__device__ __forceinline__ void load_ops(ScanOps<D, OP>& op, const char* rec, int w, int lane, int cb0) {
-    using R = Rec<D, OP>;
-    const OP* W = reinterpret_cast<const OP*>(rec + R::W);
-    const OP* Q = reinterpret_cast<const OP*>(rec + R::Q);
-    const OP* K = reinterpret_cast<const OP*>(rec + R::K);
-#pragma unroll
-    for (int kb = 0; kb < D / 32; ++kb) {
-        op.w[kb] = frag_stored<OP>(W, w * (D / 32) + kb, lane);
-        op.q[kb] = frag_stored<OP>(Q, w * (D / 32) + kb, lane);
-    }
-#pragma unroll
-    for (int i = 0; i < ScanOps<D, OP>::DB; ++i)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) op.k[i][kk] = frag_stored<OP>(K, (w * ScanOps<D, OP>::DB + i) * 2 + kk, lane);
-    const float* U = reinterpret_cast<const float*>(rec + R::U);
-    const float* O = reinterpret_cast<const float*>(rec + R::O);
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-        const size_t t = ((size_t)(w * (D / 16) + cb0 + nb) * WAVE + lane) * 4;
-        op.u[nb] = *reinterpret_cast<const f4_t*>(U + t);
-        op.o[nb] = *reinterpret_cast<const f4_t*>(O + t);
-    }
-    op.s = *reinterpret_cast<const f4_t*>(reinterpret_cast<const float*>(rec + R::S) + 16 * w + 4 * (lane >> 4));
-    op.gn = reinterpret_cast<const float*>(rec + R::M)[0];
-}
+template <int D, typename OP, bool OUT_BF16>
+constexpr size_t scan_lds_bytes() { return sizeof(ScanLds<D, OP, OUT_BF16>); }
 
 // Write 4 accumulator values (one lane's share of a 16x16 tile) as half of a
 // stored fragment: part 0 = elements 0..3, part 1 = elements 4..7.
@@ -565,21 +566,65 @@ __device__ __forceinline__ void store_part(OP* base, int frag, int part, int lan
     }
 }
 
+constexpr int SCAN_COMPUTE_WAVES = 8, SCAN_LOADER_WAVES = 4;
+constexpr int SCAN_THREADS = (SCAN_COMPUTE_WAVES + SCAN_LOADER_WAVES) * WAVE;
+
+// s_waitcnt vmcnt(n), other counters untouched (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// One loader wave's share of copying a block record into an LDS slot: the
+// -W, Qt, K^T fragments (contiguous), the slice's Ut and Ot tiles (two
+// adjacent 1 KiB tiles per token block), and s_t / gamma_n.  Every loader wave
+// issues the same number of 1 KiB direct loads (PER_WAVE).
+template <int D, typename OP>
+struct ScanDma {
+    using R = Rec<D, OP>;
+    static constexpr int FRAG_LOADS = 3 * CHUNK * D * (int)sizeof(OP) / 1024 / SCAN_LOADER_WAVES;
+    static constexpr int UO_LOADS = 16 / SCAN_LOADER_WAVES;
+    static constexpr int PER_WAVE = FRAG_LOADS + UO_LOADS + 1;
+    static_assert(3 * CHUNK * D * (int)sizeof(OP) % (1024 * SCAN_LOADER_WAVES) == 0, "fragment split");
+
+    template <typename Buf>
+    __device__ __forceinline__ static void copy(const char* rec, Buf& b, int lw, int lane, int cb0) {
+        typedef __attribute__((address_space(3))) void* lds_ptr;
+#pragma unroll
+        for (int t = 0; t < FRAG_LOADS; ++t) {
+            const int j0 = (lw * FRAG_LOADS + t) * WAVE;  // first 16-byte piece of this load
+            __builtin_amdgcn_global_load_lds(rec + (size_t)(j0 + lane) * 16, (lds_ptr)(reinterpret_cast<char*>(b.frag) + j0 * 16),
+                                             16, 0, 0);
+        }
+#pragma unroll
+        for (int t = 0; t < UO_LOADS; ++t) {
+            const int j0 = (lw * UO_LOADS + t) * WAVE, j = j0 + lane;
+            const int which = j >> 9, tb = (j >> 7) & 3, within = j & 127;
+            const char* src = rec + (which ? R::O : R::U) + ((size_t)(tb * (D / 16) + cb0) * WAVE + within) * 16;
+            __builtin_amdgcn_global_load_lds(src, (lds_ptr)(reinterpret_cast<char*>(b.uo) + j0 * 16), 16, 0, 0);
+        }
+        // s_t and gamma_n: 17 pieces.  A direct load writes lane l's 16 bytes at
+        // base + 16 l, so only lanes 0..16 may take part.
+        if (lane < CHUNK / 4 + 1)
+            __builtin_amdgcn_global_load_lds(rec + R::S + (size_t)lane * 16, (lds_ptr)reinterpret_cast<char*>(b.sg), 16, 0, 0);
+    }
+};
+
 template <int D, typename OP, bool OUT_BF16>
-__global__ __launch_bounds__(256) void chunk_scan_kernel(
+__global__ __launch_bounds__(SCAN_THREADS) void chunk_scan_kernel(
     const char* __restrict__ recs, const SeqInfo* __restrict__ info, const float* __restrict__ state_in,
     float* __restrict__ state_out, void* __restrict__ out, char* __restrict__ sink, int units, int T, int h_v) {
     using R = Rec<D, OP>;
+    using Lds = ScanLds<D, OP, OUT_BF16>;
+    using Dma = ScanDma<D, OP>;
     constexpr int SLICES = D / 32;
-    constexpr int DB = ScanOps<D, OP>::DB;
-    __shared__ __align__(16) OP sS[(D / 32) * 2 * WAVE * 8];  // S^T as B fragments (kb, row block)
-    __shared__ __align__(16) OP sU[2 * 2 * WAVE * 8];         // diag(s) U as B fragments (kk, row block)
-    constexpr int OB = OUT_BF16 ? 2 : 4;                       // bytes per output element
-    __shared__ __align__(16) char sO[4][16 * 32 * OB];         // per wave: 16 tokens x 32 outputs, row-major
+    constexpr int TPW = D / 64;  // S^T tiles per compute wave
+    extern __shared__ __align__(16) char smem_raw[];
+    Lds& L = *reinterpret_cast<Lds*>(smem_raw);
     // Workgroups are dispatched round-robin over the 8 XCDs (blockIdx % 8).
     // The SLICES workgroups of one (sequence, v-head) unit are placed on the
-    // same XCD at consecutive positions, so they read each block record from
-    // that XCD's L2 instead of from HBM.
+    // same XCD, so they share each block record through that XCD's L2.
     const int xcd = blockIdx.x % 8, m = blockIdx.x / 8;
     const int slice = m % SLICES;
     const int unit = (m / SLICES) * 8 + xcd;  // sequence * h_v + v-head
@@ -595,120 +640,121 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(
     } else {
         begin = 0; len = T; slot0 = 0;
     }
-
-    // S^T tiles for the d_k blocks this wave owns: St[i][nb], lane (j, q) holds
-    // S[r0 + 16nb + j][16 mb + 4q + 0..3] with mb = w*DB + i
-    f4_t St[DB][2];
-    const size_t sbase = (size_t)unit * D * D;
-#pragma unroll
-    for (int i = 0; i < DB; ++i)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-            const int mb = w * DB + i;
-            if (state_in) {
-                const float4 x = *reinterpret_cast<const float4*>(
-                    state_in + sbase + (size_t)(r0 + 16 * nb + j16) * D + 16 * mb + 4 * q4);
-                St[i][nb] = f4_t{x.x, x.y, x.z, x.w};
-            } else {
-                St[i][nb] = f4_t{0, 0, 0, 0};
-            }
-            store_part<OP>(sS, (mb / 2) * 2 + nb, mb % 2, lane, St[i][nb]);
-        }
-
     const int nchunks = (len + CHUNK - 1) / CHUNK;
     auto rec_of = [&](int c) { return recs + ((size_t)(slot0 + c) * h_v + h) * R::BYTES; };
 
-    auto step = [&](const ScanOps<D, OP>& op, int c) {
-        __syncthreads();  // S^T fragments of this block are complete
-        f4_t accU[2], accO[2];
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) { accU[nb] = op.u[nb]; accO[nb] = op.o[nb]; }
-#pragma unroll
-        for (int kb = 0; kb < D / 32; ++kb)
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-                const Frag<OP> bs = frag_stored<OP>(sS, kb * 2 + nb, lane);
-                mma(accU[nb], op.w[kb], bs);
-                mma(accO[nb], op.q[kb], bs);
-            }
-        // outputs: transpose the wave's 16 x 32 tile through LDS, then one
-        // unconditional 16-byte store per lane (rows past the block's end go to the sink)
-        const int tok0 = begin + c * CHUNK;
-        const int nt = min(CHUNK, len - c * CHUNK);
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int e = (4 * q4 + r) * 32 + 16 * nb + j16;
-                if constexpr (OUT_BF16) reinterpret_cast<uint16_t*>(sO[w])[e] = f32_to_bf16(accO[nb][r]);
-                else reinterpret_cast<float*>(sO[w])[e] = accO[nb][r];
-            }
-        {
-            constexpr int LPRW = 32 * OB / 16;  // lanes per output row (16 B each)
-#pragma unroll
-            for (int part = 0; part < LPRW * 16 / WAVE; ++part) {
-                const int idx = part * WAVE + lane;
-                const int row = idx / LPRW, col16 = idx % LPRW;
-                const uint4 val = *reinterpret_cast<const uint4*>(sO[w] + row * 32 * OB + col16 * 16);
-                const int t = 16 * w + row;
-                char* dst = (t < nt) ? reinterpret_cast<char*>(out) +
-                                           (((size_t)(tok0 + t) * h_v + h) * D + r0) * OB + col16 * 16
-                                     : sink + lane * 16;
-                *reinterpret_cast<uint4*>(dst) = val;
+    if (w >= SCAN_COMPUTE_WAVES) {
+        // ------------------------------ loader waves ------------------------------
+        // Block c + 2 goes into slot c % 2 once block c is done (after B2 of c);
+        // before B1 of c + 1 the wave waits for its copy of block c + 1 only.
+        const int lw = w - SCAN_COMPUTE_WAVES;
+        if (nchunks == 0) return;
+        Dma::copy(rec_of(0), L.buf[0], lw, lane, cb0);
+        if (nchunks > 1) {
+            Dma::copy(rec_of(1), L.buf[1], lw, lane, cb0);
+            wait_vmcnt<Dma::PER_WAVE>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        __syncthreads();  // P: block 0 is in LDS
+        for (int c = 0; c < nchunks; ++c) {
+            __syncthreads();  // B1
+            __syncthreads();  // B2: slot c % 2 is free
+            if (c + 2 < nchunks) {
+                Dma::copy(rec_of(c + 2), L.buf[c & 1], lw, lane, cb0);
+                wait_vmcnt<Dma::PER_WAVE>();
+            } else {
+                wait_vmcnt<0>();
             }
         }
+        return;
+    }
+
+    // ------------------------------ compute waves ------------------------------
+    const int tb = w & 3, nbA = w >> 2;  // phase A tile
+    // S^T tiles owned in phase B: number w*TPW + t -> (mb, nb) = (number / 2, number % 2);
+    // lane (j, q) holds S[r0 + 16nb + j][16 mb + 4q + 0..3]
+    f4_t St[TPW];
+    const size_t sbase = (size_t)unit * D * D;
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
+    for (int t = 0; t < TPW; ++t) {
+        const int mb = (w * TPW + t) >> 1, nb = (w * TPW + t) & 1;
+        if (state_in) {
+            const float4 x = *reinterpret_cast<const float4*>(
+                state_in + sbase + (size_t)(r0 + 16 * nb + j16) * D + 16 * mb + 4 * q4);
+            St[t] = f4_t{x.x, x.y, x.z, x.w};
+        } else {
+            St[t] = f4_t{0, 0, 0, 0};
+        }
+        store_part<OP>(L.sS, (mb / 2) * 2 + nb, mb % 2, lane, St[t]);
+    }
+    constexpr int OB = OUT_BF16 ? 2 : 4;  // bytes per output element
+    if (nchunks > 0) __syncthreads();     // P
+    for (int c = 0; c < nchunks; ++c) {
+        __syncthreads();  // B1: block c in LDS; S^T fragments complete; sU, sO free
+        const typename Lds::Buf& B = L.buf[c & 1];
+        const OP* Wb = B.frag;
+        const OP* Qb = B.frag + CHUNK * D;
+        const OP* Kb = B.frag + 2 * CHUNK * D;
+        f4_t accU = *reinterpret_cast<const f4_t*>(&B.uo[((0 * 4 + tb) * 2 + nbA) * WAVE * 4 + lane * 4]);
+        f4_t accO = *reinterpret_cast<const f4_t*>(&B.uo[((1 * 4 + tb) * 2 + nbA) * WAVE * 4 + lane * 4]);
+#pragma unroll
+        for (int kb = 0; kb < D / 32; ++kb) {
+            const Frag<OP> bs = frag_stored<OP>(L.sS, kb * 2 + nbA, lane);
+            mma(accU, frag_stored<OP>(Wb, tb * (D / 32) + kb, lane), bs);
+            mma(accO, frag_stored<OP>(Qb, tb * (D / 32) + kb, lane), bs);
+        }
+        Frag<OP> kf[TPW][2];
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) kf[t][kk] = frag_stored<OP>(Kb, ((w * TPW + t) >> 1) * 2 + kk, lane);
+        const f4_t sv = *reinterpret_cast<const f4_t*>(&B.sg[16 * tb + 4 * q4]);
+        const float gn = B.sg[CHUNK];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int e = (16 * tb + 4 * q4 + r) * 32 + 16 * nbA + j16;
+            if constexpr (OUT_BF16) reinterpret_cast<uint16_t*>(L.sO)[e] = f32_to_bf16(accO[r]);
+            else reinterpret_cast<float*>(L.sO)[e] = accO[r];
+        }
+        {
             f4_t us;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) us[r] = accU[nb][r] * op.s[r];
-            store_part<OP>(sU, (w / 2) * 2 + nb, w % 2, lane, us);
+            for (int r = 0; r < 4; ++r) us[r] = accU[r] * sv[r];
+            store_part<OP>(L.sU, (tb / 2) * 2 + nbA, tb % 2, lane, us);
         }
-        __syncthreads();  // diag(s) U complete; S^T fragments no longer read
+        __syncthreads();  // B2: diag(s) U and the outputs complete; S^T fragments and slot c % 2 no longer read
+        // phase B: S^T <- gamma_n S^T + K^T diag(s) U
 #pragma unroll
-        for (int i = 0; i < DB; ++i)
+        for (int t = 0; t < TPW; ++t) {
+            const int mb = (w * TPW + t) >> 1, nb = (w * TPW + t) & 1;
+            St[t] *= gn;
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-                St[i][nb] *= op.gn;
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) mma(St[i][nb], op.k[i][kk], frag_stored<OP>(sU, kk * 2 + nb, lane));
-                const int mb = w * DB + i;
-                store_part<OP>(sS, (mb / 2) * 2 + nb, mb % 2, lane, St[i][nb]);
+            for (int kk = 0; kk < 2; ++kk) mma(St[t], kf[t][kk], frag_stored<OP>(L.sU, kk * 2 + nb, lane));
+            store_part<OP>(L.sS, (mb / 2) * 2 + nb, mb % 2, lane, St[t]);
+        }
+        // outputs: 16 bytes per lane, rows past the block's end go to the sink
+        {
+            constexpr int LPR = 32 * OB / 16;  // lanes per output row
+            const int tok0 = begin + c * CHUNK, nt = min(CHUNK, len - c * CHUNK);
+            for (int idx = tid; idx < CHUNK * LPR; idx += SCAN_COMPUTE_WAVES * WAVE) {
+                const int row = idx / LPR, col16 = idx % LPR;
+                const uint4 val = *reinterpret_cast<const uint4*>(L.sO + row * 32 * OB + col16 * 16);
+                char* dst = (row < nt) ? reinterpret_cast<char*>(out) +
+                                             (((size_t)(tok0 + row) * h_v + h) * D + r0) * OB + col16 * 16
+                                       : sink + lane * 16;
+                *reinterpret_cast<uint4*>(dst) = val;
             }
-    };
-
-    // Three operand sets in flight (two blocks of look-ahead).  Every
-    // iteration issues the same memory operations (a prefetch past the last
-    // block re-reads the last block), so the loads of one block are never
-    // conditional on the data of another.
-    if (nchunks > 0) {
-        const int last = nchunks - 1;
-        ScanOps<D, OP> opA, opB, opC;
-        load_ops<D, OP>(opA, rec_of(0), w, lane, cb0);
-        load_ops<D, OP>(opB, rec_of(min(1, last)), w, lane, cb0);
-        load_ops<D, OP>(opC, rec_of(min(2, last)), w, lane, cb0);
-        for (int c = 0;; c += 3) {
-            step(opA, c);
-            load_ops<D, OP>(opA, rec_of(min(c + 3, last)), w, lane, cb0);
-            if (c + 1 > last) break;
-            step(opB, c + 1);
-            load_ops<D, OP>(opB, rec_of(min(c + 4, last)), w, lane, cb0);
-            if (c + 2 > last) break;
-            step(opC, c + 2);
-            load_ops<D, OP>(opC, rec_of(min(c + 5, last)), w, lane, cb0);
-            if (c + 3 > last) break;
         }
     }
 
     if (state_out) {
 #pragma unroll
-        for (int i = 0; i < DB; ++i)
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-                const f4_t x = St[i][nb];
-                *reinterpret_cast<float4*>(state_out + sbase + (size_t)(r0 + 16 * nb + j16) * D + 16 * (w * DB + i) + 4 * q4) =
-                    make_float4(x[0], x[1], x[2], x[3]);
-            }
+        for (int t = 0; t < TPW; ++t) {
+            const int mb = (w * TPW + t) >> 1, nb = (w * TPW + t) & 1;
+            *reinterpret_cast<float4*>(state_out + sbase + (size_t)(r0 + 16 * nb + j16) * D + 16 * mb + 4 * q4) =
+                make_float4(St[t][0], St[t][1], St[t][2], St[t][3]);
+        }
     }
 }
 
@@ -736,7 +782,7 @@ static hipError_t launch_prep_t(const void* q, const void* k, const void* v, con
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(slots * h_v), dim3(256), lds, stream, q, k, v, g, beta,
+    hipLaunchKernelGGL(kern, dim3(slots * h_v), dim3(PREP_THREADS), lds, stream, q, k, v, g, beta,
                        reinterpret_cast<const SeqInfo*>(info), slot_seq, T, h_k, h_v, l2norm, scale, recs);
     return hipGetLastError();
 }
@@ -758,8 +804,14 @@ hipError_t launch_prep(int d, bool in_bf16, const void* q, const void* k, const 
 template <int D, typename OP, bool OB>
 static hipError_t launch_scan_t(const void* recs, const void* info, const float* s_in, float* s_out,
                                 void* out, void* sink, int units, int T, int h_v, hipStream_t stream) {
+    constexpr size_t lds = scan_lds_bytes<D, OP, OB>();
+    static_assert(lds <= 160 * 1024, "chunk_scan LDS budget");
+    auto kern = chunk_scan_kernel<D, OP, OB>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
     const int groups = (units + 7) / 8;  // see the XCD placement in chunk_scan_kernel
-    hipLaunchKernelGGL((chunk_scan_kernel<D, OP, OB>), dim3(groups * 8 * (D / 32)), dim3(256), 0, stream,
+    hipLaunchKernelGGL(kern, dim3(groups * 8 * (D / 32)), dim3(SCAN_THREADS), lds, stream,
                        reinterpret_cast<const char*>(recs), reinterpret_cast<const SeqInfo*>(info), s_in,
                        s_out, out, reinterpret_cast<char*>(sink), units, T, h_v);
     return hipGetLastError();
