@@ -86,6 +86,57 @@ def measured_traffic(kernel):
             "total_bytes": k["fetch_bytes"] + k["write_bytes"], "source": "profiles/hbm_traffic.md"}
 
 
+def crossover(L, gdn, inputs, to_dev, torch, np, dev):
+    """Direct (token scan) vs chunked prefill: N sequences of t tokens each, 32 v-heads / 16
+    k-heads, d = 128, bf16 in and out, fp32 state in and out.  Prints one JSON line per shape."""
+    shapes = [(64, t) for t in (1, 2, 4, 8, 16, 32, 64, 128, 256)] + [(1, t) for t in (64, 256, 1024, 4096)]
+    h_k, h_v, d = 16, 32, 128
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    for N, t in shapes:
+        x = inputs.prefill_inputs(seed=1, lengths=[t] * N, h_k=h_k, h_v=h_v, d=d, io_dtype=inputs.BF16,
+                                  state_std=0.02)
+        T = N * t
+        q, k, v, g, b = (to_dev(x[n]) for n in ("q", "k", "v", "g", "beta"))
+        s_in, cu = to_dev(x["state_in"]), to_dev(x["cu_seqlens"])
+        out = torch.empty((T, h_v, d), dtype=torch.bfloat16, device=dev)
+        s_out = torch.empty_like(s_in)
+        desc = gdn.make_desc(num_seqs=N, total_tokens=T, h_k=h_k, h_v=h_v, d=d, io_dtype=gdn.GDN_BF16,
+                             out_dtype=gdn.GDN_BF16)
+        dref = ctypes.byref(desc)
+        wsb = gdn.gdn_prefill_workspace_bytes(desc)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        P = [z.data_ptr() for z in (q, k, v, g, b, s_in, out, s_out, cu)]
+
+        def chunked():
+            return L.gdn_prefill(dref, P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[8], 64, ws.data_ptr(),
+                                 wsb, sp)
+
+        def direct():
+            return L.gdn_prefill_direct(dref, P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[8], sp)
+
+        res = {}
+        for name, fn in (("chunked", chunked), ("direct", direct)):
+            for _ in range(5):
+                if fn():
+                    raise gdn.GdnError(fn(), gdn.last_error())
+            torch.cuda.synchronize()
+            reps = 20
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            res[name] = e0.elapsed_time(e1) * 1e3 / reps
+        print(json.dumps({"crossover": {"num_seqs": N, "tokens_per_seq": t, "h_v": h_v, "h_k": h_k, "d": d,
+                                        "chunked_us": round(res["chunked"], 2), "direct_us": round(res["direct"], 2),
+                                        "chunked_tok_s": T / res["chunked"] * 1e6,
+                                        "direct_tok_s": T / res["direct"] * 1e6,
+                                        "faster": min(res, key=res.get)}}), flush=True)
+        del q, k, v, g, b, s_in, cu, out, s_out, ws
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -95,6 +146,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run plain 256 MiB device copies (reference for HBM byte counters)")
+    ap.add_argument("--crossover", action="store_true",
+                    help="instead of the benchmark line: time the direct and the chunked prefill over a "
+                         "range of sequence lengths (one JSON line per shape)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on exactly one GPU; --gpus %d is not supported "
@@ -118,6 +172,10 @@ def main():
         if x.dtype == np.uint16:
             return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    if args.crossover:
+        crossover(L, gdn, inputs, to_dev, torch, np, dev)
+        return
 
     # ---------------- prefill ----------------
     w = inputs.WORKLOADS[PREFILL_WL]
@@ -227,10 +285,28 @@ def main():
     d1.record(stream)
     torch.cuda.synchronize()
     us_dec = d0.elapsed_time(d1) * 1e3 / steps
+    # the same loop captured once in a HIP graph (device-resident inputs), replayed
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cap = torch.cuda.current_stream().cuda_stream
+        for t in range(steps):
+            st = L.gdn_decode_step(ddref, base[0] + t * qs, base[1] + t * ks, base[2] + t * vs_, base[3] + t * gs,
+                                   base[4] + t * bs, sptr, optr, cap)
+            if st:
+                raise gdn.GdnError(st, gdn.last_error())
+    graph.replay()
+    torch.cuda.synchronize()
+    d0.record(stream)
+    graph.replay()
+    d1.record(stream)
+    torch.cuda.synchronize()
+    us_dec_graph = d0.elapsed_time(d1) * 1e3 / steps
+    del graph
     dbytes = algorithmic_decode(N, dh_v, dh_k, dd)
     dec_gbs = dbytes / (us_dec * 1e-6) / 1e9
     decode_info = {"workload": DECODE_WL, "steps_timed": steps, "us_per_step": us_dec,
                    "steps_per_s": 1e6 / us_dec, "tok_per_s": N * 1e6 / us_dec,
+                   "us_per_step_hip_graph": us_dec_graph,
                    "algorithmic_mb_per_step": dbytes / 1e6,
                    "roofline": {"bound": "hbm", "kernel": "decode_step", "achieved": round(dec_gbs, 1),
                                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4),

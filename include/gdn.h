@@ -13,9 +13,9 @@
  *     o_t = S_t q_t,          alpha_t = exp(g_t).
  *
  * The same section gives two ways to evaluate it.  One scans tokens directly
- * (gdn_decode_step, one token per sequence).  The other regroups the updates
- * into blocks of tokens that expose matrix work (gdn_prefill, blocks of
- * `chunk` tokens).  Section "Keep the recurrent state on chip" keeps the state
+ * (gdn_decode_step for one token per sequence, gdn_prefill_direct for short
+ * runs of tokens).  The other regroups the updates into blocks of tokens that
+ * expose matrix work (gdn_prefill, blocks of `chunk` tokens).  Section "Keep the recurrent state on chip" keeps the state
  * and its gate in fp32 and the query/key activations in bf16.  This library
  * does the same, and reads and writes each state exactly once per call.
  *
@@ -157,6 +157,29 @@ gdn_status gdn_decode_step(const gdn_desc *desc,
                            const void *q, const void *k, const void *v,
                            const float *g, const float *beta,
                            float *state, void *out, void *stream);
+
+/*
+ * Direct (token-by-token) prefill over packed sequences: the other evaluation
+ * of the workload-shapes section, which says the faster of the two depends on
+ * the shape.  Each (sequence, v-head) state is loaded once, kept in registers
+ * while the sequence's tokens stream through one by one, and written once, so
+ * no workspace is needed.  It suits short sequences: multi-token decode and
+ * verify steps of a few tokens per sequence (state_in == state_out, in place).
+ * The arithmetic is fp32 throughout, as in gdn_decode_step.
+ *
+ * Arguments and layouts are those of gdn_prefill without chunk and workspace.
+ * cu_seqlens has the same contract; here each range [cu[n], cu[n+1]) is
+ * clamped into [0, total_tokens] on its own (an inverted range has no tokens).
+ * With one token per sequence and state_in == state_out this is
+ * gdn_decode_step.
+ */
+gdn_status gdn_prefill_direct(const gdn_desc *desc,
+                              const void *q, const void *k, const void *v,
+                              const float *g, const float *beta,
+                              const float *state_in,
+                              void *out, float *state_out,
+                              const int32_t *cu_seqlens,
+                              void *stream);
 
 /* Static, English name of a status code. */
 const char *gdn_status_str(gdn_status status);

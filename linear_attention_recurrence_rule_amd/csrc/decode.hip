@@ -57,15 +57,19 @@ __device__ __forceinline__ void decode_load(DecodeIn<D>& in, const float* __rest
     in.b = beta[unit];
 }
 
+// One token of the recurrence on the register-resident state slices `sr`
+// (updated in place); writes the token's output o = S q^ at `orow` (the
+// output row of this unit and token).
 template <int D, bool OUT_BF16>
-__device__ __forceinline__ void decode_compute(DecodeIn<D>& in, float* __restrict__ state, void* out, int unit,
-                                               int l2norm, float scale, int wave, int lane) {
+__device__ __forceinline__ void decode_token(float4 (&sr)[D / 8], const float (&kin)[4], const float (&qin)[4],
+                                             float vin, float gin, float bin, void* out, size_t orow, int l2norm,
+                                             float scale, int wave, int lane) {
     constexpr int LPR = D / 4, RPI = WAVE / LPR, NL = LPR / 2;
     const int c = lane % LPR, sub = lane / LPR;
-    const float alpha = expf(in.g);
+    const float alpha = expf(gin);
     float ssk = 0.f, ssq = 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) { ssk += in.kx[e] * in.kx[e]; ssq += in.qx[e] * in.qx[e]; }
+    for (int e = 0; e < 4; ++e) { ssk += kin[e] * kin[e]; ssq += qin[e] * qin[e]; }
 #pragma unroll
     for (int mask = LPR / 2; mask >= 1; mask >>= 1) {
         ssk += shfl_xor(ssk, mask);
@@ -75,7 +79,7 @@ __device__ __forceinline__ void decode_compute(DecodeIn<D>& in, float* __restric
     const float rq = (l2norm ? 1.0f / sqrtf(ssq + 1e-6f) : 1.0f) * scale;
     float kx[4], qx[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) { kx[e] = in.kx[e] * rk; qx[e] = in.qx[e] * rq; }
+    for (int e = 0; e < 4; ++e) { kx[e] = kin[e] * rk; qx[e] = qin[e] * rq; }
     float kq = kx[0] * qx[0] + kx[1] * qx[1] + kx[2] * qx[2] + kx[3] * qx[3];
 #pragma unroll
     for (int mask = LPR / 2; mask >= 1; mask >>= 1) kq += shfl_xor(kq, mask);
@@ -84,7 +88,7 @@ __device__ __forceinline__ void decode_compute(DecodeIn<D>& in, float* __restric
     float x[LPR];
 #pragma unroll
     for (int m = 0; m < NL; ++m) {
-        const float4 sm = in.s[m];
+        const float4 sm = sr[m];
         x[m] = sm.x * kx[0] + sm.y * kx[1] + sm.z * kx[2] + sm.w * kx[3];
         x[NL + m] = sm.x * qx[0] + sm.y * qx[1] + sm.z * qx[2] + sm.w * qx[3];
     }
@@ -104,24 +108,39 @@ __device__ __forceinline__ void decode_compute(DecodeIn<D>& in, float* __restric
     const int mrow = (c < NL) ? c : c - NL;
     const int row = wave * 32 + mrow * RPI + sub;
     float u = 0.f;
-    if (c < NL) u = in.b * (in.v - alpha * red);
+    if (c < NL) u = bin * (vin - alpha * red);
     const float u_pair = shfl_xor(u, NL);
-    if (c >= NL) store1<OUT_BF16>(out, (size_t)unit * D + row, alpha * red + u_pair * kq);
+    if (c >= NL) store1<OUT_BF16>(out, orow * D + row, alpha * red + u_pair * kq);
 
     // rank-1 update; u of row m lives in lane (group base + m)
     const int base = lane - c;
-    float* S = state + (size_t)unit * D * D;
 #pragma unroll
     for (int m = 0; m < NL; ++m) {
         const float um = __shfl(u, base + m, WAVE);
-        float4 sm = in.s[m];
+        float4 sm = sr[m];
         sm.x = alpha * sm.x + um * kx[0];
         sm.y = alpha * sm.y + um * kx[1];
         sm.z = alpha * sm.z + um * kx[2];
         sm.w = alpha * sm.w + um * kx[3];
-        const int r2 = wave * 32 + m * RPI + sub;
-        *reinterpret_cast<float4*>(S + (size_t)r2 * D + 4 * c) = sm;
+        sr[m] = sm;
     }
+}
+
+// This lane's state slices of one (sequence, v-head) unit, in or out.
+template <int D>
+__device__ __forceinline__ void state_store(const float4 (&sr)[D / 8], float* __restrict__ S, int wave, int lane) {
+    constexpr int LPR = D / 4, RPI = WAVE / LPR, NL = LPR / 2;
+    const int c = lane % LPR, sub = lane / LPR;
+#pragma unroll
+    for (int m = 0; m < NL; ++m)
+        *reinterpret_cast<float4*>(S + (size_t)(wave * 32 + m * RPI + sub) * D + 4 * c) = sr[m];
+}
+
+template <int D, bool OUT_BF16>
+__device__ __forceinline__ void decode_compute(DecodeIn<D>& in, float* __restrict__ state, void* out, int unit,
+                                               int l2norm, float scale, int wave, int lane) {
+    decode_token<D, OUT_BF16>(in.s, in.kx, in.qx, in.v, in.g, in.b, out, (size_t)unit, l2norm, scale, wave, lane);
+    state_store<D>(in.s, state + (size_t)unit * D * D, wave, lane);
 }
 
 // Each workgroup walks units blockIdx.x, blockIdx.x + gridDim.x, ... with the
@@ -149,6 +168,94 @@ __global__ __launch_bounds__(2 * D) void decode_step_kernel(
         u += stride;
         if (u > last) break;
     }
+}
+
+// ---- direct scan: the token recurrence with the state in registers ---------------------
+// "Optimizing on-device inference for Apple Silicon", section "Qwen creates
+// three distinct workload shapes", runs prefill either as this direct scan or
+// in blocks; which is faster depends on the shape.  One workgroup per
+// (sequence, v-head) unit loads its state once, walks the sequence's tokens
+// with the next token's inputs loaded while the current one computes, and
+// writes the state once.  Sequence n spans tokens [cu[n], cu[n+1]), both
+// clamped into [0, T] (an empty or inverted range has no tokens).
+template <int D, bool IN_BF16>
+struct TokIn {
+    float kx[4], qx[4];
+    float v, g, b;
+};
+
+template <int D, bool IN_BF16>
+__device__ __forceinline__ void token_load(TokIn<D, IN_BF16>& in, const void* q, const void* k, const void* v,
+                                           const float* g, const float* beta, size_t tok, int h, int hk, int h_k,
+                                           int h_v, int wave, int lane) {
+    constexpr int LPR = D / 4, RPI = WAVE / LPR, NL = LPR / 2;
+    const int c = lane % LPR, sub = lane / LPR;
+    load4<IN_BF16>(k, (tok * h_k + hk) * D + 4 * c, in.kx);
+    load4<IN_BF16>(q, (tok * h_k + hk) * D + 4 * c, in.qx);
+    const int mrow = (c < NL) ? c : c - NL;
+    in.v = load1<IN_BF16>(v, (tok * h_v + h) * D + wave * 32 + mrow * RPI + sub);
+    in.g = g[tok * h_v + h];
+    in.b = beta[tok * h_v + h];
+}
+
+template <int D, bool IN_BF16, bool OUT_BF16>
+__global__ __launch_bounds__(2 * D) void direct_scan_kernel(
+    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
+    const float* __restrict__ state_in, float* __restrict__ state_out, void* __restrict__ out, int T, int h_k,
+    int h_v, int l2norm, float scale) {
+    constexpr int LPR = D / 4, RPI = WAVE / LPR, NL = LPR / 2;
+    const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
+    const int c = lane % LPR, sub = lane / LPR;
+    const int unit = blockIdx.x, n = unit / h_v, h = unit - n * h_v, hk = h / (h_v / h_k);
+    int b0 = 0, e0 = T;
+    if (cu) {
+        b0 = min(max(cu[n], 0), T);
+        e0 = min(max(cu[n + 1], b0), T);
+    }
+    float4 sr[D / 8];
+    const size_t sbase = (size_t)unit * D * D;
+#pragma unroll
+    for (int m = 0; m < NL; ++m) {
+        const size_t off = sbase + (size_t)(wave * 32 + m * RPI + sub) * D + 4 * c;
+        sr[m] = state_in ? *reinterpret_cast<const float4*>(state_in + off) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (e0 > b0) {
+        TokIn<D, IN_BF16> A, B;
+        token_load<D, IN_BF16>(A, q, k, v, g, beta, (size_t)b0, h, hk, h_k, h_v, wave, lane);
+        for (int t = b0;;) {
+            token_load<D, IN_BF16>(B, q, k, v, g, beta, (size_t)min(t + 1, e0 - 1), h, hk, h_k, h_v, wave, lane);
+            decode_token<D, OUT_BF16>(sr, A.kx, A.qx, A.v, A.g, A.b, out, (size_t)t * h_v + h, l2norm, scale, wave, lane);
+            if (++t >= e0) break;
+            token_load<D, IN_BF16>(A, q, k, v, g, beta, (size_t)min(t + 1, e0 - 1), h, hk, h_k, h_v, wave, lane);
+            decode_token<D, OUT_BF16>(sr, B.kx, B.qx, B.v, B.g, B.b, out, (size_t)t * h_v + h, l2norm, scale, wave, lane);
+            if (++t >= e0) break;
+        }
+    }
+    if (state_out) state_store<D>(sr, state_out + sbase, wave, lane);
+}
+
+template <int D, bool IB, bool OB>
+static hipError_t launch_direct_t(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                                  const int32_t* cu, const float* s_in, float* s_out, void* out, int units, int T,
+                                  int h_k, int h_v, int l2norm, float scale, hipStream_t stream) {
+    hipLaunchKernelGGL((direct_scan_kernel<D, IB, OB>), dim3(units), dim3(2 * D), 0, stream, q, k, v, g, beta, cu,
+                       s_in, s_out, out, T, h_k, h_v, l2norm, scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_direct(int d, bool in_bf16, bool out_bf16, const void* q, const void* k, const void* v,
+                         const float* g, const float* beta, const int32_t* cu, const float* s_in, float* s_out,
+                         void* out, int units, int T, int h_k, int h_v, int l2norm, float scale, hipStream_t stream) {
+#define GDN_DIR(D, IB, OB)                                                                                 \
+    if (d == D && in_bf16 == IB && out_bf16 == OB)                                                         \
+        return launch_direct_t<D, IB, OB>(q, k, v, g, beta, cu, s_in, s_out, out, units, T, h_k, h_v, l2norm, \
+                                          scale, stream);
+    GDN_DIR(128, true, true) GDN_DIR(128, true, false) GDN_DIR(128, false, true)
+    GDN_DIR(128, false, false) GDN_DIR(64, true, true) GDN_DIR(64, true, false)
+    GDN_DIR(64, false, true) GDN_DIR(64, false, false)
+#undef GDN_DIR
+    return hipErrorInvalidValue;
 }
 
 template <int D, bool IB, bool OB>

@@ -3,9 +3,9 @@
 Argument marshalling only: every step of the recurrence runs in the HIP
 kernels behind the C entry points.  PyTorch supplies device memory and the
 current stream.  The functions named like the C entry points
-(``gdn_prefill``, ``gdn_decode_step``, ``gdn_prefill_workspace_bytes``) take
-the same arguments, with torch tensors in place of raw pointers.  ``prefill``
-and ``decode_step`` also allocate the outputs.
+(``gdn_prefill``, ``gdn_prefill_direct``, ``gdn_decode_step``, ...) take the
+same arguments, with torch tensors in place of raw pointers.  ``prefill``,
+``prefill_direct`` and ``decode_step`` also allocate the outputs.
 
 There is no fallback: if the library is missing or a call fails, an
 exception is raised.
@@ -71,6 +71,8 @@ def lib():
             L.gdn_prefill_prepare.restype = ctypes.c_int
             L.gdn_prefill_scan.argtypes = [dp, vp, vp, vp, vp, ctypes.c_int32, vp, sz, vp]
             L.gdn_prefill_scan.restype = ctypes.c_int
+            L.gdn_prefill_direct.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+            L.gdn_prefill_direct.restype = ctypes.c_int
             L.gdn_decode_step.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp]
             L.gdn_decode_step.restype = ctypes.c_int
             L.gdn_status_str.argtypes = [ctypes.c_int]
@@ -145,6 +147,12 @@ def gdn_prefill_scan(desc, state_in, out, state_out, cu_seqlens, chunk, workspac
                                   _stream(stream)))
 
 
+def gdn_prefill_direct(desc, q, k, v, g, beta, state_in, out, state_out, cu_seqlens, stream=None):
+    _check(lib().gdn_prefill_direct(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                    _ptr(state_in), _ptr(out), _ptr(state_out), _ptr(cu_seqlens),
+                                    _stream(stream)))
+
+
 def gdn_decode_step(desc, q, k, v, g, beta, state, out, stream=None):
     _check(lib().gdn_decode_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                  _ptr(state), _ptr(out), _stream(stream)))
@@ -199,6 +207,33 @@ def prefill(q, k, v, g, beta, *, state_in=None, cu_seqlens=None, out_dtype=None,
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     gdn_prefill(desc, q, k, v, g, beta, state_in, out, state_out, cu_seqlens, CHUNK, workspace,
                 workspace.numel(), stream)
+    return out, state_out
+
+
+def prefill_direct(q, k, v, g, beta, *, state_in=None, state_out=None, cu_seqlens=None, out_dtype=None,
+                   qk_l2norm=True, scale=1.0, want_state=True, stream=None):
+    """Token-by-token prefill (gdn_prefill_direct).  Same arguments as ``prefill``; pass
+    ``state_out=state_in`` to update the states in place.  Returns (out, state_out or None)."""
+    dev = q.device
+    io = _io_dtype(q)
+    T, h_k, d = q.shape
+    h_v = v.shape[1]
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype, dev)
+    _need(g, "g", torch.float32, dev)
+    _need(beta, "beta", torch.float32, dev)
+    N = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    if state_in is not None:
+        _need(state_in, "state_in", torch.float32, dev)
+    od = io if out_dtype is None else out_dtype
+    desc = make_desc(num_seqs=N, total_tokens=T, h_k=h_k, h_v=h_v, d=d, io_dtype=io, out_dtype=od,
+                     qk_l2norm=qk_l2norm, scale=scale)
+    out = torch.empty((T, h_v, d), dtype=_TORCH_DT[od], device=dev)
+    if state_out is None and want_state:
+        state_out = torch.empty((N, h_v, d, d), dtype=torch.float32, device=dev)
+    gdn_prefill_direct(desc, q, k, v, g, beta, state_in, out, state_out, cu_seqlens, stream)
     return out, state_out
 
 

@@ -35,7 +35,8 @@ def L():
 def test_exports_every_declared_function(L):
     names = gdn.declared_functions()
     assert set(names) == {"gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_prefill_prepare",
-                          "gdn_prefill_scan", "gdn_decode_step", "gdn_status_str", "gdn_last_error"}
+                          "gdn_prefill_scan", "gdn_prefill_direct", "gdn_decode_step", "gdn_status_str",
+                          "gdn_last_error"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -169,8 +170,31 @@ def test_decode_rejects_bad_arguments(L):
 
 
 @fake_pointers
+def test_direct_prefill_rejects_bad_arguments(L):
+    lib = gdn.lib()
+    def call(d, **p):
+        a = dict(q=FAKE, k=FAKE + 1 << 32, v=FAKE + 2 << 32, g=FAKE + 3 << 32, b=FAKE + 4 << 32,
+                 si=None, o=FAKE + 5 << 32, so=None, cu=None)
+        a.update(p)
+        return lib.gdn_prefill_direct(ctypes.byref(d), a["q"], a["k"], a["v"], a["g"], a["b"], a["si"],
+                                      a["o"], a["so"], a["cu"], None)
+    assert call(desc(h_v=30)) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call(desc(d=32)) == gdn.GDN_ERR_UNSUPPORTED
+    assert call(desc(total_tokens=-1)) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call(desc(num_seqs=2)) == gdn.GDN_ERR_INVALID_ARGUMENT           # cu_seqlens NULL with 2 sequences
+    assert call(desc(), o=None) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call(desc(), q=FAKE + 2) == gdn.GDN_ERR_INVALID_ARGUMENT         # misaligned
+    assert call(desc(), o=FAKE + 4 << 32) == gdn.GDN_ERR_INVALID_ARGUMENT   # out overlaps beta
+    s = FAKE + 7 << 32
+    assert call(desc(), si=s, so=s + 256) == gdn.GDN_ERR_INVALID_ARGUMENT  # partial state overlap
+    assert "overlap" in gdn.last_error()
+
+
+@fake_pointers
 def test_null_descriptor(L):
     assert gdn.lib().gdn_prefill(None, None, None, None, None, None, None, None, None, None, 64,
                                  None, 0, None) == gdn.GDN_ERR_INVALID_ARGUMENT
     assert gdn.lib().gdn_decode_step(None, None, None, None, None, None, None, None, None) == \
+        gdn.GDN_ERR_INVALID_ARGUMENT
+    assert gdn.lib().gdn_prefill_direct(None, None, None, None, None, None, None, None, None, None, None) == \
         gdn.GDN_ERR_INVALID_ARGUMENT

@@ -89,3 +89,30 @@ def test_decode_deterministic_and_in_place():
     o1 = gdn.decode_step(*args, s1)
     o2 = gdn.decode_step(*args, s2)
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+def test_decode_hip_graph_replays_match_eager():
+    """Several decode steps captured once in a HIP graph; every replay (with eager work and a
+    synchronisation in between) reproduces the eager launches bit for bit."""
+    N, h_k, h_v, d, steps = 4, 2, 4, 128, 3
+    x = inputs.decode_inputs(seed=13, num_seqs=N, steps=steps, h_k=h_k, h_v=h_v, d=d, io_dtype=inputs.BF16,
+                             state_std=0.1)
+    q, k, v, g, b = (dev(x[n]) for n in ("q", "k", "v", "g", "beta"))
+    s0 = dev(x["state"])
+    state_e = s0.clone()
+    outs_e = torch.stack([gdn.decode_step(q[t], k[t], v[t], g[t], b[t], state_e, out_dtype=inputs.F32)
+                          for t in range(steps)])
+    state_g = s0.clone()
+    out_g = torch.empty((steps, N, h_v, d), dtype=torch.float32, device=s0.device)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for t in range(steps):
+            gdn.decode_step(q[t], k[t], v[t], g[t], b[t], state_g, out=out_g[t], out_dtype=inputs.F32)
+    for _ in range(3):
+        state_g.copy_(s0)
+        out_g.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, outs_e) and torch.equal(state_g, state_e)
