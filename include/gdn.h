@@ -159,6 +159,33 @@ gdn_status gdn_decode_step(const gdn_desc *desc,
                            float *state, void *out, void *stream);
 
 /*
+ * Bounded-memory prefill of one long sequence (num_seqs == 1, no
+ * cu_seqlens): the tokens run through gdn_prefill in consecutive segments of
+ * `segment_tokens` (a positive multiple of chunk), each starting from the
+ * state the previous one left.  Section "Keep the recurrent state on chip"
+ * splits long prompts into pieces the same way and carries the state between
+ * them.  Because segments start on block boundaries, the result is bit for
+ * bit that of one gdn_prefill call, while the workspace needs room for one
+ * segment only (plus a state buffer when state_out is NULL):
+ * gdn_prefill_segmented_workspace_bytes().  The segments are enqueued from
+ * the host one after another on `stream`.
+ *
+ * Other arguments are those of gdn_prefill.  Errors: as gdn_prefill, and
+ * GDN_ERR_UNSUPPORTED for num_seqs != 1, a non-NULL cu_seqlens, or a segment
+ * length that is not a positive multiple of chunk.
+ */
+size_t gdn_prefill_segmented_workspace_bytes(const gdn_desc *desc, int32_t chunk, int64_t segment_tokens);
+
+gdn_status gdn_prefill_segmented(const gdn_desc *desc,
+                                 const void *q, const void *k, const void *v,
+                                 const float *g, const float *beta,
+                                 const float *state_in,
+                                 void *out, float *state_out,
+                                 int32_t chunk, int64_t segment_tokens,
+                                 void *workspace, size_t workspace_bytes,
+                                 void *stream);
+
+/*
  * Direct (token-by-token) prefill over packed sequences: the other evaluation
  * of the workload-shapes section, which says the faster of the two depends on
  * the shape.  Each (sequence, v-head) state is loaded once, kept in registers

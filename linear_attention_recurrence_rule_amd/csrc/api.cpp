@@ -265,6 +265,25 @@ gdn_status prefill_call(Phase phase, const gdn_desc* desc, const void* q, const 
     return GDN_OK;
 }
 
+// Segment descriptor and state buffer of the segmented prefill.
+gdn_status segment_plan(const gdn_desc* desc, int32_t chunk, int64_t seg, gdn_desc* sub, size_t* need,
+                               size_t* state_off) {
+    gdn_status st = check_desc(desc, true);
+    if (st != GDN_OK) return st;
+    if (chunk != kChunk) return fail(GDN_ERR_UNSUPPORTED, "chunk must be 64 (got %d)", chunk);
+    if (desc->num_seqs != 1) return fail(GDN_ERR_UNSUPPORTED, "segmented prefill takes one sequence (num_seqs = %d)",
+                                         desc->num_seqs);
+    if (seg <= 0 || seg % kChunk != 0)
+        return fail(GDN_ERR_UNSUPPORTED, "segment_tokens must be a positive multiple of %d (got %lld)", kChunk,
+                    (long long)seg);
+    *sub = *desc;
+    sub->total_tokens = desc->total_tokens < seg ? desc->total_tokens : seg;
+    const size_t seg_ws = ws_layout(sub, true).total;
+    *state_off = align_up(seg_ws, 256);
+    *need = *state_off + (size_t)desc->h_v * desc->d_k * desc->d_k * 4;
+    return GDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -289,6 +308,72 @@ gdn_status gdn_prefill_scan(const gdn_desc* desc, const float* state_in, void* o
                             size_t workspace_bytes, void* stream) {
     return prefill_call(kScan, desc, nullptr, nullptr, nullptr, nullptr, nullptr, state_in, out, state_out,
                         cu_seqlens, chunk, workspace, workspace_bytes, stream);
+}
+
+
+size_t gdn_prefill_segmented_workspace_bytes(const gdn_desc* desc, int32_t chunk, int64_t segment_tokens) {
+    g_err[0] = 0;
+    gdn_desc sub;
+    size_t need = 0, soff = 0;
+    if (segment_plan(desc, chunk, segment_tokens, &sub, &need, &soff) != GDN_OK) return 0;
+    return need;
+}
+
+gdn_status gdn_prefill_segmented(const gdn_desc* desc, const void* q, const void* k, const void* v,
+                                 const float* g, const float* beta, const float* state_in, void* out,
+                                 float* state_out, int32_t chunk, int64_t segment_tokens, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+    g_err[0] = 0;
+    gdn_desc sub;
+    size_t need = 0, soff = 0;
+    gdn_status st = segment_plan(desc, chunk, segment_tokens, &sub, &need, &soff);
+    if (st != GDN_OK) return st;
+    if (!workspace) return fail(GDN_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+    if (workspace_bytes < need)
+        return fail(GDN_ERR_WORKSPACE, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
+    const int64_t T = desc->total_tokens;
+    const int hk = desc->h_k, hv = desc->h_v, d = desc->d_k;
+    if (T > 0 && (!q || !k || !v || !g || !beta || !out))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "q, k, v, g, beta and out must be non-NULL");
+    const size_t io = dtype_size(desc->io_dtype), os = dtype_size(desc->out_dtype);
+    const size_t sbytes = (size_t)hv * d * d * 4;
+    const Span spans[] = {
+        {(const char*)q, (size_t)T * hk * d * io, "q"},
+        {(const char*)k, (size_t)T * hk * d * io, "k"},
+        {(const char*)v, (size_t)T * hv * d * io, "v"},
+        {(const char*)g, (size_t)T * hv * 4, "g"},
+        {(const char*)beta, (size_t)T * hv * 4, "beta"},
+        {(const char*)out, (size_t)T * hv * d * os, "out"},
+        {(const char*)state_in, state_in ? sbytes : 0, "state_in"},
+        {(const char*)state_out, state_out ? sbytes : 0, "state_out"},
+        {(const char*)workspace, need, "workspace"},
+    };
+    st = check_align(spans, sizeof(spans) / sizeof(spans[0]));
+    if (st != GDN_OK) return st;
+    st = check_overlaps(spans, sizeof(spans) / sizeof(spans[0]), state_in, state_out);
+    if (st != GDN_OK) return st;
+    // the carried state: state_out, or a workspace buffer when the caller wants none
+    float* carry = state_out ? state_out : reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + soff);
+    const size_t seg_ws = soff;
+    const int64_t nseg = T == 0 ? 1 : (T + segment_tokens - 1) / segment_tokens;
+    for (int64_t i = 0; i < nseg; ++i) {
+        const int64_t t0 = i * segment_tokens;
+        gdn_desc part = *desc;
+        part.total_tokens = (T - t0) < segment_tokens ? (T - t0) : segment_tokens;
+        const char* qc = reinterpret_cast<const char*>(q) + (size_t)t0 * hk * d * io;
+        const char* kc = reinterpret_cast<const char*>(k) + (size_t)t0 * hk * d * io;
+        const char* vc = reinterpret_cast<const char*>(v) + (size_t)t0 * hv * d * io;
+        const float* gc = g + (size_t)t0 * hv;
+        const float* bc = beta + (size_t)t0 * hv;
+        char* oc = reinterpret_cast<char*>(out) + (size_t)t0 * hv * d * os;
+        const float* sin = (i == 0) ? state_in : carry;
+        // the last segment writes state_out (or nothing when it is NULL)
+        float* sout = (i + 1 == nseg) ? state_out : carry;
+        st = prefill_call(kBoth, &part, T > 0 ? qc : q, T > 0 ? kc : k, T > 0 ? vc : v, T > 0 ? gc : g,
+                          T > 0 ? bc : beta, sin, T > 0 ? oc : out, sout, nullptr, chunk, workspace, seg_ws, stream);
+        if (st != GDN_OK) return st;
+    }
+    return GDN_OK;
 }
 
 gdn_status gdn_prefill_direct(const gdn_desc* desc, const void* q, const void* k, const void* v,

@@ -35,8 +35,8 @@ def L():
 def test_exports_every_declared_function(L):
     names = gdn.declared_functions()
     assert set(names) == {"gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_prefill_prepare",
-                          "gdn_prefill_scan", "gdn_prefill_direct", "gdn_decode_step", "gdn_status_str",
-                          "gdn_last_error"}
+                          "gdn_prefill_scan", "gdn_prefill_direct", "gdn_prefill_segmented_workspace_bytes",
+                          "gdn_prefill_segmented", "gdn_decode_step", "gdn_status_str", "gdn_last_error"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -188,6 +188,40 @@ def test_direct_prefill_rejects_bad_arguments(L):
     s = FAKE + 7 << 32
     assert call(desc(), si=s, so=s + 256) == gdn.GDN_ERR_INVALID_ARGUMENT  # partial state overlap
     assert "overlap" in gdn.last_error()
+
+
+def test_segmented_workspace_bytes(L):
+    full = gdn.gdn_prefill_workspace_bytes(desc(total_tokens=1 << 17))
+    seg = gdn.gdn_prefill_segmented_workspace_bytes(desc(total_tokens=1 << 17), 4096)
+    one = gdn.gdn_prefill_workspace_bytes(desc(total_tokens=4096))
+    # one segment's workspace (aligned) plus one fp32 state of 32 heads x 128 x 128
+    assert seg == (one + 255) // 256 * 256 + 32 * 128 * 128 * 4
+    assert seg < full // 20
+    for bad in (0, 100, -64):
+        assert L.gdn_prefill_segmented_workspace_bytes(ctypes.byref(desc()), 64, bad) == 0
+        assert "segment_tokens" in gdn.last_error()
+    assert L.gdn_prefill_segmented_workspace_bytes(ctypes.byref(desc(num_seqs=2)), 64, 256) == 0
+    assert L.gdn_prefill_segmented_workspace_bytes(ctypes.byref(desc()), 32, 256) == 0
+
+
+@fake_pointers
+def test_segmented_rejects_bad_arguments(L):
+    lib = gdn.lib()
+    d = desc()
+    need = gdn.gdn_prefill_segmented_workspace_bytes(d, 1024)
+    ws = FAKE + 9 << 32
+    def call(dd, seg=1024, wsb=need, **p):
+        a = dict(q=FAKE, k=FAKE + 1 << 32, v=FAKE + 2 << 32, g=FAKE + 3 << 32, b=FAKE + 4 << 32,
+                 si=None, o=FAKE + 5 << 32, so=None, ws=ws)
+        a.update(p)
+        return lib.gdn_prefill_segmented(ctypes.byref(dd), a["q"], a["k"], a["v"], a["g"], a["b"], a["si"], a["o"],
+                                          a["so"], 64, seg, a["ws"], wsb, None)
+    assert call(d, seg=1000) == gdn.GDN_ERR_UNSUPPORTED
+    assert call(desc(num_seqs=3)) == gdn.GDN_ERR_UNSUPPORTED
+    assert call(d, wsb=need - 1) == gdn.GDN_ERR_WORKSPACE
+    assert call(d, ws=None) == gdn.GDN_ERR_WORKSPACE
+    assert call(d, o=None) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call(d, o=FAKE + 3 << 32) == gdn.GDN_ERR_INVALID_ARGUMENT  # out overlaps g
 
 
 @fake_pointers

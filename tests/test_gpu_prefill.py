@@ -220,3 +220,26 @@ def test_beta_zero_and_overwrite_through_gpu():
     assert normwise(host(out_b)[:, 0], vb[:, 0]) <= 2e-3
     S = host(st_b)[0, 0]
     assert normwise((H[order] / np.sqrt(d)) @ S.T, vb[:, 0]) <= 2e-3
+
+
+@pytest.mark.parametrize("seg", [256, 320, 2048])
+def test_segmented_equals_one_call(seg):
+    """gdn_prefill_segmented: segments on block boundaries give the one-call result bit for bit."""
+    x = inputs.prefill_inputs(seed=14, total_tokens=1000, h_k=2, h_v=4, d=128, io_dtype=inputs.BF16, state_std=0.05)
+    out, st = run_gpu(x, inputs.BF16)
+    a = [dev(x[n]) for n in ("q", "k", "v", "g", "beta")]
+    o2, s2 = gdn.prefill_segmented(*a, segment_tokens=seg, state_in=dev(x["state_in"]), out_dtype=inputs.BF16)
+    assert torch.equal(o2, out) and torch.equal(s2, st)
+    # no initial state, no final state requested (the carried state lives in the workspace)
+    z = dict(x)
+    z["state_in"] = None
+    o3, _ = run_gpu(z, inputs.BF16, state=False)
+    o4, s4 = gdn.prefill_segmented(*a, segment_tokens=seg, out_dtype=inputs.BF16, want_state=False)
+    assert s4 is None and torch.equal(o4, o3)
+
+
+def test_segmented_empty_sequence_passes_state():
+    x = inputs.prefill_inputs(seed=15, total_tokens=0, h_k=2, h_v=4, d=64, io_dtype=inputs.BF16, state_std=0.1)
+    a = [dev(x[n]) for n in ("q", "k", "v", "g", "beta")]
+    o, s = gdn.prefill_segmented(*a, segment_tokens=64, state_in=dev(x["state_in"]))
+    assert o.numel() == 0 and torch.equal(s, dev(x["state_in"]))
