@@ -17,6 +17,7 @@ hipError_t launch_decode(int d, bool in_bf16, bool out_bf16, const void* q, cons
                          int units, int h_k, int h_v, int l2norm, float scale, int grid,
                          hipStream_t stream);
 size_t prefill_record_bytes(int d, bool in_bf16);
+size_t prefill_key_record_bytes(int d, bool in_bf16);
 hipError_t launch_direct(int d, bool in_bf16, bool out_bf16, const void* q, const void* k, const void* v,
                          const float* g, const float* beta, const int32_t* cu, const float* s_in, float* s_out,
                          void* out, int units, int T, int h_k, int h_v, int l2norm, float scale, hipStream_t stream);
@@ -25,9 +26,9 @@ hipError_t launch_plan(const int32_t* cu, int N, int T, int max_slots, void* inf
 hipError_t launch_prep(int d, bool in_bf16, const void* q, const void* k, const void* v,
                        const float* g, const float* beta, const void* info, const int32_t* slot_seq,
                        int slots, int T, int h_k, int h_v, int l2norm, float scale, void* recs,
-                       hipStream_t stream);
-hipError_t launch_scan(int d, bool in_bf16, bool out_bf16, const void* recs, const void* info,
-                       const float* s_in, float* s_out, void* out, void* sink, int units, int T, int h_v,
+                       void* krecs, hipStream_t stream);
+hipError_t launch_scan(int d, bool in_bf16, bool out_bf16, const void* recs, const void* krecs, const void* info,
+                       const float* s_in, float* s_out, void* out, void* sink, int units, int T, int h_k, int h_v,
                        hipStream_t stream);
 }  // namespace gdn
 
@@ -89,12 +90,13 @@ int64_t max_slots(const gdn_desc* d, bool varlen) {
     return (T + (int64_t)d->num_seqs * (kChunk - 1)) / kChunk;
 }
 
-// Workspace: [sink 1 KiB][plan: per-sequence info, slot -> sequence][block records]
+// Workspace: [sink 1 KiB][plan: per-sequence info, slot -> sequence]
+//            [records per (block slot, v-head)][key records per (block slot, k-head)]
 // The sink absorbs the chunk scan's stores for rows past the end of a block.
 constexpr size_t kSinkBytes = 1024;
 
 struct WsLayout {
-    size_t sink_off, info_off, slot_off, rec_off, total;
+    size_t sink_off, info_off, slot_off, rec_off, key_off, total;
     int64_t slots;
 };
 
@@ -108,8 +110,10 @@ WsLayout ws_layout(const gdn_desc* d, bool varlen) {
         w.slot_off = plan + (size_t)d->num_seqs * 16;
         plan = align_up(w.slot_off + (size_t)w.slots * 4, 256);
     }
+    const bool bf16 = d->io_dtype == GDN_BF16;
     w.rec_off = plan;
-    w.total = plan + (size_t)w.slots * d->h_v * gdn::prefill_record_bytes(d->d_k, d->io_dtype == GDN_BF16);
+    w.key_off = w.rec_off + (size_t)w.slots * d->h_v * gdn::prefill_record_bytes(d->d_k, bf16);
+    w.total = w.key_off + (size_t)w.slots * d->h_k * gdn::prefill_key_record_bytes(d->d_k, bf16);
     return w;
 }
 
@@ -253,13 +257,13 @@ gdn_status prefill_call(Phase phase, const gdn_desc* desc, const void* q, const 
         }
         if (ws.slots > 0 && T > 0) {  // chunk_prep clamps token indices into [0, T)
             e = gdn::launch_prep(d, in_bf16, q, k, v, g, beta, info, slot_seq, (int)ws.slots, (int)T, hk, hv,
-                                 desc->qk_l2norm, desc->scale, wsb + ws.rec_off, s);
+                                 desc->qk_l2norm, desc->scale, wsb + ws.rec_off, wsb + ws.key_off, s);
             if (e != hipSuccess) return fail(GDN_ERR_HIP, "chunk_prep launch: %s", hipGetErrorString(e));
         }
     }
     if ((phase & kScan) && (state_out || T > 0)) {
-        e = gdn::launch_scan(d, in_bf16, out_bf16, wsb + ws.rec_off, info, state_in, state_out,
-                             out, wsb + ws.sink_off, N * hv, (int)T, hv, s);
+        e = gdn::launch_scan(d, in_bf16, out_bf16, wsb + ws.rec_off, wsb + ws.key_off, info, state_in, state_out,
+                             out, wsb + ws.sink_off, N * hv, (int)T, hk, hv, s);
         if (e != hipSuccess) return fail(GDN_ERR_HIP, "chunk_scan launch: %s", hipGetErrorString(e));
     }
     return GDN_OK;

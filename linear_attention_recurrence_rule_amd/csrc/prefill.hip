@@ -30,6 +30,8 @@
 // Ut and Ot stay fp32 in the workspace.
 #include "gdn_device.h"
 
+#include <stdlib.h>
+
 namespace gdn {
 
 struct SeqInfo {
@@ -94,16 +96,25 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t* __restrict__ c
 // ---- workspace record of one (block slot, v-head) ----------------------------------------
 template <int D, typename OP>
 struct Rec {
-    // fragment-major operands for chunk_scan (64 lanes x 8 elements per fragment)
-    static constexpr size_t W = 0;                                 // -W   : (C/16) x (D/32) frags
-    static constexpr size_t Q = W + (size_t)CHUNK * D * sizeof(OP);  // Qt  : same
-    static constexpr size_t K = Q + (size_t)CHUNK * D * sizeof(OP);  // K^T : (D/16) x (C/32) frags
-    static constexpr size_t U = K + (size_t)CHUNK * D * sizeof(OP);  // Ut  : (C/16)(D/16) acc tiles fp32
-    static constexpr size_t O = U + (size_t)CHUNK * D * 4;           // Ot  : same
-    static constexpr size_t S = O + (size_t)CHUNK * D * 4;           // s_t = exp(G_n - G_t) c_t, fp32[C]
+    // Per (block, v-head), in the matrix-core operand type OP.  -W and Qt are
+    // fragment-major (64 lanes x 8 elements per fragment); Ut and Ot are 16x16
+    // accumulator tiles (64 lanes x 4 elements), ordered by row block of d_v,
+    // then token block, so the tiles of a row slice are contiguous.
+    static constexpr size_t W = 0;                                   // -W : (C/16) x (D/32) frags
+    static constexpr size_t Q = W + (size_t)CHUNK * D * sizeof(OP);  // Qt : same
+    static constexpr size_t U = Q + (size_t)CHUNK * D * sizeof(OP);  // Ut : (D/16) x (C/16) tiles
+    static constexpr size_t O = U + (size_t)CHUNK * D * sizeof(OP);  // Ot : same
+    static constexpr size_t S = O + (size_t)CHUNK * D * sizeof(OP);  // s_t = exp(G_n - G_t) c_t, fp32[C]
     static constexpr size_t M = S + CHUNK * 4;                       // gamma_n (fp32), pad
     static constexpr size_t BYTES = M + 256;
-    static constexpr size_t FRAG_BYTES = 3 * (size_t)CHUNK * D * sizeof(OP) + CHUNK * 4 + 16;
+    static constexpr size_t TILE = 16 * 16 * sizeof(OP);             // one Ut / Ot tile
+};
+
+// Per (block, k-head): K^T fragments, (D/16) x (C/32), shared by the v-heads
+// that read this k-head.
+template <int D, typename OP>
+struct KeyRec {
+    static constexpr size_t BYTES = (size_t)CHUNK * D * sizeof(OP);
 };
 
 template <int D, typename OP>
@@ -197,7 +208,7 @@ __device__ __forceinline__ void prep_block(const void* __restrict__ q, const voi
                                            const void* __restrict__ v, const float* __restrict__ g,
                                            const float* __restrict__ beta, int tok0, int nt, int h, int T,
                                            int h_k, int h_v, int l2norm, float scale, char* __restrict__ rec,
-                                           PrepLds<D, OP>& L) {
+                                           char* __restrict__ krec_bytes, PrepLds<D, OP>& L) {
     using RC = Rec<D, OP>;
     constexpr int LK = PrepLds<D, OP>::LK, LT = PrepLds<D, OP>::LT;
     constexpr int PER_TOK = D / 8, NIT = CHUNK * PER_TOK / PREP_THREADS, W16 = IN_BF16 ? 1 : 2, ES = IN_BF16 ? 2 : 4;
@@ -323,9 +334,9 @@ __device__ __forceinline__ void prep_block(const void* __restrict__ q, const voi
     // ---- 3. X = (I + A)^{-1}, kept transposed in the upper triangle of b.ax -----------------
     // Diagonal 16x16 blocks by substitution (wave w, lane c < 16 owns column c of block w);
     // X_ij = -X_ii sum_{m=j}^{i-1} A_im X_mj by block distance (fp32 matrix cores).
-    OP* krec = reinterpret_cast<OP*>(rec + RC::K);
+    OP* krec = reinterpret_cast<OP*>(krec_bytes);
     if (wave >= 4) {  // the scan's K^T fragments, while waves 0..3 solve the diagonal blocks
-        for (int f = wave - 4; f < (D / 16) * 2; f += PREP_WAVES - 4)
+        for (int f = wave - 4; krec && f < (D / 16) * 2; f += PREP_WAVES - 4)
             frag_store<OP>(krec, f, lane, frag_colmajor<OP>(L.k, LK, f / 2, f % 2, lane));
     } else if (lane < 16) {
         const int bb = wave;
@@ -393,8 +404,8 @@ __device__ __forceinline__ void prep_block(const void* __restrict__ q, const voi
     __syncthreads();
 
     // ---- 5. Ut = T V and Ot = P Ut (fp32 accumulator tiles) --------------------------------
-    float* urec = reinterpret_cast<float*>(rec + RC::U);
-    float* orec = reinterpret_cast<float*>(rec + RC::O);
+    OP* urec = reinterpret_cast<OP*>(rec + RC::U);
+    OP* orec = reinterpret_cast<OP*>(rec + RC::O);
     for (int nb = wave; nb < D / 16; nb += PREP_WAVES) {
         const Frag<OP> fv0 = frag_colmajor<OP>(L.b.v, LK, nb, 0, lane);
         const Frag<OP> fv1 = frag_colmajor<OP>(L.b.v, LK, nb, 1, lane);
@@ -404,7 +415,7 @@ __device__ __forceinline__ void prep_block(const void* __restrict__ q, const voi
             ut[mb] = f4_t{0, 0, 0, 0};
             mma(ut[mb], frag_rowmajor<OP>(L.t, LT, mb, 0, lane), fv0);
             mma(ut[mb], frag_rowmajor<OP>(L.t, LT, mb, 1, lane), fv1);
-            *reinterpret_cast<f4_t*>(urec + ((size_t)(mb * (D / 16) + nb) * WAVE + lane) * 4) = ut[mb];
+            store4<OP>(urec + ((size_t)(nb * 4 + mb) * WAVE + lane) * 4, ut[mb]);
         }
         const Frag<OP> fu0 = frag_from_acc<OP>(ut[0], ut[1]);
         const Frag<OP> fu1 = frag_from_acc<OP>(ut[2], ut[3]);
@@ -413,7 +424,7 @@ __device__ __forceinline__ void prep_block(const void* __restrict__ q, const voi
             f4_t ot = {0, 0, 0, 0};
             mma(ot, frag_rowmajor<OP>(L.p, LT, mb, 0, lane), fu0);
             mma(ot, frag_rowmajor<OP>(L.p, LT, mb, 1, lane), fu1);
-            *reinterpret_cast<f4_t*>(orec + ((size_t)(mb * (D / 16) + nb) * WAVE + lane) * 4) = ot;
+            store4<OP>(orec + ((size_t)(nb * 4 + mb) * WAVE + lane) * 4, ot);
         }
     }
     __syncthreads();  // the values are no longer read
@@ -505,7 +516,7 @@ __global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const SeqInfo* __restrict__ info,
     const int32_t* __restrict__ slot_seq, int T, int h_k, int h_v, int l2norm, float scale,
-    char* __restrict__ recs) {
+    char* __restrict__ recs, char* __restrict__ krecs) {
     extern __shared__ __align__(16) char smem_raw[];
     PrepLds<D, OP>& L = *reinterpret_cast<PrepLds<D, OP>*>(smem_raw);
     const int slot = blockIdx.x / h_v, h = blockIdx.x - slot * h_v;
@@ -521,36 +532,67 @@ __global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
         tok0 = slot * CHUNK;
         nt = min(CHUNK, T - tok0);
     }
+    // the first v-head of each k-head writes the k-head's key record
+    const int r = h_v / h_k;
+    char* krec = (h % r == 0) ? krecs + ((size_t)slot * h_k + h / r) * KeyRec<D, OP>::BYTES : nullptr;
     prep_block<D, OP, IN_BF16>(q, k, v, g, beta, tok0, nt, h, T, h_k, h_v, l2norm, scale,
-                               recs + (size_t)blockIdx.x * Rec<D, OP>::BYTES, L);
+                               recs + (size_t)blockIdx.x * Rec<D, OP>::BYTES, krec, L);
 }
 
 // ---- sequential phase -------------------------------------------------------------------
-// One workgroup owns 32 rows of one (sequence, v-head) state, so a d-wide head
-// has d/32 workgroups.  The rows of S evolve independently.  A workgroup has
-// 12 waves.  Waves 0..7 compute; per 64-token block:
-//   phase A (contraction over d_k): wave w forms the 16 x 16 tiles (token
-//     block w % 4, row block w / 4) of U = Ut - W S^T and O = Ot + Qt S^T,
+// One workgroup owns RS rows (16 or 32) of one (sequence, v-head) state, so a
+// d-wide head has d/RS workgroups.  The rows of S evolve independently.  A
+// workgroup has 12 waves.  Waves 0..7 compute; per 64-token block:
+//   phase A (contraction over d_k): wave w forms, for token block w % 4, the
+//     16 x RS tile of U = Ut - W S^T (w < 4) or of O = Ot + Qt S^T (w >= 4),
 //     reading S (as matrix-core operands) from LDS;
-//   phase B (contraction over tokens): wave w updates the S^T tiles it owns,
-//     S^T <- gamma_n S^T + K^T diag(s) U, reading diag(s) U from LDS.
-// The fp32 state stays in registers for the whole sequence.  Waves 8..11 copy
-// the records into a two-slot LDS ring with direct global-to-LDS loads (no
-// registers), issued one block and a half before use; only they wait on them.
-template <int D, typename OP, bool OUT_BF16>
-struct ScanLds {
-    struct Buf {
-        OP frag[3 * CHUNK * D];          // -W, Qt, K^T fragments of the block (record order)
-        float uo[2 * 4 * 2 * WAVE * 4];  // Ut, Ot tiles of the slice: [Ut|Ot][token block][row block][lane]
-        float sg[CHUNK + 4];             // s_t, then gamma_n
-    } buf[2];
-    OP sS[(D / 32) * 2 * WAVE * 8];            // S^T as B fragments (kb, row block)
-    OP sU[2 * 2 * WAVE * 8];                   // diag(s) U as B fragments (kk, row block)
-    char sO[CHUNK * 32 * (OUT_BF16 ? 2 : 4)];  // the block's 64 x 32 outputs, row-major
+//   phase B (contraction over tokens): each wave updates the S^T tiles it
+//     owns, S^T <- gamma_n S^T + K^T diag(s) U, reading diag(s) U from LDS.
+// The fp32 state stays in registers for the whole sequence, and the compute
+// waves issue no global memory operation inside the block loop.
+//
+// Waves 8..11 copy the block records into a two-slot LDS ring with direct
+// global-to-LDS loads and write the outputs.  A wave that issues a vector
+// memory operation stalls while the compute unit's memory pipeline is full,
+// so only these waves touch global memory, and each barrier interval gives
+// them a bounded share of it: the copy of block c + 2 goes out in two halves
+// (after the second barrier of block c, and after the first barrier of block
+// c + 1) and must have landed by the first barrier of block c + 2.  The
+// pipeline therefore always has copies queued while the compute waves work.
+constexpr int SCAN_COMPUTE_WAVES = 8, SCAN_LOADER_WAVES = 4;
+constexpr int SCAN_THREADS = (SCAN_COMPUTE_WAVES + SCAN_LOADER_WAVES) * WAVE;
+
+template <int D, typename OP, int RS>
+struct ScanShape {
+    static constexpr int NB = RS / 16;                       // 16-row blocks of the slice
+    static constexpr int FRAG_ELEMS = 3 * CHUNK * D;         // -W, Qt, K^T fragments
+    static constexpr int UO_ELEMS = 2 * NB * 4 * WAVE * 4;   // Ut, Ot tiles: [Ut|Ot][row block][token block][lane][4]
+    static constexpr int SG_FLOATS = CHUNK + 4;              // s_t, then gamma_n
+    // direct loads of 1 KiB (64 lanes x 16 bytes), per loader wave
+    static constexpr int FRAG_LOADS = FRAG_ELEMS * (int)sizeof(OP) / 1024 / SCAN_LOADER_WAVES;
+    static constexpr int UO_LOADS = UO_ELEMS * (int)sizeof(OP) / 1024 / SCAN_LOADER_WAVES;
+    static constexpr int PER_WAVE = FRAG_LOADS + UO_LOADS + 1;  // + s_t / gamma_n
+    static constexpr int FIRST = PER_WAVE / 2;                  // loads in the first half of a copy
+    static constexpr int NTB = (D / 16) * NB;                   // S^T tiles of the slice
+    static constexpr int TPW = NTB >= SCAN_COMPUTE_WAVES ? NTB / SCAN_COMPUTE_WAVES : 1;
+    static_assert(FRAG_ELEMS * (int)sizeof(OP) % (1024 * SCAN_LOADER_WAVES) == 0, "fragment split");
+    static_assert(UO_ELEMS * (int)sizeof(OP) % (1024 * SCAN_LOADER_WAVES) == 0, "tile split");
+    static_assert(NTB % SCAN_COMPUTE_WAVES == 0 || NTB < SCAN_COMPUTE_WAVES, "S^T tile split");
 };
 
-template <int D, typename OP, bool OUT_BF16>
-constexpr size_t scan_lds_bytes() { return sizeof(ScanLds<D, OP, OUT_BF16>); }
+template <int D, typename OP, int RS>
+struct ScanSlot {
+    using Sh = ScanShape<D, OP, RS>;
+    OP frag[Sh::FRAG_ELEMS];
+    OP uo[Sh::UO_ELEMS];
+    float sg[Sh::SG_FLOATS];
+};
+
+template <int D, typename OP, bool OUT_BF16, int RS>
+constexpr size_t scan_lds_bytes() {
+    return 2 * sizeof(ScanSlot<D, OP, RS>) + ((D / 32) + 2) * (RS / 16) * WAVE * 8 * sizeof(OP) +
+           (size_t)CHUNK * RS * (OUT_BF16 ? 2 : 4);
+}
 
 // Write 4 accumulator values (one lane's share of a 16x16 tile) as half of a
 // stored fragment: part 0 = elements 0..3, part 1 = elements 4..7.
@@ -566,9 +608,6 @@ __device__ __forceinline__ void store_part(OP* base, int frag, int part, int lan
     }
 }
 
-constexpr int SCAN_COMPUTE_WAVES = 8, SCAN_LOADER_WAVES = 4;
-constexpr int SCAN_THREADS = (SCAN_COMPUTE_WAVES + SCAN_LOADER_WAVES) * WAVE;
-
 // s_waitcnt vmcnt(n), other counters untouched (gfx9 encoding)
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -576,52 +615,65 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// One loader wave's share of copying a block record into an LDS slot: the
-// -W, Qt, K^T fragments (contiguous), the slice's Ut and Ot tiles (two
-// adjacent 1 KiB tiles per token block), and s_t / gamma_n.  Every loader wave
-// issues the same number of 1 KiB direct loads (PER_WAVE).
-template <int D, typename OP>
-struct ScanDma {
-    using R = Rec<D, OP>;
-    static constexpr int FRAG_LOADS = 3 * CHUNK * D * (int)sizeof(OP) / 1024 / SCAN_LOADER_WAVES;
-    static constexpr int UO_LOADS = 16 / SCAN_LOADER_WAVES;
-    static constexpr int PER_WAVE = FRAG_LOADS + UO_LOADS + 1;
-    static_assert(3 * CHUNK * D * (int)sizeof(OP) % (1024 * SCAN_LOADER_WAVES) == 0, "fragment split");
+// Barrier for the loader waves.  A workgroup-scope release fence would make
+// them wait for every direct load still in flight (those write LDS), so they
+// wait for their own LDS reads only.  The signal fences keep the compiler from
+// moving LDS accesses across the barrier.
+__device__ __forceinline__ void loader_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
-    template <typename Buf>
-    __device__ __forceinline__ static void copy(const char* rec, Buf& b, int lw, int lane, int cb0) {
-        typedef __attribute__((address_space(3))) void* lds_ptr;
+// Loads I0..I1-1 of one loader wave's share of copying a block into a ring
+// slot.  In order: the -W and Qt fragments (v-head record) and the K^T
+// fragments (k-head record), contiguous in the slot; the slice's Ut and Ot
+// tiles (contiguous in the record); s_t / gamma_n.
+template <int D, typename OP, int RS, int I0, int I1>
+__device__ __forceinline__ void scan_copy(const char* rec, const char* krec, ScanSlot<D, OP, RS>* s, int lw,
+                                          int lane, int cb0) {
+    using Sh = ScanShape<D, OP, RS>;
+    using R = Rec<D, OP>;
+    typedef __attribute__((address_space(3))) void* lds_ptr;
+    constexpr int WQ = 2 * CHUNK * D * (int)sizeof(OP);         // bytes of -W and Qt
+    constexpr int UO_HALF = Sh::NB * 4 * (int)R::TILE;          // bytes of the slice's Ut (or Ot) tiles
 #pragma unroll
-        for (int t = 0; t < FRAG_LOADS; ++t) {
-            const int j0 = (lw * FRAG_LOADS + t) * WAVE;  // first 16-byte piece of this load
-            __builtin_amdgcn_global_load_lds(rec + (size_t)(j0 + lane) * 16, (lds_ptr)(reinterpret_cast<char*>(b.frag) + j0 * 16),
-                                             16, 0, 0);
+    for (int i = I0; i < I1; ++i) {
+        if (i < Sh::FRAG_LOADS) {
+            const int j0 = (lw * Sh::FRAG_LOADS + i) * 1024;  // byte offset of this load in the slot
+            const char* src = (j0 < WQ ? rec + j0 : krec + (j0 - WQ)) + lane * 16;
+            __builtin_amdgcn_global_load_lds(src, (lds_ptr)(reinterpret_cast<char*>(s->frag) + j0), 16, 0, 0);
+        } else if (i < Sh::FRAG_LOADS + Sh::UO_LOADS) {
+            const int j0 = (lw * Sh::UO_LOADS + (i - Sh::FRAG_LOADS)) * 1024;  // byte offset in uo
+            const char* src = (j0 < UO_HALF ? rec + R::U + j0 : rec + R::O + (j0 - UO_HALF)) +
+                              (size_t)cb0 * 4 * R::TILE + lane * 16;
+            __builtin_amdgcn_global_load_lds(src, (lds_ptr)(reinterpret_cast<char*>(s->uo) + j0), 16, 0, 0);
+        } else if (lane < CHUNK / 4 + 1) {
+            // s_t and gamma_n: 17 pieces.  A direct load writes lane l's 16
+            // bytes at base + 16 l, so only lanes 0..16 take part.
+            const char* src = rec + R::S + (size_t)lane * 16;
+            __builtin_amdgcn_global_load_lds(src, (lds_ptr)reinterpret_cast<char*>(s->sg), 16, 0, 0);
         }
-#pragma unroll
-        for (int t = 0; t < UO_LOADS; ++t) {
-            const int j0 = (lw * UO_LOADS + t) * WAVE, j = j0 + lane;
-            const int which = j >> 9, tb = (j >> 7) & 3, within = j & 127;
-            const char* src = rec + (which ? R::O : R::U) + ((size_t)(tb * (D / 16) + cb0) * WAVE + within) * 16;
-            __builtin_amdgcn_global_load_lds(src, (lds_ptr)(reinterpret_cast<char*>(b.uo) + j0 * 16), 16, 0, 0);
-        }
-        // s_t and gamma_n: 17 pieces.  A direct load writes lane l's 16 bytes at
-        // base + 16 l, so only lanes 0..16 may take part.
-        if (lane < CHUNK / 4 + 1)
-            __builtin_amdgcn_global_load_lds(rec + R::S + (size_t)lane * 16, (lds_ptr)reinterpret_cast<char*>(b.sg), 16, 0, 0);
     }
-};
+}
 
-template <int D, typename OP, bool OUT_BF16>
+template <int D, typename OP, bool OUT_BF16, int RS>
 __global__ __launch_bounds__(SCAN_THREADS) void chunk_scan_kernel(
-    const char* __restrict__ recs, const SeqInfo* __restrict__ info, const float* __restrict__ state_in,
-    float* __restrict__ state_out, void* __restrict__ out, char* __restrict__ sink, int units, int T, int h_v) {
+    const char* __restrict__ recs, const char* __restrict__ krecs, const SeqInfo* __restrict__ info,
+    const float* __restrict__ state_in, float* __restrict__ state_out, void* __restrict__ out,
+    char* __restrict__ sink, int units, int T, int h_k, int h_v) {
     using R = Rec<D, OP>;
-    using Lds = ScanLds<D, OP, OUT_BF16>;
-    using Dma = ScanDma<D, OP>;
-    constexpr int SLICES = D / 32;
-    constexpr int TPW = D / 64;  // S^T tiles per compute wave
-    extern __shared__ __align__(16) char smem_raw[];
-    Lds& L = *reinterpret_cast<Lds*>(smem_raw);
+    using Sh = ScanShape<D, OP, RS>;
+    using Slot = ScanSlot<D, OP, RS>;
+    constexpr int NB = Sh::NB, SLICES = D / RS, TPW = Sh::TPW;
+    constexpr int OB = OUT_BF16 ? 2 : 4;  // bytes per output element
+    // Separate arrays: the direct loads target only `ring`, so the loader
+    // waves' reads of `sO` need not wait for the loads in flight.
+    __shared__ __align__(16) Slot ring[2];
+    __shared__ __align__(16) OP sS[(D / 32) * NB * WAVE * 8];  // S^T as B fragments (kb, row block)
+    __shared__ __align__(16) OP sU[2 * NB * WAVE * 8];         // diag(s) U as B fragments (kk, row block)
+    __shared__ __align__(16) char sO[CHUNK * RS * OB];         // the block's 64 x RS outputs, row-major
     // Workgroups are dispatched round-robin over the 8 XCDs (blockIdx % 8).
     // The SLICES workgroups of one (sequence, v-head) unit are placed on the
     // same XCD, so they share each block record through that XCD's L2.
@@ -632,7 +684,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void chunk_scan_kernel(
     const int n = unit / h_v, h = unit - n * h_v;
     const int tid = threadIdx.x, w = tid / WAVE, lane = tid % WAVE;
     const int j16 = lane & 15, q4 = lane >> 4;
-    const int r0 = slice * 32, cb0 = r0 / 16;
+    const int r0 = slice * RS, cb0 = r0 / 16;
     int begin, len, slot0;
     if (info) {
         const SeqInfo si = info[n];
@@ -641,29 +693,50 @@ __global__ __launch_bounds__(SCAN_THREADS) void chunk_scan_kernel(
         begin = 0; len = T; slot0 = 0;
     }
     const int nchunks = (len + CHUNK - 1) / CHUNK;
+    const int hk = h / (h_v / h_k);
     auto rec_of = [&](int c) { return recs + ((size_t)(slot0 + c) * h_v + h) * R::BYTES; };
+    auto krec_of = [&](int c) { return krecs + ((size_t)(slot0 + c) * h_k + hk) * KeyRec<D, OP>::BYTES; };
 
     if (w >= SCAN_COMPUTE_WAVES) {
         // ------------------------------ loader waves ------------------------------
-        // Block c + 2 goes into slot c % 2 once block c is done (after B2 of c);
-        // before B1 of c + 1 the wave waits for its copy of block c + 1 only.
+        constexpr int F = Sh::PER_WAVE, H = Sh::FIRST;
+        constexpr int LPR = RS * OB / 16;  // 16-byte pieces per output row
+        constexpr int PIECES = CHUNK * LPR;
+        constexpr int LT = SCAN_LOADER_WAVES * WAVE;
         const int lw = w - SCAN_COMPUTE_WAVES;
         if (nchunks == 0) return;
-        Dma::copy(rec_of(0), L.buf[0], lw, lane, cb0);
+        scan_copy<D, OP, RS, 0, F>(rec_of(0), krec_of(0), &ring[0], lw, lane, cb0);
         if (nchunks > 1) {
-            Dma::copy(rec_of(1), L.buf[1], lw, lane, cb0);
-            wait_vmcnt<Dma::PER_WAVE>();
+            scan_copy<D, OP, RS, 0, F>(rec_of(1), krec_of(1), &ring[1], lw, lane, cb0);
+            wait_vmcnt<F>();
         } else {
             wait_vmcnt<0>();
         }
-        __syncthreads();  // P: block 0 is in LDS
         for (int c = 0; c < nchunks; ++c) {
-            __syncthreads();  // B1
-            __syncthreads();  // B2: slot c % 2 is free
+            loader_barrier();  // B1: block c is in slot c % 2
+            if (c >= 1 && c + 1 < nchunks) scan_copy<D, OP, RS, H, F>(rec_of(c + 1), krec_of(c + 1), &ring[(c + 1) & 1], lw, lane, cb0);
+            loader_barrier();  // B2: slot c % 2 is free; the outputs of block c are in sO
+            // outputs: 16 bytes per lane, rows past the block's end go to the sink
+            const int tok0 = begin + c * CHUNK, nt = min(CHUNK, len - c * CHUNK);
+#pragma unroll
+            for (int i = 0; i < (PIECES + LT - 1) / LT; ++i) {
+                const int p = i * LT + lw * WAVE + lane;
+                if (PIECES % LT == 0 || p < PIECES) {
+                    const int row = p / LPR, col16 = p % LPR;
+                    const uint4 val = *reinterpret_cast<const uint4*>(sO + row * RS * OB + col16 * 16);
+                    char* dst = row < nt ? reinterpret_cast<char*>(out) +
+                                               (((size_t)(tok0 + row) * h_v + h) * D + r0) * OB + col16 * 16
+                                         : sink + lane * 16;
+                    *reinterpret_cast<uint4*>(dst) = val;
+                }
+            }
+            // Loads complete in issue order, so once no more than H operations
+            // are outstanding, every load issued before the last H has landed:
+            // all of block c + 1.
             if (c + 2 < nchunks) {
-                Dma::copy(rec_of(c + 2), L.buf[c & 1], lw, lane, cb0);
-                wait_vmcnt<Dma::PER_WAVE>();
-            } else {
+                scan_copy<D, OP, RS, 0, H>(rec_of(c + 2), krec_of(c + 2), &ring[c & 1], lw, lane, cb0);
+                wait_vmcnt<H>();
+            } else if (c + 1 < nchunks) {
                 wait_vmcnt<0>();
             }
         }
@@ -671,89 +744,90 @@ __global__ __launch_bounds__(SCAN_THREADS) void chunk_scan_kernel(
     }
 
     // ------------------------------ compute waves ------------------------------
-    const int tb = w & 3, nbA = w >> 2;  // phase A tile
-    // S^T tiles owned in phase B: number w*TPW + t -> (mb, nb) = (number / 2, number % 2);
+    const int which = w >> 2, tb = w & 3;  // phase A: U (which 0) or O (which 1), token block tb
+    // S^T tiles owned in phase B: number w*TPW + i -> (mb, nb) = (number / NB, number % NB);
     // lane (j, q) holds S[r0 + 16nb + j][16 mb + 4q + 0..3]
     f4_t St[TPW];
     const size_t sbase = (size_t)unit * D * D;
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-        const int mb = (w * TPW + t) >> 1, nb = (w * TPW + t) & 1;
+    for (int i = 0; i < TPW; ++i) {
+        const int t = w * TPW + i, mb = t / NB, nb = t % NB;
+        if (t >= Sh::NTB) break;
         if (state_in) {
             const float4 x = *reinterpret_cast<const float4*>(
                 state_in + sbase + (size_t)(r0 + 16 * nb + j16) * D + 16 * mb + 4 * q4);
-            St[t] = f4_t{x.x, x.y, x.z, x.w};
+            St[i] = f4_t{x.x, x.y, x.z, x.w};
         } else {
-            St[t] = f4_t{0, 0, 0, 0};
+            St[i] = f4_t{0, 0, 0, 0};
         }
-        store_part<OP>(L.sS, (mb / 2) * 2 + nb, mb % 2, lane, St[t]);
+        store_part<OP>(sS, (mb / 2) * NB + nb, mb % 2, lane, St[i]);
     }
-    constexpr int OB = OUT_BF16 ? 2 : 4;  // bytes per output element
-    if (nchunks > 0) __syncthreads();     // P
     for (int c = 0; c < nchunks; ++c) {
-        __syncthreads();  // B1: block c in LDS; S^T fragments complete; sU, sO free
-        const typename Lds::Buf& B = L.buf[c & 1];
-        const OP* Wb = B.frag;
-        const OP* Qb = B.frag + CHUNK * D;
+        __syncthreads();  // B1: block c in its slot; S^T fragments complete; sU and sO free
+        const Slot& B = ring[c & 1];
+        const OP* Ab = B.frag + which * CHUNK * D;  // -W or Qt
         const OP* Kb = B.frag + 2 * CHUNK * D;
-        f4_t accU = *reinterpret_cast<const f4_t*>(&B.uo[((0 * 4 + tb) * 2 + nbA) * WAVE * 4 + lane * 4]);
-        f4_t accO = *reinterpret_cast<const f4_t*>(&B.uo[((1 * 4 + tb) * 2 + nbA) * WAVE * 4 + lane * 4]);
+        f4_t acc[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const OP* u = &B.uo[(((which * NB + nb) * 4 + tb) * WAVE + lane) * 4];
+            if constexpr (sizeof(OP) == 2) {
+                typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+                const h4_t x = *reinterpret_cast<const h4_t*>(u);
+                acc[nb] = f4_t{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+            } else {
+                acc[nb] = *reinterpret_cast<const f4_t*>(u);
+            }
+        }
 #pragma unroll
         for (int kb = 0; kb < D / 32; ++kb) {
-            const Frag<OP> bs = frag_stored<OP>(L.sS, kb * 2 + nbA, lane);
-            mma(accU, frag_stored<OP>(Wb, tb * (D / 32) + kb, lane), bs);
-            mma(accO, frag_stored<OP>(Qb, tb * (D / 32) + kb, lane), bs);
+            const Frag<OP> a = frag_stored<OP>(Ab, tb * (D / 32) + kb, lane);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) mma(acc[nb], a, frag_stored<OP>(sS, kb * NB + nb, lane));
         }
         Frag<OP> kf[TPW][2];
 #pragma unroll
-        for (int t = 0; t < TPW; ++t)
+        for (int i = 0; i < TPW; ++i) {
+            const int mb = (w * TPW + i) / NB;
+            if (w * TPW + i >= Sh::NTB) break;
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) kf[t][kk] = frag_stored<OP>(Kb, ((w * TPW + t) >> 1) * 2 + kk, lane);
-        const f4_t sv = *reinterpret_cast<const f4_t*>(&B.sg[16 * tb + 4 * q4]);
-        const float gn = B.sg[CHUNK];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int e = (16 * tb + 4 * q4 + r) * 32 + 16 * nbA + j16;
-            if constexpr (OUT_BF16) reinterpret_cast<uint16_t*>(L.sO)[e] = f32_to_bf16(accO[r]);
-            else reinterpret_cast<float*>(L.sO)[e] = accO[r];
+            for (int kk = 0; kk < 2; ++kk) kf[i][kk] = frag_stored<OP>(Kb, mb * 2 + kk, lane);
         }
-        {
-            f4_t us;
+        const float gn = B.sg[CHUNK];
+        if (which == 0) {
+            const f4_t sv = *reinterpret_cast<const f4_t*>(&B.sg[16 * tb + 4 * q4]);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) us[r] = accU[r] * sv[r];
-            store_part<OP>(L.sU, (tb / 2) * 2 + nbA, tb % 2, lane, us);
+            for (int nb = 0; nb < NB; ++nb) store_part<OP>(sU, (tb / 2) * NB + nb, tb % 2, lane, acc[nb] * sv);
+        } else {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int e = (16 * tb + 4 * q4 + r) * RS + 16 * nb + j16;
+                    if constexpr (OUT_BF16) reinterpret_cast<uint16_t*>(sO)[e] = f32_to_bf16(acc[nb][r]);
+                    else reinterpret_cast<float*>(sO)[e] = acc[nb][r];
+                }
         }
         __syncthreads();  // B2: diag(s) U and the outputs complete; S^T fragments and slot c % 2 no longer read
         // phase B: S^T <- gamma_n S^T + K^T diag(s) U
 #pragma unroll
-        for (int t = 0; t < TPW; ++t) {
-            const int mb = (w * TPW + t) >> 1, nb = (w * TPW + t) & 1;
-            St[t] *= gn;
+        for (int i = 0; i < TPW; ++i) {
+            const int t = w * TPW + i, mb = t / NB, nb = t % NB;
+            if (t >= Sh::NTB) break;
+            St[i] *= gn;
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) mma(St[t], kf[t][kk], frag_stored<OP>(L.sU, kk * 2 + nb, lane));
-            store_part<OP>(L.sS, (mb / 2) * 2 + nb, mb % 2, lane, St[t]);
-        }
-        // outputs: 16 bytes per lane, rows past the block's end go to the sink
-        {
-            constexpr int LPR = 32 * OB / 16;  // lanes per output row
-            const int tok0 = begin + c * CHUNK, nt = min(CHUNK, len - c * CHUNK);
-            for (int idx = tid; idx < CHUNK * LPR; idx += SCAN_COMPUTE_WAVES * WAVE) {
-                const int row = idx / LPR, col16 = idx % LPR;
-                const uint4 val = *reinterpret_cast<const uint4*>(L.sO + row * 32 * OB + col16 * 16);
-                char* dst = (row < nt) ? reinterpret_cast<char*>(out) +
-                                             (((size_t)(tok0 + row) * h_v + h) * D + r0) * OB + col16 * 16
-                                       : sink + lane * 16;
-                *reinterpret_cast<uint4*>(dst) = val;
-            }
+            for (int kk = 0; kk < 2; ++kk) mma(St[i], kf[i][kk], frag_stored<OP>(sU, kk * NB + nb, lane));
+            store_part<OP>(sS, (mb / 2) * NB + nb, mb % 2, lane, St[i]);
         }
     }
 
     if (state_out) {
 #pragma unroll
-        for (int t = 0; t < TPW; ++t) {
-            const int mb = (w * TPW + t) >> 1, nb = (w * TPW + t) & 1;
+        for (int i = 0; i < TPW; ++i) {
+            const int t = w * TPW + i, mb = t / NB, nb = t % NB;
+            if (t >= Sh::NTB) break;
             *reinterpret_cast<float4*>(state_out + sbase + (size_t)(r0 + 16 * nb + j16) * D + 16 * mb + 4 * q4) =
-                make_float4(St[t][0], St[t][1], St[t][2], St[t][3]);
+                make_float4(St[i][0], St[i][1], St[i][2], St[i][3]);
         }
     }
 }
@@ -762,6 +836,11 @@ __global__ __launch_bounds__(SCAN_THREADS) void chunk_scan_kernel(
 size_t prefill_record_bytes(int d, bool in_bf16) {
     if (d == 128) return in_bf16 ? Rec<128, _Float16>::BYTES : Rec<128, float>::BYTES;
     return in_bf16 ? Rec<64, _Float16>::BYTES : Rec<64, float>::BYTES;
+}
+
+size_t prefill_key_record_bytes(int d, bool in_bf16) {
+    if (d == 128) return in_bf16 ? KeyRec<128, _Float16>::BYTES : KeyRec<128, float>::BYTES;
+    return in_bf16 ? KeyRec<64, _Float16>::BYTES : KeyRec<64, float>::BYTES;
 }
 
 hipError_t launch_plan(const int32_t* cu, int N, int T, int max_slots, void* info, int32_t* slot_seq,
@@ -775,7 +854,7 @@ template <int D, typename OP, bool IB>
 static hipError_t launch_prep_t(const void* q, const void* k, const void* v, const float* g,
                                 const float* beta, const void* info, const int32_t* slot_seq,
                                 int slots, int T, int h_k, int h_v, int l2norm, float scale,
-                                char* recs, hipStream_t stream) {
+                                char* recs, char* krecs, hipStream_t stream) {
     constexpr size_t lds = prep_lds_bytes<D, OP>();
     static_assert(lds <= 160 * 1024, "chunk_prep LDS budget");
     auto kern = chunk_prep_kernel<D, OP, IB>;
@@ -783,46 +862,71 @@ static hipError_t launch_prep_t(const void* q, const void* k, const void* v, con
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(slots * h_v), dim3(PREP_THREADS), lds, stream, q, k, v, g, beta,
-                       reinterpret_cast<const SeqInfo*>(info), slot_seq, T, h_k, h_v, l2norm, scale, recs);
+                       reinterpret_cast<const SeqInfo*>(info), slot_seq, T, h_k, h_v, l2norm, scale, recs, krecs);
     return hipGetLastError();
 }
 
 hipError_t launch_prep(int d, bool in_bf16, const void* q, const void* k, const void* v,
                        const float* g, const float* beta, const void* info, const int32_t* slot_seq,
                        int slots, int T, int h_k, int h_v, int l2norm, float scale, void* recs,
-                       hipStream_t stream) {
+                       void* krecs, hipStream_t stream) {
     char* r = reinterpret_cast<char*>(recs);
+    char* kr = reinterpret_cast<char*>(krecs);
     if (d == 128 && in_bf16)
-        return launch_prep_t<128, _Float16, true>(q, k, v, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, stream);
+        return launch_prep_t<128, _Float16, true>(q, k, v, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, kr, stream);
     if (d == 64 && in_bf16)
-        return launch_prep_t<64, _Float16, true>(q, k, v, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, stream);
+        return launch_prep_t<64, _Float16, true>(q, k, v, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, kr, stream);
     if (d == 64 && !in_bf16)
-        return launch_prep_t<64, float, false>(q, k, v, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, stream);
+        return launch_prep_t<64, float, false>(q, k, v, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, kr, stream);
     return hipErrorInvalidValue;
 }
 
-template <int D, typename OP, bool OB>
-static hipError_t launch_scan_t(const void* recs, const void* info, const float* s_in, float* s_out,
-                                void* out, void* sink, int units, int T, int h_v, hipStream_t stream) {
-    constexpr size_t lds = scan_lds_bytes<D, OP, OB>();
-    static_assert(lds <= 160 * 1024, "chunk_scan LDS budget");
-    auto kern = chunk_scan_kernel<D, OP, OB>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
+template <int D, typename OP, bool OB, int RS>
+static hipError_t launch_scan_t(const void* recs, const void* krecs, const void* info, const float* s_in,
+                                float* s_out, void* out, void* sink, int units, int T, int h_k, int h_v,
+                                hipStream_t stream) {
+    static_assert(scan_lds_bytes<D, OP, OB, RS>() <= 160 * 1024, "chunk_scan LDS budget");
     const int groups = (units + 7) / 8;  // see the XCD placement in chunk_scan_kernel
-    hipLaunchKernelGGL(kern, dim3(groups * 8 * (D / 32)), dim3(SCAN_THREADS), lds, stream,
-                       reinterpret_cast<const char*>(recs), reinterpret_cast<const SeqInfo*>(info), s_in,
-                       s_out, out, reinterpret_cast<char*>(sink), units, T, h_v);
+    hipLaunchKernelGGL((chunk_scan_kernel<D, OP, OB, RS>), dim3(groups * 8 * (D / RS)), dim3(SCAN_THREADS), 0,
+                       stream, reinterpret_cast<const char*>(recs), reinterpret_cast<const char*>(krecs),
+                       reinterpret_cast<const SeqInfo*>(info), s_in, s_out, out, reinterpret_cast<char*>(sink), units,
+                       T, h_k, h_v);
     return hipGetLastError();
 }
 
-hipError_t launch_scan(int d, bool in_bf16, bool out_bf16, const void* recs, const void* info,
-                       const float* s_in, float* s_out, void* out, void* sink, int units, int T, int h_v,
+// Compute units of the current device (cached per device).
+static int compute_units() {
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] <= 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+int scan_rows_per_workgroup(int d, int units) {
+    // GDN_SCAN_ROWS=16 or 32 fixes the choice (tuning and tests).
+    if (const char* e = getenv("GDN_SCAN_ROWS")) {
+        const int v = atoi(e);
+        if (v == 16 || v == 32) return v;
+    }
+    // 16-row slices double the workgroups (each still copies the whole -W,
+    // Qt, K^T record part), which pays while 32-row slices leave compute
+    // units idle.
+    return (long long)units * (d / 32) < compute_units() ? 16 : 32;
+}
+
+hipError_t launch_scan(int d, bool in_bf16, bool out_bf16, const void* recs, const void* krecs, const void* info,
+                       const float* s_in, float* s_out, void* out, void* sink, int units, int T, int h_k, int h_v,
                        hipStream_t stream) {
-#define GDN_SCAN(D, OP, IB, OB)                                                                   \
-    if (d == D && in_bf16 == IB && out_bf16 == OB)                                                \
-        return launch_scan_t<D, OP, OB>(recs, info, s_in, s_out, out, sink, units, T, h_v, stream);
+    const int rs = scan_rows_per_workgroup(d, units);
+#define GDN_SCAN(D, OP, IB, OB)                                                                          \
+    if (d == D && in_bf16 == IB && out_bf16 == OB)                                                       \
+        return rs == 16 ? launch_scan_t<D, OP, OB, 16>(recs, krecs, info, s_in, s_out, out, sink, units, T, h_k, h_v, stream) \
+                        : launch_scan_t<D, OP, OB, 32>(recs, krecs, info, s_in, s_out, out, sink, units, T, h_k, h_v, stream);
     GDN_SCAN(128, _Float16, true, true) GDN_SCAN(128, _Float16, true, false)
     GDN_SCAN(64, _Float16, true, true) GDN_SCAN(64, _Float16, true, false)
     GDN_SCAN(64, float, false, true) GDN_SCAN(64, float, false, false)

@@ -63,18 +63,22 @@ def desc(**kw):
 
 
 def test_workspace_bytes(L):
-    # 64 blocks x 32 v-heads x record; record = 3 fp16 fragment sets + fp32 Ut, Ot + 512 B
-    rec = 3 * 64 * 128 * 2 + 2 * 64 * 128 * 4 + 256 + 256
+    # per (block, v-head): -W, Qt, Ut, Ot in fp16 + s_t / gamma_n (512 B);
+    # per (block, k-head): K^T in fp16.  64 blocks x (32 v-heads, 16 k-heads).
+    rec = 4 * 64 * 128 * 2 + 256 + 256
+    key = 64 * 128 * 2
     plan = (1024 + 1 * 16 + 64 * 4 + 255) // 256 * 256
-    assert gdn.gdn_prefill_workspace_bytes(desc()) == plan + 64 * 32 * rec
+    assert gdn.gdn_prefill_workspace_bytes(desc()) == plan + 64 * (32 * rec + 16 * key)
     # packed sequences: at most T/64 + N blocks in total
     n = gdn.gdn_prefill_workspace_bytes(desc(num_seqs=16, total_tokens=1000))
     slots = (1000 + 16 * 63) // 64
-    assert n == (1024 + 16 * 16 + slots * 4 + 255) // 256 * 256 + slots * 32 * rec
-    rec64f = 3 * 64 * 64 * 4 + 2 * 64 * 64 * 4 + 512
+    assert n == (1024 + 16 * 16 + slots * 4 + 255) // 256 * 256 + slots * (32 * rec + 16 * key)
+    # fp32 inputs keep fp32 operands
+    rec64f = 4 * 64 * 64 * 4 + 512
+    key64f = 64 * 64 * 4
     assert gdn.gdn_prefill_workspace_bytes(desc(total_tokens=256, h_k=1, h_v=1, d=64,
                                                 io_dtype=gdn.GDN_F32, out_dtype=gdn.GDN_F32)) == \
-        1280 + 4 * rec64f
+        1280 + 4 * (rec64f + key64f)
     assert L.gdn_prefill_workspace_bytes(ctypes.byref(desc()), 32) == 0
     assert "chunk" in gdn.last_error()
 

@@ -127,6 +127,40 @@ def test_prefill_128k_workload_sampled():
         assert eo <= 2e-3 and es <= 2e-3
 
 
+# ---- row slices of the state ------------------------------------------------------------------
+
+ROW_CASES = [  # (d, io dtype, out dtype, lengths)
+    (64, inputs.F32, inputs.F32, [257]),
+    (64, inputs.F32, inputs.BF16, [1, 130]),
+    (64, inputs.BF16, inputs.F32, [200, 0, 65]),
+    (128, inputs.BF16, inputs.F32, [333]),
+    (128, inputs.BF16, inputs.BF16, [64, 190, 1]),
+]
+
+
+@pytest.mark.parametrize("case", range(len(ROW_CASES)))
+def test_row_slices_16_and_32_agree(case, monkeypatch):
+    """The scan splits each state over workgroups of 16 or 32 rows (chosen by
+    occupancy).  Each 16 x 16 tile is computed the same way in both, so the
+    results agree bitwise, and both meet the oracle bound."""
+    d, io, od, lens = ROW_CASES[case]
+    x = inputs.prefill_inputs(seed=40 + case, lengths=lens, h_k=2, h_v=4, d=d, io_dtype=io, state_std=0.2)
+    res = {}
+    for rows in ("16", "32"):
+        monkeypatch.setenv("GDN_SCAN_ROWS", rows)
+        res[rows] = run_gpu(x, od)
+    monkeypatch.delenv("GDN_SCAN_ROWS")
+    assert torch.equal(res["16"][0], res["32"][0]) and torch.equal(res["16"][1], res["32"][1])
+    ro, rs = run_oracle(x)
+    tol = 1e-5 if io == inputs.F32 else 2e-3
+    out, st = res["16"]
+    if od == inputs.F32:
+        assert normwise(host(out), ro) <= tol
+    else:
+        check_bf16_out(host(out), ro, tol)
+    assert normwise(host(st), rs) <= tol
+
+
 # ---- invariants through the GPU path -------------------------------------------------------
 
 def test_split_run_equals_one_call():
