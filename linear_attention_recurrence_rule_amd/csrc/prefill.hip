@@ -27,7 +27,8 @@
 // to the matrix cores.  Their L2 norms become fp32 row factors c_t.  Values
 // enter as fp16 (exact for bf16 in range).  fp32 intermediates that feed the
 // matrix cores are rounded to fp16 (bf16 inputs) or stay fp32 (fp32 inputs).
-// Ut and Ot stay fp32 in the workspace.
+// Ut and Ot are stored in the operand type too; they only seed the scan's
+// fp32 accumulators.
 #include "gdn_device.h"
 
 #include <stdlib.h>
