@@ -142,6 +142,7 @@ struct PrepLds {
     OP t[CHUNK * LT];  // T = X diag(beta)
     OP p[CHUNK * LT];  // P = lower_incl(D o Q K^T)
     float G[CHUNK], ck[CHUNK], cq[CHUNK], bt[CHUNK], gck[CHUNK], gcq[CHUNK];
+    int zero;  // holds 0 (see chunk_prep_kernel)
 };
 
 template <int D, typename OP>
@@ -201,343 +202,444 @@ __device__ __forceinline__ void store4(OP* dst, const f4_t& x) {
 constexpr int PREP_THREADS = 512;
 constexpr int PREP_WAVES = PREP_THREADS / WAVE;
 
-// The block-form work of one (block, v-head) that does not depend on the
-// carried state, written as one record.  Called by a whole workgroup of
-// PREP_THREADS threads; tokens tok0 .. tok0 + nt - 1 (1 <= nt <= 64) of v-head h.
-template <int D, typename OP, bool IN_BF16>
-__device__ __forceinline__ void prep_block(const void* __restrict__ q, const void* __restrict__ k,
-                                           const void* __restrict__ v, const float* __restrict__ g,
-                                           const float* __restrict__ beta, int tok0, int nt, int h, int T,
-                                           int h_k, int h_v, int l2norm, float scale, char* __restrict__ rec,
-                                           char* __restrict__ krec_bytes, PrepLds<D, OP>& L) {
-    using RC = Rec<D, OP>;
-    constexpr int LK = PrepLds<D, OP>::LK, LT = PrepLds<D, OP>::LT;
-    constexpr int PER_TOK = D / 8, NIT = CHUNK * PER_TOK / PREP_THREADS, W16 = IN_BF16 ? 1 : 2, ES = IN_BF16 ? 2 : 4;
-    const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
-    const int li = lane & 15, lq = lane >> 4;
-    const int hk = h / (h_v / h_k);
-
-    // ---- 0. issue every input load (token indices clamped; data past nt zeroed on use) ----
-    uint4 rq[NIT][W16], rk[NIT][W16], rv[NIT][W16];
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-        const int idx = tid + PREP_THREADS * it, t = idx / PER_TOK, pc = idx % PER_TOK;
-        const size_t tok = (size_t)min(tok0 + t, T - 1);
-        const char* pq = reinterpret_cast<const char*>(q) + ((tok * h_k + hk) * D + 8 * pc) * ES;
-        const char* pk = reinterpret_cast<const char*>(k) + ((tok * h_k + hk) * D + 8 * pc) * ES;
-        const char* pv = reinterpret_cast<const char*>(v) + ((tok * h_v + h) * D + 8 * pc) * ES;
-#pragma unroll
-        for (int w = 0; w < W16; ++w) {
-            rq[it][w] = reinterpret_cast<const uint4*>(pq)[w];
-            rk[it][w] = reinterpret_cast<const uint4*>(pk)[w];
-            rv[it][w] = reinterpret_cast<const uint4*>(pv)[w];
-        }
-    }
-    const size_t tg = (size_t)min(tok0 + lane, T - 1) * h_v + h;
-    const float rg = g[tg], rb = beta[tg];
-
-    // ---- 1. per-token power-of-two scaling and norms; q, k to LDS (row-major) ---------------
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-        const int idx = tid + PREP_THREADS * it, t = idx / PER_TOK, pc = idx % PER_TOK;
-        const bool live = t < nt;
-        float kx[8], qx[8];
-        unpack8<IN_BF16>(rk[it], kx);
-        unpack8<IN_BF16>(rq[it], qx);
-        float mk = 0.f, mq = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            if (!live) { kx[e] = 0.f; qx[e] = 0.f; }
-            mk = fmaxf(mk, fabsf(kx[e]));
-            mq = fmaxf(mq, fabsf(qx[e]));
-        }
-        mk = group_max<PER_TOK>(mk);  // the PER_TOK lanes of a token are adjacent
-        mq = group_max<PER_TOK>(mq);
-        int ek = 0, eq = 0;
-        frexpf(mk, &ek);
-        frexpf(mq, &eq);
-        float ssk = 0.f, ssq = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            kx[e] = ldexpf(kx[e], -ek);  // exact; representable in OP for bf16 inputs
-            qx[e] = ldexpf(qx[e], -eq);
-            ssk += kx[e] * kx[e];
-            ssq += qx[e] * qx[e];
-        }
-        ssk = group_sum<PER_TOK>(ssk);
-        ssq = group_sum<PER_TOK>(ssq);
-        store8<OP>(L.k + t * LK + 8 * pc, kx);
-        store8<OP>(L.q + t * LK + 8 * pc, qx);
-        if (pc == 0) {
-            L.ck[t] = live ? norm_factor(ssk, ek, l2norm, 1.0f) : 0.f;
-            L.cq[t] = live ? norm_factor(ssq, eq, l2norm, scale) : 0.f;
-        }
-    }
-    float gam = 0.f;
-    if (wave == 0) {
-        const bool live = lane < nt;
-        float gx = live ? rg : 0.f;
-#pragma unroll
-        for (int off = 1; off < WAVE; off <<= 1) {
-            const float o = __shfl_up(gx, off, WAVE);
-            if (lane >= off) gx += o;
-        }
-        L.G[lane] = gx;
-        L.bt[lane] = live ? rb : 0.f;
-        gam = __expf(gx);
-    }
-    __syncthreads();
-    if (wave == 0) {
-        L.gck[lane] = gam * L.ck[lane];
-        L.gcq[lane] = gam * L.cq[lane];
-    }
-
-    // ---- 2. decay-masked Gram products: A (fp32, strictly lower) and P ----------------------
-    // 20 tile-products (10 lower 16x16 tiles of K K^T and of Q K^T) over the waves.
-    for (int tp = wave; tp < 20; tp += PREP_WAVES) {
-        const int tl = tp >> 1, isq = tp & 1;
-        const int mb = (tl >= 6) ? 3 : (tl >= 3) ? 2 : (tl >= 1) ? 1 : 0;
-        const int nb = tl - mb * (mb + 1) / 2;
-        const OP* rows = isq ? L.q : L.k;
-        f4_t acc = {0, 0, 0, 0};
-#pragma unroll
-        for (int kb = 0; kb < D / 32; ++kb)
-            mma(acc, frag_rowmajor<OP>(rows, LK, mb, kb, lane), frag_rowmajor<OP>(L.k, LK, nb, kb, lane));
-        const int j = 16 * nb + li, i0 = 16 * mb + 4 * lq;
-        const float Gj = L.G[j], ckj = L.ck[j];
-        const f4_t Gi = *reinterpret_cast<const f4_t*>(&L.G[i0]);
-        if (!isq) {
-            const f4_t cki = *reinterpret_cast<const f4_t*>(&L.ck[i0]);
-            const f4_t bti = *reinterpret_cast<const f4_t*>(&L.bt[i0]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = i0 + r;
-                if (j < i) L.b.ax[i * LDF + j] = bti[r] * __expf(Gi[r] - Gj) * acc[r] * cki[r] * ckj;
-            }
-        } else {
-            const f4_t cqi = *reinterpret_cast<const f4_t*>(&L.cq[i0]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = i0 + r;
-                const float dec = (j <= i) ? __expf(fminf(Gi[r] - Gj, 0.f)) : 0.f;
-                L.p[i * LT + j] = (OP)(dec * acc[r] * cqi[r] * ckj);
-            }
-        }
-    }
-    for (int tl = wave; tl < 6; tl += PREP_WAVES) {  // strictly-upper tiles of P are zero
-        const int nb = (tl >= 3) ? 3 : (tl >= 1) ? 2 : 1;
-        const int mb = tl - (nb - 1) * nb / 2;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) L.p[(16 * mb + 4 * lq + r) * LT + 16 * nb + li] = (OP)0.f;
-    }
-    __syncthreads();
-
-    // ---- 3. X = (I + A)^{-1}, kept transposed in the upper triangle of b.ax -----------------
-    // Diagonal 16x16 blocks by substitution (wave w, lane c < 16 owns column c of block w);
-    // X_ij = -X_ii sum_{m=j}^{i-1} A_im X_mj by block distance (fp32 matrix cores).
-    OP* krec = reinterpret_cast<OP*>(krec_bytes);
-    if (wave >= 4) {  // the scan's K^T fragments, while waves 0..3 solve the diagonal blocks
-        for (int f = wave - 4; krec && f < (D / 16) * 2; f += PREP_WAVES - 4)
-            frag_store<OP>(krec, f, lane, frag_colmajor<OP>(L.k, LK, f / 2, f % 2, lane));
-    } else if (lane < 16) {
-        const int bb = wave;
-        float x[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float* arow = &L.b.ax[(16 * bb + i) * LDF + 16 * bb];
-            float acc = (i == lane) ? 1.f : 0.f;
-#pragma unroll
-            for (int jj = 0; jj < i; ++jj) acc -= arow[jj] * x[jj];
-            x[i] = acc;
-        }
-        // X[16bb + i][16bb + lane] for i >= lane, stored at [16bb + lane][16bb + i]
-#pragma unroll
-        for (int i4 = 0; i4 < 16; i4 += 4)
-            *reinterpret_cast<f4_t*>(&L.b.ax[(16 * bb + lane) * LDF + 16 * bb + i4]) =
-                f4_t{i4 + 0 >= lane ? x[i4 + 0] : 0.f, i4 + 1 >= lane ? x[i4 + 1] : 0.f,
-                     i4 + 2 >= lane ? x[i4 + 2] : 0.f, i4 + 3 >= lane ? x[i4 + 3] : 0.f};
-    }
-    __syncthreads();
-    for (int dist = 1; dist < 4; ++dist) {
-        const int i = wave + dist, j = wave;
-        if (i < 4) {
-            f4_t acc = {0, 0, 0, 0};
-            for (int m = j; m < i; ++m) {
-                // A_im (lower, row-major) as the A operand; X_mj (stored transposed) as the B operand
-                const f4_t av = *reinterpret_cast<const f4_t*>(&L.b.ax[(16 * i + li) * LDF + 16 * m + 4 * lq]);
-                const f4_t xv = *reinterpret_cast<const f4_t*>(&L.b.ax[(16 * j + li) * LDF + 16 * m + 4 * lq]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], xv[e], acc, 0, 0, 0);
-            }
-            // res = -X_ii acc: A operand X_ii[li][4q + e] stored at [16i + 4q + e][16i + li]
-            f4_t res = {0, 0, 0, 0};
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                res = __builtin_amdgcn_mfma_f32_16x16x4f32(-L.b.ax[(16 * i + 4 * lq + e) * LDF + 16 * i + li], acc[e], res,
-                                                          0, 0, 0);
-            // lane (c, q): X[16i + 4q + r][16j + c] -> stored at [16j + c][16i + 4q + r]
-            *reinterpret_cast<f4_t*>(&L.b.ax[(16 * j + li) * LDF + 16 * i + 4 * lq]) = res;
-        }
-        __syncthreads();
-    }
-    // T = X diag(beta): T[i][j] = X[i][j] beta_j for i >= j (X_ij at [j][i]), else 0
-    for (int idx = tid; idx < CHUNK * CHUNK / 4; idx += PREP_THREADS) {
-        const int jj = idx / (CHUNK / 4), i4 = 4 * (idx % (CHUNK / 4));
-        const f4_t xv = *reinterpret_cast<const f4_t*>(&L.b.ax[jj * LDF + i4]);
-        const float bj = L.bt[jj];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) L.t[(i4 + r) * LT + jj] = (OP)((i4 + r >= jj) ? xv[r] * bj : 0.f);
-    }
-    __syncthreads();
-
-    // ---- 4. values to LDS (region b) -------------------------------------------------------
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-        const int idx = tid + PREP_THREADS * it, t = idx / PER_TOK, pc = idx % PER_TOK;
-        float vx[8];
-        unpack8<IN_BF16>(rv[it], vx);
-        if (t >= nt) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) vx[e] = 0.f;
-        }
-        store8<OP>(L.b.v + t * LK + 8 * pc, vx);
-    }
-    __syncthreads();
-
-    // ---- 5. Ut = T V and Ot = P Ut (fp32 accumulator tiles) --------------------------------
-    OP* urec = reinterpret_cast<OP*>(rec + RC::U);
-    OP* orec = reinterpret_cast<OP*>(rec + RC::O);
-    for (int nb = wave; nb < D / 16; nb += PREP_WAVES) {
-        const Frag<OP> fv0 = frag_colmajor<OP>(L.b.v, LK, nb, 0, lane);
-        const Frag<OP> fv1 = frag_colmajor<OP>(L.b.v, LK, nb, 1, lane);
-        f4_t ut[4];
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-            ut[mb] = f4_t{0, 0, 0, 0};
-            mma(ut[mb], frag_rowmajor<OP>(L.t, LT, mb, 0, lane), fv0);
-            mma(ut[mb], frag_rowmajor<OP>(L.t, LT, mb, 1, lane), fv1);
-            store4<OP>(urec + ((size_t)(nb * 4 + mb) * WAVE + lane) * 4, ut[mb]);
-        }
-        const Frag<OP> fu0 = frag_from_acc<OP>(ut[0], ut[1]);
-        const Frag<OP> fu1 = frag_from_acc<OP>(ut[2], ut[3]);
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-            f4_t ot = {0, 0, 0, 0};
-            mma(ot, frag_rowmajor<OP>(L.p, LT, mb, 0, lane), fu0);
-            mma(ot, frag_rowmajor<OP>(L.p, LT, mb, 1, lane), fu1);
-            store4<OP>(orec + ((size_t)(nb * 4 + mb) * WAVE + lane) * 4, ot);
-        }
-    }
-    __syncthreads();  // the values are no longer read
-
-    // ---- 6. W^T = (diag(gam c) K)^T T^T: the scan's -W fragments, and -W row-major in LDS -----
-    // Units (kb, tb): d-blocks 2kb, 2kb+1 and token block tb; a wave's units share kb for d = 128.
-    OP* wrec = reinterpret_cast<OP*>(rec + RC::W);
-    OP* qrec = reinterpret_cast<OP*>(rec + RC::Q);
-    constexpr int UPW = (D / 32) * 4 / PREP_WAVES;  // units per wave
-    {
-        int cur_kb = -1;
-        Frag<OP> aw[2][2];
-        for (int uu = 0; uu < UPW; ++uu) {
-            const int unit = wave * UPW + uu, kb = unit / 4, tb = unit % 4;
-            if (kb != cur_kb) {
-                cur_kb = kb;
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-                    for (int kk = 0; kk < 2; ++kk) {
-                        Frag<OP> f = frag_colmajor<OP>(L.k, LK, 2 * kb + s2, kk, lane);
-#pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            frag_set(f, e, frag_get(f, e) * L.gck[32 * kk + 4 * lq + (e & 3) + 16 * (e >> 2)]);
-                        aw[s2][kk] = f;
-                    }
-            }
-            f4_t acc[2];
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                acc[s2] = f4_t{0, 0, 0, 0};
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) mma(acc[s2], aw[s2][kk], frag_rowmajor<OP>(L.t, LT, tb, kk, lane));
-            }
-            // lane (j, q): acc[s2][r] = W[token 16tb + j][d 16(2kb + s2) + 4q + r]
-            Frag<OP> fw;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) { frag_set(fw, e, -acc[0][e]); frag_set(fw, e + 4, -acc[1][e]); }
-            frag_store<OP>(wrec, tb * (D / 32) + kb, lane, fw);
-            const int tok = 16 * tb + li;
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) store4<OP>(L.b.w + tok * LK + 16 * (2 * kb + s2) + 4 * lq, -acc[s2]);
-        }
-    }
-    __syncthreads();  // -W complete in LDS
-
-    // ---- 7. Qt^T = (diag(gam cq) Q)^T + (-W)^T P^T: the scan's Qt fragments ----------------
-    {
-        int cur_kb = -1;
-        Frag<OP> aw[2][2];
-        for (int uu = 0; uu < UPW; ++uu) {
-            const int unit = wave * UPW + uu, kb = unit / 4, tb = unit % 4;
-            if (kb != cur_kb) {
-                cur_kb = kb;
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-                    for (int kk = 0; kk < 2; ++kk) aw[s2][kk] = frag_colmajor<OP>(L.b.w, LK, 2 * kb + s2, kk, lane);
-            }
-            const int tok = 16 * tb + li;
-            const float gq = L.gcq[tok];
-            f4_t acc[2];
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                const OP* qr = L.q + tok * LK + 16 * (2 * kb + s2) + 4 * lq;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc[s2][r] = (float)qr[r] * gq;
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) mma(acc[s2], aw[s2][kk], frag_rowmajor<OP>(L.p, LT, tb, kk, lane));
-            }
-            Frag<OP> fq;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) { frag_set(fq, e, acc[0][e]); frag_set(fq, e + 4, acc[1][e]); }
-            frag_store<OP>(qrec, tb * (D / 32) + kb, lane, fq);
-        }
-    }
-
-    // ---- 8. s_t = exp(G_n - G_t) c_t and gamma_n -------------------------------------------
-    if (tid < CHUNK) {
-        const float Gn = L.G[max(nt - 1, 0)];
-        reinterpret_cast<float*>(rec + RC::S)[tid] = (tid < nt) ? __expf(Gn - L.G[tid]) * L.ck[tid] : 0.f;
-        if (tid == 0) reinterpret_cast<float*>(rec + RC::M)[0] = __expf(Gn);
-    }
+// Workgroup barrier that orders LDS accesses only: each wave waits for its own
+// LDS operations, not for its global stores or loads in flight (a workgroup
+// release fence would wait for those too).  The signal fences keep the
+// compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// One workgroup per (block slot, v-head).
+// C + X Y for 16x16 fp32 matrices, X^T and Y (and C) in accumulator layout:
+// lane (j, q) holds M[4q + r][j] in element r.  Instruction e contracts over
+// k = 4q + e, taking X[i][4q + e] = X^T[4q + e][i] and Y[4q + e][j].
+__device__ __forceinline__ f4_t mm16(const f4_t& xt, const f4_t& y, f4_t c) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(xt[e], y[e], c, 0, 0, 0);
+    return c;
+}
+
+// One thread's share of a block's raw inputs for one (k-head, v-head).
+template <int D, bool IN_BF16>
+struct PrepIn {
+    static constexpr int PER_TOK = D / 8, NIT = CHUNK * PER_TOK / PREP_THREADS, W16 = IN_BF16 ? 1 : 2;
+    static constexpr int ES = IN_BF16 ? 2 : 4;  // bytes per input element
+    uint4 q[NIT][W16], k[NIT][W16], v[NIT][W16];
+    float g, b;
+
+    // Token indices are clamped into [0, T); data past a block's end is zeroed on use.
+    __device__ __forceinline__ void load_qk(const void* qp, const void* kp, int tok0, int T, int h_k, int hk) {
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int idx = threadIdx.x + PREP_THREADS * it, t = idx / PER_TOK, pc = idx % PER_TOK;
+            const size_t off = (((size_t)min(tok0 + t, T - 1) * h_k + hk) * D + 8 * pc) * ES;
+#pragma unroll
+            for (int w = 0; w < W16; ++w) {
+                q[it][w] = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(qp) + off)[w];
+                k[it][w] = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(kp) + off)[w];
+            }
+        }
+    }
+    __device__ __forceinline__ void load_v(const void* vp, int tok0, int T, int h_v, int h) {
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int idx = threadIdx.x + PREP_THREADS * it, t = idx / PER_TOK, pc = idx % PER_TOK;
+            const size_t off = (((size_t)min(tok0 + t, T - 1) * h_v + h) * D + 8 * pc) * ES;
+#pragma unroll
+            for (int w = 0; w < W16; ++w)
+                v[it][w] = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(vp) + off)[w];
+        }
+    }
+    __device__ __forceinline__ void load_gb(const float* gp, const float* bp, int tok0, int T, int h_v, int h) {
+        const size_t tg = (size_t)min(tok0 + (int)(threadIdx.x % WAVE), T - 1) * h_v + h;
+        g = gp[tg];
+        b = bp[tg];
+    }
+};
+
+// The block-form work that does not depend on the carried state, for
+// (block, v-head) tasks.  A workgroup of PREP_THREADS threads takes a run of
+// (block slot, k-head) items and, per item, the k-head's v-heads in turn: the
+// queries and keys are scaled once per item, the K^T fragments are written
+// once per item, and each v-head's work is written as one record.  The next
+// task's inputs are loaded into registers as soon as the current ones have
+// been consumed, so their latency is hidden behind the current task.
+// Waves per SIMD the LDS allows (two workgroups per CU when they fit), as a register budget.
+template <int D, typename OP>
+constexpr int prep_min_waves() { return 2 * prep_lds_bytes<D, OP>() <= 160 * 1024 ? 4 : 2; }
+
 template <int D, typename OP, bool IN_BF16>
-__global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
+__global__ __launch_bounds__(PREP_THREADS, (prep_min_waves<D, OP>())) void chunk_prep_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const SeqInfo* __restrict__ info,
     const int32_t* __restrict__ slot_seq, int T, int h_k, int h_v, int l2norm, float scale,
-    char* __restrict__ recs, char* __restrict__ krecs) {
+    char* __restrict__ recs, char* __restrict__ krecs, int slots, int items_per_wg) {
+    using RC = Rec<D, OP>;
+    using In = PrepIn<D, IN_BF16>;
+    constexpr int LK = PrepLds<D, OP>::LK, LT = PrepLds<D, OP>::LT;
+    constexpr int PER_TOK = In::PER_TOK, NIT = In::NIT;
     extern __shared__ __align__(16) char smem_raw[];
     PrepLds<D, OP>& L = *reinterpret_cast<PrepLds<D, OP>*>(smem_raw);
-    const int slot = blockIdx.x / h_v, h = blockIdx.x - slot * h_v;
+    const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
+    const int li = lane & 15, lq = lane >> 4;
+    const int ratio = h_v / h_k;
+    const int items = slots * h_k;
+    const int i0 = blockIdx.x * items_per_wg, i1 = min(items, i0 + items_per_wg);
+    if (i0 >= i1) return;
+    // token range of a block slot; false for an unused slot of packed sequences
+    auto slot_range = [&](int slot, int& tok0, int& nt) {
+        if (slot_seq) {
+            const int n = slot_seq[slot];
+            if (n < 0) { tok0 = 0; nt = 0; return false; }
+            const SeqInfo si = info[n];
+            const int j = slot - si.slot_base;
+            tok0 = si.begin + j * CHUNK;
+            nt = min(CHUNK, si.len - j * CHUNK);
+        } else {
+            tok0 = slot * CHUNK;
+            nt = min(CHUNK, T - tok0);
+        }
+        return true;
+    };
+
+    if (tid == 0) L.zero = 0;
+    lds_barrier();
+    In in;
     int tok0, nt;
-    if (slot_seq) {
-        const int n = slot_seq[slot];
-        if (n < 0) return;
-        const SeqInfo si = info[n];
-        const int j = slot - si.slot_base;
-        tok0 = si.begin + j * CHUNK;
-        nt = min(CHUNK, si.len - j * CHUNK);
-    } else {
-        tok0 = slot * CHUNK;
-        nt = min(CHUNK, T - tok0);
+    bool live = slot_range(i0 / h_k, tok0, nt);
+    in.load_qk(q, k, tok0, T, h_k, i0 % h_k);
+    in.load_v(v, tok0, T, h_v, (i0 % h_k) * ratio);
+    in.load_gb(g, beta, tok0, T, h_v, (i0 % h_k) * ratio);
+    for (int item = i0; item < i1; ++item) {
+        const int slot = item / h_k, hk = item % h_k;
+        const int ctok0 = tok0, cnt = nt;
+        const bool clive = live;
+        int ntok0 = 0, nnt = 0;
+        const bool more = item + 1 < i1;
+        const bool nlive = more && slot_range((item + 1) / h_k, ntok0, nnt);
+
+        // ---- 1. per-token power-of-two scaling and norms; q, k to LDS (row-major) -----------
+        if (clive) {
+#pragma unroll
+            for (int it = 0; it < NIT; ++it) {
+                const int idx = tid + PREP_THREADS * it, t = idx / PER_TOK, pc = idx % PER_TOK;
+                const bool tl = t < cnt;
+                float kx[8], qx[8];
+                unpack8<IN_BF16>(in.k[it], kx);
+                unpack8<IN_BF16>(in.q[it], qx);
+                float mk = 0.f, mq = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    if (!tl) { kx[e] = 0.f; qx[e] = 0.f; }
+                    mk = fmaxf(mk, fabsf(kx[e]));
+                    mq = fmaxf(mq, fabsf(qx[e]));
+                }
+                mk = group_max<PER_TOK>(mk);  // the PER_TOK lanes of a token are adjacent
+                mq = group_max<PER_TOK>(mq);
+                int ek = 0, eq = 0;
+                frexpf(mk, &ek);
+                frexpf(mq, &eq);
+                float ssk = 0.f, ssq = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    kx[e] = ldexpf(kx[e], -ek);  // exact; representable in OP for bf16 inputs
+                    qx[e] = ldexpf(qx[e], -eq);
+                    ssk += kx[e] * kx[e];
+                    ssq += qx[e] * qx[e];
+                }
+                ssk = group_sum<PER_TOK>(ssk);
+                ssq = group_sum<PER_TOK>(ssq);
+                store8<OP>(L.k + t * LK + 8 * pc, kx);
+                store8<OP>(L.q + t * LK + 8 * pc, qx);
+                if (pc == 0) {
+                    L.ck[t] = tl ? norm_factor(ssk, ek, l2norm, 1.0f) : 0.f;
+                    L.cq[t] = tl ? norm_factor(ssq, eq, l2norm, scale) : 0.f;
+                }
+            }
+        }
+        if (more) in.load_qk(q, k, ntok0, T, h_k, (item + 1) % h_k);
+
+        for (int jv = 0; jv < ratio; ++jv) {
+            // Lane indices re-derived through a volatile LDS read of 0.  Otherwise the
+            // compiler hoists the task's per-lane LDS address arithmetic out of the
+            // loops and keeps ~90 more registers live (wave stays uniform).
+            const int tid = threadIdx.x + *reinterpret_cast<volatile int*>(&L.zero);
+            const int lane = tid % WAVE, li = lane & 15, lq = lane >> 4;
+            const int h = hk * ratio + jv;
+            // the next task: this item's next v-head, or the next item's first
+            const bool nxt = jv + 1 < ratio || more;
+            const int nx_tok0 = jv + 1 < ratio ? ctok0 : ntok0;
+            const int nx_h = jv + 1 < ratio ? h + 1 : ((item + 1) % h_k) * ratio;
+            if (!clive) {
+                if (nxt) {
+                    in.load_gb(g, beta, nx_tok0, T, h_v, nx_h);
+                    in.load_v(v, nx_tok0, T, h_v, nx_h);
+                }
+                continue;
+            }
+            char* rec = recs + ((size_t)slot * h_v + h) * RC::BYTES;
+            // the first v-head of each k-head writes the k-head's key record
+            OP* krec = jv == 0 ? reinterpret_cast<OP*>(krecs + ((size_t)slot * h_k + hk) * KeyRec<D, OP>::BYTES)
+                               : nullptr;
+
+            // ---- 1b. cumulative log-decay G, gamma = exp(G), beta ---------------------------
+            float gam = 0.f;
+            if (wave == 0) {
+                const bool tl = lane < cnt;
+                float gx = tl ? in.g : 0.f;
+#pragma unroll
+                for (int off = 1; off < WAVE; off <<= 1) {
+                    const float o = __shfl_up(gx, off, WAVE);
+                    if (lane >= off) gx += o;
+                }
+                L.G[lane] = gx;
+                L.bt[lane] = tl ? in.b : 0.f;
+                gam = __expf(gx);
+            }
+            if (nxt) in.load_gb(g, beta, nx_tok0, T, h_v, nx_h);
+            lds_barrier();
+            if (wave == 0) {
+                L.gck[lane] = gam * L.ck[lane];
+                L.gcq[lane] = gam * L.cq[lane];
+            }
+
+            // ---- 2. decay-masked Gram products: A (fp32, strictly lower) and P ----------------------
+            // 20 tile-products (10 lower 16x16 tiles of K K^T and of Q K^T) over the waves.
+            for (int tp = wave; tp < 20; tp += PREP_WAVES) {
+                const int tl = tp >> 1, isq = tp & 1;
+                const int mb = (tl >= 6) ? 3 : (tl >= 3) ? 2 : (tl >= 1) ? 1 : 0;
+                const int nb = tl - mb * (mb + 1) / 2;
+                const OP* rows = isq ? L.q : L.k;
+                f4_t acc = {0, 0, 0, 0};
+#pragma unroll
+                for (int kb = 0; kb < D / 32; ++kb)
+                    mma(acc, frag_rowmajor<OP>(rows, LK, mb, kb, lane), frag_rowmajor<OP>(L.k, LK, nb, kb, lane));
+                const int j = 16 * nb + li, i0 = 16 * mb + 4 * lq;
+                const float Gj = L.G[j], ckj = L.ck[j];
+                const f4_t Gi = *reinterpret_cast<const f4_t*>(&L.G[i0]);
+                if (!isq) {
+                    const f4_t cki = *reinterpret_cast<const f4_t*>(&L.ck[i0]);
+                    const f4_t bti = *reinterpret_cast<const f4_t*>(&L.bt[i0]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = i0 + r;
+                        if (j < i) L.b.ax[i * LDF + j] = bti[r] * __expf(Gi[r] - Gj) * acc[r] * cki[r] * ckj;
+                    }
+                } else {
+                    const f4_t cqi = *reinterpret_cast<const f4_t*>(&L.cq[i0]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = i0 + r;
+                        const float dec = (j <= i) ? __expf(fminf(Gi[r] - Gj, 0.f)) : 0.f;
+                        L.p[i * LT + j] = (OP)(dec * acc[r] * cqi[r] * ckj);
+                    }
+                }
+            }
+            for (int tl = wave; tl < 6; tl += PREP_WAVES) {  // strictly-upper tiles of P are zero
+                const int nb = (tl >= 3) ? 3 : (tl >= 1) ? 2 : 1;
+                const int mb = tl - (nb - 1) * nb / 2;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) L.p[(16 * mb + 4 * lq + r) * LT + 16 * nb + li] = (OP)0.f;
+            }
+            lds_barrier();
+
+            // ---- 3. X = (I + A)^{-1}, kept transposed in the upper triangle of b.ax -----------------
+            // Diagonal 16x16 blocks by substitution (wave w, lane c < 16 owns column c of block w);
+            // X_ij = -X_ii sum_{m=j}^{i-1} A_im X_mj by block distance (fp32 matrix cores).
+            if (wave >= 4) {  // the scan's K^T fragments, while waves 0..3 solve the diagonal blocks
+                for (int f = wave - 4; krec && f < (D / 16) * 2; f += PREP_WAVES - 4)
+                    frag_store<OP>(krec, f, lane, frag_colmajor<OP>(L.k, LK, f / 2, f % 2, lane));
+            } else {
+                // Diagonal block bb: X_bb = (I + N)^{-1} for the strictly lower 16x16 N, as the
+                // exact product (I - N)(I + N^2)(I + N^4)(I + N^8) (N^16 = 0), in fp32 matrix-core
+                // products held in registers.  Each matrix is kept with its transpose: C = X Y
+                // takes X^T and Y in accumulator layout (see mm16).
+                const int bb = wave;
+                const float* blk = &L.b.ax[(16 * bb) * LDF + 16 * bb];
+                const f4_t rowv = *reinterpret_cast<const f4_t*>(&blk[li * LDF + 4 * lq]);
+                f4_t n, nt, eye;  // lane (j, q) element r: N[4q + r][j], N^T[4q + r][j], I
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 4 * lq + r;
+                    n[r] = row > li ? blk[row * LDF + li] : 0.f;  // entries on and above the diagonal are stale
+                    nt[r] = li > row ? rowv[r] : 0.f;
+                    eye[r] = row == li ? 1.f : 0.f;
+                }
+                const f4_t z = {0, 0, 0, 0};
+                const f4_t n2 = mm16(nt, n, z), n2t = mm16(n, nt, z);
+                const f4_t n4 = mm16(n2t, n2, z), n4t = mm16(n2, n2t, z);
+                const f4_t n8 = mm16(n4t, n4, z);
+                const f4_t m = eye - n, mt = eye - nt;
+                const f4_t p1 = mm16(mt, n2, m), p1t = mm16(n2, mt, mt);
+                const f4_t p2 = mm16(p1t, n4, p1), p2t = mm16(n4, p1t, p1t);
+                const f4_t x = mm16(p2t, n8, p2);
+                // lane (j, q) holds X[4q + r][j] (zero above the diagonal); X_ij is stored at [j][i]
+                *reinterpret_cast<f4_t*>(&L.b.ax[(16 * bb + li) * LDF + 16 * bb + 4 * lq]) = x;
+            }
+            lds_barrier();
+            for (int dist = 1; dist < 4; ++dist) {
+                const int i = wave + dist, j = wave;
+                if (i < 4) {
+                    f4_t acc = {0, 0, 0, 0};
+                    for (int m = j; m < i; ++m) {
+                        // A_im (lower, row-major) as the A operand; X_mj (stored transposed) as the B operand
+                        const f4_t av = *reinterpret_cast<const f4_t*>(&L.b.ax[(16 * i + li) * LDF + 16 * m + 4 * lq]);
+                        const f4_t xv = *reinterpret_cast<const f4_t*>(&L.b.ax[(16 * j + li) * LDF + 16 * m + 4 * lq]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], xv[e], acc, 0, 0, 0);
+                    }
+                    // res = -X_ii acc: A operand X_ii[li][4q + e] stored at [16i + 4q + e][16i + li]
+                    f4_t res = {0, 0, 0, 0};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        res = __builtin_amdgcn_mfma_f32_16x16x4f32(-L.b.ax[(16 * i + 4 * lq + e) * LDF + 16 * i + li], acc[e], res,
+                                                                  0, 0, 0);
+                    // lane (c, q): X[16i + 4q + r][16j + c] -> stored at [16j + c][16i + 4q + r]
+                    *reinterpret_cast<f4_t*>(&L.b.ax[(16 * j + li) * LDF + 16 * i + 4 * lq]) = res;
+                }
+                lds_barrier();
+            }
+            // T = X diag(beta): T[i][j] = X[i][j] beta_j for i >= j (X_ij at [j][i]), else 0
+            for (int idx = tid; idx < CHUNK * CHUNK / 4; idx += PREP_THREADS) {
+                const int jj = idx / (CHUNK / 4), i4 = 4 * (idx % (CHUNK / 4));
+                const f4_t xv = *reinterpret_cast<const f4_t*>(&L.b.ax[jj * LDF + i4]);
+                const float bj = L.bt[jj];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) L.t[(i4 + r) * LT + jj] = (OP)((i4 + r >= jj) ? xv[r] * bj : 0.f);
+            }
+            lds_barrier();
+
+
+            // ---- 4. values to LDS (region b) ---------------------------------------------------
+#pragma unroll
+            for (int it = 0; it < NIT; ++it) {
+                const int idx = tid + PREP_THREADS * it, t = idx / PER_TOK, pc = idx % PER_TOK;
+                float vx[8];
+                unpack8<IN_BF16>(in.v[it], vx);
+                if (t >= cnt) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) vx[e] = 0.f;
+                }
+                store8<OP>(L.b.v + t * LK + 8 * pc, vx);
+            }
+            if (nxt) in.load_v(v, nx_tok0, T, h_v, nx_h);
+            lds_barrier();
+
+            // ---- 5. Ut = T V and Ot = P Ut (fp32 accumulator tiles) --------------------------------
+            OP* urec = reinterpret_cast<OP*>(rec + RC::U);
+            OP* orec = reinterpret_cast<OP*>(rec + RC::O);
+            for (int nb = wave; nb < D / 16; nb += PREP_WAVES) {
+                const Frag<OP> fv0 = frag_colmajor<OP>(L.b.v, LK, nb, 0, lane);
+                const Frag<OP> fv1 = frag_colmajor<OP>(L.b.v, LK, nb, 1, lane);
+                f4_t ut[4];
+#pragma unroll
+                for (int mb = 0; mb < 4; ++mb) {
+                    ut[mb] = f4_t{0, 0, 0, 0};
+                    mma(ut[mb], frag_rowmajor<OP>(L.t, LT, mb, 0, lane), fv0);
+                    mma(ut[mb], frag_rowmajor<OP>(L.t, LT, mb, 1, lane), fv1);
+                    store4<OP>(urec + ((size_t)(nb * 4 + mb) * WAVE + lane) * 4, ut[mb]);
+                }
+                const Frag<OP> fu0 = frag_from_acc<OP>(ut[0], ut[1]);
+                const Frag<OP> fu1 = frag_from_acc<OP>(ut[2], ut[3]);
+#pragma unroll
+                for (int mb = 0; mb < 4; ++mb) {
+                    f4_t ot = {0, 0, 0, 0};
+                    mma(ot, frag_rowmajor<OP>(L.p, LT, mb, 0, lane), fu0);
+                    mma(ot, frag_rowmajor<OP>(L.p, LT, mb, 1, lane), fu1);
+                    store4<OP>(orec + ((size_t)(nb * 4 + mb) * WAVE + lane) * 4, ot);
+                }
+            }
+            lds_barrier();  // the values are no longer read
+
+            // ---- 6. W^T = (diag(gam c) K)^T T^T: the scan's -W fragments, and -W row-major in LDS -----
+            // Units (kb, tb): d-blocks 2kb, 2kb+1 and token block tb; a wave's units share kb for d = 128.
+            OP* wrec = reinterpret_cast<OP*>(rec + RC::W);
+            OP* qrec = reinterpret_cast<OP*>(rec + RC::Q);
+            constexpr int UPW = (D / 32) * 4 / PREP_WAVES;  // units per wave
+            {
+                int cur_kb = -1;
+                Frag<OP> aw[2][2];
+                for (int uu = 0; uu < UPW; ++uu) {
+                    const int unit = wave * UPW + uu, kb = unit / 4, tb = unit % 4;
+                    if (kb != cur_kb) {
+                        cur_kb = kb;
+#pragma unroll
+                        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                            for (int kk = 0; kk < 2; ++kk) {
+                                Frag<OP> f = frag_colmajor<OP>(L.k, LK, 2 * kb + s2, kk, lane);
+#pragma unroll
+                                for (int e = 0; e < 8; ++e)
+                                    frag_set(f, e, frag_get(f, e) * L.gck[32 * kk + 4 * lq + (e & 3) + 16 * (e >> 2)]);
+                                aw[s2][kk] = f;
+                            }
+                    }
+                    f4_t acc[2];
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2) {
+                        acc[s2] = f4_t{0, 0, 0, 0};
+#pragma unroll
+                        for (int kk = 0; kk < 2; ++kk) mma(acc[s2], aw[s2][kk], frag_rowmajor<OP>(L.t, LT, tb, kk, lane));
+                    }
+                    // lane (j, q): acc[s2][r] = W[token 16tb + j][d 16(2kb + s2) + 4q + r]
+                    Frag<OP> fw;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) { frag_set(fw, e, -acc[0][e]); frag_set(fw, e + 4, -acc[1][e]); }
+                    frag_store<OP>(wrec, tb * (D / 32) + kb, lane, fw);
+                    const int tok = 16 * tb + li;
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2) store4<OP>(L.b.w + tok * LK + 16 * (2 * kb + s2) + 4 * lq, -acc[s2]);
+                }
+            }
+            lds_barrier();  // -W complete in LDS
+
+            // ---- 7. Qt^T = (diag(gam cq) Q)^T + (-W)^T P^T: the scan's Qt fragments ----------------
+            {
+                int cur_kb = -1;
+                Frag<OP> aw[2][2];
+                for (int uu = 0; uu < UPW; ++uu) {
+                    const int unit = wave * UPW + uu, kb = unit / 4, tb = unit % 4;
+                    if (kb != cur_kb) {
+                        cur_kb = kb;
+#pragma unroll
+                        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                            for (int kk = 0; kk < 2; ++kk) aw[s2][kk] = frag_colmajor<OP>(L.b.w, LK, 2 * kb + s2, kk, lane);
+                    }
+                    const int tok = 16 * tb + li;
+                    const float gq = L.gcq[tok];
+                    f4_t acc[2];
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2) {
+                        const OP* qr = L.q + tok * LK + 16 * (2 * kb + s2) + 4 * lq;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) acc[s2][r] = (float)qr[r] * gq;
+#pragma unroll
+                        for (int kk = 0; kk < 2; ++kk) mma(acc[s2], aw[s2][kk], frag_rowmajor<OP>(L.p, LT, tb, kk, lane));
+                    }
+                    Frag<OP> fq;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) { frag_set(fq, e, acc[0][e]); frag_set(fq, e + 4, acc[1][e]); }
+                    frag_store<OP>(qrec, tb * (D / 32) + kb, lane, fq);
+                }
+            }
+
+            // ---- 8. s_t = exp(G_n - G_t) c_t and gamma_n -------------------------------------------
+            if (tid < CHUNK) {
+                const float Gn = L.G[max(cnt - 1, 0)];
+                reinterpret_cast<float*>(rec + RC::S)[tid] = (tid < cnt) ? __expf(Gn - L.G[tid]) * L.ck[tid] : 0.f;
+                if (tid == 0) reinterpret_cast<float*>(rec + RC::M)[0] = __expf(Gn);
+            }
+
+            lds_barrier();  // LDS is reused by the next task
+        }
+        tok0 = ntok0;
+        nt = nnt;
+        live = nlive;
     }
-    // the first v-head of each k-head writes the k-head's key record
-    const int r = h_v / h_k;
-    char* krec = (h % r == 0) ? krecs + ((size_t)slot * h_k + h / r) * KeyRec<D, OP>::BYTES : nullptr;
-    prep_block<D, OP, IN_BF16>(q, k, v, g, beta, tok0, nt, h, T, h_k, h_v, l2norm, scale,
-                               recs + (size_t)blockIdx.x * Rec<D, OP>::BYTES, krec, L);
 }
 
 // ---- sequential phase -------------------------------------------------------------------
@@ -614,17 +716,6 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Barrier for the loader waves.  A workgroup-scope release fence would make
-// them wait for every direct load still in flight (those write LDS), so they
-// wait for their own LDS reads only.  The signal fences keep the compiler from
-// moving LDS accesses across the barrier.
-__device__ __forceinline__ void loader_barrier() {
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 // Loads I0..I1-1 of one loader wave's share of copying a block into a ring
@@ -714,9 +805,9 @@ __global__ __launch_bounds__(SCAN_THREADS) void chunk_scan_kernel(
             wait_vmcnt<0>();
         }
         for (int c = 0; c < nchunks; ++c) {
-            loader_barrier();  // B1: block c is in slot c % 2
+            lds_barrier();  // B1: block c is in slot c % 2
             if (c >= 1 && c + 1 < nchunks) scan_copy<D, OP, RS, H, F>(rec_of(c + 1), krec_of(c + 1), &ring[(c + 1) & 1], lw, lane, cb0);
-            loader_barrier();  // B2: slot c % 2 is free; the outputs of block c are in sO
+            lds_barrier();  // B2: slot c % 2 is free; the outputs of block c are in sO
             // outputs: 16 bytes per lane, rows past the block's end go to the sink
             const int tok0 = begin + c * CHUNK, nt = min(CHUNK, len - c * CHUNK);
 #pragma unroll
@@ -851,6 +942,19 @@ hipError_t launch_plan(const int32_t* cu, int N, int T, int max_slots, void* inf
     return hipGetLastError();
 }
 
+// Compute units of the current device (cached per device).
+static int compute_units() {
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] <= 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 template <int D, typename OP, bool IB>
 static hipError_t launch_prep_t(const void* q, const void* k, const void* v, const float* g,
                                 const float* beta, const void* info, const int32_t* slot_seq,
@@ -862,8 +966,14 @@ static hipError_t launch_prep_t(const void* q, const void* k, const void* v, con
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(slots * h_v), dim3(PREP_THREADS), lds, stream, q, k, v, g, beta,
-                       reinterpret_cast<const SeqInfo*>(info), slot_seq, T, h_k, h_v, l2norm, scale, recs, krecs);
+    // One run of (block slot, k-head) items per resident workgroup.
+    constexpr int per_cu = 2 * lds <= 160 * 1024 ? 2 : 1;
+    const int items = slots * h_k, resident = per_cu * compute_units();
+    const int per = (items + resident - 1) / resident;
+    const int grid = (items + per - 1) / per;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(PREP_THREADS), lds, stream, q, k, v, g, beta,
+                       reinterpret_cast<const SeqInfo*>(info), slot_seq, T, h_k, h_v, l2norm, scale, recs, krecs,
+                       slots, per);
     return hipGetLastError();
 }
 
@@ -893,19 +1003,6 @@ static hipError_t launch_scan_t(const void* recs, const void* krecs, const void*
                        reinterpret_cast<const SeqInfo*>(info), s_in, s_out, out, reinterpret_cast<char*>(sink), units,
                        T, h_k, h_v);
     return hipGetLastError();
-}
-
-// Compute units of the current device (cached per device).
-static int compute_units() {
-    static int cached[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] <= 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cached[dev] = n;
-    }
-    return cached[dev];
 }
 
 int scan_rows_per_workgroup(int d, int units) {
