@@ -159,6 +159,31 @@ gdn_status gdn_decode_step(const gdn_desc *desc,
                            float *state, void *out, void *stream);
 
 /*
+ * One decode step over a pool of states, for a serving loop that keeps one
+ * state per live request and steps any subset of them together.  It is
+ * gdn_decode_step with one indirection: sequence n reads and updates, in
+ * place, slot state_slots[n] of
+ *
+ *   state_pool   fp32 [num_slots, h_v, d_v, d_k] (device; caller-owned),
+ *   state_slots  int32 [num_seqs] (device; caller-owned).
+ *
+ * The section "Decode: minimise bytes moved per token" counts each state
+ * read and written once per token; the indirection adds none.  Each slot
+ * index is read on the device.  A slot outside [0, num_slots) skips its
+ * sequence: that state is not touched and the sequence's output rows are
+ * written as zeros.  Two sequences naming the same slot race (the result is
+ * undefined; nothing faults).  Other arguments, shapes and errors are those of
+ * gdn_decode_step, plus GDN_ERR_INVALID_ARGUMENT for num_slots < 1 or a NULL
+ * state_pool or state_slots.
+ */
+gdn_status gdn_decode_step_slots(const gdn_desc *desc,
+                                 const void *q, const void *k, const void *v,
+                                 const float *g, const float *beta,
+                                 float *state_pool, int32_t num_slots,
+                                 const int32_t *state_slots,
+                                 void *out, void *stream);
+
+/*
  * Bounded-memory prefill of one long sequence (num_seqs == 1, no
  * cu_seqlens): the tokens run through gdn_prefill in consecutive segments of
  * `segment_tokens` (a positive multiple of chunk), each starting from the

@@ -13,9 +13,9 @@
 
 namespace gdn {
 hipError_t launch_decode(int d, bool in_bf16, bool out_bf16, const void* q, const void* k,
-                         const void* v, const float* g, const float* beta, float* state, void* out,
-                         int units, int h_k, int h_v, int l2norm, float scale, int grid,
-                         hipStream_t stream);
+                         const void* v, const float* g, const float* beta, float* state, const int32_t* slots,
+                         int num_slots, void* out, int units, int h_k, int h_v, int l2norm, float scale,
+                         int grid, hipStream_t stream);
 size_t prefill_record_bytes(int d, bool in_bf16);
 size_t prefill_key_record_bytes(int d, bool in_bf16);
 hipError_t launch_direct(int d, bool in_bf16, bool out_bf16, const void* q, const void* k, const void* v,
@@ -288,6 +288,34 @@ gdn_status segment_plan(const gdn_desc* desc, int32_t chunk, int64_t seg, gdn_de
     return GDN_OK;
 }
 
+// Shared by gdn_decode_step (slots == NULL: sequence n uses state n) and
+// gdn_decode_step_slots.
+gdn_status decode_call(const gdn_desc* desc, const void* q, const void* k, const void* v, const float* g,
+                       const float* beta, float* state, int32_t num_slots, const int32_t* slots, void* out,
+                       void* stream) {
+    const int N = desc->num_seqs, hk = desc->h_k, hv = desc->h_v, d = desc->d_k;
+    const size_t io = dtype_size(desc->io_dtype), os = dtype_size(desc->out_dtype);
+    const Span spans[] = {
+        {(const char*)q, (size_t)N * hk * d * io, "q"},
+        {(const char*)k, (size_t)N * hk * d * io, "k"},
+        {(const char*)v, (size_t)N * hv * d * io, "v"},
+        {(const char*)g, (size_t)N * hv * 4, "g"},
+        {(const char*)beta, (size_t)N * hv * 4, "beta"},
+        {(const char*)out, (size_t)N * hv * d * os, "out"},
+        {(const char*)state, (size_t)num_slots * hv * d * d * 4, "state"},
+        {(const char*)slots, slots ? (size_t)N * 4 : 0, "state_slots"},
+    };
+    gdn_status st = check_align(spans, sizeof(spans) / sizeof(spans[0]));
+    if (st != GDN_OK) return st;
+    st = check_overlaps(spans, sizeof(spans) / sizeof(spans[0]), nullptr, nullptr);
+    if (st != GDN_OK) return st;
+    hipError_t e = gdn::launch_decode(d, desc->io_dtype == GDN_BF16, desc->out_dtype == GDN_BF16, q, k, v, g,
+                                      beta, state, slots, num_slots, out, N * hv, hk, hv, desc->qk_l2norm,
+                                      desc->scale, decode_grid(N * hv), reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+    return GDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -425,26 +453,20 @@ gdn_status gdn_decode_step(const gdn_desc* desc, const void* q, const void* k, c
     if (st != GDN_OK) return st;
     if (!q || !k || !v || !g || !beta || !state || !out)
         return fail(GDN_ERR_INVALID_ARGUMENT, "q, k, v, g, beta, state and out must be non-NULL");
-    const int N = desc->num_seqs, hk = desc->h_k, hv = desc->h_v, d = desc->d_k;
-    const size_t io = dtype_size(desc->io_dtype), os = dtype_size(desc->out_dtype);
-    const Span spans[] = {
-        {(const char*)q, (size_t)N * hk * d * io, "q"},
-        {(const char*)k, (size_t)N * hk * d * io, "k"},
-        {(const char*)v, (size_t)N * hv * d * io, "v"},
-        {(const char*)g, (size_t)N * hv * 4, "g"},
-        {(const char*)beta, (size_t)N * hv * 4, "beta"},
-        {(const char*)out, (size_t)N * hv * d * os, "out"},
-        {(const char*)state, (size_t)N * hv * d * d * 4, "state"},
-    };
-    st = check_align(spans, sizeof(spans) / sizeof(spans[0]));
+    return decode_call(desc, q, k, v, g, beta, state, desc->num_seqs, nullptr, out, stream);
+}
+
+gdn_status gdn_decode_step_slots(const gdn_desc* desc, const void* q, const void* k, const void* v,
+                                 const float* g, const float* beta, float* state_pool, int32_t num_slots,
+                                 const int32_t* state_slots, void* out, void* stream) {
+    g_err[0] = 0;
+    gdn_status st = check_desc(desc, false);
     if (st != GDN_OK) return st;
-    st = check_overlaps(spans, sizeof(spans) / sizeof(spans[0]), nullptr, nullptr);
-    if (st != GDN_OK) return st;
-    hipError_t e = gdn::launch_decode(d, desc->io_dtype == GDN_BF16, desc->out_dtype == GDN_BF16, q, k, v, g,
-                                      beta, state, out, N * hv, hk, hv, desc->qk_l2norm, desc->scale,
-                                      decode_grid(N * hv), reinterpret_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return fail(GDN_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
-    return GDN_OK;
+    if (!q || !k || !v || !g || !beta || !state_pool || !state_slots || !out)
+        return fail(GDN_ERR_INVALID_ARGUMENT,
+                    "q, k, v, g, beta, state_pool, state_slots and out must be non-NULL");
+    if (num_slots < 1) return fail(GDN_ERR_INVALID_ARGUMENT, "num_slots must be >= 1 (got %d)", num_slots);
+    return decode_call(desc, q, k, v, g, beta, state_pool, num_slots, state_slots, out, stream);
 }
 
 }  // extern "C"

@@ -33,21 +33,28 @@ struct DecodeIn {
     float4 s[D / 8];  // this lane's state slices (D/8 = LPR/2 rows)
     float kx[4], qx[4];
     float v, g, b;
+    int slot;  // state slot of the unit's sequence; -1: skip the unit
 };
 
+// Sequence n's state is slot slots[n] of the state array (slot n when slots is
+// NULL); a slot outside [0, num_slots) skips the unit.
 template <int D, bool IN_BF16>
-__device__ __forceinline__ void decode_load(DecodeIn<D>& in, const float* __restrict__ state, const void* q,
+__device__ __forceinline__ void decode_load(DecodeIn<D>& in, const float* __restrict__ state,
+                                            const int32_t* __restrict__ slots, int num_slots, const void* q,
                                             const void* k, const void* v, const float* g, const float* beta,
                                             int unit, int h_k, int h_v, int wave, int lane) {
     constexpr int LPR = D / 4, RPI = WAVE / LPR, NL = LPR / 2;
     const int n = unit / h_v, h = unit - n * h_v;
     const int hk = h / (h_v / h_k);
     const int c = lane % LPR, sub = lane / LPR;
-    const float* S = state + (size_t)unit * D * D;
+    const int slot = slots ? slots[n] : n;
+    in.slot = (slot >= 0 && slot < num_slots) ? slot : -1;
+    const float* S = state + ((size_t)max(in.slot, 0) * h_v + h) * D * D;
 #pragma unroll
     for (int m = 0; m < NL; ++m) {
         const int row = wave * 32 + m * RPI + sub;
-        in.s[m] = *reinterpret_cast<const float4*>(S + (size_t)row * D + 4 * c);
+        in.s[m] = in.slot >= 0 ? *reinterpret_cast<const float4*>(S + (size_t)row * D + 4 * c)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     load4<IN_BF16>(k, ((size_t)n * h_k + hk) * D + 4 * c, in.kx);
     load4<IN_BF16>(q, ((size_t)n * h_k + hk) * D + 4 * c, in.qx);
@@ -138,9 +145,16 @@ __device__ __forceinline__ void state_store(const float4 (&sr)[D / 8], float* __
 
 template <int D, bool OUT_BF16>
 __device__ __forceinline__ void decode_compute(DecodeIn<D>& in, float* __restrict__ state, void* out, int unit,
-                                               int l2norm, float scale, int wave, int lane) {
+                                               int h_v, int l2norm, float scale, int wave, int lane) {
+    if (in.slot < 0) {  // skipped: zero outputs, state untouched
+        constexpr int LPR = D / 4, RPI = WAVE / LPR, NL = LPR / 2;
+        const int c = lane % LPR, sub = lane / LPR;
+        if (c >= NL) store1<OUT_BF16>(out, (size_t)unit * D + wave * 32 + (c - NL) * RPI + sub, 0.f);
+        return;
+    }
+    const int h = unit % h_v;
     decode_token<D, OUT_BF16>(in.s, in.kx, in.qx, in.v, in.g, in.b, out, (size_t)unit, l2norm, scale, wave, lane);
-    state_store<D>(in.s, state + (size_t)unit * D * D, wave, lane);
+    state_store<D>(in.s, state + ((size_t)in.slot * h_v + h) * D * D, wave, lane);
 }
 
 // Each workgroup walks units blockIdx.x, blockIdx.x + gridDim.x, ... with the
@@ -151,20 +165,21 @@ template <int D, bool IN_BF16, bool OUT_BF16>
 __global__ __launch_bounds__(2 * D) void decode_step_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ state,
-    void* __restrict__ out, int units, int h_k, int h_v, int l2norm, float scale) {
+    const int32_t* __restrict__ slots, int num_slots, void* __restrict__ out, int units, int h_k, int h_v,
+    int l2norm, float scale) {
     const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
     const int stride = gridDim.x, last = units - 1;
     int u = blockIdx.x;
     if (u > last) return;
     DecodeIn<D> A, B;
-    decode_load<D, IN_BF16>(A, state, q, k, v, g, beta, u, h_k, h_v, wave, lane);
+    decode_load<D, IN_BF16>(A, state, slots, num_slots, q, k, v, g, beta, u, h_k, h_v, wave, lane);
     for (;;) {
-        decode_load<D, IN_BF16>(B, state, q, k, v, g, beta, min(u + stride, last), h_k, h_v, wave, lane);
-        decode_compute<D, OUT_BF16>(A, state, out, u, l2norm, scale, wave, lane);
+        decode_load<D, IN_BF16>(B, state, slots, num_slots, q, k, v, g, beta, min(u + stride, last), h_k, h_v, wave, lane);
+        decode_compute<D, OUT_BF16>(A, state, out, u, h_v, l2norm, scale, wave, lane);
         u += stride;
         if (u > last) break;
-        decode_load<D, IN_BF16>(A, state, q, k, v, g, beta, min(u + stride, last), h_k, h_v, wave, lane);
-        decode_compute<D, OUT_BF16>(B, state, out, u, l2norm, scale, wave, lane);
+        decode_load<D, IN_BF16>(A, state, slots, num_slots, q, k, v, g, beta, min(u + stride, last), h_k, h_v, wave, lane);
+        decode_compute<D, OUT_BF16>(B, state, out, u, h_v, l2norm, scale, wave, lane);
         u += stride;
         if (u > last) break;
     }
@@ -260,22 +275,23 @@ hipError_t launch_direct(int d, bool in_bf16, bool out_bf16, const void* q, cons
 
 template <int D, bool IB, bool OB>
 static hipError_t launch_decode_t(const void* q, const void* k, const void* v, const float* g,
-                                  const float* beta, float* state, void* out, int units, int h_k,
-                                  int h_v, int l2norm, float scale, int grid, hipStream_t stream) {
+                                  const float* beta, float* state, const int32_t* slots, int num_slots,
+                                  void* out, int units, int h_k, int h_v, int l2norm, float scale, int grid,
+                                  hipStream_t stream) {
     hipLaunchKernelGGL((decode_step_kernel<D, IB, OB>), dim3(grid), dim3(2 * D), 0, stream, q, k, v,
-                       g, beta, state, out, units, h_k, h_v, l2norm, scale);
+                       g, beta, state, slots, num_slots, out, units, h_k, h_v, l2norm, scale);
     return hipGetLastError();
 }
 
 hipError_t launch_decode(int d, bool in_bf16, bool out_bf16, const void* q, const void* k,
-                         const void* v, const float* g, const float* beta, float* state, void* out,
-                         int units, int h_k, int h_v, int l2norm, float scale, int grid,
-                         hipStream_t stream) {
+                         const void* v, const float* g, const float* beta, float* state, const int32_t* slots,
+                         int num_slots, void* out, int units, int h_k, int h_v, int l2norm, float scale,
+                         int grid, hipStream_t stream) {
     if (grid < 1 || grid > units) grid = units;
 #define GDN_DEC(D, IB, OB)                                                                        \
     if (d == D && in_bf16 == IB && out_bf16 == OB)                                                \
-        return launch_decode_t<D, IB, OB>(q, k, v, g, beta, state, out, units, h_k, h_v, l2norm, \
-                                          scale, grid, stream);
+        return launch_decode_t<D, IB, OB>(q, k, v, g, beta, state, slots, num_slots, out, units, h_k, h_v, \
+                                          l2norm, scale, grid, stream);
     GDN_DEC(128, true, true) GDN_DEC(128, true, false) GDN_DEC(128, false, true)
     GDN_DEC(128, false, false) GDN_DEC(64, true, true) GDN_DEC(64, true, false)
     GDN_DEC(64, false, true) GDN_DEC(64, false, false)

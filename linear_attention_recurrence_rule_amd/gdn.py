@@ -80,6 +80,8 @@ def lib():
             L.gdn_prefill_direct.restype = ctypes.c_int
             L.gdn_decode_step.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp]
             L.gdn_decode_step.restype = ctypes.c_int
+            L.gdn_decode_step_slots.argtypes = [dp, vp, vp, vp, vp, vp, vp, ctypes.c_int32, vp, vp, vp]
+            L.gdn_decode_step_slots.restype = ctypes.c_int
             L.gdn_status_str.argtypes = [ctypes.c_int]
             L.gdn_status_str.restype = ctypes.c_char_p
             L.gdn_last_error.argtypes = []
@@ -175,6 +177,12 @@ def gdn_prefill_direct(desc, q, k, v, g, beta, state_in, out, state_out, cu_seql
 def gdn_decode_step(desc, q, k, v, g, beta, state, out, stream=None):
     _check(lib().gdn_decode_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                  _ptr(state), _ptr(out), _stream(stream)))
+
+
+def gdn_decode_step_slots(desc, q, k, v, g, beta, state_pool, num_slots, state_slots, out, stream=None):
+    _check(lib().gdn_decode_step_slots(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                       _ptr(state_pool), int(num_slots), _ptr(state_slots), _ptr(out),
+                                       _stream(stream)))
 
 
 # ---- allocating wrappers ---------------------------------------------------------------
@@ -301,4 +309,28 @@ def decode_step(q, k, v, g, beta, state, *, out=None, out_dtype=None, qk_l2norm=
     if out is None:
         out = torch.empty((N, h_v, d), dtype=_TORCH_DT[od], device=dev)
     gdn_decode_step(desc, q, k, v, g, beta, state, out, stream)
+    return out
+
+
+def decode_step_slots(q, k, v, g, beta, state_pool, state_slots, *, out=None, out_dtype=None, qk_l2norm=True,
+                      scale=1.0, stream=None):
+    """decode_step over a state pool: sequence n updates state_pool[state_slots[n]]
+    in place.  state_pool [num_slots, h_v, d, d] fp32; state_slots [N] int32 on the
+    device.  A slot outside [0, num_slots) skips the sequence (zero output rows)."""
+    dev = q.device
+    io = _io_dtype(q)
+    N, h_k, d = q.shape
+    h_v = v.shape[1]
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype, dev)
+    _need(g, "g", torch.float32, dev)
+    _need(beta, "beta", torch.float32, dev)
+    _need(state_pool, "state_pool", torch.float32, dev)
+    _need(state_slots, "state_slots", torch.int32, dev)
+    od = io if out_dtype is None else out_dtype
+    desc = make_desc(num_seqs=N, total_tokens=N, h_k=h_k, h_v=h_v, d=d, io_dtype=io, out_dtype=od,
+                     qk_l2norm=qk_l2norm, scale=scale)
+    if out is None:
+        out = torch.empty((N, h_v, d), dtype=_TORCH_DT[od], device=dev)
+    gdn_decode_step_slots(desc, q, k, v, g, beta, state_pool, state_pool.shape[0], state_slots, out, stream)
     return out

@@ -36,7 +36,8 @@ def test_exports_every_declared_function(L):
     names = gdn.declared_functions()
     assert set(names) == {"gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_prefill_prepare",
                           "gdn_prefill_scan", "gdn_prefill_direct", "gdn_prefill_segmented_workspace_bytes",
-                          "gdn_prefill_segmented", "gdn_decode_step", "gdn_status_str", "gdn_last_error"}
+                          "gdn_prefill_segmented", "gdn_decode_step", "gdn_decode_step_slots",
+                          "gdn_status_str", "gdn_last_error"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -171,6 +172,26 @@ def test_decode_rejects_bad_arguments(L):
     assert call(desc(num_seqs=64), s=None) == gdn.GDN_ERR_INVALID_ARGUMENT
     assert call(desc(num_seqs=64), o=FAKE + 5 << 32) == gdn.GDN_ERR_INVALID_ARGUMENT  # out == state
     assert call(desc(num_seqs=0)) == gdn.GDN_ERR_INVALID_ARGUMENT
+
+
+@fake_pointers
+def test_decode_slots_rejects_bad_arguments(L):
+    lib = gdn.lib()
+    def call(d, **p):
+        a = dict(q=FAKE, k=FAKE + 1 << 32, v=FAKE + 2 << 32, g=FAKE + 3 << 32, b=FAKE + 4 << 32,
+                 s=FAKE + 5 << 32, n=8, i=FAKE + 6 << 32, o=FAKE + 7 << 32)
+        a.update(p)
+        return lib.gdn_decode_step_slots(ctypes.byref(d), a["q"], a["k"], a["v"], a["g"], a["b"], a["s"],
+                                         a["n"], a["i"], a["o"], None)
+    assert call(desc(num_seqs=4, h_v=30)) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call(desc(num_seqs=4, d=32)) == gdn.GDN_ERR_UNSUPPORTED
+    assert call(desc(num_seqs=4), s=None) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call(desc(num_seqs=4), i=None) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call(desc(num_seqs=4), n=0) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert "num_slots" in gdn.last_error()
+    assert call(desc(num_seqs=4), i=FAKE + 6 << 32 | 2) == gdn.GDN_ERR_INVALID_ARGUMENT      # misaligned slots
+    assert call(desc(num_seqs=4), i=(FAKE + 5 << 32) + 64) == gdn.GDN_ERR_INVALID_ARGUMENT  # slots inside the pool
+    assert "overlap" in gdn.last_error()
 
 
 @fake_pointers

@@ -116,3 +116,39 @@ def test_decode_hip_graph_replays_match_eager():
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out_g, outs_e) and torch.equal(state_g, state_e)
+
+
+@pytest.mark.parametrize("d,io", [(128, inputs.BF16), (64, inputs.F32)])
+def test_decode_slots_pool(d, io):
+    """gdn_decode_step_slots: sequence n steps pool slot slots[n] in place.  Valid
+    slots match gdn_decode_step on the gathered states bit for bit and the oracle
+    within the bound; out-of-range slots give zero outputs; untouched slots keep
+    their contents exactly."""
+    N, h_k, h_v, num_slots = 6, 2, 4, 10
+    slots = np.array([3, 0, 9, 5, -1, 12], dtype=np.int32)
+    x = inputs.decode_inputs(seed=77 + d, num_seqs=N, steps=1, h_k=h_k, h_v=h_v, d=d, io_dtype=io, state_std=0.3)
+    pool0 = (0.3 * np.random.default_rng(78 + d).standard_normal((num_slots, h_v, d, d))).astype(np.float32)
+    pool = dev(pool0)
+    q, k, v, g, b = (dev(x[n][0]) for n in ("q", "k", "v", "g", "beta"))
+    out = gdn.decode_step_slots(q, k, v, g, b, pool, dev(slots), out_dtype=inputs.F32)
+    valid = [n for n in range(N) if 0 <= slots[n] < num_slots]
+    # the same step through gdn_decode_step on the gathered states
+    vi = torch.tensor(valid, device=q.device)
+    st = dev(pool0[slots[valid]])
+    ref_out = gdn.decode_step(q[vi].contiguous(), k[vi].contiguous(), v[vi].contiguous(), g[vi].contiguous(),
+                              b[vi].contiguous(), st, out_dtype=inputs.F32)
+    assert torch.equal(out[vi], ref_out)
+    assert torch.equal(pool[torch.tensor(slots[valid].astype(np.int64), device=q.device)], st)
+    # skipped sequences: zero outputs
+    for n in range(N):
+        if n not in valid:
+            assert torch.count_nonzero(out[n]).item() == 0
+    # slots nobody named are untouched
+    untouched = sorted(set(range(num_slots)) - set(int(s) for s in slots[valid]))
+    assert torch.equal(pool[untouched].cpu(), torch.from_numpy(pool0[untouched]))
+    # and the oracle
+    ro, rs = oracle.decode_step(x["q"][0][valid], x["k"][0][valid], x["v"][0][valid], x["g"][0][valid],
+                                x["beta"][0][valid], pool0[slots[valid]].astype(np.float64), h_k=h_k, h_v=h_v)
+    tol = 2e-3 if io == inputs.BF16 else 1e-5
+    assert normwise(host(out[vi]), ro) <= tol
+    assert normwise(host(st), rs) <= tol
