@@ -502,13 +502,17 @@ __global__ __launch_bounds__(PREP_THREADS, (prep_min_waves<D, OP>())) void chunk
                 }
                 lds_barrier();
             }
-            // T = X diag(beta): T[i][j] = X[i][j] beta_j for i >= j (X_ij at [j][i]), else 0
-            for (int idx = tid; idx < CHUNK * CHUNK / 4; idx += PREP_THREADS) {
-                const int jj = idx / (CHUNK / 4), i4 = 4 * (idx % (CHUNK / 4));
-                const f4_t xv = *reinterpret_cast<const f4_t*>(&L.b.ax[jj * LDF + i4]);
-                const float bj = L.bt[jj];
+            // T = X diag(beta): T[i][j] = X[i][j] beta_j for i >= j (X_ij at [j][i]), else 0.
+            // Lane i of wave w forms T[i][8w .. 8w + 7]: eight reads along a row of the
+            // stored X^T (consecutive lanes, consecutive words) and one write of a row piece.
+            static_assert(CHUNK / 8 * CHUNK == PREP_THREADS, "T tiling");
+            {
+                const int i = tid % CHUNK, j0 = 8 * (tid / CHUNK);
+                float tv[8];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) L.t[(i4 + r) * LT + jj] = (OP)((i4 + r >= jj) ? xv[r] * bj : 0.f);
+                for (int r = 0; r < 8; ++r)
+                    tv[r] = (i >= j0 + r) ? L.b.ax[(j0 + r) * LDF + i] * L.bt[j0 + r] : 0.f;
+                store8<OP>(L.t + i * LT + j0, tv);
             }
             lds_barrier();
 
