@@ -120,18 +120,18 @@ struct KeyRec {
 
 template <int D, typename OP>
 constexpr int ldsk() { return D + 16 / (int)sizeof(OP); }  // row stride of [token][d] tiles
-template <typename OP>
-constexpr int ldt() { return CHUNK + 16 / (int)sizeof(OP); }  // row stride of [token][token] tiles
 constexpr int LDF = CHUNK + 4;                                  // fp32 64x64 tiles
 
-// LDS of chunk_prep (about 70 KiB at d = 128, so two workgroups share a
+// LDS of chunk_prep (about 68 KiB at d = 128, so two workgroups share a
 // compute unit).  q and k are kept row-major ([token][d]).  Operands that
-// contract over tokens are read from them as column fragments, so nothing is
-// ever written transposed.  Region b holds, by phase: A (strictly lower) with
-// X^T = ((I + A)^{-1})^T in its upper triangle, then the values V, then -W.
+// contract over tokens are read from them as column fragments.  T and P are
+// only ever read as matrix-core fragments, so they are stored fragment-major
+// (64 lanes x 8 elements per fragment, one contiguous 16-byte read per lane).
+// Region b holds, by phase: A (strictly lower) with X^T = ((I + A)^{-1})^T in
+// its upper triangle, then the values V, then -W.
 template <int D, typename OP>
 struct PrepLds {
-    static constexpr int LK = ldsk<D, OP>(), LT = ldt<OP>();
+    static constexpr int LK = ldsk<D, OP>();
     OP k[CHUNK * LK];  // keys scaled per token by a power of two (exact)
     OP q[CHUNK * LK];  // queries, likewise
     union B {
@@ -139,8 +139,8 @@ struct PrepLds {
         OP v[CHUNK * LK];       // values [token][d]
         OP w[CHUNK * LK];       // -W [token][d]
     } b;
-    OP t[CHUNK * LT];  // T = X diag(beta)
-    OP p[CHUNK * LT];  // P = lower_incl(D o Q K^T)
+    OP t[CHUNK * CHUNK];  // T = X diag(beta), fragment-major: (row block, 32-column block) fragments
+    OP p[CHUNK * CHUNK];  // P = lower_incl(D o Q K^T), likewise
     float G[CHUNK], ck[CHUNK], cq[CHUNK], bt[CHUNK], gck[CHUNK], gcq[CHUNK];
     int zero;  // holds 0 (see chunk_prep_kernel)
 };
@@ -213,6 +213,20 @@ __device__ __forceinline__ void lds_barrier() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Write 4 accumulator values (one lane's share of a 16x16 tile) as half of a
+// stored fragment: part 0 = elements 0..3, part 1 = elements 4..7.
+template <typename OP>
+__device__ __forceinline__ void store_part(OP* base, int frag, int part, int lane, const f4_t& x) {
+    OP* p = base + ((size_t)frag * WAVE + lane) * 8 + 4 * part;
+    if constexpr (sizeof(OP) == 2) {
+        typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+        h4_t h = {(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
+        *reinterpret_cast<h4_t*>(p) = h;
+    } else {
+        *reinterpret_cast<f4_t*>(p) = x;
+    }
+}
+
 // C + X Y for 16x16 fp32 matrices, X^T and Y (and C) in accumulator layout:
 // lane (j, q) holds M[4q + r][j] in element r.  Instruction e contracts over
 // k = 4q + e, taking X[i][4q + e] = X^T[4q + e][i] and Y[4q + e][j].
@@ -279,7 +293,7 @@ __global__ __launch_bounds__(PREP_THREADS, (prep_min_waves<D, OP>())) void chunk
     char* __restrict__ recs, char* __restrict__ krecs, int slots, int items_per_wg) {
     using RC = Rec<D, OP>;
     using In = PrepIn<D, IN_BF16>;
-    constexpr int LK = PrepLds<D, OP>::LK, LT = PrepLds<D, OP>::LT;
+    constexpr int LK = PrepLds<D, OP>::LK;
     constexpr int PER_TOK = In::PER_TOK, NIT = In::NIT;
     extern __shared__ __align__(16) char smem_raw[];
     PrepLds<D, OP>& L = *reinterpret_cast<PrepLds<D, OP>*>(smem_raw);
@@ -412,15 +426,14 @@ __global__ __launch_bounds__(PREP_THREADS, (prep_min_waves<D, OP>())) void chunk
                 const int tl = tp >> 1, isq = tp & 1;
                 const int mb = (tl >= 6) ? 3 : (tl >= 3) ? 2 : (tl >= 1) ? 1 : 0;
                 const int nb = tl - mb * (mb + 1) / 2;
-                const OP* rows = isq ? L.q : L.k;
                 f4_t acc = {0, 0, 0, 0};
-#pragma unroll
-                for (int kb = 0; kb < D / 32; ++kb)
-                    mma(acc, frag_rowmajor<OP>(rows, LK, mb, kb, lane), frag_rowmajor<OP>(L.k, LK, nb, kb, lane));
-                const int j = 16 * nb + li, i0 = 16 * mb + 4 * lq;
-                const float Gj = L.G[j], ckj = L.ck[j];
-                const f4_t Gi = *reinterpret_cast<const f4_t*>(&L.G[i0]);
                 if (!isq) {
+#pragma unroll
+                    for (int kb = 0; kb < D / 32; ++kb)
+                        mma(acc, frag_rowmajor<OP>(L.k, LK, mb, kb, lane), frag_rowmajor<OP>(L.k, LK, nb, kb, lane));
+                    const int j = 16 * nb + li, i0 = 16 * mb + 4 * lq;
+                    const float Gj = L.G[j], ckj = L.ck[j];
+                    const f4_t Gi = *reinterpret_cast<const f4_t*>(&L.G[i0]);
                     const f4_t cki = *reinterpret_cast<const f4_t*>(&L.ck[i0]);
                     const f4_t bti = *reinterpret_cast<const f4_t*>(&L.bt[i0]);
 #pragma unroll
@@ -429,20 +442,28 @@ __global__ __launch_bounds__(PREP_THREADS, (prep_min_waves<D, OP>())) void chunk
                         if (j < i) L.b.ax[i * LDF + j] = bti[r] * __expf(Gi[r] - Gj) * acc[r] * cki[r] * ckj;
                     }
                 } else {
-                    const f4_t cqi = *reinterpret_cast<const f4_t*>(&L.cq[i0]);
+                    // The transposed tile K Q^T: lane (j, q) gets (Q K^T)[16mb + j][16nb + 4q + r],
+                    // which is this lane's half of P's fragment (mb, nb / 2).
+#pragma unroll
+                    for (int kb = 0; kb < D / 32; ++kb)
+                        mma(acc, frag_rowmajor<OP>(L.k, LK, nb, kb, lane), frag_rowmajor<OP>(L.q, LK, mb, kb, lane));
+                    const int i = 16 * mb + li, c0 = 16 * nb + 4 * lq;
+                    const float Gi = L.G[i], cqi = L.cq[i];
+                    const f4_t Gc = *reinterpret_cast<const f4_t*>(&L.G[c0]);
+                    const f4_t ckc = *reinterpret_cast<const f4_t*>(&L.ck[c0]);
+                    f4_t pv;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int i = i0 + r;
-                        const float dec = (j <= i) ? __expf(fminf(Gi[r] - Gj, 0.f)) : 0.f;
-                        L.p[i * LT + j] = (OP)(dec * acc[r] * cqi[r] * ckj);
+                        const float dec = (c0 + r <= i) ? __expf(fminf(Gi - Gc[r], 0.f)) : 0.f;
+                        pv[r] = dec * acc[r] * cqi * ckc[r];
                     }
+                    store_part<OP>(L.p, mb * 2 + nb / 2, nb % 2, lane, pv);
                 }
             }
             for (int tl = wave; tl < 6; tl += PREP_WAVES) {  // strictly-upper tiles of P are zero
                 const int nb = (tl >= 3) ? 3 : (tl >= 1) ? 2 : 1;
                 const int mb = tl - (nb - 1) * nb / 2;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) L.p[(16 * mb + 4 * lq + r) * LT + 16 * nb + li] = (OP)0.f;
+                store_part<OP>(L.p, mb * 2 + nb / 2, nb % 2, lane, f4_t{0.f, 0.f, 0.f, 0.f});
             }
             lds_barrier();
 
@@ -503,16 +524,18 @@ __global__ __launch_bounds__(PREP_THREADS, (prep_min_waves<D, OP>())) void chunk
                 lds_barrier();
             }
             // T = X diag(beta): T[i][j] = X[i][j] beta_j for i >= j (X_ij at [j][i]), else 0.
-            // Lane i of wave w forms T[i][8w .. 8w + 7]: eight reads along a row of the
-            // stored X^T (consecutive lanes, consecutive words) and one write of a row piece.
-            static_assert(CHUNK / 8 * CHUNK == PREP_THREADS, "T tiling");
+            // Wave f forms fragment f of T (row block f / 2, column block f % 2); a lane's
+            // eight reads run along rows of the stored X^T (conflict-free), then one write.
+            static_assert(2 * (CHUNK / 16) == PREP_WAVES, "one T fragment per wave");
             {
-                const int i = tid % CHUNK, j0 = 8 * (tid / CHUNK);
-                float tv[8];
+                const int f = tid / WAVE, i = 16 * (f / 2) + li;
+                Frag<OP> tf;
 #pragma unroll
-                for (int r = 0; r < 8; ++r)
-                    tv[r] = (i >= j0 + r) ? L.b.ax[(j0 + r) * LDF + i] * L.bt[j0 + r] : 0.f;
-                store8<OP>(L.t + i * LT + j0, tv);
+                for (int e = 0; e < 8; ++e) {
+                    const int j = 32 * (f % 2) + 4 * lq + (e & 3) + 16 * (e >> 2);
+                    frag_set(tf, e, (i >= j) ? L.b.ax[j * LDF + i] * L.bt[j] : 0.f);
+                }
+                frag_store<OP>(L.t, f, lane, tf);
             }
             lds_barrier();
 
@@ -542,8 +565,8 @@ __global__ __launch_bounds__(PREP_THREADS, (prep_min_waves<D, OP>())) void chunk
 #pragma unroll
                 for (int mb = 0; mb < 4; ++mb) {
                     ut[mb] = f4_t{0, 0, 0, 0};
-                    mma(ut[mb], frag_rowmajor<OP>(L.t, LT, mb, 0, lane), fv0);
-                    mma(ut[mb], frag_rowmajor<OP>(L.t, LT, mb, 1, lane), fv1);
+                    mma(ut[mb], frag_stored<OP>(L.t, mb * 2 + 0, lane), fv0);
+                    mma(ut[mb], frag_stored<OP>(L.t, mb * 2 + 1, lane), fv1);
                     store4<OP>(urec + ((size_t)(nb * 4 + mb) * WAVE + lane) * 4, ut[mb]);
                 }
                 const Frag<OP> fu0 = frag_from_acc<OP>(ut[0], ut[1]);
@@ -551,8 +574,8 @@ __global__ __launch_bounds__(PREP_THREADS, (prep_min_waves<D, OP>())) void chunk
 #pragma unroll
                 for (int mb = 0; mb < 4; ++mb) {
                     f4_t ot = {0, 0, 0, 0};
-                    mma(ot, frag_rowmajor<OP>(L.p, LT, mb, 0, lane), fu0);
-                    mma(ot, frag_rowmajor<OP>(L.p, LT, mb, 1, lane), fu1);
+                    mma(ot, frag_stored<OP>(L.p, mb * 2 + 0, lane), fu0);
+                    mma(ot, frag_stored<OP>(L.p, mb * 2 + 1, lane), fu1);
                     store4<OP>(orec + ((size_t)(nb * 4 + mb) * WAVE + lane) * 4, ot);
                 }
             }
@@ -586,7 +609,7 @@ __global__ __launch_bounds__(PREP_THREADS, (prep_min_waves<D, OP>())) void chunk
                     for (int s2 = 0; s2 < 2; ++s2) {
                         acc[s2] = f4_t{0, 0, 0, 0};
 #pragma unroll
-                        for (int kk = 0; kk < 2; ++kk) mma(acc[s2], aw[s2][kk], frag_rowmajor<OP>(L.t, LT, tb, kk, lane));
+                        for (int kk = 0; kk < 2; ++kk) mma(acc[s2], aw[s2][kk], frag_stored<OP>(L.t, tb * 2 + kk, lane));
                     }
                     // lane (j, q): acc[s2][r] = W[token 16tb + j][d 16(2kb + s2) + 4q + r]
                     Frag<OP> fw;
@@ -622,7 +645,7 @@ __global__ __launch_bounds__(PREP_THREADS, (prep_min_waves<D, OP>())) void chunk
 #pragma unroll
                         for (int r = 0; r < 4; ++r) acc[s2][r] = (float)qr[r] * gq;
 #pragma unroll
-                        for (int kk = 0; kk < 2; ++kk) mma(acc[s2], aw[s2][kk], frag_rowmajor<OP>(L.p, LT, tb, kk, lane));
+                        for (int kk = 0; kk < 2; ++kk) mma(acc[s2], aw[s2][kk], frag_stored<OP>(L.p, tb * 2 + kk, lane));
                     }
                     Frag<OP> fq;
 #pragma unroll
@@ -701,19 +724,6 @@ constexpr size_t scan_lds_bytes() {
            (size_t)CHUNK * RS * (OUT_BF16 ? 2 : 4);
 }
 
-// Write 4 accumulator values (one lane's share of a 16x16 tile) as half of a
-// stored fragment: part 0 = elements 0..3, part 1 = elements 4..7.
-template <typename OP>
-__device__ __forceinline__ void store_part(OP* base, int frag, int part, int lane, const f4_t& x) {
-    OP* p = base + ((size_t)frag * WAVE + lane) * 8 + 4 * part;
-    if constexpr (sizeof(OP) == 2) {
-        typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
-        h4_t h = {(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
-        *reinterpret_cast<h4_t*>(p) = h;
-    } else {
-        *reinterpret_cast<f4_t*>(p) = x;
-    }
-}
 
 // s_waitcnt vmcnt(n), other counters untouched (gfx9 encoding)
 template <int N>
