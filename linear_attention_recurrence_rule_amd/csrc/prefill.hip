@@ -227,6 +227,25 @@ __device__ __forceinline__ void store_part(OP* base, int frag, int part, int lan
     }
 }
 
+// Row fragment of a row-major matrix M (leading dimension ld) for products
+// whose two operands are both read this way: lane (i, q) holds the eight
+// consecutive elements M[16 rb + i][32 kb + 8q + e], one 16-byte read (two for
+// fp32) per lane, so each quarter-wave reads distinct banks.  The contraction
+// index of element e is 8q + e; it differs from frag_rowmajor's, which is
+// harmless when both operands use this one.
+template <typename OP>
+__device__ __forceinline__ Frag<OP> frag_row8(const OP* M, int ld, int rb, int kb, int lane) {
+    const OP* p = M + (size_t)(16 * rb + (lane & 15)) * ld + 32 * kb + 8 * (lane >> 4);
+    Frag<OP> f;
+    if constexpr (sizeof(OP) == 2) {
+        f.v = *reinterpret_cast<const h8_t*>(p);
+    } else {
+        f.lo = *reinterpret_cast<const f4_t*>(p);
+        f.hi = *reinterpret_cast<const f4_t*>(p + 4);
+    }
+    return f;
+}
+
 // C + X Y for 16x16 fp32 matrices, X^T and Y (and C) in accumulator layout:
 // lane (j, q) holds M[4q + r][j] in element r.  Instruction e contracts over
 // k = 4q + e, taking X[i][4q + e] = X^T[4q + e][i] and Y[4q + e][j].
@@ -430,7 +449,7 @@ __global__ __launch_bounds__(PREP_THREADS, (prep_min_waves<D, OP>())) void chunk
                 if (!isq) {
 #pragma unroll
                     for (int kb = 0; kb < D / 32; ++kb)
-                        mma(acc, frag_rowmajor<OP>(L.k, LK, mb, kb, lane), frag_rowmajor<OP>(L.k, LK, nb, kb, lane));
+                        mma(acc, frag_row8<OP>(L.k, LK, mb, kb, lane), frag_row8<OP>(L.k, LK, nb, kb, lane));
                     const int j = 16 * nb + li, i0 = 16 * mb + 4 * lq;
                     const float Gj = L.G[j], ckj = L.ck[j];
                     const f4_t Gi = *reinterpret_cast<const f4_t*>(&L.G[i0]);
@@ -446,7 +465,7 @@ __global__ __launch_bounds__(PREP_THREADS, (prep_min_waves<D, OP>())) void chunk
                     // which is this lane's half of P's fragment (mb, nb / 2).
 #pragma unroll
                     for (int kb = 0; kb < D / 32; ++kb)
-                        mma(acc, frag_rowmajor<OP>(L.k, LK, nb, kb, lane), frag_rowmajor<OP>(L.q, LK, mb, kb, lane));
+                        mma(acc, frag_row8<OP>(L.k, LK, nb, kb, lane), frag_row8<OP>(L.q, LK, mb, kb, lane));
                     const int i = 16 * mb + li, c0 = 16 * nb + 4 * lq;
                     const float Gi = L.G[i], cqi = L.cq[i];
                     const f4_t Gc = *reinterpret_cast<const f4_t*>(&L.G[c0]);
