@@ -137,6 +137,53 @@ def crossover(L, gdn, inputs, to_dev, torch, np, dev):
         del q, k, v, g, b, s_in, cu, out, s_out, ws
 
 
+def two_level(L, gdn, inputs, to_dev, torch, np, dev):
+    """One long bf16 prompt with few heads (d = 128): gdn_prefill against the two-level scan
+    (gdn_prefill_two_level) at several segment counts.  Prints one JSON line per shape."""
+    shapes = [(2, 1, 16384), (4, 2, 32768), (8, 4, 32768), (32, 16, 4096)]
+    d = 128
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    for h_v, h_k, T in shapes:
+        x = inputs.prefill_inputs(seed=2, total_tokens=T, h_k=h_k, h_v=h_v, d=d, io_dtype=inputs.BF16,
+                                  state_std=0.02)
+        q, k, v, g, b = (to_dev(x[n]) for n in ("q", "k", "v", "g", "beta"))
+        s_in = to_dev(x["state_in"])
+        out = torch.empty((T, h_v, d), dtype=torch.bfloat16, device=dev)
+        s_out = torch.empty_like(s_in)
+        desc = gdn.make_desc(num_seqs=1, total_tokens=T, h_k=h_k, h_v=h_v, d=d, io_dtype=gdn.GDN_BF16,
+                             out_dtype=gdn.GDN_BF16)
+        dref = ctypes.byref(desc)
+        P = [z.data_ptr() for z in (q, k, v, g, b, s_in, out, s_out)]
+        res = {}
+        for segs in (1, 2, 4, 8, 16):
+            wsb = gdn.gdn_prefill_two_level_workspace_bytes(desc, segs)
+            ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+
+            def fn():
+                return L.gdn_prefill_two_level(dref, P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], 64, segs,
+                                               ws.data_ptr(), wsb, sp)
+            for _ in range(3):
+                if fn():
+                    raise gdn.GdnError(fn(), gdn.last_error())
+            torch.cuda.synchronize()
+            reps = 10
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            res[segs] = e0.elapsed_time(e1) * 1e3 / reps
+            del ws
+        best = min(res, key=res.get)
+        print(json.dumps({"two_level": {"h_v": h_v, "h_k": h_k, "d": d, "tokens": T,
+                                        "us_by_segments": {str(k2): round(v2, 1) for k2, v2 in res.items()},
+                                        "best_segments": best, "speedup_vs_one_level": round(res[1] / res[best], 2)}}),
+              flush=True)
+        del q, k, v, g, b, s_in, out, s_out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -149,6 +196,9 @@ def main():
     ap.add_argument("--crossover", action="store_true",
                     help="instead of the benchmark line: time the direct and the chunked prefill over a "
                          "range of sequence lengths (one JSON line per shape)")
+    ap.add_argument("--two-level", action="store_true",
+                    help="instead of the benchmark line: time one long few-head prompt through gdn_prefill "
+                         "and the two-level scan at several segment counts (one JSON line per shape)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on exactly one GPU; --gpus %d is not supported "
@@ -175,6 +225,9 @@ def main():
 
     if args.crossover:
         crossover(L, gdn, inputs, to_dev, torch, np, dev)
+        return
+    if args.two_level:
+        two_level(L, gdn, inputs, to_dev, torch, np, dev)
         return
 
     # ---------------- prefill ----------------

@@ -211,6 +211,37 @@ gdn_status gdn_prefill_segmented(const gdn_desc *desc,
                                  void *stream);
 
 /*
+ * Two-level prefill of one long sequence (num_seqs == 1, no cu_seqlens), for
+ * shapes whose (v-head x row-slice) units leave compute units idle, such as a
+ * long prompt with few heads.  The block chain of the scan is cut into
+ * `segments` segments of whole blocks.  A run of blocks maps the state
+ * affinely, S_end = S_start R + B (the section "Keep the recurrent state on
+ * chip" carries the state across pieces of a prompt the same way), so:
+ * (1) one state-carrying pass over all segments at once yields each segment's
+ * B (run from zero) and R (run from the identity without the value term);
+ * (2) a short sequential pass composes the segments' start states in fp32;
+ * (3) the scan reruns every segment from its start state, in parallel, and
+ * writes the outputs.  This does about three times the state-dependent
+ * work of gdn_prefill on `segments`-fold more parallel units.  The result
+ * matches gdn_prefill within the same tolerance; the rounding order differs.
+ * segments == 1 (or a sequence of one block) is gdn_prefill.
+ *
+ * Workspace: gdn_prefill_two_level_workspace_bytes().  Other arguments and
+ * errors are those of gdn_prefill, plus GDN_ERR_UNSUPPORTED for
+ * num_seqs != 1 and GDN_ERR_INVALID_ARGUMENT for segments < 1.
+ */
+size_t gdn_prefill_two_level_workspace_bytes(const gdn_desc *desc, int32_t chunk, int32_t segments);
+
+gdn_status gdn_prefill_two_level(const gdn_desc *desc,
+                                 const void *q, const void *k, const void *v,
+                                 const float *g, const float *beta,
+                                 const float *state_in,
+                                 void *out, float *state_out,
+                                 int32_t chunk, int32_t segments,
+                                 void *workspace, size_t workspace_bytes,
+                                 void *stream);
+
+/*
  * Direct (token-by-token) prefill over packed sequences: the other evaluation
  * of the workload-shapes section, which says the faster of the two depends on
  * the shape.  Each (sequence, v-head) state is loaded once, kept in registers

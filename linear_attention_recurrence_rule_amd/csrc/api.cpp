@@ -18,6 +18,11 @@ hipError_t launch_decode(int d, bool in_bf16, bool out_bf16, const void* q, cons
                          int grid, hipStream_t stream);
 size_t prefill_record_bytes(int d, bool in_bf16);
 size_t prefill_key_record_bytes(int d, bool in_bf16);
+hipError_t launch_segment_info(void* info, int P, int sb, int T, hipStream_t stream);
+hipError_t launch_compose(int d, const float* state_in, const float* R, const float* B, float* starts, int P,
+                          int h_v, hipStream_t stream);
+hipError_t launch_scan_transition(int d, bool in_bf16, const void* recs, const void* krecs, const void* info,
+                                  float* s_out, void* sink, int units, int T, int h_k, int h_v, hipStream_t stream);
 hipError_t launch_direct(int d, bool in_bf16, bool out_bf16, const void* q, const void* k, const void* v,
                          const float* g, const float* beta, const int32_t* cu, const float* s_in, float* s_out,
                          void* out, int units, int T, int h_k, int h_v, int l2norm, float scale, hipStream_t stream);
@@ -269,6 +274,42 @@ gdn_status prefill_call(Phase phase, const gdn_desc* desc, const void* q, const 
     return GDN_OK;
 }
 
+// Two-level plan of one sequence: P segments of sb blocks each (the last may
+// be shorter), and the workspace after the single-sequence prefill layout:
+// segment table, per-segment affine parts B and transitions R (segments
+// 0..P-2, adjacent), and start and end states of every segment.
+struct TwoLevel {
+    int64_t nblocks;
+    int P, sb;
+    size_t info_off, b_off, r_off, start_off, end_off, total;
+};
+
+gdn_status two_level_plan(const gdn_desc* desc, int32_t chunk, int32_t segments, TwoLevel* tl) {
+    gdn_status st = check_desc(desc, true);
+    if (st != GDN_OK) return st;
+    if (chunk != kChunk) return fail(GDN_ERR_UNSUPPORTED, "chunk must be 64 (got %d)", chunk);
+    if (desc->num_seqs != 1)
+        return fail(GDN_ERR_UNSUPPORTED, "two-level prefill takes one sequence (num_seqs = %d)", desc->num_seqs);
+    if (segments < 1) return fail(GDN_ERR_INVALID_ARGUMENT, "segments must be >= 1 (got %d)", segments);
+    const int64_t T = desc->total_tokens;
+    tl->nblocks = (T + kChunk - 1) / kChunk;
+    const int64_t want = segments < tl->nblocks ? segments : (tl->nblocks > 0 ? tl->nblocks : 1);
+    tl->sb = (int)(tl->nblocks > 0 ? (tl->nblocks + want - 1) / want : 1);
+    tl->P = (int)(tl->nblocks > 0 ? (tl->nblocks + tl->sb - 1) / tl->sb : 1);
+    if (tl->P == 1) {  // the plain prefill
+        tl->total = ws_layout(desc, true).total;
+        return GDN_OK;
+    }
+    const size_t st_bytes = (size_t)desc->h_v * desc->d_k * desc->d_k * 4;
+    tl->info_off = align_up(ws_layout(desc, false).total, 256);
+    tl->b_off = align_up(tl->info_off + (size_t)tl->P * 16, 256);
+    tl->r_off = tl->b_off + (size_t)(tl->P - 1) * st_bytes;
+    tl->start_off = tl->r_off + (size_t)(tl->P - 1) * st_bytes;
+    tl->end_off = tl->start_off + (size_t)tl->P * st_bytes;
+    tl->total = tl->end_off + (size_t)tl->P * st_bytes;
+    return GDN_OK;
+}
+
 // Segment descriptor and state buffer of the segmented prefill.
 gdn_status segment_plan(const gdn_desc* desc, int32_t chunk, int64_t seg, gdn_desc* sub, size_t* need,
                                size_t* state_off) {
@@ -467,6 +508,79 @@ gdn_status gdn_decode_step_slots(const gdn_desc* desc, const void* q, const void
                     "q, k, v, g, beta, state_pool, state_slots and out must be non-NULL");
     if (num_slots < 1) return fail(GDN_ERR_INVALID_ARGUMENT, "num_slots must be >= 1 (got %d)", num_slots);
     return decode_call(desc, q, k, v, g, beta, state_pool, num_slots, state_slots, out, stream);
+}
+
+
+size_t gdn_prefill_two_level_workspace_bytes(const gdn_desc* desc, int32_t chunk, int32_t segments) {
+    g_err[0] = 0;
+    TwoLevel tl;
+    return two_level_plan(desc, chunk, segments, &tl) == GDN_OK ? tl.total : 0;
+}
+
+gdn_status gdn_prefill_two_level(const gdn_desc* desc, const void* q, const void* k, const void* v,
+                                 const float* g, const float* beta, const float* state_in, void* out,
+                                 float* state_out, int32_t chunk, int32_t segments, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+    g_err[0] = 0;
+    TwoLevel tl;
+    gdn_status st = two_level_plan(desc, chunk, segments, &tl);
+    if (st != GDN_OK) return st;
+    if (tl.P == 1)
+        return prefill_call(kBoth, desc, q, k, v, g, beta, state_in, out, state_out, nullptr, chunk, workspace,
+                            workspace_bytes, stream);
+    if (!workspace) return fail(GDN_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", tl.total);
+    if (workspace_bytes < tl.total)
+        return fail(GDN_ERR_WORKSPACE, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, tl.total);
+    const int64_t T = desc->total_tokens;
+    const int hk = desc->h_k, hv = desc->h_v, d = desc->d_k;
+    if (!q || !k || !v || !g || !beta || !out)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "q, k, v, g, beta and out must be non-NULL");
+    const size_t io = dtype_size(desc->io_dtype), os = dtype_size(desc->out_dtype);
+    const size_t sbytes = (size_t)hv * d * d * 4;
+    const Span spans[] = {
+        {(const char*)q, (size_t)T * hk * d * io, "q"},
+        {(const char*)k, (size_t)T * hk * d * io, "k"},
+        {(const char*)v, (size_t)T * hv * d * io, "v"},
+        {(const char*)g, (size_t)T * hv * 4, "g"},
+        {(const char*)beta, (size_t)T * hv * 4, "beta"},
+        {(const char*)out, (size_t)T * hv * d * os, "out"},
+        {(const char*)state_in, state_in ? sbytes : 0, "state_in"},
+        {(const char*)state_out, state_out ? sbytes : 0, "state_out"},
+        {(const char*)workspace, tl.total, "workspace"},
+    };
+    st = check_align(spans, sizeof(spans) / sizeof(spans[0]));
+    if (st != GDN_OK) return st;
+    st = check_overlaps(spans, sizeof(spans) / sizeof(spans[0]), state_in, state_out);
+    if (st != GDN_OK) return st;
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const bool in_bf16 = desc->io_dtype == GDN_BF16, out_bf16 = desc->out_dtype == GDN_BF16;
+    const WsLayout ws = ws_layout(desc, false);
+    char* wsb = reinterpret_cast<char*>(workspace);
+    char* recs = wsb + ws.rec_off;
+    char* krecs = wsb + ws.key_off;
+    void* info = wsb + tl.info_off;
+    float* R = reinterpret_cast<float*>(wsb + tl.r_off);
+    float* B = reinterpret_cast<float*>(wsb + tl.b_off);
+    float* starts = reinterpret_cast<float*>(wsb + tl.start_off);
+    float* ends = reinterpret_cast<float*>(wsb + tl.end_off);
+    const int P = tl.P;
+    hipError_t e = gdn::launch_prep(d, in_bf16, q, k, v, g, beta, nullptr, nullptr, (int)tl.nblocks, (int)T, hk, hv,
+                                    desc->qk_l2norm, desc->scale, recs, krecs, s);
+    if (e == hipSuccess) e = gdn::launch_segment_info(info, P, tl.sb, (int)T, s);
+    // segments 0..P-2 in one pass: affine parts B from zero, transitions R from the identity
+    // (B and R are adjacent, so one state_out array holds both halves)
+    if (e == hipSuccess)
+        e = gdn::launch_scan_transition(d, in_bf16, recs, krecs, info, B, wsb + ws.sink_off, 2 * (P - 1) * hv,
+                                        (int)T, hk, hv, s);
+    if (e == hipSuccess) e = gdn::launch_compose(d, state_in, R, B, starts, P, hv, s);
+    if (e == hipSuccess)
+        e = gdn::launch_scan(d, in_bf16, out_bf16, recs, krecs, info, starts, ends, out, wsb + ws.sink_off, P * hv,
+                             (int)T, hk, hv, s);
+    if (e == hipSuccess && state_out)
+        e = hipMemcpyAsync(state_out, ends + (size_t)(P - 1) * hv * d * d, sbytes, hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "two-level prefill launch: %s", hipGetErrorString(e));
+    return GDN_OK;
 }
 
 }  // extern "C"

@@ -783,7 +783,11 @@ __device__ __forceinline__ void scan_copy(const char* rec, const char* krec, Sca
     }
 }
 
-template <int D, typename OP, bool OUT_BF16, int RS>
+// MODE 0: the scan.  MODE 1: both parts of a segment's state map, no outputs:
+// the first half of the units runs from zero (the affine part B), the second
+// half from the identity without Ut (the transition R), so that
+// S_end = S_start R + B.  Both halves write state_out at their unit.
+template <int D, typename OP, bool OUT_BF16, int RS, int MODE = 0>
 __global__ __launch_bounds__(SCAN_THREADS) void chunk_scan_kernel(
     const char* __restrict__ recs, const char* __restrict__ krecs, const SeqInfo* __restrict__ info,
     const float* __restrict__ state_in, float* __restrict__ state_out, void* __restrict__ out,
@@ -806,7 +810,10 @@ __global__ __launch_bounds__(SCAN_THREADS) void chunk_scan_kernel(
     const int slice = m % SLICES;
     const int unit = (m / SLICES) * 8 + xcd;  // sequence * h_v + v-head
     if (unit >= units) return;
-    const int n = unit / h_v, h = unit - n * h_v;
+    // MODE 1: units [units/2, units) are the transition runs of the same segments
+    const bool lin = MODE == 1 && unit >= units / 2;
+    const int su = lin ? unit - units / 2 : unit;
+    const int n = su / h_v, h = su - n * h_v;
     const int tid = threadIdx.x, w = tid / WAVE, lane = tid % WAVE;
     const int j16 = lane & 15, q4 = lane >> 4;
     const int r0 = slice * RS, cb0 = r0 / 16;
@@ -844,7 +851,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void chunk_scan_kernel(
             // outputs: 16 bytes per lane, rows past the block's end go to the sink
             const int tok0 = begin + c * CHUNK, nt = min(CHUNK, len - c * CHUNK);
 #pragma unroll
-            for (int i = 0; i < (PIECES + LT - 1) / LT; ++i) {
+            for (int i = 0; i < (MODE == 0 ? (PIECES + LT - 1) / LT : 0); ++i) {
                 const int p = i * LT + lw * WAVE + lane;
                 if (PIECES % LT == 0 || p < PIECES) {
                     const int row = p / LPR, col16 = p % LPR;
@@ -878,7 +885,11 @@ __global__ __launch_bounds__(SCAN_THREADS) void chunk_scan_kernel(
     for (int i = 0; i < TPW; ++i) {
         const int t = w * TPW + i, mb = t / NB, nb = t % NB;
         if (t >= Sh::NTB) break;
-        if (state_in) {
+        if (lin) {  // identity: S[r][c] = (r == c)
+            const int row = r0 + 16 * nb + j16, col = 16 * mb + 4 * q4;
+            St[i] = f4_t{row == col ? 1.f : 0.f, row == col + 1 ? 1.f : 0.f, row == col + 2 ? 1.f : 0.f,
+                         row == col + 3 ? 1.f : 0.f};
+        } else if (state_in) {
             const float4 x = *reinterpret_cast<const float4*>(
                 state_in + sbase + (size_t)(r0 + 16 * nb + j16) * D + 16 * mb + 4 * q4);
             St[i] = f4_t{x.x, x.y, x.z, x.w};
@@ -896,7 +907,9 @@ __global__ __launch_bounds__(SCAN_THREADS) void chunk_scan_kernel(
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             const OP* u = &B.uo[(((which * NB + nb) * 4 + tb) * WAVE + lane) * 4];
-            if constexpr (sizeof(OP) == 2) {
+            if (lin) {
+                acc[nb] = f4_t{0.f, 0.f, 0.f, 0.f};
+            } else if constexpr (sizeof(OP) == 2) {
                 typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
                 const h4_t x = *reinterpret_cast<const h4_t*>(u);
                 acc[nb] = f4_t{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
@@ -904,11 +917,13 @@ __global__ __launch_bounds__(SCAN_THREADS) void chunk_scan_kernel(
                 acc[nb] = *reinterpret_cast<const f4_t*>(u);
             }
         }
+        if (MODE == 0 || which == 0) {  // O is needed only by the scan itself
 #pragma unroll
-        for (int kb = 0; kb < D / 32; ++kb) {
-            const Frag<OP> a = frag_stored<OP>(Ab, tb * (D / 32) + kb, lane);
+            for (int kb = 0; kb < D / 32; ++kb) {
+                const Frag<OP> a = frag_stored<OP>(Ab, tb * (D / 32) + kb, lane);
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) mma(acc[nb], a, frag_stored<OP>(sS, kb * NB + nb, lane));
+                for (int nb = 0; nb < NB; ++nb) mma(acc[nb], a, frag_stored<OP>(sS, kb * NB + nb, lane));
+            }
         }
         Frag<OP> kf[TPW][2];
 #pragma unroll
@@ -923,7 +938,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void chunk_scan_kernel(
             const f4_t sv = *reinterpret_cast<const f4_t*>(&B.sg[16 * tb + 4 * q4]);
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) store_part<OP>(sU, (tb / 2) * NB + nb, tb % 2, lane, acc[nb] * sv);
-        } else {
+        } else if (MODE == 0) {
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -1025,13 +1040,13 @@ hipError_t launch_prep(int d, bool in_bf16, const void* q, const void* k, const 
     return hipErrorInvalidValue;
 }
 
-template <int D, typename OP, bool OB, int RS>
+template <int D, typename OP, bool OB, int RS, int MODE = 0>
 static hipError_t launch_scan_t(const void* recs, const void* krecs, const void* info, const float* s_in,
                                 float* s_out, void* out, void* sink, int units, int T, int h_k, int h_v,
                                 hipStream_t stream) {
     static_assert(scan_lds_bytes<D, OP, OB, RS>() <= 160 * 1024, "chunk_scan LDS budget");
     const int groups = (units + 7) / 8;  // see the XCD placement in chunk_scan_kernel
-    hipLaunchKernelGGL((chunk_scan_kernel<D, OP, OB, RS>), dim3(groups * 8 * (D / RS)), dim3(SCAN_THREADS), 0,
+    hipLaunchKernelGGL((chunk_scan_kernel<D, OP, OB, RS, MODE>), dim3(groups * 8 * (D / RS)), dim3(SCAN_THREADS), 0,
                        stream, reinterpret_cast<const char*>(recs), reinterpret_cast<const char*>(krecs),
                        reinterpret_cast<const SeqInfo*>(info), s_in, s_out, out, reinterpret_cast<char*>(sink), units,
                        T, h_k, h_v);
@@ -1062,6 +1077,99 @@ hipError_t launch_scan(int d, bool in_bf16, bool out_bf16, const void* recs, con
     GDN_SCAN(64, _Float16, true, true) GDN_SCAN(64, _Float16, true, false)
     GDN_SCAN(64, float, false, true) GDN_SCAN(64, float, false, false)
 #undef GDN_SCAN
+    return hipErrorInvalidValue;
+}
+
+// ---- two-level scan of one long sequence -------------------------------------------------
+// The state map of a run of blocks is affine, S_end = S_start R + B (section
+// "Keep the recurrent state on chip" carries S across pieces of a prompt the
+// same way).  Split into P segments, each segment's R and B come from two
+// state-carrying passes run in parallel (MODE 2 from the identity, MODE 1 from
+// zero), the segments' start states from a short sequential composition, and
+// the outputs from the scan rerun on all segments in parallel.
+
+__global__ void segment_info_kernel(SeqInfo* __restrict__ info, int P, int sb, int T) {
+    const int s = blockIdx.x * blockDim.x + threadIdx.x;
+    if (s < P) {
+        const int b = s * sb * CHUNK;
+        info[s] = SeqInfo{b, min(sb * CHUNK, T - b), s * sb, 0};
+    }
+}
+
+// Segment start states: S_0 = state_in (or zero), S_{s+1} = S_s R_s + B_s.
+// One workgroup per (v-head, 16 rows): rows evolve independently.  R_s is
+// staged through LDS with coalesced loads.  fp32.
+template <int D>
+__global__ __launch_bounds__(512) void compose_kernel(const float* __restrict__ state_in,
+                                                      const float* __restrict__ R, const float* __restrict__ B,
+                                                      float* __restrict__ starts, int P, int h_v) {
+    constexpr int ROWS = 16, CPT = D * ROWS / 512, GROUPS = D / CPT;  // columns per thread, column groups
+    __shared__ float Rl[D * D];
+    __shared__ float cur[ROWS][D];
+    const int h = blockIdx.x / (D / ROWS), r0 = (blockIdx.x % (D / ROWS)) * ROWS;
+    const int lr = threadIdx.x / GROUPS, c0 = (threadIdx.x % GROUPS) * CPT;
+    const size_t hd = (size_t)h * D * D, row = (size_t)(r0 + lr) * D;
+    float s[CPT];
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+        s[j] = state_in ? state_in[hd + row + c0 + j] : 0.f;
+        starts[hd + row + c0 + j] = s[j];
+    }
+    for (int st = 0; st + 1 < P; ++st) {
+        const size_t m = (size_t)(st * h_v) * D * D + hd;
+        __syncthreads();  // the previous step's reads of Rl and cur are done
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) cur[lr][c0 + j] = s[j];
+#pragma unroll
+        for (int i = 0; i < D * D / 4 / 512; ++i) {
+            const int e = (i * 512 + threadIdx.x) * 4;
+            *reinterpret_cast<float4*>(&Rl[e]) = *reinterpret_cast<const float4*>(R + m + e);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) s[j] = B[m + row + c0 + j];
+#pragma unroll 8
+        for (int k = 0; k < D; ++k) {
+            const float a = cur[lr][k];
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) s[j] = fmaf(a, Rl[k * D + c0 + j], s[j]);
+        }
+        const size_t o = (size_t)((st + 1) * h_v) * D * D + hd;
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) starts[o + row + c0 + j] = s[j];
+    }
+}
+
+hipError_t launch_segment_info(void* info, int P, int sb, int T, hipStream_t stream) {
+    hipLaunchKernelGGL(segment_info_kernel, dim3((P + 255) / 256), dim3(256), 0, stream,
+                       reinterpret_cast<SeqInfo*>(info), P, sb, T);
+    return hipGetLastError();
+}
+
+hipError_t launch_compose(int d, const float* state_in, const float* R, const float* B, float* starts, int P,
+                          int h_v, hipStream_t stream) {
+    if (d == 128)
+        hipLaunchKernelGGL(compose_kernel<128>, dim3(h_v * 8), dim3(512), 0, stream, state_in, R, B, starts, P, h_v);
+    else if (d == 64)
+        hipLaunchKernelGGL(compose_kernel<64>, dim3(h_v * 4), dim3(512), 0, stream, state_in, R, B, starts, P, h_v);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+// Both state-map parts of every segment in `info` (MODE 1): units = 2 x
+// (segments x v-heads); state_out receives B for the first half, R for the second.
+hipError_t launch_scan_transition(int d, bool in_bf16, const void* recs, const void* krecs, const void* info,
+                                  float* s_out, void* sink, int units, int T, int h_k, int h_v, hipStream_t stream) {
+    const int rs = scan_rows_per_workgroup(d, units);
+#define GDN_TR(D, OP, IB)                                                                                        \
+    if (d == D && in_bf16 == IB)                                                                                 \
+        return rs == 16 ? launch_scan_t<D, OP, false, 16, 1>(recs, krecs, info, nullptr, s_out, nullptr, sink,    \
+                                                              units, T, h_k, h_v, stream)                        \
+                        : launch_scan_t<D, OP, false, 32, 1>(recs, krecs, info, nullptr, s_out, nullptr, sink,    \
+                                                              units, T, h_k, h_v, stream);
+    GDN_TR(128, _Float16, true) GDN_TR(64, _Float16, true) GDN_TR(64, float, false)
+#undef GDN_TR
     return hipErrorInvalidValue;
 }
 

@@ -76,6 +76,11 @@ def lib():
             L.gdn_prefill_segmented.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32, ctypes.c_int64,
                                                 vp, sz, vp]
             L.gdn_prefill_segmented.restype = ctypes.c_int
+            L.gdn_prefill_two_level_workspace_bytes.argtypes = [dp, ctypes.c_int32, ctypes.c_int32]
+            L.gdn_prefill_two_level_workspace_bytes.restype = sz
+            L.gdn_prefill_two_level.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32, ctypes.c_int32,
+                                                vp, sz, vp]
+            L.gdn_prefill_two_level.restype = ctypes.c_int
             L.gdn_prefill_direct.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
             L.gdn_prefill_direct.restype = ctypes.c_int
             L.gdn_decode_step.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -165,6 +170,20 @@ def gdn_prefill_segmented(desc, q, k, v, g, beta, state_in, out, state_out, chun
                           workspace_bytes, stream=None):
     _check(lib().gdn_prefill_segmented(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                        _ptr(state_in), _ptr(out), _ptr(state_out), int(chunk), int(segment_tokens),
+                                       _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def gdn_prefill_two_level_workspace_bytes(desc: GdnDesc, segments: int, chunk: int = CHUNK) -> int:
+    n = lib().gdn_prefill_two_level_workspace_bytes(ctypes.byref(desc), int(chunk), int(segments))
+    if n == 0:
+        raise GdnError(GDN_ERR_INVALID_ARGUMENT, last_error())
+    return n
+
+
+def gdn_prefill_two_level(desc, q, k, v, g, beta, state_in, out, state_out, chunk, segments, workspace,
+                          workspace_bytes, stream=None):
+    _check(lib().gdn_prefill_two_level(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                       _ptr(state_in), _ptr(out), _ptr(state_out), int(chunk), int(segments),
                                        _ptr(workspace), int(workspace_bytes), _stream(stream)))
 
 
@@ -260,6 +279,32 @@ def prefill_segmented(q, k, v, g, beta, *, segment_tokens, state_in=None, out_dt
     workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     gdn_prefill_segmented(desc, q, k, v, g, beta, state_in, out, state_out, CHUNK, segment_tokens, workspace,
                           nbytes, stream)
+    return out, state_out
+
+
+def prefill_two_level(q, k, v, g, beta, *, segments, state_in=None, out_dtype=None, qk_l2norm=True, scale=1.0,
+                      want_state=True, stream=None):
+    """One long sequence by the two-level scan (gdn_prefill_two_level) with ``segments``
+    segments.  Returns (out, state_out or None)."""
+    dev = q.device
+    io = _io_dtype(q)
+    T, h_k, d = q.shape
+    h_v = v.shape[1]
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype, dev)
+    _need(g, "g", torch.float32, dev)
+    _need(beta, "beta", torch.float32, dev)
+    if state_in is not None:
+        _need(state_in, "state_in", torch.float32, dev)
+    od = io if out_dtype is None else out_dtype
+    desc = make_desc(num_seqs=1, total_tokens=T, h_k=h_k, h_v=h_v, d=d, io_dtype=io, out_dtype=od,
+                     qk_l2norm=qk_l2norm, scale=scale)
+    out = torch.empty((T, h_v, d), dtype=_TORCH_DT[od], device=dev)
+    state_out = torch.empty((1, h_v, d, d), dtype=torch.float32, device=dev) if want_state else None
+    nbytes = gdn_prefill_two_level_workspace_bytes(desc, segments)
+    workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    gdn_prefill_two_level(desc, q, k, v, g, beta, state_in, out, state_out, CHUNK, segments, workspace, nbytes,
+                          stream)
     return out, state_out
 
 

@@ -36,7 +36,8 @@ def test_exports_every_declared_function(L):
     names = gdn.declared_functions()
     assert set(names) == {"gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_prefill_prepare",
                           "gdn_prefill_scan", "gdn_prefill_direct", "gdn_prefill_segmented_workspace_bytes",
-                          "gdn_prefill_segmented", "gdn_decode_step", "gdn_decode_step_slots",
+                          "gdn_prefill_segmented", "gdn_prefill_two_level_workspace_bytes", "gdn_prefill_two_level",
+                          "gdn_decode_step", "gdn_decode_step_slots",
                           "gdn_status_str", "gdn_last_error"}
     for n in names:
         assert hasattr(L, n), n
@@ -191,6 +192,46 @@ def test_decode_slots_rejects_bad_arguments(L):
     assert "num_slots" in gdn.last_error()
     assert call(desc(num_seqs=4), i=FAKE + 6 << 32 | 2) == gdn.GDN_ERR_INVALID_ARGUMENT      # misaligned slots
     assert call(desc(num_seqs=4), i=(FAKE + 5 << 32) + 64) == gdn.GDN_ERR_INVALID_ARGUMENT  # slots inside the pool
+    assert "overlap" in gdn.last_error()
+
+
+def test_two_level_workspace_bytes(L):
+    one = gdn.gdn_prefill_workspace_bytes(desc(total_tokens=4096))
+    assert gdn.gdn_prefill_two_level_workspace_bytes(desc(total_tokens=4096), 1) == one
+    # 64 blocks in 8 segments of 8: single-sequence records, a 256-byte segment table, then
+    # R and B for 7 segments and start and end states for 8 (32 v-heads, d = 128, fp32)
+    rec = 4 * 64 * 128 * 2 + 512
+    key = 64 * 128 * 2
+    base = 1024 + 64 * (32 * rec + 16 * key)
+    st = 32 * 128 * 128 * 4
+    assert gdn.gdn_prefill_two_level_workspace_bytes(desc(total_tokens=4096), 8) == base + 256 + (7 + 7 + 8 + 8) * st
+    # more segments than blocks: one segment per block
+    assert gdn.gdn_prefill_two_level_workspace_bytes(desc(total_tokens=200), 99) == \
+        gdn.gdn_prefill_two_level_workspace_bytes(desc(total_tokens=200), 4)
+    assert L.gdn_prefill_two_level_workspace_bytes(ctypes.byref(desc(num_seqs=2)), 64, 4) == 0
+    assert "one sequence" in gdn.last_error()
+    assert L.gdn_prefill_two_level_workspace_bytes(ctypes.byref(desc()), 64, 0) == 0
+    assert "segments" in gdn.last_error()
+
+
+@fake_pointers
+def test_two_level_rejects_bad_arguments(L):
+    lib = gdn.lib()
+    d0 = desc(total_tokens=4096)
+    need = gdn.gdn_prefill_two_level_workspace_bytes(d0, 4)
+    ws = FAKE + 9 << 32
+    def call(d, **p):
+        a = dict(q=FAKE, k=FAKE + 1 << 32, v=FAKE + 2 << 32, g=FAKE + 3 << 32, b=FAKE + 4 << 32,
+                 si=None, o=FAKE + 5 << 32, so=None, seg=4, ws=ws, n=need)
+        a.update(p)
+        return lib.gdn_prefill_two_level(ctypes.byref(d), a["q"], a["k"], a["v"], a["g"], a["b"], a["si"], a["o"],
+                                         a["so"], 64, a["seg"], a["ws"], a["n"], None)
+    assert call(desc(total_tokens=4096, num_seqs=2)) == gdn.GDN_ERR_UNSUPPORTED
+    assert call(d0, seg=0) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call(d0, n=need - 1) == gdn.GDN_ERR_WORKSPACE
+    assert call(d0, ws=None) == gdn.GDN_ERR_WORKSPACE
+    assert call(d0, o=None) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call(d0, o=ws + 4096) == gdn.GDN_ERR_INVALID_ARGUMENT   # out inside the workspace
     assert "overlap" in gdn.last_error()
 
 

@@ -277,3 +277,39 @@ def test_segmented_empty_sequence_passes_state():
     a = [dev(x[n]) for n in ("q", "k", "v", "g", "beta")]
     o, s = gdn.prefill_segmented(*a, segment_tokens=64, state_in=dev(x["state_in"]))
     assert o.numel() == 0 and torch.equal(s, dev(x["state_in"]))
+
+
+# ---- two-level scan (one long sequence, few heads) -----------------------------------------
+
+@pytest.mark.parametrize("segments", [2, 5, 64])
+def test_two_level_bf16_matches_oracle(segments):
+    """gdn_prefill_two_level: segments' transitions and affine parts, composed start
+    states, then the scan rerun per segment.  bf16, d = 128, 2381 tokens (37 blocks
+    + 13 tokens), a non-zero start state; 64 segments caps at one block each."""
+    x = inputs.prefill_inputs(seed=90 + segments, total_tokens=2381, h_k=1, h_v=2, d=128, io_dtype=inputs.BF16,
+                              state_std=0.2)
+    out, st = gdn.prefill_two_level(dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["g"]), dev(x["beta"]),
+                                    segments=segments, state_in=dev(x["state_in"]), out_dtype=inputs.F32)
+    ro, rs = run_oracle(x)
+    eo, es = normwise(host(out), ro), normwise(host(st), rs)
+    print("two-level %d segments: out %.3g state %.3g" % (segments, eo, es))
+    assert eo <= 2e-3 and es <= 2e-3
+    # and against the one-level path on the same inputs
+    o1, s1 = run_gpu(x, inputs.F32)
+    assert normwise(host(out), host(o1)) <= 2e-3 and normwise(host(st), host(s1)) <= 2e-3
+
+
+def test_two_level_fp32_matches_oracle():
+    x = inputs.prefill_inputs(seed=95, total_tokens=1000, h_k=1, h_v=2, d=64, io_dtype=inputs.F32, state_std=0.3)
+    out, st = gdn.prefill_two_level(dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["g"]), dev(x["beta"]),
+                                    segments=4, state_in=dev(x["state_in"]), out_dtype=inputs.F32)
+    ro, rs = run_oracle(x)
+    assert normwise(host(out), ro) <= 1e-5 and normwise(host(st), rs) <= 1e-5
+
+
+def test_two_level_one_segment_is_prefill():
+    x = inputs.prefill_inputs(seed=96, total_tokens=700, h_k=2, h_v=4, d=128, io_dtype=inputs.BF16, state_std=0.1)
+    out, st = gdn.prefill_two_level(dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["g"]), dev(x["beta"]),
+                                    segments=1, state_in=dev(x["state_in"]), out_dtype=inputs.BF16)
+    o1, s1 = run_gpu(x, inputs.BF16)
+    assert torch.equal(out, o1) and torch.equal(st, s1)
