@@ -246,6 +246,24 @@ __device__ __forceinline__ Frag<OP> frag_row8(const OP* M, int ld, int rb, int k
     return f;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave, in registers (DPP):
+// Hillis-Steele inside each row of 16 lanes (row_shr 1, 2, 4, 8), then the
+// row totals are carried forward with row_bcast 15 (rows 1, 3) and
+// row_bcast 31 (rows 2, 3).  Lanes without a source add 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add_src(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xF, false));
+}
+__device__ __forceinline__ float wave_inclusive_sum(float x) {
+    x += dpp_add_src<0x111, 0xF>(x);  // row_shr:1
+    x += dpp_add_src<0x112, 0xF>(x);  // row_shr:2
+    x += dpp_add_src<0x114, 0xF>(x);  // row_shr:4
+    x += dpp_add_src<0x118, 0xF>(x);  // row_shr:8
+    x += dpp_add_src<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
+    x += dpp_add_src<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
+    return x;
+}
+
 // C + X Y for 16x16 fp32 matrices, X^T and Y (and C) in accumulator layout:
 // lane (j, q) holds M[4q + r][j] in element r.  Instruction e contracts over
 // k = 4q + e, taking X[i][4q + e] = X^T[4q + e][i] and Y[4q + e][j].
@@ -422,12 +440,7 @@ __global__ __launch_bounds__(PREP_THREADS, (prep_min_waves<D, OP>())) void chunk
             float gam = 0.f;
             if (wave == 0) {
                 const bool tl = lane < cnt;
-                float gx = tl ? in.g : 0.f;
-#pragma unroll
-                for (int off = 1; off < WAVE; off <<= 1) {
-                    const float o = __shfl_up(gx, off, WAVE);
-                    if (lane >= off) gx += o;
-                }
+                const float gx = wave_inclusive_sum(tl ? in.g : 0.f);
                 L.G[lane] = gx;
                 L.bt[lane] = tl ? in.b : 0.f;
                 gam = __expf(gx);
