@@ -299,6 +299,15 @@ def test_two_level_bf16_matches_oracle(segments):
     assert normwise(host(out), host(o1)) <= 2e-3 and normwise(host(st), host(s1)) <= 2e-3
 
 
+def test_two_level_bf16_d64_matches_oracle():
+    x = inputs.prefill_inputs(seed=94, total_tokens=777, h_k=2, h_v=4, d=64, io_dtype=inputs.BF16, state_std=0.3)
+    out, st = gdn.prefill_two_level(dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["g"]), dev(x["beta"]),
+                                    segments=3, state_in=dev(x["state_in"]), out_dtype=inputs.BF16)
+    ro, rs = run_oracle(x)
+    check_bf16_out(host(out), ro, 2e-3)
+    assert normwise(host(st), rs) <= 2e-3
+
+
 def test_two_level_fp32_matches_oracle():
     x = inputs.prefill_inputs(seed=95, total_tokens=1000, h_k=1, h_v=2, d=64, io_dtype=inputs.F32, state_std=0.3)
     out, st = gdn.prefill_two_level(dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["g"]), dev(x["beta"]),
