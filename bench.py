@@ -184,6 +184,105 @@ def two_level(L, gdn, inputs, to_dev, torch, np, dev):
         del q, k, v, g, b, s_in, out, s_out
 
 
+def prefill_configs(L, gdn, inputs, to_dev, torch, np, dev):
+    """Every prefill workload (single-head fp32 T=256, 4K, 128K with an initial state, 16 packed
+    sequences of drawn lengths) through gdn_prefill: time per call, tok/s, the per-kernel split
+    and both roofline fractions of the whole call.  Prints one JSON line per workload."""
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    for name, w in inputs.WORKLOADS.items():
+        if w.kind != "prefill":
+            continue
+        print("configs: generating %s" % name, file=sys.stderr, flush=True)
+        x = inputs.workload_inputs(w)
+        T, N, h_k, h_v, d = x["total_tokens"], x["num_seqs"], w.h_k, w.h_v, w.d
+        q, k, v, g, b = (to_dev(x[n]) for n in ("q", "k", "v", "g", "beta"))
+        s_in, cu = to_dev(x["state_in"]), to_dev(x["cu_seqlens"])
+        odt = torch.bfloat16 if w.out_dtype == inputs.BF16 else torch.float32
+        out = torch.empty((T, h_v, d), dtype=odt, device=dev)
+        s_out = torch.empty((N, h_v, d, d), dtype=torch.float32, device=dev)
+        desc = gdn.make_desc(num_seqs=N, total_tokens=T, h_k=h_k, h_v=h_v, d=d, io_dtype=w.io_dtype,
+                             out_dtype=w.out_dtype)
+        dref = ctypes.byref(desc)
+        wsb = gdn.gdn_prefill_workspace_bytes(desc)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        ptr = lambda z: None if z is None else z.data_ptr()  # noqa: E731
+        P = [ptr(z) for z in (q, k, v, g, b, s_in, out, s_out, cu)]
+
+        def call():
+            st = L.gdn_prefill(dref, P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[8], 64, ws.data_ptr(),
+                               wsb, sp)
+            if st:
+                raise gdn.GdnError(st, gdn.last_error())
+
+        def prep():
+            st = L.gdn_prefill_prepare(dref, P[0], P[1], P[2], P[3], P[4], P[8], 64, ws.data_ptr(), wsb, sp)
+            if st:
+                raise gdn.GdnError(st, gdn.last_error())
+
+        def scan():
+            st = L.gdn_prefill_scan(dref, P[5], P[6], P[7], P[8], 64, ws.data_ptr(), wsb, sp)
+            if st:
+                raise gdn.GdnError(st, gdn.last_error())
+
+        def direct():
+            st = L.gdn_prefill_direct(dref, P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[8], sp)
+            if st:
+                raise gdn.GdnError(st, gdn.last_error())
+
+        reps = 50 if T <= 8192 else 10
+        for _ in range(5):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+        for e in evs:
+            e[0].record(stream)
+            prep()
+            e[1].record(stream)
+            scan()
+            e[2].record(stream)
+        torch.cuda.synchronize()
+        us_prep = 1e3 * float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+        us_scan = 1e3 * float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+        us_direct = None
+        if T <= 8192:
+            for _ in range(3):
+                direct()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(reps):
+                direct()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us_direct = round(e0.elapsed_time(e1) * 1e3 / reps, 2)
+        io = 2 if w.io_dtype == inputs.BF16 else 4
+        ob = 2 if w.out_dtype == inputs.BF16 else 4
+        f_prep, f_scan, nbytes = algorithmic_prefill(T, h_v, h_k, d, out_bytes=ob, io_bytes=io,
+                                                     state_in=s_in is not None)
+        nbytes += (N - 1) * h_v * d * d * 4 * (2 if s_in is not None else 1)
+        mfma_peak = PEAK_FP16_TFLOPS if w.io_dtype == inputs.BF16 else 157.3
+        print(json.dumps({"prefill_config": {
+            "workload": name, "num_seqs": N, "total_tokens": T, "h_v": h_v, "h_k": h_k, "d": d,
+            "io_dtype": "bf16" if w.io_dtype == inputs.BF16 else "f32",
+            "state_in": "N(0,%g)" % w.state_std if s_in is not None else "zeros",
+            "us_per_call": round(us, 2), "tok_per_s": T / us * 1e6,
+            "kernels_us": {"chunk_prep": round(us_prep, 2), "chunk_scan": round(us_scan, 2)},
+            "direct_us": us_direct,
+            "mfma_peak_tflops": mfma_peak,
+            "mfma_frac_whole_call": round((f_prep + f_scan) / (us * 1e-6) / (mfma_peak * 1e12), 4),
+            "hbm_frac_whole_call": round(nbytes / (us * 1e-6) / (PEAK_HBM_GBS * 1e9), 4),
+            "algorithmic_gflop": round((f_prep + f_scan) / 1e9, 3), "algorithmic_mib": round(nbytes / 2 ** 20, 2),
+            "reps": reps}}), flush=True)
+        del q, k, v, g, b, s_in, cu, out, s_out, ws, x
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -199,6 +298,9 @@ def main():
     ap.add_argument("--two-level", action="store_true",
                     help="instead of the benchmark line: time one long few-head prompt through gdn_prefill "
                          "and the two-level scan at several segment counts (one JSON line per shape)")
+    ap.add_argument("--configs", action="store_true",
+                    help="instead of the benchmark line: every prefill workload (fp32 single head, 4K, 128K, "
+                         "16 packed sequences) with tok/s and roofline fractions (one JSON line each)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on exactly one GPU; --gpus %d is not supported "
@@ -228,6 +330,9 @@ def main():
         return
     if args.two_level:
         two_level(L, gdn, inputs, to_dev, torch, np, dev)
+        return
+    if args.configs:
+        prefill_configs(L, gdn, inputs, to_dev, torch, np, dev)
         return
 
     # ---------------- prefill ----------------
