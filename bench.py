@@ -184,10 +184,11 @@ def two_level(L, gdn, inputs, to_dev, torch, np, dev):
         del q, k, v, g, b, s_in, out, s_out
 
 
-def prefill_configs(L, gdn, inputs, to_dev, torch, np, dev):
+def prefill_configs(L, gdn, inputs, to_dev, torch, np, dev, with_cpu=True):
     """Every prefill workload (single-head fp32 T=256, 4K, 128K with an initial state, 16 packed
     sequences of drawn lengths) through gdn_prefill: time per call, tok/s, the per-kernel split
-    and both roofline fractions of the whole call.  Prints one JSON line per workload."""
+    and both roofline fractions of the whole call; up to 8K tokens also the direct token scan and
+    the fp64 CPU oracle on one thread and on all usable cores.  Prints one JSON line per workload."""
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
     for name, w in inputs.WORKLOADS.items():
@@ -230,17 +231,25 @@ def prefill_configs(L, gdn, inputs, to_dev, torch, np, dev):
             if st:
                 raise gdn.GdnError(st, gdn.last_error())
 
-        reps = 50 if T <= 8192 else 10
-        for _ in range(5):
+        reps = 100 if T <= 8192 else 10
+
+        def timed(fn, n):
+            """Median over 5 repetitions of n back-to-back calls, µs per call."""
+            res = []
+            for _ in range(5):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(n):
+                    fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                res.append(e0.elapsed_time(e1) * 1e3 / n)
+            return float(np.median(res))
+
+        for _ in range(10):
             call()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            call()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / reps
+        us = timed(call, reps)
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
         for e in evs:
             e[0].record(stream)
@@ -249,19 +258,28 @@ def prefill_configs(L, gdn, inputs, to_dev, torch, np, dev):
             scan()
             e[2].record(stream)
         torch.cuda.synchronize()
-        us_prep = 1e3 * float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-        us_scan = 1e3 * float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+        us_prep = 1e3 * float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
+        us_scan = 1e3 * float(np.median([e[1].elapsed_time(e[2]) for e in evs]))
         us_direct = None
         if T <= 8192:
             for _ in range(3):
                 direct()
             torch.cuda.synchronize()
-            e0.record(stream)
-            for _ in range(reps):
-                direct()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            us_direct = round(e0.elapsed_time(e1) * 1e3 / reps, 2)
+            us_direct = round(timed(direct, 10 if T > 1024 else reps), 2)
+        cpu = None
+        if with_cpu and T <= 8192:
+            from oracle import oracle
+            ncpu = len(os.sched_getaffinity(0))
+            cpu = {}
+            for threads in sorted({1, max(1, min(N * h_v, ncpu))}):
+                ts = []
+                for _ in range(3):
+                    t0 = time.perf_counter()
+                    oracle.scan(x["q"], x["k"], x["v"], x["g"], x["beta"], h_k=h_k, h_v=h_v, state_in=x["state_in"],
+                                cu_seqlens=x["cu_seqlens"], threads=threads)
+                    ts.append(time.perf_counter() - t0)
+                cpu["oracle_s_%d_threads" % threads] = round(float(np.median(ts)), 4)
+            cpu["host_cores"] = ncpu
         io = 2 if w.io_dtype == inputs.BF16 else 4
         ob = 2 if w.out_dtype == inputs.BF16 else 4
         f_prep, f_scan, nbytes = algorithmic_prefill(T, h_v, h_k, d, out_bytes=ob, io_bytes=io,
@@ -279,7 +297,8 @@ def prefill_configs(L, gdn, inputs, to_dev, torch, np, dev):
             "mfma_frac_whole_call": round((f_prep + f_scan) / (us * 1e-6) / (mfma_peak * 1e12), 4),
             "hbm_frac_whole_call": round(nbytes / (us * 1e-6) / (PEAK_HBM_GBS * 1e9), 4),
             "algorithmic_gflop": round((f_prep + f_scan) / 1e9, 3), "algorithmic_mib": round(nbytes / 2 ** 20, 2),
-            "reps": reps}}), flush=True)
+            "reps": reps, "timing": "median of 5 repetitions of back-to-back calls after 10 warm-up calls",
+            "cpu_oracle": cpu}}), flush=True)
         del q, k, v, g, b, s_in, cu, out, s_out, ws, x
 
 
@@ -332,7 +351,7 @@ def main():
         two_level(L, gdn, inputs, to_dev, torch, np, dev)
         return
     if args.configs:
-        prefill_configs(L, gdn, inputs, to_dev, torch, np, dev)
+        prefill_configs(L, gdn, inputs, to_dev, torch, np, dev, with_cpu=not args.no_cpu_baseline)
         return
 
     # ---------------- prefill ----------------
