@@ -66,30 +66,27 @@ __device__ __forceinline__ void decode_load(DecodeIn<D>& in, const float* __rest
 
 // One token of the recurrence on the register-resident state slices `sr`
 // (updated in place); writes the token's output o = S q^ at `orow` (the
-// output row of this unit and token).
+// output row of this unit and token).  `ub` is this wave's 32-float LDS
+// area, through which u is broadcast to the lanes of its row group.
+// Cross-lane sums run on DPP and v_permlane16_swap (no LDS round trips).
 template <int D, bool OUT_BF16>
 __device__ __forceinline__ void decode_token(float4 (&sr)[D / 8], const float (&kin)[4], const float (&qin)[4],
                                              float vin, float gin, float bin, void* out, size_t orow, int l2norm,
-                                             float scale, int wave, int lane) {
+                                             float scale, float* ub, int wave, int lane) {
     constexpr int LPR = D / 4, RPI = WAVE / LPR, NL = LPR / 2;
     const int c = lane % LPR, sub = lane / LPR;
     const float alpha = expf(gin);
     float ssk = 0.f, ssq = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) { ssk += kin[e] * kin[e]; ssq += qin[e] * qin[e]; }
-#pragma unroll
-    for (int mask = LPR / 2; mask >= 1; mask >>= 1) {
-        ssk += shfl_xor(ssk, mask);
-        ssq += shfl_xor(ssq, mask);
-    }
+    ssk = lane_group_sum<LPR>(ssk);
+    ssq = lane_group_sum<LPR>(ssq);
     const float rk = l2norm ? 1.0f / sqrtf(ssk + 1e-6f) : 1.0f;
     const float rq = (l2norm ? 1.0f / sqrtf(ssq + 1e-6f) : 1.0f) * scale;
     float kx[4], qx[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) { kx[e] = kin[e] * rk; qx[e] = qin[e] * rq; }
-    float kq = kx[0] * qx[0] + kx[1] * qx[1] + kx[2] * qx[2] + kx[3] * qx[3];
-#pragma unroll
-    for (int mask = LPR / 2; mask >= 1; mask >>= 1) kq += shfl_xor(kq, mask);
+    const float kq = lane_group_sum<LPR>(kx[0] * qx[0] + kx[1] * qx[1] + kx[2] * qx[2] + kx[3] * qx[3]);
 
     // partial row sums: x[m] = (S k^) part, x[NL + m] = (S q^) part
     float x[LPR];
@@ -99,36 +96,35 @@ __device__ __forceinline__ void decode_token(float4 (&sr)[D / 8], const float (&
         x[m] = sm.x * kx[0] + sm.y * kx[1] + sm.z * kx[2] + sm.w * kx[3];
         x[NL + m] = sm.x * qx[0] + sm.y * qx[1] + sm.z * qx[2] + sm.w * qx[3];
     }
-    // reduce-scatter over the LPR lanes of each row group: afterwards lane c holds x[c] summed
-#pragma unroll
-    for (int half = LPR / 2; half >= 1; half >>= 1) {
-        const bool upper = (c & half) != 0;
-#pragma unroll
-        for (int i = 0; i < half; ++i) {
-            const float send = upper ? x[i] : x[i + half];
-            const float keep = upper ? x[i + half] : x[i];
-            x[i] = keep + shfl_xor(send, half);
-        }
-    }
-    const float red = x[0];
+    // afterwards lane c holds x[c] summed over its row group
+    const float red = reduce_scatter<LPR>(x, c);
     // lanes c < NL: row (c) has p = S k^ ; lanes c >= NL: row (c - NL) has S q^
     const int mrow = (c < NL) ? c : c - NL;
     const int row = wave * 32 + mrow * RPI + sub;
     float u = 0.f;
     if (c < NL) u = bin * (vin - alpha * red);
-    const float u_pair = shfl_xor(u, NL);
+    // lane c >= NL takes u from lane c - NL
+    float u_pair;
+    if constexpr (NL == 16) u_pair = permlane16_swap(u, u).x;
+    else u_pair = row_partner<8>(u);
     if (c >= NL) store1<OUT_BF16>(out, orow * D + row, alpha * red + u_pair * kq);
 
-    // rank-1 update; u of row m lives in lane (group base + m)
-    const int base = lane - c;
+    // rank-1 update; u of row m of this row group, broadcast through LDS
+    // (one wave's LDS operations complete in order)
+    if (c < NL) ub[sub * NL + c] = u;
+    float um[NL];
+#pragma unroll
+    for (int j = 0; j < NL / 4; ++j) {
+        const float4 t = *reinterpret_cast<const float4*>(ub + sub * NL + 4 * j);
+        um[4 * j] = t.x; um[4 * j + 1] = t.y; um[4 * j + 2] = t.z; um[4 * j + 3] = t.w;
+    }
 #pragma unroll
     for (int m = 0; m < NL; ++m) {
-        const float um = __shfl(u, base + m, WAVE);
         float4 sm = sr[m];
-        sm.x = alpha * sm.x + um * kx[0];
-        sm.y = alpha * sm.y + um * kx[1];
-        sm.z = alpha * sm.z + um * kx[2];
-        sm.w = alpha * sm.w + um * kx[3];
+        sm.x = alpha * sm.x + um[m] * kx[0];
+        sm.y = alpha * sm.y + um[m] * kx[1];
+        sm.z = alpha * sm.z + um[m] * kx[2];
+        sm.w = alpha * sm.w + um[m] * kx[3];
         sr[m] = sm;
     }
 }
@@ -145,7 +141,7 @@ __device__ __forceinline__ void state_store(const float4 (&sr)[D / 8], float* __
 
 template <int D, bool OUT_BF16>
 __device__ __forceinline__ void decode_compute(DecodeIn<D>& in, float* __restrict__ state, void* out, int unit,
-                                               int h_v, int l2norm, float scale, int wave, int lane) {
+                                               int h_v, int l2norm, float scale, float* ub, int wave, int lane) {
     if (in.slot < 0) {  // skipped: zero outputs, state untouched
         constexpr int LPR = D / 4, RPI = WAVE / LPR, NL = LPR / 2;
         const int c = lane % LPR, sub = lane / LPR;
@@ -153,7 +149,8 @@ __device__ __forceinline__ void decode_compute(DecodeIn<D>& in, float* __restric
         return;
     }
     const int h = unit % h_v;
-    decode_token<D, OUT_BF16>(in.s, in.kx, in.qx, in.v, in.g, in.b, out, (size_t)unit, l2norm, scale, wave, lane);
+    decode_token<D, OUT_BF16>(in.s, in.kx, in.qx, in.v, in.g, in.b, out, (size_t)unit, l2norm, scale, ub, wave,
+                              lane);
     state_store<D>(in.s, state + ((size_t)in.slot * h_v + h) * D * D, wave, lane);
 }
 
@@ -169,17 +166,19 @@ __global__ __launch_bounds__(2 * D) void decode_step_kernel(
     int l2norm, float scale) {
     const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
     const int stride = gridDim.x, last = units - 1;
+    __shared__ __align__(16) float ubuf[(D / 32) * 32];
+    float* ub = ubuf + wave * 32;
     int u = blockIdx.x;
     if (u > last) return;
     DecodeIn<D> A, B;
     decode_load<D, IN_BF16>(A, state, slots, num_slots, q, k, v, g, beta, u, h_k, h_v, wave, lane);
     for (;;) {
         decode_load<D, IN_BF16>(B, state, slots, num_slots, q, k, v, g, beta, min(u + stride, last), h_k, h_v, wave, lane);
-        decode_compute<D, OUT_BF16>(A, state, out, u, h_v, l2norm, scale, wave, lane);
+        decode_compute<D, OUT_BF16>(A, state, out, u, h_v, l2norm, scale, ub, wave, lane);
         u += stride;
         if (u > last) break;
         decode_load<D, IN_BF16>(A, state, slots, num_slots, q, k, v, g, beta, min(u + stride, last), h_k, h_v, wave, lane);
-        decode_compute<D, OUT_BF16>(B, state, out, u, h_v, l2norm, scale, wave, lane);
+        decode_compute<D, OUT_BF16>(B, state, out, u, h_v, l2norm, scale, ub, wave, lane);
         u += stride;
         if (u > last) break;
     }
@@ -190,9 +189,11 @@ __global__ __launch_bounds__(2 * D) void decode_step_kernel(
 // three distinct workload shapes", runs prefill either as this direct scan or
 // in blocks; which is faster depends on the shape.  One workgroup per
 // (sequence, v-head) unit loads its state once, walks the sequence's tokens
-// with the next token's inputs loaded while the current one computes, and
-// writes the state once.  Sequence n spans tokens [cu[n], cu[n+1]), both
+// with the inputs of the next DIRECT_PREFETCH tokens in flight while one
+// computes, and writes the state once.  Sequence n spans tokens [cu[n], cu[n+1]), both
 // clamped into [0, T] (an empty or inverted range has no tokens).
+constexpr int DIRECT_PREFETCH = 4;  // tokens whose inputs are loaded ahead
+
 template <int D, bool IN_BF16>
 struct TokIn {
     float kx[4], qx[4];
@@ -228,6 +229,8 @@ __global__ __launch_bounds__(2 * D) void direct_scan_kernel(
         b0 = min(max(cu[n], 0), T);
         e0 = min(max(cu[n + 1], b0), T);
     }
+    __shared__ __align__(16) float ubuf[(D / 32) * 32];
+    float* ub = ubuf + wave * 32;
     float4 sr[D / 8];
     const size_t sbase = (size_t)unit * D * D;
 #pragma unroll
@@ -236,15 +239,23 @@ __global__ __launch_bounds__(2 * D) void direct_scan_kernel(
         sr[m] = state_in ? *reinterpret_cast<const float4*>(state_in + off) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     if (e0 > b0) {
-        TokIn<D, IN_BF16> A, B;
-        token_load<D, IN_BF16>(A, q, k, v, g, beta, (size_t)b0, h, hk, h_k, h_v, wave, lane);
-        for (int t = b0;;) {
-            token_load<D, IN_BF16>(B, q, k, v, g, beta, (size_t)min(t + 1, e0 - 1), h, hk, h_k, h_v, wave, lane);
-            decode_token<D, OUT_BF16>(sr, A.kx, A.qx, A.v, A.g, A.b, out, (size_t)t * h_v + h, l2norm, scale, wave, lane);
-            if (++t >= e0) break;
-            token_load<D, IN_BF16>(A, q, k, v, g, beta, (size_t)min(t + 1, e0 - 1), h, hk, h_k, h_v, wave, lane);
-            decode_token<D, OUT_BF16>(sr, B.kx, B.qx, B.v, B.g, B.b, out, (size_t)t * h_v + h, l2norm, scale, wave, lane);
-            if (++t >= e0) break;
+        // the inputs of the next P tokens are in flight while a token computes
+        // (past the end the last token is read again, unused)
+        TokIn<D, IN_BF16> buf[DIRECT_PREFETCH];
+#pragma unroll
+        for (int i = 0; i < DIRECT_PREFETCH; ++i)
+            token_load<D, IN_BF16>(buf[i], q, k, v, g, beta, (size_t)min(b0 + i, e0 - 1), h, hk, h_k, h_v, wave, lane);
+        for (int t = b0; t < e0; t += DIRECT_PREFETCH) {
+#pragma unroll
+            for (int i = 0; i < DIRECT_PREFETCH; ++i) {
+                if (t + i < e0) {
+                    const TokIn<D, IN_BF16> cur = buf[i];
+                    token_load<D, IN_BF16>(buf[i], q, k, v, g, beta, (size_t)min(t + i + DIRECT_PREFETCH, e0 - 1), h,
+                                           hk, h_k, h_v, wave, lane);
+                    decode_token<D, OUT_BF16>(sr, cur.kx, cur.qx, cur.v, cur.g, cur.b, out, (size_t)(t + i) * h_v + h,
+                                              l2norm, scale, ub, wave, lane);
+                }
+            }
         }
     }
     if (state_out) state_store<D>(sr, state_out + sbase, wave, lane);

@@ -206,4 +206,75 @@ __device__ __forceinline__ float group_max(float x) {
     return x;
 }
 
+// Lanes i and i ^ 16 trade values across the two 16-lane rows of each
+// 32-lane half (v_permlane16_swap: the odd rows of the first operand trade
+// places with the even rows of the second).  With a in every lane and b in
+// every lane, an even-row lane gets (its own a, its partner's a) and an
+// odd-row lane gets (its partner's b, its own b).
+struct F2 {
+    float x, y;
+};
+__device__ __forceinline__ F2 permlane16_swap(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+
+// Partner lane of a butterfly step inside a row of 16 lanes (DPP): lane
+// i ^ H for H = 8, 2, 1, and the mirror lane (i & ~7) | (7 - (i & 7)) for
+// H = 4, which differs from i in bit 2 (all a butterfly step needs).
+template <int H>
+__device__ __forceinline__ float row_partner(float x) {
+    static_assert(H == 8 || H == 4 || H == 2 || H == 1, "butterfly step inside a row");
+    if constexpr (H == 8) return dpp<0x128>(x);
+    else if constexpr (H == 4) return dpp<0x141>(x);
+    else if constexpr (H == 2) return dpp<0x4E>(x);
+    else return dpp<0xB1>(x);
+}
+
+// One butterfly step of reduce_scatter inside a row of 16 lanes.
+template <int H, int N>
+__device__ __forceinline__ void rs_step(float (&x)[N], int c) {
+    const bool upper = (c & H) != 0;
+#pragma unroll
+    for (int i = 0; i < H; ++i) {
+        const float lo = x[i] + row_partner<H>(x[i]);
+        const float hi = x[i + H] + row_partner<H>(x[i + H]);
+        x[i] = upper ? hi : lo;
+    }
+}
+
+// Sum over aligned groups of N = 16 or 32 lanes, result in every lane.
+template <int N>
+__device__ __forceinline__ float lane_group_sum(float x) {
+    static_assert(N == 16 || N == 32, "group of 16 or 32 lanes");
+    x = group_sum<16>(x);
+    if constexpr (N == 32) {
+        const F2 r = permlane16_swap(x, x);
+        x = r.x + r.y;
+    }
+    return x;
+}
+
+// Reduce-scatter over aligned groups of N = 16 or 32 lanes: lane c of a group
+// (c = lane % N) holds x[0..N-1]; afterwards x[0] is the group's sum of
+// element c.  Each step halves the elements a lane carries: the lane whose
+// step bit is clear keeps the lower half and the other the upper half, and
+// each adds its partner's copy of the half it keeps.
+template <int N>
+__device__ __forceinline__ float reduce_scatter(float (&x)[N], int c) {
+    static_assert(N == 16 || N == 32, "group of 16 or 32 lanes");
+    if constexpr (N == 32) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const F2 r = permlane16_swap(x[i], x[i + 16]);
+            x[i] = r.x + r.y;
+        }
+    }
+    rs_step<8>(x, c);
+    rs_step<4>(x, c);
+    rs_step<2>(x, c);
+    rs_step<1>(x, c);
+    return x[0];
+}
+
 }  // namespace gdn
