@@ -31,7 +31,7 @@ def run_oracle(x, **kw):
 @pytest.mark.parametrize("io", [inputs.BF16, inputs.F32])
 @pytest.mark.parametrize("out_dt", [inputs.F32, inputs.BF16])
 def test_direct_varlen_grid(d, io, out_dt):
-    lens = [5, 0, 17, 1, 64, 130]
+    lens = [5, 0, 17, 1, 64, 130, 2, 3]  # around and below the four-token input prefetch
     x = inputs.prefill_inputs(seed=40 + d + io, lengths=lens, h_k=2, h_v=4, d=d, io_dtype=io, state_std=0.2)
     out, st = run_direct(x, out_dt)
     ro, rs = run_oracle(x)

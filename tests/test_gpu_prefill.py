@@ -107,6 +107,13 @@ def test_prefill_varlen_workload_sampled():
         r = ro[sub["cu"][i]:sub["cu"][i + 1], 0]
         assert normwise(go, r) <= 2e-3, (n, h, normwise(go, r))
         assert normwise(s[n, h], rs[i, 0]) <= 2e-3
+    # bf16 outputs, as the timed configuration writes them
+    del out, st
+    out_b, st_b = run_gpu(x, inputs.BF16)
+    o, s = host(out_b), host(st_b)
+    for i, (n, h) in enumerate(units):
+        check_bf16_out(o[cu[n]:cu[n + 1], h], ro[sub["cu"][i]:sub["cu"][i + 1], 0], 2e-3)
+        assert normwise(s[n, h], rs[i, 0]) <= 2e-3
 
 
 def test_prefill_128k_workload_sampled():
@@ -125,6 +132,13 @@ def test_prefill_128k_workload_sampled():
         es = normwise(s[0, h], rs[i, 0])
         print("128k head %d: out %.3g state %.3g" % (h, eo, es))
         assert eo <= 2e-3 and es <= 2e-3
+    # bf16 outputs, as the timed configuration writes them
+    del out, st
+    out_b, st_b = run_gpu(x, inputs.BF16)
+    o, s = host(out_b), host(st_b)
+    for i, (n, h) in enumerate(units):
+        check_bf16_out(o[:, h], ro[i * T:(i + 1) * T, 0], 2e-3)
+        assert normwise(s[0, h], rs[i, 0]) <= 2e-3
 
 
 # ---- row slices of the state ------------------------------------------------------------------
