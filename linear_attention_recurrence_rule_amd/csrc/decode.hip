@@ -18,8 +18,9 @@
 // Layout: a workgroup has d/32 waves, and each wave owns 32 state rows.  A
 // lane holds 4 consecutive entries (16 bytes) of one row, so d/4 lanes cover a
 // row, and each wave-wide load reads 1 KiB of contiguous state.  The row sums
-// are a reduce-scatter across the d/4 lanes of a row.  After it, lane c of a
-// row group holds either S k^ or S q^ of one row.  A grid of a few workgroups
+// are a reduce-scatter across the d/4 lanes of a row (DPP inside 16-lane rows,
+// v_permlane16_swap between them).  After it, lane c of a row group holds
+// either S k^ or S q^ of one row.  A grid of a few workgroups
 // per compute unit walks the (sequence, v-head) units.  The next unit's state
 // and token inputs are loaded while the current unit computes and stores.
 #include "gdn_device.h"

@@ -168,8 +168,6 @@ __device__ __forceinline__ void frag_store(OP* base, int frag, int lane, const F
     }
 }
 
-__device__ __forceinline__ float shfl_xor(float x, int mask) { return __shfl_xor(x, mask, WAVE); }
-
 // Cross-lane moves inside a row of 16 lanes (DPP, no LDS round trip).
 // CTRL: quad_perm(1,0,3,2) = 0xB1, quad_perm(2,3,0,1) = 0x4E, row_ror:4 = 0x124,
 // row_ror:8 = 0x128, row_half_mirror = 0x141.
