@@ -10,7 +10,9 @@ The same JSON line also reports:
   * roofline of the dominant prefill kernel: algorithmic flops per launch over
     its average HIP-event duration, against the 2.5 PFLOP/s dense fp16
     matrix-core peak; the decode kernel's algorithmic bytes against 8 TB/s;
-  * cpu_baseline: the fp64 CPU oracle on this host, same workload.
+  * cpu_baseline: the fp64 CPU oracle on this host, same workload;
+  * ceilings: measured matrix-core and read-modify-write stream rates on this
+    GPU, and each roofline's fraction of them beside its fraction of the spec peak.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -84,6 +86,60 @@ def measured_traffic(kernel):
         return None
     return {"fetch_bytes": k["fetch_bytes"], "write_bytes": k["write_bytes"],
             "total_bytes": k["fetch_bytes"] + k["write_bytes"], "source": "profiles/hbm_traffic.md"}
+
+
+def measure_ceilings(torch, np, dev):
+    """What plain code reaches on this GPU, as second roofline denominators
+    (linear_attention_recurrence_rule_amd/libgdn_calibrate.so): a matrix-core loop of
+    64 x 128 x 128 fp16 products with register operands, and one in-place read-modify-write
+    pass over 128 MiB of random fp32 data (the decode step's state traffic).  Median of 5."""
+    path = os.path.join(ROOT, "linear_attention_recurrence_rule_amd", "libgdn_calibrate.so")
+    if not os.path.exists(path):
+        return None
+    C = ctypes.CDLL(path)
+    C.gdn_calib_mfma_f16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    C.gdn_calib_mfma_f16_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    C.gdn_calib_mfma_f16_flops.restype = ctypes.c_double
+    C.gdn_calib_rmw_f32.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+
+    def median_us(fn, reps):
+        res = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            res.append(e0.elapsed_time(e1) * 1e3 / reps)
+        return float(np.median(res))
+
+    wgs, iters = 8 * cus, 500
+    sink = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
+
+    def mfma():
+        st = C.gdn_calib_mfma_f16(iters, wgs, sink.data_ptr(), sp)
+        if st:
+            raise RuntimeError("gdn_calib_mfma_f16: hip error %d" % st)
+    for _ in range(2):
+        mfma()
+    us_mfma = median_us(mfma, 3)
+    x = torch.randn(32 << 20, dtype=torch.float32, device=dev)
+
+    def rmw():
+        st = C.gdn_calib_rmw_f32(x.data_ptr(), x.numel(), wgs, sp)
+        if st:
+            raise RuntimeError("gdn_calib_rmw_f32: hip error %d" % st)
+    for _ in range(3):
+        rmw()
+    us_rmw = median_us(rmw, 10)
+    del sink, x
+    return {"mfma_f16_tflops": round(C.gdn_calib_mfma_f16_flops(iters, wgs) / (us_mfma * 1e-6) / 1e12, 1),
+            "rmw_stream_gbs": round(2 * (32 << 20) * 4 / (us_rmw * 1e-6) / 1e9, 1),
+            "source": "libgdn_calibrate.so: fp16 matrix-core loop, 128 MiB fp32 read-modify-write stream"}
 
 
 def crossover(L, gdn, inputs, to_dev, torch, np, dev):
@@ -490,6 +546,11 @@ def main():
                                 "traffic": measured_traffic("decode_step")}}
     del dq, dk, dv, dg, db, state, dout
 
+    ceilings = measure_ceilings(torch, np, dev)
+    if ceilings:
+        roofline["frac_of_measured_ceiling"] = round(ach / ceilings["mfma_f16_tflops"], 4)
+        decode_info["roofline"]["frac_of_measured_ceiling"] = round(dec_gbs / ceilings["rmw_stream_gbs"], 4)
+
     if args.calibrate_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -521,6 +582,7 @@ def main():
         "config": {"workload": PREFILL_WL, "total_tokens": T, "h_v": h_v, "h_k": h_k, "d": d, "chunk": 64,
                    "io_dtype": "bf16", "out_dtype": "bf16", "state_in": "zeros"},
         "roofline": roofline, "cpu_baseline": cpu, "prefill": prefill_info, "decode": decode_info,
+        "ceilings": ceilings,
     }
     print(json.dumps(rec))
 

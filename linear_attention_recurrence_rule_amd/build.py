@@ -16,6 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgdn.so")
+CAL_LIB = os.path.join(HERE, "libgdn_calibrate.so")
 SOURCES = ["decode.hip", "prefill.hip", "api.cpp"]
 ARCH = "gfx950"
 
@@ -57,6 +58,14 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp%d" % os.getpid()
     subprocess.check_call([cc, "--offload-arch=" + ARCH, "-shared", "-fPIC"] + objs + ["-o", tmp])
     os.replace(tmp, LIB)
+    # the measured-ceiling kernels bench.py reports beside the spec peaks (not part of gdn.h)
+    tmp = CAL_LIB + ".tmp%d" % os.getpid()
+    out = subprocess.run([cc] + flags() + ["-shared", "-x", "hip", os.path.join(CSRC, "calibrate.hip"), "-o", tmp],
+                         stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if out.returncode:
+        sys.stderr.write(out.stdout)
+        raise RuntimeError("hipcc failed for: calibrate.hip")
+    os.replace(tmp, CAL_LIB)
     return LIB
 
 

@@ -298,3 +298,22 @@ def test_null_descriptor(L):
         gdn.GDN_ERR_INVALID_ARGUMENT
     assert gdn.lib().gdn_prefill_direct(None, None, None, None, None, None, None, None, None, None, None) == \
         gdn.GDN_ERR_INVALID_ARGUMENT
+
+
+def test_calibration_library_loads_and_rejects_bad_arguments():
+    """libgdn_calibrate.so (the measured-ceiling kernels bench.py reports) loads and checks its
+    arguments on the host; no launch is reached."""
+    from linear_attention_recurrence_rule_amd import build
+    path = build.CAL_LIB
+    if not os.path.exists(path):
+        build.build()
+    C = ctypes.CDLL(path)
+    for name in ("gdn_calib_mfma_f16", "gdn_calib_mfma_f16_flops", "gdn_calib_rmw_f32"):
+        assert hasattr(C, name), name
+    C.gdn_calib_mfma_f16_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    C.gdn_calib_mfma_f16_flops.restype = ctypes.c_double
+    assert C.gdn_calib_mfma_f16_flops(10, 3) == 2.0 * 16 * 128 * 128 * 10 * 3 * 4
+    C.gdn_calib_mfma_f16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    C.gdn_calib_rmw_f32.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    assert C.gdn_calib_mfma_f16(0, 8, None, None) != 0        # no iterations, no sink
+    assert C.gdn_calib_rmw_f32(None, 1024, 8, None) != 0      # no buffer
