@@ -38,6 +38,25 @@ def test_decode_small(d, io, out_dt):
         assert normwise(host(state), ref_state) <= tol
 
 
+@pytest.mark.parametrize("h_k,h_v", [(3, 3), (1, 8)])
+@pytest.mark.parametrize("d,io", [(128, inputs.BF16), (64, inputs.F32)])
+def test_decode_head_ratios(h_k, h_v, d, io):
+    """One and eight v-heads per k-head, three steps in place."""
+    N, steps = 5, 3
+    x = inputs.decode_inputs(seed=31 + h_v + d, num_seqs=N, steps=steps, h_k=h_k, h_v=h_v, d=d, io_dtype=io,
+                             state_std=0.3)
+    state = dev(x["state"])
+    ref_state = x["state"].astype(np.float64)
+    tol = 2e-3 if io == inputs.BF16 else 1e-5
+    for t in range(steps):
+        out = gdn.decode_step(dev(x["q"][t]), dev(x["k"][t]), dev(x["v"][t]), dev(x["g"][t]),
+                              dev(x["beta"][t]), state, out_dtype=inputs.F32)
+        ro, ref_state = oracle.decode_step(x["q"][t], x["k"][t], x["v"][t], x["g"][t], x["beta"][t],
+                                           ref_state, h_k=h_k, h_v=h_v)
+        assert normwise(host(out), ro) <= tol, normwise(host(out), ro)
+        assert normwise(host(state), ref_state) <= tol
+
+
 def test_decode_no_norm_and_scale():
     N, h_k, h_v, d = 2, 1, 2, 128
     x = inputs.decode_inputs(seed=5, num_seqs=N, steps=1, h_k=h_k, h_v=h_v, d=d, io_dtype=inputs.F32)

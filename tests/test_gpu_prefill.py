@@ -64,6 +64,22 @@ def test_bf16_d128_lengths(T):
     assert eo <= 2e-3 and es <= 2e-3
 
 
+@pytest.mark.parametrize("h_k,h_v", [(3, 3), (1, 4), (2, 16)])
+@pytest.mark.parametrize("d,io", [(128, inputs.BF16), (64, inputs.F32)])
+def test_head_ratios(h_k, h_v, d, io):
+    """v-heads per k-head of 1, 4 and 8 (the prep loops over a k-head's v-heads; the
+    scan maps each v-head to its k-head's key records), packed ragged sequences,
+    initial state."""
+    x = inputs.prefill_inputs(seed=90 + h_v + d, lengths=[70, 129, 1], h_k=h_k, h_v=h_v, d=d, io_dtype=io,
+                              state_std=0.1)
+    out, st = run_gpu(x, inputs.F32)
+    ro, rs = run_oracle(x)
+    tol = 1e-5 if io == inputs.F32 else 2e-3
+    eo, es = normwise(host(out), ro), normwise(host(st), rs)
+    print("h_k=%d h_v=%d d=%d: out %.3g state %.3g" % (h_k, h_v, d, eo, es))
+    assert eo <= tol and es <= tol
+
+
 def test_prefill_4k_workload():
     """T=4096, 32 v-heads over 16 q/k heads, d=128, bf16, zero state: full compare."""
     w = inputs.WORKLOADS["prefill_t4096_hv32_hk16_d128"]
