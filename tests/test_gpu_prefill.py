@@ -97,6 +97,22 @@ def test_many_packed_sequences():
     assert np.array_equal(host(st)[zero], x["state_in"][zero])
 
 
+@pytest.mark.parametrize("qk_scale", [2.0 ** 16, 2.0 ** -20])
+def test_extreme_qk_magnitudes(qk_scale):
+    """q and k multiplied by 2^16 (beyond the fp16 range unscaled) or 2^-20 (fp16
+    subnormals unscaled), exactly in bf16: the per-token power-of-two scaling keeps the
+    matrix-core operands in range, and the normalised result matches the oracle."""
+    x = inputs.prefill_inputs(seed=8, lengths=[150, 70], h_k=2, h_v=4, d=128, io_dtype=inputs.BF16, state_std=0.1)
+    for n in ("q", "k"):
+        x[n] = inputs.f32_to_bf16_bits(inputs.bf16_bits_to_f32(x[n]) * np.float32(qk_scale))
+    out, st = run_gpu(x, inputs.F32)
+    ro, rs = run_oracle(x)
+    eo, es = normwise(host(out), ro), normwise(host(st), rs)
+    print("q, k x %g: out %.3g state %.3g" % (qk_scale, eo, es))
+    assert np.isfinite(host(out)).all() and np.isfinite(host(st)).all()
+    assert eo <= 2e-3 and es <= 2e-3
+
+
 def test_prefill_4k_workload():
     """T=4096, 32 v-heads over 16 q/k heads, d=128, bf16, zero state: full compare."""
     w = inputs.WORKLOADS["prefill_t4096_hv32_hk16_d128"]
