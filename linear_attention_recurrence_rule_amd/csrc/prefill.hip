@@ -129,6 +129,13 @@ constexpr int LDF = CHUNK + 4;                                  // fp32 64x64 ti
 // (64 lanes x 8 elements per fragment, one contiguous 16-byte read per lane).
 // Region b holds, by phase: A (strictly lower) with X^T = ((I + A)^{-1})^T in
 // its upper triangle, then the values V, then -W.
+// The in-block cumulative log-decay G.  Decay ratios are exp(G_i - G_j); after
+// a run of strong decay both G_i and G_j are large and their fp32 difference
+// carries ~1e-7 |G| of cancellation error.  fp16 operands absorb that; the
+// fp32 path (a 1e-5 budget) keeps G in fp64 and takes the differences there.
+template <typename OP> struct GType { using T = float; };
+template <> struct GType<float> { using T = double; };
+
 template <int D, typename OP>
 struct PrepLds {
     static constexpr int LK = ldsk<D, OP>();
@@ -141,7 +148,8 @@ struct PrepLds {
     } b;
     OP t[CHUNK * CHUNK];  // T = X diag(beta), fragment-major: (row block, 32-column block) fragments
     OP p[CHUNK * CHUNK];  // P = lower_incl(D o Q K^T), likewise
-    float G[CHUNK], ck[CHUNK], cq[CHUNK], bt[CHUNK], gck[CHUNK], gcq[CHUNK];
+    typename GType<OP>::T G[CHUNK];
+    float ck[CHUNK], cq[CHUNK], bt[CHUNK], gck[CHUNK], gcq[CHUNK];
     int zero;  // holds 0 (see chunk_prep_kernel)
 };
 
@@ -261,6 +269,23 @@ __device__ __forceinline__ float wave_inclusive_sum(float x) {
     x += dpp_add_src<0x118, 0xF>(x);  // row_shr:8
     x += dpp_add_src<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
     x += dpp_add_src<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
+    return x;
+}
+// The same in fp64: each DPP move carries both 32-bit halves.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_add_src64(double x) {
+    const unsigned long long b = (unsigned long long)__double_as_longlong(x);
+    const unsigned lo = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)b, CTRL, ROW_MASK, 0xF, false);
+    const unsigned hi = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)(b >> 32), CTRL, ROW_MASK, 0xF, false);
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+__device__ __forceinline__ double wave_inclusive_sum(double x) {
+    x += dpp_add_src64<0x111, 0xF>(x);
+    x += dpp_add_src64<0x112, 0xF>(x);
+    x += dpp_add_src64<0x114, 0xF>(x);
+    x += dpp_add_src64<0x118, 0xF>(x);
+    x += dpp_add_src64<0x142, 0xA>(x);
+    x += dpp_add_src64<0x143, 0xC>(x);
     return x;
 }
 
@@ -437,13 +462,21 @@ __global__ __launch_bounds__(PREP_THREADS, (prep_min_waves<D, OP>())) void chunk
                                : nullptr;
 
             // ---- 1b. cumulative log-decay G, gamma = exp(G), beta ---------------------------
+            using GT = typename GType<OP>::T;
             float gam = 0.f;
             if (wave == 0) {
                 const bool tl = lane < cnt;
-                const float gx = wave_inclusive_sum(tl ? in.g : 0.f);
-                L.G[lane] = gx;
-                L.bt[lane] = tl ? in.b : 0.f;
-                gam = __expf(gx);
+                if constexpr (sizeof(GT) == 4) {
+                    const float gx = wave_inclusive_sum(tl ? in.g : 0.f);
+                    L.G[lane] = gx;
+                    L.bt[lane] = tl ? in.b : 0.f;
+                    gam = __expf(gx);
+                } else {
+                    const GT gx = wave_inclusive_sum(tl ? (GT)in.g : (GT)0);
+                    L.G[lane] = gx;
+                    L.bt[lane] = tl ? in.b : 0.f;
+                    gam = __expf((float)gx);
+                }
             }
             if (nxt) in.load_gb(g, beta, nx_tok0, T, h_v, nx_h);
             lds_barrier();
@@ -464,14 +497,27 @@ __global__ __launch_bounds__(PREP_THREADS, (prep_min_waves<D, OP>())) void chunk
                     for (int kb = 0; kb < D / 32; ++kb)
                         mma(acc, frag_row8<OP>(L.k, LK, mb, kb, lane), frag_row8<OP>(L.k, LK, nb, kb, lane));
                     const int j = 16 * nb + li, i0 = 16 * mb + 4 * lq;
-                    const float Gj = L.G[j], ckj = L.ck[j];
-                    const f4_t Gi = *reinterpret_cast<const f4_t*>(&L.G[i0]);
-                    const f4_t cki = *reinterpret_cast<const f4_t*>(&L.ck[i0]);
-                    const f4_t bti = *reinterpret_cast<const f4_t*>(&L.bt[i0]);
+                    if constexpr (sizeof(GT) == 4) {
+                        const float Gj = L.G[j], ckj = L.ck[j];
+                        const f4_t Gi = *reinterpret_cast<const f4_t*>(&L.G[i0]);
+                        const f4_t cki = *reinterpret_cast<const f4_t*>(&L.ck[i0]);
+                        const f4_t bti = *reinterpret_cast<const f4_t*>(&L.bt[i0]);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int i = i0 + r;
-                        if (j < i) L.b.ax[i * LDF + j] = bti[r] * __expf(Gi[r] - Gj) * acc[r] * cki[r] * ckj;
+                        for (int r = 0; r < 4; ++r) {
+                            const int i = i0 + r;
+                            if (j < i) L.b.ax[i * LDF + j] = bti[r] * __expf(Gi[r] - Gj) * acc[r] * cki[r] * ckj;
+                        }
+                    } else {
+                        const GT Gj = L.G[j];
+                        const float ckj = L.ck[j];
+                        const f4_t cki = *reinterpret_cast<const f4_t*>(&L.ck[i0]);
+                        const f4_t bti = *reinterpret_cast<const f4_t*>(&L.bt[i0]);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int i = i0 + r;
+                            if (j < i)
+                                L.b.ax[i * LDF + j] = bti[r] * __expf((float)(L.G[i] - Gj)) * acc[r] * cki[r] * ckj;
+                        }
                     }
                 } else {
                     // The transposed tile K Q^T: lane (j, q) gets (Q K^T)[16mb + j][16nb + 4q + r],
@@ -480,14 +526,25 @@ __global__ __launch_bounds__(PREP_THREADS, (prep_min_waves<D, OP>())) void chunk
                     for (int kb = 0; kb < D / 32; ++kb)
                         mma(acc, frag_row8<OP>(L.k, LK, nb, kb, lane), frag_row8<OP>(L.q, LK, mb, kb, lane));
                     const int i = 16 * mb + li, c0 = 16 * nb + 4 * lq;
-                    const float Gi = L.G[i], cqi = L.cq[i];
-                    const f4_t Gc = *reinterpret_cast<const f4_t*>(&L.G[c0]);
-                    const f4_t ckc = *reinterpret_cast<const f4_t*>(&L.ck[c0]);
                     f4_t pv;
+                    if constexpr (sizeof(GT) == 4) {
+                        const float Gi = L.G[i], cqi = L.cq[i];
+                        const f4_t Gc = *reinterpret_cast<const f4_t*>(&L.G[c0]);
+                        const f4_t ckc = *reinterpret_cast<const f4_t*>(&L.ck[c0]);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float dec = (c0 + r <= i) ? __expf(fminf(Gi - Gc[r], 0.f)) : 0.f;
-                        pv[r] = dec * acc[r] * cqi * ckc[r];
+                        for (int r = 0; r < 4; ++r) {
+                            const float dec = (c0 + r <= i) ? __expf(fminf(Gi - Gc[r], 0.f)) : 0.f;
+                            pv[r] = dec * acc[r] * cqi * ckc[r];
+                        }
+                    } else {
+                        const GT Gi = L.G[i];
+                        const float cqi = L.cq[i];
+                        const f4_t ckc = *reinterpret_cast<const f4_t*>(&L.ck[c0]);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const float dec = (c0 + r <= i) ? __expf(fminf((float)(Gi - L.G[c0 + r]), 0.f)) : 0.f;
+                            pv[r] = dec * acc[r] * cqi * ckc[r];
+                        }
                     }
                     store_part<OP>(L.p, mb * 2 + nb / 2, nb % 2, lane, pv);
                 }
@@ -688,9 +745,16 @@ __global__ __launch_bounds__(PREP_THREADS, (prep_min_waves<D, OP>())) void chunk
 
             // ---- 8. s_t = exp(G_n - G_t) c_t and gamma_n -------------------------------------------
             if (tid < CHUNK) {
-                const float Gn = L.G[max(cnt - 1, 0)];
-                reinterpret_cast<float*>(rec + RC::S)[tid] = (tid < cnt) ? __expf(Gn - L.G[tid]) * L.ck[tid] : 0.f;
-                if (tid == 0) reinterpret_cast<float*>(rec + RC::M)[0] = __expf(Gn);
+                if constexpr (sizeof(GT) == 4) {
+                    const float Gn = L.G[max(cnt - 1, 0)];
+                    reinterpret_cast<float*>(rec + RC::S)[tid] = (tid < cnt) ? __expf(Gn - L.G[tid]) * L.ck[tid] : 0.f;
+                    if (tid == 0) reinterpret_cast<float*>(rec + RC::M)[0] = __expf(Gn);
+                } else {
+                    const GT Gn = L.G[max(cnt - 1, 0)];
+                    reinterpret_cast<float*>(rec + RC::S)[tid] =
+                        (tid < cnt) ? __expf((float)(Gn - L.G[tid])) * L.ck[tid] : 0.f;
+                    if (tid == 0) reinterpret_cast<float*>(rec + RC::M)[0] = __expf((float)Gn);
+                }
             }
 
             lds_barrier();  // LDS is reused by the next task

@@ -113,6 +113,29 @@ def test_extreme_qk_magnitudes(qk_scale):
     assert eo <= 2e-3 and es <= 2e-3
 
 
+@pytest.mark.parametrize("d,io", [(128, inputs.BF16), (64, inputs.F32)])
+def test_extreme_gates(d, io):
+    """Gates at their ends, mixed within blocks: no decay (g = 0), near-total forgetting
+    (g = -30, a state reset inside a block), beta = 0 (no write) and beta = 1 (full
+    overwrite), among ordinary values."""
+    x = inputs.prefill_inputs(seed=12 + d, lengths=[200, 65], h_k=2, h_v=4, d=d, io_dtype=io, state_std=0.2)
+    rng = np.random.default_rng(13)
+    pick = rng.integers(0, 4, x["g"].shape)
+    x["g"] = np.where(pick == 0, 0.0, np.where(pick == 1, -30.0, x["g"])).astype(np.float32)
+    pick = rng.integers(0, 4, x["beta"].shape)
+    x["beta"] = np.where(pick == 0, 0.0, np.where(pick == 1, 1.0, x["beta"])).astype(np.float32)
+    tol = 1e-5 if io == inputs.F32 else 2e-3
+    ro, rs = run_oracle(x)
+    for run in (lambda: run_gpu(x, inputs.F32),
+                lambda: gdn.prefill_direct(dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["g"]), dev(x["beta"]),
+                                           state_in=dev(x["state_in"]), cu_seqlens=dev(x["cu_seqlens"]),
+                                           out_dtype=inputs.F32)):
+        out, st = run()
+        eo, es = normwise(host(out), ro), normwise(host(st), rs)
+        print("extreme gates d=%d: out %.3g state %.3g" % (d, eo, es))
+        assert eo <= tol and es <= tol
+
+
 def test_prefill_4k_workload():
     """T=4096, 32 v-heads over 16 q/k heads, d=128, bf16, zero state: full compare."""
     w = inputs.WORKLOADS["prefill_t4096_hv32_hk16_d128"]
