@@ -57,6 +57,28 @@ def test_decode_head_ratios(h_k, h_v, d, io):
         assert normwise(host(state), ref_state) <= tol
 
 
+def test_decode_extreme_gates():
+    """Decode steps with alpha = 1 (g = 0), near-total forgetting (g = -30), beta = 0 and
+    beta = 1 mixed across heads and steps."""
+    N, h_k, h_v, d, steps = 4, 2, 4, 128, 4
+    x = inputs.decode_inputs(seed=41, num_seqs=N, steps=steps, h_k=h_k, h_v=h_v, d=d, io_dtype=inputs.BF16,
+                             state_std=0.3)
+    rng = np.random.default_rng(42)
+    pick = rng.integers(0, 4, x["g"].shape)
+    x["g"] = np.where(pick == 0, 0.0, np.where(pick == 1, -30.0, x["g"])).astype(np.float32)
+    pick = rng.integers(0, 4, x["beta"].shape)
+    x["beta"] = np.where(pick == 0, 0.0, np.where(pick == 1, 1.0, x["beta"])).astype(np.float32)
+    state = dev(x["state"])
+    ref_state = x["state"].astype(np.float64)
+    for t in range(steps):
+        out = gdn.decode_step(dev(x["q"][t]), dev(x["k"][t]), dev(x["v"][t]), dev(x["g"][t]),
+                              dev(x["beta"][t]), state, out_dtype=inputs.F32)
+        ro, ref_state = oracle.decode_step(x["q"][t], x["k"][t], x["v"][t], x["g"][t], x["beta"][t],
+                                           ref_state, h_k=h_k, h_v=h_v)
+        assert normwise(host(out), ro) <= 2e-3
+        assert normwise(host(state), ref_state) <= 2e-3
+
+
 def test_decode_no_norm_and_scale():
     N, h_k, h_v, d = 2, 1, 2, 128
     x = inputs.decode_inputs(seed=5, num_seqs=N, steps=1, h_k=h_k, h_v=h_v, d=d, io_dtype=inputs.F32)

@@ -136,6 +136,27 @@ def test_extreme_gates(d, io):
         assert eo <= tol and es <= tol
 
 
+def test_large_values_within_contract():
+    """Values up to ~2^12 and an initial state of std 100 (inside the documented range of
+    |v|, |S| < 2^14): the fp16 operands of the bf16 path keep their relative accuracy."""
+    x = inputs.prefill_inputs(seed=14, lengths=[190, 66], h_k=2, h_v=4, d=128, io_dtype=inputs.BF16, state_std=0.1)
+    x["v"] = inputs.f32_to_bf16_bits(inputs.bf16_bits_to_f32(x["v"]) * np.float32(1000.0))
+    x["state_in"] = (x["state_in"] * np.float32(1000.0)).astype(np.float32)
+    out, st = run_gpu(x, inputs.F32)
+    ro, rs = run_oracle(x)
+    eo, es = normwise(host(out), ro), normwise(host(st), rs)
+    print("large values: out %.3g state %.3g (max |v| %.0f)" % (eo, es, np.abs(inputs.bf16_bits_to_f32(x["v"])).max()))
+    assert np.isfinite(host(out)).all() and eo <= 2e-3 and es <= 2e-3
+
+
+def test_no_tokens_passes_state_through():
+    """total_tokens = 0: no output rows, and the final state equals the initial state."""
+    x = inputs.prefill_inputs(seed=16, total_tokens=0, h_k=2, h_v=4, d=128, io_dtype=inputs.BF16, state_std=0.1)
+    out, st = run_gpu(x, inputs.BF16)
+    assert out.shape[0] == 0
+    assert torch.equal(st, dev(x["state_in"]))
+
+
 def test_prefill_4k_workload():
     """T=4096, 32 v-heads over 16 q/k heads, d=128, bf16, zero state: full compare."""
     w = inputs.WORKLOADS["prefill_t4096_hv32_hk16_d128"]
