@@ -157,6 +157,26 @@ def test_no_tokens_passes_state_through():
     assert torch.equal(st, dev(x["state_in"]))
 
 
+@pytest.mark.parametrize("d,io", [(128, inputs.BF16), (64, inputs.F32)])
+@pytest.mark.parametrize("l2norm,scale", [(False, 0.5), (True, 0.125)])
+def test_norm_modes_and_query_scale(d, io, l2norm, scale):
+    """Without the in-kernel L2 norm (q and k scaled by 1/16, exactly, so the raw
+    recurrence stays stable) and with it plus a query scale, against the oracle."""
+    x = inputs.prefill_inputs(seed=17 + d, lengths=[140, 33], h_k=2, h_v=4, d=d, io_dtype=io, state_std=0.1)
+    if not l2norm:
+        for n in ("q", "k"):
+            if io == inputs.BF16:
+                x[n] = inputs.f32_to_bf16_bits(inputs.bf16_bits_to_f32(x[n]) * np.float32(1 / 16))
+            else:
+                x[n] = (x[n] * np.float32(1 / 16)).astype(np.float32)
+    out, st = run_gpu(x, inputs.F32, qk_l2norm=l2norm, scale=scale)
+    ro, rs = run_oracle(x, qk_l2norm=l2norm, scale=scale)
+    tol = 1e-5 if io == inputs.F32 else 2e-3
+    eo, es = normwise(host(out), ro), normwise(host(st), rs)
+    print("l2norm=%d scale=%g d=%d: out %.3g state %.3g" % (l2norm, scale, d, eo, es))
+    assert eo <= tol and es <= tol
+
+
 def test_prefill_4k_workload():
     """T=4096, 32 v-heads over 16 q/k heads, d=128, bf16, zero state: full compare."""
     w = inputs.WORKLOADS["prefill_t4096_hv32_hk16_d128"]
