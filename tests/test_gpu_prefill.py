@@ -443,6 +443,25 @@ def test_two_level_fp32_matches_oracle():
     assert normwise(host(out), ro) <= 1e-5 and normwise(host(st), rs) <= 1e-5
 
 
+@pytest.mark.parametrize("d,io", [(64, inputs.F32), (128, inputs.BF16)])
+def test_two_level_extreme_gates(d, io):
+    """Two-level scan with no-decay, near-total-forgetting and full-overwrite gates mixed
+    in (segment state maps with transition parts near zero)."""
+    x = inputs.prefill_inputs(seed=96 + d, total_tokens=900, h_k=1, h_v=2, d=d, io_dtype=io, state_std=0.3)
+    rng = np.random.default_rng(97)
+    pick = rng.integers(0, 5, x["g"].shape)
+    x["g"] = np.where(pick == 0, 0.0, np.where(pick == 1, -30.0, x["g"])).astype(np.float32)
+    pick = rng.integers(0, 5, x["beta"].shape)
+    x["beta"] = np.where(pick == 0, 1.0, x["beta"]).astype(np.float32)
+    out, st = gdn.prefill_two_level(dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["g"]), dev(x["beta"]),
+                                    segments=5, state_in=dev(x["state_in"]), out_dtype=inputs.F32)
+    ro, rs = run_oracle(x)
+    tol = 1e-5 if io == inputs.F32 else 2e-3
+    eo, es = normwise(host(out), ro), normwise(host(st), rs)
+    print("two-level extreme gates d=%d: out %.3g state %.3g" % (d, eo, es))
+    assert eo <= tol and es <= tol
+
+
 def test_two_level_one_segment_is_prefill():
     x = inputs.prefill_inputs(seed=96, total_tokens=700, h_k=2, h_v=4, d=128, io_dtype=inputs.BF16, state_std=0.1)
     out, st = gdn.prefill_two_level(dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["g"]), dev(x["beta"]),
