@@ -79,6 +79,23 @@ def test_decode_extreme_gates():
         assert normwise(host(state), ref_state) <= 2e-3
 
 
+def test_decode_many_units():
+    """1000 sequences x 4 v-heads (4000 units, several per persistent workgroup), two steps
+    in place, d = 64 fp32 against the oracle."""
+    N, h_k, h_v, d, steps = 1000, 2, 4, 64, 2
+    x = inputs.decode_inputs(seed=43, num_seqs=N, steps=steps, h_k=h_k, h_v=h_v, d=d, io_dtype=inputs.F32,
+                             state_std=0.3)
+    state = dev(x["state"])
+    ref_state = x["state"].astype(np.float64)
+    for t in range(steps):
+        out = gdn.decode_step(dev(x["q"][t]), dev(x["k"][t]), dev(x["v"][t]), dev(x["g"][t]),
+                              dev(x["beta"][t]), state, out_dtype=inputs.F32)
+        ro, ref_state = oracle.decode_step(x["q"][t], x["k"][t], x["v"][t], x["g"][t], x["beta"][t],
+                                           ref_state, h_k=h_k, h_v=h_v, threads=16)
+        assert normwise(host(out), ro) <= 1e-5
+        assert normwise(host(state), ref_state) <= 1e-5
+
+
 def test_decode_no_norm_and_scale():
     N, h_k, h_v, d = 2, 1, 2, 128
     x = inputs.decode_inputs(seed=5, num_seqs=N, steps=1, h_k=h_k, h_v=h_v, d=d, io_dtype=inputs.F32)
