@@ -177,6 +177,28 @@ def test_norm_modes_and_query_scale(d, io, l2norm, scale):
     assert eo <= tol and es <= tol
 
 
+def test_malformed_cu_seqlens_stay_in_bounds():
+    """cu_seqlens that decrease, overshoot total_tokens or go negative: the kernels clamp
+    them (results are unspecified by contract), so the calls complete, write finite values
+    and leave the rest of the GPU state intact."""
+    T = 250
+    x = inputs.prefill_inputs(seed=18, total_tokens=T, h_k=2, h_v=4, d=128, io_dtype=inputs.BF16, state_std=0.1)
+    cu = dev(np.array([0, 300, 100, 5000, -7, 250], dtype=np.int32))
+    s0 = dev((0.1 * np.random.default_rng(19).standard_normal((5, 4, 128, 128))).astype(np.float32))
+    args = (dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["g"]), dev(x["beta"]))
+    out, st = gdn.prefill(*args, state_in=s0, cu_seqlens=cu, out_dtype=inputs.F32)
+    out_d, st_d = gdn.prefill_direct(*args, state_in=s0, cu_seqlens=cu, out_dtype=inputs.F32)
+    torch.cuda.synchronize()
+    for t in (out, st, out_d, st_d):
+        assert torch.isfinite(t).all()
+    # a well-formed call afterwards still matches the oracle
+    good = inputs.prefill_inputs(seed=20, lengths=[100, 150], h_k=2, h_v=4, d=128, io_dtype=inputs.BF16,
+                                 state_std=0.1)
+    o2, s2 = run_gpu(good, inputs.F32)
+    ro, rs = run_oracle(good)
+    assert normwise(host(o2), ro) <= 2e-3 and normwise(host(s2), rs) <= 2e-3
+
+
 def test_prefill_4k_workload():
     """T=4096, 32 v-heads over 16 q/k heads, d=128, bf16, zero state: full compare."""
     w = inputs.WORKLOADS["prefill_t4096_hv32_hk16_d128"]
