@@ -199,6 +199,19 @@ def test_malformed_cu_seqlens_stay_in_bounds():
     assert normwise(host(o2), ro) <= 2e-3 and normwise(host(s2), rs) <= 2e-3
 
 
+@pytest.mark.parametrize("gate_mean", [0.0, -4.0])
+def test_fp32_long_sequence(gate_mean):
+    """fp32 path over 64 blocks (T = 4096, d = 64): the 1e-5 bound holds along the whole
+    block chain, with ordinary gates and with slow ones (alpha ~ 0.98, long memory)."""
+    x = inputs.prefill_inputs(seed=21, total_tokens=4096, h_k=1, h_v=2, d=64, io_dtype=inputs.F32, state_std=0.1,
+                              gate_mean=gate_mean)
+    out, st = run_gpu(x, inputs.F32)
+    ro, rs = run_oracle(x)
+    eo, es = normwise(host(out), ro), normwise(host(st), rs)
+    print("fp32 T=4096 gate mean %g: out %.3g state %.3g" % (gate_mean, eo, es))
+    assert eo <= 1e-5 and es <= 1e-5
+
+
 def test_prefill_4k_workload():
     """T=4096, 32 v-heads over 16 q/k heads, d=128, bf16, zero state: full compare."""
     w = inputs.WORKLOADS["prefill_t4096_hv32_hk16_d128"]
