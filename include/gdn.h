@@ -118,6 +118,14 @@ size_t gdn_prefill_workspace_bytes(const gdn_desc *desc, int32_t chunk);
  *   chunk       block length in tokens: 64.
  *   workspace   device scratch of at least gdn_prefill_workspace_bytes().
  *               Contents on entry do not matter.
+ *
+ * A single sequence (num_seqs == 1, no cu_seqlens) whose block records would
+ * not stay in the last-level cache between the two kernels is run as
+ * consecutive segments of whole blocks (as gdn_prefill_segmented, within the
+ * same workspace).  The results are bit-identical to one pass, and 9-22%
+ * faster from 8K tokens on at 32 v-heads, d = 128.  The environment variable
+ * GDN_PREFILL_SEGMENT_TOKENS=0 turns this off, and a positive multiple of 64
+ * fixes the segment length.
  */
 gdn_status gdn_prefill(const gdn_desc *desc,
                        const void *q, const void *k, const void *v,

@@ -212,6 +212,35 @@ def test_fp32_long_sequence(gate_mean):
     assert eo <= 1e-5 and es <= 1e-5
 
 
+def test_long_prompt_runs_as_segments(monkeypatch):
+    """A single sequence whose block records exceed the last-level cache runs inside
+    gdn_prefill as consecutive segments: bit-identical to one call (also without a state
+    output, where the carried state lives in the workspace, and in place), and within
+    tolerance of the oracle."""
+    x = inputs.prefill_inputs(seed=22, total_tokens=8256, h_k=16, h_v=32, d=128, io_dtype=inputs.BF16,
+                              state_std=0.05)
+    monkeypatch.setenv("GDN_PREFILL_SEGMENT_TOKENS", "0")
+    o1, s1 = run_gpu(x, inputs.BF16)
+    monkeypatch.delenv("GDN_PREFILL_SEGMENT_TOKENS")
+    o2, s2 = run_gpu(x, inputs.BF16)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    o3, _ = run_gpu(x, inputs.BF16, state=False)
+    assert torch.equal(o3, o1)
+    # in place through the C ABI: state_in == state_out
+    st = dev(x["state_in"])
+    desc = gdn.make_desc(num_seqs=1, total_tokens=x["total_tokens"], h_k=16, h_v=32, d=128, io_dtype=gdn.GDN_BF16,
+                         out_dtype=gdn.GDN_BF16)
+    ws = torch.empty(gdn.gdn_prefill_workspace_bytes(desc), dtype=torch.uint8, device=st.device)
+    o4 = torch.empty_like(o1)
+    gdn.gdn_prefill(desc, dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["g"]), dev(x["beta"]), st, o4, st, None, 64,
+                    ws, ws.numel())
+    torch.cuda.synchronize()
+    assert torch.equal(o4, o1) and torch.equal(st, s1)
+    ro, rs = run_oracle(x, threads=16)
+    check_bf16_out(host(o1), ro, 2e-3)
+    assert normwise(host(s1), rs) <= 2e-3
+
+
 def test_prefill_4k_workload():
     """T=4096, 32 v-heads over 16 q/k heads, d=128, bf16, zero state: full compare."""
     w = inputs.WORKLOADS["prefill_t4096_hv32_hk16_d128"]
