@@ -306,6 +306,17 @@ def prefill_configs(L, gdn, inputs, to_dev, torch, np, dev, with_cpu=True):
             call()
         torch.cuda.synchronize()
         us = timed(call, reps)
+        # gdn_prefill may run a long single sequence as segments; the one-pass time
+        # (prepare + scan over all blocks, as split below) is reported beside it
+        prev = os.environ.get("GDN_PREFILL_SEGMENT_TOKENS")
+        os.environ["GDN_PREFILL_SEGMENT_TOKENS"] = "0"
+        try:
+            us_one_pass = timed(call, reps)
+        finally:
+            if prev is None:
+                os.environ.pop("GDN_PREFILL_SEGMENT_TOKENS", None)
+            else:
+                os.environ["GDN_PREFILL_SEGMENT_TOKENS"] = prev
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
         for e in evs:
             e[0].record(stream)
@@ -347,7 +358,8 @@ def prefill_configs(L, gdn, inputs, to_dev, torch, np, dev, with_cpu=True):
             "io_dtype": "bf16" if w.io_dtype == inputs.BF16 else "f32",
             "state_in": "N(0,%g)" % w.state_std if s_in is not None else "zeros",
             "us_per_call": round(us, 2), "tok_per_s": T / us * 1e6,
-            "kernels_us": {"chunk_prep": round(us_prep, 2), "chunk_scan": round(us_scan, 2)},
+            "us_one_pass": round(us_one_pass, 2),
+            "kernels_us_one_pass": {"chunk_prep": round(us_prep, 2), "chunk_scan": round(us_scan, 2)},
             "direct_us": us_direct,
             "mfma_peak_tflops": mfma_peak,
             "mfma_frac_whole_call": round((f_prep + f_scan) / (us * 1e-6) / (mfma_peak * 1e12), 4),

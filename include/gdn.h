@@ -138,8 +138,9 @@ gdn_status gdn_prefill(const gdn_desc *desc,
 
 /*
  * The two phases of gdn_prefill, for callers that schedule or time them
- * separately.  gdn_prefill is exactly gdn_prefill_prepare followed by
- * gdn_prefill_scan on the same stream, with the same workspace.
+ * separately.  gdn_prefill_prepare followed by gdn_prefill_scan on the same
+ * stream, with the same workspace, is gdn_prefill in one pass (bit-identical
+ * to gdn_prefill also where it runs segments).
  *
  * gdn_prefill_prepare: everything that does not depend on the carried state,
  *   for all blocks at once (parallel over blocks and v-heads).  Reads q, k, v,
