@@ -221,6 +221,14 @@ __device__ __forceinline__ void lds_barrier() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Six 16x16 fp32 matrices in accumulator layout, kept in the blocks of b.ax above the
+// diagonal (unused once A is formed): slot s is block (0,1), (0,2), (0,3), (1,2), (1,3), (2,3).
+// Lane (j, q) owns row j, columns 4q..4q+3 of its block (one 16-byte access).
+__device__ __forceinline__ float* prep_xslot(float* ax, int s, int li, int lq) {
+    const int r = (s >= 3) + (s >= 5), c = s < 3 ? s + 1 : s < 5 ? s - 1 : 3;
+    return ax + (16 * r + li) * LDF + 16 * c + 4 * lq;
+}
+
 // Write 4 accumulator values (one lane's share of a 16x16 tile) as half of a
 // stored fragment: part 0 = elements 0..3, part 1 = elements 4..7.
 template <typename OP>
@@ -478,7 +486,7 @@ __global__ __launch_bounds__(PREP_THREADS, (prep_min_waves<D, OP>())) void chunk
                     gam = __expf((float)gx);
                 }
             }
-            if (nxt) in.load_gb(g, beta, nx_tok0, T, h_v, nx_h);
+            if (nxt && wave == 0) in.load_gb(g, beta, nx_tok0, T, h_v, nx_h);  // only wave 0 reads them
             lds_barrier();
             if (wave == 0) {
                 L.gck[lane] = gam * L.ck[lane];
@@ -556,17 +564,23 @@ __global__ __launch_bounds__(PREP_THREADS, (prep_min_waves<D, OP>())) void chunk
             }
             lds_barrier();
 
-            // ---- 3. X = (I + A)^{-1}, kept transposed in the upper triangle of b.ax -----------------
-            // Diagonal 16x16 blocks by substitution (wave w, lane c < 16 owns column c of block w);
-            // X_ij = -X_ii sum_{m=j}^{i-1} A_im X_mj by block distance (fp32 matrix cores).
-            if (wave >= 4) {  // the scan's K^T fragments, while waves 0..3 solve the diagonal blocks
+            // ---- 3. T = (I + A)^{-1} diag(beta), written straight into T's fragments ---------------
+            // X = (I + A)^{-1} by 16x16 blocks, in fp32 matrix-core products held in registers.
+            // 3a (waves 0..3): wave bb inverts the diagonal block X_bb; waves 4..7 write the scan's
+            //   K^T fragments meanwhile.
+            // 3b (waves 0..5): one wave per block below the diagonal, from
+            //   X_ij = -X_ii sum_{m=j}^{i-1} A_im X_mj; the waves that need X_10 or X_21 form it
+            //   themselves rather than wait for another wave.
+            // Matrices in accumulator layout, lane (j, q) holding M[4q + r][j] in element r; the
+            // product C = X Y takes X^T and Y (mm16), and C^T = Y^T X^T the same two swapped.
+            // T's fragment half (block row a, block column b) is X_ab^T in this layout scaled by
+            // beta, so no pass re-reads X.
+            if (wave >= 4) {
                 for (int f = wave - 4; krec && f < (D / 16) * 2; f += PREP_WAVES - 4)
                     frag_store<OP>(krec, f, lane, frag_colmajor<OP>(L.k, LK, f / 2, f % 2, lane));
             } else {
-                // Diagonal block bb: X_bb = (I + N)^{-1} for the strictly lower 16x16 N, as the
-                // exact product (I - N)(I + N^2)(I + N^4)(I + N^8) (N^16 = 0), in fp32 matrix-core
-                // products held in registers.  Each matrix is kept with its transpose: C = X Y
-                // takes X^T and Y in accumulator layout (see mm16).
+                // X_bb = (I + N)^{-1} for the strictly lower 16x16 N, as the exact product
+                // (I - N)(I + N^2)(I + N^4)(I + N^8) (N^16 = 0); each matrix is kept with its transpose.
                 const int bb = wave;
                 const float* blk = &L.b.ax[(16 * bb) * LDF + 16 * bb];
                 const f4_t rowv = *reinterpret_cast<const f4_t*>(&blk[li * LDF + 4 * lq]);
@@ -585,49 +599,62 @@ __global__ __launch_bounds__(PREP_THREADS, (prep_min_waves<D, OP>())) void chunk
                 const f4_t m = eye - n, mt = eye - nt;
                 const f4_t p1 = mm16(mt, n2, m), p1t = mm16(n2, mt, mt);
                 const f4_t p2 = mm16(p1t, n4, p1), p2t = mm16(n4, p1t, p1t);
-                const f4_t x = mm16(p2t, n8, p2);
-                // lane (j, q) holds X[4q + r][j] (zero above the diagonal); X_ij is stored at [j][i]
-                *reinterpret_cast<f4_t*>(&L.b.ax[(16 * bb + li) * LDF + 16 * bb + 4 * lq]) = x;
+                const f4_t x = mm16(p2t, n8, p2), xt = mm16(n8, p2t, p2t);
+                // 3b reads X_00, X_11, X_22 and X_11^T, X_22^T, X_33^T (slots 0..5 above the diagonal)
+                if (bb < 3) *reinterpret_cast<f4_t*>(prep_xslot(L.b.ax, bb, li, lq)) = x;
+                if (bb > 0) *reinterpret_cast<f4_t*>(prep_xslot(L.b.ax, bb + 2, li, lq)) = xt;
+                f4_t tv = xt * *reinterpret_cast<const f4_t*>(&L.bt[16 * bb + 4 * lq]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) tv[r] = 4 * lq + r <= li ? tv[r] : 0.f;  // X_bb is lower triangular
+                store_part<OP>(L.t, 2 * bb + (bb >> 1), bb & 1, lane, tv);
             }
             lds_barrier();
-            for (int dist = 1; dist < 4; ++dist) {
-                const int i = wave + dist, j = wave;
-                if (i < 4) {
-                    f4_t acc = {0, 0, 0, 0};
-                    for (int m = j; m < i; ++m) {
-                        // A_im (lower, row-major) as the A operand; X_mj (stored transposed) as the B operand
-                        const f4_t av = *reinterpret_cast<const f4_t*>(&L.b.ax[(16 * i + li) * LDF + 16 * m + 4 * lq]);
-                        const f4_t xv = *reinterpret_cast<const f4_t*>(&L.b.ax[(16 * j + li) * LDF + 16 * m + 4 * lq]);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], xv[e], acc, 0, 0, 0);
-                    }
-                    // res = -X_ii acc: A operand X_ii[li][4q + e] stored at [16i + 4q + e][16i + li]
-                    f4_t res = {0, 0, 0, 0};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        res = __builtin_amdgcn_mfma_f32_16x16x4f32(-L.b.ax[(16 * i + 4 * lq + e) * LDF + 16 * i + li], acc[e], res,
-                                                                  0, 0, 0);
-                    // lane (c, q): X[16i + 4q + r][16j + c] -> stored at [16j + c][16i + 4q + r]
-                    *reinterpret_cast<f4_t*>(&L.b.ax[(16 * j + li) * LDF + 16 * i + 4 * lq]) = res;
+            if (wave < 6) {
+                // A_ij^T in accumulator layout: A_ij row-major at [16 i + j'][16 j + 4q + r]
+                auto at = [&](int i, int j) {
+                    return *reinterpret_cast<const f4_t*>(&L.b.ax[(16 * i + li) * LDF + 16 * j + 4 * lq]);
+                };
+                auto xs = [&](int s) { return *reinterpret_cast<const f4_t*>(prep_xslot(L.b.ax, s, li, lq)); };
+                const f4_t z = {0, 0, 0, 0};
+                int a, b;  // the block this wave forms
+                f4_t res;  // -(sum) before the final product, as X_ab^T
+                if (wave == 0) {          // X_10 = -X_11 A_10 X_00
+                    a = 1; b = 0;
+                    res = mm16(mm16(at(1, 0), xs(0), z), xs(3), z);
+                } else if (wave == 1) {   // X_21 = -X_22 A_21 X_11
+                    a = 2; b = 1;
+                    res = mm16(mm16(at(2, 1), xs(1), z), xs(4), z);
+                } else if (wave == 2) {   // X_32 = -X_33 A_32 X_22
+                    a = 3; b = 2;
+                    res = mm16(mm16(at(3, 2), xs(2), z), xs(5), z);
+                } else if (wave == 3) {   // X_20 = -X_22 (A_20 X_00 + A_21 X_10)
+                    a = 2; b = 0;
+                    const f4_t x00 = xs(0);
+                    const f4_t x10 = -mm16(xs(3), mm16(at(1, 0), x00, z), z);
+                    res = mm16(mm16(at(2, 1), x10, mm16(at(2, 0), x00, z)), xs(4), z);
+                } else if (wave == 4) {   // X_31 = -X_33 (A_31 X_11 + A_32 X_21)
+                    a = 3; b = 1;
+                    const f4_t x11 = xs(1);
+                    const f4_t x21 = -mm16(xs(4), mm16(at(2, 1), x11, z), z);
+                    res = mm16(mm16(at(3, 2), x21, mm16(at(3, 1), x11, z)), xs(5), z);
+                } else {                  // X_30 = -X_33 (A_30 X_00 + A_31 X_10 + A_32 X_20)
+                    a = 3; b = 0;
+                    const f4_t x00 = xs(0), x22t = xs(4);
+                    const f4_t x10 = -mm16(xs(3), mm16(at(1, 0), x00, z), z);
+                    const f4_t x20 = -mm16(x22t, mm16(at(2, 1), x10, mm16(at(2, 0), x00, z)), z);
+                    res = mm16(mm16(at(3, 2), x20, mm16(at(3, 1), x10, mm16(at(3, 0), x00, z))), xs(5), z);
                 }
-                lds_barrier();
-            }
-            // T = X diag(beta): T[i][j] = X[i][j] beta_j for i >= j (X_ij at [j][i]), else 0.
-            // Wave f forms fragment f of T (row block f / 2, column block f % 2); a lane's
-            // eight reads run along rows of the stored X^T (conflict-free), then one write.
-            static_assert(2 * (CHUNK / 16) == PREP_WAVES, "one T fragment per wave");
-            {
-                const int f = tid / WAVE, i = 16 * (f / 2) + li;
-                Frag<OP> tf;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int j = 32 * (f % 2) + 4 * lq + (e & 3) + 16 * (e >> 2);
-                    frag_set(tf, e, (i >= j) ? L.b.ax[j * LDF + i] * L.bt[j] : 0.f);
+                store_part<OP>(L.t, 2 * a + (b >> 1), b & 1, lane,
+                               -res * *reinterpret_cast<const f4_t*>(&L.bt[16 * b + 4 * lq]));
+            } else {
+                // the halves of T above the diagonal: fragment 0 part 1, fragments 1 and 3, fragment 5 part 1
+                for (int h = wave - 6; h < 6; h += 2) {
+                    const int f = h == 0 ? 0 : h <= 2 ? 1 : h <= 4 ? 3 : 5;
+                    const int part = (h == 0 || h == 2 || h == 4 || h == 5) ? 1 : 0;
+                    store_part<OP>(L.t, f, part, lane, f4_t{0.f, 0.f, 0.f, 0.f});
                 }
-                frag_store<OP>(L.t, f, lane, tf);
             }
             lds_barrier();
-
 
             // ---- 4. values to LDS (region b) ---------------------------------------------------
 #pragma unroll
