@@ -123,13 +123,32 @@ __device__ __forceinline__ Frag<OP> frag_rowmajor(const OP* M, int ld, int rb, i
 // 32*kb + (4q + e) for e < 4 and 32*kb + 16 + 4q + (e - 4) for e >= 4, at
 // column 16*cb + (lane % 16).  It serves as a B fragment of M, or as an A
 // fragment of M^T.
+//
+// In LDS with 2-byte elements it takes two transposing reads
+// (ds_read_b64_tr_b16).  Within each group of 16 lanes such a read hands lane
+// 4a + c element c of the 8 bytes that lanes a, a + 4, a + 8 and a + 12
+// addressed.  So lane s of group q addresses row 32*kb + 4q + (s >> 2), columns
+// 16*cb + 4(s & 3) .. + 3, and lane (i, q) receives column 16*cb + i of rows
+// 32*kb + 4q .. + 3; the second read does the same 16 rows down.  M, ld and
+// 16*cb keep every address 8-byte aligned (ld even, M 8-byte aligned).
 template <typename OP>
 __device__ __forceinline__ Frag<OP> frag_colmajor(const OP* M, int ld, int cb, int kb, int lane) {
-    const int i = lane & 15, q = lane >> 4;
-    const OP* p = M + (size_t)(32 * kb + 4 * q) * ld + 16 * cb + i;
     Frag<OP> f;
+    if constexpr (sizeof(OP) == 2) {
+        typedef short s4_t __attribute__((ext_vector_type(4)));
+        typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) s4_t* lds_s4;
+        const int s = lane & 15, q = lane >> 4;
+        const OP* p = M + (size_t)(32 * kb + 4 * q + (s >> 2)) * ld + 16 * cb + 4 * (s & 3);
+        const h4_t a = __builtin_bit_cast(h4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)p));
+        const h4_t b = __builtin_bit_cast(h4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(p + 16 * ld)));
+        f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    } else {
+        const int i = lane & 15, q = lane >> 4;
+        const OP* p = M + (size_t)(32 * kb + 4 * q) * ld + 16 * cb + i;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) frag_set_raw(f, e, p[(size_t)((e & 3) + 16 * (e >> 2)) * ld]);
+        for (int e = 0; e < 8; ++e) frag_set_raw(f, e, p[(size_t)((e & 3) + 16 * (e >> 2)) * ld]);
+    }
     return f;
 }
 
