@@ -54,15 +54,20 @@ def algorithmic_decode(N, h_v, h_k, d, io_bytes=2, out_bytes=2):
 
 
 def kernel_source_digest():
-    """Digest of the HIP sources; counter figures are only reported for the
-    kernels they were measured on."""
+    """Digest of the HIP sources with comments and trailing blanks removed;
+    counter figures are only reported for the kernels they were measured on,
+    and an edit to a comment does not change a kernel."""
     import hashlib
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "linear_attention_recurrence_rule_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
         if name.endswith((".hip", ".h")):
             with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+                src = re.sub(rb"/\*.*?\*/", b"", f.read(), flags=re.S)
+            src = re.sub(rb"//[^\n]*", b"", src)
+            src = b"\n".join(line.rstrip() for line in src.split(b"\n") if line.strip())
+            h.update(name.encode() + b"\0" + src)
     return h.hexdigest()[:16]
 
 

@@ -617,7 +617,7 @@ __global__ __launch_bounds__(PREP_THREADS, (prep_min_waves<D, OP>())) void chunk
                 auto xs = [&](int s) { return *reinterpret_cast<const f4_t*>(prep_xslot(L.b.ax, s, li, lq)); };
                 const f4_t z = {0, 0, 0, 0};
                 int a, b;  // the block this wave forms
-                f4_t res;  // -(sum) before the final product, as X_ab^T
+                f4_t res;  // (X_aa sum)^T in accumulator layout, that is -X_ab^T
                 if (wave == 0) {          // X_10 = -X_11 A_10 X_00
                     a = 1; b = 0;
                     res = mm16(mm16(at(1, 0), xs(0), z), xs(3), z);
