@@ -51,12 +51,6 @@ __device__ __forceinline__ void load4(const void* base, size_t idx, float x[4]) 
 }
 
 template <bool BF16>
-__device__ __forceinline__ void load8(const void* base, size_t idx, float x[8]) {
-    load4<BF16>(base, idx, x);
-    load4<BF16>(base, idx + 4, x + 4);
-}
-
-template <bool BF16>
 __device__ __forceinline__ float load1(const void* base, size_t idx) {
     if constexpr (BF16) return bf16_to_f32(reinterpret_cast<const uint16_t*>(base)[idx]);
     else return reinterpret_cast<const float*>(base)[idx];
@@ -97,26 +91,6 @@ __device__ __forceinline__ void mma(f4_t& acc, const Frag<float>& a, const Frag<
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[1], b.hi[1], acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[2], b.hi[2], acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[3], b.hi[3], acc, 0, 0, 0);
-}
-
-// Fragment of a row-major matrix M (leading dimension ld, in elements) for the
-// 16-row block `rb` and the 32-wide contraction block `kb`.  It serves as an
-// A fragment of M, or as a B fragment of M^T.
-template <typename OP>
-__device__ __forceinline__ Frag<OP> frag_rowmajor(const OP* M, int ld, int rb, int kb, int lane) {
-    const int i = lane & 15, q = lane >> 4;
-    const OP* p = M + (size_t)(16 * rb + i) * ld + 32 * kb + 4 * q;
-    Frag<OP> f;
-    if constexpr (sizeof(OP) == 2) {
-        typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
-        h4_t a = *reinterpret_cast<const h4_t*>(p);
-        h4_t b = *reinterpret_cast<const h4_t*>(p + 16);
-        f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-    } else {
-        f.lo = *reinterpret_cast<const f4_t*>(p);
-        f.hi = *reinterpret_cast<const f4_t*>(p + 16);
-    }
-    return f;
 }
 
 // Column fragment of a row-major matrix M: the contraction runs down the rows

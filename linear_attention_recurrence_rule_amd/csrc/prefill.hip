@@ -247,8 +247,8 @@ __device__ __forceinline__ void store_part(OP* base, int frag, int part, int lan
 // whose two operands are both read this way: lane (i, q) holds the eight
 // consecutive elements M[16 rb + i][32 kb + 8q + e], one 16-byte read (two for
 // fp32) per lane, so each quarter-wave reads distinct banks.  The contraction
-// index of element e is 8q + e; it differs from frag_rowmajor's, which is
-// harmless when both operands use this one.
+// index of element e is 8q + e, not the accumulator order of frag_colmajor and
+// frag_from_acc; a product must take both operands in the same order.
 template <typename OP>
 __device__ __forceinline__ Frag<OP> frag_row8(const OP* M, int ld, int rb, int kb, int lane) {
     const OP* p = M + (size_t)(16 * rb + (lane & 15)) * ld + 32 * kb + 8 * (lane >> 4);
