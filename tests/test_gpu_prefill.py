@@ -324,6 +324,7 @@ ROW_CASES = [  # (d, io dtype, out dtype, lengths)
     (64, inputs.F32, inputs.F32, [257]),
     (64, inputs.F32, inputs.BF16, [1, 130]),
     (64, inputs.BF16, inputs.F32, [200, 0, 65]),
+    (64, inputs.BF16, inputs.BF16, [100, 64, 3]),
     (128, inputs.BF16, inputs.F32, [333]),
     (128, inputs.BF16, inputs.BF16, [64, 190, 1]),
 ]
