@@ -4,11 +4,13 @@ TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
 the CPU-baseline leg of ``bench.py`` may import this module.  It shares no code
 with the GPU library and never imports the product package.
 
-The arithmetic lives in ``gdn_oracle.c``.  That file cites the layer
+The recurrence lives in ``gdn_oracle.c``.  That file cites the layer
 description in "Optimizing on-device inference for Apple Silicon" (section
 "Qwen creates three distinct workload shapes") and states the recurrence it
-evaluates.  This module only widens the caller's arrays to float64 and passes
-pointers.
+evaluates; for it this module only widens the caller's arrays to float64 and
+passes pointers.  The two per-token operations beside the decode step (gate
+activations and the output normalisation) are plain float64 numpy at the end
+of this module.
 
 Parity pins: every function here is checked by ``tests/test_oracle_pins.py``
 against closed forms, brute-force matrix products, a hand-worked example and
@@ -129,3 +131,51 @@ def decode_step(q, k, v, g, beta, state, *, h_k, h_v, qk_l2norm=True, scale=1.0,
     cu = np.arange(N + 1, dtype=np.int32)
     return scan(q, k, v, g, beta, h_k=h_k, h_v=h_v, state_in=state, cu_seqlens=cu,
                 qk_l2norm=qk_l2norm, scale=scale, threads=threads)
+
+
+# ---- the per-token ops beside the decode step --------------------------------------------
+# The pages' decode path fuses "the recurrent update with its normalisation"
+# (section "Reduce intermediate traffic and state traffic").  Two per-token
+# operations sit next to the update.  The activations turn raw gate inputs into
+# g and beta: the decode workload draws both raw inputs from N(0, 1) and sets
+# g = -softplus(x_g), beta = sigmoid(x_beta).  The normalisation scales each
+# head's output o to unit root-mean-square over d_v (with a per-channel weight).
+
+
+def gate_activations(x_g, x_beta):
+    """g = -softplus(x_g) = -log(1 + exp(x_g)), so alpha = exp(g) = 1 / (1 + exp(x_g)),
+    and beta = 1 / (1 + exp(-x_beta)); fp64, finite for every finite input
+    (softplus(x) = max(x, 0) + log1p(exp(-|x|)); the logistic function is taken on
+    exp(-|y|) <= 1)."""
+    x = widen(x_g)
+    y = widen(x_beta)
+    g = -(np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x))))
+    e = np.exp(-np.abs(y))
+    beta = np.where(y >= 0.0, 1.0 / (1.0 + e), e / (1.0 + e))
+    return g, beta
+
+
+def output_rms_norm(o, weight=None, eps=1e-6):
+    """Each head's output vector (last axis, d_v) divided by its root-mean-square,
+    o / sqrt(mean_j o_j^2 + eps), then multiplied channel-wise by `weight` ([d_v];
+    None for ones).  fp64."""
+    o = widen(o)
+    out = o / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + float(eps))
+    if weight is not None:
+        out = out * widen(weight)
+    return out
+
+
+def decode_step_ex(q, k, v, g, beta, state, *, h_k, h_v, raw_gates=False, output_norm=False,
+                   norm_weight=None, norm_eps=1e-6, qk_l2norm=True, scale=1.0, threads=0):
+    """decode_step with the per-token ops beside it: with raw_gates, `g` and `beta`
+    are the raw inputs x_g, x_beta and pass through gate_activations first; with
+    output_norm, each head's output passes through output_rms_norm.  The state
+    update does not depend on the normalisation."""
+    if raw_gates:
+        g, beta = gate_activations(g, beta)
+    o, s = decode_step(q, k, v, g, beta, state, h_k=h_k, h_v=h_v, qk_l2norm=qk_l2norm, scale=scale,
+                       threads=threads)
+    if output_norm:
+        o = output_rms_norm(o, norm_weight, norm_eps)
+    return o, s

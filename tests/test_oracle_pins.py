@@ -13,7 +13,11 @@ qualitatively and print no worked example.  So the oracle is pinned by:
     (state, values), the contraction bound, grouped-head sharing equal to
     duplicated heads, and packed sequences equal to separate calls;
   * a mutation check: plausible mistakes planted in a copy of the oracle's C
-    source must each fail at least one of the pins above.
+    source must each fail at least one of the pins above;
+  * for the per-token ops beside the decode step (gate activations, output
+    normalisation): closed forms (softplus(0) = ln 2, exp(-softplus(x)) =
+    1 / (1 + e^x), a hand-worked norm), identities and invariants, each also
+    shown to fail for planted mistakes.
 """
 import json
 import os
@@ -279,3 +283,150 @@ def test_pins_catch_planted_mistake(name, tmp_path):
                         os.path.abspath(__file__), "-k", "not planted"],
                        cwd=root, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, "mutation %s survived every pin:\n%s" % (name, r.stdout[-2000:])
+
+
+# ---- the per-token ops beside the decode step ---------------------------------------------
+# gate_activations and output_rms_norm are pinned by closed forms and identities of the
+# two functions, written independently of the oracle's code; each pin helper returns the
+# names of the pins an implementation fails, so planted mistakes can be checked too.
+
+def gate_pin_failures(fn):
+    fails = []
+    g, b = fn(np.array([0.0]), np.array([0.0]))
+    # softplus(0) = ln 2 and the logistic function at 0 is 1/2
+    if abs(g[0] + 0.6931471805599453) > 1e-15 or abs(b[0] - 0.5) > 1e-15:
+        fails.append("values at zero")
+    x = np.linspace(-30.0, 30.0, 121)
+    g, b = fn(x, x)
+    _, b_neg = fn(x, -x)
+    # exp(-softplus(x)) = 1 / (1 + e^x): the decay of input x is the write strength of input -x
+    if not np.allclose(np.exp(g), b_neg, rtol=1e-13, atol=0.0):
+        fails.append("alpha is the logistic function of -x")
+    g_neg, _ = fn(-x, x)
+    # softplus(x) - softplus(-x) = x
+    if not np.allclose(g_neg - g, x, rtol=0.0, atol=1e-12):
+        fails.append("odd part of softplus")
+    if not (np.all(np.diff(g) < 0.0) and np.all(np.diff(b) > 0.0) and np.all(g < 0.0)):
+        fails.append("monotone, g < 0")
+    g, b = fn(np.array([-800.0, 800.0]), np.array([-800.0, 800.0]))
+    if not (np.all(np.isfinite(g)) and g[0] == 0.0 and g[1] == -800.0 and b[0] == 0.0 and b[1] == 1.0):
+        fails.append("finite at the ends")
+    return fails
+
+
+def norm_pin_failures(fn):
+    fails = []
+    # hand-worked: o = (3, 4) has mean square 12.5; 3/sqrt(12.5) and 2*4/sqrt(12.5)
+    out = fn(np.array([[3.0, 4.0]]), np.array([1.0, 2.0]), 0.0)
+    if not np.allclose(out, [[0.8485281374238570, 2.2627416997969525]], rtol=1e-15, atol=0.0):
+        fails.append("hand-worked (3, 4)")
+    # eps inside the root: eps = 12.5 doubles the mean square, o / 5
+    out = fn(np.array([[3.0, 4.0]]), None, 12.5)
+    if not np.allclose(out, [[0.6, 0.8]], rtol=1e-15, atol=0.0):
+        fails.append("eps inside the square root")
+    rng = np.random.default_rng(5)
+    o = 7.0 * rng.standard_normal((4, 3, 16))
+    out = fn(o, None, 0.0)
+    if not np.allclose(np.sqrt(np.mean(out * out, axis=-1)), 1.0, rtol=1e-14, atol=0.0):
+        fails.append("unit root-mean-square per head")
+    o2 = o.copy()
+    o2[1, 2] *= 3.0
+    o2[0, 1] += 1.0
+    out2 = fn(o2, None, 0.0)
+    # each head on its own: scaling a head leaves it unchanged, other heads never move
+    same = np.ones((4, 3), dtype=bool)
+    same[0, 1] = False
+    if not (np.allclose(out2[same], out[same], rtol=1e-14, atol=0.0) and
+            not np.allclose(out2[0, 1], out[0, 1])):
+        fails.append("heads independent, scale invariant")
+    w = rng.standard_normal(16)
+    if not np.allclose(fn(o, w, 0.0), out * w, rtol=1e-14, atol=0.0):
+        fails.append("channel-wise weight")
+    if not np.all(fn(np.zeros((2, 8)), None, 1e-6) == 0.0):
+        fails.append("zero output stays zero")
+    return fails
+
+
+def test_gate_activations_pins():
+    assert gate_pin_failures(oracle.gate_activations) == []
+
+
+def test_output_rms_norm_pins():
+    assert norm_pin_failures(oracle.output_rms_norm) == []
+
+
+def _planted_gates():
+    def sign(x, y):
+        g, b = oracle.gate_activations(x, y)
+        return -g, b
+    def argument(x, y):
+        return oracle.gate_activations(-np.asarray(x), y)
+    def beta_flip(x, y):
+        return oracle.gate_activations(x, -np.asarray(y))
+    def naive(x, y):
+        x = np.asarray(x, dtype=np.float64)
+        y = np.asarray(y, dtype=np.float64)
+        with np.errstate(over="ignore"):
+            return -np.log1p(np.exp(x)), 1.0 / (1.0 + np.exp(-y))
+    return {"sign": sign, "argument": argument, "beta_flip": beta_flip, "naive_overflow": naive}
+
+
+def _planted_norms():
+    def mean_not_rms(o, w, eps):
+        o = np.asarray(o, dtype=np.float64)
+        out = o / (np.mean(o * o, axis=-1, keepdims=True) + eps)
+        return out if w is None else out * w
+    def eps_outside(o, w, eps):
+        o = np.asarray(o, dtype=np.float64)
+        out = o / (np.sqrt(np.mean(o * o, axis=-1, keepdims=True)) + eps)
+        return out if w is None else out * w
+    def wrong_axis(o, w, eps):
+        o = np.asarray(o, dtype=np.float64)
+        out = o / np.sqrt(np.mean(o * o, axis=0, keepdims=True) + eps)
+        return out if w is None else out * w
+    def weight_divides(o, w, eps):
+        out = oracle.output_rms_norm(o, None, eps)
+        return out if w is None else out / w
+    def sum_not_mean(o, w, eps):
+        o = np.asarray(o, dtype=np.float64)
+        out = o / np.sqrt(np.sum(o * o, axis=-1, keepdims=True) + eps)
+        return out if w is None else out * w
+    return {"mean_not_rms": mean_not_rms, "eps_outside": eps_outside, "wrong_axis": wrong_axis,
+            "weight_divides": weight_divides, "sum_not_mean": sum_not_mean}
+
+
+@pytest.mark.parametrize("name", sorted(_planted_gates()))
+def test_gate_pins_catch_planted_mistake(name):
+    with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
+        assert gate_pin_failures(_planted_gates()[name]) != []
+
+
+@pytest.mark.parametrize("name", sorted(_planted_norms()))
+def test_norm_pins_catch_planted_mistake(name):
+    with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
+        assert norm_pin_failures(_planted_norms()[name]) != []
+
+
+def test_decode_step_ex_composes_the_pinned_parts():
+    """Both options off is decode_step; raw gate inputs of 0 are g = -ln 2, beta = 1/2;
+    the output norm leaves the state alone and gives each head unit root-mean-square."""
+    rng = np.random.default_rng(6)
+    N, h_k, h_v, d = 3, 2, 4, 16
+    q = rng.standard_normal((N, h_k, d))
+    k = rng.standard_normal((N, h_k, d))
+    v = rng.standard_normal((N, h_v, d))
+    xg = rng.standard_normal((N, h_v))
+    xb = rng.standard_normal((N, h_v))
+    S = 0.2 * rng.standard_normal((N, h_v, d, d))
+    o0, s0 = oracle.decode_step(q, k, v, xg, xb, S, h_k=h_k, h_v=h_v)
+    o1, s1 = oracle.decode_step_ex(q, k, v, xg, xb, S, h_k=h_k, h_v=h_v)
+    assert np.array_equal(o0, o1) and np.array_equal(s0, s1)
+    z = np.zeros((N, h_v))
+    o2, s2 = oracle.decode_step_ex(q, k, v, z, z, S, h_k=h_k, h_v=h_v, raw_gates=True)
+    o3, s3 = oracle.decode_step(q, k, v, np.full((N, h_v), -np.log(2.0)), np.full((N, h_v), 0.5), S,
+                                h_k=h_k, h_v=h_v)
+    assert np.allclose(o2, o3, rtol=1e-14, atol=1e-15) and np.allclose(s2, s3, rtol=1e-14, atol=1e-15)
+    o4, s4 = oracle.decode_step_ex(q, k, v, xg, xb, S, h_k=h_k, h_v=h_v, output_norm=True, norm_eps=0.0)
+    assert np.array_equal(s4, s0)
+    assert np.allclose(np.sqrt(np.mean(o4 * o4, axis=-1)), 1.0, rtol=1e-14)
+    assert np.allclose(o4 * np.sqrt(np.mean(o0 * o0, axis=-1, keepdims=True)), o0, rtol=1e-13)
