@@ -6,7 +6,9 @@ q/k heads, d = 128, bf16 in and out, fp32 state, 64-token blocks), with inputs
 already resident in HBM.  ``value`` is prefill tokens/s over the K timed steps.
 The same JSON line also reports:
   * decode: 512 consecutive gdn_decode_step launches on the decode workload
-    (64 sequences x 32 v-heads, d = 128, fp32 state);
+    (64 sequences x 32 v-heads, d = 128, fp32 state), the same loop replayed
+    from a HIP graph, and the same steps through gdn_decode_step_ex with raw
+    gate inputs and the output normalisation folded in;
   * roofline of the dominant prefill kernel: algorithmic flops per launch over
     its average HIP-event duration, against the 2.5 PFLOP/s dense fp16
     matrix-core peak; the decode kernel's algorithmic bytes against 8 TB/s;
@@ -552,11 +554,38 @@ def main():
     torch.cuda.synchronize()
     us_dec_graph = d0.elapsed_time(d1) * 1e3 / steps
     del graph
+    # the same steps with the per-token ops beside the update folded in
+    # (gdn_decode_step_ex): raw gate inputs (the workload's N(0, 1) draws x_g, x_beta)
+    # and each head's output normalised, with a channel weight
+    dxg, dxb = to_dev(y["x_g"]), to_dev(y["x_beta"])
+    nw = (1.0 + 0.25 * torch.randn(dd, generator=torch.Generator().manual_seed(0))).to(dev)
+    xg_base, xb_base, nw_ptr = dxg.data_ptr(), dxb.data_ptr(), nw.data_ptr()
+    fuse = gdn.GDN_FUSE_GATE_ACTIVATIONS | gdn.GDN_FUSE_OUTPUT_NORM
+
+    def fused_call(t):
+        st = L.gdn_decode_step_ex(ddref, base[0] + t * qs, base[1] + t * ks, base[2] + t * vs_, xg_base + t * gs,
+                                  xb_base + t * bs, sptr, optr, fuse, nw_ptr, 1e-6, sp)
+        if st:
+            raise gdn.GdnError(st, gdn.last_error())
+
+    for t in range(10):
+        fused_call(t % steps)
+    torch.cuda.synchronize()
+    d0.record(stream)
+    for t in range(steps):
+        fused_call(t)
+    d1.record(stream)
+    torch.cuda.synchronize()
+    us_dec_fused = d0.elapsed_time(d1) * 1e3 / steps
+    del dxg, dxb, nw
     dbytes = algorithmic_decode(N, dh_v, dh_k, dd)
     dec_gbs = dbytes / (us_dec * 1e-6) / 1e9
     decode_info = {"workload": DECODE_WL, "steps_timed": steps, "us_per_step": us_dec,
                    "steps_per_s": 1e6 / us_dec, "tok_per_s": N * 1e6 / us_dec,
                    "us_per_step_hip_graph": us_dec_graph,
+                   "us_per_step_fused": us_dec_fused,
+                   "fused": "gdn_decode_step_ex: raw gate inputs and the per-head output RMS norm in the step "
+                            "(%.1f%% of HBM peak)" % (100 * dbytes / (us_dec_fused * 1e-6) / (PEAK_HBM_GBS * 1e9)),
                    "algorithmic_mb_per_step": dbytes / 1e6,
                    "roofline": {"bound": "hbm", "kernel": "decode_step", "achieved": round(dec_gbs, 1),
                                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4),

@@ -204,6 +204,40 @@ gdn_status gdn_decode_step_slots(const gdn_desc *desc,
                                  void *out, void *stream);
 
 /*
+ * One decode step with the per-token operations beside the recurrent update
+ * folded into the same kernel.  The section "Reduce intermediate traffic and
+ * state traffic" fuses the recurrent update with its normalisation, so that
+ * temporaries stay in registers instead of passing through memory.  `fuse` is
+ * a bitwise OR of:
+ *
+ *   GDN_FUSE_GATE_ACTIVATIONS  g and beta hold raw gate inputs x_g, x_beta
+ *                              (fp32 [num_seqs, h_v]); the step uses
+ *                              alpha = exp(-softplus(x_g)) = 1 / (1 + e^x_g)
+ *                              and beta = 1 / (1 + e^-x_beta).
+ *   GDN_FUSE_OUTPUT_NORM       each (sequence, v-head) output o (d_v values)
+ *                              is written as o / sqrt(mean(o^2) + norm_eps),
+ *                              times norm_weight channel-wise.  norm_weight
+ *                              is fp32 [d_v] on the device, shared by all
+ *                              heads, or NULL for ones; norm_eps is finite
+ *                              and > 0.  The state update is not affected.
+ *
+ * Without flags this is gdn_decode_step (bit-identical results); norm_weight
+ * and norm_eps are read only with GDN_FUSE_OUTPUT_NORM.  The state is still
+ * read and written once.  Other arguments, shapes and errors are those of
+ * gdn_decode_step, plus GDN_ERR_INVALID_ARGUMENT for unknown flags, a
+ * norm_eps that is not finite and positive, or a norm_weight that overlaps
+ * another buffer.
+ */
+typedef enum { GDN_FUSE_GATE_ACTIVATIONS = 1, GDN_FUSE_OUTPUT_NORM = 2 } gdn_fuse_flag;
+
+gdn_status gdn_decode_step_ex(const gdn_desc *desc,
+                              const void *q, const void *k, const void *v,
+                              const float *g, const float *beta,
+                              float *state, void *out,
+                              int32_t fuse, const float *norm_weight, float norm_eps,
+                              void *stream);
+
+/*
  * Bounded-memory prefill of one long sequence (num_seqs == 1, no
  * cu_seqlens): the tokens run through gdn_prefill in consecutive segments of
  * `segment_tokens` (a positive multiple of chunk), each starting from the

@@ -16,7 +16,7 @@ namespace gdn {
 hipError_t launch_decode(int d, bool in_bf16, bool out_bf16, const void* q, const void* k,
                          const void* v, const float* g, const float* beta, float* state, const int32_t* slots,
                          int num_slots, void* out, int units, int h_k, int h_v, int l2norm, float scale,
-                         int grid, hipStream_t stream);
+                         int fuse, const float* norm_w, float norm_eps, int grid, hipStream_t stream);
 size_t prefill_record_bytes(int d, bool in_bf16);
 size_t prefill_key_record_bytes(int d, bool in_bf16);
 hipError_t launch_segment_info(void* info, int P, int sb, int T, hipStream_t stream);
@@ -133,7 +133,8 @@ struct Span {
 gdn_status check_align(const Span* s, int count) {
     for (int i = 0; i < count; ++i) {
         if (!s[i].p || !s[i].n) continue;
-        const bool small = !strcmp(s[i].name, "g") || !strcmp(s[i].name, "beta") || !strcmp(s[i].name, "cu_seqlens");
+        const bool small = !strcmp(s[i].name, "g") || !strcmp(s[i].name, "beta") ||
+                           !strcmp(s[i].name, "cu_seqlens") || !strcmp(s[i].name, "norm_weight");
         const uintptr_t a = small ? 4 : (!strcmp(s[i].name, "workspace") ? 256 : 16);
         if (reinterpret_cast<uintptr_t>(s[i].p) % a)
             return fail(GDN_ERR_INVALID_ARGUMENT, "%s must be %zu-byte aligned", s[i].name, (size_t)a);
@@ -357,11 +358,11 @@ gdn_status segment_plan(const gdn_desc* desc, int32_t chunk, int64_t seg, gdn_de
     return GDN_OK;
 }
 
-// Shared by gdn_decode_step (slots == NULL: sequence n uses state n) and
-// gdn_decode_step_slots.
+// Shared by gdn_decode_step (slots == NULL: sequence n uses state n),
+// gdn_decode_step_slots and gdn_decode_step_ex (fuse flags, norm weight and eps).
 gdn_status decode_call(const gdn_desc* desc, const void* q, const void* k, const void* v, const float* g,
                        const float* beta, float* state, int32_t num_slots, const int32_t* slots, void* out,
-                       void* stream) {
+                       void* stream, int fuse = 0, const float* norm_w = nullptr, float norm_eps = 0.f) {
     const int N = desc->num_seqs, hk = desc->h_k, hv = desc->h_v, d = desc->d_k;
     const size_t io = dtype_size(desc->io_dtype), os = dtype_size(desc->out_dtype);
     const Span spans[] = {
@@ -373,6 +374,7 @@ gdn_status decode_call(const gdn_desc* desc, const void* q, const void* k, const
         {(const char*)out, (size_t)N * hv * d * os, "out"},
         {(const char*)state, (size_t)num_slots * hv * d * d * 4, "state"},
         {(const char*)slots, slots ? (size_t)N * 4 : 0, "state_slots"},
+        {(const char*)norm_w, norm_w ? (size_t)d * 4 : 0, "norm_weight"},
     };
     gdn_status st = check_align(spans, sizeof(spans) / sizeof(spans[0]));
     if (st != GDN_OK) return st;
@@ -380,7 +382,8 @@ gdn_status decode_call(const gdn_desc* desc, const void* q, const void* k, const
     if (st != GDN_OK) return st;
     hipError_t e = gdn::launch_decode(d, desc->io_dtype == GDN_BF16, desc->out_dtype == GDN_BF16, q, k, v, g,
                                       beta, state, slots, num_slots, out, N * hv, hk, hv, desc->qk_l2norm,
-                                      desc->scale, decode_grid(N * hv), reinterpret_cast<hipStream_t>(stream));
+                                      desc->scale, fuse, norm_w, norm_eps, decode_grid(N * hv),
+                                      reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
     return GDN_OK;
 }
@@ -537,6 +540,23 @@ gdn_status gdn_decode_step(const gdn_desc* desc, const void* q, const void* k, c
     if (!q || !k || !v || !g || !beta || !state || !out)
         return fail(GDN_ERR_INVALID_ARGUMENT, "q, k, v, g, beta, state and out must be non-NULL");
     return decode_call(desc, q, k, v, g, beta, state, desc->num_seqs, nullptr, out, stream);
+}
+
+gdn_status gdn_decode_step_ex(const gdn_desc* desc, const void* q, const void* k, const void* v,
+                              const float* g, const float* beta, float* state, void* out, int32_t fuse,
+                              const float* norm_weight, float norm_eps, void* stream) {
+    g_err[0] = 0;
+    gdn_status st = check_desc(desc, false);
+    if (st != GDN_OK) return st;
+    if (!q || !k || !v || !g || !beta || !state || !out)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "q, k, v, g, beta, state and out must be non-NULL");
+    if (fuse & ~(GDN_FUSE_GATE_ACTIVATIONS | GDN_FUSE_OUTPUT_NORM))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "unknown fuse flags 0x%x", (unsigned)fuse);
+    const bool norm = (fuse & GDN_FUSE_OUTPUT_NORM) != 0;
+    if (norm && !(std::isfinite(norm_eps) && norm_eps > 0.f))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "norm_eps must be finite and > 0 (got %g)", (double)norm_eps);
+    return decode_call(desc, q, k, v, g, beta, state, desc->num_seqs, nullptr, out, stream, fuse,
+                       norm ? norm_weight : nullptr, norm ? norm_eps : 0.f);
 }
 
 gdn_status gdn_decode_step_slots(const gdn_desc* desc, const void* q, const void* k, const void* v,

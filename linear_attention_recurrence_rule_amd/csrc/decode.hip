@@ -15,6 +15,14 @@
 // Both dot products S k^ and S q^ are taken from the state as loaded, in one
 // pass.
 //
+// Two per-token operations beside the update can be folded in (flags `fuse`):
+// the gate activations, alpha = 1 / (1 + exp(x_g)) (that is exp(-softplus(x_g)))
+// and beta = 1 / (1 + exp(-x_beta)) from raw inputs, and the normalisation of
+// each head's output, o / sqrt(mean(o^2) + eps) * w over d_v.  The latter needs
+// the head's d outputs, which are spread over the workgroup's waves: each wave
+// sums its 32 rows, and one LDS exchange behind a barrier (per unit, on every
+// path) combines them.
+//
 // Layout: a workgroup has d/32 waves, and each wave owns 32 state rows.  A
 // lane holds 4 consecutive entries (16 bytes) of one row, so d/4 lanes cover a
 // row, and each wave-wide load reads 1 KiB of contiguous state.  The row sums
@@ -34,6 +42,7 @@ struct DecodeIn {
     float4 s[D / 8];  // this lane's state slices (D/8 = LPR/2 rows)
     float kx[4], qx[4];
     float v, g, b;
+    float w;   // output-norm weight of this lane's row
     int slot;  // state slot of the unit's sequence; -1: skip the unit
 };
 
@@ -43,7 +52,8 @@ template <int D, bool IN_BF16>
 __device__ __forceinline__ void decode_load(DecodeIn<D>& in, const float* __restrict__ state,
                                             const int32_t* __restrict__ slots, int num_slots, const void* q,
                                             const void* k, const void* v, const float* g, const float* beta,
-                                            int unit, int h_k, int h_v, int wave, int lane) {
+                                            const float* __restrict__ norm_w, int unit, int h_k, int h_v, int wave,
+                                            int lane) {
     constexpr int LPR = D / 4, RPI = WAVE / LPR, NL = LPR / 2;
     const int n = unit / h_v, h = unit - n * h_v;
     const int hk = h / (h_v / h_k);
@@ -61,22 +71,26 @@ __device__ __forceinline__ void decode_load(DecodeIn<D>& in, const float* __rest
     load4<IN_BF16>(q, ((size_t)n * h_k + hk) * D + 4 * c, in.qx);
     const int mrow = (c < NL) ? c : c - NL;
     in.v = load1<IN_BF16>(v, (size_t)unit * D + wave * 32 + mrow * RPI + sub);
+    in.w = norm_w ? norm_w[wave * 32 + mrow * RPI + sub] : 1.f;
     in.g = g[unit];
     in.b = beta[unit];
 }
 
 // One token of the recurrence on the register-resident state slices `sr`
-// (updated in place); writes the token's output o = S q^ at `orow` (the
-// output row of this unit and token).  `ub` is this wave's 32-float LDS
-// area, through which u is broadcast to the lanes of its row group.
-// Cross-lane sums run on DPP and v_permlane16_swap (no LDS round trips).
-template <int D, bool OUT_BF16>
+// (updated in place), with decay alpha and write strength bin; writes the
+// token's output o = S q^ at `orow` (the output row of this unit and token).
+// `ub` is this wave's 32-float LDS area, through which u is broadcast to the
+// lanes of its row group.  Cross-lane sums run on DPP and v_permlane16_swap.
+// With NORM the output is normalised over the head's d rows first: wrow is
+// the weight of this lane's row and nb the unit's D/32-float LDS exchange
+// area; every wave of the workgroup must call it.
+template <int D, bool OUT_BF16, bool NORM = false>
 __device__ __forceinline__ void decode_token(float4 (&sr)[D / 8], const float (&kin)[4], const float (&qin)[4],
-                                             float vin, float gin, float bin, void* out, size_t orow, int l2norm,
-                                             float scale, float* ub, int wave, int lane) {
+                                             float vin, float alpha, float bin, void* out, size_t orow, int l2norm,
+                                             float scale, float* ub, int wave, int lane, float wrow = 1.f,
+                                             float eps = 0.f, float* nb = nullptr) {
     constexpr int LPR = D / 4, RPI = WAVE / LPR, NL = LPR / 2;
     const int c = lane % LPR, sub = lane / LPR;
-    const float alpha = expf(gin);
     float ssk = 0.f, ssq = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) { ssk += kin[e] * kin[e]; ssq += qin[e] * qin[e]; }
@@ -108,7 +122,23 @@ __device__ __forceinline__ void decode_token(float4 (&sr)[D / 8], const float (&
     float u_pair;
     if constexpr (NL == 16) u_pair = permlane16_swap(u, u).x;
     else u_pair = row_partner<8>(u);
-    if (c >= NL) store1<OUT_BF16>(out, orow * D + row, alpha * red + u_pair * kq);
+    const float ov = alpha * red + u_pair * kq;  // lanes c >= NL: the output of `row`
+    if constexpr (NORM) {
+        // sum of squares: this wave's 32 rows (the halves of the wave are its two
+        // 32-lane sums), then the waves' sums through LDS
+        const float o2 = lane_group_sum<32>(c >= NL ? ov * ov : 0.f);
+        const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(o2), 0)) +
+                         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(o2), 32));
+        if (lane == 0) nb[wave] = ws;
+        lds_barrier();
+        float tot = 0.f;
+#pragma unroll
+        for (int w = 0; w < D / 32; ++w) tot += nb[w];
+        const float r = 1.0f / sqrtf(tot * (1.0f / D) + eps);
+        if (c >= NL) store1<OUT_BF16>(out, orow * D + row, ov * r * wrow);
+    } else {
+        if (c >= NL) store1<OUT_BF16>(out, orow * D + row, ov);
+    }
 
     // rank-1 update; u of row m of this row group, broadcast through LDS
     // (one wave's LDS operations complete in order)
@@ -140,49 +170,84 @@ __device__ __forceinline__ void state_store(const float4 (&sr)[D / 8], float* __
         *reinterpret_cast<float4*>(S + (size_t)(wave * 32 + m * RPI + sub) * D + 4 * c) = sr[m];
 }
 
-template <int D, bool OUT_BF16>
+// raw_gates: in.g and in.b are the raw gate inputs (see the header).
+template <int D, bool OUT_BF16, bool NORM>
 __device__ __forceinline__ void decode_compute(DecodeIn<D>& in, float* __restrict__ state, void* out, int unit,
-                                               int h_v, int l2norm, float scale, float* ub, int wave, int lane) {
+                                               int h_v, int l2norm, float scale, float* ub, int wave, int lane,
+                                               bool raw_gates, float eps, float* nb) {
     if (in.slot < 0) {  // skipped: zero outputs, state untouched
         constexpr int LPR = D / 4, RPI = WAVE / LPR, NL = LPR / 2;
         const int c = lane % LPR, sub = lane / LPR;
         if (c >= NL) store1<OUT_BF16>(out, (size_t)unit * D + wave * 32 + (c - NL) * RPI + sub, 0.f);
+        if constexpr (NORM) lds_barrier();  // one barrier per unit on every path
         return;
     }
     const int h = unit % h_v;
-    decode_token<D, OUT_BF16>(in.s, in.kx, in.qx, in.v, in.g, in.b, out, (size_t)unit, l2norm, scale, ub, wave,
-                              lane);
+    float alpha, bta;
+    if (raw_gates) {
+        alpha = 1.0f / (1.0f + expf(in.g));
+        bta = 1.0f / (1.0f + expf(-in.b));
+    } else {
+        alpha = expf(in.g);
+        bta = in.b;
+    }
+    decode_token<D, OUT_BF16, NORM>(in.s, in.kx, in.qx, in.v, alpha, bta, out, (size_t)unit, l2norm, scale, ub,
+                                    wave, lane, in.w, eps, nb);
     state_store<D>(in.s, state + ((size_t)in.slot * h_v + h) * D * D, wave, lane);
 }
 
 // Each workgroup walks units blockIdx.x, blockIdx.x + gridDim.x, ... with the
 // next unit's state and token inputs loaded while the current unit computes.
 // Every iteration issues the same loads (past the end it re-reads the last
-// unit, unused), so each wait covers exactly one unit's data.
+// unit, unused), so each wait covers exactly one unit's data.  Units alternate
+// between two LDS exchange areas for the output norm: a wave writes the area
+// of unit i + 2 only after the barrier of unit i + 1, which every wave reaches
+// after its reads of unit i.
+template <int D, bool IN_BF16, bool OUT_BF16, bool NORM>
+__device__ __forceinline__ void decode_units(const void* __restrict__ q, const void* __restrict__ k,
+                                             const void* __restrict__ v, const float* __restrict__ g,
+                                             const float* __restrict__ beta, float* __restrict__ state,
+                                             const int32_t* __restrict__ slots, int num_slots, void* __restrict__ out,
+                                             int units, int h_k, int h_v, int l2norm, float scale, bool raw_gates,
+                                             const float* __restrict__ norm_w, float eps, float* ub, float* nsum) {
+    const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
+    const int stride = gridDim.x, last = units - 1;
+    int u = blockIdx.x;
+    if (u > last) return;
+    DecodeIn<D> A, B;
+    decode_load<D, IN_BF16>(A, state, slots, num_slots, q, k, v, g, beta, norm_w, u, h_k, h_v, wave, lane);
+    for (;;) {
+        decode_load<D, IN_BF16>(B, state, slots, num_slots, q, k, v, g, beta, norm_w, min(u + stride, last), h_k,
+                                h_v, wave, lane);
+        decode_compute<D, OUT_BF16, NORM>(A, state, out, u, h_v, l2norm, scale, ub, wave, lane, raw_gates, eps, nsum);
+        u += stride;
+        if (u > last) break;
+        decode_load<D, IN_BF16>(A, state, slots, num_slots, q, k, v, g, beta, norm_w, min(u + stride, last), h_k,
+                                h_v, wave, lane);
+        decode_compute<D, OUT_BF16, NORM>(B, state, out, u, h_v, l2norm, scale, ub, wave, lane, raw_gates, eps,
+                                          nsum + D / 32);
+        u += stride;
+        if (u > last) break;
+    }
+}
+
+// fuse: bit 0 raw gate inputs, bit 1 output norm (weights norm_w, NULL for ones).
 template <int D, bool IN_BF16, bool OUT_BF16>
 __global__ __launch_bounds__(2 * D) void decode_step_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ state,
     const int32_t* __restrict__ slots, int num_slots, void* __restrict__ out, int units, int h_k, int h_v,
-    int l2norm, float scale) {
-    const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
-    const int stride = gridDim.x, last = units - 1;
+    int l2norm, float scale, int fuse, const float* __restrict__ norm_w, float norm_eps) {
     __shared__ __align__(16) float ubuf[(D / 32) * 32];
-    float* ub = ubuf + wave * 32;
-    int u = blockIdx.x;
-    if (u > last) return;
-    DecodeIn<D> A, B;
-    decode_load<D, IN_BF16>(A, state, slots, num_slots, q, k, v, g, beta, u, h_k, h_v, wave, lane);
-    for (;;) {
-        decode_load<D, IN_BF16>(B, state, slots, num_slots, q, k, v, g, beta, min(u + stride, last), h_k, h_v, wave, lane);
-        decode_compute<D, OUT_BF16>(A, state, out, u, h_v, l2norm, scale, ub, wave, lane);
-        u += stride;
-        if (u > last) break;
-        decode_load<D, IN_BF16>(A, state, slots, num_slots, q, k, v, g, beta, min(u + stride, last), h_k, h_v, wave, lane);
-        decode_compute<D, OUT_BF16>(B, state, out, u, h_v, l2norm, scale, ub, wave, lane);
-        u += stride;
-        if (u > last) break;
-    }
+    __shared__ __align__(16) float nsum[2 * (D / 32)];
+    float* ub = ubuf + (threadIdx.x / WAVE) * 32;
+    const bool raw_gates = (fuse & 1) != 0;
+    if (fuse & 2)
+        decode_units<D, IN_BF16, OUT_BF16, true>(q, k, v, g, beta, state, slots, num_slots, out, units, h_k, h_v,
+                                                 l2norm, scale, raw_gates, norm_w, norm_eps, ub, nsum);
+    else
+        decode_units<D, IN_BF16, OUT_BF16, false>(q, k, v, g, beta, state, slots, num_slots, out, units, h_k, h_v,
+                                                  l2norm, scale, raw_gates, nullptr, 0.f, ub, nsum);
 }
 
 // ---- direct scan: the token recurrence with the state in registers ---------------------
@@ -253,8 +318,8 @@ __global__ __launch_bounds__(2 * D) void direct_scan_kernel(
                     const TokIn<D, IN_BF16> cur = buf[i];
                     token_load<D, IN_BF16>(buf[i], q, k, v, g, beta, (size_t)min(t + i + DIRECT_PREFETCH, e0 - 1), h,
                                            hk, h_k, h_v, wave, lane);
-                    decode_token<D, OUT_BF16>(sr, cur.kx, cur.qx, cur.v, cur.g, cur.b, out, (size_t)(t + i) * h_v + h,
-                                              l2norm, scale, ub, wave, lane);
+                    decode_token<D, OUT_BF16>(sr, cur.kx, cur.qx, cur.v, expf(cur.g), cur.b, out,
+                                              (size_t)(t + i) * h_v + h, l2norm, scale, ub, wave, lane);
                 }
             }
         }
@@ -288,22 +353,23 @@ hipError_t launch_direct(int d, bool in_bf16, bool out_bf16, const void* q, cons
 template <int D, bool IB, bool OB>
 static hipError_t launch_decode_t(const void* q, const void* k, const void* v, const float* g,
                                   const float* beta, float* state, const int32_t* slots, int num_slots,
-                                  void* out, int units, int h_k, int h_v, int l2norm, float scale, int grid,
-                                  hipStream_t stream) {
+                                  void* out, int units, int h_k, int h_v, int l2norm, float scale, int fuse,
+                                  const float* norm_w, float norm_eps, int grid, hipStream_t stream) {
     hipLaunchKernelGGL((decode_step_kernel<D, IB, OB>), dim3(grid), dim3(2 * D), 0, stream, q, k, v,
-                       g, beta, state, slots, num_slots, out, units, h_k, h_v, l2norm, scale);
+                       g, beta, state, slots, num_slots, out, units, h_k, h_v, l2norm, scale, fuse, norm_w,
+                       norm_eps);
     return hipGetLastError();
 }
 
 hipError_t launch_decode(int d, bool in_bf16, bool out_bf16, const void* q, const void* k,
                          const void* v, const float* g, const float* beta, float* state, const int32_t* slots,
                          int num_slots, void* out, int units, int h_k, int h_v, int l2norm, float scale,
-                         int grid, hipStream_t stream) {
+                         int fuse, const float* norm_w, float norm_eps, int grid, hipStream_t stream) {
     if (grid < 1 || grid > units) grid = units;
 #define GDN_DEC(D, IB, OB)                                                                        \
     if (d == D && in_bf16 == IB && out_bf16 == OB)                                                \
         return launch_decode_t<D, IB, OB>(q, k, v, g, beta, state, slots, num_slots, out, units, h_k, h_v, \
-                                          l2norm, scale, grid, stream);
+                                          l2norm, scale, fuse, norm_w, norm_eps, grid, stream);
     GDN_DEC(128, true, true) GDN_DEC(128, true, false) GDN_DEC(128, false, true)
     GDN_DEC(128, false, false) GDN_DEC(64, true, true) GDN_DEC(64, true, false)
     GDN_DEC(64, false, true) GDN_DEC(64, false, false)

@@ -169,6 +169,17 @@ __device__ __forceinline__ float dpp(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
+// Workgroup barrier that orders LDS accesses only: each wave waits for its own
+// LDS operations, not for its global stores or loads in flight (a workgroup
+// release fence would wait for those too).  The signal fences keep the
+// compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // Sum / max over aligned groups of N lanes (N = 8 or 16), result in every lane.
 template <int N>
 __device__ __forceinline__ float group_sum(float x) {

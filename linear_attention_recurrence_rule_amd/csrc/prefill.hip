@@ -210,17 +210,6 @@ __device__ __forceinline__ void store4(OP* dst, const f4_t& x) {
 constexpr int PREP_THREADS = 512;
 constexpr int PREP_WAVES = PREP_THREADS / WAVE;
 
-// Workgroup barrier that orders LDS accesses only: each wave waits for its own
-// LDS operations, not for its global stores or loads in flight (a workgroup
-// release fence would wait for those too).  The signal fences keep the
-// compiler from moving memory accesses across the barrier.
-__device__ __forceinline__ void lds_barrier() {
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
 // Six 16x16 fp32 matrices in accumulator layout, kept in the blocks of b.ax above the
 // diagonal (unused once A is formed): slot s is block (0,1), (0,2), (0,3), (1,2), (1,3), (2,3).
 // Lane (j, q) owns row j, columns 4q..4q+3 of its block (one 16-byte access).

@@ -87,6 +87,8 @@ def lib():
             L.gdn_decode_step.restype = ctypes.c_int
             L.gdn_decode_step_slots.argtypes = [dp, vp, vp, vp, vp, vp, vp, ctypes.c_int32, vp, vp, vp]
             L.gdn_decode_step_slots.restype = ctypes.c_int
+            L.gdn_decode_step_ex.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32, vp, ctypes.c_float, vp]
+            L.gdn_decode_step_ex.restype = ctypes.c_int
             L.gdn_status_str.argtypes = [ctypes.c_int]
             L.gdn_status_str.restype = ctypes.c_char_p
             L.gdn_last_error.argtypes = []
@@ -196,6 +198,16 @@ def gdn_prefill_direct(desc, q, k, v, g, beta, state_in, out, state_out, cu_seql
 def gdn_decode_step(desc, q, k, v, g, beta, state, out, stream=None):
     _check(lib().gdn_decode_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                  _ptr(state), _ptr(out), _stream(stream)))
+
+
+GDN_FUSE_GATE_ACTIVATIONS = 1
+GDN_FUSE_OUTPUT_NORM = 2
+
+
+def gdn_decode_step_ex(desc, q, k, v, g, beta, state, out, fuse, norm_weight, norm_eps, stream=None):
+    _check(lib().gdn_decode_step_ex(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                    _ptr(state), _ptr(out), int(fuse), _ptr(norm_weight), float(norm_eps),
+                                    _stream(stream)))
 
 
 def gdn_decode_step_slots(desc, q, k, v, g, beta, state_pool, num_slots, state_slots, out, stream=None):
@@ -354,6 +366,36 @@ def decode_step(q, k, v, g, beta, state, *, out=None, out_dtype=None, qk_l2norm=
     if out is None:
         out = torch.empty((N, h_v, d), dtype=_TORCH_DT[od], device=dev)
     gdn_decode_step(desc, q, k, v, g, beta, state, out, stream)
+    return out
+
+
+def decode_step_fused(q, k, v, g, beta, state, *, raw_gates=True, output_norm=True, norm_weight=None,
+                      norm_eps=1e-6, out=None, out_dtype=None, qk_l2norm=True, scale=1.0, stream=None):
+    """decode_step with the per-token operations beside it folded in: with
+    raw_gates, g and beta are the raw inputs x_g, x_beta (alpha = 1 / (1 + e^x_g),
+    beta = 1 / (1 + e^-x_beta)); with output_norm, each head's output is divided by
+    its root-mean-square over d (plus norm_eps inside the root) and multiplied by
+    norm_weight ([d] fp32, None for ones).  state is updated in place."""
+    dev = q.device
+    io = _io_dtype(q)
+    N, h_k, d = q.shape
+    h_v = v.shape[1]
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype, dev)
+    _need(g, "g", torch.float32, dev)
+    _need(beta, "beta", torch.float32, dev)
+    _need(state, "state", torch.float32, dev)
+    if norm_weight is not None:
+        _need(norm_weight, "norm_weight", torch.float32, dev)
+        if norm_weight.numel() != d:
+            raise ValueError("norm_weight must hold d = %d values (got %d)" % (d, norm_weight.numel()))
+    od = io if out_dtype is None else out_dtype
+    desc = make_desc(num_seqs=N, total_tokens=N, h_k=h_k, h_v=h_v, d=d, io_dtype=io, out_dtype=od,
+                     qk_l2norm=qk_l2norm, scale=scale)
+    if out is None:
+        out = torch.empty((N, h_v, d), dtype=_TORCH_DT[od], device=dev)
+    fuse = (GDN_FUSE_GATE_ACTIVATIONS if raw_gates else 0) | (GDN_FUSE_OUTPUT_NORM if output_norm else 0)
+    gdn_decode_step_ex(desc, q, k, v, g, beta, state, out, fuse, norm_weight, norm_eps, stream)
     return out
 
 

@@ -89,9 +89,11 @@ def _qkv(rng, shape_qk, shape_v, io_dtype):
 
 
 def _gates(rng, shape, gate_mean):
+    """g and beta (float32), and the raw inputs x_g, x_b they come from (float32)."""
     xg = rng.standard_normal(shape, dtype=np.float32).astype(np.float64) + gate_mean
     xb = rng.standard_normal(shape, dtype=np.float32).astype(np.float64)
-    return (-_softplus(xg)).astype(np.float32), _sigmoid(xb).astype(np.float32)
+    return ((-_softplus(xg)).astype(np.float32), _sigmoid(xb).astype(np.float32),
+            xg.astype(np.float32), xb.astype(np.float32))
 
 
 def prefill_inputs(*, seed, total_tokens=None, lengths=None, h_k, h_v, d, io_dtype,
@@ -114,7 +116,7 @@ def prefill_inputs(*, seed, total_tokens=None, lengths=None, h_k, h_v, d, io_dty
         cu = None
         N = 1
     q, k, v = _qkv(rng, (T, h_k, d), (T, h_v, d), io_dtype)
-    g, beta = _gates(rng, (T, h_v), gate_mean)
+    g, beta, _, _ = _gates(rng, (T, h_v), gate_mean)
     s0 = None
     if state_std > 0:
         s0 = (state_std * rng.standard_normal((N, h_v, d, d), dtype=np.float32)).astype(np.float32)
@@ -125,12 +127,13 @@ def prefill_inputs(*, seed, total_tokens=None, lengths=None, h_k, h_v, d, io_dty
 def decode_inputs(*, seed, num_seqs, steps, h_k, h_v, d, io_dtype, state_std=0.02,
                   gate_mean=0.0):
     """``steps`` fresh tokens per sequence, pre-drawn: q,k [steps,N,h_k,d],
-    v [steps,N,h_v,d], g,beta [steps,N,h_v], initial state [N,h_v,d,d]."""
+    v [steps,N,h_v,d], g,beta [steps,N,h_v], initial state [N,h_v,d,d]; also the
+    raw gate inputs x_g, x_beta [steps,N,h_v] that g and beta come from."""
     rng = np.random.default_rng(seed)
     q, k, v = _qkv(rng, (steps, num_seqs, h_k, d), (steps, num_seqs, h_v, d), io_dtype)
-    g, beta = _gates(rng, (steps, num_seqs, h_v), gate_mean)
+    g, beta, x_g, x_b = _gates(rng, (steps, num_seqs, h_v), gate_mean)
     s0 = (state_std * rng.standard_normal((num_seqs, h_v, d, d), dtype=np.float32)).astype(np.float32)
-    return dict(q=q, k=k, v=v, g=g, beta=beta, state=s0, num_seqs=num_seqs, steps=steps,
+    return dict(q=q, k=k, v=v, g=g, beta=beta, x_g=x_g, x_beta=x_b, state=s0, num_seqs=num_seqs, steps=steps,
                 h_k=h_k, h_v=h_v, d=d, io_dtype=io_dtype)
 
 

@@ -37,7 +37,7 @@ def test_exports_every_declared_function(L):
     assert set(names) == {"gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_prefill_prepare",
                           "gdn_prefill_scan", "gdn_prefill_direct", "gdn_prefill_segmented_workspace_bytes",
                           "gdn_prefill_segmented", "gdn_prefill_two_level_workspace_bytes", "gdn_prefill_two_level",
-                          "gdn_decode_step", "gdn_decode_step_slots",
+                          "gdn_decode_step", "gdn_decode_step_slots", "gdn_decode_step_ex",
                           "gdn_status_str", "gdn_last_error"}
     for n in names:
         assert hasattr(L, n), n
@@ -192,6 +192,28 @@ def test_decode_slots_rejects_bad_arguments(L):
     assert "num_slots" in gdn.last_error()
     assert call(desc(num_seqs=4), i=FAKE + 6 << 32 | 2) == gdn.GDN_ERR_INVALID_ARGUMENT      # misaligned slots
     assert call(desc(num_seqs=4), i=(FAKE + 5 << 32) + 64) == gdn.GDN_ERR_INVALID_ARGUMENT  # slots inside the pool
+    assert "overlap" in gdn.last_error()
+
+
+@fake_pointers
+def test_decode_ex_rejects_bad_arguments(L):
+    lib = gdn.lib()
+    def call(d, **p):
+        a = dict(q=FAKE, k=FAKE + 1 << 32, v=FAKE + 2 << 32, g=FAKE + 3 << 32, b=FAKE + 4 << 32,
+                 s=FAKE + 5 << 32, o=FAKE + 6 << 32, f=3, w=FAKE + 7 << 32, e=1e-6)
+        a.update(p)
+        return lib.gdn_decode_step_ex(ctypes.byref(d), a["q"], a["k"], a["v"], a["g"], a["b"], a["s"], a["o"],
+                                      a["f"], a["w"], a["e"], None)
+    assert call(desc(num_seqs=8, h_v=30)) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call(desc(num_seqs=8, d=32)) == gdn.GDN_ERR_UNSUPPORTED
+    assert call(desc(num_seqs=8), s=None) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call(desc(num_seqs=8), f=4) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert "flags" in gdn.last_error()
+    for eps in (0.0, -1e-6, float("nan"), float("inf")):
+        assert call(desc(num_seqs=8), e=eps) == gdn.GDN_ERR_INVALID_ARGUMENT
+        assert "norm_eps" in gdn.last_error()
+    assert call(desc(num_seqs=8), w=(FAKE + 7 << 32) | 2) == gdn.GDN_ERR_INVALID_ARGUMENT    # misaligned weight
+    assert call(desc(num_seqs=8), w=(FAKE + 5 << 32) + 256) == gdn.GDN_ERR_INVALID_ARGUMENT  # weight inside state
     assert "overlap" in gdn.last_error()
 
 

@@ -210,3 +210,98 @@ def test_decode_slots_pool(d, io):
     tol = 2e-3 if io == inputs.BF16 else 1e-5
     assert normwise(host(out[vi]), ro) <= tol
     assert normwise(host(st), rs) <= tol
+
+
+# ---- gdn_decode_step_ex: raw gate inputs and the output normalisation folded in ----------------
+
+def _fused_step(x, t, state, fuse, w, out_dt, eps=1e-6):
+    out = gdn.decode_step_fused(dev(x["q"][t]), dev(x["k"][t]), dev(x["v"][t]),
+                                dev(x["x_g"][t] if fuse & 1 else x["g"][t]),
+                                dev(x["x_beta"][t] if fuse & 1 else x["beta"][t]), state,
+                                raw_gates=bool(fuse & 1), output_norm=bool(fuse & 2),
+                                norm_weight=None if w is None else dev(w), norm_eps=eps, out_dtype=out_dt)
+    return out
+
+
+def _fused_ref(x, t, ref_state, fuse, w, eps=1e-6):
+    return oracle.decode_step_ex(x["q"][t], x["k"][t], x["v"][t],
+                                 x["x_g"][t] if fuse & 1 else x["g"][t],
+                                 x["x_beta"][t] if fuse & 1 else x["beta"][t], ref_state,
+                                 h_k=x["h_k"], h_v=x["h_v"], raw_gates=bool(fuse & 1),
+                                 output_norm=bool(fuse & 2), norm_weight=w, norm_eps=eps)
+
+
+@pytest.mark.parametrize("fuse", [1, 2, 3])
+@pytest.mark.parametrize("d,io,out_dt", [(128, inputs.BF16, inputs.BF16), (128, inputs.BF16, inputs.F32),
+                                         (64, inputs.F32, inputs.F32), (64, inputs.BF16, inputs.BF16)])
+def test_decode_fused_matches_oracle(fuse, d, io, out_dt):
+    """Three steps in place with raw gates (x_g, x_beta ~ N(0, 1)), the output norm
+    (random channel weights, eps 1e-6), or both."""
+    N, h_k, h_v, steps = 5, 2, 4, 3
+    x = inputs.decode_inputs(seed=61 + d + io + 4 * fuse, num_seqs=N, steps=steps, h_k=h_k, h_v=h_v, d=d,
+                             io_dtype=io, state_std=0.3)
+    w = (1.0 + 0.5 * np.random.default_rng(fuse).standard_normal(d)).astype(np.float32)
+    state = dev(x["state"])
+    ref_state = x["state"].astype(np.float64)
+    tol = 2e-3 if io == inputs.BF16 else 1e-5
+    for t in range(steps):
+        out = _fused_step(x, t, state, fuse, w, out_dt)
+        ro, ref_state = _fused_ref(x, t, ref_state, fuse, w)
+        o = host(out)
+        if out_dt == inputs.F32:
+            assert normwise(o, ro) <= tol, normwise(o, ro)
+        else:
+            check_bf16_out(o, ro, tol)
+        assert normwise(host(state), ref_state) <= tol
+
+
+def test_decode_fused_flags_off_and_norm_leave_the_state_bitwise():
+    """No flags is gdn_decode_step bit for bit; the output norm changes only the outputs
+    (the state after flags 2 equals the state after 0, and after 3 the state after 1)."""
+    N, h_k, h_v, d = 6, 2, 8, 128
+    x = inputs.decode_inputs(seed=71, num_seqs=N, steps=1, h_k=h_k, h_v=h_v, d=d, io_dtype=inputs.BF16,
+                             state_std=0.3)
+    ref = dev(x["state"])
+    out_ref = gdn.decode_step(dev(x["q"][0]), dev(x["k"][0]), dev(x["v"][0]), dev(x["g"][0]), dev(x["beta"][0]),
+                              ref, out_dtype=inputs.F32)
+    states = {}
+    for fuse in (0, 1, 2, 3):
+        st = dev(x["state"])
+        out = _fused_step(x, 0, st, fuse, None, inputs.F32)
+        states[fuse] = st
+        if fuse == 0:
+            assert torch.equal(out, out_ref) and torch.equal(st, ref)
+    assert torch.equal(states[2], states[0]) and torch.equal(states[3], states[1])
+
+
+def test_decode_fused_extreme_raw_gates():
+    """Raw gate inputs at +-100 and 0: alpha and beta reach 0 and 1 without overflow."""
+    N, h_k, h_v, d = 4, 1, 6, 64
+    x = inputs.decode_inputs(seed=73, num_seqs=N, steps=1, h_k=h_k, h_v=h_v, d=d, io_dtype=inputs.F32,
+                             state_std=0.5)
+    vals = np.array([-100.0, 0.0, 100.0], dtype=np.float32)
+    x["x_g"][0] = vals[np.arange(N * h_v).reshape(N, h_v) % 3]
+    x["x_beta"][0] = vals[(np.arange(N * h_v).reshape(N, h_v) // 3) % 3]
+    state = dev(x["state"])
+    out = _fused_step(x, 0, state, 3, None, inputs.F32)
+    ro, rs = _fused_ref(x, 0, x["state"].astype(np.float64), 3, None)
+    assert np.isfinite(host(out)).all()
+    assert normwise(host(out), ro) <= 1e-5 and normwise(host(state), rs) <= 1e-5
+
+
+def test_decode_fused_full_workload():
+    """The 64-sequence x 32-v-head, d = 128 decode workload with both folds, raw gates
+    from the workload's own N(0, 1) draws: four units per persistent workgroup, so the
+    output norm's two alternating LDS exchange areas are both reused; two steps in place."""
+    w_ = inputs.WORKLOADS["decode_n64_hv32_hk16_d128_512steps"]
+    x = inputs.workload_inputs(w_, steps=2)
+    w = (1.0 + 0.25 * np.random.default_rng(5).standard_normal(w_.d)).astype(np.float32)
+    state = dev(x["state"])
+    ref_state = x["state"].astype(np.float64)
+    for t in range(2):
+        out = _fused_step(x, t, state, 3, w, inputs.BF16)
+        ro, ref_state = oracle.decode_step_ex(x["q"][t], x["k"][t], x["v"][t], x["x_g"][t], x["x_beta"][t],
+                                              ref_state, h_k=w_.h_k, h_v=w_.h_v, raw_gates=True, output_norm=True,
+                                              norm_weight=w, norm_eps=1e-6, threads=16)
+        check_bf16_out(host(out), ro, 2e-3)
+        assert normwise(host(state), ref_state) <= 2e-3
