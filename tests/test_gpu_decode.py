@@ -305,3 +305,33 @@ def test_decode_fused_full_workload():
                                               norm_weight=w, norm_eps=1e-6, threads=16)
         check_bf16_out(host(out), ro, 2e-3)
         assert normwise(host(state), ref_state) <= 2e-3
+
+
+def test_decode_fused_hip_graph_replays_match_eager():
+    """The fused step (raw gates, output norm with weights) captured once in a HIP graph; every
+    replay, with eager work and a synchronisation in between, reproduces the eager launches bit
+    for bit."""
+    N, h_k, h_v, d, steps = 4, 2, 4, 128, 3
+    x = inputs.decode_inputs(seed=17, num_seqs=N, steps=steps, h_k=h_k, h_v=h_v, d=d, io_dtype=inputs.BF16,
+                             state_std=0.1)
+    q, k, v, xg, xb = (dev(x[n]) for n in ("q", "k", "v", "x_g", "x_beta"))
+    w = dev((1.0 + 0.5 * np.random.default_rng(3).standard_normal(d)).astype(np.float32))
+    s0 = dev(x["state"])
+    state_e = s0.clone()
+    outs_e = torch.stack([gdn.decode_step_fused(q[t], k[t], v[t], xg[t], xb[t], state_e, norm_weight=w,
+                                                out_dtype=inputs.F32) for t in range(steps)])
+    state_g = s0.clone()
+    out_g = torch.empty((steps, N, h_v, d), dtype=torch.float32, device=s0.device)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for t in range(steps):
+            gdn.decode_step_fused(q[t], k[t], v[t], xg[t], xb[t], state_g, norm_weight=w, out=out_g[t],
+                                  out_dtype=inputs.F32)
+    for _ in range(3):
+        state_g.copy_(s0)
+        out_g.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, outs_e) and torch.equal(state_g, state_e)
