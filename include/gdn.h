@@ -318,6 +318,23 @@ gdn_status gdn_prefill_direct(const gdn_desc *desc,
                               const int32_t *cu_seqlens,
                               void *stream);
 
+/*
+ * gdn_prefill_direct with the per-token operations of gdn_decode_step_ex
+ * folded in, token by token: raw gate inputs (GDN_FUSE_GATE_ACTIVATIONS) and
+ * each (token, v-head) output normalised over d_v (GDN_FUSE_OUTPUT_NORM, with
+ * norm_weight and norm_eps as there), for multi-token decode and verify steps.
+ * Without flags this is gdn_prefill_direct.  Errors: those of
+ * gdn_prefill_direct and the flag, eps and weight checks of gdn_decode_step_ex.
+ */
+gdn_status gdn_prefill_direct_ex(const gdn_desc *desc,
+                                 const void *q, const void *k, const void *v,
+                                 const float *g, const float *beta,
+                                 const float *state_in,
+                                 void *out, float *state_out,
+                                 const int32_t *cu_seqlens,
+                                 int32_t fuse, const float *norm_weight, float norm_eps,
+                                 void *stream);
+
 /* Static, English name of a status code. */
 const char *gdn_status_str(gdn_status status);
 

@@ -26,7 +26,8 @@ hipError_t launch_scan_transition(int d, bool in_bf16, const void* recs, const v
                                   float* s_out, void* sink, int units, int T, int h_k, int h_v, hipStream_t stream);
 hipError_t launch_direct(int d, bool in_bf16, bool out_bf16, const void* q, const void* k, const void* v,
                          const float* g, const float* beta, const int32_t* cu, const float* s_in, float* s_out,
-                         void* out, int units, int T, int h_k, int h_v, int l2norm, float scale, hipStream_t stream);
+                         void* out, int units, int T, int h_k, int h_v, int l2norm, float scale, int fuse, const float* norm_w,
+                         float norm_eps, hipStream_t stream);
 hipError_t launch_plan(const int32_t* cu, int N, int T, int max_slots, void* info, int32_t* slot_seq,
                        hipStream_t stream);
 hipError_t launch_prep(int d, bool in_bf16, const void* q, const void* k, const void* v,
@@ -176,6 +177,45 @@ int env_int(const char* name, int dflt) {
 int decode_grid(int units) {
     const int grid = cu_count() * env_int("GDN_DECODE_WG_PER_CU", 2);
     return grid < units ? grid : units;
+}
+
+// Shared by gdn_prefill_direct and gdn_prefill_direct_ex (fuse flags, norm weight and eps).
+gdn_status direct_call(const gdn_desc* desc, const void* q, const void* k, const void* v, const float* g,
+                       const float* beta, const float* state_in, void* out, float* state_out,
+                       const int32_t* cu_seqlens, void* stream, int fuse, const float* norm_w, float norm_eps) {
+    gdn_status st = check_desc(desc, false);  // every head width and dtype the direct kernels build
+    if (st != GDN_OK) return st;
+    if (desc->total_tokens < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "total_tokens must be >= 0");
+    if (desc->total_tokens > kMaxTokens) return fail(GDN_ERR_UNSUPPORTED, "total_tokens above 2^30 not supported");
+    const int64_t T = desc->total_tokens;
+    const int N = desc->num_seqs, hk = desc->h_k, hv = desc->h_v, d = desc->d_k;
+    if (!cu_seqlens && N != 1) return fail(GDN_ERR_INVALID_ARGUMENT, "cu_seqlens is NULL but num_seqs = %d", N);
+    if (T > 0 && (!q || !k || !v || !g || !beta || !out))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "q, k, v, g, beta and out must be non-NULL");
+    const size_t io = dtype_size(desc->io_dtype), os = dtype_size(desc->out_dtype);
+    const size_t sbytes = (size_t)N * hv * d * d * 4;
+    const Span spans[] = {
+        {(const char*)q, (size_t)T * hk * d * io, "q"},
+        {(const char*)k, (size_t)T * hk * d * io, "k"},
+        {(const char*)v, (size_t)T * hv * d * io, "v"},
+        {(const char*)g, (size_t)T * hv * 4, "g"},
+        {(const char*)beta, (size_t)T * hv * 4, "beta"},
+        {(const char*)out, (size_t)T * hv * d * os, "out"},
+        {(const char*)state_in, state_in ? sbytes : 0, "state_in"},
+        {(const char*)state_out, state_out ? sbytes : 0, "state_out"},
+        {(const char*)cu_seqlens, cu_seqlens ? (size_t)(N + 1) * 4 : 0, "cu_seqlens"},
+        {(const char*)norm_w, norm_w ? (size_t)d * 4 : 0, "norm_weight"},
+    };
+    st = check_align(spans, sizeof(spans) / sizeof(spans[0]));
+    if (st != GDN_OK) return st;
+    st = check_overlaps(spans, sizeof(spans) / sizeof(spans[0]), state_in, state_out);
+    if (st != GDN_OK) return st;
+    if (!state_out && T == 0) return GDN_OK;  // nothing to compute or write
+    hipError_t e = gdn::launch_direct(d, desc->io_dtype == GDN_BF16, desc->out_dtype == GDN_BF16, q, k, v, g, beta,
+                                      cu_seqlens, state_in, state_out, out, N * hv, (int)T, hk, hv, desc->qk_l2norm,
+                                      desc->scale, fuse, norm_w, norm_eps, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "direct prefill launch: %s", hipGetErrorString(e));
+    return GDN_OK;
 }
 
 }  // namespace
@@ -494,43 +534,6 @@ gdn_status gdn_prefill_segmented(const gdn_desc* desc, const void* q, const void
     return GDN_OK;
 }
 
-gdn_status gdn_prefill_direct(const gdn_desc* desc, const void* q, const void* k, const void* v,
-                              const float* g, const float* beta, const float* state_in, void* out,
-                              float* state_out, const int32_t* cu_seqlens, void* stream) {
-    g_err[0] = 0;
-    gdn_status st = check_desc(desc, false);  // every head width and dtype the direct kernels build
-    if (st != GDN_OK) return st;
-    if (desc->total_tokens < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "total_tokens must be >= 0");
-    if (desc->total_tokens > kMaxTokens) return fail(GDN_ERR_UNSUPPORTED, "total_tokens above 2^30 not supported");
-    const int64_t T = desc->total_tokens;
-    const int N = desc->num_seqs, hk = desc->h_k, hv = desc->h_v, d = desc->d_k;
-    if (!cu_seqlens && N != 1) return fail(GDN_ERR_INVALID_ARGUMENT, "cu_seqlens is NULL but num_seqs = %d", N);
-    if (T > 0 && (!q || !k || !v || !g || !beta || !out))
-        return fail(GDN_ERR_INVALID_ARGUMENT, "q, k, v, g, beta and out must be non-NULL");
-    const size_t io = dtype_size(desc->io_dtype), os = dtype_size(desc->out_dtype);
-    const size_t sbytes = (size_t)N * hv * d * d * 4;
-    const Span spans[] = {
-        {(const char*)q, (size_t)T * hk * d * io, "q"},
-        {(const char*)k, (size_t)T * hk * d * io, "k"},
-        {(const char*)v, (size_t)T * hv * d * io, "v"},
-        {(const char*)g, (size_t)T * hv * 4, "g"},
-        {(const char*)beta, (size_t)T * hv * 4, "beta"},
-        {(const char*)out, (size_t)T * hv * d * os, "out"},
-        {(const char*)state_in, state_in ? sbytes : 0, "state_in"},
-        {(const char*)state_out, state_out ? sbytes : 0, "state_out"},
-        {(const char*)cu_seqlens, cu_seqlens ? (size_t)(N + 1) * 4 : 0, "cu_seqlens"},
-    };
-    st = check_align(spans, sizeof(spans) / sizeof(spans[0]));
-    if (st != GDN_OK) return st;
-    st = check_overlaps(spans, sizeof(spans) / sizeof(spans[0]), state_in, state_out);
-    if (st != GDN_OK) return st;
-    if (!state_out && T == 0) return GDN_OK;  // nothing to compute or write
-    hipError_t e = gdn::launch_direct(d, desc->io_dtype == GDN_BF16, desc->out_dtype == GDN_BF16, q, k, v, g, beta,
-                                      cu_seqlens, state_in, state_out, out, N * hv, (int)T, hk, hv, desc->qk_l2norm,
-                                      desc->scale, reinterpret_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return fail(GDN_ERR_HIP, "direct prefill launch: %s", hipGetErrorString(e));
-    return GDN_OK;
-}
 
 gdn_status gdn_decode_step(const gdn_desc* desc, const void* q, const void* k, const void* v,
                            const float* g, const float* beta, float* state, void* out, void* stream) {
@@ -540,6 +543,27 @@ gdn_status gdn_decode_step(const gdn_desc* desc, const void* q, const void* k, c
     if (!q || !k || !v || !g || !beta || !state || !out)
         return fail(GDN_ERR_INVALID_ARGUMENT, "q, k, v, g, beta, state and out must be non-NULL");
     return decode_call(desc, q, k, v, g, beta, state, desc->num_seqs, nullptr, out, stream);
+}
+
+gdn_status gdn_prefill_direct(const gdn_desc* desc, const void* q, const void* k, const void* v,
+                              const float* g, const float* beta, const float* state_in, void* out,
+                              float* state_out, const int32_t* cu_seqlens, void* stream) {
+    g_err[0] = 0;
+    return direct_call(desc, q, k, v, g, beta, state_in, out, state_out, cu_seqlens, stream, 0, nullptr, 0.f);
+}
+
+gdn_status gdn_prefill_direct_ex(const gdn_desc* desc, const void* q, const void* k, const void* v,
+                                 const float* g, const float* beta, const float* state_in, void* out,
+                                 float* state_out, const int32_t* cu_seqlens, int32_t fuse,
+                                 const float* norm_weight, float norm_eps, void* stream) {
+    g_err[0] = 0;
+    if (fuse & ~(GDN_FUSE_GATE_ACTIVATIONS | GDN_FUSE_OUTPUT_NORM))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "unknown fuse flags 0x%x", (unsigned)fuse);
+    const bool norm = (fuse & GDN_FUSE_OUTPUT_NORM) != 0;
+    if (norm && !(std::isfinite(norm_eps) && norm_eps > 0.f))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "norm_eps must be finite and > 0 (got %g)", (double)norm_eps);
+    return direct_call(desc, q, k, v, g, beta, state_in, out, state_out, cu_seqlens, stream, fuse,
+                       norm ? norm_weight : nullptr, norm ? norm_eps : 0.f);
 }
 
 gdn_status gdn_decode_step_ex(const gdn_desc* desc, const void* q, const void* k, const void* v,

@@ -76,6 +76,19 @@ __device__ __forceinline__ void decode_load(DecodeIn<D>& in, const float* __rest
     in.b = beta[unit];
 }
 
+// Decay and write strength of one token: from g and beta as given, or from
+// raw gate inputs (alpha = 1 / (1 + e^x_g), beta = 1 / (1 + e^-x_beta)).  Both
+// kernels take them from here, so a token is computed the same way in each.
+__device__ __forceinline__ void token_gates(float g, float b, bool raw_gates, float& alpha, float& beta) {
+    if (raw_gates) {
+        alpha = 1.0f / (1.0f + expf(g));
+        beta = 1.0f / (1.0f + expf(-b));
+    } else {
+        alpha = expf(g);
+        beta = b;
+    }
+}
+
 // One token of the recurrence on the register-resident state slices `sr`
 // (updated in place), with decay alpha and write strength bin; writes the
 // token's output o = S q^ at `orow` (the output row of this unit and token).
@@ -91,9 +104,11 @@ __device__ __forceinline__ void decode_token(float4 (&sr)[D / 8], const float (&
                                              float eps = 0.f, float* nb = nullptr) {
     constexpr int LPR = D / 4, RPI = WAVE / LPR, NL = LPR / 2;
     const int c = lane % LPR, sub = lane / LPR;
+    // Every multiply-add below is an explicit fmaf: the rounding then does not
+    // depend on how the compiler contracts in each kernel that inlines this.
     float ssk = 0.f, ssq = 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) { ssk += kin[e] * kin[e]; ssq += qin[e] * qin[e]; }
+    for (int e = 0; e < 4; ++e) { ssk = fmaf(kin[e], kin[e], ssk); ssq = fmaf(qin[e], qin[e], ssq); }
     ssk = lane_group_sum<LPR>(ssk);
     ssq = lane_group_sum<LPR>(ssq);
     const float rk = l2norm ? 1.0f / sqrtf(ssk + 1e-6f) : 1.0f;
@@ -101,15 +116,15 @@ __device__ __forceinline__ void decode_token(float4 (&sr)[D / 8], const float (&
     float kx[4], qx[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) { kx[e] = kin[e] * rk; qx[e] = qin[e] * rq; }
-    const float kq = lane_group_sum<LPR>(kx[0] * qx[0] + kx[1] * qx[1] + kx[2] * qx[2] + kx[3] * qx[3]);
+    const float kq = lane_group_sum<LPR>(fmaf(kx[3], qx[3], fmaf(kx[2], qx[2], fmaf(kx[1], qx[1], kx[0] * qx[0]))));
 
     // partial row sums: x[m] = (S k^) part, x[NL + m] = (S q^) part
     float x[LPR];
 #pragma unroll
     for (int m = 0; m < NL; ++m) {
         const float4 sm = sr[m];
-        x[m] = sm.x * kx[0] + sm.y * kx[1] + sm.z * kx[2] + sm.w * kx[3];
-        x[NL + m] = sm.x * qx[0] + sm.y * qx[1] + sm.z * qx[2] + sm.w * qx[3];
+        x[m] = fmaf(sm.w, kx[3], fmaf(sm.z, kx[2], fmaf(sm.y, kx[1], sm.x * kx[0])));
+        x[NL + m] = fmaf(sm.w, qx[3], fmaf(sm.z, qx[2], fmaf(sm.y, qx[1], sm.x * qx[0])));
     }
     // afterwards lane c holds x[c] summed over its row group
     const float red = reduce_scatter<LPR>(x, c);
@@ -117,12 +132,12 @@ __device__ __forceinline__ void decode_token(float4 (&sr)[D / 8], const float (&
     const int mrow = (c < NL) ? c : c - NL;
     const int row = wave * 32 + mrow * RPI + sub;
     float u = 0.f;
-    if (c < NL) u = bin * (vin - alpha * red);
+    if (c < NL) u = bin * fmaf(-alpha, red, vin);
     // lane c >= NL takes u from lane c - NL
     float u_pair;
     if constexpr (NL == 16) u_pair = permlane16_swap(u, u).x;
     else u_pair = row_partner<8>(u);
-    const float ov = alpha * red + u_pair * kq;  // lanes c >= NL: the output of `row`
+    const float ov = fmaf(alpha, red, u_pair * kq);  // lanes c >= NL: the output of `row`
     if constexpr (NORM) {
         // sum of squares: this wave's 32 rows (the halves of the wave are its two
         // 32-lane sums), then the waves' sums through LDS
@@ -152,10 +167,10 @@ __device__ __forceinline__ void decode_token(float4 (&sr)[D / 8], const float (&
 #pragma unroll
     for (int m = 0; m < NL; ++m) {
         float4 sm = sr[m];
-        sm.x = alpha * sm.x + um[m] * kx[0];
-        sm.y = alpha * sm.y + um[m] * kx[1];
-        sm.z = alpha * sm.z + um[m] * kx[2];
-        sm.w = alpha * sm.w + um[m] * kx[3];
+        sm.x = fmaf(um[m], kx[0], alpha * sm.x);
+        sm.y = fmaf(um[m], kx[1], alpha * sm.y);
+        sm.z = fmaf(um[m], kx[2], alpha * sm.z);
+        sm.w = fmaf(um[m], kx[3], alpha * sm.w);
         sr[m] = sm;
     }
 }
@@ -184,13 +199,7 @@ __device__ __forceinline__ void decode_compute(DecodeIn<D>& in, float* __restric
     }
     const int h = unit % h_v;
     float alpha, bta;
-    if (raw_gates) {
-        alpha = 1.0f / (1.0f + expf(in.g));
-        bta = 1.0f / (1.0f + expf(-in.b));
-    } else {
-        alpha = expf(in.g);
-        bta = in.b;
-    }
+    token_gates(in.g, in.b, raw_gates, alpha, bta);
     decode_token<D, OUT_BF16, NORM>(in.s, in.kx, in.qx, in.v, alpha, bta, out, (size_t)unit, l2norm, scale, ub,
                                     wave, lane, in.w, eps, nb);
     state_store<D>(in.s, state + ((size_t)in.slot * h_v + h) * D * D, wave, lane);
@@ -280,12 +289,17 @@ __device__ __forceinline__ void token_load(TokIn<D, IN_BF16>& in, const void* q,
     in.b = beta[tok * h_v + h];
 }
 
-template <int D, bool IN_BF16, bool OUT_BF16>
-__global__ __launch_bounds__(2 * D) void direct_scan_kernel(
-    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
-    const float* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
-    const float* __restrict__ state_in, float* __restrict__ state_out, void* __restrict__ out, int T, int h_k,
-    int h_v, int l2norm, float scale) {
+// The scan of one workgroup's unit; with NORM each token's output is normalised
+// over the head's d rows (the decode step's exchange, the two LDS areas
+// alternating by token).  raw_gates: g and beta hold raw gate inputs.
+template <int D, bool IN_BF16, bool OUT_BF16, bool NORM>
+__device__ __forceinline__ void direct_unit(const void* __restrict__ q, const void* __restrict__ k,
+                                            const void* __restrict__ v, const float* __restrict__ g,
+                                            const float* __restrict__ beta, const int32_t* __restrict__ cu,
+                                            const float* __restrict__ state_in, float* __restrict__ state_out,
+                                            void* __restrict__ out, int T, int h_k, int h_v, int l2norm, float scale,
+                                            bool raw_gates, const float* __restrict__ norm_w, float eps, float* ub,
+                                            float* nsum) {
     constexpr int LPR = D / 4, RPI = WAVE / LPR, NL = LPR / 2;
     const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
     const int c = lane % LPR, sub = lane / LPR;
@@ -295,8 +309,8 @@ __global__ __launch_bounds__(2 * D) void direct_scan_kernel(
         b0 = min(max(cu[n], 0), T);
         e0 = min(max(cu[n + 1], b0), T);
     }
-    __shared__ __align__(16) float ubuf[(D / 32) * 32];
-    float* ub = ubuf + wave * 32;
+    const int mrow = (c < NL) ? c : c - NL;
+    const float wrow = (NORM && norm_w) ? norm_w[wave * 32 + mrow * RPI + sub] : 1.f;
     float4 sr[D / 8];
     const size_t sbase = (size_t)unit * D * D;
 #pragma unroll
@@ -318,8 +332,11 @@ __global__ __launch_bounds__(2 * D) void direct_scan_kernel(
                     const TokIn<D, IN_BF16> cur = buf[i];
                     token_load<D, IN_BF16>(buf[i], q, k, v, g, beta, (size_t)min(t + i + DIRECT_PREFETCH, e0 - 1), h,
                                            hk, h_k, h_v, wave, lane);
-                    decode_token<D, OUT_BF16>(sr, cur.kx, cur.qx, cur.v, expf(cur.g), cur.b, out,
-                                              (size_t)(t + i) * h_v + h, l2norm, scale, ub, wave, lane);
+                    float alpha, bta;
+                    token_gates(cur.g, cur.b, raw_gates, alpha, bta);
+                    decode_token<D, OUT_BF16, NORM>(sr, cur.kx, cur.qx, cur.v, alpha, bta, out,
+                                                    (size_t)(t + i) * h_v + h, l2norm, scale, ub, wave, lane, wrow,
+                                                    eps, nsum + ((t + i - b0) & 1) * (D / 32));
                 }
             }
         }
@@ -327,22 +344,43 @@ __global__ __launch_bounds__(2 * D) void direct_scan_kernel(
     if (state_out) state_store<D>(sr, state_out + sbase, wave, lane);
 }
 
+// fuse: bit 0 raw gate inputs, bit 1 output norm (weights norm_w, NULL for ones).
+template <int D, bool IN_BF16, bool OUT_BF16>
+__global__ __launch_bounds__(2 * D) void direct_scan_kernel(
+    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
+    const float* __restrict__ state_in, float* __restrict__ state_out, void* __restrict__ out, int T, int h_k,
+    int h_v, int l2norm, float scale, int fuse, const float* __restrict__ norm_w, float norm_eps) {
+    __shared__ __align__(16) float ubuf[(D / 32) * 32];
+    __shared__ __align__(16) float nsum[2 * (D / 32)];
+    float* ub = ubuf + (threadIdx.x / WAVE) * 32;
+    const bool raw_gates = (fuse & 1) != 0;
+    if (fuse & 2)
+        direct_unit<D, IN_BF16, OUT_BF16, true>(q, k, v, g, beta, cu, state_in, state_out, out, T, h_k, h_v, l2norm,
+                                                scale, raw_gates, norm_w, norm_eps, ub, nsum);
+    else
+        direct_unit<D, IN_BF16, OUT_BF16, false>(q, k, v, g, beta, cu, state_in, state_out, out, T, h_k, h_v,
+                                                 l2norm, scale, raw_gates, nullptr, 0.f, ub, nsum);
+}
+
 template <int D, bool IB, bool OB>
 static hipError_t launch_direct_t(const void* q, const void* k, const void* v, const float* g, const float* beta,
                                   const int32_t* cu, const float* s_in, float* s_out, void* out, int units, int T,
-                                  int h_k, int h_v, int l2norm, float scale, hipStream_t stream) {
+                                  int h_k, int h_v, int l2norm, float scale, int fuse, const float* norm_w,
+                                  float norm_eps, hipStream_t stream) {
     hipLaunchKernelGGL((direct_scan_kernel<D, IB, OB>), dim3(units), dim3(2 * D), 0, stream, q, k, v, g, beta, cu,
-                       s_in, s_out, out, T, h_k, h_v, l2norm, scale);
+                       s_in, s_out, out, T, h_k, h_v, l2norm, scale, fuse, norm_w, norm_eps);
     return hipGetLastError();
 }
 
 hipError_t launch_direct(int d, bool in_bf16, bool out_bf16, const void* q, const void* k, const void* v,
                          const float* g, const float* beta, const int32_t* cu, const float* s_in, float* s_out,
-                         void* out, int units, int T, int h_k, int h_v, int l2norm, float scale, hipStream_t stream) {
+                         void* out, int units, int T, int h_k, int h_v, int l2norm, float scale, int fuse,
+                         const float* norm_w, float norm_eps, hipStream_t stream) {
 #define GDN_DIR(D, IB, OB)                                                                                 \
     if (d == D && in_bf16 == IB && out_bf16 == OB)                                                         \
         return launch_direct_t<D, IB, OB>(q, k, v, g, beta, cu, s_in, s_out, out, units, T, h_k, h_v, l2norm, \
-                                          scale, stream);
+                                          scale, fuse, norm_w, norm_eps, stream);
     GDN_DIR(128, true, true) GDN_DIR(128, true, false) GDN_DIR(128, false, true)
     GDN_DIR(128, false, false) GDN_DIR(64, true, true) GDN_DIR(64, true, false)
     GDN_DIR(64, false, true) GDN_DIR(64, false, false)

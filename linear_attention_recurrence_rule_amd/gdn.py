@@ -89,6 +89,9 @@ def lib():
             L.gdn_decode_step_slots.restype = ctypes.c_int
             L.gdn_decode_step_ex.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32, vp, ctypes.c_float, vp]
             L.gdn_decode_step_ex.restype = ctypes.c_int
+            L.gdn_prefill_direct_ex.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32, vp,
+                                                ctypes.c_float, vp]
+            L.gdn_prefill_direct_ex.restype = ctypes.c_int
             L.gdn_status_str.argtypes = [ctypes.c_int]
             L.gdn_status_str.restype = ctypes.c_char_p
             L.gdn_last_error.argtypes = []
@@ -202,6 +205,13 @@ def gdn_decode_step(desc, q, k, v, g, beta, state, out, stream=None):
 
 GDN_FUSE_GATE_ACTIVATIONS = 1
 GDN_FUSE_OUTPUT_NORM = 2
+
+
+def gdn_prefill_direct_ex(desc, q, k, v, g, beta, state_in, out, state_out, cu_seqlens, fuse, norm_weight,
+                          norm_eps, stream=None):
+    _check(lib().gdn_prefill_direct_ex(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                       _ptr(state_in), _ptr(out), _ptr(state_out), _ptr(cu_seqlens), int(fuse),
+                                       _ptr(norm_weight), float(norm_eps), _stream(stream)))
 
 
 def gdn_decode_step_ex(desc, q, k, v, g, beta, state, out, fuse, norm_weight, norm_eps, stream=None):
@@ -321,9 +331,12 @@ def prefill_two_level(q, k, v, g, beta, *, segments, state_in=None, out_dtype=No
 
 
 def prefill_direct(q, k, v, g, beta, *, state_in=None, state_out=None, cu_seqlens=None, out_dtype=None,
-                   qk_l2norm=True, scale=1.0, want_state=True, stream=None):
+                   qk_l2norm=True, scale=1.0, want_state=True, raw_gates=False, output_norm=False,
+                   norm_weight=None, norm_eps=1e-6, stream=None):
     """Token-by-token prefill (gdn_prefill_direct).  Same arguments as ``prefill``; pass
-    ``state_out=state_in`` to update the states in place.  Returns (out, state_out or None)."""
+    ``state_out=state_in`` to update the states in place.  raw_gates and output_norm fold in
+    the per-token operations of decode_step_fused (through gdn_prefill_direct_ex).
+    Returns (out, state_out or None)."""
     dev = q.device
     io = _io_dtype(q)
     T, h_k, d = q.shape
@@ -343,7 +356,16 @@ def prefill_direct(q, k, v, g, beta, *, state_in=None, state_out=None, cu_seqlen
     out = torch.empty((T, h_v, d), dtype=_TORCH_DT[od], device=dev)
     if state_out is None and want_state:
         state_out = torch.empty((N, h_v, d, d), dtype=torch.float32, device=dev)
-    gdn_prefill_direct(desc, q, k, v, g, beta, state_in, out, state_out, cu_seqlens, stream)
+    fuse = (GDN_FUSE_GATE_ACTIVATIONS if raw_gates else 0) | (GDN_FUSE_OUTPUT_NORM if output_norm else 0)
+    if fuse:
+        if norm_weight is not None:
+            _need(norm_weight, "norm_weight", torch.float32, dev)
+            if norm_weight.numel() != d:
+                raise ValueError("norm_weight must hold d = %d values (got %d)" % (d, norm_weight.numel()))
+        gdn_prefill_direct_ex(desc, q, k, v, g, beta, state_in, out, state_out, cu_seqlens, fuse, norm_weight,
+                              norm_eps, stream)
+    else:
+        gdn_prefill_direct(desc, q, k, v, g, beta, state_in, out, state_out, cu_seqlens, stream)
     return out, state_out
 
 

@@ -179,3 +179,15 @@ def decode_step_ex(q, k, v, g, beta, state, *, h_k, h_v, raw_gates=False, output
     if output_norm:
         o = output_rms_norm(o, norm_weight, norm_eps)
     return o, s
+
+
+def scan_ex(q, k, v, g, beta, *, h_k, h_v, state_in=None, cu_seqlens=None, raw_gates=False, output_norm=False,
+            norm_weight=None, norm_eps=1e-6, qk_l2norm=True, scale=1.0, threads=0):
+    """scan with the same per-token operations as decode_step_ex, token by token."""
+    if raw_gates:
+        g, beta = gate_activations(g, beta)
+    o, s = scan(q, k, v, g, beta, h_k=h_k, h_v=h_v, state_in=state_in, cu_seqlens=cu_seqlens,
+                qk_l2norm=qk_l2norm, scale=scale, threads=threads)
+    if output_norm:
+        o = output_rms_norm(o, norm_weight, norm_eps)
+    return o, s

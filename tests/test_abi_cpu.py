@@ -37,7 +37,7 @@ def test_exports_every_declared_function(L):
     assert set(names) == {"gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_prefill_prepare",
                           "gdn_prefill_scan", "gdn_prefill_direct", "gdn_prefill_segmented_workspace_bytes",
                           "gdn_prefill_segmented", "gdn_prefill_two_level_workspace_bytes", "gdn_prefill_two_level",
-                          "gdn_decode_step", "gdn_decode_step_slots", "gdn_decode_step_ex",
+                          "gdn_decode_step", "gdn_decode_step_slots", "gdn_decode_step_ex", "gdn_prefill_direct_ex",
                           "gdn_status_str", "gdn_last_error"}
     for n in names:
         assert hasattr(L, n), n
@@ -215,6 +215,25 @@ def test_decode_ex_rejects_bad_arguments(L):
     assert call(desc(num_seqs=8), w=(FAKE + 7 << 32) | 2) == gdn.GDN_ERR_INVALID_ARGUMENT    # misaligned weight
     assert call(desc(num_seqs=8), w=(FAKE + 5 << 32) + 256) == gdn.GDN_ERR_INVALID_ARGUMENT  # weight inside state
     assert "overlap" in gdn.last_error()
+
+
+@fake_pointers
+def test_direct_ex_rejects_bad_arguments(L):
+    lib = gdn.lib()
+    def call(d, **p):
+        a = dict(q=FAKE, k=FAKE + 1 << 32, v=FAKE + 2 << 32, g=FAKE + 3 << 32, b=FAKE + 4 << 32,
+                 si=FAKE + 5 << 32, o=FAKE + 6 << 32, so=FAKE + 5 << 32, cu=None, f=3, w=FAKE + 7 << 32, e=1e-6)
+        a.update(p)
+        return lib.gdn_prefill_direct_ex(ctypes.byref(d), a["q"], a["k"], a["v"], a["g"], a["b"], a["si"], a["o"],
+                                         a["so"], a["cu"], a["f"], a["w"], a["e"], None)
+    assert call(desc(total_tokens=16, h_v=30)) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call(desc(total_tokens=16), f=8) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert "flags" in gdn.last_error()
+    assert call(desc(total_tokens=16), e=0.0) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call(desc(total_tokens=16), e=float("nan")) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call(desc(total_tokens=16), w=(FAKE + 6 << 32) + 64) == gdn.GDN_ERR_INVALID_ARGUMENT  # weight in out
+    assert "overlap" in gdn.last_error()
+    assert call(desc(total_tokens=16, num_seqs=2)) == gdn.GDN_ERR_INVALID_ARGUMENT  # no cu_seqlens
 
 
 def test_two_level_workspace_bytes(L):

@@ -112,3 +112,47 @@ def test_direct_matches_chunked_and_edge_cases():
     e = inputs.prefill_inputs(seed=12, lengths=[0, 0], h_k=2, h_v=4, d=128, io_dtype=inputs.BF16, state_std=0.1)
     oe, se = run_direct(e, inputs.BF16)
     assert oe.numel() == 0 and torch.equal(se, dev(e["state_in"]))
+
+
+# ---- gdn_prefill_direct_ex: the decode step's per-token operations, token by token -------------
+
+@pytest.mark.parametrize("fuse", [1, 2, 3])
+@pytest.mark.parametrize("d,io,out_dt", [(128, inputs.BF16, inputs.F32), (128, inputs.BF16, inputs.BF16),
+                                         (64, inputs.F32, inputs.F32)])
+def test_direct_fused_matches_oracle(fuse, d, io, out_dt):
+    """Multi-token decode / verify shapes (1, 3, 16 and 40 tokens per sequence) with raw gate
+    inputs ~ N(0, 1), the output norm (random channel weights), or both."""
+    x = inputs.prefill_inputs(seed=81 + d + fuse, lengths=[1, 3, 16, 40], h_k=2, h_v=4, d=d, io_dtype=io,
+                              state_std=0.3)
+    rng = np.random.default_rng(90 + fuse)
+    if fuse & 1:
+        x["g"] = rng.standard_normal(x["g"].shape, dtype=np.float32)
+        x["beta"] = rng.standard_normal(x["beta"].shape, dtype=np.float32)
+    w = (1.0 + 0.5 * rng.standard_normal(d)).astype(np.float32)
+    out, st = run_direct(x, out_dt, raw_gates=bool(fuse & 1), output_norm=bool(fuse & 2), norm_weight=dev(w))
+    ro, rs = oracle.scan_ex(x["q"], x["k"], x["v"], x["g"], x["beta"], h_k=x["h_k"], h_v=x["h_v"],
+                            state_in=x["state_in"], cu_seqlens=x["cu_seqlens"], raw_gates=bool(fuse & 1),
+                            output_norm=bool(fuse & 2), norm_weight=w)
+    tol = 2e-3 if io == inputs.BF16 else 1e-5
+    if out_dt == inputs.F32:
+        assert normwise(host(out), ro) <= tol, normwise(host(out), ro)
+    else:
+        check_bf16_out(host(out), ro, tol)
+    assert normwise(host(st), rs) <= tol
+
+
+def test_direct_fused_flags_off_and_norm_leave_the_state_bitwise():
+    x = inputs.prefill_inputs(seed=95, lengths=[5, 12], h_k=2, h_v=4, d=128, io_dtype=inputs.BF16, state_std=0.3)
+    o0, s0 = run_direct(x, inputs.F32)
+    d_ = dev
+    ref = gdn.gdn_prefill_direct_ex
+    desc = gdn.make_desc(num_seqs=2, total_tokens=17, h_k=2, h_v=4, d=128, io_dtype=gdn.GDN_BF16,
+                         out_dtype=gdn.GDN_F32)
+    q, k, v, g, b = (d_(x[n]) for n in ("q", "k", "v", "g", "beta"))
+    s_in, cu = d_(x["state_in"]), d_(x["cu_seqlens"])
+    o1, s1 = torch.empty_like(o0), torch.empty_like(s0)
+    ref(desc, q, k, v, g, b, s_in, o1, s1, cu, 0, None, 0.0)
+    assert torch.equal(o1, o0) and torch.equal(s1, s0)
+    o2, s2 = torch.empty_like(o0), torch.empty_like(s0)
+    ref(desc, q, k, v, g, b, s_in, o2, s2, cu, gdn.GDN_FUSE_OUTPUT_NORM, None, 1e-6)
+    assert torch.equal(s2, s0) and not torch.equal(o2, o0)

@@ -430,3 +430,24 @@ def test_decode_step_ex_composes_the_pinned_parts():
     assert np.array_equal(s4, s0)
     assert np.allclose(np.sqrt(np.mean(o4 * o4, axis=-1)), 1.0, rtol=1e-14)
     assert np.allclose(o4 * np.sqrt(np.mean(o0 * o0, axis=-1, keepdims=True)), o0, rtol=1e-13)
+
+
+def test_scan_ex_is_decode_step_ex_token_by_token():
+    """Two tokens through scan_ex equal two decode_step_ex calls; no options is scan."""
+    rng = np.random.default_rng(8)
+    h_k, h_v, d = 1, 2, 8
+    q, k, v = rng.standard_normal((2, h_k, d)), rng.standard_normal((2, h_k, d)), rng.standard_normal((2, h_v, d))
+    xg, xb = rng.standard_normal((2, h_v)), rng.standard_normal((2, h_v))
+    S0 = 0.3 * rng.standard_normal((1, h_v, d, d))
+    w = rng.standard_normal(d)
+    o, s = oracle.scan_ex(q, k, v, xg, xb, h_k=h_k, h_v=h_v, state_in=S0, raw_gates=True, output_norm=True,
+                          norm_weight=w)
+    st = S0
+    for t in range(2):
+        ot, st = oracle.decode_step_ex(q[t:t + 1], k[t:t + 1], v[t:t + 1], xg[t:t + 1], xb[t:t + 1], st, h_k=h_k,
+                                       h_v=h_v, raw_gates=True, output_norm=True, norm_weight=w)
+        assert np.allclose(o[t], ot[0], rtol=1e-13, atol=1e-14)
+    assert np.allclose(s, st, rtol=1e-13, atol=1e-14)
+    o0, s0 = oracle.scan(q, k, v, xg, xb, h_k=h_k, h_v=h_v, state_in=S0)
+    o1, s1 = oracle.scan_ex(q, k, v, xg, xb, h_k=h_k, h_v=h_v, state_in=S0)
+    assert np.array_equal(o0, o1) and np.array_equal(s0, s1)
