@@ -358,3 +358,27 @@ def test_calibration_library_loads_and_rejects_bad_arguments():
     C.gdn_calib_rmw_f32.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
     assert C.gdn_calib_mfma_f16(0, 8, None, None) != 0        # no iterations, no sink
     assert C.gdn_calib_rmw_f32(None, 1024, 8, None) != 0      # no buffer
+
+
+def test_header_is_plain_c(tmp_path):
+    """include/gdn.h is a C header: it compiles as strict C99 (and as C++) with every
+    declaration, the flag enum included."""
+    import shutil
+    import subprocess
+    src = tmp_path / "use_gdn.c"
+    src.write_text('#include "gdn.h"\n'
+                   "int main(void) {\n"
+                   "    gdn_fuse_flag f = GDN_FUSE_GATE_ACTIVATIONS;\n"
+                   "    gdn_desc d;\n"
+                   "    (void)f; (void)d;\n"
+                   "    (void)gdn_decode_step_ex; (void)gdn_prefill_direct_ex; (void)gdn_prefill;\n"
+                   "    return 0;\n"
+                   "}\n")
+    inc = os.path.join(ROOT, "include")
+    for cc, std in (("gcc", "-std=c99"), ("g++", "-std=c++17")):
+        if shutil.which(cc) is None:
+            pytest.skip("%s not available" % cc)
+        lang = ["-x", "c++"] if cc == "g++" else []
+        r = subprocess.run([cc, std, "-Wall", "-Wextra", "-pedantic", "-Werror", "-fsyntax-only", "-I", inc] + lang +
+                           [str(src)], capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
