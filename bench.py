@@ -247,6 +247,63 @@ def two_level(L, gdn, inputs, to_dev, torch, np, dev):
         del q, k, v, g, b, s_in, out, s_out
 
 
+def decode_sweep(L, gdn, inputs, to_dev, torch, np, dev):
+    """gdn_decode_step by batch size: N sequences x 32 v-heads (16 k-heads), d = 128, bf16 in
+    and out, fp32 state, 64 consecutive steps per N (fresh inputs each step); plain and with
+    both per-token folds (gdn_decode_step_ex).  One JSON line per N."""
+    h_k, h_v, d, steps = 16, 32, 128, 64
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    fuse = gdn.GDN_FUSE_GATE_ACTIVATIONS | gdn.GDN_FUSE_OUTPUT_NORM
+    for N in (1, 4, 16, 64, 256, 1024):
+        y = inputs.decode_inputs(seed=7, num_seqs=N, steps=steps, h_k=h_k, h_v=h_v, d=d, io_dtype=inputs.BF16)
+        q, k, v, g, b, xg, xb = (to_dev(y[n]) for n in ("q", "k", "v", "g", "beta", "x_g", "x_beta"))
+        state = to_dev(y["state"])
+        out = torch.empty((N, h_v, d), dtype=torch.bfloat16, device=dev)
+        w = torch.ones(d, dtype=torch.float32, device=dev)
+        desc = gdn.make_desc(num_seqs=N, total_tokens=N, h_k=h_k, h_v=h_v, d=d, io_dtype=gdn.GDN_BF16,
+                             out_dtype=gdn.GDN_BF16)
+        dref = ctypes.byref(desc)
+        qs, ks, vs_, gs = q.stride(0) * 2, k.stride(0) * 2, v.stride(0) * 2, g.stride(0) * 4
+        P = [t.data_ptr() for t in (q, k, v, g, b, xg, xb)]
+
+        def plain(t):
+            st = L.gdn_decode_step(dref, P[0] + t * qs, P[1] + t * ks, P[2] + t * vs_, P[3] + t * gs, P[4] + t * gs,
+                                   state.data_ptr(), out.data_ptr(), sp)
+            if st:
+                raise gdn.GdnError(st, gdn.last_error())
+
+        def fused(t):
+            st = L.gdn_decode_step_ex(dref, P[0] + t * qs, P[1] + t * ks, P[2] + t * vs_, P[5] + t * gs,
+                                      P[6] + t * gs, state.data_ptr(), out.data_ptr(), fuse, w.data_ptr(), 1e-6, sp)
+            if st:
+                raise gdn.GdnError(st, gdn.last_error())
+
+        res = {}
+        for name, fn in (("plain", plain), ("fused", fused)):
+            for t in range(5):
+                fn(t)
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(3):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for t in range(steps):
+                    fn(t)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e3 / steps)
+            res[name] = float(np.median(ts))
+        nbytes = algorithmic_decode(N, h_v, h_k, d)
+        print(json.dumps({"decode_sweep": {
+            "num_seqs": N, "h_v": h_v, "h_k": h_k, "d": d, "us_per_step": round(res["plain"], 2),
+            "us_per_step_fused": round(res["fused"], 2), "tok_per_s": round(N * 1e6 / res["plain"]),
+            "state_mib": round(N * h_v * d * d * 4 / 2 ** 20, 1),
+            "gb_per_s": round(nbytes / (res["plain"] * 1e-6) / 1e9, 1),
+            "hbm_frac": round(nbytes / (res["plain"] * 1e-6) / (PEAK_HBM_GBS * 1e9), 4)}}), flush=True)
+        del q, k, v, g, b, xg, xb, state, out, w
+
+
 def prefill_configs(L, gdn, inputs, to_dev, torch, np, dev, with_cpu=True):
     """Every prefill workload (single-head fp32 T=256, 4K, 128K with an initial state, 16 packed
     sequences of drawn lengths) through gdn_prefill: time per call, tok/s, the per-kernel split
@@ -395,6 +452,9 @@ def main():
     ap.add_argument("--configs", action="store_true",
                     help="instead of the benchmark line: every prefill workload (fp32 single head, 4K, 128K, "
                          "16 packed sequences) with tok/s and roofline fractions (one JSON line each)")
+    ap.add_argument("--decode-sweep", action="store_true",
+                    help="instead of the benchmark line: the decode step by batch size, 1 to 1024 sequences "
+                         "of 32 v-heads, plain and fused (one JSON line per size)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on exactly one GPU; --gpus %d is not supported "
@@ -427,6 +487,9 @@ def main():
         return
     if args.configs:
         prefill_configs(L, gdn, inputs, to_dev, torch, np, dev, with_cpu=not args.no_cpu_baseline)
+        return
+    if args.decode_sweep:
+        decode_sweep(L, gdn, inputs, to_dev, torch, np, dev)
         return
 
     # ---------------- prefill ----------------
