@@ -249,8 +249,8 @@ def two_level(L, gdn, inputs, to_dev, torch, np, dev):
 
 def decode_sweep(L, gdn, inputs, to_dev, torch, np, dev):
     """gdn_decode_step by batch size: N sequences x 32 v-heads (16 k-heads), d = 128, bf16 in
-    and out, fp32 state, 64 consecutive steps per N (fresh inputs each step); plain and with
-    both per-token folds (gdn_decode_step_ex).  One JSON line per N."""
+    and out, fp32 state, 64 consecutive steps per N (fresh inputs each step); plain, replayed
+    from a HIP graph, and with both per-token folds (gdn_decode_step_ex).  One JSON line per N."""
     h_k, h_v, d, steps = 16, 32, 128, 64
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
@@ -294,9 +294,31 @@ def decode_sweep(L, gdn, inputs, to_dev, torch, np, dev):
                 torch.cuda.synchronize()
                 ts.append(e0.elapsed_time(e1) * 1e3 / steps)
             res[name] = float(np.median(ts))
+        # the same 64 plain steps captured once in a HIP graph and replayed (launch cost removed)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            cap = torch.cuda.current_stream().cuda_stream
+            for t in range(steps):
+                st = L.gdn_decode_step(dref, P[0] + t * qs, P[1] + t * ks, P[2] + t * vs_, P[3] + t * gs,
+                                       P[4] + t * gs, state.data_ptr(), out.data_ptr(), cap)
+                if st:
+                    raise gdn.GdnError(st, gdn.last_error())
+        graph.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            graph.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3 / steps)
+        res["graph"] = float(np.median(ts))
+        del graph
         nbytes = algorithmic_decode(N, h_v, h_k, d)
         print(json.dumps({"decode_sweep": {
             "num_seqs": N, "h_v": h_v, "h_k": h_k, "d": d, "us_per_step": round(res["plain"], 2),
+            "us_per_step_hip_graph": round(res["graph"], 2),
             "us_per_step_fused": round(res["fused"], 2), "tok_per_s": round(N * 1e6 / res["plain"]),
             "state_mib": round(N * h_v * d * d * 4 / 2 ** 20, 1),
             "gb_per_s": round(nbytes / (res["plain"] * 1e-6) / 1e9, 1),
