@@ -218,10 +218,10 @@ __device__ __forceinline__ void decode_units(const void* __restrict__ q, const v
                                              const float* __restrict__ beta, float* __restrict__ state,
                                              const int32_t* __restrict__ slots, int num_slots, void* __restrict__ out,
                                              int units, int h_k, int h_v, int l2norm, float scale, bool raw_gates,
-                                             const float* __restrict__ norm_w, float eps, float* ub, float* nsum) {
-    const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
-    const int stride = gridDim.x, last = units - 1;
-    int u = blockIdx.x;
+                                             const float* __restrict__ norm_w, float eps, float* ub, float* nsum,
+                                             int wave, int u, int stride) {
+    const int lane = threadIdx.x % WAVE;
+    const int last = units - 1;
     if (u > last) return;
     DecodeIn<D> A, B;
     decode_load<D, IN_BF16>(A, state, slots, num_slots, q, k, v, g, beta, norm_w, u, h_k, h_v, wave, lane);
@@ -241,6 +241,11 @@ __device__ __forceinline__ void decode_units(const void* __restrict__ q, const v
 }
 
 // fuse: bit 0 raw gate inputs, bit 1 output norm (weights norm_w, NULL for ones).
+// A workgroup of D/32 waves owns whole units (wave w: rows 32w..32w+31).  With
+// one-wave workgroups (no output norm: the rows of a unit are independent) the
+// D/32 row groups of a unit are D/32 workgroups, so a few units still spread
+// over many compute units: workgroup b takes row group b % (D/32) of units
+// b / (D/32), b / (D/32) + gridDim.x / (D/32), ...
 template <int D, bool IN_BF16, bool OUT_BF16>
 __global__ __launch_bounds__(2 * D) void decode_step_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
@@ -249,14 +254,20 @@ __global__ __launch_bounds__(2 * D) void decode_step_kernel(
     int l2norm, float scale, int fuse, const float* __restrict__ norm_w, float norm_eps) {
     __shared__ __align__(16) float ubuf[(D / 32) * 32];
     __shared__ __align__(16) float nsum[2 * (D / 32)];
-    float* ub = ubuf + (threadIdx.x / WAVE) * 32;
+    constexpr int NW = D / 32;
+    const bool split = blockDim.x == WAVE;  // one-wave workgroups (launched only without the norm)
+    const int wave = split ? (int)(blockIdx.x % NW) : (int)(threadIdx.x / WAVE);
+    const int u0 = split ? (int)(blockIdx.x / NW) : (int)blockIdx.x;
+    const int stride = split ? (int)(gridDim.x / NW) : (int)gridDim.x;
+    float* ub = ubuf + wave * 32;
     const bool raw_gates = (fuse & 1) != 0;
     if (fuse & 2)
         decode_units<D, IN_BF16, OUT_BF16, true>(q, k, v, g, beta, state, slots, num_slots, out, units, h_k, h_v,
-                                                 l2norm, scale, raw_gates, norm_w, norm_eps, ub, nsum);
+                                                 l2norm, scale, raw_gates, norm_w, norm_eps, ub, nsum, wave, u0,
+                                                 stride);
     else
         decode_units<D, IN_BF16, OUT_BF16, false>(q, k, v, g, beta, state, slots, num_slots, out, units, h_k, h_v,
-                                                  l2norm, scale, raw_gates, nullptr, 0.f, ub, nsum);
+                                                  l2norm, scale, raw_gates, nullptr, 0.f, ub, nsum, wave, u0, stride);
 }
 
 // ---- direct scan: the token recurrence with the state in registers ---------------------
@@ -363,6 +374,8 @@ __global__ __launch_bounds__(2 * D) void direct_scan_kernel(
                                                  l2norm, scale, raw_gates, nullptr, 0.f, ub, nsum);
 }
 
+int compute_units();  // of the current device (prefill.hip)
+
 template <int D, bool IB, bool OB>
 static hipError_t launch_direct_t(const void* q, const void* k, const void* v, const float* g, const float* beta,
                                   const int32_t* cu, const float* s_in, float* s_out, void* out, int units, int T,
@@ -393,6 +406,15 @@ static hipError_t launch_decode_t(const void* q, const void* k, const void* v, c
                                   const float* beta, float* state, const int32_t* slots, int num_slots,
                                   void* out, int units, int h_k, int h_v, int l2norm, float scale, int fuse,
                                   const float* norm_w, float norm_eps, int grid, hipStream_t stream) {
+    // Too few units to fill the chip (and no output norm): one-wave workgroups, one per
+    // row group of a unit, so each unit's rows spread over D/32 compute units.
+    const bool split = !(fuse & 2) && (long long)units * (D / 32) <= 2LL * compute_units();
+    if (split) {
+        hipLaunchKernelGGL((decode_step_kernel<D, IB, OB>), dim3(units * (D / 32)), dim3(WAVE), 0, stream, q, k, v,
+                           g, beta, state, slots, num_slots, out, units, h_k, h_v, l2norm, scale, fuse, norm_w,
+                           norm_eps);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL((decode_step_kernel<D, IB, OB>), dim3(grid), dim3(2 * D), 0, stream, q, k, v,
                        g, beta, state, slots, num_slots, out, units, h_k, h_v, l2norm, scale, fuse, norm_w,
                        norm_eps);

@@ -1084,7 +1084,7 @@ hipError_t launch_plan(const int32_t* cu, int N, int T, int max_slots, void* inf
 }
 
 // Compute units of the current device (cached per device).
-static int compute_units() {
+int compute_units() {
     static int cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
