@@ -58,3 +58,33 @@ def gather_units(inp, units, h_k, h_v):
                beta=cat(bs)[:, None], cu=np.concatenate([[0], np.cumsum(lens)]).astype(np.int32),
                state_in=np.stack(s0)[:, None] if s0 else None)
     return sub
+
+
+def _slices(n, step):
+    for i in range(0, n, step):
+        yield slice(i, min(n, i + step))
+
+
+def normwise_blocks(t, r, step=4096):
+    """normwise(host(t), r) over the leading axis in slices, so a large device
+    tensor is never widened to float64 on the host in one piece."""
+    rmax = max(float(np.abs(r).max()), 1e-300)
+    err = 0.0
+    for s in _slices(r.shape[0], step):
+        err = max(err, float(np.abs(host(t[s]) - r[s]).max()))
+    return err / rmax
+
+
+def check_bf16_out_blocks(t, r, tol, step=4096):
+    """check_bf16_out over the leading axis in slices, with the bound taken
+    from the whole reference tensor."""
+    rmax = float(np.abs(r).max())
+    bad_total, worst = 0, 0.0
+    for s in _slices(r.shape[0], step):
+        x, rs = host(t[s]), r[s]
+        bound = tol * rmax + bf16_half_ulp(rs)
+        excess = np.abs(x - rs) - bound
+        bad_total += int((excess > 0).sum())
+        worst = max(worst, float(excess.max()))
+    assert bad_total == 0, "bf16 output outside tol*max|r| + ulp/2 at %d elements (worst excess %.3g)" % (
+        bad_total, worst)

@@ -10,7 +10,7 @@ import torch
 
 from linear_attention_recurrence_rule_amd import gdn, inputs
 from oracle import oracle
-from tests.gpu_helpers import check_bf16_out, dev, host, normwise
+from tests.gpu_helpers import check_bf16_out, check_bf16_out_blocks, dev, host, normwise, normwise_blocks
 
 pytestmark = pytest.mark.gpu
 
@@ -108,35 +108,39 @@ def test_decode_no_norm_and_scale():
     assert normwise(host(state), rs) <= 1e-5
 
 
-def test_decode_full_workload_sampled():
-    """64 sequences x 32 v-heads x d=128, 512 steps, bf16 in/out; 40 sampled
-    (sequence, v-head) units are followed by the oracle over all 512 steps."""
+def test_decode_full_workload():
+    """64 sequences x 32 v-heads x d=128, 512 steps: every output of every step and
+    the whole final state against the oracle, for fp32 and bf16 outputs.  A unit's
+    512 decode steps are the token scan of one 512-token sequence, so the oracle
+    runs them as 64 packed 512-token sequences."""
     w = inputs.WORKLOADS["decode_n64_hv32_hk16_d128_512steps"]
     x = inputs.workload_inputs(w)
     N, h_k, h_v, d, steps = w.num_seqs, w.h_k, w.h_v, w.d, w.steps
+
+    def packed(a):  # [steps, N, heads, ...] -> [N * steps, heads, ...]
+        a = np.swapaxes(a, 0, 1)
+        return np.ascontiguousarray(a.reshape((N * steps,) + a.shape[2:]))
+
+    cu = (np.arange(N + 1) * steps).astype(np.int32)
+    ro, rs = oracle.scan(packed(x["q"]), packed(x["k"]), packed(x["v"]), packed(x["g"]), packed(x["beta"]),
+                         h_k=h_k, h_v=h_v, state_in=x["state"], cu_seqlens=cu, threads=16)
+    ro = np.swapaxes(ro.reshape(N, steps, h_v, d), 0, 1)  # back to [steps, N, h_v, d]
     q, k, v, g, b = (dev(x[n]) for n in ("q", "k", "v", "g", "beta"))
-    state = dev(x["state"])
-    outs = torch.empty((steps, N, h_v, d), dtype=torch.bfloat16, device=state.device)
-    for t in range(steps):
-        gdn.decode_step(q[t], k[t], v[t], g[t], b[t], state, out=outs[t])
-    torch.cuda.synchronize()
-    rng = np.random.default_rng(0)
-    units = [(int(n), int(h)) for n, h in zip(rng.integers(0, N, 40), rng.integers(0, h_v, 40))]
-    r = h_v // h_k
-    # a unit's 512 decode steps are the token scan of one 512-token sequence
-    pq = np.concatenate([x["q"][:, n, h // r] for n, h in units])[:, None]
-    pk = np.concatenate([x["k"][:, n, h // r] for n, h in units])[:, None]
-    pv = np.concatenate([x["v"][:, n, h] for n, h in units])[:, None]
-    pg = np.concatenate([x["g"][:, n, h] for n, h in units])[:, None]
-    pb = np.concatenate([x["beta"][:, n, h] for n, h in units])[:, None]
-    s0 = np.stack([x["state"][n, h] for n, h in units])[:, None]
-    cu = (np.arange(len(units) + 1) * steps).astype(np.int32)
-    ro, rs = oracle.scan(pq, pk, pv, pg, pb, h_k=1, h_v=1, state_in=s0, cu_seqlens=cu)
-    st = host(state)
-    o = host(outs)
-    for i, (n, h) in enumerate(units):
-        assert normwise(st[n, h], rs[i, 0]) <= 2e-3
-        check_bf16_out(o[:, n, h], ro[i * steps:(i + 1) * steps, 0], 2e-3)
+    for out_dt, tdt in ((inputs.F32, torch.float32), (inputs.BF16, torch.bfloat16)):
+        state = dev(x["state"])
+        outs = torch.empty((steps, N, h_v, d), dtype=tdt, device=state.device)
+        for t in range(steps):
+            gdn.decode_step(q[t], k[t], v[t], g[t], b[t], state, out=outs[t], out_dtype=out_dt)
+        torch.cuda.synchronize()
+        es = normwise(host(state), rs)
+        if out_dt == inputs.F32:
+            eo = normwise_blocks(outs, ro, step=64)
+            print("decode 512 steps fp32-out: out %.3g state %.3g" % (eo, es))
+            assert eo <= 2e-3
+        else:
+            check_bf16_out_blocks(outs, ro, 2e-3, step=64)
+        assert es <= 2e-3
+        del state, outs
 
 
 def test_decode_deterministic_and_in_place():

@@ -15,7 +15,7 @@ import torch
 
 from linear_attention_recurrence_rule_amd import gdn, inputs
 from oracle import oracle
-from tests.gpu_helpers import check_bf16_out, dev, gather_units, host, normwise
+from tests.gpu_helpers import check_bf16_out, check_bf16_out_blocks, dev, gather_units, host, normwise, normwise_blocks
 
 pytestmark = pytest.mark.gpu
 
@@ -266,56 +266,37 @@ def test_prefill_4k_long_memory():
     assert eo <= 2e-3 and es <= 2e-3
 
 
-def test_prefill_varlen_workload_sampled():
-    """16 packed sequences, lengths drawn in [256, 16384]; 6 sampled (sequence, v-head)
-    units are recomputed by the oracle, every output of those units is compared."""
+def test_prefill_varlen_workload_full():
+    """16 packed sequences, lengths drawn in [256, 16384]: every (sequence, v-head)
+    unit, every output and every final state against the oracle."""
     w = inputs.WORKLOADS["varlen_n16_hv32_hk16_d128"]
     x = inputs.workload_inputs(w)
+    ro, rs = run_oracle(x, threads=16)
     out, st = run_gpu(x, inputs.F32)
-    rng = np.random.default_rng(1)
-    units = [(int(n), int(h)) for n, h in zip(rng.integers(0, 16, 6), rng.integers(0, 32, 6))]
-    sub = gather_units(x, units, w.h_k, w.h_v)
-    ro, rs = oracle.scan(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], h_k=1, h_v=1,
-                         state_in=sub["state_in"], cu_seqlens=sub["cu"], threads=16)
-    o, s = host(out), host(st)
-    cu = x["cu_seqlens"]
-    for i, (n, h) in enumerate(units):
-        go = o[cu[n]:cu[n + 1], h]
-        r = ro[sub["cu"][i]:sub["cu"][i + 1], 0]
-        assert normwise(go, r) <= 2e-3, (n, h, normwise(go, r))
-        assert normwise(s[n, h], rs[i, 0]) <= 2e-3
-    # bf16 outputs, as the timed configuration writes them
+    eo, es = normwise_blocks(out, ro), normwise(host(st), rs)
+    print("varlen %d tokens, fp32-out: out %.3g state %.3g" % (w.total_tokens or x["total_tokens"], eo, es))
+    assert eo <= 2e-3 and es <= 2e-3
     del out, st
+    # bf16 outputs, as the timed configuration writes them
     out_b, st_b = run_gpu(x, inputs.BF16)
-    o, s = host(out_b), host(st_b)
-    for i, (n, h) in enumerate(units):
-        check_bf16_out(o[cu[n]:cu[n + 1], h], ro[sub["cu"][i]:sub["cu"][i + 1], 0], 2e-3)
-        assert normwise(s[n, h], rs[i, 0]) <= 2e-3
+    check_bf16_out_blocks(out_b, ro, 2e-3)
+    assert normwise(host(st_b), rs) <= 2e-3
 
 
-def test_prefill_128k_workload_sampled():
-    """T=131072, 32 v-heads, d=128, initial state N(0, 0.02): 2 sampled v-heads in full."""
+def test_prefill_128k_workload_full():
+    """T=131072, 32 v-heads over 16 q/k heads, d=128, initial state N(0, 0.02):
+    every output of every v-head and the whole final state against the oracle."""
     w = inputs.WORKLOADS["prefill_t131072_hv32_hk16_d128"]
     x = inputs.workload_inputs(w)
+    ro, rs = run_oracle(x, threads=16)
     out, st = run_gpu(x, inputs.F32)
-    units = [(0, 5), (0, 30)]
-    sub = gather_units(x, units, w.h_k, w.h_v)
-    ro, rs = oracle.scan(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], h_k=1, h_v=1,
-                         state_in=sub["state_in"], cu_seqlens=sub["cu"], threads=16)
-    o, s = host(out), host(st)
-    T = w.total_tokens
-    for i, (n, h) in enumerate(units):
-        eo = normwise(o[:, h], ro[i * T:(i + 1) * T, 0])
-        es = normwise(s[0, h], rs[i, 0])
-        print("128k head %d: out %.3g state %.3g" % (h, eo, es))
-        assert eo <= 2e-3 and es <= 2e-3
-    # bf16 outputs, as the timed configuration writes them
+    eo, es = normwise_blocks(out, ro), normwise(host(st), rs)
+    print("128k fp32-out: out %.3g state %.3g" % (eo, es))
+    assert eo <= 2e-3 and es <= 2e-3
     del out, st
     out_b, st_b = run_gpu(x, inputs.BF16)
-    o, s = host(out_b), host(st_b)
-    for i, (n, h) in enumerate(units):
-        check_bf16_out(o[:, h], ro[i * T:(i + 1) * T, 0], 2e-3)
-        assert normwise(s[0, h], rs[i, 0]) <= 2e-3
+    check_bf16_out_blocks(out_b, ro, 2e-3)
+    assert normwise(host(st_b), rs) <= 2e-3
 
 
 # ---- row slices of the state ------------------------------------------------------------------
