@@ -781,6 +781,516 @@ __global__ __launch_bounds__(PREP_THREADS, (prep_min_waves<D, OP>())) void chunk
     }
 }
 
+// ---- block-form work for bf16 inputs: a k-head's v-heads in pairs -------------------------
+// One workgroup per compute unit (8 waves) takes a run of items (block slot,
+// k-head, pair of the k-head's v-heads) and computes both v-heads' records
+// together, so that every phase has work for all eight waves and the raw
+// Gram products K K^T and Q K^T are formed once per item (only the decay
+// masks, beta and the norm factors differ between the two v-heads).  Six
+// LDS-only barriers per item, against eight per v-head in chunk_prep_kernel.
+//   P1  q, k scaled per token by a power of two (exact) and norms; v to LDS.
+//   P2a waves 0..NH-1: cumulative log-decay G and the per-token exponent terms
+//       of their v-head; waves 2..5: the raw off-diagonal K K^T and the Q K^T
+//       tiles; waves 6, 7: the raw diagonal K K^T tiles; waves 0, 1 also
+//       write the key record.
+//   P2b decay masks: A_ij^T tiles (i > j blocks), P fragments, and the
+//       diagonal blocks N_bb of A, which waves 6, 7 invert by forward
+//       substitution on the vector unit (one lane per column of a block).
+//   P4  the six blocks of X = (I + A)^{-1} below the diagonal (fp32 matrix
+//       cores), written as T = X diag(beta) fragments.
+//   P5  Ut = T V and Ot = P Ut; -W = -T diag(gamma c) K.
+//   P6  Qt = diag(gamma c_q) Q - P W.
+// Decay ratios are formed as exp2(r_i - c_j) with r_i = G_i log2(e) +
+// log2(beta_i c_i) and c_j = G_j log2(e) - log2(c_j); only entries with
+// i >= j are kept, so the exponent r_i - c_j carries exp(G_i - G_j) <= 1.
+constexpr float LOG2E_F = 1.4426950408889634f;
+
+template <int D, int NH>
+struct PairLds {
+    static constexpr int LK = D + 8;  // row stride of [token][d] fp16 tiles
+    static constexpr int XS = 20;     // row stride of 16 x 16 fp32 blocks
+    _Float16 k[CHUNK * LK];           // keys scaled per token by a power of two (exact)
+    _Float16 q[CHUNK * LK];           // queries, likewise
+    _Float16 v[NH][CHUNK * LK];       // values
+    union {
+        struct {
+            float a[NH][6][WAVE * 4];   // A_ij^T (block i > j) in accumulator layout
+            float nb[NH][4][16 * XS];   // diagonal blocks N_bb of A, row-major
+            float xd[NH][4][16 * XS];   // X_bb = (I + N_bb)^{-1}, column-major [col][row]
+        } s;
+        _Float16 w[NH][CHUNK * LK];     // -W [token][d]
+    } aw;
+    _Float16 t[NH][CHUNK * CHUNK];    // T = X diag(beta), fragment-major
+    _Float16 p[NH][CHUNK * CHUNK];    // P, fragment-major
+    float ra[NH][CHUNK], rq[NH][CHUNK], cb[NH][CHUNK];  // exponent terms (above)
+    float gck[NH][CHUNK], gcq[NH][CHUNK], bt[NH][CHUNK];
+    float ck[CHUNK], cq[CHUNK];
+};
+
+template <int D, int NH>
+constexpr size_t pair_lds_bytes() { return sizeof(PairLds<D, NH>); }
+
+// Slot of the off-diagonal block (i, j), i > j: (1,0) (2,0) (2,1) (3,0) (3,1) (3,2).
+__device__ __forceinline__ constexpr int aslot(int i, int j) { return i * (i - 1) / 2 + j; }
+
+template <int D, int NH>
+__global__ __launch_bounds__(PREP_THREADS, 1) void chunk_prep_pair_kernel(
+    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, const SeqInfo* __restrict__ info,
+    const int32_t* __restrict__ slot_seq, int T, int h_k, int h_v, int l2norm, float scale,
+    char* __restrict__ recs, char* __restrict__ krecs, int slots, int items_per_wg) {
+    using OP = _Float16;
+    using RC = Rec<D, OP>;
+    using LT = PairLds<D, NH>;
+    constexpr int LK = LT::LK, XS = LT::XS;
+    constexpr int PER_TOK = D / 8;                       // threads per token row, 8 elements each
+    constexpr int NIT = CHUNK * PER_TOK / PREP_THREADS;  // row pieces per thread
+    constexpr int KF = (D / 16) * 2;                     // K^T fragments of the key record
+    constexpr int NKB = D / 32;                          // contraction blocks over d
+    static_assert(NIT >= 1, "row pieces");
+    extern __shared__ __align__(16) char smem_raw[];
+    LT& L = *reinterpret_cast<LT*>(smem_raw);
+    const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
+    const int li = lane & 15, lq = lane >> 4;
+    const int ratio = h_v / h_k, pairs = ratio / NH;
+    const int per_slot = h_k * pairs;
+    const int items = slots * per_slot;
+    const int i0 = blockIdx.x * items_per_wg, i1 = min(items, i0 + items_per_wg);
+    if (i0 >= i1) return;
+    auto slot_range = [&](int slot, int& tok0, int& nt) {
+        if (slot_seq) {
+            const int n = slot_seq[slot];
+            if (n < 0) { tok0 = 0; nt = 0; return false; }
+            const SeqInfo si = info[n];
+            const int j = slot - si.slot_base;
+            tok0 = si.begin + j * CHUNK;
+            nt = min(CHUNK, si.len - j * CHUNK);
+        } else {
+            tok0 = slot * CHUNK;
+            nt = min(CHUNK, T - tok0);
+        }
+        return true;
+    };
+    // the next item's raw inputs, in registers (token indices clamped into [0, T))
+    uint4 rq_[NIT], rk_[NIT], rv_[NH][NIT];
+    float rg = 0.f, rb = 0.f;  // waves 0..NH-1: g and beta of token `lane`, v-head h0 + wave
+    auto load_in = [&](int tok0, int hk, int h0) {
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int idx = tid + PREP_THREADS * it, t = idx / PER_TOK, pc = idx % PER_TOK;
+            const size_t tt = (size_t)min(tok0 + t, T - 1);
+            rq_[it] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(q) + (tt * h_k + hk) * D + 8 * pc);
+            rk_[it] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(k) + (tt * h_k + hk) * D + 8 * pc);
+#pragma unroll
+            for (int j = 0; j < NH; ++j)
+                rv_[j][it] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(v) +
+                                                             (tt * h_v + h0 + j) * D + 8 * pc);
+        }
+        if (wave < NH) {
+            const size_t tg = (size_t)min(tok0 + lane, T - 1) * h_v + h0 + wave;
+            rg = g[tg];
+            rb = beta[tg];
+        }
+    };
+    auto heads_of = [&](int item, int& hk, int& pr) {
+        hk = (item / pairs) % h_k;
+        pr = item % pairs;
+        return hk * ratio + pr * NH;
+    };
+
+    int tok0, nt;
+    bool live = slot_range(i0 / per_slot, tok0, nt);
+    {
+        int hk, pr;
+        const int h0 = heads_of(i0, hk, pr);
+        load_in(tok0, hk, h0);
+    }
+    for (int item = i0; item < i1; ++item) {
+        const int slot = item / per_slot;
+        int hk, pr;
+        const int h0 = heads_of(item, hk, pr);
+        const int cnt = nt;
+        const bool clive = live;
+        const bool more = item + 1 < i1;
+        int ntok0 = 0, nnt = 0;
+        const bool nlive = more && slot_range((item + 1) / per_slot, ntok0, nnt);
+        int nhk = 0, npr = 0;
+        const int nh0 = more ? heads_of(item + 1, nhk, npr) : 0;
+        if (!clive) {  // an unused slot of packed sequences: nothing to write
+            if (more) load_in(ntok0, nhk, nh0);
+            tok0 = ntok0; nt = nnt; live = nlive;
+            continue;
+        }
+
+        // ---- P1: q, k scaled per token by a power of two, norms; q, k, v to LDS ----------
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int idx = tid + PREP_THREADS * it, t = idx / PER_TOK, pc = idx % PER_TOK;
+            const bool tl = t < cnt;
+            float kx[8], qx[8];
+            unpack8<true>(&rk_[it], kx);
+            unpack8<true>(&rq_[it], qx);
+            float mk = 0.f, mq = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                if (!tl) { kx[e] = 0.f; qx[e] = 0.f; }
+                mk = fmaxf(mk, fabsf(kx[e]));
+                mq = fmaxf(mq, fabsf(qx[e]));
+            }
+            mk = group_max<PER_TOK>(mk);  // the PER_TOK lanes of a token are adjacent
+            mq = group_max<PER_TOK>(mq);
+            int ek = 0, eq = 0;
+            frexpf(mk, &ek);
+            frexpf(mq, &eq);
+            float ssk = 0.f, ssq = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                kx[e] = ldexpf(kx[e], -ek);  // exact: a bf16 value fits fp16 after the scaling
+                qx[e] = ldexpf(qx[e], -eq);
+                ssk = fmaf(kx[e], kx[e], ssk);
+                ssq = fmaf(qx[e], qx[e], ssq);
+            }
+            ssk = group_sum<PER_TOK>(ssk);
+            ssq = group_sum<PER_TOK>(ssq);
+            store8<OP>(L.k + t * LK + 8 * pc, kx);
+            store8<OP>(L.q + t * LK + 8 * pc, qx);
+            if (pc == 0) {
+                L.ck[t] = tl ? norm_factor(ssk, ek, l2norm, 1.0f) : 0.f;
+                L.cq[t] = tl ? norm_factor(ssq, eq, l2norm, scale) : 0.f;
+            }
+#pragma unroll
+            for (int j = 0; j < NH; ++j) {
+                float vx[8];
+                unpack8<true>(&rv_[j][it], vx);
+                if (!tl) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) vx[e] = 0.f;
+                }
+                store8<OP>(L.v[j] + t * LK + 8 * pc, vx);
+            }
+        }
+        const float cg = rg, cbeta = rb;
+        if (more) load_in(ntok0, nhk, nh0);
+        lds_barrier();  // B1
+
+        // ---- P2a ------------------------------------------------------------------------------
+        f4_t acc[4];
+        if (wave < 2) {
+            if (wave < NH) {
+                const int hh = wave;
+                const bool tl = lane < cnt;
+                const float gl = wave_inclusive_sum(tl ? cg : 0.f) * LOG2E_F;
+                const float ckv = L.ck[lane], cqv = L.cq[lane];
+                const float bv = tl ? cbeta : 0.f;
+                L.ra[hh][lane] = gl + __builtin_amdgcn_logf(bv * ckv);
+                L.rq[hh][lane] = gl + __builtin_amdgcn_logf(cqv);
+                L.cb[hh][lane] = gl - __builtin_amdgcn_logf(ckv);
+                L.bt[hh][lane] = bv;
+                const float gam = __builtin_amdgcn_exp2f(gl);
+                L.gck[hh][lane] = gam * ckv;
+                L.gcq[hh][lane] = gam * cqv;
+                const float gln = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gl), max(cnt - 1, 0)));
+                char* rec = recs + ((size_t)slot * h_v + h0 + hh) * RC::BYTES;
+                reinterpret_cast<float*>(rec + RC::S)[lane] = tl ? __builtin_amdgcn_exp2f(gln - gl) * ckv : 0.f;
+                if (lane == 0) reinterpret_cast<float*>(rec + RC::M)[0] = __builtin_amdgcn_exp2f(gln);
+            }
+            if (pr == 0) {  // the k-head's key record, once per k-head
+                OP* krec = reinterpret_cast<OP*>(krecs + ((size_t)slot * h_k + hk) * KeyRec<D, OP>::BYTES);
+                for (int f = wave; f < KF; f += 2)
+                    frag_store<OP>(krec, f, lane, frag_colmajor<OP>(L.k, LK, f / 2, f % 2, lane));
+            }
+        } else if (wave < 6) {
+            // tiles u = wave - 2 + 4m: u < 6 the off-diagonal K K^T block of slot u, computed
+            // as K_j K_i^T so that lane (j', q) holds A_ij^T[4q + r][j']; u >= 6 the tile
+            // K_nb Q_mb^T, which is this lane's half of P's fragment (mb, nb / 2).
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int u = wave - 2 + 4 * m;
+                acc[m] = f4_t{0.f, 0.f, 0.f, 0.f};
+                if (u < 6) {
+                    const int bi = u >= 3 ? 3 : (u >= 1 ? 2 : 1), bj = u - bi * (bi - 1) / 2;
+#pragma unroll
+                    for (int kb = 0; kb < NKB; ++kb)
+                        mma(acc[m], frag_row8<OP>(L.k, LK, bj, kb, lane), frag_row8<OP>(L.k, LK, bi, kb, lane));
+                } else {
+                    const int tl = u - 6;
+                    const int mb = (tl >= 6) ? 3 : (tl >= 3) ? 2 : (tl >= 1) ? 1 : 0, nb = tl - mb * (mb + 1) / 2;
+#pragma unroll
+                    for (int kb = 0; kb < NKB; ++kb)
+                        mma(acc[m], frag_row8<OP>(L.k, LK, nb, kb, lane), frag_row8<OP>(L.q, LK, mb, kb, lane));
+                }
+            }
+        } else if (wave - 6 < NH) {
+            // the raw diagonal blocks K_b K_b^T (symmetric): lane (j', q) holds (K K^T)[16b + 4q + r][16b + j']
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                acc[b] = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+                    mma(acc[b], frag_row8<OP>(L.k, LK, b, kb, lane), frag_row8<OP>(L.k, LK, b, kb, lane));
+            }
+        }
+        lds_barrier();  // B2
+
+        // ---- P2b ------------------------------------------------------------------------------
+        if (wave < 2) {
+            // zero halves: P above the diagonal (6 tiles), T above the diagonal (6 halves)
+            for (int hh = 0; hh < NH; ++hh) {
+                for (int x = wave; x < 12; x += 2) {
+                    const f4_t z = {0.f, 0.f, 0.f, 0.f};
+                    if (x < 6) {
+                        const int nb = (x >= 3) ? 3 : (x >= 1) ? 2 : 1, mb = x - (nb - 1) * nb / 2;
+                        store_part<OP>(L.p[hh], mb * 2 + nb / 2, nb % 2, lane, z);
+                    } else {
+                        const int h = x - 6;
+                        const int f = h == 0 ? 0 : h <= 2 ? 1 : h <= 4 ? 3 : 5;
+                        const int part = (h == 0 || h == 2 || h == 4 || h == 5) ? 1 : 0;
+                        store_part<OP>(L.t[hh], f, part, lane, z);
+                    }
+                }
+            }
+        } else if (wave < 6) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int u = wave - 2 + 4 * m;
+                if (u < 6) {
+                    const int bi = u >= 3 ? 3 : (u >= 1 ? 2 : 1), bj = u - bi * (bi - 1) / 2;
+#pragma unroll
+                    for (int hh = 0; hh < NH; ++hh) {
+                        const float r = L.ra[hh][16 * bi + li];
+                        const f4_t c = *reinterpret_cast<const f4_t*>(&L.cb[hh][16 * bj + 4 * lq]);
+                        f4_t x;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) x[e] = acc[m][e] * __builtin_amdgcn_exp2f(r - c[e]);
+                        *reinterpret_cast<f4_t*>(&L.aw.s.a[hh][u][lane * 4]) = x;
+                    }
+                } else {
+                    const int tl = u - 6;
+                    const int mb = (tl >= 6) ? 3 : (tl >= 3) ? 2 : (tl >= 1) ? 1 : 0, nb = tl - mb * (mb + 1) / 2;
+                    const int i = 16 * mb + li, c0 = 16 * nb + 4 * lq;
+#pragma unroll
+                    for (int hh = 0; hh < NH; ++hh) {
+                        const float r = L.rq[hh][i];
+                        const f4_t c = *reinterpret_cast<const f4_t*>(&L.cb[hh][c0]);
+                        f4_t x;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            x[e] = (mb > nb || c0 + e <= i) ? acc[m][e] * __builtin_amdgcn_exp2f(r - c[e]) : 0.f;
+                        store_part<OP>(L.p[hh], mb * 2 + nb / 2, nb % 2, lane, x);
+                    }
+                }
+            }
+        } else if (wave - 6 < NH) {
+            const int hh = wave - 6;
+            // N_bb[j'][4q + r] (strictly lower) from the symmetric raw block, row-major
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const float r = L.ra[hh][16 * b + li];
+                const f4_t c = *reinterpret_cast<const f4_t*>(&L.cb[hh][16 * b + 4 * lq]);
+                f4_t x;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = (4 * lq + e < li) ? acc[b][e] * __builtin_amdgcn_exp2f(r - c[e]) : 0.f;
+                *reinterpret_cast<f4_t*>(&L.aw.s.nb[hh][b][li * XS + 4 * lq]) = x;
+            }
+            // Forward substitution (I + N) X = I: lane (b, j) computes column j of X_bb,
+            // X[i][j] = [i == j] - sum_{m < i} N[i][m] X[m][j].  N's rows are read as
+            // broadcasts (the 16 lanes of a block read the same address).
+            const int b = lq, j = li;
+            const float* Nb = L.aw.s.nb[hh][b];
+            float x[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float s = (i == j) ? 1.f : 0.f;
+#pragma unroll
+                for (int m4 = 0; m4 < i; m4 += 4) {
+                    const f4_t nr = *reinterpret_cast<const f4_t*>(&Nb[i * XS + m4]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (m4 + e < i) s = fmaf(-nr[e], x[m4 + e], s);
+                }
+                x[i] = s;
+            }
+            float* xd = L.aw.s.xd[hh][b];
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                *reinterpret_cast<f4_t*>(&xd[j * XS + 4 * c]) = f4_t{x[4 * c], x[4 * c + 1], x[4 * c + 2], x[4 * c + 3]};
+            // T's diagonal block: T[16b + i][16b + j] = X[i][j] beta_{16b + j}, element
+            // (j % 4) + 4 (b % 2) of lane ((j / 4), i) of fragment (b, b / 2)
+            const float bj = L.bt[hh][16 * b + j];
+            OP* tf = L.t[hh] + ((size_t)(2 * b + (b >> 1)) * WAVE + (j >> 2) * 16) * 8 + (j & 3) + 4 * (b & 1);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) tf[i * 8] = (OP)(x[i] * bj);
+        }
+        lds_barrier();  // B3
+
+        // ---- P4: blocks of X below the diagonal, as T = X diag(beta) fragment halves ----------
+        // Matrices in accumulator layout (lane (j, q) holds M[4q + r][j]); mm16(xt, y, c) =
+        // c + X Y takes X^T and Y.  T's fragment half (block row a, block column b) is
+        // X_ab^T in this layout, times beta of the column.
+        {
+            const int hh = wave >> 2;
+            if (hh < NH) {
+                // roles by wave: head 0 waves 0..3 take roles 3, 2, 0, 1 and head 1 roles 2, 3, 1, 0,
+                // so the two waves that share a SIMD (w, w + 4) carry about equal matrix work
+                const int role = ((hh ? 0x0132 : 0x1023) >> (4 * (wave & 3))) & 0xf;
+                const f4_t z = {0.f, 0.f, 0.f, 0.f};
+                auto at = [&](int i, int j) { return *reinterpret_cast<const f4_t*>(&L.aw.s.a[hh][aslot(i, j)][lane * 4]); };
+                auto xa = [&](int b) { return *reinterpret_cast<const f4_t*>(&L.aw.s.xd[hh][b][li * XS + 4 * lq]); };
+                auto xt = [&](int b) {
+                    const float* x = L.aw.s.xd[hh][b];
+                    return f4_t{x[(4 * lq) * XS + li], x[(4 * lq + 1) * XS + li], x[(4 * lq + 2) * XS + li],
+                                x[(4 * lq + 3) * XS + li]};
+                };
+                auto put = [&](int a, int b, const f4_t& negxt) {  // negxt = -X_ab^T
+                    store_part<OP>(L.t[hh], 2 * a + (b >> 1), b & 1, lane,
+                                   -negxt * *reinterpret_cast<const f4_t*>(&L.bt[hh][16 * b + 4 * lq]));
+                };
+                if (role == 0) {  // X_10 = -X_11 A_10 X_00; X_20 = -X_22 (A_20 X_00 + A_21 X_10)
+                    const f4_t x00 = xa(0), x11t = xt(1);
+                    const f4_t r = mm16(at(1, 0), x00, z);
+                    put(1, 0, mm16(r, x11t, z));
+                    const f4_t x10 = -mm16(x11t, r, z);
+                    const f4_t y = mm16(at(2, 1), x10, mm16(at(2, 0), x00, z));
+                    put(2, 0, mm16(y, xt(2), z));
+                } else if (role == 1) {  // X_21 = -X_22 A_21 X_11; X_31 = -X_33 (A_31 X_11 + A_32 X_21)
+                    const f4_t x11 = xa(1), x22t = xt(2);
+                    const f4_t r = mm16(at(2, 1), x11, z);
+                    put(2, 1, mm16(r, x22t, z));
+                    const f4_t x21 = -mm16(x22t, r, z);
+                    const f4_t y = mm16(at(3, 2), x21, mm16(at(3, 1), x11, z));
+                    put(3, 1, mm16(y, xt(3), z));
+                } else if (role == 2) {  // X_32 = -X_33 A_32 X_22
+                    put(3, 2, mm16(mm16(at(3, 2), xa(2), z), xt(3), z));
+                } else {
+                    // X_30 = -(X_32 Y_00 + X_33 Y_10), Y_00 = A_20 X_00 + A_21 X_10,
+                    // Y_10 = A_30 X_00 + A_31 X_10 (the lower-left 32 x 32 block of X is
+                    // -X_lower-right (A_lower-left X_upper-left))
+                    const f4_t x00 = xa(0), x33t = xt(3);
+                    const f4_t x10 = -mm16(xt(1), mm16(at(1, 0), x00, z), z);
+                    const f4_t y00 = mm16(at(2, 1), x10, mm16(at(2, 0), x00, z));
+                    const f4_t y10 = mm16(at(3, 1), x10, mm16(at(3, 0), x00, z));
+                    const f4_t x32t = -mm16(mm16(at(3, 2), xa(2), z), x33t, z);
+                    put(3, 0, mm16(y10, x33t, mm16(y00, x32t, z)));
+                }
+            }
+        }
+        lds_barrier();  // B4: T complete; A, N and X no longer read
+
+        // ---- P5: Ut = T V and Ot = P Ut; -W ----------------------------------------------------
+        for (int u = wave; u < NH * (D / 16); u += PREP_WAVES) {
+            const int hh = u / (D / 16), nb = u % (D / 16);
+            char* rec = recs + ((size_t)slot * h_v + h0 + hh) * RC::BYTES;
+            OP* urec = reinterpret_cast<OP*>(rec + RC::U);
+            OP* orec = reinterpret_cast<OP*>(rec + RC::O);
+            const Frag<OP> fv0 = frag_colmajor<OP>(L.v[hh], LK, nb, 0, lane);
+            const Frag<OP> fv1 = frag_colmajor<OP>(L.v[hh], LK, nb, 1, lane);
+            f4_t ut[4];
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+                ut[mb] = f4_t{0, 0, 0, 0};
+                mma(ut[mb], frag_stored<OP>(L.t[hh], mb * 2 + 0, lane), fv0);
+                mma(ut[mb], frag_stored<OP>(L.t[hh], mb * 2 + 1, lane), fv1);
+                store4<OP>(urec + ((size_t)(nb * 4 + mb) * WAVE + lane) * 4, ut[mb]);
+            }
+            const Frag<OP> fu0 = frag_from_acc<OP>(ut[0], ut[1]);
+            const Frag<OP> fu1 = frag_from_acc<OP>(ut[2], ut[3]);
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+                f4_t ot = {0, 0, 0, 0};
+                mma(ot, frag_stored<OP>(L.p[hh], mb * 2 + 0, lane), fu0);
+                mma(ot, frag_stored<OP>(L.p[hh], mb * 2 + 1, lane), fu1);
+                store4<OP>(orec + ((size_t)(nb * 4 + mb) * WAVE + lane) * 4, ot);
+            }
+        }
+        // W^T = (diag(gamma c) K)^T T^T: units (head, kb, tb) with d-blocks 2kb, 2kb + 1 and
+        // token block tb; a wave's units share (head, kb)
+        constexpr int WUNITS = NH * NKB * 4, UPW = WUNITS / PREP_WAVES > 0 ? WUNITS / PREP_WAVES : 1;
+        {
+            int cur = -1;
+            Frag<OP> aw[2][2];
+            for (int uu = 0; uu < UPW; ++uu) {
+                const int unit = wave * UPW + uu;
+                if (unit >= WUNITS) break;
+                const int hh = unit / (NKB * 4), kb = (unit / 4) % NKB, tb = unit % 4;
+                if (unit / 4 != cur) {
+                    cur = unit / 4;
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                        for (int kk = 0; kk < 2; ++kk) {
+                            Frag<OP> f = frag_colmajor<OP>(L.k, LK, 2 * kb + s2, kk, lane);
+                            const f4_t s0 = *reinterpret_cast<const f4_t*>(&L.gck[hh][32 * kk + 4 * lq]);
+                            const f4_t s1 = *reinterpret_cast<const f4_t*>(&L.gck[hh][32 * kk + 16 + 4 * lq]);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                frag_set(f, e, frag_get(f, e) * s0[e]);
+                                frag_set(f, e + 4, frag_get(f, e + 4) * s1[e]);
+                            }
+                            aw[s2][kk] = f;
+                        }
+                }
+                char* rec = recs + ((size_t)slot * h_v + h0 + hh) * RC::BYTES;
+                OP* wrec = reinterpret_cast<OP*>(rec + RC::W);
+                f4_t a2[2];
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    a2[s2] = f4_t{0, 0, 0, 0};
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk) mma(a2[s2], aw[s2][kk], frag_stored<OP>(L.t[hh], tb * 2 + kk, lane));
+                }
+                // lane (j, q): a2[s2][r] = W[token 16tb + j][d 16(2kb + s2) + 4q + r]
+                Frag<OP> fw;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) { frag_set(fw, e, -a2[0][e]); frag_set(fw, e + 4, -a2[1][e]); }
+                frag_store<OP>(wrec, tb * NKB + kb, lane, fw);
+                const int tok = 16 * tb + li;
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) store4<OP>(L.aw.w[hh] + tok * LK + 16 * (2 * kb + s2) + 4 * lq, -a2[s2]);
+            }
+        }
+        lds_barrier();  // B5: -W complete in LDS
+
+        // ---- P6: Qt^T = (diag(gamma c_q) Q)^T + (-W)^T P^T --------------------------------------
+        {
+            int cur = -1;
+            Frag<OP> aw[2][2];
+            for (int uu = 0; uu < UPW; ++uu) {
+                const int unit = wave * UPW + uu;
+                if (unit >= WUNITS) break;
+                const int hh = unit / (NKB * 4), kb = (unit / 4) % NKB, tb = unit % 4;
+                if (unit / 4 != cur) {
+                    cur = unit / 4;
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                        for (int kk = 0; kk < 2; ++kk) aw[s2][kk] = frag_colmajor<OP>(L.aw.w[hh], LK, 2 * kb + s2, kk, lane);
+                }
+                char* rec = recs + ((size_t)slot * h_v + h0 + hh) * RC::BYTES;
+                OP* qrec = reinterpret_cast<OP*>(rec + RC::Q);
+                const int tok = 16 * tb + li;
+                const float gq = L.gcq[hh][tok];
+                f4_t a2[2];
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const OP* qr = L.q + tok * LK + 16 * (2 * kb + s2) + 4 * lq;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) a2[s2][r] = (float)qr[r] * gq;
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk) mma(a2[s2], aw[s2][kk], frag_stored<OP>(L.p[hh], tb * 2 + kk, lane));
+                }
+                Frag<OP> fq;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) { frag_set(fq, e, a2[0][e]); frag_set(fq, e + 4, a2[1][e]); }
+                frag_store<OP>(qrec, tb * NKB + kb, lane, fq);
+            }
+        }
+        lds_barrier();  // B6: LDS is reused by the next item
+        tok0 = ntok0;
+        nt = nnt;
+        live = nlive;
+    }
+}
+
 // ---- sequential phase -------------------------------------------------------------------
 // One workgroup owns RS rows (16 or 32) of one (sequence, v-head) state, so a
 // d-wide head has d/RS workgroups.  The rows of S evolve independently.  A
@@ -1096,6 +1606,27 @@ int compute_units() {
     return cached[dev];
 }
 
+template <int D, int NH>
+static hipError_t launch_prep_pair_t(const void* q, const void* k, const void* v, const float* g,
+                                     const float* beta, const void* info, const int32_t* slot_seq,
+                                     int slots, int T, int h_k, int h_v, int l2norm, float scale,
+                                     char* recs, char* krecs, hipStream_t stream) {
+    constexpr size_t lds = pair_lds_bytes<D, NH>();
+    static_assert(lds <= 160 * 1024, "chunk_prep_pair LDS budget");
+    auto kern = chunk_prep_pair_kernel<D, NH>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    // one workgroup per compute unit, each a contiguous run of items
+    const int items = slots * h_k * (h_v / h_k / NH), resident = compute_units();
+    const int per = (items + resident - 1) / resident;
+    const int grid = (items + per - 1) / per;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(PREP_THREADS), lds, stream, q, k, v, g, beta,
+                       reinterpret_cast<const SeqInfo*>(info), slot_seq, T, h_k, h_v, l2norm, scale, recs, krecs,
+                       slots, per);
+    return hipGetLastError();
+}
+
 template <int D, typename OP, bool IB>
 static hipError_t launch_prep_t(const void* q, const void* k, const void* v, const float* g,
                                 const float* beta, const void* info, const int32_t* slot_seq,
@@ -1124,10 +1655,13 @@ hipError_t launch_prep(int d, bool in_bf16, const void* q, const void* k, const 
                        void* krecs, hipStream_t stream) {
     char* r = reinterpret_cast<char*>(recs);
     char* kr = reinterpret_cast<char*>(krecs);
+    const bool pair = (h_v / h_k) % 2 == 0;
     if (d == 128 && in_bf16)
-        return launch_prep_t<128, _Float16, true>(q, k, v, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, kr, stream);
+        return pair ? launch_prep_pair_t<128, 2>(q, k, v, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, kr, stream)
+                    : launch_prep_pair_t<128, 1>(q, k, v, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, kr, stream);
     if (d == 64 && in_bf16)
-        return launch_prep_t<64, _Float16, true>(q, k, v, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, kr, stream);
+        return pair ? launch_prep_pair_t<64, 2>(q, k, v, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, kr, stream)
+                    : launch_prep_pair_t<64, 1>(q, k, v, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, kr, stream);
     if (d == 64 && !in_bf16)
         return launch_prep_t<64, float, false>(q, k, v, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, kr, stream);
     return hipErrorInvalidValue;
