@@ -364,7 +364,7 @@ def prefill_configs(L, gdn, inputs, to_dev, torch, np, dev, with_cpu=True):
                 raise gdn.GdnError(st, gdn.last_error())
 
         def scan():
-            st = L.gdn_prefill_scan(dref, P[5], P[6], P[7], P[8], 64, ws.data_ptr(), wsb, sp)
+            st = L.gdn_prefill_scan(dref, P[0], P[1], P[2], P[5], P[6], P[7], P[8], 64, ws.data_ptr(), wsb, sp)
             if st:
                 raise gdn.GdnError(st, gdn.last_error())
 
@@ -542,7 +542,7 @@ def main():
             raise gdn.GdnError(st, gdn.last_error())
 
     def scan_call():
-        st = L.gdn_prefill_scan(dref, None, out.data_ptr(), s_out.data_ptr(), None, 64, ws.data_ptr(),
+        st = L.gdn_prefill_scan(dref, P[0], P[1], P[2], None, out.data_ptr(), s_out.data_ptr(), None, 64, ws.data_ptr(),
                                 ws_bytes, sp)
         if st:
             raise gdn.GdnError(st, gdn.last_error())

@@ -142,14 +142,14 @@ gdn_status gdn_prefill(const gdn_desc *desc,
  * stream, with the same workspace, is gdn_prefill in one pass (bit-identical
  * to gdn_prefill also where it runs segments).
  *
- * gdn_prefill_prepare: everything that does not depend on the carried state,
- *   for all blocks at once (parallel over blocks and v-heads).  Reads q, k, v,
- *   g, beta and cu_seqlens.  Writes only the workspace.
+ * gdn_prefill_prepare: the state-free work of every block at once (parallel
+ *   over blocks and heads).  Reads q, k, v, g, beta and cu_seqlens.  Writes
+ *   only the workspace.
  * gdn_prefill_scan: walks each sequence's blocks in order with the state held
- *   on chip.  Reads the prepared workspace and state_in, and writes out and
- *   state_out.  Pass the same desc, cu_seqlens (as a layout flag: NULL or
- *   not) and workspace as the prepare call.  The workspace must not change in
- *   between.
+ *   on chip.  Reads q, k, v (the same tensors), the prepared workspace and
+ *   state_in, and writes out and state_out.  Pass the same desc, cu_seqlens
+ *   (as a layout flag: NULL or not) and workspace as the prepare call.  The
+ *   workspace and the inputs must not change in between.
  * Arguments, validation and errors are those of gdn_prefill.
  */
 gdn_status gdn_prefill_prepare(const gdn_desc *desc,
@@ -160,6 +160,7 @@ gdn_status gdn_prefill_prepare(const gdn_desc *desc,
                                void *stream);
 
 gdn_status gdn_prefill_scan(const gdn_desc *desc,
+                            const void *q, const void *k, const void *v,
                             const float *state_in, void *out, float *state_out,
                             const int32_t *cu_seqlens, int32_t chunk,
                             void *workspace, size_t workspace_bytes,

@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgdn.so")
 CAL_LIB = os.path.join(HERE, "libgdn_calibrate.so")
-SOURCES = ["decode.hip", "prefill.hip", "api.cpp"]
+SOURCES = ["decode.hip", "prefill.hip", "prefill_bf16.hip", "api.cpp"]
 ARCH = "gfx950"
 
 

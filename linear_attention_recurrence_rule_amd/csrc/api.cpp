@@ -22,8 +22,9 @@ size_t prefill_key_record_bytes(int d, bool in_bf16);
 hipError_t launch_segment_info(void* info, int P, int sb, int T, hipStream_t stream);
 hipError_t launch_compose(int d, const float* state_in, const float* R, const float* B, float* starts, int P,
                           int h_v, hipStream_t stream);
-hipError_t launch_scan_transition(int d, bool in_bf16, const void* recs, const void* krecs, const void* info,
-                                  float* s_out, void* sink, int units, int T, int h_k, int h_v, hipStream_t stream);
+hipError_t launch_scan_transition(int d, bool in_bf16, int rows, const void* q, const void* k, const void* v,
+                                  const void* recs, const void* krecs, const void* info, float* s_out, void* sink,
+                                  int units, int T, int h_k, int h_v, hipStream_t stream);
 hipError_t launch_direct(int d, bool in_bf16, bool out_bf16, const void* q, const void* k, const void* v,
                          const float* g, const float* beta, const int32_t* cu, const float* s_in, float* s_out,
                          void* out, int units, int T, int h_k, int h_v, int l2norm, float scale, int fuse, const float* norm_w,
@@ -34,9 +35,9 @@ hipError_t launch_prep(int d, bool in_bf16, const void* q, const void* k, const 
                        const float* g, const float* beta, const void* info, const int32_t* slot_seq,
                        int slots, int T, int h_k, int h_v, int l2norm, float scale, void* recs,
                        void* krecs, hipStream_t stream);
-hipError_t launch_scan(int d, bool in_bf16, bool out_bf16, const void* recs, const void* krecs, const void* info,
-                       const float* s_in, float* s_out, void* out, void* sink, int units, int T, int h_k, int h_v,
-                       hipStream_t stream);
+hipError_t launch_scan(int d, bool in_bf16, bool out_bf16, int rows, const void* q, const void* k, const void* v,
+                       const void* recs, const void* krecs, const void* info, const float* s_in, float* s_out,
+                       void* out, void* sink, int units, int T, int h_k, int h_v, hipStream_t stream);
 }  // namespace gdn
 
 namespace {
@@ -254,7 +255,7 @@ enum Phase { kPrepare = 1, kScan = 2, kBoth = 3 };
 gdn_status prefill_call(Phase phase, const gdn_desc* desc, const void* q, const void* k, const void* v,
                         const float* g, const float* beta, const float* state_in, void* out,
                         float* state_out, const int32_t* cu_seqlens, int32_t chunk, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+                        size_t workspace_bytes, void* stream, int scan_rows = 0) {
     g_err[0] = 0;
     gdn_status st = check_desc(desc, true);
     if (st != GDN_OK) return st;
@@ -264,7 +265,8 @@ gdn_status prefill_call(Phase phase, const gdn_desc* desc, const void* q, const 
     if (!cu_seqlens && N != 1) return fail(GDN_ERR_INVALID_ARGUMENT, "cu_seqlens is NULL but num_seqs = %d", N);
     if (T > 0 && (phase & kPrepare) && (!q || !k || !v || !g || !beta))
         return fail(GDN_ERR_INVALID_ARGUMENT, "q, k, v, g and beta must be non-NULL");
-    if (T > 0 && (phase & kScan) && !out) return fail(GDN_ERR_INVALID_ARGUMENT, "out must be non-NULL");
+    if (T > 0 && (phase & kScan) && (!q || !k || !v || !out))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "q, k, v and out must be non-NULL");
     const bool varlen = cu_seqlens != nullptr;
     const WsLayout ws = ws_layout(desc, varlen);
     // the requirement is what gdn_prefill_workspace_bytes reports, whichever layout is used
@@ -309,8 +311,8 @@ gdn_status prefill_call(Phase phase, const gdn_desc* desc, const void* q, const 
         }
     }
     if ((phase & kScan) && (state_out || T > 0)) {
-        e = gdn::launch_scan(d, in_bf16, out_bf16, wsb + ws.rec_off, wsb + ws.key_off, info, state_in, state_out,
-                             out, wsb + ws.sink_off, N * hv, (int)T, hk, hv, s);
+        e = gdn::launch_scan(d, in_bf16, out_bf16, scan_rows, q, k, v, wsb + ws.rec_off, wsb + ws.key_off, info,
+                             state_in, state_out, out, wsb + ws.sink_off, N * hv, (int)T, hk, hv, s);
         if (e != hipSuccess) return fail(GDN_ERR_HIP, "chunk_scan launch: %s", hipGetErrorString(e));
     }
     return GDN_OK;
@@ -461,10 +463,11 @@ gdn_status gdn_prefill_prepare(const gdn_desc* desc, const void* q, const void* 
                         workspace, workspace_bytes, stream);
 }
 
-gdn_status gdn_prefill_scan(const gdn_desc* desc, const float* state_in, void* out, float* state_out,
+gdn_status gdn_prefill_scan(const gdn_desc* desc, const void* q, const void* k, const void* v,
+                            const float* state_in, void* out, float* state_out,
                             const int32_t* cu_seqlens, int32_t chunk, void* workspace,
                             size_t workspace_bytes, void* stream) {
-    return prefill_call(kScan, desc, nullptr, nullptr, nullptr, nullptr, nullptr, state_in, out, state_out,
+    return prefill_call(kScan, desc, q, k, v, nullptr, nullptr, state_in, out, state_out,
                         cu_seqlens, chunk, workspace, workspace_bytes, stream);
 }
 
@@ -657,12 +660,12 @@ gdn_status gdn_prefill_two_level(const gdn_desc* desc, const void* q, const void
     // segments 0..P-2 in one pass: affine parts B from zero, transitions R from the identity
     // (B and R are adjacent, so one state_out array holds both halves)
     if (e == hipSuccess)
-        e = gdn::launch_scan_transition(d, in_bf16, recs, krecs, info, B, wsb + ws.sink_off, 2 * (P - 1) * hv,
-                                        (int)T, hk, hv, s);
+        e = gdn::launch_scan_transition(d, in_bf16, 0, q, k, v, recs, krecs, info, B, wsb + ws.sink_off,
+                                        2 * (P - 1) * hv, (int)T, hk, hv, s);
     if (e == hipSuccess) e = gdn::launch_compose(d, state_in, R, B, starts, P, hv, s);
     if (e == hipSuccess)
-        e = gdn::launch_scan(d, in_bf16, out_bf16, recs, krecs, info, starts, ends, out, wsb + ws.sink_off, P * hv,
-                             (int)T, hk, hv, s);
+        e = gdn::launch_scan(d, in_bf16, out_bf16, 0, q, k, v, recs, krecs, info, starts, ends, out,
+                             wsb + ws.sink_off, P * hv, (int)T, hk, hv, s);
     if (e == hipSuccess && state_out)
         e = hipMemcpyAsync(state_out, ends + (size_t)(P - 1) * hv * d * d, sbytes, hipMemcpyDeviceToDevice, s);
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "two-level prefill launch: %s", hipGetErrorString(e));

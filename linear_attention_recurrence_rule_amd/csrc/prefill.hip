@@ -1,10 +1,12 @@
-// Blocked ("chunked") prefill of the gated delta rule on gfx950.
+// Blocked ("chunked") prefill of the gated delta rule on gfx950: the fp32-input
+// kernels, the varlen plan, the two-level scan's segment kernels and the host
+// launchers of both input types (the bf16-input kernels are in prefill_bf16.hip).
 //
 // "Optimizing on-device inference for Apple Silicon", section "Qwen creates
 // three distinct workload shapes", says the recurrence can be regrouped into
 // blocks of tokens that expose matrix work.  Section "Keep the recurrent state
 // on chip" keeps the state on chip for the whole scan and writes it back once,
-// in fp32.  This file implements that blocked form with matrix-core tiles.
+// in fp32.
 //
 // Per block of n <= 64 tokens (chunk) and v-head, with block-initial state S
 // (d_v x d_k), cumulative log-decay G_i = g_1 + ... + g_i, effective keys k_i
@@ -23,21 +25,13 @@
 // S's rows evolve independently, so a v-head's state can be split by rows
 // over several workgroups.
 //
-// Precision.  q/k are scaled per token by a power of two (exact) and fed raw
-// to the matrix cores.  Their L2 norms become fp32 row factors c_t.  Values
-// enter as fp16 (exact for bf16 in range).  fp32 intermediates that feed the
-// matrix cores are rounded to fp16 (bf16 inputs) or stay fp32 (fp32 inputs).
-// Ut and Ot are stored in the operand type too; they only seed the scan's
-// fp32 accumulators.
-#include "gdn_device.h"
+// Precision (fp32 inputs).  q/k are scaled per token by a power of two (exact)
+// and their L2 norms become fp32 row factors c_t; every matrix product runs on
+// the fp32 matrix cores, with fp32 intermediates and records.
+#include "prefill_shared.h"
 
-#include <stdlib.h>
 
 namespace gdn {
-
-struct SeqInfo {
-    int32_t begin, len, slot_base, pad;
-};
 
 // ---- varlen plan: per-sequence token range and block-slot base, slot -> sequence ----
 // One workgroup.  cu_seqlens is clamped into a non-decreasing sequence inside
@@ -218,20 +212,6 @@ __device__ __forceinline__ float* prep_xslot(float* ax, int s, int li, int lq) {
     return ax + (16 * r + li) * LDF + 16 * c + 4 * lq;
 }
 
-// Write 4 accumulator values (one lane's share of a 16x16 tile) as half of a
-// stored fragment: part 0 = elements 0..3, part 1 = elements 4..7.
-template <typename OP>
-__device__ __forceinline__ void store_part(OP* base, int frag, int part, int lane, const f4_t& x) {
-    OP* p = base + ((size_t)frag * WAVE + lane) * 8 + 4 * part;
-    if constexpr (sizeof(OP) == 2) {
-        typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
-        h4_t h = {(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
-        *reinterpret_cast<h4_t*>(p) = h;
-    } else {
-        *reinterpret_cast<f4_t*>(p) = x;
-    }
-}
-
 // Row fragment of a row-major matrix M (leading dimension ld) for products
 // whose two operands are both read this way: lane (i, q) holds the eight
 // consecutive elements M[16 rb + i][32 kb + 8q + e], one 16-byte read (two for
@@ -249,50 +229,6 @@ __device__ __forceinline__ Frag<OP> frag_row8(const OP* M, int ld, int rb, int k
         f.hi = *reinterpret_cast<const f4_t*>(p + 4);
     }
     return f;
-}
-
-// Inclusive prefix sum over the 64 lanes of a wave, in registers (DPP):
-// Hillis-Steele inside each row of 16 lanes (row_shr 1, 2, 4, 8), then the
-// row totals are carried forward with row_bcast 15 (rows 1, 3) and
-// row_bcast 31 (rows 2, 3).  Lanes without a source add 0.
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ float dpp_add_src(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xF, false));
-}
-__device__ __forceinline__ float wave_inclusive_sum(float x) {
-    x += dpp_add_src<0x111, 0xF>(x);  // row_shr:1
-    x += dpp_add_src<0x112, 0xF>(x);  // row_shr:2
-    x += dpp_add_src<0x114, 0xF>(x);  // row_shr:4
-    x += dpp_add_src<0x118, 0xF>(x);  // row_shr:8
-    x += dpp_add_src<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
-    x += dpp_add_src<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
-    return x;
-}
-// The same in fp64: each DPP move carries both 32-bit halves.
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ double dpp_add_src64(double x) {
-    const unsigned long long b = (unsigned long long)__double_as_longlong(x);
-    const unsigned lo = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)b, CTRL, ROW_MASK, 0xF, false);
-    const unsigned hi = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)(b >> 32), CTRL, ROW_MASK, 0xF, false);
-    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
-}
-__device__ __forceinline__ double wave_inclusive_sum(double x) {
-    x += dpp_add_src64<0x111, 0xF>(x);
-    x += dpp_add_src64<0x112, 0xF>(x);
-    x += dpp_add_src64<0x114, 0xF>(x);
-    x += dpp_add_src64<0x118, 0xF>(x);
-    x += dpp_add_src64<0x142, 0xA>(x);
-    x += dpp_add_src64<0x143, 0xC>(x);
-    return x;
-}
-
-// C + X Y for 16x16 fp32 matrices, X^T and Y (and C) in accumulator layout:
-// lane (j, q) holds M[4q + r][j] in element r.  Instruction e contracts over
-// k = 4q + e, taking X[i][4q + e] = X^T[4q + e][i] and Y[4q + e][j].
-__device__ __forceinline__ f4_t mm16(const f4_t& xt, const f4_t& y, f4_t c) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(xt[e], y[e], c, 0, 0, 0);
-    return c;
 }
 
 // One thread's share of a block's raw inputs for one (k-head, v-head).
@@ -781,648 +717,6 @@ __global__ __launch_bounds__(PREP_THREADS, (prep_min_waves<D, OP>())) void chunk
     }
 }
 
-// s_waitcnt vmcnt(n), other counters untouched (gfx9 encoding)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// ---- block-form work for bf16 inputs: a k-head's v-heads in pairs -------------------------
-// One workgroup per compute unit takes a run of items (block slot, k-head,
-// pair of the k-head's v-heads) and computes both v-heads' records together,
-// so that every phase has work for all eight compute waves and the raw Gram
-// products K K^T and Q K^T are formed once per item (only the decay masks,
-// beta and the norm factors differ between the two v-heads).
-//
-// Two loader waves copy each item's raw bf16 q, k, v tiles and its g, beta
-// into LDS with direct global-to-LDS loads while the eight compute waves work
-// on the previous item.  The compute waves issue no global loads, only
-// record stores: the memory counter that a wave waits on covers its loads and
-// its stores alike, so a wave that both loaded inputs and wrote records would
-// wait for its record stores to drain before each item.
-//   P2a waves 0, 1: the diagonal blocks of K K^T and Q Q^T (bf16 matrix cores
-//       on the raw inputs), whose diagonals give the norm factors, then G
-//       (cumulative log-decay) and the per-token exponent terms of v-head
-//       `wave`; waves 2..5: the raw off-diagonal K K^T and the Q K^T tiles;
-//       waves 6, 7: the raw diagonal K K^T tiles.
-//   P2b decay masks: A_ij^T tiles (i > j blocks), P fragments, and the diagonal
-//       blocks N_bb of A, which waves 6, 7 invert by forward substitution on
-//       the vector unit (one lane per column of a block).
-//   P4  the six blocks of X = (I + A)^{-1} below the diagonal (fp32 matrix
-//       cores), written as T = X diag(beta) fragments.
-//   P5  Ut = T V and Ot = P Ut; -W = -T diag(gamma c) K; the key record
-//       (normalised keys, fp16) from the same key fragments.
-//   P6  Qt = diag(gamma c_q) Q - P W (q is double-buffered).
-// Decay ratios are exp2(r_i - c_j) with r_i = G_i log2(e) + log2(beta_i c_i)
-// and c_j = G_j log2(e) - log2(c_j); only entries with i >= j are kept, so
-// the exponent carries exp(G_i - G_j) <= 1.
-// Raw tiles are stored unpadded, rows of D bf16, with the 16-byte units of
-// row r permuted by XOR with (r mod units per row), so that the reads of a
-// column or of 16 rows at one column spread over the LDS banks.
-constexpr float LOG2E_F = 1.4426950408889634f;
-constexpr int PAIR_COMPUTE_WAVES = 8, PAIR_LOADER_WAVES = 2;
-constexpr int PAIR_THREADS = (PAIR_COMPUTE_WAVES + PAIR_LOADER_WAVES) * WAVE;
-
-typedef __bf16 bf8_t __attribute__((ext_vector_type(8)));
-typedef short s4v_t __attribute__((ext_vector_type(4)));
-typedef _Float16 h4v_t __attribute__((ext_vector_type(4)));
-
-struct PairMeta {
-    int32_t tok0, nt, live, pad;
-};
-
-template <int D, int NH>
-struct PairLds {
-    static constexpr int LK = D + 8;    // row stride of the fp16 -W tile
-    static constexpr int XS = 20;       // row stride of 16 x 16 fp32 blocks
-    uint16_t kraw[CHUNK * D];           // raw bf16 keys (swizzled rows)
-    uint16_t vraw[NH][CHUNK * D];       // raw bf16 values
-    uint16_t qraw[2][CHUNK * D];        // raw bf16 queries, by item parity
-    float gb[2][NH][2][CHUNK];          // g and beta of the v-heads, by item parity
-    union {
-        struct {
-            float a[NH][6][WAVE * 4];   // A_ij^T (block i > j) in accumulator layout
-            float nb[NH][4][16 * XS];   // diagonal blocks N_bb of A, row-major
-            float xd[NH][4][16 * XS];   // X_bb = (I + N_bb)^{-1}, column-major [col][row]
-        } s;
-        _Float16 w[NH][CHUNK * LK];     // -W [token][d]
-    } aw;
-    _Float16 t[NH][CHUNK * CHUNK];      // T = X diag(beta), fragment-major
-    _Float16 p[NH][CHUNK * CHUNK];      // P, fragment-major
-    float cn[2][2 * CHUNK];             // norm factors c_k, c_q (one copy per wave 0, 1)
-    float ra[NH][CHUNK], rq[NH][CHUNK], cb[NH][CHUNK];  // exponent terms (above)
-    float gck[NH][CHUNK], gcq[NH][CHUNK], bt[NH][CHUNK];
-    PairMeta meta[2];
-    int zero;  // holds 0 (see chunk_prep_pair_kernel)
-};
-
-template <int D, int NH>
-constexpr size_t pair_lds_bytes() { return sizeof(PairLds<D, NH>); }
-
-// Slot of the off-diagonal block (i, j), i > j: (1,0) (2,0) (2,1) (3,0) (3,1) (3,2).
-__device__ __forceinline__ constexpr int aslot(int i, int j) { return i * (i - 1) / 2 + j; }
-
-// Byte offset of the 16-byte unit u of row r in a swizzled raw tile of D bf16 per row.
-template <int D>
-__device__ __forceinline__ int raw_unit(int r, int u) {
-    constexpr int UPR = D / 8;
-    return r * (D * 2) + ((u ^ (r & (UPR - 1))) << 4);
-}
-
-// Row fragment (8 consecutive d of one token) of a raw tile, for products whose two
-// operands are both read this way (the Gram products): lane (i, q) holds
-// M[16 rb + i][32 kb + 8 q + e].
-template <int D>
-__device__ __forceinline__ bf8_t raw_row8(const uint16_t* M, int rb, int kb, int lane) {
-    const int r = 16 * rb + (lane & 15), u = 4 * kb + (lane >> 4);
-    return *reinterpret_cast<const bf8_t*>(reinterpret_cast<const char*>(M) + raw_unit<D>(r, u));
-}
-
-__device__ __forceinline__ void mma_bf16(f4_t& acc, const bf8_t& a, const bf8_t& b) {
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
-}
-
-// Column fragment of a raw tile as fp32 (the layout of frag_colmajor): the
-// contraction runs down the rows 32 kb + (4q + e) for e < 4 and
-// 32 kb + 16 + 4q + (e - 4) for e >= 4, at column 16 cb + (lane % 16).  Two
-// transposing reads (ds_read_b64_tr_b16) of the swizzled rows.
-template <int D>
-__device__ __forceinline__ void raw_col(const uint16_t* M, int cb, int kb, int lane, float x[8]) {
-    typedef __attribute__((address_space(3))) s4v_t* lds_s4;
-    const int s = lane & 15, q = lane >> 4;
-    const int r = 32 * kb + 4 * q + (s >> 2), col = 16 * cb + 4 * (s & 3);
-    const char* base = reinterpret_cast<const char*>(M);
-    const int o0 = raw_unit<D>(r, col >> 3) + ((col & 7) << 1);
-    const int o1 = raw_unit<D>(r + 16, col >> 3) + ((col & 7) << 1);
-    const s4v_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(base + o0));
-    const s4v_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(base + o1));
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        x[e] = __uint_as_float((uint32_t)(uint16_t)a[e] << 16);
-        x[e + 4] = __uint_as_float((uint32_t)(uint16_t)b[e] << 16);
-    }
-}
-
-template <int D, int NH>
-__global__ __launch_bounds__(PAIR_THREADS, 1) void chunk_prep_pair_kernel(
-    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
-    const float* __restrict__ g, const float* __restrict__ beta, const SeqInfo* __restrict__ info,
-    const int32_t* __restrict__ slot_seq, int T, int h_k, int h_v, int l2norm, float scale,
-    char* __restrict__ recs, char* __restrict__ krecs, int slots, int items_per_wg) {
-    using OP = _Float16;
-    using RC = Rec<D, OP>;
-    using LT = PairLds<D, NH>;
-    constexpr int LK = LT::LK, XS = LT::XS;
-    constexpr int NKB = D / 32;       // contraction blocks over d
-    extern __shared__ __align__(16) char smem_raw[];
-    LT& L = *reinterpret_cast<LT*>(smem_raw);
-    const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
-    const int li = lane & 15, lq = lane >> 4;
-    const int ratio = h_v / h_k, pairs = ratio / NH;
-    const int per_slot = h_k * pairs;
-    const int items = slots * per_slot;
-    const int i0 = blockIdx.x * items_per_wg, i1 = min(items, i0 + items_per_wg);
-    if (i0 >= i1) return;
-    auto heads_of = [&](int item, int& hk, int& pr) {
-        hk = (item / pairs) % h_k;
-        pr = item % pairs;
-        return hk * ratio + pr * NH;
-    };
-
-    if (wave >= PAIR_COMPUTE_WAVES) {
-        // ------------------------------ loader waves ------------------------------
-        // Item i + 1's copies go out while item i is computed, each into a buffer that
-        // is free by then: q, g and beta (double-buffered) after B1; k (read up to P5)
-        // and the first half of v after B5; the second half of v after B6.  k, q, g and
-        // beta must have landed by the next B1, v by the next B4.  Every item issues the
-        // same number of loads (a dead item loads token 0), so the explicit vmcnt counts
-        // below hold: loads complete in issue order.
-        typedef __attribute__((address_space(3))) void* lds_ptr;
-        const int lw = wave - PAIR_COMPUTE_WAVES;
-        constexpr int RPI = 1024 / (2 * D);           // rows per direct load
-        constexpr int UPR = D / 8;                    // 16-byte units per row
-        constexpr int NL = CHUNK / RPI;               // loads per tile
-        constexpr int PER = NL / PAIR_LOADER_WAVES;   // loads per tile and loader wave
-        constexpr int GB = 2 * NH / PAIR_LOADER_WAVES > 0 ? 2 * NH / PAIR_LOADER_WAVES : 1;  // g/beta loads per wave
-        constexpr int VH = NH * PER / 2 > 0 ? NH * PER / 2 : 1;  // loads per half of v, per wave
-        static_assert(NL % PAIR_LOADER_WAVES == 0 && (NH * PER) % 2 == 0, "copy split");
-        auto meta_of = [&](int item) {
-            PairMeta m{0, 0, 0, 0};
-            const int slot = item / per_slot;
-            if (slot_seq) {
-                const int n = slot_seq[slot];
-                if (n >= 0) {
-                    const SeqInfo si = info[n];
-                    const int j = slot - si.slot_base;
-                    m.tok0 = si.begin + j * CHUNK;
-                    m.nt = min(CHUNK, si.len - j * CHUNK);
-                    m.live = 1;
-                }
-            } else {
-                m.tok0 = slot * CHUNK;
-                m.nt = min(CHUNK, T - slot * CHUNK);
-                m.live = 1;
-            }
-            return m;
-        };
-        // one direct load (64 lanes x 16 bytes = RPI rows) of row group m4 of a tile:
-        // the LDS slot of unit p in row r holds the global unit p ^ (r mod UPR)
-        auto tile_load = [&](const uint16_t* base, size_t row_stride, int tok0, uint16_t* dst, int m4) {
-            const int r = m4 * RPI + lane / UPR, p = lane % UPR;
-            const int u = p ^ (r & (UPR - 1));
-            const size_t tt = (size_t)min(tok0 + r, T - 1);
-            __builtin_amdgcn_global_load_lds(base + tt * row_stride + 8 * u, (lds_ptr)(dst + m4 * 512), 16, 0, 0);
-        };
-        auto issue_qgb = [&](int item, int tok0, int par) {  // PER + GB loads
-            int hk, pr;
-            const int h0 = heads_of(item, hk, pr);
-            for (int i = 0; i < PER; ++i)
-                tile_load(reinterpret_cast<const uint16_t*>(q) + (size_t)hk * D, (size_t)h_k * D, tok0, L.qraw[par],
-                          lw + PAIR_LOADER_WAVES * i);
-            for (int i = 0; i < GB; ++i) {
-                const int x = lw + PAIR_LOADER_WAVES * i;  // (head, g or beta)
-                const int j = min(x >> 1, NH - 1);
-                const size_t tg = (size_t)min(tok0 + lane, T - 1) * h_v + h0 + j;
-                const float* src = (x & 1) ? beta + tg : g + tg;
-                __builtin_amdgcn_global_load_lds(src, (lds_ptr)&L.gb[par][j][x & 1][0], 4, 0, 0);
-            }
-        };
-        auto issue_k = [&](int item, int tok0) {  // PER loads
-            int hk, pr;
-            heads_of(item, hk, pr);
-            for (int i = 0; i < PER; ++i)
-                tile_load(reinterpret_cast<const uint16_t*>(k) + (size_t)hk * D, (size_t)h_k * D, tok0, L.kraw,
-                          lw + PAIR_LOADER_WAVES * i);
-        };
-        auto issue_v = [&](int item, int tok0, int half) {  // VH loads
-            int hk, pr;
-            const int h0 = heads_of(item, hk, pr);
-            for (int i = 0; i < VH; ++i) {
-                const int x = half * VH + i;  // (head, row group) pairs of this wave
-                const int j = x / PER, m4 = lw + PAIR_LOADER_WAVES * (x % PER);
-                tile_load(reinterpret_cast<const uint16_t*>(v) + (size_t)(h0 + j) * D, (size_t)h_v * D, tok0,
-                          L.vraw[j], m4);
-            }
-        };
-        int par = 0;
-        PairMeta m = meta_of(i0);
-        if (lw == 0 && lane == 0) L.meta[0] = m;
-        issue_qgb(i0, m.live ? m.tok0 : 0, 0);
-        issue_k(i0, m.live ? m.tok0 : 0);
-        issue_v(i0, m.live ? m.tok0 : 0, 0);
-        issue_v(i0, m.live ? m.tok0 : 0, 1);
-        wait_vmcnt<0>();
-        for (int item = i0; item < i1; ++item, par ^= 1) {
-            const bool more = item + 1 < i1;
-            const PairMeta mn = more ? meta_of(item + 1) : PairMeta{0, 0, 0, 0};
-            const int ntok0 = mn.live ? mn.tok0 : 0;
-            lds_barrier();  // B1
-            if (more) {
-                if (lw == 0 && lane == 0) L.meta[par ^ 1] = mn;
-                issue_qgb(item + 1, ntok0, par ^ 1);
-            }
-            lds_barrier();  // B2
-            lds_barrier();  // B3
-            if (item > i0) {  // this item's v has landed (issued before the next item's q, g, beta)
-                if (more) wait_vmcnt<PER + GB>();
-                else wait_vmcnt<0>();
-            }
-            lds_barrier();  // B4
-            lds_barrier();  // B5: k and v are no longer read
-            if (more) {
-                issue_k(item + 1, ntok0);
-                issue_v(item + 1, ntok0, 0);
-            }
-            lds_barrier();  // B6
-            if (more) {
-                issue_v(item + 1, ntok0, 1);
-                wait_vmcnt<2 * VH>();  // the next item's q, g, beta and k have landed
-            }
-        }
-        return;
-    }
-
-    // ------------------------------ compute waves ------------------------------
-    if (tid == 0) L.zero = 0;
-    int par = 0;
-    for (int item = i0; item < i1; ++item, par ^= 1) {
-        const int slot = item / per_slot;
-        int hk, pr;
-        const int h0 = heads_of(item, hk, pr);
-        lds_barrier();  // B1: this item's raw inputs and meta are in LDS
-        // Lane indices re-derived through a volatile LDS read of 0: left loop-invariant,
-        // the compiler hoists the per-lane LDS address arithmetic of every phase out of
-        // the item loop and runs out of registers (the value is uniform over the wave).
-        const int lane = (threadIdx.x + *(volatile __attribute__((address_space(3))) int*)(&L.zero)) % WAVE;
-        const int li = lane & 15, lq = lane >> 4;
-        const PairMeta meta = L.meta[par];
-        const bool live = meta.live != 0;
-        const int cnt = meta.nt;
-        const uint16_t* qr = L.qraw[par];
-
-        // ---- P2a ------------------------------------------------------------------------------
-        f4_t acc[4];
-        if (live) {
-            if (wave < 2) {
-                // diagonal blocks of K K^T (b = 0..3) and Q Q^T (b = 4..7); the diagonal of
-                // each is the squared norm of its 16 tokens
-                float* cn = L.cn[wave];
-#pragma unroll
-                for (int b = 0; b < 8; ++b) {
-                    const uint16_t* M = b < 4 ? L.kraw : qr;
-                    f4_t d = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int kb = 0; kb < NKB; ++kb) {
-                        const bf8_t x = raw_row8<D>(M, b & 3, kb, lane);
-                        mma_bf16(d, x, x);
-                    }
-                    // lane (j, q) holds rows 4q + r of column j: the diagonal is r = j - 4q
-                    if ((li >> 2) == lq) {
-                        const float ss = d[li & 3];
-                        const float mul = b < 4 ? 1.0f : scale;
-                        cn[16 * b + li] = l2norm ? mul * rsqrtf(ss + 1e-6f) : mul;
-                    }
-                }
-                if (wave < NH) {
-                    const int hh = wave;
-                    const bool tl = lane < cnt;
-                    const float ckv = tl ? cn[lane] : 0.f, cqv = tl ? cn[CHUNK + lane] : 0.f;
-                    const float gl = wave_inclusive_sum(tl ? L.gb[par][hh][0][lane] : 0.f) * LOG2E_F;
-                    const float bv = tl ? L.gb[par][hh][1][lane] : 0.f;
-                    L.ra[hh][lane] = gl + __builtin_amdgcn_logf(bv * ckv);
-                    L.rq[hh][lane] = gl + __builtin_amdgcn_logf(cqv);
-                    L.cb[hh][lane] = gl - __builtin_amdgcn_logf(ckv);
-                    L.bt[hh][lane] = bv;
-                    const float gam = __builtin_amdgcn_exp2f(gl);
-                    L.gck[hh][lane] = gam * ckv;
-                    L.gcq[hh][lane] = gam * cqv;
-                    const float gln = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gl), max(cnt - 1, 0)));
-                    char* rec = recs + ((size_t)slot * h_v + h0 + hh) * RC::BYTES;
-                    reinterpret_cast<float*>(rec + RC::S)[lane] = tl ? __builtin_amdgcn_exp2f(gln - gl) : 0.f;
-                    if (lane == 0) reinterpret_cast<float*>(rec + RC::M)[0] = __builtin_amdgcn_exp2f(gln);
-                }
-            } else if (wave < 6) {
-                // tiles u = wave - 2 + 4m: u < 6 the off-diagonal K K^T block of slot u, computed
-                // as K_j K_i^T so that lane (j', q) holds A_ij^T[4q + r][j']; u >= 6 the tile
-                // K_nb Q_mb^T, which is this lane's half of P's fragment (mb, nb / 2).
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const int u = wave - 2 + 4 * m;
-                    acc[m] = f4_t{0.f, 0.f, 0.f, 0.f};
-                    if (u < 6) {
-                        const int bi = u >= 3 ? 3 : (u >= 1 ? 2 : 1), bj = u - bi * (bi - 1) / 2;
-#pragma unroll
-                        for (int kb = 0; kb < NKB; ++kb)
-                            mma_bf16(acc[m], raw_row8<D>(L.kraw, bj, kb, lane), raw_row8<D>(L.kraw, bi, kb, lane));
-                    } else {
-                        const int tl = u - 6;
-                        const int mb = (tl >= 6) ? 3 : (tl >= 3) ? 2 : (tl >= 1) ? 1 : 0, nb = tl - mb * (mb + 1) / 2;
-#pragma unroll
-                        for (int kb = 0; kb < NKB; ++kb)
-                            mma_bf16(acc[m], raw_row8<D>(L.kraw, nb, kb, lane), raw_row8<D>(qr, mb, kb, lane));
-                    }
-                }
-            } else if (wave - 6 < NH) {
-                // the raw diagonal blocks K_b K_b^T (symmetric): lane (j', q) holds (K K^T)[16b + 4q + r][16b + j']
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    acc[b] = f4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int kb = 0; kb < NKB; ++kb) {
-                        const bf8_t x = raw_row8<D>(L.kraw, b, kb, lane);
-                        mma_bf16(acc[b], x, x);
-                    }
-                }
-            }
-        }
-        lds_barrier();  // B2
-
-        // ---- P2b ------------------------------------------------------------------------------
-        if (live) {
-            if (wave < 2) {
-                // zero halves: P above the diagonal (6 tiles), T above the diagonal (6 halves)
-                for (int hh = 0; hh < NH; ++hh) {
-                    for (int x = wave; x < 12; x += 2) {
-                        const f4_t z = {0.f, 0.f, 0.f, 0.f};
-                        if (x < 6) {
-                            const int nb = (x >= 3) ? 3 : (x >= 1) ? 2 : 1, mb = x - (nb - 1) * nb / 2;
-                            store_part<OP>(L.p[hh], mb * 2 + nb / 2, nb % 2, lane, z);
-                        } else {
-                            const int h = x - 6;
-                            const int f = h == 0 ? 0 : h <= 2 ? 1 : h <= 4 ? 3 : 5;
-                            const int part = (h == 0 || h == 2 || h == 4 || h == 5) ? 1 : 0;
-                            store_part<OP>(L.t[hh], f, part, lane, z);
-                        }
-                    }
-                }
-            } else if (wave < 6) {
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const int u = wave - 2 + 4 * m;
-                    if (u < 6) {
-                        const int bi = u >= 3 ? 3 : (u >= 1 ? 2 : 1), bj = u - bi * (bi - 1) / 2;
-#pragma unroll
-                        for (int hh = 0; hh < NH; ++hh) {
-                            const float r = L.ra[hh][16 * bi + li];
-                            const f4_t c = *reinterpret_cast<const f4_t*>(&L.cb[hh][16 * bj + 4 * lq]);
-                            f4_t x;
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) x[e] = acc[m][e] * __builtin_amdgcn_exp2f(r - c[e]);
-                            *reinterpret_cast<f4_t*>(&L.aw.s.a[hh][u][lane * 4]) = x;
-                        }
-                    } else {
-                        const int tl = u - 6;
-                        const int mb = (tl >= 6) ? 3 : (tl >= 3) ? 2 : (tl >= 1) ? 1 : 0, nb = tl - mb * (mb + 1) / 2;
-                        const int i = 16 * mb + li, c0 = 16 * nb + 4 * lq;
-#pragma unroll
-                        for (int hh = 0; hh < NH; ++hh) {
-                            const float r = L.rq[hh][i];
-                            const f4_t c = *reinterpret_cast<const f4_t*>(&L.cb[hh][c0]);
-                            f4_t x;
-#pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                x[e] = (mb > nb || c0 + e <= i) ? acc[m][e] * __builtin_amdgcn_exp2f(r - c[e]) : 0.f;
-                            store_part<OP>(L.p[hh], mb * 2 + nb / 2, nb % 2, lane, x);
-                        }
-                    }
-                }
-            } else if (wave - 6 < NH) {
-                const int hh = wave - 6;
-                // N_bb[j'][4q + r] (strictly lower) from the symmetric raw block, row-major
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const float r = L.ra[hh][16 * b + li];
-                    const f4_t c = *reinterpret_cast<const f4_t*>(&L.cb[hh][16 * b + 4 * lq]);
-                    f4_t x;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) x[e] = (4 * lq + e < li) ? acc[b][e] * __builtin_amdgcn_exp2f(r - c[e]) : 0.f;
-                    *reinterpret_cast<f4_t*>(&L.aw.s.nb[hh][b][li * XS + 4 * lq]) = x;
-                }
-                // Forward substitution (I + N) X = I: lane (b, j) computes column j of X_bb,
-                // X[i][j] = [i == j] - sum_{m < i} N[i][m] X[m][j].  N's rows are read as
-                // broadcasts (the 16 lanes of a block read the same address).
-                const int b = lq, j = li;
-                const float* Nb = L.aw.s.nb[hh][b];
-                float x[16];
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    float s = (i == j) ? 1.f : 0.f;
-#pragma unroll
-                    for (int m4 = 0; m4 < i; m4 += 4) {
-                        const f4_t nr = *reinterpret_cast<const f4_t*>(&Nb[i * XS + m4]);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (m4 + e < i) s = fmaf(-nr[e], x[m4 + e], s);
-                    }
-                    x[i] = s;
-                }
-                float* xd = L.aw.s.xd[hh][b];
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    *reinterpret_cast<f4_t*>(&xd[j * XS + 4 * c]) = f4_t{x[4 * c], x[4 * c + 1], x[4 * c + 2], x[4 * c + 3]};
-                // T's diagonal block: T[16b + i][16b + j] = X[i][j] beta_{16b + j}, element
-                // (j % 4) + 4 (b % 2) of lane ((j / 4), i) of fragment (b, b / 2)
-                const float bj = L.bt[hh][16 * b + j];
-                OP* tf = L.t[hh] + ((size_t)(2 * b + (b >> 1)) * WAVE + (j >> 2) * 16) * 8 + (j & 3) + 4 * (b & 1);
-#pragma unroll
-                for (int i = 0; i < 16; ++i) tf[i * 8] = (OP)(x[i] * bj);
-            }
-        }
-        lds_barrier();  // B3
-
-        // ---- P4: blocks of X below the diagonal, as T = X diag(beta) fragment halves ----------
-        // Matrices in accumulator layout (lane (j, q) holds M[4q + r][j]); mm16(xt, y, c) =
-        // c + X Y takes X^T and Y.  T's fragment half (block row a, block column b) is
-        // X_ab^T in this layout, times beta of the column.
-        if (live) {
-            const int hh = wave >> 2;
-            if (hh < NH) {
-                // roles by wave: head 0 waves 0..3 take roles 3, 2, 0, 1 and head 1 roles 2, 3, 1, 0,
-                // so the two waves that share a SIMD (w, w + 4) carry about equal matrix work
-                const int role = ((hh ? 0x0132 : 0x1023) >> (4 * (wave & 3))) & 0xf;
-                const f4_t z = {0.f, 0.f, 0.f, 0.f};
-                auto at = [&](int i, int j) { return *reinterpret_cast<const f4_t*>(&L.aw.s.a[hh][aslot(i, j)][lane * 4]); };
-                auto xa = [&](int b) { return *reinterpret_cast<const f4_t*>(&L.aw.s.xd[hh][b][li * XS + 4 * lq]); };
-                auto xt = [&](int b) {
-                    const float* x = L.aw.s.xd[hh][b];
-                    return f4_t{x[(4 * lq) * XS + li], x[(4 * lq + 1) * XS + li], x[(4 * lq + 2) * XS + li],
-                                x[(4 * lq + 3) * XS + li]};
-                };
-                auto put = [&](int a, int b, const f4_t& negxt) {  // negxt = -X_ab^T
-                    store_part<OP>(L.t[hh], 2 * a + (b >> 1), b & 1, lane,
-                                   -negxt * *reinterpret_cast<const f4_t*>(&L.bt[hh][16 * b + 4 * lq]));
-                };
-                if (role == 0) {  // X_10 = -X_11 A_10 X_00; X_20 = -X_22 (A_20 X_00 + A_21 X_10)
-                    const f4_t x00 = xa(0), x11t = xt(1);
-                    const f4_t r = mm16(at(1, 0), x00, z);
-                    put(1, 0, mm16(r, x11t, z));
-                    const f4_t x10 = -mm16(x11t, r, z);
-                    const f4_t y = mm16(at(2, 1), x10, mm16(at(2, 0), x00, z));
-                    put(2, 0, mm16(y, xt(2), z));
-                } else if (role == 1) {  // X_21 = -X_22 A_21 X_11; X_31 = -X_33 (A_31 X_11 + A_32 X_21)
-                    const f4_t x11 = xa(1), x22t = xt(2);
-                    const f4_t r = mm16(at(2, 1), x11, z);
-                    put(2, 1, mm16(r, x22t, z));
-                    const f4_t x21 = -mm16(x22t, r, z);
-                    const f4_t y = mm16(at(3, 2), x21, mm16(at(3, 1), x11, z));
-                    put(3, 1, mm16(y, xt(3), z));
-                } else if (role == 2) {  // X_32 = -X_33 A_32 X_22
-                    put(3, 2, mm16(mm16(at(3, 2), xa(2), z), xt(3), z));
-                } else {
-                    // X_30 = -(X_32 Y_00 + X_33 Y_10), Y_00 = A_20 X_00 + A_21 X_10,
-                    // Y_10 = A_30 X_00 + A_31 X_10 (the lower-left 32 x 32 block of X is
-                    // -X_lower-right (A_lower-left X_upper-left))
-                    const f4_t x00 = xa(0), x33t = xt(3);
-                    const f4_t x10 = -mm16(xt(1), mm16(at(1, 0), x00, z), z);
-                    const f4_t y00 = mm16(at(2, 1), x10, mm16(at(2, 0), x00, z));
-                    const f4_t y10 = mm16(at(3, 1), x10, mm16(at(3, 0), x00, z));
-                    const f4_t x32t = -mm16(mm16(at(3, 2), xa(2), z), x33t, z);
-                    put(3, 0, mm16(y10, x33t, mm16(y00, x32t, z)));
-                }
-            }
-        }
-        lds_barrier();  // B4: T complete; A, N and X no longer read
-
-        // ---- P5: Ut = T V and Ot = P Ut; -W ----------------------------------------------------
-        constexpr int WUNITS = NH * NKB * 4, UPW = WUNITS / PAIR_COMPUTE_WAVES > 0 ? WUNITS / PAIR_COMPUTE_WAVES : 1;
-        if (live) {
-            for (int u = wave; u < NH * (D / 16); u += PAIR_COMPUTE_WAVES) {
-                const int hh = u / (D / 16), nb = u % (D / 16);
-                char* rec = recs + ((size_t)slot * h_v + h0 + hh) * RC::BYTES;
-                OP* urec = reinterpret_cast<OP*>(rec + RC::U);
-                OP* orec = reinterpret_cast<OP*>(rec + RC::O);
-                Frag<OP> fv[2];
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    float x[8];
-                    raw_col<D>(L.vraw[hh], nb, kk, lane, x);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) frag_set(fv[kk], e, x[e]);
-                }
-                f4_t ut[4];
-#pragma unroll
-                for (int mb = 0; mb < 4; ++mb) {
-                    ut[mb] = f4_t{0, 0, 0, 0};
-                    mma(ut[mb], frag_stored<OP>(L.t[hh], mb * 2 + 0, lane), fv[0]);
-                    mma(ut[mb], frag_stored<OP>(L.t[hh], mb * 2 + 1, lane), fv[1]);
-                    store4<OP>(urec + ((size_t)(nb * 4 + mb) * WAVE + lane) * 4, ut[mb]);
-                }
-                const Frag<OP> fu0 = frag_from_acc<OP>(ut[0], ut[1]);
-                const Frag<OP> fu1 = frag_from_acc<OP>(ut[2], ut[3]);
-#pragma unroll
-                for (int mb = 0; mb < 4; ++mb) {
-                    f4_t ot = {0, 0, 0, 0};
-                    mma(ot, frag_stored<OP>(L.p[hh], mb * 2 + 0, lane), fu0);
-                    mma(ot, frag_stored<OP>(L.p[hh], mb * 2 + 1, lane), fu1);
-                    store4<OP>(orec + ((size_t)(nb * 4 + mb) * WAVE + lane) * 4, ot);
-                }
-            }
-            // W^T = (diag(gamma c) K)^T T^T: units (head, kb, tb) with d-blocks 2kb, 2kb + 1 and
-            // token block tb; a wave's units share (head, kb)
-            int cur = -1;
-            Frag<OP> aw[2][2];
-            for (int uu = 0; uu < UPW; ++uu) {
-                const int unit = wave * UPW + uu;
-                if (unit >= WUNITS) break;
-                const int hh = unit / (NKB * 4), kb = (unit / 4) % NKB, tb = unit % 4;
-                if (unit / 4 != cur) {
-                    cur = unit / 4;
-                    // the key record (normalised keys, fp16) is written once per k-head, by
-                    // the waves that hold the first v-head's (kb, token block 0) units
-                    const bool krec_w = pr == 0 && hh == 0 && unit % 4 == 0;
-                    OP* krec = reinterpret_cast<OP*>(krecs + ((size_t)slot * h_k + hk) * KeyRec<D, OP>::BYTES);
-#pragma unroll
-                    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-                        for (int kk = 0; kk < 2; ++kk) {
-                            float x[8];
-                            raw_col<D>(L.kraw, 2 * kb + s2, kk, lane, x);
-                            const f4_t s0 = *reinterpret_cast<const f4_t*>(&L.gck[hh][32 * kk + 4 * lq]);
-                            const f4_t s1 = *reinterpret_cast<const f4_t*>(&L.gck[hh][32 * kk + 16 + 4 * lq]);
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                frag_set(aw[s2][kk], e, x[e] * s0[e]);
-                                frag_set(aw[s2][kk], e + 4, x[e + 4] * s1[e]);
-                            }
-                            if (krec_w) {
-                                const f4_t c0 = *reinterpret_cast<const f4_t*>(&L.cn[0][32 * kk + 4 * lq]);
-                                const f4_t c1 = *reinterpret_cast<const f4_t*>(&L.cn[0][32 * kk + 16 + 4 * lq]);
-                                Frag<OP> fr;
-#pragma unroll
-                                for (int e = 0; e < 4; ++e) {
-                                    const int t0 = 32 * kk + 4 * lq + e, t1 = t0 + 16;
-                                    frag_set(fr, e, t0 < cnt ? x[e] * c0[e] : 0.f);
-                                    frag_set(fr, e + 4, t1 < cnt ? x[e + 4] * c1[e] : 0.f);
-                                }
-                                frag_store<OP>(krec, (2 * kb + s2) * 2 + kk, lane, fr);
-                            }
-                        }
-                }
-                char* rec = recs + ((size_t)slot * h_v + h0 + hh) * RC::BYTES;
-                OP* wrec = reinterpret_cast<OP*>(rec + RC::W);
-                f4_t a2[2];
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    a2[s2] = f4_t{0, 0, 0, 0};
-#pragma unroll
-                    for (int kk = 0; kk < 2; ++kk) mma(a2[s2], aw[s2][kk], frag_stored<OP>(L.t[hh], tb * 2 + kk, lane));
-                }
-                // lane (j, q): a2[s2][r] = W[token 16tb + j][d 16(2kb + s2) + 4q + r]
-                Frag<OP> fw;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) { frag_set(fw, e, -a2[0][e]); frag_set(fw, e + 4, -a2[1][e]); }
-                frag_store<OP>(wrec, tb * NKB + kb, lane, fw);
-                const int tok = 16 * tb + li;
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) store4<OP>(L.aw.w[hh] + tok * LK + 16 * (2 * kb + s2) + 4 * lq, -a2[s2]);
-            }
-        }
-        lds_barrier();  // B5: -W complete in LDS; k and v no longer read
-
-        // ---- P6: Qt^T = (diag(gamma c_q) Q)^T + (-W)^T P^T --------------------------------------
-        if (live) {
-            int cur = -1;
-            Frag<OP> aw[2][2];
-            for (int uu = 0; uu < UPW; ++uu) {
-                const int unit = wave * UPW + uu;
-                if (unit >= WUNITS) break;
-                const int hh = unit / (NKB * 4), kb = (unit / 4) % NKB, tb = unit % 4;
-                if (unit / 4 != cur) {
-                    cur = unit / 4;
-#pragma unroll
-                    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-                        for (int kk = 0; kk < 2; ++kk) aw[s2][kk] = frag_colmajor<OP>(L.aw.w[hh], LK, 2 * kb + s2, kk, lane);
-                }
-                char* rec = recs + ((size_t)slot * h_v + h0 + hh) * RC::BYTES;
-                OP* qrec = reinterpret_cast<OP*>(rec + RC::Q);
-                const int tok = 16 * tb + li;
-                const float gq = L.gcq[hh][tok];
-                f4_t a2[2];
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    // the raw queries of token tok at d = 16 (2kb + s2) + 4q .. + 3 (8 bytes)
-                    const int col = 16 * (2 * kb + s2) + 4 * lq;
-                    const uint2 w2 = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(qr) +
-                                                                     raw_unit<D>(tok, col >> 3) + ((col & 7) << 1));
-                    a2[s2][0] = __uint_as_float(w2.x << 16) * gq;
-                    a2[s2][1] = __uint_as_float(w2.x & 0xffff0000u) * gq;
-                    a2[s2][2] = __uint_as_float(w2.y << 16) * gq;
-                    a2[s2][3] = __uint_as_float(w2.y & 0xffff0000u) * gq;
-#pragma unroll
-                    for (int kk = 0; kk < 2; ++kk) mma(a2[s2], aw[s2][kk], frag_stored<OP>(L.p[hh], tb * 2 + kk, lane));
-                }
-                Frag<OP> fq;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) { frag_set(fq, e, a2[0][e]); frag_set(fq, e + 4, a2[1][e]); }
-                frag_store<OP>(qrec, tb * NKB + kb, lane, fq);
-            }
-        }
-        lds_barrier();  // B6: LDS is reused by the next item
-    }
-}
-
 // ---- sequential phase -------------------------------------------------------------------
 // One workgroup owns RS rows (16 or 32) of one (sequence, v-head) state, so a
 // d-wide head has d/RS workgroups.  The rows of S evolve independently.  A
@@ -1702,14 +996,25 @@ __global__ __launch_bounds__(SCAN_THREADS) void chunk_scan_kernel(
 }
 
 // ---- host launchers ----------------------------------------------------------------------
+size_t tp_record_bytes();
+hipError_t launch_prep_bf16(int d, const void* q, const void* k, const float* g, const float* beta,
+                            const void* info, const int32_t* slot_seq, int slots, int T, int h_k, int h_v,
+                            int l2norm, float scale, void* recs, hipStream_t stream);
+hipError_t launch_scan_bf16(int d, bool out_bf16, int rows, int mode, const void* q, const void* k, const void* v,
+                            const void* recs, const void* info, const float* s_in, float* s_out, void* out, void* sink,
+                            int units, int T, int h_k, int h_v, hipStream_t stream);
+
+// Workspace record sizes: bf16 inputs use one record per (block slot, v-head)
+// (prefill_bf16.hip); fp32 inputs one per (block slot, v-head) plus a key
+// record per (block slot, k-head).
 size_t prefill_record_bytes(int d, bool in_bf16) {
-    if (d == 128) return in_bf16 ? Rec<128, _Float16>::BYTES : Rec<128, float>::BYTES;
-    return in_bf16 ? Rec<64, _Float16>::BYTES : Rec<64, float>::BYTES;
+    if (in_bf16) return tp_record_bytes();
+    return d == 128 ? Rec<128, float>::BYTES : Rec<64, float>::BYTES;
 }
 
 size_t prefill_key_record_bytes(int d, bool in_bf16) {
-    if (d == 128) return in_bf16 ? KeyRec<128, _Float16>::BYTES : KeyRec<128, float>::BYTES;
-    return in_bf16 ? KeyRec<64, _Float16>::BYTES : KeyRec<64, float>::BYTES;
+    if (in_bf16) return 0;
+    return d == 128 ? KeyRec<128, float>::BYTES : KeyRec<64, float>::BYTES;
 }
 
 hipError_t launch_plan(const int32_t* cu, int N, int T, int max_slots, void* info, int32_t* slot_seq,
@@ -1730,27 +1035,6 @@ int compute_units() {
         cached[dev] = n;
     }
     return cached[dev];
-}
-
-template <int D, int NH>
-static hipError_t launch_prep_pair_t(const void* q, const void* k, const void* v, const float* g,
-                                     const float* beta, const void* info, const int32_t* slot_seq,
-                                     int slots, int T, int h_k, int h_v, int l2norm, float scale,
-                                     char* recs, char* krecs, hipStream_t stream) {
-    constexpr size_t lds = pair_lds_bytes<D, NH>();
-    static_assert(lds <= 160 * 1024, "chunk_prep_pair LDS budget");
-    auto kern = chunk_prep_pair_kernel<D, NH>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    // one workgroup per compute unit, each a contiguous run of items
-    const int items = slots * h_k * (h_v / h_k / NH), resident = compute_units();
-    const int per = (items + resident - 1) / resident;
-    const int grid = (items + per - 1) / per;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(PAIR_THREADS), lds, stream, q, k, v, g, beta,
-                       reinterpret_cast<const SeqInfo*>(info), slot_seq, T, h_k, h_v, l2norm, scale, recs, krecs,
-                       slots, per);
-    return hipGetLastError();
 }
 
 template <int D, typename OP, bool IB>
@@ -1779,17 +1063,11 @@ hipError_t launch_prep(int d, bool in_bf16, const void* q, const void* k, const 
                        const float* g, const float* beta, const void* info, const int32_t* slot_seq,
                        int slots, int T, int h_k, int h_v, int l2norm, float scale, void* recs,
                        void* krecs, hipStream_t stream) {
-    char* r = reinterpret_cast<char*>(recs);
-    char* kr = reinterpret_cast<char*>(krecs);
-    const bool pair = (h_v / h_k) % 2 == 0;
-    if (d == 128 && in_bf16)
-        return pair ? launch_prep_pair_t<128, 2>(q, k, v, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, kr, stream)
-                    : launch_prep_pair_t<128, 1>(q, k, v, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, kr, stream);
-    if (d == 64 && in_bf16)
-        return pair ? launch_prep_pair_t<64, 2>(q, k, v, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, kr, stream)
-                    : launch_prep_pair_t<64, 1>(q, k, v, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, kr, stream);
-    if (d == 64 && !in_bf16)
-        return launch_prep_t<64, float, false>(q, k, v, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, kr, stream);
+    if (in_bf16)
+        return launch_prep_bf16(d, q, k, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, recs, stream);
+    if (d == 64)
+        return launch_prep_t<64, float, false>(q, k, v, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale,
+                                               reinterpret_cast<char*>(recs), reinterpret_cast<char*>(krecs), stream);
     return hipErrorInvalidValue;
 }
 
@@ -1806,28 +1084,26 @@ static hipError_t launch_scan_t(const void* recs, const void* krecs, const void*
     return hipGetLastError();
 }
 
-int scan_rows_per_workgroup(int d, int units) {
-    // GDN_SCAN_ROWS=16 or 32 fixes the choice (tuning and tests).
-    if (const char* e = getenv("GDN_SCAN_ROWS")) {
-        const int v = atoi(e);
-        if (v == 16 || v == 32) return v;
-    }
-    // 16-row slices double the workgroups (each still copies the whole -W,
-    // Qt, K^T record part), which pays while 32-row slices leave compute
-    // units idle.
+// Rows of a state per scan workgroup: `requested` (16 or 32), or for 0 the
+// default: 16-row slices double the workgroups (each still copies the whole
+// shared part of a block), which pays while 32-row slices leave compute units
+// idle.
+int scan_rows_per_workgroup(int d, int units, int requested) {
+    if (requested == 16 || requested == 32) return requested;
     return (long long)units * (d / 32) < compute_units() ? 16 : 32;
 }
 
-hipError_t launch_scan(int d, bool in_bf16, bool out_bf16, const void* recs, const void* krecs, const void* info,
-                       const float* s_in, float* s_out, void* out, void* sink, int units, int T, int h_k, int h_v,
-                       hipStream_t stream) {
-    const int rs = scan_rows_per_workgroup(d, units);
+hipError_t launch_scan(int d, bool in_bf16, bool out_bf16, int rows, const void* q, const void* k, const void* v,
+                       const void* recs, const void* krecs, const void* info, const float* s_in, float* s_out,
+                       void* out, void* sink, int units, int T, int h_k, int h_v, hipStream_t stream) {
+    const int rs = scan_rows_per_workgroup(d, units, rows);
+    if (in_bf16)
+        return launch_scan_bf16(d, out_bf16, rs, 0, q, k, v, recs, info, s_in, s_out, out, sink, units, T, h_k, h_v,
+                                stream);
 #define GDN_SCAN(D, OP, IB, OB)                                                                          \
     if (d == D && in_bf16 == IB && out_bf16 == OB)                                                       \
         return rs == 16 ? launch_scan_t<D, OP, OB, 16>(recs, krecs, info, s_in, s_out, out, sink, units, T, h_k, h_v, stream) \
                         : launch_scan_t<D, OP, OB, 32>(recs, krecs, info, s_in, s_out, out, sink, units, T, h_k, h_v, stream);
-    GDN_SCAN(128, _Float16, true, true) GDN_SCAN(128, _Float16, true, false)
-    GDN_SCAN(64, _Float16, true, true) GDN_SCAN(64, _Float16, true, false)
     GDN_SCAN(64, float, false, true) GDN_SCAN(64, float, false, false)
 #undef GDN_SCAN
     return hipErrorInvalidValue;
@@ -1836,10 +1112,12 @@ hipError_t launch_scan(int d, bool in_bf16, bool out_bf16, const void* recs, con
 // ---- two-level scan of one long sequence -------------------------------------------------
 // The state map of a run of blocks is affine, S_end = S_start R + B (section
 // "Keep the recurrent state on chip" carries S across pieces of a prompt the
-// same way).  Split into P segments, each segment's R and B come from two
-// state-carrying passes run in parallel (MODE 2 from the identity, MODE 1 from
-// zero), the segments' start states from a short sequential composition, and
-// the outputs from the scan rerun on all segments in parallel.
+// same way).  Split into P segments, each segment's R and B come from one
+// state-carrying pass over all segments in parallel (the transition scan: half
+// of its units start from the identity without the value term and give R, the
+// other half start from zero and give B), the segments' start states from a
+// short sequential composition, and the outputs from the scan rerun on all
+// segments in parallel.
 
 __global__ void segment_info_kernel(SeqInfo* __restrict__ info, int P, int sb, int T) {
     const int s = blockIdx.x * blockDim.x + threadIdx.x;
@@ -1912,17 +1190,18 @@ hipError_t launch_compose(int d, const float* state_in, const float* R, const fl
 
 // Both state-map parts of every segment in `info` (MODE 1): units = 2 x
 // (segments x v-heads); state_out receives B for the first half, R for the second.
-hipError_t launch_scan_transition(int d, bool in_bf16, const void* recs, const void* krecs, const void* info,
-                                  float* s_out, void* sink, int units, int T, int h_k, int h_v, hipStream_t stream) {
-    const int rs = scan_rows_per_workgroup(d, units);
-#define GDN_TR(D, OP, IB)                                                                                        \
-    if (d == D && in_bf16 == IB)                                                                                 \
-        return rs == 16 ? launch_scan_t<D, OP, false, 16, 1>(recs, krecs, info, nullptr, s_out, nullptr, sink,    \
-                                                              units, T, h_k, h_v, stream)                        \
-                        : launch_scan_t<D, OP, false, 32, 1>(recs, krecs, info, nullptr, s_out, nullptr, sink,    \
-                                                              units, T, h_k, h_v, stream);
-    GDN_TR(128, _Float16, true) GDN_TR(64, _Float16, true) GDN_TR(64, float, false)
-#undef GDN_TR
+hipError_t launch_scan_transition(int d, bool in_bf16, int rows, const void* q, const void* k, const void* v,
+                                  const void* recs, const void* krecs, const void* info, float* s_out, void* sink,
+                                  int units, int T, int h_k, int h_v, hipStream_t stream) {
+    const int rs = scan_rows_per_workgroup(d, units, rows);
+    if (in_bf16)
+        return launch_scan_bf16(d, false, rs, 1, q, k, v, recs, info, nullptr, s_out, nullptr, sink, units, T, h_k,
+                                h_v, stream);
+    if (d == 64)
+        return rs == 16 ? launch_scan_t<64, float, false, 16, 1>(recs, krecs, info, nullptr, s_out, nullptr, sink,
+                                                                 units, T, h_k, h_v, stream)
+                        : launch_scan_t<64, float, false, 32, 1>(recs, krecs, info, nullptr, s_out, nullptr, sink,
+                                                                 units, T, h_k, h_v, stream);
     return hipErrorInvalidValue;
 }
 

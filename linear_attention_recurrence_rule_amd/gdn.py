@@ -69,7 +69,7 @@ def lib():
             L.gdn_prefill.restype = ctypes.c_int
             L.gdn_prefill_prepare.argtypes = [dp, vp, vp, vp, vp, vp, vp, ctypes.c_int32, vp, sz, vp]
             L.gdn_prefill_prepare.restype = ctypes.c_int
-            L.gdn_prefill_scan.argtypes = [dp, vp, vp, vp, vp, ctypes.c_int32, vp, sz, vp]
+            L.gdn_prefill_scan.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32, vp, sz, vp]
             L.gdn_prefill_scan.restype = ctypes.c_int
             L.gdn_prefill_segmented_workspace_bytes.argtypes = [dp, ctypes.c_int32, ctypes.c_int64]
             L.gdn_prefill_segmented_workspace_bytes.restype = sz
@@ -157,11 +157,11 @@ def gdn_prefill_prepare(desc, q, k, v, g, beta, cu_seqlens, chunk, workspace, wo
                                      _stream(stream)))
 
 
-def gdn_prefill_scan(desc, state_in, out, state_out, cu_seqlens, chunk, workspace, workspace_bytes,
+def gdn_prefill_scan(desc, q, k, v, state_in, out, state_out, cu_seqlens, chunk, workspace, workspace_bytes,
                      stream=None):
-    _check(lib().gdn_prefill_scan(ctypes.byref(desc), _ptr(state_in), _ptr(out), _ptr(state_out),
-                                  _ptr(cu_seqlens), int(chunk), _ptr(workspace), int(workspace_bytes),
-                                  _stream(stream)))
+    _check(lib().gdn_prefill_scan(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(state_in), _ptr(out),
+                                  _ptr(state_out), _ptr(cu_seqlens), int(chunk), _ptr(workspace),
+                                  int(workspace_bytes), _stream(stream)))
 
 
 def gdn_prefill_segmented_workspace_bytes(desc: GdnDesc, segment_tokens: int, chunk: int = CHUNK) -> int:

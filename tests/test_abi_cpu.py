@@ -65,16 +65,16 @@ def desc(**kw):
 
 
 def test_workspace_bytes(L):
-    # per (block, v-head): -W, Qt, Ut, Ot in fp16 + s_t / gamma_n (512 B);
-    # per (block, k-head): K^T in fp16.  64 blocks x (32 v-heads, 16 k-heads).
-    rec = 4 * 64 * 128 * 2 + 256 + 256
-    key = 64 * 128 * 2
+    # bf16 inputs, per (block, v-head): the six non-zero 1 KiB fragments of T and
+    # of P (fp16) and 1 KiB of per-token factors; no key records.
+    # 64 blocks x 32 v-heads.
+    rec = 2 * 6 * 1024 + 1024
     plan = (1024 + 1 * 16 + 64 * 4 + 255) // 256 * 256
-    assert gdn.gdn_prefill_workspace_bytes(desc()) == plan + 64 * (32 * rec + 16 * key)
+    assert gdn.gdn_prefill_workspace_bytes(desc()) == plan + 64 * 32 * rec
     # packed sequences: at most T/64 + N blocks in total
     n = gdn.gdn_prefill_workspace_bytes(desc(num_seqs=16, total_tokens=1000))
     slots = (1000 + 16 * 63) // 64
-    assert n == (1024 + 16 * 16 + slots * 4 + 255) // 256 * 256 + slots * (32 * rec + 16 * key)
+    assert n == (1024 + 16 * 16 + slots * 4 + 255) // 256 * 256 + slots * 32 * rec
     # fp32 inputs keep fp32 operands
     rec64f = 4 * 64 * 64 * 4 + 512
     key64f = 64 * 64 * 4
@@ -152,11 +152,16 @@ def test_prefill_phases_reject_bad_arguments(L):
                                    FAKE + 4 << 32, None, 64, ws, need - 1, None) == gdn.GDN_ERR_WORKSPACE
     assert lib.gdn_prefill_prepare(by(desc(d=48)), FAKE, FAKE + 1 << 32, FAKE + 2 << 32, FAKE + 3 << 32,
                                    FAKE + 4 << 32, None, 64, ws, need, None) == gdn.GDN_ERR_UNSUPPORTED
-    # scan: out required, aliasing checked
-    assert lib.gdn_prefill_scan(by(d), None, None, None, None, 64, ws, need, None) == gdn.GDN_ERR_INVALID_ARGUMENT
-    assert lib.gdn_prefill_scan(by(d), None, ws + 8, None, None, 64, ws, need, None) == gdn.GDN_ERR_INVALID_ARGUMENT
-    assert lib.gdn_prefill_scan(by(desc(num_seqs=2)), None, FAKE, None, None, 64, ws, need, None) == \
+    # scan: q, k, v and out required, aliasing checked
+    qkv = (FAKE, FAKE + 1 << 32, FAKE + 2 << 32)
+    assert lib.gdn_prefill_scan(by(d), *qkv, None, None, None, None, 64, ws, need, None) == \
         gdn.GDN_ERR_INVALID_ARGUMENT
+    assert lib.gdn_prefill_scan(by(d), None, qkv[1], qkv[2], None, FAKE + 5 << 32, None, None, 64, ws, need,
+                                None) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert lib.gdn_prefill_scan(by(d), *qkv, None, ws + 8, None, None, 64, ws, need, None) == \
+        gdn.GDN_ERR_INVALID_ARGUMENT
+    assert lib.gdn_prefill_scan(by(desc(num_seqs=2)), *qkv, None, FAKE + 5 << 32, None, None, 64, ws, need,
+                                None) == gdn.GDN_ERR_INVALID_ARGUMENT
 
 
 @fake_pointers
@@ -241,9 +246,8 @@ def test_two_level_workspace_bytes(L):
     assert gdn.gdn_prefill_two_level_workspace_bytes(desc(total_tokens=4096), 1) == one
     # 64 blocks in 8 segments of 8: single-sequence records, a 256-byte segment table, then
     # R and B for 7 segments and start and end states for 8 (32 v-heads, d = 128, fp32)
-    rec = 4 * 64 * 128 * 2 + 512
-    key = 64 * 128 * 2
-    base = 1024 + 64 * (32 * rec + 16 * key)
+    rec = 2 * 6 * 1024 + 1024
+    base = 1024 + 64 * 32 * rec
     st = 32 * 128 * 128 * 4
     assert gdn.gdn_prefill_two_level_workspace_bytes(desc(total_tokens=4096), 8) == base + 256 + (7 + 7 + 8 + 8) * st
     # more segments than blocks: one segment per block
