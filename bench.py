@@ -394,15 +394,15 @@ def prefill_configs(L, gdn, inputs, to_dev, torch, np, dev, with_cpu=True):
         us = timed(call, reps)
         # gdn_prefill may run a long single sequence as segments; the one-pass time
         # (prepare + scan over all blocks, as split below) is reported beside it
-        prev = os.environ.get("GDN_PREFILL_SEGMENT_TOKENS")
-        os.environ["GDN_PREFILL_SEGMENT_TOKENS"] = "0"
-        try:
-            us_one_pass = timed(call, reps)
-        finally:
-            if prev is None:
-                os.environ.pop("GDN_PREFILL_SEGMENT_TOKENS", None)
-            else:
-                os.environ["GDN_PREFILL_SEGMENT_TOKENS"] = prev
+        one_pass = gdn.GdnPrefillOptions(0, 0, -1)
+
+        def call_one_pass():
+            st = L.gdn_prefill_ex(dref, P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[8], 64,
+                                  ctypes.byref(one_pass), ws.data_ptr(), wsb, sp)
+            if st:
+                raise gdn.GdnError(st, gdn.last_error())
+
+        us_one_pass = timed(call_one_pass, reps)
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
         for e in evs:
             e[0].record(stream)

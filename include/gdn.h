@@ -47,11 +47,14 @@
  *   - qk_l2norm = 1 normalises q and k per (token, k-head) inside the kernel,
  *     x / sqrt(sum x^2 + 1e-6).  The query is then multiplied by `scale`.
  *   - Supported shapes: d_k = d_v in {64, 128}; h_v % h_k == 0; chunk = 64.
- *   - Numerics: bf16 inputs feed fp16 matrix-core operands inside the prefill.
- *     Normalised q/k, decays and triangular factors are exact or bounded by 1.
- *     Values, states and value-sized intermediates (|v|, |S|, and |S k| for a
- *     unit key) must stay below 2^14 in magnitude.  fp32 inputs use fp32
- *     matrix-core operands throughout.
+ *   - Numerics: bf16-input prefill runs the state-side products (K S^T, Q S^T
+ *     and the state update) on bf16 matrix cores with the state and the
+ *     update's operand split into bf16 high and low parts (fp32 range, about
+ *     16 significant bits).  The two token-by-token contractions (U = T R and
+ *     P U, with R = v - decayed (S k)) take fp16 operands: |v - S k| and |U|
+ *     must stay below 65504.  Beyond that the results become infinite or NaN
+ *     and the prefill status word reports GDN_PREFILL_STATUS_NONFINITE.
+ *     fp32 inputs use fp32 matrix-core operands throughout.
  *   - Errors: every scalar and pointer check runs on the host before anything
  *     is enqueued.  A failed check returns GDN_ERR_INVALID_ARGUMENT or
  *     GDN_ERR_UNSUPPORTED, and the call then has no effect.  A failed launch
@@ -122,10 +125,14 @@ size_t gdn_prefill_workspace_bytes(const gdn_desc *desc, int32_t chunk);
  * A single sequence (num_seqs == 1, no cu_seqlens) whose block records would
  * not stay in the last-level cache between the two kernels is run as
  * consecutive segments of whole blocks (as gdn_prefill_segmented, within the
- * same workspace).  The results are bit-identical to one pass, and 9-22%
- * faster from 8K tokens on at 32 v-heads, d = 128.  The environment variable
- * GDN_PREFILL_SEGMENT_TOKENS=0 turns this off, and a positive multiple of 64
- * fixes the segment length.
+ * same workspace).  The results are bit-identical to one pass.
+ * gdn_prefill_ex chooses the segment length (or one pass) explicitly.
+ *
+ * Status word.  Every prefill call leaves a 32-bit word of
+ * gdn_prefill_status_flag bits in the workspace, at byte offset
+ * gdn_prefill_status_offset().  The call's first kernel resets it, and the
+ * last one to finish has set its bits when the stream reaches the end of the
+ * call; the caller reads it after that (the library does not synchronise).
  */
 gdn_status gdn_prefill(const gdn_desc *desc,
                        const void *q, const void *k, const void *v,
@@ -135,6 +142,66 @@ gdn_status gdn_prefill(const gdn_desc *desc,
                        const int32_t *cu_seqlens, int32_t chunk,
                        void *workspace, size_t workspace_bytes,
                        void *stream);
+
+/*
+ * gdn_prefill with explicit tuning choices.  options == NULL is gdn_prefill.
+ *
+ *   scan_rows       rows of a state per scan workgroup: 0 for the default, or
+ *                   16 or 32 (the results are bit-identical: rows evolve
+ *                   independently and each row's arithmetic is the same).
+ *   reserved        must be 0.
+ *   segment_tokens  a single sequence (num_seqs == 1, no cu_seqlens) only:
+ *                   0 chooses as gdn_prefill does, -1 runs one pass, and a
+ *                   positive multiple of chunk runs segments of that length
+ *                   within the same workspace (bit-identical to one pass).
+ *                   Other callers must pass 0 or -1.
+ *
+ * Errors: those of gdn_prefill, plus GDN_ERR_INVALID_ARGUMENT for a
+ * scan_rows other than 0, 16 or 32, a non-zero reserved field, or a negative
+ * segment length other than -1; GDN_ERR_UNSUPPORTED for a positive segment
+ * length that is not a multiple of chunk or is given with packed sequences;
+ * GDN_ERR_WORKSPACE when the segments need more workspace than was given.
+ */
+typedef struct {
+    int32_t scan_rows;
+    int32_t reserved;
+    int64_t segment_tokens;
+} gdn_prefill_options;
+
+gdn_status gdn_prefill_ex(const gdn_desc *desc,
+                          const void *q, const void *k, const void *v,
+                          const float *g, const float *beta,
+                          const float *state_in,
+                          void *out, float *state_out,
+                          const int32_t *cu_seqlens, int32_t chunk,
+                          const gdn_prefill_options *options,
+                          void *workspace, size_t workspace_bytes,
+                          void *stream);
+
+/*
+ * Bits of the prefill status word.
+ *   GDN_PREFILL_STATUS_CU_SEQLENS_CLAMPED  cu_seqlens broke its contract (did
+ *       not start at 0, decreased, left [0, total_tokens] or did not end at
+ *       total_tokens) and was clamped; the results are then unspecified.
+ *   GDN_PREFILL_STATUS_NONFINITE  an output or a final state came out
+ *       infinite or NaN: an input was, or a bf16-input call went beyond the
+ *       fp16 range of its matrix-core operands (see Numerics above).
+ */
+typedef enum {
+    GDN_PREFILL_STATUS_CU_SEQLENS_CLAMPED = 1,
+    GDN_PREFILL_STATUS_NONFINITE = 2
+} gdn_prefill_status_flag;
+
+/*
+ * Byte offset of the status word inside the workspace of gdn_prefill,
+ * gdn_prefill_ex, gdn_prefill_prepare/gdn_prefill_scan, gdn_prefill_segmented
+ * and gdn_prefill_two_level (the same offset for all; 4-byte aligned).
+ * gdn_prefill_prepare resets the word and gdn_prefill_scan adds to it; each
+ * of the other calls resets it once and then adds the bits of all its
+ * kernels.  Returns 0 (never a valid offset) and sets gdn_last_error() for an
+ * invalid descriptor or chunk.
+ */
+size_t gdn_prefill_status_offset(const gdn_desc *desc, int32_t chunk);
 
 /*
  * The two phases of gdn_prefill, for callers that schedule or time them

@@ -30,14 +30,16 @@ hipError_t launch_direct(int d, bool in_bf16, bool out_bf16, const void* q, cons
                          void* out, int units, int T, int h_k, int h_v, int l2norm, float scale, int fuse, const float* norm_w,
                          float norm_eps, hipStream_t stream);
 hipError_t launch_plan(const int32_t* cu, int N, int T, int max_slots, void* info, int32_t* slot_seq,
-                       hipStream_t stream);
+                       unsigned* status, hipStream_t stream);
+hipError_t launch_status_reset(unsigned* status, hipStream_t stream);
 hipError_t launch_prep(int d, bool in_bf16, const void* q, const void* k, const void* v,
                        const float* g, const float* beta, const void* info, const int32_t* slot_seq,
                        int slots, int T, int h_k, int h_v, int l2norm, float scale, void* recs,
-                       void* krecs, hipStream_t stream);
+                       void* krecs, unsigned* clear_status, hipStream_t stream);
 hipError_t launch_scan(int d, bool in_bf16, bool out_bf16, int rows, const void* q, const void* k, const void* v,
                        const void* recs, const void* krecs, const void* info, const float* s_in, float* s_out,
-                       void* out, void* sink, int units, int T, int h_k, int h_v, hipStream_t stream);
+                       void* out, void* sink, int units, int T, int h_k, int h_v, unsigned* status,
+                       hipStream_t stream);
 }  // namespace gdn
 
 namespace {
@@ -98,10 +100,11 @@ int64_t max_slots(const gdn_desc* d, bool varlen) {
     return (T + (int64_t)d->num_seqs * (kChunk - 1)) / kChunk;
 }
 
-// Workspace: [sink 1 KiB][plan: per-sequence info, slot -> sequence]
+// Workspace: [sink 1 KiB][status word, 256 B][plan: per-sequence info, slot -> sequence]
 //            [records per (block slot, v-head)][key records per (block slot, k-head)]
 // The sink absorbs the chunk scan's stores for rows past the end of a block.
 constexpr size_t kSinkBytes = 1024;
+constexpr size_t kStatusOff = kSinkBytes, kStatusBytes = 256;
 
 struct WsLayout {
     size_t sink_off, info_off, slot_off, rec_off, key_off, total;
@@ -112,7 +115,7 @@ WsLayout ws_layout(const gdn_desc* d, bool varlen) {
     WsLayout w{};
     w.slots = max_slots(d, varlen);
     w.sink_off = 0;
-    size_t plan = kSinkBytes;
+    size_t plan = kStatusOff + kStatusBytes;
     if (varlen) {
         w.info_off = plan;
         w.slot_off = plan + (size_t)d->num_seqs * 16;
@@ -167,16 +170,10 @@ int cu_count() {
     return cus;
 }
 
-int env_int(const char* name, int dflt) {
-    const char* e = getenv(name);
-    const int v = e ? atoi(e) : 0;
-    return v > 0 ? v : dflt;
-}
-
-// Decode workgroups: a few per compute unit, each walking several (sequence,
+// Decode workgroups: two per compute unit, each walking several (sequence,
 // v-head) units so that one unit's loads overlap the previous unit's work.
 int decode_grid(int units) {
-    const int grid = cu_count() * env_int("GDN_DECODE_WG_PER_CU", 2);
+    const int grid = cu_count() * 2;
     return grid < units ? grid : units;
 }
 
@@ -252,10 +249,12 @@ enum Phase { kPrepare = 1, kScan = 2, kBoth = 3 };
 
 // Validation shared by gdn_prefill and its two phases.  Pointers that a phase
 // does not use are passed as NULL and not checked.
+// clear_status: the prepare phase resets the status word (false for the
+// segments after the first of a segmented call, which add to it).
 gdn_status prefill_call(Phase phase, const gdn_desc* desc, const void* q, const void* k, const void* v,
                         const float* g, const float* beta, const float* state_in, void* out,
                         float* state_out, const int32_t* cu_seqlens, int32_t chunk, void* workspace,
-                        size_t workspace_bytes, void* stream, int scan_rows = 0) {
+                        size_t workspace_bytes, void* stream, int scan_rows = 0, bool clear_status = true) {
     g_err[0] = 0;
     gdn_status st = check_desc(desc, true);
     if (st != GDN_OK) return st;
@@ -298,21 +297,32 @@ gdn_status prefill_call(Phase phase, const gdn_desc* desc, const void* q, const 
     char* wsb = reinterpret_cast<char*>(workspace);
     void* info = varlen ? wsb + ws.info_off : nullptr;
     int32_t* slot_seq = varlen ? reinterpret_cast<int32_t*>(wsb + ws.slot_off) : nullptr;
+    unsigned* status = reinterpret_cast<unsigned*>(wsb + kStatusOff);
     hipError_t e = hipSuccess;
     if (phase & kPrepare) {
+        // the status word is reset by the plan (which may set the clamped bit) or else by chunk_prep
+        bool reset = !clear_status;
         if (varlen) {
-            e = gdn::launch_plan(cu_seqlens, N, (int)T, (int)ws.slots, info, slot_seq, s);
+            e = gdn::launch_plan(cu_seqlens, N, (int)T, (int)ws.slots, info, slot_seq, clear_status ? status : nullptr,
+                                 s);
             if (e != hipSuccess) return fail(GDN_ERR_HIP, "plan launch: %s", hipGetErrorString(e));
+            reset = true;
         }
         if (ws.slots > 0 && T > 0) {  // chunk_prep clamps token indices into [0, T)
             e = gdn::launch_prep(d, in_bf16, q, k, v, g, beta, info, slot_seq, (int)ws.slots, (int)T, hk, hv,
-                                 desc->qk_l2norm, desc->scale, wsb + ws.rec_off, wsb + ws.key_off, s);
+                                 desc->qk_l2norm, desc->scale, wsb + ws.rec_off, wsb + ws.key_off,
+                                 reset ? nullptr : status, s);
             if (e != hipSuccess) return fail(GDN_ERR_HIP, "chunk_prep launch: %s", hipGetErrorString(e));
+            reset = true;
+        }
+        if (!reset) {  // no kernel to reset it: an empty problem (a kernel, not a memset node, so capturable)
+            e = gdn::launch_status_reset(status, s);
+            if (e != hipSuccess) return fail(GDN_ERR_HIP, "status reset: %s", hipGetErrorString(e));
         }
     }
     if ((phase & kScan) && (state_out || T > 0)) {
         e = gdn::launch_scan(d, in_bf16, out_bf16, scan_rows, q, k, v, wsb + ws.rec_off, wsb + ws.key_off, info,
-                             state_in, state_out, out, wsb + ws.sink_off, N * hv, (int)T, hk, hv, s);
+                             state_in, state_out, out, wsb + ws.sink_off, N * hv, (int)T, hk, hv, status, s);
         if (e != hipSuccess) return fail(GDN_ERR_HIP, "chunk_scan launch: %s", hipGetErrorString(e));
     }
     return GDN_OK;
@@ -358,20 +368,14 @@ gdn_status two_level_plan(const gdn_desc* desc, int32_t chunk, int32_t segments,
 // gdn_prefill runs a long single sequence as consecutive segments of whole
 // blocks, so that each segment's block records (written by chunk_prep, read
 // by chunk_scan) stay in the last-level cache (256 MiB on MI355X) between the
-// two kernels instead of going out to HBM and back.  Measured at 32 v-heads,
-// d = 128: 9-15% faster from 8K to 128K tokens.  Results are bit-identical to
-// a single call: the block grid is the same, and the fp32 state passes
+// two kernels instead of going out to HBM and back.  Results are bit-identical
+// to a single call: the block grid is the same, and the fp32 state passes
 // between segments unrounded.  Returns the segment length in tokens, or 0 to
-// run one call.  GDN_PREFILL_SEGMENT_TOKENS=0 turns this off, and a positive
-// multiple of 64 fixes the length (tuning and tests).
+// run one call.
 constexpr size_t kSegmentRecordBudget = (size_t)146 << 20;
 
 int64_t auto_segment_tokens(const gdn_desc* d) {
     if (d->num_seqs != 1 || d->total_tokens <= 0) return 0;
-    if (const char* e = getenv("GDN_PREFILL_SEGMENT_TOKENS")) {
-        const long long v = atoll(e);
-        return (v > 0 && v % kChunk == 0) ? (int64_t)v : 0;
-    }
     const bool bf16 = d->io_dtype == GDN_BF16;
     const size_t per_block = (size_t)d->h_v * gdn::prefill_record_bytes(d->d_k, bf16) +
                              (size_t)d->h_k * gdn::prefill_key_record_bytes(d->d_k, bf16);
@@ -399,6 +403,12 @@ gdn_status segment_plan(const gdn_desc* desc, int32_t chunk, int64_t seg, gdn_de
     *need = *state_off + (size_t)desc->h_v * desc->d_k * desc->d_k * 4;
     return GDN_OK;
 }
+
+// The segmented prefill (defined with gdn_prefill_segmented), shared with gdn_prefill_ex.
+gdn_status segmented_call(const gdn_desc* desc, const void* q, const void* k, const void* v, const float* g,
+                          const float* beta, const float* state_in, void* out, float* state_out, int32_t chunk,
+                          int64_t segment_tokens, void* workspace, size_t workspace_bytes, void* stream,
+                          int scan_rows);
 
 // Shared by gdn_decode_step (slots == NULL: sequence n uses state n),
 // gdn_decode_step_slots and gdn_decode_step_ex (fuse flags, norm weight and eps).
@@ -434,26 +444,64 @@ gdn_status decode_call(const gdn_desc* desc, const void* q, const void* k, const
 
 extern "C" {
 
-gdn_status gdn_prefill(const gdn_desc* desc, const void* q, const void* k, const void* v,
-                       const float* g, const float* beta, const float* state_in, void* out,
-                       float* state_out, const int32_t* cu_seqlens, int32_t chunk, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+gdn_status gdn_prefill_ex(const gdn_desc* desc, const void* q, const void* k, const void* v,
+                          const float* g, const float* beta, const float* state_in, void* out,
+                          float* state_out, const int32_t* cu_seqlens, int32_t chunk,
+                          const gdn_prefill_options* options, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+    g_err[0] = 0;
+    gdn_prefill_options opt = {0, 0, 0};
+    if (options) opt = *options;
+    if (opt.scan_rows != 0 && opt.scan_rows != 16 && opt.scan_rows != 32)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "scan_rows must be 0, 16 or 32 (got %d)", opt.scan_rows);
+    if (opt.reserved != 0) return fail(GDN_ERR_INVALID_ARGUMENT, "options.reserved must be 0");
+    if (opt.segment_tokens < -1)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "segment_tokens must be -1, 0 or positive (got %lld)",
+                    (long long)opt.segment_tokens);
+    const bool single = !cu_seqlens && desc && desc->num_seqs == 1;
+    if (opt.segment_tokens > 0 && !single)
+        return fail(GDN_ERR_UNSUPPORTED, "segment_tokens needs one sequence without cu_seqlens");
+    if (opt.segment_tokens > 0 && opt.segment_tokens % kChunk != 0)
+        return fail(GDN_ERR_UNSUPPORTED, "segment_tokens must be a multiple of %d (got %lld)", kChunk,
+                    (long long)opt.segment_tokens);
     // A long single sequence runs as consecutive segments (same results, see
     // auto_segment_tokens), after the checks of the one-call contract.
-    if (!cu_seqlens && desc && check_desc(desc, true) == GDN_OK && chunk == kChunk) {
-        const int64_t seg = auto_segment_tokens(desc);
+    if (single && opt.segment_tokens != -1 && check_desc(desc, true) == GDN_OK && chunk == kChunk) {
+        const int64_t seg = opt.segment_tokens > 0 ? opt.segment_tokens : auto_segment_tokens(desc);
         if (seg > 0 && seg < desc->total_tokens) {
             const size_t need = ws_layout(desc, true).total;
             if (!workspace) return fail(GDN_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
             if (workspace_bytes < need)
                 return fail(GDN_ERR_WORKSPACE, "workspace too small: %zu bytes given, %zu needed", workspace_bytes,
                             need);
-            return gdn_prefill_segmented(desc, q, k, v, g, beta, state_in, out, state_out, chunk, seg, workspace,
-                                         workspace_bytes, stream);
+            gdn_desc sub;
+            size_t seg_need = 0, soff = 0;
+            gdn_status st = segment_plan(desc, chunk, seg, &sub, &seg_need, &soff);
+            if (st != GDN_OK) return st;
+            if (seg_need > workspace_bytes)
+                return fail(GDN_ERR_WORKSPACE, "segments of %lld tokens need %zu workspace bytes, %zu given",
+                            (long long)seg, seg_need, workspace_bytes);
+            return segmented_call(desc, q, k, v, g, beta, state_in, out, state_out, chunk, seg, workspace,
+                                  workspace_bytes, stream, opt.scan_rows);
         }
     }
     return prefill_call(kBoth, desc, q, k, v, g, beta, state_in, out, state_out, cu_seqlens, chunk,
-                        workspace, workspace_bytes, stream);
+                        workspace, workspace_bytes, stream, opt.scan_rows);
+}
+
+gdn_status gdn_prefill(const gdn_desc* desc, const void* q, const void* k, const void* v,
+                       const float* g, const float* beta, const float* state_in, void* out,
+                       float* state_out, const int32_t* cu_seqlens, int32_t chunk, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    return gdn_prefill_ex(desc, q, k, v, g, beta, state_in, out, state_out, cu_seqlens, chunk, nullptr, workspace,
+                          workspace_bytes, stream);
+}
+
+size_t gdn_prefill_status_offset(const gdn_desc* desc, int32_t chunk) {
+    g_err[0] = 0;
+    if (check_desc(desc, true) != GDN_OK) return 0;
+    if (chunk != kChunk) { fail(GDN_ERR_UNSUPPORTED, "chunk must be 64 (got %d)", chunk); return 0; }
+    return kStatusOff;
 }
 
 gdn_status gdn_prefill_prepare(const gdn_desc* desc, const void* q, const void* k, const void* v,
@@ -480,11 +528,14 @@ size_t gdn_prefill_segmented_workspace_bytes(const gdn_desc* desc, int32_t chunk
     return need;
 }
 
-gdn_status gdn_prefill_segmented(const gdn_desc* desc, const void* q, const void* k, const void* v,
-                                 const float* g, const float* beta, const float* state_in, void* out,
-                                 float* state_out, int32_t chunk, int64_t segment_tokens, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
-    g_err[0] = 0;
+}  // extern "C"
+
+namespace {
+
+gdn_status segmented_call(const gdn_desc* desc, const void* q, const void* k, const void* v, const float* g,
+                          const float* beta, const float* state_in, void* out, float* state_out, int32_t chunk,
+                          int64_t segment_tokens, void* workspace, size_t workspace_bytes, void* stream,
+                          int scan_rows) {
     gdn_desc sub;
     size_t need = 0, soff = 0;
     gdn_status st = segment_plan(desc, chunk, segment_tokens, &sub, &need, &soff);
@@ -531,10 +582,24 @@ gdn_status gdn_prefill_segmented(const gdn_desc* desc, const void* q, const void
         // the last segment writes state_out (or nothing when it is NULL)
         float* sout = (i + 1 == nseg) ? state_out : carry;
         st = prefill_call(kBoth, &part, T > 0 ? qc : q, T > 0 ? kc : k, T > 0 ? vc : v, T > 0 ? gc : g,
-                          T > 0 ? bc : beta, sin, T > 0 ? oc : out, sout, nullptr, chunk, workspace, seg_ws, stream);
+                          T > 0 ? bc : beta, sin, T > 0 ? oc : out, sout, nullptr, chunk, workspace, seg_ws, stream,
+                          scan_rows, i == 0);
         if (st != GDN_OK) return st;
     }
     return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_prefill_segmented(const gdn_desc* desc, const void* q, const void* k, const void* v,
+                                 const float* g, const float* beta, const float* state_in, void* out,
+                                 float* state_out, int32_t chunk, int64_t segment_tokens, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+    g_err[0] = 0;
+    return segmented_call(desc, q, k, v, g, beta, state_in, out, state_out, chunk, segment_tokens, workspace,
+                          workspace_bytes, stream, 0);
 }
 
 
@@ -654,8 +719,9 @@ gdn_status gdn_prefill_two_level(const gdn_desc* desc, const void* q, const void
     float* starts = reinterpret_cast<float*>(wsb + tl.start_off);
     float* ends = reinterpret_cast<float*>(wsb + tl.end_off);
     const int P = tl.P;
+    unsigned* status = reinterpret_cast<unsigned*>(wsb + kStatusOff);
     hipError_t e = gdn::launch_prep(d, in_bf16, q, k, v, g, beta, nullptr, nullptr, (int)tl.nblocks, (int)T, hk, hv,
-                                    desc->qk_l2norm, desc->scale, recs, krecs, s);
+                                    desc->qk_l2norm, desc->scale, recs, krecs, status, s);
     if (e == hipSuccess) e = gdn::launch_segment_info(info, P, tl.sb, (int)T, s);
     // segments 0..P-2 in one pass: affine parts B from zero, transitions R from the identity
     // (B and R are adjacent, so one state_out array holds both halves)
@@ -665,7 +731,7 @@ gdn_status gdn_prefill_two_level(const gdn_desc* desc, const void* q, const void
     if (e == hipSuccess) e = gdn::launch_compose(d, state_in, R, B, starts, P, hv, s);
     if (e == hipSuccess)
         e = gdn::launch_scan(d, in_bf16, out_bf16, 0, q, k, v, recs, krecs, info, starts, ends, out,
-                             wsb + ws.sink_off, P * hv, (int)T, hk, hv, s);
+                             wsb + ws.sink_off, P * hv, (int)T, hk, hv, status, s);
     if (e == hipSuccess && state_out)
         e = hipMemcpyAsync(state_out, ends + (size_t)(P - 1) * hv * d * d, sbytes, hipMemcpyDeviceToDevice, s);
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "two-level prefill launch: %s", hipGetErrorString(e));

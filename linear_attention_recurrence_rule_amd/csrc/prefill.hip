@@ -35,22 +35,28 @@ namespace gdn {
 
 // ---- varlen plan: per-sequence token range and block-slot base, slot -> sequence ----
 // One workgroup.  cu_seqlens is clamped into a non-decreasing sequence inside
-// [0, T] so that every index stays in bounds whatever the caller passed.
+// [0, T] so that every index stays in bounds whatever the caller passed.  The
+// plan also resets the prefill status word, setting the clamped bit when the
+// array broke its contract (first entry not 0, a decrease, an entry outside
+// [0, T], last entry not T).
 __global__ __launch_bounds__(256) void plan_kernel(const int32_t* __restrict__ cu, int N, int T,
                                                    int max_slots, SeqInfo* __restrict__ info,
-                                                   int32_t* __restrict__ slot_seq) {
-    __shared__ int s_carry_tok, s_carry_slot;
+                                                   int32_t* __restrict__ slot_seq, unsigned* __restrict__ status) {
+    __shared__ int s_carry_tok, s_carry_slot, s_bad;
     __shared__ int s_scan[256];
     const int tid = threadIdx.x;
-    if (tid == 0) { s_carry_tok = 0; s_carry_slot = 0; }
+    if (tid == 0) { s_carry_tok = 0; s_carry_slot = 0; s_bad = 0; }
     __syncthreads();
     for (int base = 0; base < N; base += 256) {
         const int n = base + tid;
         // running max of clamped ends (prefix max over this block, seeded by the carry)
         int end = 0;
         if (n < N) {
-            end = cu[n + 1];
-            end = end < 0 ? 0 : (end > T ? T : end);
+            const int raw_begin = cu[n], raw_end = cu[n + 1];
+            if (raw_end < raw_begin || raw_end < 0 || raw_end > T || (n == 0 && raw_begin != 0) ||
+                (n == N - 1 && raw_end != T))
+                atomicOr(&s_bad, 1);
+            end = raw_end < 0 ? 0 : (raw_end > T ? T : raw_end);
         }
         s_scan[tid] = end;
         __syncthreads();
@@ -86,6 +92,7 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t* __restrict__ c
     }
     const int used = s_carry_slot;
     for (int s = used + tid; s < max_slots; s += 256) slot_seq[s] = -1;
+    if (tid == 0 && status) *status = s_bad ? (unsigned)GDN_PREFILL_STATUS_CU_SEQLENS_CLAMPED : 0u;
 }
 
 // ---- workspace record of one (block slot, v-head) ----------------------------------------
@@ -285,8 +292,10 @@ __global__ __launch_bounds__(PREP_THREADS, (prep_min_waves<D, OP>())) void chunk
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const SeqInfo* __restrict__ info,
     const int32_t* __restrict__ slot_seq, int T, int h_k, int h_v, int l2norm, float scale,
-    char* __restrict__ recs, char* __restrict__ krecs, int slots, int items_per_wg) {
+    char* __restrict__ recs, char* __restrict__ krecs, int slots, int items_per_wg,
+    unsigned* __restrict__ clear_status) {
     using RC = Rec<D, OP>;
+    if (clear_status && blockIdx.x == 0 && threadIdx.x == 0) *clear_status = 0u;  // a new call's status word
     using In = PrepIn<D, IN_BF16>;
     constexpr int LK = PrepLds<D, OP>::LK;
     constexpr int PER_TOK = In::PER_TOK, NIT = In::NIT;
@@ -814,7 +823,7 @@ template <int D, typename OP, bool OUT_BF16, int RS, int MODE = 0>
 __global__ __launch_bounds__(SCAN_THREADS) void chunk_scan_kernel(
     const char* __restrict__ recs, const char* __restrict__ krecs, const SeqInfo* __restrict__ info,
     const float* __restrict__ state_in, float* __restrict__ state_out, void* __restrict__ out,
-    char* __restrict__ sink, int units, int T, int h_k, int h_v) {
+    char* __restrict__ sink, int units, int T, int h_k, int h_v, unsigned* __restrict__ status) {
     using R = Rec<D, OP>;
     using Sh = ScanShape<D, OP, RS>;
     using Slot = ScanSlot<D, OP, RS>;
@@ -921,6 +930,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void chunk_scan_kernel(
         }
         store_part<OP>(sS, (mb / 2) * NB + nb, mb % 2, lane, St[i]);
     }
+    bool bad = false;  // a non-finite output or final state in this lane
     for (int c = 0; c < nchunks; ++c) {
         __syncthreads();  // B1: block c in its slot; S^T fragments complete; sU and sO free
         const Slot& B = ring[c & 1];
@@ -963,13 +973,15 @@ __global__ __launch_bounds__(SCAN_THREADS) void chunk_scan_kernel(
             for (int nb = 0; nb < NB; ++nb) store_part<OP>(sU, (tb / 2) * NB + nb, tb % 2, lane, acc[nb] * sv);
         } else if (MODE == 0) {
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
+            for (int nb = 0; nb < NB; ++nb) {
+                bad |= any_nonfinite(acc[nb]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int e = (16 * tb + 4 * q4 + r) * RS + 16 * nb + j16;
                     if constexpr (OUT_BF16) reinterpret_cast<uint16_t*>(sO)[e] = f32_to_bf16(acc[nb][r]);
                     else reinterpret_cast<float*>(sO)[e] = acc[nb][r];
                 }
+            }
         }
         __syncthreads();  // B2: diag(s) U and the outputs complete; S^T fragments and slot c % 2 no longer read
         // phase B: S^T <- gamma_n S^T + K^T diag(s) U
@@ -993,16 +1005,22 @@ __global__ __launch_bounds__(SCAN_THREADS) void chunk_scan_kernel(
                 make_float4(St[i][0], St[i][1], St[i][2], St[i][3]);
         }
     }
+    if (MODE == 0) {
+#pragma unroll
+        for (int i = 0; i < TPW; ++i)
+            if (w * TPW + i < Sh::NTB) bad |= any_nonfinite(St[i]);
+        report_status(status, bad, GDN_PREFILL_STATUS_NONFINITE);
+    }
 }
 
 // ---- host launchers ----------------------------------------------------------------------
 size_t tp_record_bytes();
 hipError_t launch_prep_bf16(int d, const void* q, const void* k, const float* g, const float* beta,
                             const void* info, const int32_t* slot_seq, int slots, int T, int h_k, int h_v,
-                            int l2norm, float scale, void* recs, hipStream_t stream);
+                            int l2norm, float scale, void* recs, unsigned* clear_status, hipStream_t stream);
 hipError_t launch_scan_bf16(int d, bool out_bf16, int rows, int mode, const void* q, const void* k, const void* v,
                             const void* recs, const void* info, const float* s_in, float* s_out, void* out, void* sink,
-                            int units, int T, int h_k, int h_v, hipStream_t stream);
+                            int units, int T, int h_k, int h_v, unsigned* status, hipStream_t stream);
 
 // Workspace record sizes: bf16 inputs use one record per (block slot, v-head)
 // (prefill_bf16.hip); fp32 inputs one per (block slot, v-head) plus a key
@@ -1018,9 +1036,16 @@ size_t prefill_key_record_bytes(int d, bool in_bf16) {
 }
 
 hipError_t launch_plan(const int32_t* cu, int N, int T, int max_slots, void* info, int32_t* slot_seq,
-                       hipStream_t stream) {
+                       unsigned* status, hipStream_t stream) {
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, cu, N, T, max_slots,
-                       reinterpret_cast<SeqInfo*>(info), slot_seq);
+                       reinterpret_cast<SeqInfo*>(info), slot_seq, status);
+    return hipGetLastError();
+}
+
+__global__ void status_reset_kernel(unsigned* __restrict__ status) { *status = 0u; }
+
+hipError_t launch_status_reset(unsigned* status, hipStream_t stream) {
+    hipLaunchKernelGGL(status_reset_kernel, dim3(1), dim3(1), 0, stream, status);
     return hipGetLastError();
 }
 
@@ -1041,7 +1066,7 @@ template <int D, typename OP, bool IB>
 static hipError_t launch_prep_t(const void* q, const void* k, const void* v, const float* g,
                                 const float* beta, const void* info, const int32_t* slot_seq,
                                 int slots, int T, int h_k, int h_v, int l2norm, float scale,
-                                char* recs, char* krecs, hipStream_t stream) {
+                                char* recs, char* krecs, unsigned* clear_status, hipStream_t stream) {
     constexpr size_t lds = prep_lds_bytes<D, OP>();
     static_assert(lds <= 160 * 1024, "chunk_prep LDS budget");
     auto kern = chunk_prep_kernel<D, OP, IB>;
@@ -1055,55 +1080,63 @@ static hipError_t launch_prep_t(const void* q, const void* k, const void* v, con
     const int grid = (items + per - 1) / per;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(PREP_THREADS), lds, stream, q, k, v, g, beta,
                        reinterpret_cast<const SeqInfo*>(info), slot_seq, T, h_k, h_v, l2norm, scale, recs, krecs,
-                       slots, per);
+                       slots, per, clear_status);
     return hipGetLastError();
 }
 
 hipError_t launch_prep(int d, bool in_bf16, const void* q, const void* k, const void* v,
                        const float* g, const float* beta, const void* info, const int32_t* slot_seq,
                        int slots, int T, int h_k, int h_v, int l2norm, float scale, void* recs,
-                       void* krecs, hipStream_t stream) {
+                       void* krecs, unsigned* clear_status, hipStream_t stream) {
     if (in_bf16)
-        return launch_prep_bf16(d, q, k, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, recs, stream);
+        return launch_prep_bf16(d, q, k, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, recs,
+                                clear_status, stream);
     if (d == 64)
         return launch_prep_t<64, float, false>(q, k, v, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale,
-                                               reinterpret_cast<char*>(recs), reinterpret_cast<char*>(krecs), stream);
+                                               reinterpret_cast<char*>(recs), reinterpret_cast<char*>(krecs),
+                                               clear_status, stream);
     return hipErrorInvalidValue;
 }
 
 template <int D, typename OP, bool OB, int RS, int MODE = 0>
 static hipError_t launch_scan_t(const void* recs, const void* krecs, const void* info, const float* s_in,
                                 float* s_out, void* out, void* sink, int units, int T, int h_k, int h_v,
-                                hipStream_t stream) {
+                                unsigned* status, hipStream_t stream) {
     static_assert(scan_lds_bytes<D, OP, OB, RS>() <= 160 * 1024, "chunk_scan LDS budget");
     const int groups = (units + 7) / 8;  // see the XCD placement in chunk_scan_kernel
     hipLaunchKernelGGL((chunk_scan_kernel<D, OP, OB, RS, MODE>), dim3(groups * 8 * (D / RS)), dim3(SCAN_THREADS), 0,
                        stream, reinterpret_cast<const char*>(recs), reinterpret_cast<const char*>(krecs),
                        reinterpret_cast<const SeqInfo*>(info), s_in, s_out, out, reinterpret_cast<char*>(sink), units,
-                       T, h_k, h_v);
+                       T, h_k, h_v, status);
     return hipGetLastError();
 }
 
 // Rows of a state per scan workgroup: `requested` (16 or 32), or for 0 the
-// default: 16-row slices double the workgroups (each still copies the whole
-// shared part of a block), which pays while 32-row slices leave compute units
-// idle.
-int scan_rows_per_workgroup(int d, int units, int requested) {
+// default.  bf16 inputs: 16 rows, whose layout gives every SIMD one chain wave
+// and keeps q in LDS (32-row workgroups measured about twice as slow per
+// block at any occupancy).  fp32 inputs: 16-row slices double the workgroups
+// (each still copies the whole shared part of a block), which pays while
+// 32-row slices leave compute units idle.
+int scan_rows_per_workgroup(int d, bool in_bf16, int units, int requested) {
     if (requested == 16 || requested == 32) return requested;
+    if (in_bf16) return 16;
     return (long long)units * (d / 32) < compute_units() ? 16 : 32;
 }
 
 hipError_t launch_scan(int d, bool in_bf16, bool out_bf16, int rows, const void* q, const void* k, const void* v,
                        const void* recs, const void* krecs, const void* info, const float* s_in, float* s_out,
-                       void* out, void* sink, int units, int T, int h_k, int h_v, hipStream_t stream) {
-    const int rs = scan_rows_per_workgroup(d, units, rows);
+                       void* out, void* sink, int units, int T, int h_k, int h_v, unsigned* status,
+                       hipStream_t stream) {
+    const int rs = scan_rows_per_workgroup(d, in_bf16, units, rows);
     if (in_bf16)
         return launch_scan_bf16(d, out_bf16, rs, 0, q, k, v, recs, info, s_in, s_out, out, sink, units, T, h_k, h_v,
-                                stream);
-#define GDN_SCAN(D, OP, IB, OB)                                                                          \
-    if (d == D && in_bf16 == IB && out_bf16 == OB)                                                       \
-        return rs == 16 ? launch_scan_t<D, OP, OB, 16>(recs, krecs, info, s_in, s_out, out, sink, units, T, h_k, h_v, stream) \
-                        : launch_scan_t<D, OP, OB, 32>(recs, krecs, info, s_in, s_out, out, sink, units, T, h_k, h_v, stream);
+                                status, stream);
+#define GDN_SCAN(D, OP, IB, OB)                                                                                \
+    if (d == D && in_bf16 == IB && out_bf16 == OB)                                                             \
+        return rs == 16 ? launch_scan_t<D, OP, OB, 16>(recs, krecs, info, s_in, s_out, out, sink, units, T, h_k, \
+                                                       h_v, status, stream)                                    \
+                        : launch_scan_t<D, OP, OB, 32>(recs, krecs, info, s_in, s_out, out, sink, units, T, h_k, \
+                                                       h_v, status, stream);
     GDN_SCAN(64, float, false, true) GDN_SCAN(64, float, false, false)
 #undef GDN_SCAN
     return hipErrorInvalidValue;
@@ -1193,15 +1226,15 @@ hipError_t launch_compose(int d, const float* state_in, const float* R, const fl
 hipError_t launch_scan_transition(int d, bool in_bf16, int rows, const void* q, const void* k, const void* v,
                                   const void* recs, const void* krecs, const void* info, float* s_out, void* sink,
                                   int units, int T, int h_k, int h_v, hipStream_t stream) {
-    const int rs = scan_rows_per_workgroup(d, units, rows);
+    const int rs = scan_rows_per_workgroup(d, in_bf16, units, rows);
     if (in_bf16)
         return launch_scan_bf16(d, false, rs, 1, q, k, v, recs, info, nullptr, s_out, nullptr, sink, units, T, h_k,
-                                h_v, stream);
+                                h_v, nullptr, stream);
     if (d == 64)
         return rs == 16 ? launch_scan_t<64, float, false, 16, 1>(recs, krecs, info, nullptr, s_out, nullptr, sink,
-                                                                 units, T, h_k, h_v, stream)
+                                                                 units, T, h_k, h_v, nullptr, stream)
                         : launch_scan_t<64, float, false, 32, 1>(recs, krecs, info, nullptr, s_out, nullptr, sink,
-                                                                 units, T, h_k, h_v, stream);
+                                                                 units, T, h_k, h_v, nullptr, stream);
     return hipErrorInvalidValue;
 }
 

@@ -160,9 +160,11 @@ template <int D, int NH>
 __global__ __launch_bounds__(PAIR_THREADS, 1) void chunk_prep_pair_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const float* __restrict__ g,
     const float* __restrict__ beta, const SeqInfo* __restrict__ info, const int32_t* __restrict__ slot_seq,
-    int T, int h_k, int h_v, int l2norm, float scale, char* __restrict__ recs, int slots, int items_per_wg) {
+    int T, int h_k, int h_v, int l2norm, float scale, char* __restrict__ recs, int slots, int items_per_wg,
+    unsigned* __restrict__ clear_status) {
     using OP = _Float16;
     using LT = PairLds<D, NH>;
+    if (clear_status && blockIdx.x == 0 && threadIdx.x == 0) *clear_status = 0u;  // a new call's status word
     constexpr int XS = LT::XS;
     constexpr int NKB = D / 32;  // contraction blocks over d
     extern __shared__ __align__(16) char smem_raw[];
@@ -629,7 +631,7 @@ __global__ __launch_bounds__(TPS_MAX_THREADS) void chunk_scan_tp_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const char* __restrict__ recs, const SeqInfo* __restrict__ info, const float* __restrict__ state_in,
     float* __restrict__ state_out, void* __restrict__ out, char* __restrict__ sink, int units, int T, int h_k,
-    int h_v) {
+    int h_v, unsigned* __restrict__ status) {
     using Sh = TpShape<D, NB>;
     using Ro = TpsRoles<D, NB>;
     using Slot = TpSlot<D, NB>;
@@ -672,6 +674,8 @@ __global__ __launch_bounds__(TPS_MAX_THREADS) void chunk_scan_tp_kernel(
     auto rec_of = [&](int c) __attribute__((always_inline)) {
         return recs + ((size_t)(slot0 + c) * h_v + h) * TpRec::BYTES;
     };
+
+    bool bad = false;  // a non-finite output or final state in this lane (token and chain waves)
 
     if (w >= Ro::CHAIN + Ro::OUTW) {
         // ------------------------------ copier waves ------------------------------
@@ -860,6 +864,7 @@ __global__ __launch_bounds__(TPS_MAX_THREADS) void chunk_scan_tp_kernel(
                         if (kb <= kbt)
                             mma(o, frag_stored<_Float16>(B.tp[1], tri_frag(tb, kb), lane),
                                 frag_stored<_Float16>(sU, kb * NB + nb, lane));
+                    bad |= any_nonfinite(o);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int e = (16 * tb + 4 * q4 + r) * RS + 16 * nb + j16;
@@ -878,6 +883,7 @@ __global__ __launch_bounds__(TPS_MAX_THREADS) void chunk_scan_tp_kernel(
         }
         lds_barrier();  // B1 after the last block
         lds_barrier();  // BF
+        if (MODE == 0) report_status(status, bad, GDN_PREFILL_STATUS_NONFINITE);
         return;
     }
 
@@ -974,6 +980,11 @@ __global__ __launch_bounds__(TPS_MAX_THREADS) void chunk_scan_tp_kernel(
             *reinterpret_cast<float4*>(state_out + sbase + (size_t)srow * D + 16 * (mb0 + i) + 4 * q4) =
                 make_float4(St[i][0], St[i][1], St[i][2], St[i][3]);
     }
+    if (MODE == 0) {
+#pragma unroll
+        for (int i = 0; i < 2 * KPW; ++i) bad |= any_nonfinite(St[i]);
+        report_status(status, bad, GDN_PREFILL_STATUS_NONFINITE);
+    }
 }
 
 // ============================================================================================
@@ -986,7 +997,8 @@ size_t tp_record_bytes() { return TpRec::BYTES; }
 template <int D, int NH>
 static hipError_t launch_prep_pair_t(const void* q, const void* k, const float* g, const float* beta,
                                      const void* info, const int32_t* slot_seq, int slots, int T, int h_k, int h_v,
-                                     int l2norm, float scale, char* recs, hipStream_t stream) {
+                                     int l2norm, float scale, char* recs, unsigned* clear_status,
+                                     hipStream_t stream) {
     constexpr size_t lds = pair_lds_bytes<D, NH>();
     static_assert(lds <= 160 * 1024, "chunk_prep_pair LDS budget");
     auto kern = chunk_prep_pair_kernel<D, NH>;
@@ -998,43 +1010,45 @@ static hipError_t launch_prep_pair_t(const void* q, const void* k, const float* 
     const int per = (items + resident - 1) / resident;
     const int grid = (items + per - 1) / per;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(PAIR_THREADS), lds, stream, q, k, g, beta,
-                       reinterpret_cast<const SeqInfo*>(info), slot_seq, T, h_k, h_v, l2norm, scale, recs, slots, per);
+                       reinterpret_cast<const SeqInfo*>(info), slot_seq, T, h_k, h_v, l2norm, scale, recs, slots, per,
+                       clear_status);
     return hipGetLastError();
 }
 
 hipError_t launch_prep_bf16(int d, const void* q, const void* k, const float* g, const float* beta,
                             const void* info, const int32_t* slot_seq, int slots, int T, int h_k, int h_v,
-                            int l2norm, float scale, void* recs, hipStream_t stream) {
+                            int l2norm, float scale, void* recs, unsigned* clear_status, hipStream_t stream) {
     char* r = reinterpret_cast<char*>(recs);
+    unsigned* cs = clear_status;
     const bool pair = (h_v / h_k) % 2 == 0;
     if (d == 128)
-        return pair ? launch_prep_pair_t<128, 2>(q, k, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, stream)
-                    : launch_prep_pair_t<128, 1>(q, k, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, stream);
+        return pair ? launch_prep_pair_t<128, 2>(q, k, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, cs, stream)
+                    : launch_prep_pair_t<128, 1>(q, k, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, cs, stream);
     if (d == 64)
-        return pair ? launch_prep_pair_t<64, 2>(q, k, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, stream)
-                    : launch_prep_pair_t<64, 1>(q, k, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, stream);
+        return pair ? launch_prep_pair_t<64, 2>(q, k, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, cs, stream)
+                    : launch_prep_pair_t<64, 1>(q, k, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, cs, stream);
     return hipErrorInvalidValue;
 }
 
 template <int D, bool OB, int NB, int MODE>
 static hipError_t launch_scan_tp_t(const void* q, const void* k, const void* v, const void* recs, const void* info,
                                    const float* s_in, float* s_out, void* out, void* sink, int units, int T, int h_k,
-                                   int h_v, hipStream_t stream) {
+                                   int h_v, unsigned* status, hipStream_t stream) {
     static_assert(tp_scan_lds_bytes<D, NB>(OB) <= 160 * 1024, "chunk_scan_tp LDS budget");
     const int groups = (units + 7) / 8;  // see the XCD placement in chunk_scan_tp_kernel
     hipLaunchKernelGGL((chunk_scan_tp_kernel<D, OB, NB, MODE>), dim3(groups * 8 * (D / (16 * NB))), dim3(TpsRoles<D, NB>::THREADS),
                        0, stream, q, k, v, reinterpret_cast<const char*>(recs), reinterpret_cast<const SeqInfo*>(info),
-                       s_in, s_out, out, reinterpret_cast<char*>(sink), units, T, h_k, h_v);
+                       s_in, s_out, out, reinterpret_cast<char*>(sink), units, T, h_k, h_v, status);
     return hipGetLastError();
 }
 
 hipError_t launch_scan_bf16(int d, bool out_bf16, int rows, int mode, const void* q, const void* k, const void* v,
                             const void* recs, const void* info, const float* s_in, float* s_out, void* out, void* sink,
-                            int units, int T, int h_k, int h_v, hipStream_t stream) {
+                            int units, int T, int h_k, int h_v, unsigned* status, hipStream_t stream) {
 #define GDN_TPS(D, OB, NB, MODE)                                                                              \
     if (d == D && out_bf16 == OB && rows == 16 * NB && mode == MODE)                                          \
         return launch_scan_tp_t<D, OB, NB, MODE>(q, k, v, recs, info, s_in, s_out, out, sink, units, T, h_k, h_v, \
-                                                 stream);
+                                                 status, stream);
     GDN_TPS(128, true, 1, 0) GDN_TPS(128, false, 1, 0) GDN_TPS(128, true, 2, 0) GDN_TPS(128, false, 2, 0)
     GDN_TPS(64, true, 1, 0) GDN_TPS(64, false, 1, 0) GDN_TPS(64, true, 2, 0) GDN_TPS(64, false, 2, 0)
     GDN_TPS(128, false, 1, 1) GDN_TPS(128, false, 2, 1) GDN_TPS(64, false, 1, 1) GDN_TPS(64, false, 2, 1)

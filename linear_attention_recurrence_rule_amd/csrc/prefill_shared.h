@@ -2,6 +2,7 @@
 // inputs; prefill_bf16.hip: bf16 inputs).
 #pragma once
 #include "gdn_device.h"
+#include "gdn.h"  // gdn_prefill_status_flag
 
 namespace gdn {
 
@@ -73,6 +74,17 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Sets `bit` in the prefill status word (when there is one) if any lane of the
+// wave has `bad` set: one vector atomic per wave.
+__device__ __forceinline__ void report_status(unsigned* status, bool bad, unsigned bit) {
+    if (status && __any(bad) && (threadIdx.x % WAVE) == 0) atomicOr(status, bit);
+}
+
+__device__ __forceinline__ bool any_nonfinite(const f4_t& x) {
+    return !__builtin_isfinite(x[0]) || !__builtin_isfinite(x[1]) || !__builtin_isfinite(x[2]) ||
+           !__builtin_isfinite(x[3]);
 }
 
 }  // namespace gdn

@@ -36,6 +36,15 @@ class GdnDesc(ctypes.Structure):
                 ("qk_l2norm", ctypes.c_int32), ("scale", ctypes.c_float)]
 
 
+class GdnPrefillOptions(ctypes.Structure):
+    _fields_ = [("scan_rows", ctypes.c_int32), ("reserved", ctypes.c_int32), ("segment_tokens", ctypes.c_int64)]
+
+
+# bits of the prefill status word (gdn_prefill_status_offset)
+GDN_PREFILL_STATUS_CU_SEQLENS_CLAMPED = 1
+GDN_PREFILL_STATUS_NONFINITE = 2
+
+
 class GdnError(RuntimeError):
     def __init__(self, status, detail):
         self.status = status
@@ -67,6 +76,11 @@ def lib():
             L.gdn_prefill_workspace_bytes.restype = sz
             L.gdn_prefill.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32, vp, sz, vp]
             L.gdn_prefill.restype = ctypes.c_int
+            L.gdn_prefill_ex.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32,
+                                         ctypes.POINTER(GdnPrefillOptions), vp, sz, vp]
+            L.gdn_prefill_ex.restype = ctypes.c_int
+            L.gdn_prefill_status_offset.argtypes = [dp, ctypes.c_int32]
+            L.gdn_prefill_status_offset.restype = sz
             L.gdn_prefill_prepare.argtypes = [dp, vp, vp, vp, vp, vp, vp, ctypes.c_int32, vp, sz, vp]
             L.gdn_prefill_prepare.restype = ctypes.c_int
             L.gdn_prefill_scan.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32, vp, sz, vp]
@@ -148,6 +162,29 @@ def gdn_prefill(desc, q, k, v, g, beta, state_in, out, state_out, cu_seqlens, ch
     _check(lib().gdn_prefill(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                              _ptr(state_in), _ptr(out), _ptr(state_out), _ptr(cu_seqlens), int(chunk),
                              _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def gdn_prefill_ex(desc, q, k, v, g, beta, state_in, out, state_out, cu_seqlens, chunk, options, workspace,
+                   workspace_bytes, stream=None):
+    """options: a GdnPrefillOptions, or None for the defaults (then this is gdn_prefill)."""
+    opt = ctypes.byref(options) if options is not None else None
+    _check(lib().gdn_prefill_ex(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                _ptr(state_in), _ptr(out), _ptr(state_out), _ptr(cu_seqlens), int(chunk), opt,
+                                _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def gdn_prefill_status_offset(desc: GdnDesc, chunk: int = CHUNK) -> int:
+    n = lib().gdn_prefill_status_offset(ctypes.byref(desc), int(chunk))
+    if n == 0:
+        raise GdnError(GDN_ERR_INVALID_ARGUMENT, last_error())
+    return n
+
+
+def prefill_status(desc: GdnDesc, workspace: torch.Tensor, chunk: int = CHUNK) -> int:
+    """The status word a prefill call left in `workspace` (a uint8 device tensor).  Reads it
+    with a device-to-host copy, which waits for the current stream."""
+    off = gdn_prefill_status_offset(desc, chunk)
+    return int(workspace[off:off + 4].cpu().view(torch.int32).item()) & 0xFFFFFFFF
 
 
 def gdn_prefill_prepare(desc, q, k, v, g, beta, cu_seqlens, chunk, workspace, workspace_bytes,
@@ -249,9 +286,10 @@ def _need(t, name, dtype=None, device=None):
 
 
 def prefill(q, k, v, g, beta, *, state_in=None, cu_seqlens=None, out_dtype=None, qk_l2norm=True,
-            scale=1.0, want_state=True, workspace=None, stream=None):
+            scale=1.0, want_state=True, workspace=None, stream=None, options=None):
     """q, k [T, h_k, d]; v [T, h_v, d]; g, beta [T, h_v] fp32; state_in [N, h_v, d, d] fp32 or
-    None; cu_seqlens int32 [N+1] or None.  Returns (out [T, h_v, d], state_out or None)."""
+    None; cu_seqlens int32 [N+1] or None; options a GdnPrefillOptions (gdn_prefill_ex) or None.
+    Returns (out [T, h_v, d], state_out or None)."""
     dev = q.device
     io = _io_dtype(q)
     T, h_k, d = q.shape
@@ -273,8 +311,12 @@ def prefill(q, k, v, g, beta, *, state_in=None, cu_seqlens=None, out_dtype=None,
     nbytes = gdn_prefill_workspace_bytes(desc)
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
-    gdn_prefill(desc, q, k, v, g, beta, state_in, out, state_out, cu_seqlens, CHUNK, workspace,
-                workspace.numel(), stream)
+    if options is None:
+        gdn_prefill(desc, q, k, v, g, beta, state_in, out, state_out, cu_seqlens, CHUNK, workspace,
+                    workspace.numel(), stream)
+    else:
+        gdn_prefill_ex(desc, q, k, v, g, beta, state_in, out, state_out, cu_seqlens, CHUNK, options, workspace,
+                       workspace.numel(), stream)
     return out, state_out
 
 

@@ -34,7 +34,8 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = gdn.declared_functions()
-    assert set(names) == {"gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_prefill_prepare",
+    assert set(names) == {"gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_prefill_ex", "gdn_prefill_status_offset",
+                          "gdn_prefill_prepare",
                           "gdn_prefill_scan", "gdn_prefill_direct", "gdn_prefill_segmented_workspace_bytes",
                           "gdn_prefill_segmented", "gdn_prefill_two_level_workspace_bytes", "gdn_prefill_two_level",
                           "gdn_decode_step", "gdn_decode_step_slots", "gdn_decode_step_ex", "gdn_prefill_direct_ex",
@@ -69,20 +70,29 @@ def test_workspace_bytes(L):
     # of P (fp16) and 1 KiB of per-token factors; no key records.
     # 64 blocks x 32 v-heads.
     rec = 2 * 6 * 1024 + 1024
-    plan = (1024 + 1 * 16 + 64 * 4 + 255) // 256 * 256
+    plan = (1280 + 1 * 16 + 64 * 4 + 255) // 256 * 256  # 1 KiB sink, 256 B status word, then the plan
     assert gdn.gdn_prefill_workspace_bytes(desc()) == plan + 64 * 32 * rec
     # packed sequences: at most T/64 + N blocks in total
     n = gdn.gdn_prefill_workspace_bytes(desc(num_seqs=16, total_tokens=1000))
     slots = (1000 + 16 * 63) // 64
-    assert n == (1024 + 16 * 16 + slots * 4 + 255) // 256 * 256 + slots * 32 * rec
+    assert n == (1280 + 16 * 16 + slots * 4 + 255) // 256 * 256 + slots * 32 * rec
     # fp32 inputs keep fp32 operands
     rec64f = 4 * 64 * 64 * 4 + 512
     key64f = 64 * 64 * 4
     assert gdn.gdn_prefill_workspace_bytes(desc(total_tokens=256, h_k=1, h_v=1, d=64,
                                                 io_dtype=gdn.GDN_F32, out_dtype=gdn.GDN_F32)) == \
-        1280 + 4 * (rec64f + key64f)
+        1536 + 4 * (rec64f + key64f)
     assert L.gdn_prefill_workspace_bytes(ctypes.byref(desc()), 32) == 0
     assert "chunk" in gdn.last_error()
+
+
+def test_status_offset(L):
+    d = desc()
+    assert gdn.gdn_prefill_status_offset(d) == 1024  # after the 1 KiB sink, 4-byte aligned
+    assert gdn.gdn_prefill_status_offset(desc(num_seqs=3, total_tokens=10)) == 1024
+    assert L.gdn_prefill_status_offset(ctypes.byref(d), 32) == 0
+    assert "chunk" in gdn.last_error()
+    assert L.gdn_prefill_status_offset(ctypes.byref(desc(d=96)), 64) == 0
 
 
 FAKE = 0x10000  # never dereferenced: every case below fails validation first
@@ -247,7 +257,7 @@ def test_two_level_workspace_bytes(L):
     # 64 blocks in 8 segments of 8: single-sequence records, a 256-byte segment table, then
     # R and B for 7 segments and start and end states for 8 (32 v-heads, d = 128, fp32)
     rec = 2 * 6 * 1024 + 1024
-    base = 1024 + 64 * 32 * rec
+    base = 1280 + 64 * 32 * rec
     st = 32 * 128 * 128 * 4
     assert gdn.gdn_prefill_two_level_workspace_bytes(desc(total_tokens=4096), 8) == base + 256 + (7 + 7 + 8 + 8) * st
     # more segments than blocks: one segment per block
@@ -386,3 +396,42 @@ def test_header_is_plain_c(tmp_path):
         r = subprocess.run([cc, std, "-Wall", "-Wextra", "-pedantic", "-Werror", "-fsyntax-only", "-I", inc] + lang +
                            [str(src)], capture_output=True, text=True)
         assert r.returncode == 0, r.stderr
+
+
+def call_prefill_ex(d, opt, *, cu=None):
+    F = 0x10000
+    return gdn.lib().gdn_prefill_ex(ctypes.byref(d), F, F + (1 << 32), F + (2 << 32), F + (3 << 32),
+                                    F + (4 << 32), None, F + (5 << 32), None, cu, 64,
+                                    ctypes.byref(opt) if opt is not None else None, None, 0, None)
+
+
+@pytest.mark.parametrize("opt,status,msg", [
+    ((8, 0, 0), gdn.GDN_ERR_INVALID_ARGUMENT, "scan_rows"),
+    ((48, 0, 0), gdn.GDN_ERR_INVALID_ARGUMENT, "scan_rows"),
+    ((16, 1, 0), gdn.GDN_ERR_INVALID_ARGUMENT, "reserved"),
+    ((0, 0, -2), gdn.GDN_ERR_INVALID_ARGUMENT, "segment_tokens"),
+    ((0, 0, 100), gdn.GDN_ERR_UNSUPPORTED, "multiple"),
+])
+def test_prefill_ex_rejects_bad_options(L, opt, status, msg):
+    """Options are checked before anything else (the fake pointers are never used)."""
+    assert call_prefill_ex(desc(), gdn.GdnPrefillOptions(*opt)) == status
+    assert msg in gdn.last_error()
+
+
+def test_prefill_ex_segments_need_one_sequence(L):
+    st = call_prefill_ex(desc(num_seqs=2, total_tokens=256), gdn.GdnPrefillOptions(0, 0, 128), cu=0x20000)
+    assert st == gdn.GDN_ERR_UNSUPPORTED and "one sequence" in gdn.last_error()
+
+
+def test_prefill_ex_defaults_validate_like_prefill(L):
+    """NULL options or explicit defaults reach the gdn_prefill checks (here: no workspace)."""
+    for opt in (None, gdn.GdnPrefillOptions(0, 0, 0), gdn.GdnPrefillOptions(32, 0, -1)):
+        assert call_prefill_ex(desc(), opt) == gdn.GDN_ERR_WORKSPACE
+
+
+def test_no_environment_tuning():
+    """The library reads no environment variables: tuning goes through gdn_prefill_ex."""
+    import glob, os
+    csrc = os.path.join(os.path.dirname(gdn.__file__), "csrc")
+    for f in glob.glob(os.path.join(csrc, "*")):
+        assert "getenv" not in open(f).read(), f

@@ -186,7 +186,15 @@ def test_malformed_cu_seqlens_stay_in_bounds():
     cu = dev(np.array([0, 300, 100, 5000, -7, 250], dtype=np.int32))
     s0 = dev((0.1 * np.random.default_rng(19).standard_normal((5, 4, 128, 128))).astype(np.float32))
     args = (dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["g"]), dev(x["beta"]))
-    out, st = gdn.prefill(*args, state_in=s0, cu_seqlens=cu, out_dtype=inputs.F32)
+    desc5 = gdn.make_desc(num_seqs=5, total_tokens=T, h_k=2, h_v=4, d=128, io_dtype=gdn.GDN_BF16,
+                          out_dtype=gdn.GDN_F32)
+    ws = torch.full((gdn.gdn_prefill_workspace_bytes(desc5),), 0xAB, dtype=torch.uint8, device=s0.device)
+    out, st = gdn.prefill(*args, state_in=s0, cu_seqlens=cu, out_dtype=inputs.F32, workspace=ws)
+    assert gdn.prefill_status(desc5, ws) == gdn.GDN_PREFILL_STATUS_CU_SEQLENS_CLAMPED
+    # the same call with a well-formed array leaves a clear status word in the same workspace
+    gdn.prefill(*args, state_in=s0, cu_seqlens=dev(np.array([0, 50, 50, 120, 200, 250], dtype=np.int32)),
+                out_dtype=inputs.F32, workspace=ws)
+    assert gdn.prefill_status(desc5, ws) == 0
     out_d, st_d = gdn.prefill_direct(*args, state_in=s0, cu_seqlens=cu, out_dtype=inputs.F32)
     torch.cuda.synchronize()
     for t in (out, st, out_d, st_d):
@@ -197,6 +205,64 @@ def test_malformed_cu_seqlens_stay_in_bounds():
     o2, s2 = run_gpu(good, inputs.F32)
     ro, rs = run_oracle(good)
     assert normwise(host(o2), ro) <= 2e-3 and normwise(host(s2), rs) <= 2e-3
+
+
+def _status_run(x, out_dtype, **kw):
+    """Prefill x with a caller workspace; returns (out, state, status word)."""
+    T, h_k, d = x["q"].shape
+    h_v = x["v"].shape[1]
+    N = 1 if x["cu_seqlens"] is None else len(x["cu_seqlens"]) - 1
+    desc = gdn.make_desc(num_seqs=N, total_tokens=T, h_k=h_k, h_v=h_v, d=d,
+                         io_dtype=gdn.GDN_BF16 if x["q"].dtype == np.uint16 else gdn.GDN_F32,
+                         out_dtype=gdn.GDN_BF16 if out_dtype == inputs.BF16 else gdn.GDN_F32)
+    ws = torch.full((gdn.gdn_prefill_workspace_bytes(desc),), 0xFF, dtype=torch.uint8, device="cuda")
+    out, st = run_gpu(x, out_dtype, workspace=ws, **kw)
+    return out, st, gdn.prefill_status(desc, ws)
+
+
+def test_status_word_clean_run():
+    """An ordinary call leaves a zero status word (the word starts as garbage)."""
+    x = inputs.prefill_inputs(seed=23, lengths=[100, 1, 190], h_k=2, h_v=4, d=128, io_dtype=inputs.BF16,
+                              state_std=0.1)
+    _, _, status = _status_run(x, inputs.F32)
+    assert status == 0
+    x = inputs.prefill_inputs(seed=24, total_tokens=300, h_k=1, h_v=2, d=64, io_dtype=inputs.F32, state_std=0.1)
+    _, _, status = _status_run(x, inputs.F32)
+    assert status == 0
+
+
+@pytest.mark.parametrize("what", ["v", "state"])
+def test_large_values_are_reported_or_exact(what):
+    """Values up to 2^20 or an initial state of size 2^16 go beyond the fp16 range of the
+    bf16 path's token contractions.  The call must then either meet the 2e-3 bound or raise
+    GDN_PREFILL_STATUS_NONFINITE in the status word, as gdn.h documents.  The fp32 path
+    has no such limit: on the same data at d = 64 it meets 1e-5 with a clear status."""
+    for d, io in ((128, inputs.BF16), (64, inputs.F32)):
+        x = inputs.prefill_inputs(seed=25, total_tokens=200, h_k=2, h_v=4, d=d, io_dtype=io, state_std=0.1)
+        if what == "v":
+            rng = np.random.default_rng(26)
+            big = (2.0 ** rng.integers(12, 21, size=x["v"].shape)).astype(np.float32) * \
+                rng.choice([-1.0, 1.0], size=x["v"].shape).astype(np.float32)
+            x["v"] = inputs.f32_to_bf16_bits(big) if io == inputs.BF16 else big  # powers of two: exact
+        else:
+            x["state_in"] = (x["state_in"] * (2.0 ** 16 / 0.1)).astype(np.float32)
+        out, st, status = _status_run(x, inputs.F32)
+        ro, rs = run_oracle(x)
+        if io == inputs.F32:
+            assert status == 0
+            assert normwise(host(out), ro) <= 1e-5 and normwise(host(st), rs) <= 1e-5
+        elif status & gdn.GDN_PREFILL_STATUS_NONFINITE:
+            assert not (torch.isfinite(out).all() and torch.isfinite(st).all())
+        else:
+            assert normwise(host(out), ro) <= 2e-3 and normwise(host(st), rs) <= 2e-3
+
+
+def test_nonfinite_input_is_reported():
+    """A NaN in the input reaches the outputs; the status word says so."""
+    x = inputs.prefill_inputs(seed=27, total_tokens=130, h_k=2, h_v=4, d=128, io_dtype=inputs.BF16, state_std=0.1)
+    x["state_in"][0, 1, 3, 5] = np.nan
+    _, _, status = _status_run(x, inputs.BF16)
+    assert status == gdn.GDN_PREFILL_STATUS_NONFINITE
 
 
 @pytest.mark.parametrize("gate_mean", [0.0, -4.0])
@@ -212,19 +278,20 @@ def test_fp32_long_sequence(gate_mean):
     assert eo <= 1e-5 and es <= 1e-5
 
 
-def test_long_prompt_runs_as_segments(monkeypatch):
-    """A single sequence whose block records exceed the last-level cache runs inside
-    gdn_prefill as consecutive segments: bit-identical to one call (also without a state
-    output, where the carried state lives in the workspace, and in place), and within
-    tolerance of the oracle."""
+def test_long_prompt_runs_as_segments():
+    """A single sequence can run inside gdn_prefill_ex as consecutive segments (explicit
+    lengths, or the automatic choice gdn_prefill makes): bit-identical to one pass (also
+    without a state output, where the carried state lives in the workspace, and in place),
+    and within tolerance of the oracle."""
     x = inputs.prefill_inputs(seed=22, total_tokens=8256, h_k=16, h_v=32, d=128, io_dtype=inputs.BF16,
                               state_std=0.05)
-    monkeypatch.setenv("GDN_PREFILL_SEGMENT_TOKENS", "0")
-    o1, s1 = run_gpu(x, inputs.BF16)
-    monkeypatch.delenv("GDN_PREFILL_SEGMENT_TOKENS")
-    o2, s2 = run_gpu(x, inputs.BF16)
+    o1, s1 = run_gpu(x, inputs.BF16, options=gdn.GdnPrefillOptions(0, 0, -1))  # one pass
+    for seg in (1024, 4096 + 64):
+        o2, s2 = run_gpu(x, inputs.BF16, options=gdn.GdnPrefillOptions(0, 0, seg))
+        assert torch.equal(o1, o2) and torch.equal(s1, s2), seg
+    o2, s2 = run_gpu(x, inputs.BF16)  # automatic
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
-    o3, _ = run_gpu(x, inputs.BF16, state=False)
+    o3, _ = run_gpu(x, inputs.BF16, state=False, options=gdn.GdnPrefillOptions(0, 0, 1024))
     assert torch.equal(o3, o1)
     # in place through the C ABI: state_in == state_out
     st = dev(x["state_in"])
@@ -312,21 +379,19 @@ ROW_CASES = [  # (d, io dtype, out dtype, lengths)
 
 
 @pytest.mark.parametrize("case", range(len(ROW_CASES)))
-def test_row_slices_16_and_32_agree(case, monkeypatch):
-    """The scan splits each state over workgroups of 16 or 32 rows (chosen by
-    occupancy).  Each 16 x 16 tile is computed the same way in both, so the
-    results agree bitwise, and both meet the oracle bound."""
+def test_row_slices_16_and_32_agree(case):
+    """The scan splits each state over workgroups of 16 or 32 rows (gdn_prefill_ex's
+    scan_rows).  Each row's arithmetic is the same in both, so the results agree bitwise
+    with each other and with the default, and meet the oracle bound."""
     d, io, od, lens = ROW_CASES[case]
     x = inputs.prefill_inputs(seed=40 + case, lengths=lens, h_k=2, h_v=4, d=d, io_dtype=io, state_std=0.2)
-    res = {}
-    for rows in ("16", "32"):
-        monkeypatch.setenv("GDN_SCAN_ROWS", rows)
-        res[rows] = run_gpu(x, od)
-    monkeypatch.delenv("GDN_SCAN_ROWS")
-    assert torch.equal(res["16"][0], res["32"][0]) and torch.equal(res["16"][1], res["32"][1])
+    res = {rows: run_gpu(x, od, options=gdn.GdnPrefillOptions(rows, 0, 0)) for rows in (16, 32)}
+    default = run_gpu(x, od)
+    assert torch.equal(res[16][0], res[32][0]) and torch.equal(res[16][1], res[32][1])
+    assert torch.equal(res[16][0], default[0]) and torch.equal(res[16][1], default[1])
     ro, rs = run_oracle(x)
     tol = 1e-5 if io == inputs.F32 else 2e-3
-    out, st = res["16"]
+    out, st = res[16]
     if od == inputs.F32:
         assert normwise(host(out), ro) <= tol
     else:
