@@ -403,6 +403,34 @@ gdn_status gdn_prefill_direct_ex(const gdn_desc *desc,
                                  int32_t fuse, const float *norm_weight, float norm_eps,
                                  void *stream);
 
+/*
+ * gdn_prefill for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, and harnesses that forbid hipMalloc.
+ * The workspace is the library's own: a static device array of
+ * GDN_PREFILL_NOALLOC_WORKSPACE_BYTES (32 MiB) on each GPU it runs on, held
+ * until the process ends.  The call allocates nothing.  Its first call on a
+ * device looks up that device's copy of the array (no allocation either).
+ *
+ * Problems whose gdn_prefill_workspace_bytes() exceeds the array are
+ * rejected with GDN_ERR_WORKSPACE before anything is enqueued (at 32 v-heads
+ * and d = 128 the array holds about 4900 tokens).  All calls on one GPU share
+ * the array, so calls that overlap on one GPU (on different streams, or
+ * from different host threads without ordering) race; serialise them.  The
+ * contents left by an earlier call do not matter.  The status word of the
+ * call lands in the shared array and is not exposed.  Other arguments,
+ * results and errors are those of gdn_prefill, whose result this is bit for
+ * bit.
+ */
+#define GDN_PREFILL_NOALLOC_WORKSPACE_BYTES (32u << 20)
+
+gdn_status gdn_prefill_noalloc(const gdn_desc *desc,
+                               const void *q, const void *k, const void *v,
+                               const float *g, const float *beta,
+                               const float *state_in,
+                               void *out, float *state_out,
+                               const int32_t *cu_seqlens, int32_t chunk,
+                               void *stream);
+
 /* Static, English name of a status code. */
 const char *gdn_status_str(gdn_status status);
 

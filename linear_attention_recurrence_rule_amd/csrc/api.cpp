@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -175,6 +176,35 @@ int cu_count() {
 int decode_grid(int units) {
     const int grid = cu_count() * 2;
     return grid < units ? grid : units;
+}
+
+// Workspace of gdn_prefill_noalloc: a file-scope device array (each GPU the
+// library runs on holds its own copy until the process ends).  In host code
+// `scratch` only names the symbol: its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is passed on.
+constexpr size_t kNoallocBytes = (size_t)GDN_PREFILL_NOALLOC_WORKSPACE_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoallocBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device.
+gdn_status scratch_address(void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(GDN_ERR_UNSUPPORTED, "device index %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(GDN_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return GDN_OK;
 }
 
 // Shared by gdn_prefill_direct and gdn_prefill_direct_ex (fuse flags, norm weight and eps).
@@ -736,6 +766,24 @@ gdn_status gdn_prefill_two_level(const gdn_desc* desc, const void* q, const void
         e = hipMemcpyAsync(state_out, ends + (size_t)(P - 1) * hv * d * d, sbytes, hipMemcpyDeviceToDevice, s);
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "two-level prefill launch: %s", hipGetErrorString(e));
     return GDN_OK;
+}
+
+gdn_status gdn_prefill_noalloc(const gdn_desc* desc, const void* q, const void* k, const void* v,
+                               const float* g, const float* beta, const float* state_in, void* out,
+                               float* state_out, const int32_t* cu_seqlens, int32_t chunk, void* stream) {
+    g_err[0] = 0;
+    gdn_status st = check_desc(desc, true);
+    if (st != GDN_OK) return st;
+    if (chunk != kChunk) return fail(GDN_ERR_UNSUPPORTED, "chunk must be 64 (got %d)", chunk);
+    const size_t need = ws_layout(desc, true).total;
+    if (need > kNoallocBytes)
+        return fail(GDN_ERR_WORKSPACE, "this problem needs %zu workspace bytes; gdn_prefill_noalloc has %zu", need,
+                    kNoallocBytes);
+    void* ws = nullptr;
+    st = scratch_address(&ws);
+    if (st != GDN_OK) return st;
+    return gdn_prefill_ex(desc, q, k, v, g, beta, state_in, out, state_out, cu_seqlens, chunk, nullptr, ws,
+                          kNoallocBytes, stream);
 }
 
 }  // extern "C"

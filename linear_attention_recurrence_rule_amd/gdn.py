@@ -81,6 +81,8 @@ def lib():
             L.gdn_prefill_ex.restype = ctypes.c_int
             L.gdn_prefill_status_offset.argtypes = [dp, ctypes.c_int32]
             L.gdn_prefill_status_offset.restype = sz
+            L.gdn_prefill_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32, vp]
+            L.gdn_prefill_noalloc.restype = ctypes.c_int
             L.gdn_prefill_prepare.argtypes = [dp, vp, vp, vp, vp, vp, vp, ctypes.c_int32, vp, sz, vp]
             L.gdn_prefill_prepare.restype = ctypes.c_int
             L.gdn_prefill_scan.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32, vp, sz, vp]
@@ -171,6 +173,16 @@ def gdn_prefill_ex(desc, q, k, v, g, beta, state_in, out, state_out, cu_seqlens,
     _check(lib().gdn_prefill_ex(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                 _ptr(state_in), _ptr(out), _ptr(state_out), _ptr(cu_seqlens), int(chunk), opt,
                                 _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+GDN_PREFILL_NOALLOC_WORKSPACE_BYTES = 32 << 20
+
+
+def gdn_prefill_noalloc(desc, q, k, v, g, beta, state_in, out, state_out, cu_seqlens, chunk, stream=None):
+    """gdn_prefill with the library's static workspace (no allocation anywhere)."""
+    _check(lib().gdn_prefill_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                     _ptr(state_in), _ptr(out), _ptr(state_out), _ptr(cu_seqlens), int(chunk),
+                                     _stream(stream)))
 
 
 def gdn_prefill_status_offset(desc: GdnDesc, chunk: int = CHUNK) -> int:

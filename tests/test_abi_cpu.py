@@ -35,6 +35,7 @@ def L():
 def test_exports_every_declared_function(L):
     names = gdn.declared_functions()
     assert set(names) == {"gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_prefill_ex", "gdn_prefill_status_offset",
+                          "gdn_prefill_noalloc",
                           "gdn_prefill_prepare",
                           "gdn_prefill_scan", "gdn_prefill_direct", "gdn_prefill_segmented_workspace_bytes",
                           "gdn_prefill_segmented", "gdn_prefill_two_level_workspace_bytes", "gdn_prefill_two_level",
