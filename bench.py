@@ -3,15 +3,21 @@
 
 One step = one gdn_prefill call on the 4K-token workload (32 v-heads over 16
 q/k heads, d = 128, bf16 in and out, fp32 state, 64-token blocks), with inputs
-already resident in HBM.  ``value`` is prefill tokens/s over the K timed steps.
+already resident in HBM.  ``value`` is prefill tokens/s over the K timed steps,
+after --warmup calls and at least 0.25 s of warm-up calls.
 The same JSON line also reports:
+  * the other prefill workloads (fp32 single head T = 256, 128K tokens with an
+    initial state, 16 packed sequences): tok/s and whole-call fractions of the
+    matrix-core and HBM peaks;
   * decode: 512 consecutive gdn_decode_step launches on the decode workload
     (64 sequences x 32 v-heads, d = 128, fp32 state), the same loop replayed
-    from a HIP graph, and the same steps through gdn_decode_step_ex with raw
-    gate inputs and the output normalisation folded in;
+    from a HIP graph, the same steps through gdn_decode_step_ex with raw gate
+    inputs and the output normalisation folded in, the same steps rotating over
+    four copies of the state (cache-cold), and 256 sequences (a 512 MiB state);
   * roofline of the dominant prefill kernel: algorithmic flops per launch over
-    its average HIP-event duration, against the 2.5 PFLOP/s dense fp16
-    matrix-core peak; the decode kernel's algorithmic bytes against 8 TB/s;
+    its average duration in a loop of back-to-back launches of that kernel's
+    phase alone, against the 2.5 PFLOP/s dense fp16 matrix-core peak; the
+    decode kernel's algorithmic bytes per cache-cold step against 8 TB/s;
   * cpu_baseline: the fp64 CPU oracle on this host, same workload;
   * ceilings: measured matrix-core and read-modify-write stream rates on this
     GPU, and each roofline's fraction of them beside its fraction of the spec peak.
@@ -33,6 +39,7 @@ sys.path.insert(0, ROOT)
 METRIC = "GDN prefill tok/s @4K (MFMA %) + decode steps/s (state GB/s, % HBM peak)"
 PEAK_FP16_TFLOPS = 2500.0     # MI355X dense fp16/bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E peak
+PEAK_FP32_TFLOPS = 157.3      # MI355X dense fp32 matrix-core peak
 PREFILL_WL = "prefill_t4096_hv32_hk16_d128"
 DECODE_WL = "decode_n64_hv32_hk16_d128_512steps"
 
@@ -71,6 +78,35 @@ def kernel_source_digest():
             src = b"\n".join(line.rstrip() for line in src.split(b"\n") if line.strip())
             h.update(name.encode() + b"\0" + src)
     return h.hexdigest()[:16]
+
+
+def make_timers(torch, np, stream):
+    """warm(fn): run fn back to back for at least min_s seconds of wall time (the clocks
+    ramp up over the first few milliseconds).  loop_us(fn, n): median over `reps`
+    repetitions of n back-to-back calls, in µs per call, from HIP events recorded on
+    the stream the kernels are launched on."""
+    def warm(fn, min_s=0.25, min_calls=3):
+        t0, n = time.perf_counter(), 0
+        while n < min_calls or time.perf_counter() - t0 < min_s:
+            fn()
+            n += 1
+            if n % 16 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        return n
+
+    def loop_us(fn, n, reps=3):
+        res = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(n):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            res.append(e0.elapsed_time(e1) * 1e3 / n)
+        return float(np.median(res))
+    return warm, loop_us
 
 
 def measured_traffic(kernel):
@@ -326,134 +362,119 @@ def decode_sweep(L, gdn, inputs, to_dev, torch, np, dev):
         del q, k, v, g, b, xg, xb, state, out, w
 
 
+def time_prefill_workload(L, gdn, inputs, to_dev, torch, np, dev, name, *, with_cpu=False, with_direct=False):
+    """One prefill workload through gdn_prefill: time per call, tok/s, both whole-call roofline
+    fractions, and the one-pass kernel split (prepare-only and scan-only loops, back to back).
+    Optionally the direct token scan and the fp64 CPU oracle (one thread and all usable cores)."""
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    warm, loop_us = make_timers(torch, np, stream)
+    w = inputs.WORKLOADS[name]
+    x = inputs.workload_inputs(w)
+    T, N, h_k, h_v, d = x["total_tokens"], x["num_seqs"], w.h_k, w.h_v, w.d
+    q, k, v, g, b = (to_dev(x[n]) for n in ("q", "k", "v", "g", "beta"))
+    s_in, cu = to_dev(x["state_in"]), to_dev(x["cu_seqlens"])
+    odt = torch.bfloat16 if w.out_dtype == inputs.BF16 else torch.float32
+    out = torch.empty((T, h_v, d), dtype=odt, device=dev)
+    s_out = torch.empty((N, h_v, d, d), dtype=torch.float32, device=dev)
+    desc = gdn.make_desc(num_seqs=N, total_tokens=T, h_k=h_k, h_v=h_v, d=d, io_dtype=w.io_dtype,
+                         out_dtype=w.out_dtype)
+    dref = ctypes.byref(desc)
+    wsb = gdn.gdn_prefill_workspace_bytes(desc)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    ptr = lambda z: None if z is None else z.data_ptr()  # noqa: E731
+    P = [ptr(z) for z in (q, k, v, g, b, s_in, out, s_out, cu)]
+
+    def chk(st):
+        if st:
+            raise gdn.GdnError(st, gdn.last_error())
+
+    def call():
+        chk(L.gdn_prefill(dref, P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[8], 64, ws.data_ptr(), wsb, sp))
+
+    one_pass = gdn.GdnPrefillOptions(0, 0, -1)
+
+    def call_one_pass():
+        chk(L.gdn_prefill_ex(dref, P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[8], 64, ctypes.byref(one_pass),
+                             ws.data_ptr(), wsb, sp))
+
+    def prep():
+        chk(L.gdn_prefill_prepare(dref, P[0], P[1], P[2], P[3], P[4], P[8], 64, ws.data_ptr(), wsb, sp))
+
+    def scan():
+        chk(L.gdn_prefill_scan(dref, P[0], P[1], P[2], P[5], P[6], P[7], P[8], 64, ws.data_ptr(), wsb, sp))
+
+    def direct():
+        chk(L.gdn_prefill_direct(dref, P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[8], sp))
+
+    reps = 100 if T <= 8192 else 10
+    warm(call, 0.2)
+    us = loop_us(call, reps)
+    us_one_pass = loop_us(call_one_pass, reps)
+    prep()
+    warm(prep, 0.1)
+    us_prep = loop_us(prep, reps)
+    prep()
+    warm(scan, 0.1)
+    us_scan = loop_us(scan, reps)
+    us_direct = None
+    if with_direct and T <= 8192:
+        warm(direct, 0.1)
+        us_direct = round(loop_us(direct, 10 if T > 1024 else reps), 2)
+    cpu = None
+    if with_cpu and T <= 8192:
+        from oracle import oracle
+        ncpu = len(os.sched_getaffinity(0))
+        cpu = {}
+        for threads in sorted({1, max(1, min(N * h_v, ncpu))}):
+            ts = []
+            for _ in range(3):
+                t0 = time.perf_counter()
+                oracle.scan(x["q"], x["k"], x["v"], x["g"], x["beta"], h_k=h_k, h_v=h_v, state_in=x["state_in"],
+                            cu_seqlens=x["cu_seqlens"], threads=threads)
+                ts.append(time.perf_counter() - t0)
+            cpu["oracle_s_%d_threads" % threads] = round(float(np.median(ts)), 4)
+        cpu["host_cores"] = ncpu
+    io = 2 if w.io_dtype == inputs.BF16 else 4
+    ob = 2 if w.out_dtype == inputs.BF16 else 4
+    f_prep, f_scan, nbytes = algorithmic_prefill(T, h_v, h_k, d, out_bytes=ob, io_bytes=io,
+                                                 state_in=s_in is not None)
+    nbytes += (N - 1) * h_v * d * d * 4 * (2 if s_in is not None else 1)
+    mfma_peak = PEAK_FP16_TFLOPS if w.io_dtype == inputs.BF16 else PEAK_FP32_TFLOPS
+    res = {
+        "workload": name, "num_seqs": N, "total_tokens": T, "h_v": h_v, "h_k": h_k, "d": d,
+        "io_dtype": "bf16" if w.io_dtype == inputs.BF16 else "f32",
+        "state_in": "N(0,%g)" % w.state_std if s_in is not None else "zeros",
+        "us_per_call": round(us, 2), "tok_per_s": T / us * 1e6,
+        "us_one_pass": round(us_one_pass, 2),
+        "kernels_us_one_pass": {"chunk_prep": round(us_prep, 2), "chunk_scan": round(us_scan, 2)},
+        "mfma_peak_tflops": mfma_peak,
+        "mfma_frac_whole_call": round((f_prep + f_scan) / (us * 1e-6) / (mfma_peak * 1e12), 4),
+        "hbm_frac_whole_call": round(nbytes / (us * 1e-6) / (PEAK_HBM_GBS * 1e9), 4),
+        "algorithmic_gflop": round((f_prep + f_scan) / 1e9, 3), "algorithmic_mib": round(nbytes / 2 ** 20, 2),
+        "timing": "median of 3 repetitions of %d back-to-back calls after >=0.2 s of warm-up calls; "
+                  "kernel split from prepare-only and scan-only loops" % reps,
+    }
+    if with_direct:
+        res["direct_us"] = us_direct
+    if with_cpu:
+        res["cpu_oracle"] = cpu
+    del q, k, v, g, b, s_in, cu, out, s_out, ws, x
+    return res
+
+
 def prefill_configs(L, gdn, inputs, to_dev, torch, np, dev, with_cpu=True):
     """Every prefill workload (single-head fp32 T=256, 4K, 128K with an initial state, 16 packed
     sequences of drawn lengths) through gdn_prefill: time per call, tok/s, the per-kernel split
     and both roofline fractions of the whole call; up to 8K tokens also the direct token scan and
     the fp64 CPU oracle on one thread and on all usable cores.  Prints one JSON line per workload."""
-    stream = torch.cuda.current_stream()
-    sp = stream.cuda_stream
     for name, w in inputs.WORKLOADS.items():
         if w.kind != "prefill":
             continue
         print("configs: generating %s" % name, file=sys.stderr, flush=True)
-        x = inputs.workload_inputs(w)
-        T, N, h_k, h_v, d = x["total_tokens"], x["num_seqs"], w.h_k, w.h_v, w.d
-        q, k, v, g, b = (to_dev(x[n]) for n in ("q", "k", "v", "g", "beta"))
-        s_in, cu = to_dev(x["state_in"]), to_dev(x["cu_seqlens"])
-        odt = torch.bfloat16 if w.out_dtype == inputs.BF16 else torch.float32
-        out = torch.empty((T, h_v, d), dtype=odt, device=dev)
-        s_out = torch.empty((N, h_v, d, d), dtype=torch.float32, device=dev)
-        desc = gdn.make_desc(num_seqs=N, total_tokens=T, h_k=h_k, h_v=h_v, d=d, io_dtype=w.io_dtype,
-                             out_dtype=w.out_dtype)
-        dref = ctypes.byref(desc)
-        wsb = gdn.gdn_prefill_workspace_bytes(desc)
-        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
-        ptr = lambda z: None if z is None else z.data_ptr()  # noqa: E731
-        P = [ptr(z) for z in (q, k, v, g, b, s_in, out, s_out, cu)]
-
-        def call():
-            st = L.gdn_prefill(dref, P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[8], 64, ws.data_ptr(),
-                               wsb, sp)
-            if st:
-                raise gdn.GdnError(st, gdn.last_error())
-
-        def prep():
-            st = L.gdn_prefill_prepare(dref, P[0], P[1], P[2], P[3], P[4], P[8], 64, ws.data_ptr(), wsb, sp)
-            if st:
-                raise gdn.GdnError(st, gdn.last_error())
-
-        def scan():
-            st = L.gdn_prefill_scan(dref, P[0], P[1], P[2], P[5], P[6], P[7], P[8], 64, ws.data_ptr(), wsb, sp)
-            if st:
-                raise gdn.GdnError(st, gdn.last_error())
-
-        def direct():
-            st = L.gdn_prefill_direct(dref, P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[8], sp)
-            if st:
-                raise gdn.GdnError(st, gdn.last_error())
-
-        reps = 100 if T <= 8192 else 10
-
-        def timed(fn, n):
-            """Median over 5 repetitions of n back-to-back calls, µs per call."""
-            res = []
-            for _ in range(5):
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                for _ in range(n):
-                    fn()
-                e1.record(stream)
-                torch.cuda.synchronize()
-                res.append(e0.elapsed_time(e1) * 1e3 / n)
-            return float(np.median(res))
-
-        for _ in range(10):
-            call()
-        torch.cuda.synchronize()
-        us = timed(call, reps)
-        # gdn_prefill may run a long single sequence as segments; the one-pass time
-        # (prepare + scan over all blocks, as split below) is reported beside it
-        one_pass = gdn.GdnPrefillOptions(0, 0, -1)
-
-        def call_one_pass():
-            st = L.gdn_prefill_ex(dref, P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[8], 64,
-                                  ctypes.byref(one_pass), ws.data_ptr(), wsb, sp)
-            if st:
-                raise gdn.GdnError(st, gdn.last_error())
-
-        us_one_pass = timed(call_one_pass, reps)
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
-        for e in evs:
-            e[0].record(stream)
-            prep()
-            e[1].record(stream)
-            scan()
-            e[2].record(stream)
-        torch.cuda.synchronize()
-        us_prep = 1e3 * float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
-        us_scan = 1e3 * float(np.median([e[1].elapsed_time(e[2]) for e in evs]))
-        us_direct = None
-        if T <= 8192:
-            for _ in range(3):
-                direct()
-            torch.cuda.synchronize()
-            us_direct = round(timed(direct, 10 if T > 1024 else reps), 2)
-        cpu = None
-        if with_cpu and T <= 8192:
-            from oracle import oracle
-            ncpu = len(os.sched_getaffinity(0))
-            cpu = {}
-            for threads in sorted({1, max(1, min(N * h_v, ncpu))}):
-                ts = []
-                for _ in range(3):
-                    t0 = time.perf_counter()
-                    oracle.scan(x["q"], x["k"], x["v"], x["g"], x["beta"], h_k=h_k, h_v=h_v, state_in=x["state_in"],
-                                cu_seqlens=x["cu_seqlens"], threads=threads)
-                    ts.append(time.perf_counter() - t0)
-                cpu["oracle_s_%d_threads" % threads] = round(float(np.median(ts)), 4)
-            cpu["host_cores"] = ncpu
-        io = 2 if w.io_dtype == inputs.BF16 else 4
-        ob = 2 if w.out_dtype == inputs.BF16 else 4
-        f_prep, f_scan, nbytes = algorithmic_prefill(T, h_v, h_k, d, out_bytes=ob, io_bytes=io,
-                                                     state_in=s_in is not None)
-        nbytes += (N - 1) * h_v * d * d * 4 * (2 if s_in is not None else 1)
-        mfma_peak = PEAK_FP16_TFLOPS if w.io_dtype == inputs.BF16 else 157.3
-        print(json.dumps({"prefill_config": {
-            "workload": name, "num_seqs": N, "total_tokens": T, "h_v": h_v, "h_k": h_k, "d": d,
-            "io_dtype": "bf16" if w.io_dtype == inputs.BF16 else "f32",
-            "state_in": "N(0,%g)" % w.state_std if s_in is not None else "zeros",
-            "us_per_call": round(us, 2), "tok_per_s": T / us * 1e6,
-            "us_one_pass": round(us_one_pass, 2),
-            "kernels_us_one_pass": {"chunk_prep": round(us_prep, 2), "chunk_scan": round(us_scan, 2)},
-            "direct_us": us_direct,
-            "mfma_peak_tflops": mfma_peak,
-            "mfma_frac_whole_call": round((f_prep + f_scan) / (us * 1e-6) / (mfma_peak * 1e12), 4),
-            "hbm_frac_whole_call": round(nbytes / (us * 1e-6) / (PEAK_HBM_GBS * 1e9), 4),
-            "algorithmic_gflop": round((f_prep + f_scan) / 1e9, 3), "algorithmic_mib": round(nbytes / 2 ** 20, 2),
-            "reps": reps, "timing": "median of 5 repetitions of back-to-back calls after 10 warm-up calls",
-            "cpu_oracle": cpu}}), flush=True)
-        del q, k, v, g, b, s_in, cu, out, s_out, ws, x
+        print(json.dumps({"prefill_config": time_prefill_workload(L, gdn, inputs, to_dev, torch, np, dev, name,
+                                                                  with_cpu=with_cpu, with_direct=True)}),
+              flush=True)
 
 
 def main():
@@ -547,9 +568,11 @@ def main():
         if st:
             raise gdn.GdnError(st, gdn.last_error())
 
+    warm, loop_us = make_timers(torch, np, stream)
+    # warm-up: --warmup calls, and at least 0.25 s of back-to-back calls whatever --warmup says
     for _ in range(args.warmup):
         prefill_call()
-    torch.cuda.synchronize()
+    warm(prefill_call, 0.25)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_wall = time.perf_counter()
     e0.record(stream)
@@ -561,18 +584,15 @@ def main():
     ms_step = e0.elapsed_time(e1) / args.steps
     tok_s = T / (ms_step * 1e-3)
 
-    # per-kernel durations (events between the two launches of each call)
-    n_k = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_k)]
-    for i in range(n_k):
-        evs[i][0].record(stream)
-        prepare_call()
-        evs[i][1].record(stream)
-        scan_call()
-        evs[i][2].record(stream)
-    torch.cuda.synchronize()
-    us_prep = 1e3 * float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    us_scan = 1e3 * float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    # per-kernel durations: prepare-only and scan-only loops of back-to-back launches on the
+    # launch stream (the scan rereads the one prepared workspace), each after its own warm-up
+    n_k = max(args.steps, 50)
+    prepare_call()
+    warm(prepare_call, 0.1)
+    us_prep = loop_us(prepare_call, n_k)
+    prepare_call()
+    warm(scan_call, 0.1)
+    us_scan = loop_us(scan_call, n_k)
     f_prep, f_scan, nbytes = algorithmic_prefill(T, h_v, h_k, d)
     kern = {"chunk_prep": (us_prep, f_prep), "chunk_scan": (us_scan, f_scan)}
     dom = max(kern, key=lambda n: kern[n][0])
@@ -581,7 +601,9 @@ def main():
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": PEAK_FP16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / PEAK_FP16_TFLOPS, 4), "traffic": measured_traffic(dom),
                 "avg_launch_us": round(us_dom, 2),
-                "algorithmic_gflop_per_launch": round(f_dom / 1e9, 3)}
+                "algorithmic_gflop_per_launch": round(f_dom / 1e9, 3),
+                "timing": "average launch of %d back-to-back %s calls (HIP events on the launch stream)"
+                          % (n_k, "gdn_prefill_scan" if dom == "chunk_scan" else "gdn_prefill_prepare")}
     prefill_info = {
         "tok_per_s": tok_s, "us_per_call": ms_step * 1e3,
         "mfma_frac_whole_call": (f_prep + f_scan) / (ms_step * 1e-3) / (PEAK_FP16_TFLOPS * 1e12),
@@ -591,6 +613,16 @@ def main():
         "wall_s_timed_loop": t_wall,
     }
     del ws, out, q, k, v, g, b
+
+    # ---------------- the other prefill configs ----------------
+    others = {}
+    for name in ("single_head_t256_d64_f32", "prefill_t131072_hv32_hk16_d128", "varlen_n16_hv32_hk16_d128"):
+        print("bench: %s" % name, file=sys.stderr, flush=True)
+        r = time_prefill_workload(L, gdn, inputs, to_dev, torch, np, dev, name)
+        others[name] = {k2: r[k2] for k2 in ("num_seqs", "total_tokens", "io_dtype", "state_in", "tok_per_s",
+                                             "us_per_call", "mfma_frac_whole_call", "hbm_frac_whole_call",
+                                             "mfma_peak_tflops", "kernels_us_one_pass")}
+        torch.cuda.empty_cache()
 
     # ---------------- decode ----------------
     wd = inputs.WORKLOADS[DECODE_WL]
@@ -606,38 +638,26 @@ def main():
     base = [dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dg.data_ptr(), db.data_ptr()]
     sptr, optr = state.data_ptr(), dout.data_ptr()
 
-    def decode_call(t):
+    def decode_call(t, sp_=None, st_ptr=None):
         st = L.gdn_decode_step(ddref, base[0] + t * qs, base[1] + t * ks, base[2] + t * vs_, base[3] + t * gs,
-                               base[4] + t * bs, sptr, optr, sp)
+                               base[4] + t * bs, st_ptr or sptr, optr, sp_ or sp)
         if st:
             raise gdn.GdnError(st, gdn.last_error())
 
-    for t in range(10):
-        decode_call(t % steps)
-    torch.cuda.synchronize()
-    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    d0.record(stream)
-    for t in range(steps):
-        decode_call(t)
-    d1.record(stream)
-    torch.cuda.synchronize()
-    us_dec = d0.elapsed_time(d1) * 1e3 / steps
+    def decode_loop():
+        for t in range(steps):
+            decode_call(t)
+    warm(lambda: decode_call(0), 0.1)
+    us_dec = loop_us(decode_loop, 1) / steps
     # the same loop captured once in a HIP graph (device-resident inputs), replayed
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         cap = torch.cuda.current_stream().cuda_stream
         for t in range(steps):
-            st = L.gdn_decode_step(ddref, base[0] + t * qs, base[1] + t * ks, base[2] + t * vs_, base[3] + t * gs,
-                                   base[4] + t * bs, sptr, optr, cap)
-            if st:
-                raise gdn.GdnError(st, gdn.last_error())
+            decode_call(t, sp_=cap)
     graph.replay()
     torch.cuda.synchronize()
-    d0.record(stream)
-    graph.replay()
-    d1.record(stream)
-    torch.cuda.synchronize()
-    us_dec_graph = d0.elapsed_time(d1) * 1e3 / steps
+    us_dec_graph = loop_us(graph.replay, 1) / steps
     del graph
     # the same steps with the per-token ops beside the update folded in
     # (gdn_decode_step_ex): raw gate inputs (the workload's N(0, 1) draws x_g, x_beta)
@@ -647,24 +667,51 @@ def main():
     xg_base, xb_base, nw_ptr = dxg.data_ptr(), dxb.data_ptr(), nw.data_ptr()
     fuse = gdn.GDN_FUSE_GATE_ACTIVATIONS | gdn.GDN_FUSE_OUTPUT_NORM
 
-    def fused_call(t):
-        st = L.gdn_decode_step_ex(ddref, base[0] + t * qs, base[1] + t * ks, base[2] + t * vs_, xg_base + t * gs,
-                                  xb_base + t * bs, sptr, optr, fuse, nw_ptr, 1e-6, sp)
-        if st:
-            raise gdn.GdnError(st, gdn.last_error())
-
-    for t in range(10):
-        fused_call(t % steps)
-    torch.cuda.synchronize()
-    d0.record(stream)
-    for t in range(steps):
-        fused_call(t)
-    d1.record(stream)
-    torch.cuda.synchronize()
-    us_dec_fused = d0.elapsed_time(d1) * 1e3 / steps
+    def fused_loop():
+        for t in range(steps):
+            st = L.gdn_decode_step_ex(ddref, base[0] + t * qs, base[1] + t * ks, base[2] + t * vs_, xg_base + t * gs,
+                                      xb_base + t * bs, sptr, optr, fuse, nw_ptr, 1e-6, sp)
+            if st:
+                raise gdn.GdnError(st, gdn.last_error())
+    fused_loop()
+    us_dec_fused = loop_us(fused_loop, 1) / steps
     del dxg, dxb, nw
+    # cache-cold: the same steps rotating over four copies of the 128 MiB state (512 MiB in all,
+    # twice the 256 MiB last-level cache), so each step's state was evicted since it was last used
+    copies = [state] + [state.clone() for _ in range(3)]
+    cptr = [c.data_ptr() for c in copies]
+
+    def cold_loop():
+        for t in range(steps):
+            decode_call(t, st_ptr=cptr[t % 4])
+    cold_loop()
+    us_dec_cold = loop_us(cold_loop, 1) / steps
+    del copies
     dbytes = algorithmic_decode(N, dh_v, dh_k, dd)
     dec_gbs = dbytes / (us_dec * 1e-6) / 1e9
+    cold_gbs = dbytes / (us_dec_cold * 1e-6) / 1e9
+    # decode at N = 256 sequences (a 512 MiB state, beyond the cache by itself)
+    N2 = 256
+    y2 = inputs.decode_inputs(seed=8, num_seqs=N2, steps=16, h_k=dh_k, h_v=dh_v, d=dd, io_dtype=inputs.BF16)
+    q2, k2_, v2, g2, b2 = (to_dev(y2[n]) for n in ("q", "k", "v", "g", "beta"))
+    st2 = to_dev(y2["state"])
+    o2 = torch.empty((N2, dh_v, dd), dtype=torch.bfloat16, device=dev)
+    desc2 = gdn.make_desc(num_seqs=N2, total_tokens=N2, h_k=dh_k, h_v=dh_v, d=dd, io_dtype=gdn.GDN_BF16,
+                          out_dtype=gdn.GDN_BF16)
+    d2ref = ctypes.byref(desc2)
+    b2p = [t_.data_ptr() for t_ in (q2, k2_, v2, g2, b2)]
+    s2 = [t_.stride(0) * t_.element_size() for t_ in (q2, k2_, v2, g2, b2)]
+
+    def loop256():
+        for t in range(16):
+            st = L.gdn_decode_step(d2ref, *[b2p[i] + t * s2[i] for i in range(5)], st2.data_ptr(), o2.data_ptr(), sp)
+            if st:
+                raise gdn.GdnError(st, gdn.last_error())
+    loop256()
+    us_256 = loop_us(loop256, 4) / 16
+    bytes256 = algorithmic_decode(N2, dh_v, dh_k, dd)
+    gbs256 = bytes256 / (us_256 * 1e-6) / 1e9
+    del q2, k2_, v2, g2, b2, st2, o2, y2
     decode_info = {"workload": DECODE_WL, "steps_timed": steps, "us_per_step": us_dec,
                    "steps_per_s": 1e6 / us_dec, "tok_per_s": N * 1e6 / us_dec,
                    "us_per_step_hip_graph": us_dec_graph,
@@ -672,15 +719,25 @@ def main():
                    "fused": "gdn_decode_step_ex: raw gate inputs and the per-head output RMS norm in the step "
                             "(%.1f%% of HBM peak)" % (100 * dbytes / (us_dec_fused * 1e-6) / (PEAK_HBM_GBS * 1e9)),
                    "algorithmic_mb_per_step": dbytes / 1e6,
-                   "roofline": {"bound": "hbm", "kernel": "decode_step", "achieved": round(dec_gbs, 1),
-                                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+                   "cache_assisted": {"gb_per_s": round(dec_gbs, 1), "hbm_frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+                                      "note": "the 128 MiB state stays partly in the 256 MiB last-level cache "
+                                              "between steps"},
+                   "cache_cold": {"us_per_step": round(us_dec_cold, 2), "gb_per_s": round(cold_gbs, 1),
+                                  "hbm_frac": round(cold_gbs / PEAK_HBM_GBS, 4),
+                                  "how": "steps rotate over 4 copies of the state (512 MiB)"},
+                   "n256": {"num_seqs": N2, "state_mib": N2 * dh_v * dd * dd * 4 / 2 ** 20,
+                            "us_per_step": round(us_256, 2), "tok_per_s": round(N2 * 1e6 / us_256),
+                            "gb_per_s": round(gbs256, 1), "hbm_frac": round(gbs256 / PEAK_HBM_GBS, 4)},
+                   "roofline": {"bound": "hbm", "kernel": "decode_step", "achieved": round(cold_gbs, 1),
+                                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(cold_gbs / PEAK_HBM_GBS, 4),
+                                "basis": "cache-cold steps (state rotated over 512 MiB)",
                                 "traffic": measured_traffic("decode_step")}}
     del dq, dk, dv, dg, db, state, dout
 
     ceilings = measure_ceilings(torch, np, dev)
     if ceilings:
         roofline["frac_of_measured_ceiling"] = round(ach / ceilings["mfma_f16_tflops"], 4)
-        decode_info["roofline"]["frac_of_measured_ceiling"] = round(dec_gbs / ceilings["rmw_stream_gbs"], 4)
+        decode_info["roofline"]["frac_of_measured_ceiling"] = round(cold_gbs / ceilings["rmw_stream_gbs"], 4)
 
     if args.calibrate_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -712,7 +769,8 @@ def main():
         "vs_baseline": None, "dtype": "f16-mfma/f32", "data": "synthetic",
         "config": {"workload": PREFILL_WL, "total_tokens": T, "h_v": h_v, "h_k": h_k, "d": d, "chunk": 64,
                    "io_dtype": "bf16", "out_dtype": "bf16", "state_in": "zeros"},
-        "roofline": roofline, "cpu_baseline": cpu, "prefill": prefill_info, "decode": decode_info,
+        "roofline": roofline, "cpu_baseline": cpu, "prefill": prefill_info, "prefill_other_configs": others,
+        "decode": decode_info,
         "ceilings": ceilings,
     }
     print(json.dumps(rec))
