@@ -795,8 +795,28 @@ __global__ __launch_bounds__(TPS_MAX_THREADS) void chunk_scan_tp_kernel(
         };
         auto step = [&](int c, bf8_t(&cur)[NKB]) __attribute__((always_inline)) {
             const Slot& B = ring[c % RING];
+            typedef __attribute__((address_space(3))) s4v_t* lds_s4;
             f4_t zc[NB];
             lds_barrier();  // B1: block c in its slot, S^T of block c in LDS
+            // Everything of block c's slot that the later phases read, read now (one LDS round
+            // trip less in each of them): factors, v, and the T and P fragments of token block
+            // tb (for tb < 2 the second fragment repeats the first and goes unused).
+            const f4_t gck = *reinterpret_cast<const f4_t*>(&B.fac[TpRec::GCK + 16 * tb + 4 * q4]);
+            const f4_t sc = *reinterpret_cast<const f4_t*>(&B.fac[TpRec::SCK + 16 * tb + 4 * q4]);
+            const f4_t gcq = *reinterpret_cast<const f4_t*>(&B.fac[TpRec::GCQ + 16 * tb + 4 * q4]);
+            s4v_t vv[NB];
+            if (!lin) {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)  // v[token 16tb + 4q + e][row 16nb + j], e = 0..3
+                    vv[nb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_s4)(B.vs + (16 * tb + 4 * q4 + (j16 >> 2)) * RS + 16 * nb + 4 * (j16 & 3)));
+            }
+            Frag<_Float16> tf[2], pf[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                tf[kb] = frag_stored<_Float16>(B.tp[0], tri_frag(tb, kb), lane);
+                if (MODE == 0) pf[kb] = frag_stored<_Float16>(B.tp[1], tri_frag(tb, kb), lane);
+            }
             if (MODE == 0) {
                 if constexpr (Sh::QDMA) {
 #pragma unroll
@@ -814,56 +834,40 @@ __global__ __launch_bounds__(TPS_MAX_THREADS) void chunk_scan_tp_kernel(
                 }
             }
             lds_barrier();  // BX: partial products in LDS
-            {   // R = V - diag(gamma c) (Y_0 + Y_1), token block tb
-                const f4_t gck = *reinterpret_cast<const f4_t*>(&B.fac[TpRec::GCK + 16 * tb + 4 * q4]);
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    f4_t yy = *reinterpret_cast<const f4_t*>(sY + (((nb * CPB) * 4 + tb) * WAVE + lane) * 4);
+            for (int nb = 0; nb < NB; ++nb) {  // R = V - diag(gamma c) Y, token block tb
+                f4_t yy = *reinterpret_cast<const f4_t*>(sY + (((nb * CPB) * 4 + tb) * WAVE + lane) * 4);
 #pragma unroll
-                    for (int cq = 1; cq < CPB; ++cq)
-                        yy += *reinterpret_cast<const f4_t*>(sY + (((nb * CPB + cq) * 4 + tb) * WAVE + lane) * 4);
-                    f4_t r;
-                    if (lin) {
-                        r = -(gck * yy);
-                    } else {
-                        // v[token 16tb + 4q + e][row 16nb + j] for e = 0..3: one transposing read
-                        typedef __attribute__((address_space(3))) s4v_t* lds_s4;
-                        const s4v_t vv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_s4)(B.vs + (16 * tb + 4 * q4 + (j16 >> 2)) * RS + 16 * nb + 4 * (j16 & 3)));
+                for (int cq = 1; cq < CPB; ++cq)
+                    yy += *reinterpret_cast<const f4_t*>(sY + (((nb * CPB + cq) * 4 + tb) * WAVE + lane) * 4);
+                f4_t r;
+                if (lin) {
+                    r = -(gck * yy);
+                } else {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            r[e] = __uint_as_float((uint32_t)(uint16_t)vv[e] << 16) - gck[e] * yy[e];
-                    }
-                    store_part<_Float16>(sR, kbt * NB + nb, part, lane, r);
+                    for (int e = 0; e < 4; ++e)
+                        r[e] = __uint_as_float((uint32_t)(uint16_t)vv[nb][e] << 16) - gck[e] * yy[e];
                 }
+                store_part<_Float16>(sR, kbt * NB + nb, part, lane, r);
             }
             lds_barrier();  // BR: R in LDS
-            {   // U = T R for token block tb (T is zero right of its diagonal block), and
-                // diag(s c) U split into high and low parts
-                const f4_t sc = *reinterpret_cast<const f4_t*>(&B.fac[TpRec::SCK + 16 * tb + 4 * q4]);
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    f4_t u = {0.f, 0.f, 0.f, 0.f};
+            for (int nb = 0; nb < NB; ++nb) {  // U = T R (T is zero right of its diagonal block), its parts
+                f4_t u = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int kb = 0; kb < 2; ++kb)
-                        if (kb <= kbt)
-                            mma(u, frag_stored<_Float16>(B.tp[0], tri_frag(tb, kb), lane),
-                                frag_stored<_Float16>(sR, kb * NB + nb, lane));
-                    if (MODE == 0) store_part<_Float16>(sU, kbt * NB + nb, part, lane, u);
-                    store_split(sUh, sUl, kbt * NB + nb, part, lane, u * sc);
-                }
+                for (int kb = 0; kb < 2; ++kb)
+                    if (kb <= kbt) mma(u, tf[kb], frag_stored<_Float16>(sR, kb * NB + nb, lane));
+                if (MODE == 0) store_part<_Float16>(sU, kbt * NB + nb, part, lane, u);
+                store_split(sUh, sUl, kbt * NB + nb, part, lane, u * sc);
             }
             lds_barrier();  // BU: U and its parts in LDS
             if (MODE == 0) {  // O = diag(gamma c_q) Z + P U, token block tb
-                const f4_t gcq = *reinterpret_cast<const f4_t*>(&B.fac[TpRec::GCQ + 16 * tb + 4 * q4]);
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
                     f4_t o = gcq * zc[nb];
 #pragma unroll
                     for (int kb = 0; kb < 2; ++kb)
-                        if (kb <= kbt)
-                            mma(o, frag_stored<_Float16>(B.tp[1], tri_frag(tb, kb), lane),
-                                frag_stored<_Float16>(sU, kb * NB + nb, lane));
+                        if (kb <= kbt) mma(o, pf[kb], frag_stored<_Float16>(sU, kb * NB + nb, lane));
                     bad |= any_nonfinite(o);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
