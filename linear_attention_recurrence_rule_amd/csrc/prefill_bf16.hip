@@ -992,6 +992,316 @@ __global__ __launch_bounds__(TPS_MAX_THREADS) void chunk_scan_tp_kernel(
 }
 
 // ============================================================================================
+// chunk_scan_tpf: the scan for 16-row slices, two waves per token block
+// ============================================================================================
+// The inputs and the arithmetic of chunk_scan_tp (MODE 0, one 16-row slice per
+// workgroup), with the roles arranged so that no partial product crosses waves.
+// Every wave that contracts with S^T reads the whole of its bf16 high / low
+// parts from LDS, and per-wave LDS reads are the scarce resource, so the work of
+// token block tb is split over two waves:
+//   Y-wave tb (w = tb):     Y and R, U = T R and the parts of diag(s c) U, and
+//                           the update of the fp32 S^T tiles 16 TPW tb .. + 16 TPW - 1
+//                           of the keys (TPW = D / 64 tiles), which it holds;
+//   Z-wave tb (w = 4 + tb): Z = Q^raw S^T and O = diag(gamma c_q) Z + P U, and
+//                           the output stores;
+//   copier waves (w = 8..11) stream the inputs as in chunk_scan_tp.
+// Three barriers per block:
+//   B1  block c in its slot, S^T published  -> Y-waves: Y, R;  Z-waves: Z
+//   BR  R in LDS                            -> Y-waves: U, its parts;  Z-waves: block c - 1's outputs to HBM
+//   BU  U and its parts in LDS              -> Y-waves: S^T update, published;  Z-waves: O, to LDS
+// The Y- and Z-waves issue no global loads inside the block loop, so the
+// Z-waves' stores never hold up a load wait.
+
+constexpr int TPF_YW = 4, TPF_ZW = 4, TPF_LOAD = 4;
+constexpr int TPF_COMPUTE = TPF_YW + TPF_ZW;
+constexpr int TPF_THREADS = (TPF_COMPUTE + TPF_LOAD) * WAVE;
+
+template <int D, bool OUT_BF16>
+constexpr size_t tpf_scan_lds_bytes() {
+    return 3 * sizeof(TpSlot<D, 1>)           // ring
+           + 2 * (size_t)CHUNK * D * 2        // q ring
+           + 2 * (D / 32) * WAVE * 8 * 2      // S^T high / low
+           + 4 * 2 * WAVE * 8 * 2             // R, U, the high / low parts of diag(s c) U
+           + (size_t)CHUNK * 16 * (OUT_BF16 ? 2 : 4);  // outputs
+}
+
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(TPF_THREADS) void chunk_scan_tpf_kernel(
+    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
+    const char* __restrict__ recs, const SeqInfo* __restrict__ info, const float* __restrict__ state_in,
+    float* __restrict__ state_out, void* __restrict__ out, char* __restrict__ sink, int units, int T, int h_k,
+    int h_v, unsigned* __restrict__ status) {
+    using Slot = TpSlot<D, 1>;
+    constexpr int RS = 16, SLICES = D / RS, NKB = D / 32, TPW = D / 64, RING = 3;
+    constexpr int NK = CHUNK * D * 2 / 1024;   // 1 KiB loads of a raw q or k tile
+    constexpr int NV = CHUNK * RS * 2 / 1024;  // 1 KiB loads of the v slice
+    constexpr int KL = NK / TPF_LOAD;          // k (or q) loads per copier wave
+    constexpr int TPL = 2 * TpRec::NF / TPF_LOAD;  // T and P loads per copier wave
+    static_assert(NK % TPF_LOAD == 0 && (2 * TpRec::NF) % TPF_LOAD == 0 && NV + 1 <= TPF_LOAD,
+                  "copy split over the copier waves");
+    static_assert(TPW >= 1 && TPW <= 2, "one or two key tiles per compute wave");
+    constexpr int OB = OUT_BF16 ? 2 : 4;  // bytes per output element
+    __shared__ __align__(16) Slot ring[RING];
+    __shared__ __align__(16) uint16_t sQ[2][CHUNK * D];           // raw q ring (swizzled rows)
+    __shared__ __align__(16) uint16_t sShi[NKB * WAVE * 8];       // S^T high / low B fragments (kb)
+    __shared__ __align__(16) uint16_t sSlo[NKB * WAVE * 8];
+    __shared__ __align__(16) _Float16 sR[2 * WAVE * 8];           // R, fp16 B fragments (32-token block)
+    __shared__ __align__(16) _Float16 sU[2 * WAVE * 8];           // U
+    __shared__ __align__(16) uint16_t sUh[2 * WAVE * 8];          // diag(s c) U, bf16 high / low parts
+    __shared__ __align__(16) uint16_t sUl[2 * WAVE * 8];
+    __shared__ __align__(16) char sO[CHUNK * RS * OB];            // one block's 64 x 16 outputs, row-major
+    // XCD placement as in chunk_scan_tp: a unit's SLICES workgroups share an XCD.
+    const int xcd = blockIdx.x % 8, m = blockIdx.x / 8;
+    const int slice = m % SLICES;
+    const int unit = (m / SLICES) * 8 + xcd;  // sequence * h_v + v-head
+    if (unit >= units) return;
+    const int n = unit / h_v, h = unit - n * h_v;
+    const int tid = threadIdx.x, lane = tid % WAVE;
+    const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);
+    const int j16 = lane & 15, q4 = lane >> 4;
+    const int r0 = slice * RS;
+    int begin, len, slot0;
+    if (info) {
+        const SeqInfo si = info[n];
+        begin = si.begin; len = si.len; slot0 = si.slot_base;
+    } else {
+        begin = 0; len = T; slot0 = 0;
+    }
+    const int nchunks = (len + CHUNK - 1) / CHUNK;
+    const int hk = h / (h_v / h_k);
+
+    if (w >= TPF_COMPUTE) {
+        // ------------------------------ copier waves ------------------------------
+        // Block c + 2 is copied during block c: k after B1 (the slot of block c - 1 is
+        // free), q after BR (block c's q has been read), T, P, the v slice and the
+        // factors after BU.  Every load moves 16 bytes a lane; copiers 0 .. NV - 1 also
+        // take a 1 KiB piece of the v slice, copier NV the factors.  Before B1 of block
+        // c + 1 a copier waits until only block c + 2's loads are in flight.
+        typedef __attribute__((address_space(3))) void* lds_ptr;
+        const int lw = w - TPF_COMPUTE;
+        constexpr int RPI = 1024 / (2 * D), UPR = D / 8;  // rows per 1 KiB load, 16-byte units per row
+        auto tile_load = [&](const void* base, int tok0, uint16_t* dst, int i) __attribute__((always_inline)) {
+            const int r = i * RPI + lane / UPR, p = lane % UPR;
+            const int u = p ^ (r & (UPR - 1));  // the global unit this lane's LDS slot holds (raw_unit)
+            const size_t tt = (size_t)min(tok0 + r, T - 1);
+            const uint16_t* src = reinterpret_cast<const uint16_t*>(base) + (tt * h_k + hk) * D + 8 * u;
+            __builtin_amdgcn_global_load_lds(src, (lds_ptr)(dst + i * 512), 16, 0, 0);
+        };
+        auto copy_k = [&](int c) __attribute__((always_inline)) {
+#pragma unroll
+            for (int mm = 0; mm < KL; ++mm) tile_load(k, begin + c * CHUNK, ring[c % RING].k, TPF_LOAD * mm + lw);
+        };
+        auto copy_q = [&](int c) __attribute__((always_inline)) {
+#pragma unroll
+            for (int mm = 0; mm < KL; ++mm) tile_load(q, begin + c * CHUNK, sQ[c & 1], TPF_LOAD * mm + lw);
+        };
+        auto copy_rest = [&](int c) __attribute__((always_inline)) {
+            Slot* sl = &ring[c % RING];
+            const char* rec = recs + ((size_t)(slot0 + c) * h_v + h) * TpRec::BYTES;
+#pragma unroll
+            for (int mm = 0; mm < TPL; ++mm) {
+                const int j = TPF_LOAD * mm + lw;
+                __builtin_amdgcn_global_load_lds(rec + (size_t)j * 1024 + lane * 16,
+                                                 (lds_ptr)(reinterpret_cast<char*>(sl->tp) + j * 1024), 16, 0, 0);
+            }
+            if (lw < NV) {  // tokens 32 lw .. + 31 of the v slice, half a token's 16 values a lane
+                const int r = lw * (CHUNK / NV) + lane / 2;
+                const size_t tt = (size_t)min(begin + c * CHUNK + r, T - 1);
+                const uint16_t* src = reinterpret_cast<const uint16_t*>(v) + (tt * h_v + h) * D + r0 + 8 * (lane & 1);
+                __builtin_amdgcn_global_load_lds(src, (lds_ptr)(sl->vs + lw * 512), 16, 0, 0);
+            } else if (lw == NV) {
+                __builtin_amdgcn_global_load_lds(rec + TpRec::F + lane * 16, (lds_ptr)(sl->fac), 16, 0, 0);
+            }
+        };
+        // loads per block of this copier: k, q, T and P, and one v or factor load for copiers 0 .. NV
+        constexpr int LB = 2 * KL + TPL;
+        auto wait_all_but_block = [&]() __attribute__((always_inline)) {  // all but one block's loads landed
+            if (lw <= NV) wait_vmcnt<LB + 1>();
+            else wait_vmcnt<LB>();
+        };
+        if (nchunks > 0) { copy_k(0); copy_q(0); copy_rest(0); }
+        if (nchunks > 1) {
+            copy_k(1); copy_q(1); copy_rest(1);
+            wait_all_but_block();
+        } else {
+            wait_vmcnt<0>();
+        }
+        for (int c = 0; c < nchunks; ++c) {
+            lds_barrier();  // B1
+            if (c + 2 < nchunks) copy_k(c + 2);
+            lds_barrier();  // BR
+            if (c + 2 < nchunks) copy_q(c + 2);
+            lds_barrier();  // BU
+            if (c + 2 < nchunks) copy_rest(c + 2);
+            if (c + 1 < nchunks) {
+                if (c + 2 < nchunks) wait_all_but_block();
+                else wait_vmcnt<0>();
+            }
+        }
+        lds_barrier();  // B1 after the last block
+        return;
+    }
+
+    bool bad = false;  // a non-finite output or final state in this lane
+    typedef __attribute__((address_space(3))) s4v_t* lds_s4;
+    if (w >= TPF_YW) {
+        // ------------------------------ Z-waves ------------------------------
+        const int tb = w - TPF_YW, kbt = tb >> 1;
+        constexpr int LPR = RS * OB / 16;  // 16-byte pieces per output row
+        constexpr int PIECES = CHUNK * LPR;
+        auto store_out = [&](int c) __attribute__((always_inline)) {  // block c's outputs, sO to HBM
+            const int nt = min(CHUNK, len - c * CHUNK), t = tb * WAVE + lane;
+            for (int p = t; p < PIECES; p += TPF_ZW * WAVE) {
+                const int row = p / LPR, col16 = p % LPR;
+                const uint4 val = *reinterpret_cast<const uint4*>(sO + row * RS * OB + col16 * 16);
+                char* dst = row < nt ? reinterpret_cast<char*>(out) +
+                                           (((size_t)(begin + c * CHUNK + row) * h_v + h) * D + r0) * OB + col16 * 16
+                                     : sink + (t % WAVE) * 16;
+                *reinterpret_cast<uint4*>(dst) = val;
+            }
+        };
+        for (int c = 0; c < nchunks; ++c) {
+            const Slot& B = ring[c % RING];
+            lds_barrier();  // B1: block c in its slot, S^T published, block c - 1's outputs in sO
+            // ---- Z = Q^raw S^T for token block tb (high and low parts in two accumulators) ----
+            f4_t z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                const bf8_t qa = raw_rowfrag<D>(sQ[c & 1], tb, kb, lane);
+                mma_bf16(z0, qa, bfrag(sShi, kb, lane));
+                mma_bf16(z1, qa, bfrag(sSlo, kb, lane));
+            }
+            // Z is complete in this phase: keeps the compiler from sinking its products
+            // into phase BU, where they would contend with the Y-wave's update on this SIMD.
+            asm volatile("" : "+v"(z0), "+v"(z1));
+            const f4_t gcq = *reinterpret_cast<const f4_t*>(&B.fac[TpRec::GCQ + 16 * tb + 4 * q4]);
+            Frag<_Float16> pf[2];  // (for tb < 2 the second fragment repeats the first and goes unused)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) pf[kb] = frag_stored<_Float16>(B.tp[1], tri_frag(tb, kb), lane);
+            lds_barrier();  // BR
+            if (c >= 1) store_out(c - 1);
+            lds_barrier();  // BU: U in LDS; sO is no longer read
+            {   // ---- O = diag(gamma c_q) Z + P U ----
+                f4_t o = gcq * (z0 + z1);
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+                    if (kb <= kbt) mma(o, pf[kb], frag_stored<_Float16>(sU, kb, lane));
+                bad |= any_nonfinite(o);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int e = (16 * tb + 4 * q4 + r) * RS + j16;
+                    if constexpr (OUT_BF16) reinterpret_cast<__bf16*>(sO)[e] = (__bf16)o[r];
+                    else reinterpret_cast<float*>(sO)[e] = o[r];
+                }
+            }
+        }
+        lds_barrier();  // B1 after the last block: its outputs are in sO
+        if (nchunks > 0) store_out(nchunks - 1);
+        report_status(status, bad, GDN_PREFILL_STATUS_NONFINITE);
+        return;
+    }
+
+    // ------------------------------ Y-waves ------------------------------
+    const int tb = w, kbt = tb >> 1, part = tb & 1;  // token block, its 32-token block and half
+    f4_t St[TPW];  // S^T tiles 16 (TPW w + i) .. + 15 of the keys x this slice's 16 rows
+    const size_t sbase = (size_t)unit * D * D;
+    const int srow = r0 + j16;
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+        const int col = 16 * (TPW * w + i) + 4 * q4;
+        if (state_in) {
+            const float4 x = *reinterpret_cast<const float4*>(state_in + sbase + (size_t)srow * D + col);
+            St[i] = f4_t{x.x, x.y, x.z, x.w};
+        } else {
+            St[i] = f4_t{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    auto publish = [&]() __attribute__((always_inline)) {  // this wave's tiles as high / low B fragment parts
+        if constexpr (TPW == 2) {
+            bf8_t hi, lo;
+            split_from_acc(St[0], St[1], hi, lo);
+            bfrag_store(sShi, w, lane, hi);
+            bfrag_store(sSlo, w, lane, lo);
+        } else {
+            store_split(sShi, sSlo, w >> 1, w & 1, lane, St[0]);
+        }
+    };
+    publish();
+    for (int c = 0; c < nchunks; ++c) {
+        const Slot& B = ring[c % RING];
+        lds_barrier();  // B1: block c in its slot, S^T published
+        // ---- Y = K^raw S^T and R = V - diag(gamma c) Y for token block tb ----
+        const s4v_t vv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(  // v[token 16tb + 4q + e][row j]
+            (lds_s4)(B.vs + (16 * tb + 4 * q4 + (j16 >> 2)) * RS + 4 * (j16 & 3)));
+        const f4_t gck = *reinterpret_cast<const f4_t*>(&B.fac[TpRec::GCK + 16 * tb + 4 * q4]);
+        f4_t y0 = {0.f, 0.f, 0.f, 0.f}, y1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            const bf8_t ka = raw_rowfrag<D>(B.k, tb, kb, lane);
+            mma_bf16(y0, ka, bfrag(sShi, kb, lane));
+            mma_bf16(y1, ka, bfrag(sSlo, kb, lane));
+        }
+        {
+            const f4_t yy = y0 + y1;
+            f4_t r;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) r[e] = __uint_as_float((uint32_t)(uint16_t)vv[e] << 16) - gck[e] * yy[e];
+            store_part<_Float16>(sR, kbt, part, lane, r);
+        }
+        const f4_t sc = *reinterpret_cast<const f4_t*>(&B.fac[TpRec::SCK + 16 * tb + 4 * q4]);
+        Frag<_Float16> tf[2];  // (for tb < 2 the second fragment repeats the first and goes unused)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) tf[kb] = frag_stored<_Float16>(B.tp[0], tri_frag(tb, kb), lane);
+        lds_barrier();  // BR: R in LDS; S^T is no longer read
+        // ---- U = T R and the parts of diag(s c) U ----
+        {
+            f4_t u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                if (kb <= kbt) mma(u, tf[kb], frag_stored<_Float16>(sR, kb, lane));
+            store_part<_Float16>(sU, kbt, part, lane, u);
+            store_split(sUh, sUl, kbt, part, lane, u * sc);
+        }
+        bf8_t kt[TPW][2];  // K^raw^T column fragments of this wave's key tiles
+#pragma unroll
+        for (int i = 0; i < TPW; ++i)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) kt[i][kk] = raw_colfrag<D>(B.k, TPW * w + i, kk, lane);
+        lds_barrier();  // BU: U and its parts in LDS
+        // ---- S^T <- gamma_n S^T + K^raw^T diag(s c) U on this wave's tiles ----
+        {
+            const float gn = B.fac[TpRec::GN];
+            bf8_t uh[2], ul[2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                uh[kk] = bfrag(sUh, kk, lane);
+                ul[kk] = bfrag(sUl, kk, lane);
+            }
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) {
+                St[i] *= gn;
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    mma_bf16(St[i], kt[i][kk], uh[kk]);
+                    mma_bf16(St[i], kt[i][kk], ul[kk]);
+                }
+            }
+            publish();
+        }
+    }
+    lds_barrier();  // B1 after the last block
+    if (state_out) {
+#pragma unroll
+        for (int i = 0; i < TPW; ++i)
+            *reinterpret_cast<float4*>(state_out + sbase + (size_t)srow * D + 16 * (TPW * w + i) + 4 * q4) =
+                make_float4(St[i][0], St[i][1], St[i][2], St[i][3]);
+    }
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) bad |= any_nonfinite(St[i]);
+    report_status(status, bad, GDN_PREFILL_STATUS_NONFINITE);
+}
+
+// ============================================================================================
 // host launchers
 // ============================================================================================
 int compute_units();
@@ -1046,15 +1356,33 @@ static hipError_t launch_scan_tp_t(const void* q, const void* k, const void* v, 
     return hipGetLastError();
 }
 
+template <int D, bool OB>
+static hipError_t launch_scan_tpf_t(const void* q, const void* k, const void* v, const void* recs, const void* info,
+                                    const float* s_in, float* s_out, void* out, void* sink, int units, int T, int h_k,
+                                    int h_v, unsigned* status, hipStream_t stream) {
+    static_assert(tpf_scan_lds_bytes<D, OB>() <= 160 * 1024, "chunk_scan_tpf LDS budget");
+    const int groups = (units + 7) / 8;  // see the XCD placement in chunk_scan_tp_kernel
+    hipLaunchKernelGGL((chunk_scan_tpf_kernel<D, OB>), dim3(groups * 8 * (D / 16)), dim3(TPF_THREADS), 0, stream, q, k,
+                       v, reinterpret_cast<const char*>(recs), reinterpret_cast<const SeqInfo*>(info), s_in, s_out, out,
+                       reinterpret_cast<char*>(sink), units, T, h_k, h_v, status);
+    return hipGetLastError();
+}
+
 hipError_t launch_scan_bf16(int d, bool out_bf16, int rows, int mode, const void* q, const void* k, const void* v,
                             const void* recs, const void* info, const float* s_in, float* s_out, void* out, void* sink,
                             int units, int T, int h_k, int h_v, unsigned* status, hipStream_t stream) {
+    // The scan proper on 16-row slices runs on chunk_scan_tpf; chunk_scan_tp takes
+    // 32-row slices and the segment maps (MODE 1).
+#define GDN_TPF(D, OB)                                                                                         \
+    if (d == D && out_bf16 == OB && rows == 16 && mode == 0)                                                  \
+        return launch_scan_tpf_t<D, OB>(q, k, v, recs, info, s_in, s_out, out, sink, units, T, h_k, h_v, status, stream);
+    GDN_TPF(128, true) GDN_TPF(128, false) GDN_TPF(64, true) GDN_TPF(64, false)
+#undef GDN_TPF
 #define GDN_TPS(D, OB, NB, MODE)                                                                              \
     if (d == D && out_bf16 == OB && rows == 16 * NB && mode == MODE)                                          \
         return launch_scan_tp_t<D, OB, NB, MODE>(q, k, v, recs, info, s_in, s_out, out, sink, units, T, h_k, h_v, \
                                                  status, stream);
-    GDN_TPS(128, true, 1, 0) GDN_TPS(128, false, 1, 0) GDN_TPS(128, true, 2, 0) GDN_TPS(128, false, 2, 0)
-    GDN_TPS(64, true, 1, 0) GDN_TPS(64, false, 1, 0) GDN_TPS(64, true, 2, 0) GDN_TPS(64, false, 2, 0)
+    GDN_TPS(128, true, 2, 0) GDN_TPS(128, false, 2, 0) GDN_TPS(64, true, 2, 0) GDN_TPS(64, false, 2, 0)
     GDN_TPS(128, false, 1, 1) GDN_TPS(128, false, 2, 1) GDN_TPS(64, false, 1, 1) GDN_TPS(64, false, 2, 1)
 #undef GDN_TPS
     return hipErrorInvalidValue;

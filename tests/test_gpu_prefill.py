@@ -381,22 +381,26 @@ ROW_CASES = [  # (d, io dtype, out dtype, lengths)
 @pytest.mark.parametrize("case", range(len(ROW_CASES)))
 def test_row_slices_16_and_32_agree(case):
     """The scan splits each state over workgroups of 16 or 32 rows (gdn_prefill_ex's
-    scan_rows).  Each row's arithmetic is the same in both, so the results agree bitwise
-    with each other and with the default, and meet the oracle bound."""
+    scan_rows).  fp32 inputs run the same per-row arithmetic either way, so those results
+    agree bitwise.  bf16 inputs take two kernels that sum the key contractions in different
+    orders (over the whole key range in one wave with 16 rows, over key halves with 32), so
+    those agree to rounding.  Both meet the oracle bound, and the default is 16 rows."""
     d, io, od, lens = ROW_CASES[case]
     x = inputs.prefill_inputs(seed=40 + case, lengths=lens, h_k=2, h_v=4, d=d, io_dtype=io, state_std=0.2)
     res = {rows: run_gpu(x, od, options=gdn.GdnPrefillOptions(rows, 0, 0)) for rows in (16, 32)}
     default = run_gpu(x, od)
-    assert torch.equal(res[16][0], res[32][0]) and torch.equal(res[16][1], res[32][1])
     assert torch.equal(res[16][0], default[0]) and torch.equal(res[16][1], default[1])
+    if io == inputs.F32:
+        assert torch.equal(res[16][0], res[32][0]) and torch.equal(res[16][1], res[32][1])
     ro, rs = run_oracle(x)
     tol = 1e-5 if io == inputs.F32 else 2e-3
-    out, st = res[16]
-    if od == inputs.F32:
-        assert normwise(host(out), ro) <= tol
-    else:
-        check_bf16_out(host(out), ro, tol)
-    assert normwise(host(st), rs) <= tol
+    for rows in (16, 32):
+        out, st = res[rows]
+        if od == inputs.F32:
+            assert normwise(host(out), ro) <= tol
+        else:
+            check_bf16_out(host(out), ro, tol)
+        assert normwise(host(st), rs) <= tol
 
 
 # ---- invariants through the GPU path -------------------------------------------------------
