@@ -117,12 +117,14 @@ __device__ __forceinline__ float bf16_hi_bits(uint32_t w) { return __uint_as_flo
 //       on the raw inputs), whose diagonals give the norm factors, then G and
 //       the per-token terms of v-head `wave`; waves 2..5: the raw off-diagonal
 //       K K^T and the Q K^T tiles; waves 6, 7: the raw diagonal K K^T tiles.
-//   P2b decay masks: A_ij^T tiles (i > j blocks), P fragments, and the diagonal
-//       blocks N_bb of A, which waves 6, 7 invert by forward substitution on
-//       the vector unit (one lane per column of a block).
+//   P2b decay masks: A_ij^T tiles (i > j blocks), P fragment halves (to the
+//       records), and the diagonal blocks N_bb of A, which waves 6, 7 invert by
+//       forward substitution on the vector unit (one lane per column of a block);
+//       waves 0, 1 write the zero halves of the records' fragments.
 //   P4  the six blocks of X = (I + A)^{-1} below the diagonal (fp32 matrix
-//       cores), written as T = X diag(beta) fragments.
-//   P5  T and P fragments to the records.
+//       cores), written with the four diagonal ones as T = X diag(beta)
+//       fragment halves to the records.
+// The records' fragments go out half by half, straight from the registers.
 // Decay ratios are exp2(r_i - c_j) with r_i = G_i log2(e) + log2(beta_i c_i)
 // and c_j = G_j log2(e) - log2(c_j); only entries with i >= j are kept, so
 // the exponent carries exp(G_i - G_j) <= 1.
@@ -140,10 +142,8 @@ struct PairLds {
     uint16_t qraw[CHUNK * D];           // raw bf16 queries
     float gb[NH][2][CHUNK];             // g and beta of the v-heads
     float a[NH][6][WAVE * 4];           // A_ij^T (block i > j) in accumulator layout
-    float nb[NH][4][16 * XS];           // diagonal blocks N_bb of A, row-major
+    float nb[NH][4][16 * XS];           // diagonal blocks N_bb of A, transposed (row j = column j of N)
     float xd[NH][4][16 * XS];           // X_bb = (I + N_bb)^{-1}, column-major [col][row]
-    _Float16 t[NH][CHUNK * CHUNK];      // T = X diag(beta), fragment-major
-    _Float16 p[NH][CHUNK * CHUNK];      // P, fragment-major
     float cn[2][2 * CHUNK];             // norm factors c_k, c_q (one copy per wave 0, 1)
     float ra[NH][CHUNK], rq[NH][CHUNK], cb[NH][CHUNK], bt[NH][CHUNK];
     PairMeta meta[2];
@@ -245,7 +245,6 @@ __global__ __launch_bounds__(PAIR_THREADS, 1) void chunk_prep_pair_kernel(
                 issue(item + 1, m.live ? m.tok0 : 0);
             }
             lds_barrier();  // B3
-            lds_barrier();  // B4
             wait_vmcnt<0>();
         }
         return;
@@ -348,20 +347,15 @@ __global__ __launch_bounds__(PAIR_THREADS, 1) void chunk_prep_pair_kernel(
         // ---- P2b ------------------------------------------------------------------------------
         if (live) {
             if (wave < 2) {
-                // zero halves: P above the diagonal (6 tiles), T above the diagonal (6 halves)
+                // the halves above the diagonal in the stored fragments, blocks (0, 1) and (2, 3)
+                // of T (wave 0) and of P (wave 1)
+                const f4_t z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
                 for (int hh = 0; hh < NH; ++hh) {
-                    for (int x = wave; x < 12; x += 2) {
-                        const f4_t z = {0.f, 0.f, 0.f, 0.f};
-                        if (x < 6) {
-                            const int nb = (x >= 3) ? 3 : (x >= 1) ? 2 : 1, mb = x - (nb - 1) * nb / 2;
-                            store_part<OP>(L.p[hh], mb * 2 + nb / 2, nb % 2, lane, z);
-                        } else {
-                            const int h = x - 6;
-                            const int f = h == 0 ? 0 : h <= 2 ? 1 : h <= 4 ? 3 : 5;
-                            const int part = (h == 0 || h == 2 || h == 4 || h == 5) ? 1 : 0;
-                            store_part<OP>(L.t[hh], f, part, lane, z);
-                        }
-                    }
+                    OP* rec = reinterpret_cast<OP*>(recs + ((size_t)slot * h_v + h0 + hh) * TpRec::BYTES +
+                                                    (wave ? TpRec::P : TpRec::T));
+                    store_part<OP>(rec, tri_frag(0, 0), 1, lane, z);
+                    store_part<OP>(rec, tri_frag(2, 1), 1, lane, z);
                 }
             } else if (wave < 6) {
 #pragma unroll
@@ -390,50 +384,50 @@ __global__ __launch_bounds__(PAIR_THREADS, 1) void chunk_prep_pair_kernel(
 #pragma unroll
                             for (int e = 0; e < 4; ++e)
                                 x[e] = (mb > nb || c0 + e <= i) ? acc[m][e] * __builtin_amdgcn_exp2f(r - c[e]) : 0.f;
-                            store_part<OP>(L.p[hh], mb * 2 + nb / 2, nb % 2, lane, x);
+                            store_part<OP>(reinterpret_cast<OP*>(recs + ((size_t)slot * h_v + h0 + hh) * TpRec::BYTES +
+                                                                 TpRec::P),
+                                           tri_frag(mb, nb / 2), nb % 2, lane, x);
                         }
                     }
                 }
             } else if (wave - 6 < NH) {
                 const int hh = wave - 6;
-                // N_bb[j'][4q + r] (strictly lower) from the symmetric raw block, row-major
+                // N_bb (strictly lower) transposed, from the symmetric raw block: lane (j', q)
+                // holds N[4q + r][j'] = raw[4q + r][j'] exp2(r_{4q+r} - c_j'), stored at row j'
+                // of N^T
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
-                    const float r = L.ra[hh][16 * b + li];
-                    const f4_t c = *reinterpret_cast<const f4_t*>(&L.cb[hh][16 * b + 4 * lq]);
+                    const f4_t r = *reinterpret_cast<const f4_t*>(&L.ra[hh][16 * b + 4 * lq]);
+                    const float c = L.cb[hh][16 * b + li];
                     f4_t x;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) x[e] = (4 * lq + e < li) ? acc[b][e] * __builtin_amdgcn_exp2f(r - c[e]) : 0.f;
+                    for (int e = 0; e < 4; ++e) x[e] = (4 * lq + e > li) ? acc[b][e] * __builtin_amdgcn_exp2f(r[e] - c) : 0.f;
                     *reinterpret_cast<f4_t*>(&L.nb[hh][b][li * XS + 4 * lq]) = x;
                 }
-                // Forward substitution (I + N) X = I: lane (b, j) computes column j of X_bb,
-                // X[i][j] = [i == j] - sum_{m < i} N[i][m] X[m][j].  N's rows are read as
-                // broadcasts (the 16 lanes of a block read the same address).
+                // Forward substitution (I + N) X = I, column by column of N: lane (b, j)
+                // computes column j of X_bb.  Once x_m = X[m][j] is final, it is taken out of
+                // every later row, s_i -= N[i][m] x_m, so each step's updates are independent.
+                // The rows of N^T are read as broadcasts (the 16 lanes of a block read the
+                // same address).
                 const int b = lq, j = li;
-                const float* Nb = L.nb[hh][b];
+                const float* Nt = L.nb[hh][b];
                 float x[16];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    float s = (i == j) ? 1.f : 0.f;
+                for (int i = 0; i < 16; ++i) x[i] = (i == j) ? 1.f : 0.f;
 #pragma unroll
-                    for (int m4 = 0; m4 < i; m4 += 4) {
-                        const f4_t nr = *reinterpret_cast<const f4_t*>(&Nb[i * XS + m4]);
+                for (int m = 0; m < 15; ++m) {
+#pragma unroll
+                    for (int i4 = ((m + 1) / 4) * 4; i4 < 16; i4 += 4) {
+                        const f4_t nc = *reinterpret_cast<const f4_t*>(&Nt[m * XS + i4]);
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            if (m4 + e < i) s = fmaf(-nr[e], x[m4 + e], s);
+                            if (i4 + e > m) x[i4 + e] = fmaf(-nc[e], x[m], x[i4 + e]);
                     }
-                    x[i] = s;
                 }
                 float* xd = L.xd[hh][b];
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
                     *reinterpret_cast<f4_t*>(&xd[j * XS + 4 * c]) = f4_t{x[4 * c], x[4 * c + 1], x[4 * c + 2], x[4 * c + 3]};
-                // T's diagonal block: T[16b + i][16b + j] = X[i][j] beta_{16b + j}, element
-                // (j % 4) + 4 (b % 2) of lane ((j / 4), i) of fragment (b, b / 2)
-                const float bj = L.bt[hh][16 * b + j];
-                OP* tf = L.t[hh] + ((size_t)(2 * b + (b >> 1)) * WAVE + (j >> 2) * 16) * 8 + (j & 3) + 4 * (b & 1);
-#pragma unroll
-                for (int i = 0; i < 16; ++i) tf[i * 8] = (OP)(x[i] * bj);
             }
         }
         lds_barrier();  // B3: P complete
@@ -457,9 +451,11 @@ __global__ __launch_bounds__(PAIR_THREADS, 1) void chunk_prep_pair_kernel(
                                 x[(4 * lq + 3) * XS + li]};
                 };
                 auto put = [&](int a, int b, const f4_t& negxt) {  // negxt = -X_ab^T
-                    store_part<OP>(L.t[hh], 2 * a + (b >> 1), b & 1, lane,
+                    store_part<OP>(reinterpret_cast<OP*>(recs + ((size_t)slot * h_v + h0 + hh) * TpRec::BYTES + TpRec::T),
+                                   tri_frag(a, b >> 1), b & 1, lane,
                                    -negxt * *reinterpret_cast<const f4_t*>(&L.bt[hh][16 * b + 4 * lq]));
                 };
+                put(role, role, -xt(role));  // T's diagonal block role
                 if (role == 0) {  // X_10 = -X_11 A_10 X_00; X_20 = -X_22 (A_20 X_00 + A_21 X_10)
                     const f4_t x00 = xa(0), x11t = xt(1);
                     const f4_t r = mm16(at(1, 0), x00, z);
@@ -487,19 +483,6 @@ __global__ __launch_bounds__(PAIR_THREADS, 1) void chunk_prep_pair_kernel(
                     const f4_t x32t = -mm16(mm16(at(3, 2), xa(2), z), x33t, z);
                     put(3, 0, mm16(y10, x33t, mm16(y00, x32t, z)));
                 }
-            }
-        }
-        lds_barrier();  // B4: T complete
-
-        // ---- P5: the non-zero T and P fragments to the records (1 KiB each) ----------------------
-        if (live) {
-            for (int u = wave; u < NH * 2 * TpRec::NF; u += PAIR_COMPUTE_WAVES) {
-                const int hh = u / (2 * TpRec::NF), which = (u / TpRec::NF) & 1, f6 = u % TpRec::NF;
-                const int mb = f6 < 2 ? f6 : 2 + (f6 - 2) / 2, kb = f6 < 2 ? 0 : (f6 - 2) % 2;
-                const OP* src = (which ? L.p[hh] : L.t[hh]) + ((size_t)(mb * 2 + kb) * WAVE + lane) * 8;
-                char* dst = recs + ((size_t)slot * h_v + h0 + hh) * TpRec::BYTES + (which ? TpRec::P : TpRec::T) +
-                            (size_t)f6 * 1024 + lane * 16;
-                *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
             }
         }
     }
