@@ -221,6 +221,15 @@ __device__ __forceinline__ F2 permlane16_swap(float a, float b) {
     return {__uint_as_float(r[0]), __uint_as_float(r[1])};
 }
 
+// Lanes i and i ^ 32 trade values (v_permlane32_swap: the upper half of the
+// first operand trades places with the lower half of the second).  With a in
+// every lane and b in every lane, a lower-half lane gets (its own a, its
+// partner's a) and an upper-half lane gets (its partner's b, its own b).
+__device__ __forceinline__ F2 permlane32_swap(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+
 // Partner lane of a butterfly step inside a row of 16 lanes (DPP): lane
 // i ^ H for H = 8, 2, 1, and the mirror lane (i & ~7) | (7 - (i & 7)) for
 // H = 4, which differs from i in bit 2 (all a butterfly step needs).

@@ -144,7 +144,6 @@ struct PairLds {
     float a[NH][6][WAVE * 4];           // A_ij^T (block i > j) in accumulator layout
     float nb[NH][4][16 * XS];           // diagonal blocks N_bb of A, transposed (row j = column j of N)
     float xd[NH][4][16 * XS];           // X_bb = (I + N_bb)^{-1}, column-major [col][row]
-    float cn[2][2 * CHUNK];             // norm factors c_k, c_q (one copy per wave 0, 1)
     float ra[NH][CHUNK], rq[NH][CHUNK], cb[NH][CHUNK], bt[NH][CHUNK];
     PairMeta meta[2];
     int zero;                           // holds 0 (see the compute waves)
@@ -169,7 +168,8 @@ __global__ __launch_bounds__(PAIR_THREADS, 1) void chunk_prep_pair_kernel(
     constexpr int NKB = D / 32;  // contraction blocks over d
     extern __shared__ __align__(16) char smem_raw[];
     LT& L = *reinterpret_cast<LT*>(smem_raw);
-    const int tid = threadIdx.x, wave = tid / WAVE;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);  // wave-uniform: role branches stay scalar
     const int ratio = h_v / h_k, pairs = ratio / NH;
     const int per_slot = h_k * pairs;
     const int items = slots * per_slot;
@@ -213,7 +213,11 @@ __global__ __launch_bounds__(PAIR_THREADS, 1) void chunk_prep_pair_kernel(
         auto issue = [&](int item, int tok0) {
             int hk, pr;
             const int h0 = heads_of(item, hk, pr);
-            for (int i = lw; i < 2 * NL; i += PAIR_LOADER_WAVES) {
+            static_assert((2 * NL) % PAIR_LOADER_WAVES == 0 && (2 * NH) % PAIR_LOADER_WAVES == 0,
+                          "loads in multiples of the loader count");
+#pragma unroll
+            for (int mm = 0; mm < 2 * NL / PAIR_LOADER_WAVES; ++mm) {
+                const int i = mm * PAIR_LOADER_WAVES + lw;
                 const int m4 = i % NL;
                 const int r = m4 * RPI + lane / UPR, p = lane % UPR;
                 const int u = p ^ (r & (UPR - 1));  // the global unit this lane's LDS slot holds
@@ -222,7 +226,9 @@ __global__ __launch_bounds__(PAIR_THREADS, 1) void chunk_prep_pair_kernel(
                 uint16_t* dst = i < NL ? L.kraw : L.qraw;
                 __builtin_amdgcn_global_load_lds(src + 8 * u, (lds_ptr)(dst + m4 * 512), 16, 0, 0);
             }
-            for (int i = lw; i < 2 * NH; i += PAIR_LOADER_WAVES) {  // g and beta, one fp32 per lane
+#pragma unroll
+            for (int mm = 0; mm < 2 * NH / PAIR_LOADER_WAVES; ++mm) {  // g and beta, one fp32 per lane
+                const int i = mm * PAIR_LOADER_WAVES + lw;
                 const int j = i >> 1;
                 const size_t tg = (size_t)min(tok0 + lane, T - 1) * h_v + h0 + j;
                 const float* src = (i & 1) ? beta + tg : g + tg;
@@ -268,53 +274,71 @@ __global__ __launch_bounds__(PAIR_THREADS, 1) void chunk_prep_pair_kernel(
         const int cnt = meta.nt;
 
         // ---- P2a ------------------------------------------------------------------------------
+        // The 16 off-diagonal tiles u (u < 6 the K K^T block of slot u, u >= 6 the Q K^T tile
+        // u - 6) go to waves 0..5: two each to waves 0..3, four each to waves 4, 5.
+        const int u0 = wave < 4 ? 2 * wave : 8 + 4 * (wave - 4), nt = wave < 4 ? 2 : wave < 6 ? 4 : 0;
         f4_t acc[4];
         if (live) {
-            if (wave < 2) {
-                // diagonal blocks of K K^T (b = 0..3) and Q Q^T (b = 4..7); the diagonal of
-                // each is the squared norm of its 16 tokens
-                float* cn = L.cn[wave];
+            if (wave < 4) {
+                // block wave b: the squared norms of tokens 16b .. 16b + 15 (lane (i, q) sums the
+                // squares of its 32 elements of row 16b + i, then the four rows of 16 lanes add
+                // up), then those tokens' per-token terms for each v-head
+                const int b = wave;
+                float sk = 0.f, sq = 0.f;
 #pragma unroll
-                for (int b = 0; b < 8; ++b) {
-                    const uint16_t* M = b < 4 ? L.kraw : L.qraw;
-                    f4_t dg = {0.f, 0.f, 0.f, 0.f};
+                for (int kb = 0; kb < NKB; ++kb) {
+                    typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
+                    const bf8_t xk = raw_row8<D>(L.kraw, b, kb, lane), xq = raw_row8<D>(L.qraw, b, kb, lane);
 #pragma unroll
-                    for (int kb = 0; kb < NKB; ++kb) {
-                        const bf8_t x = raw_row8<D>(M, b & 3, kb, lane);
-                        mma_bf16(dg, x, x);
-                    }
-                    // lane (j, q) holds rows 4q + r of column j: the diagonal is r = j - 4q
-                    if ((li >> 2) == lq) {
-                        const float ss = dg[li & 3];
-                        const float mul = b < 4 ? 1.0f : scale;
-                        cn[16 * b + li] = l2norm ? mul * rsqrtf(ss + 1e-6f) : mul;
+                    for (int e = 0; e < 8; e += 2) {  // bf16 pair dot products, fp32 sums
+                        const bf2_t pk = {xk[e], xk[e + 1]}, pq = {xq[e], xq[e + 1]};
+                        sk = __builtin_amdgcn_fdot2_f32_bf16(pk, pk, sk, false);
+                        sq = __builtin_amdgcn_fdot2_f32_bf16(pq, pq, sq, false);
                     }
                 }
-                if (wave < NH) {
-                    const int hh = wave;
-                    const bool tl = lane < cnt;
-                    const float ckv = tl ? cn[lane] : 0.f, cqv = tl ? cn[CHUNK + lane] : 0.f;
-                    const float gl = wave_inclusive_sum(tl ? L.gb[hh][0][lane] : 0.f) * LOG2E_F;
-                    const float bv = tl ? L.gb[hh][1][lane] : 0.f;
-                    L.ra[hh][lane] = gl + __builtin_amdgcn_logf(bv * ckv);
-                    L.rq[hh][lane] = gl + __builtin_amdgcn_logf(cqv);
-                    L.cb[hh][lane] = gl - __builtin_amdgcn_logf(ckv);
-                    L.bt[hh][lane] = bv;
-                    const float gam = __builtin_amdgcn_exp2f(gl);
+                F2 t = permlane16_swap(sk, sk);
+                sk = t.x + t.y;
+                t = permlane32_swap(sk, sk);
+                sk = t.x + t.y;
+                t = permlane16_swap(sq, sq);
+                sq = t.x + t.y;
+                t = permlane32_swap(sq, sq);
+                sq = t.x + t.y;
+                const bool tl = lane < cnt;
+                const float ckv = tl ? (l2norm ? rsqrtf(sk + 1e-6f) : 1.0f) : 0.f;
+                const float cqv = tl ? (l2norm ? scale * rsqrtf(sq + 1e-6f) : scale) : 0.f;
+                float gv[NH], bv[NH];
+#pragma unroll
+                for (int hh = 0; hh < NH; ++hh) {
+                    gv[hh] = tl ? L.gb[hh][0][lane] : 0.f;
+                    bv[hh] = tl ? L.gb[hh][1][lane] : 0.f;
+                }
+#pragma unroll
+                for (int hh = 0; hh < NH; ++hh) {
+                    const float gl = wave_inclusive_sum(gv[hh]) * LOG2E_F;
                     const float gln = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gl), max(cnt - 1, 0)));
                     float* f = reinterpret_cast<float*>(recs + ((size_t)slot * h_v + h0 + hh) * TpRec::BYTES + TpRec::F);
-                    f[TpRec::GCK + lane] = gam * ckv;
-                    f[TpRec::GCQ + lane] = gam * cqv;
-                    f[TpRec::SCK + lane] = tl ? __builtin_amdgcn_exp2f(gln - gl) * ckv : 0.f;
-                    if (lane == 0) f[TpRec::GN] = __builtin_amdgcn_exp2f(gln);
+                    if (lq == b) {  // tokens 16b .. 16b + 15
+                        L.ra[hh][lane] = gl + __builtin_amdgcn_logf(bv[hh] * ckv);
+                        L.rq[hh][lane] = gl + __builtin_amdgcn_logf(cqv);
+                        L.cb[hh][lane] = gl - __builtin_amdgcn_logf(ckv);
+                        L.bt[hh][lane] = bv[hh];
+                        const float gam = __builtin_amdgcn_exp2f(gl);
+                        f[TpRec::GCK + lane] = gam * ckv;
+                        f[TpRec::GCQ + lane] = gam * cqv;
+                        f[TpRec::SCK + lane] = tl ? __builtin_amdgcn_exp2f(gln - gl) * ckv : 0.f;
+                    }
+                    if (b == 0 && lane == 0) f[TpRec::GN] = __builtin_amdgcn_exp2f(gln);
                 }
-            } else if (wave < 6) {
-                // tiles u = wave - 2 + 4m: u < 6 the off-diagonal K K^T block of slot u, computed
-                // as K_j K_i^T so that lane (j', q) holds A_ij^T[4q + r][j']; u >= 6 the tile
-                // K_nb Q_mb^T, which is this lane's half of P's fragment (mb, nb / 2).
+            }
+            if (wave < 6) {
+                // tile u < 6: the off-diagonal K K^T block of slot u, computed as K_j K_i^T so that
+                // lane (j', q) holds A_ij^T[4q + r][j']; u >= 6: the tile K_nb Q_mb^T, which is this
+                // lane's half of P's fragment (mb, nb / 2)
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    const int u = wave - 2 + 4 * m;
+                    if (m >= nt) break;
+                    const int u = u0 + m;
                     acc[m] = f4_t{0.f, 0.f, 0.f, 0.f};
                     if (u < 6) {
                         const int bi = u >= 3 ? 3 : (u >= 1 ? 2 : 1), bj = u - bi * (bi - 1) / 2;
@@ -342,7 +366,7 @@ __global__ __launch_bounds__(PAIR_THREADS, 1) void chunk_prep_pair_kernel(
                 }
             }
         }
-        lds_barrier();  // B2: the raw inputs are no longer read
+        lds_barrier();  // B2: the raw inputs are no longer read; the per-token terms in LDS
 
         // ---- P2b ------------------------------------------------------------------------------
         if (live) {
@@ -357,10 +381,12 @@ __global__ __launch_bounds__(PAIR_THREADS, 1) void chunk_prep_pair_kernel(
                     store_part<OP>(rec, tri_frag(0, 0), 1, lane, z);
                     store_part<OP>(rec, tri_frag(2, 1), 1, lane, z);
                 }
-            } else if (wave < 6) {
+            }
+            if (wave < 6) {
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    const int u = wave - 2 + 4 * m;
+                    if (m >= nt) break;
+                    const int u = u0 + m;
                     if (u < 6) {
                         const int bi = u >= 3 ? 3 : (u >= 1 ? 2 : 1), bj = u - bi * (bi - 1) / 2;
 #pragma unroll
