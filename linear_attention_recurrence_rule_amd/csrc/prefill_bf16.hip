@@ -1328,8 +1328,10 @@ static hipError_t launch_prep_pair_t(const void* q, const void* k, const float* 
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    // one workgroup per compute unit, each a contiguous run of items
-    const int items = slots * h_k * (h_v / h_k / NH), resident = compute_units();
+    // two workgroups per compute unit (one's memory waits overlap the other's work), each a
+    // contiguous run of items
+    static_assert(2 * lds <= 160 * 1024, "two chunk_prep_pair workgroups per compute unit");
+    const int items = slots * h_k * (h_v / h_k / NH), resident = 2 * compute_units();
     const int per = (items + resident - 1) / resident;
     const int grid = (items + per - 1) / per;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(PAIR_THREADS), lds, stream, q, k, g, beta,
