@@ -1018,6 +1018,9 @@ __global__ __launch_bounds__(TPS_MAX_THREADS) void chunk_scan_tp_kernel(
 //   B1  block c in its slot, S^T published  -> Y-waves: Y, R;  Z-waves: Z
 //   BR  R in LDS                            -> Y-waves: U, its parts;  Z-waves: block c - 1's outputs to HBM
 //   BU  U and its parts in LDS              -> Y-waves: S^T update, published;  Z-waves: O, to LDS
+// Reads that phase B1 does not need (T, P and their factors) wait until after BR:
+// phase B1 is the one bound by the workgroup's LDS read bandwidth, and for the same
+// reason a Y-wave takes its own share of S^T from registers.
 // The Y- and Z-waves issue no global loads inside the block loop, so the
 // Z-waves' stores never hold up a load wait.
 
@@ -1183,11 +1186,11 @@ __global__ __launch_bounds__(TPF_THREADS) void chunk_scan_tpf_kernel(
             // Z is complete in this phase: keeps the compiler from sinking its products
             // into phase BU, where they would contend with the Y-wave's update on this SIMD.
             asm volatile("" : "+v"(z0), "+v"(z1));
+            lds_barrier();  // BR
             const f4_t gcq = *reinterpret_cast<const f4_t*>(&B.fac[TpRec::GCQ + 16 * tb + 4 * q4]);
             Frag<_Float16> pf[2];  // (for tb < 2 the second fragment repeats the first and goes unused)
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) pf[kb] = frag_stored<_Float16>(B.tp[1], tri_frag(tb, kb), lane);
-            lds_barrier();  // BR
             if (c >= 1) store_out(c - 1);
             lds_barrier();  // BU: U in LDS; sO is no longer read
             {   // ---- O = diag(gamma c_q) Z + P U ----
@@ -1225,10 +1228,13 @@ __global__ __launch_bounds__(TPF_THREADS) void chunk_scan_tpf_kernel(
             St[i] = f4_t{0.f, 0.f, 0.f, 0.f};
         }
     }
+    bf8_t own_hi, own_lo;  // this wave's share of the high / low S^T fragments (TPW == 2)
     auto publish = [&]() __attribute__((always_inline)) {  // this wave's tiles as high / low B fragment parts
         if constexpr (TPW == 2) {
             bf8_t hi, lo;
             split_from_acc(St[0], St[1], hi, lo);
+            own_hi = hi;
+            own_lo = lo;
             bfrag_store(sShi, w, lane, hi);
             bfrag_store(sSlo, w, lane, lo);
         } else {
@@ -1245,10 +1251,16 @@ __global__ __launch_bounds__(TPF_THREADS) void chunk_scan_tpf_kernel(
         const f4_t gck = *reinterpret_cast<const f4_t*>(&B.fac[TpRec::GCK + 16 * tb + 4 * q4]);
         f4_t y0 = {0.f, 0.f, 0.f, 0.f}, y1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
+        for (int kr = 0; kr < NKB; ++kr) {  // from this wave's own key block on (its fragments in registers)
+            const int kb = TPW == 2 ? (kr + w) % NKB : kr;
             const bf8_t ka = raw_rowfrag<D>(B.k, tb, kb, lane);
-            mma_bf16(y0, ka, bfrag(sShi, kb, lane));
-            mma_bf16(y1, ka, bfrag(sSlo, kb, lane));
+            if (TPW == 2 && kr == 0) {
+                mma_bf16(y0, ka, own_hi);
+                mma_bf16(y1, ka, own_lo);
+            } else {
+                mma_bf16(y0, ka, bfrag(sShi, kb, lane));
+                mma_bf16(y1, ka, bfrag(sSlo, kb, lane));
+            }
         }
         {
             const f4_t yy = y0 + y1;
@@ -1257,11 +1269,11 @@ __global__ __launch_bounds__(TPF_THREADS) void chunk_scan_tpf_kernel(
             for (int e = 0; e < 4; ++e) r[e] = __uint_as_float((uint32_t)(uint16_t)vv[e] << 16) - gck[e] * yy[e];
             store_part<_Float16>(sR, kbt, part, lane, r);
         }
+        lds_barrier();  // BR: R in LDS; S^T is no longer read
         const f4_t sc = *reinterpret_cast<const f4_t*>(&B.fac[TpRec::SCK + 16 * tb + 4 * q4]);
         Frag<_Float16> tf[2];  // (for tb < 2 the second fragment repeats the first and goes unused)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) tf[kb] = frag_stored<_Float16>(B.tp[0], tri_frag(tb, kb), lane);
-        lds_barrier();  // BR: R in LDS; S^T is no longer read
         // ---- U = T R and the parts of diag(s c) U ----
         {
             f4_t u = {0.f, 0.f, 0.f, 0.f};
