@@ -1005,9 +1005,9 @@ __global__ __launch_bounds__(TPS_MAX_THREADS) void chunk_scan_tp_kernel(
 // ============================================================================================
 // The inputs and the arithmetic of chunk_scan_tp (MODE 0, one 16-row slice per
 // workgroup), with the roles arranged so that no partial product crosses waves.
-// Every wave that contracts with S^T reads the whole of its bf16 high / low
-// parts from LDS, and per-wave LDS reads are the scarce resource, so the work of
-// token block tb is split over two waves:
+// Every wave that contracts with S^T reads its bf16 high / low parts from LDS
+// (a Y-wave all but its own share), and per-wave LDS reads are the scarce
+// resource, so the work of token block tb is split over two waves:
 //   Y-wave tb (w = tb):     Y and R, U = T R and the parts of diag(s c) U, and
 //                           the update of the fp32 S^T tiles 16 TPW tb .. + 16 TPW - 1
 //                           of the keys (TPW = D / 64 tiles), which it holds;
