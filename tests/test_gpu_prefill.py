@@ -113,6 +113,23 @@ def test_extreme_qk_magnitudes(qk_scale):
     assert eo <= 2e-3 and es <= 2e-3
 
 
+@pytest.mark.parametrize("d,h_k,h_v", [(128, 2, 2), (64, 2, 2), (128, 1, 3), (64, 3, 3)])
+def test_odd_head_ratios_bf16(d, h_k, h_v):
+    """v-heads per k-head of 1 and 3: the bf16 prepare kernel then takes one v-head per
+    item instead of pairs (the pair kernel with NH = 1); outputs and final states
+    against the oracle, packed sequences with a ragged tail and an initial state."""
+    x = inputs.prefill_inputs(seed=50 + d + h_v, lengths=[130, 64, 7], h_k=h_k, h_v=h_v, d=d,
+                              io_dtype=inputs.BF16, state_std=0.2)
+    ro, rs = run_oracle(x)
+    for od in (inputs.F32, inputs.BF16):
+        out, st = run_gpu(x, od)
+        if od == inputs.F32:
+            assert normwise(host(out), ro) <= 2e-3
+        else:
+            check_bf16_out(host(out), ro, 2e-3)
+        assert normwise(host(st), rs) <= 2e-3
+
+
 @pytest.mark.parametrize("d,io", [(128, inputs.BF16), (64, inputs.F32)])
 def test_extreme_gates(d, io):
     """Gates at their ends, mixed within blocks: no decay (g = 0), near-total forgetting
