@@ -13,7 +13,8 @@ The same JSON line also reports:
     (64 sequences x 32 v-heads, d = 128, fp32 state), the same loop replayed
     from a HIP graph, the same steps through gdn_decode_step_ex with raw gate
     inputs and the output normalisation folded in, the same steps rotating over
-    four copies of the state (cache-cold), and 256 sequences (a 512 MiB state);
+    eight copies of the state (cache-cold; with the nontemporal state accesses of
+    GDN_STREAM_STATE and without), and 256 sequences (a 512 MiB state);
   * roofline of the dominant prefill kernel: algorithmic flops per launch over
     its average duration in a loop of back-to-back launches of that kernel's
     phase alone, against the 2.5 PFLOP/s dense fp16 matrix-core peak; the
@@ -134,8 +135,12 @@ def measured_traffic(kernel):
 def measure_ceilings(torch, np, dev):
     """What plain code reaches on this GPU, as second roofline denominators
     (linear_attention_recurrence_rule_amd/libgdn_calibrate.so): a matrix-core loop of
-    64 x 128 x 128 fp16 products with register operands, and one in-place read-modify-write
-    pass over 128 MiB of random fp32 data (the decode step's state traffic).  Median of 5."""
+    64 x 128 x 128 fp16 products with register operands, and in-place read-modify-write
+    passes over random fp32 data (the decode step's state traffic): over one 128 MiB array
+    again and again (partly held by the 256 MiB last-level cache), rotating over eight 128 MiB
+    arrays (each pass from HBM, as the cache-cold decode steps rotate their state), and over
+    one 1 GiB array.  Median of 5; each stream takes its best of 2, 8 and 16 workgroups per
+    compute unit."""
     path = os.path.join(ROOT, "linear_attention_recurrence_rule_amd", "libgdn_calibrate.so")
     if not os.path.exists(path):
         return None
@@ -170,24 +175,40 @@ def measure_ceilings(torch, np, dev):
     for _ in range(2):
         mfma()
     us_mfma = median_us(mfma, 3)
-    rates = {}
-    for mib in (128, 1024):  # 128 MiB: partly held by the 256 MiB last-level cache; 1 GiB: not
-        x = torch.randn(mib << 18, dtype=torch.float32, device=dev)
-
-        def rmw():
-            st = C.gdn_calib_rmw_f32(x.data_ptr(), x.numel(), wgs, sp)
-            if st:
-                raise RuntimeError("gdn_calib_rmw_f32: hip error %d" % st)
-        for _ in range(3):
-            rmw()
-        us_rmw = median_us(rmw, 10 if mib == 128 else 3)
-        rates[mib] = 2 * x.numel() * 4 / (us_rmw * 1e-6) / 1e9
-        del x
     del sink
+
+    def stream_rate(arrays, reps):
+        best = 0.0
+        for per_cu in (2, 8, 16):
+            turn = [0]
+
+            def rmw():
+                x = arrays[turn[0] % len(arrays)]
+                turn[0] += 1
+                st = C.gdn_calib_rmw_f32(x.data_ptr(), x.numel(), per_cu * cus, sp)
+                if st:
+                    raise RuntimeError("gdn_calib_rmw_f32: hip error %d" % st)
+            for _ in range(2 * len(arrays)):
+                rmw()
+            us_rmw = median_us(rmw, reps)
+            best = max(best, 2 * arrays[0].numel() * 4 / (us_rmw * 1e-6) / 1e9)
+        return best
+
+    rates = {}
+    arrays = [torch.randn(128 << 18, dtype=torch.float32, device=dev)]
+    rates["hot"] = stream_rate(arrays[:1], 16)
+    arrays += [torch.randn(128 << 18, dtype=torch.float32, device=dev) for _ in range(7)]
+    rates["cold"] = stream_rate(arrays, 16)
+    del arrays
+    big = torch.randn(1024 << 18, dtype=torch.float32, device=dev)
+    rates["1gib"] = stream_rate([big], 3)
+    del big
     return {"mfma_f16_tflops": round(C.gdn_calib_mfma_f16_flops(iters, wgs) / (us_mfma * 1e-6) / 1e12, 1),
-            "rmw_stream_gbs": round(rates[128], 1), "rmw_stream_gbs_1gib": round(rates[1024], 1),
-            "source": "libgdn_calibrate.so: fp16 matrix-core loop; fp32 read-modify-write streams over "
-                      "128 MiB (cache-assisted) and 1 GiB (from HBM)"}
+            "rmw_stream_gbs": round(rates["hot"], 1), "rmw_stream_gbs_cold": round(rates["cold"], 1),
+            "rmw_stream_gbs_1gib": round(rates["1gib"], 1),
+            "source": "libgdn_calibrate.so: fp16 matrix-core loop; fp32 read-modify-write streams "
+                      "(4 float4 in flight per lane) over one 128 MiB array (cache-assisted), eight "
+                      "128 MiB arrays in turn (from HBM) and one 1 GiB array"}
 
 
 def crossover(L, gdn, inputs, to_dev, torch, np, dev):
@@ -291,7 +312,8 @@ def two_level(L, gdn, inputs, to_dev, torch, np, dev):
 def decode_sweep(L, gdn, inputs, to_dev, torch, np, dev):
     """gdn_decode_step by batch size: N sequences x 32 v-heads (16 k-heads), d = 128, bf16 in
     and out, fp32 state, 64 consecutive steps per N (fresh inputs each step); plain, replayed
-    from a HIP graph, and with both per-token folds (gdn_decode_step_ex).  One JSON line per N."""
+    from a HIP graph, with both per-token folds (gdn_decode_step_ex), and with the nontemporal
+    state accesses (GDN_STREAM_STATE).  One JSON line per N."""
     h_k, h_v, d, steps = 16, 32, 128, 64
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
@@ -320,8 +342,15 @@ def decode_sweep(L, gdn, inputs, to_dev, torch, np, dev):
             if st:
                 raise gdn.GdnError(st, gdn.last_error())
 
+        def streamed(t):
+            st = L.gdn_decode_step_ex(dref, P[0] + t * qs, P[1] + t * ks, P[2] + t * vs_, P[3] + t * gs,
+                                      P[4] + t * gs, state.data_ptr(), out.data_ptr(), gdn.GDN_STREAM_STATE, None,
+                                      0.0, sp)
+            if st:
+                raise gdn.GdnError(st, gdn.last_error())
+
         res = {}
-        for name, fn in (("plain", plain), ("fused", fused)):
+        for name, fn in (("plain", plain), ("fused", fused), ("stream", streamed)):
             for t in range(5):
                 fn(t)
             torch.cuda.synchronize()
@@ -360,7 +389,8 @@ def decode_sweep(L, gdn, inputs, to_dev, torch, np, dev):
         print(json.dumps({"decode_sweep": {
             "num_seqs": N, "h_v": h_v, "h_k": h_k, "d": d, "us_per_step": round(res["plain"], 2),
             "us_per_step_hip_graph": round(res["graph"], 2),
-            "us_per_step_fused": round(res["fused"], 2), "tok_per_s": round(N * 1e6 / res["plain"]),
+            "us_per_step_fused": round(res["fused"], 2), "us_per_step_stream_state": round(res["stream"], 2),
+            "tok_per_s": round(N * 1e6 / res["plain"]),
             "state_mib": round(N * h_v * d * d * 4 / 2 ** 20, 1),
             "gb_per_s": round(nbytes / (res["plain"] * 1e-6) / 1e9, 1),
             "hbm_frac": round(nbytes / (res["plain"] * 1e-6) / (PEAK_HBM_GBS * 1e9), 4)}}), flush=True)
@@ -685,20 +715,35 @@ def main():
     fused_loop()
     us_dec_fused = loop_us(fused_loop, 1) / steps
     del dxg, dxb, nw
-    # cache-cold: the same steps rotating over four copies of the 128 MiB state (512 MiB in all,
-    # twice the 256 MiB last-level cache), so each step's state was evicted since it was last used
-    copies = [state] + [state.clone() for _ in range(3)]
+    # cache-cold: the same steps rotating over eight copies of the 128 MiB state (1 GiB in all,
+    # four times the 256 MiB last-level cache), so each step's state was evicted since it was
+    # last used; with the default cache policy and with GDN_STREAM_STATE (nontemporal state
+    # accesses), the call for a state that other layers' states push out of the cache
+    copies = [state] + [state.clone() for _ in range(7)]
     cptr = [c.data_ptr() for c in copies]
 
     def cold_loop():
         for t in range(steps):
-            decode_call(t, st_ptr=cptr[t % 4])
+            decode_call(t, st_ptr=cptr[t % 8])
+
+    def stream_call(t, st_ptr):
+        st = L.gdn_decode_step_ex(ddref, base[0] + t * qs, base[1] + t * ks, base[2] + t * vs_, base[3] + t * gs,
+                                  base[4] + t * bs, st_ptr, optr, gdn.GDN_STREAM_STATE, None, 0.0, sp)
+        if st:
+            raise gdn.GdnError(st, gdn.last_error())
+
+    def cold_stream_loop():
+        for t in range(steps):
+            stream_call(t, cptr[t % 8])
     cold_loop()
-    us_dec_cold = loop_us(cold_loop, 1) / steps
+    us_dec_cold_cached = loop_us(cold_loop, 1) / steps
+    cold_stream_loop()
+    us_dec_cold = loop_us(cold_stream_loop, 1) / steps
     del copies
     dbytes = algorithmic_decode(N, dh_v, dh_k, dd)
     dec_gbs = dbytes / (us_dec * 1e-6) / 1e9
     cold_gbs = dbytes / (us_dec_cold * 1e-6) / 1e9
+    cold_cached_gbs = dbytes / (us_dec_cold_cached * 1e-6) / 1e9
     # decode at N = 256 sequences (a 512 MiB state, beyond the cache by itself)
     N2 = 256
     y2 = inputs.decode_inputs(seed=8, num_seqs=N2, steps=16, h_k=dh_k, h_v=dh_v, d=dd, io_dtype=inputs.BF16)
@@ -711,13 +756,16 @@ def main():
     b2p = [t_.data_ptr() for t_ in (q2, k2_, v2, g2, b2)]
     s2 = [t_.stride(0) * t_.element_size() for t_ in (q2, k2_, v2, g2, b2)]
 
-    def loop256():
+    def loop256(flags):
         for t in range(16):
-            st = L.gdn_decode_step(d2ref, *[b2p[i] + t * s2[i] for i in range(5)], st2.data_ptr(), o2.data_ptr(), sp)
+            st = L.gdn_decode_step_ex(d2ref, *[b2p[i] + t * s2[i] for i in range(5)], st2.data_ptr(),
+                                      o2.data_ptr(), flags, None, 0.0, sp)
             if st:
                 raise gdn.GdnError(st, gdn.last_error())
-    loop256()
-    us_256 = loop_us(loop256, 4) / 16
+    loop256(0)
+    us_256_cached = loop_us(lambda: loop256(0), 4) / 16
+    loop256(gdn.GDN_STREAM_STATE)
+    us_256 = loop_us(lambda: loop256(gdn.GDN_STREAM_STATE), 4) / 16
     bytes256 = algorithmic_decode(N2, dh_v, dh_k, dd)
     gbs256 = bytes256 / (us_256 * 1e-6) / 1e9
     del q2, k2_, v2, g2, b2, st2, o2, y2
@@ -733,20 +781,26 @@ def main():
                                               "between steps"},
                    "cache_cold": {"us_per_step": round(us_dec_cold, 2), "gb_per_s": round(cold_gbs, 1),
                                   "hbm_frac": round(cold_gbs / PEAK_HBM_GBS, 4),
-                                  "how": "steps rotate over 4 copies of the state (512 MiB)"},
+                                  "how": "steps rotate over 8 copies of the state (1 GiB), called with "
+                                         "GDN_STREAM_STATE (nontemporal state accesses)",
+                                  "default_policy": {"us_per_step": round(us_dec_cold_cached, 2),
+                                                     "gb_per_s": round(cold_cached_gbs, 1),
+                                                     "hbm_frac": round(cold_cached_gbs / PEAK_HBM_GBS, 4)}},
                    "n256": {"num_seqs": N2, "state_mib": N2 * dh_v * dd * dd * 4 / 2 ** 20,
                             "us_per_step": round(us_256, 2), "tok_per_s": round(N2 * 1e6 / us_256),
-                            "gb_per_s": round(gbs256, 1), "hbm_frac": round(gbs256 / PEAK_HBM_GBS, 4)},
+                            "gb_per_s": round(gbs256, 1), "hbm_frac": round(gbs256 / PEAK_HBM_GBS, 4),
+                            "how": "16 steps in place, GDN_STREAM_STATE",
+                            "default_policy_us_per_step": round(us_256_cached, 2)},
                    "roofline": {"bound": "hbm", "kernel": "decode_step", "achieved": round(cold_gbs, 1),
                                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(cold_gbs / PEAK_HBM_GBS, 4),
-                                "basis": "cache-cold steps (state rotated over 512 MiB)",
+                                "basis": "cache-cold steps (state rotated over 1 GiB, GDN_STREAM_STATE)",
                                 "traffic": measured_traffic("decode_step")}}
     del dq, dk, dv, dg, db, state, dout
 
     ceilings = measure_ceilings(torch, np, dev)
     if ceilings:
         roofline["frac_of_measured_ceiling"] = round(ach / ceilings["mfma_f16_tflops"], 4)
-        decode_info["roofline"]["frac_of_measured_ceiling"] = round(cold_gbs / ceilings["rmw_stream_gbs_1gib"], 4)
+        decode_info["roofline"]["frac_of_measured_ceiling"] = round(cold_gbs / ceilings["rmw_stream_gbs_cold"], 4)
         decode_info["cache_assisted"]["frac_of_measured_ceiling"] = round(dec_gbs / ceilings["rmw_stream_gbs"], 4)
 
     if args.calibrate_copy:

@@ -239,7 +239,8 @@ gdn_status gdn_prefill_scan(const gdn_desc *desc,
  * normalisation and the exponential gate ("Reduce intermediate traffic and
  * state traffic": the recurrent update is fused with its normalisation).
  * Shapes are those above with tokens = num_seqs.  `state` is read and written
- * in place, once each.
+ * in place, once each.  GDN_ERR_UNSUPPORTED if num_seqs * h_v * 2 * d_k
+ * reaches 2^32 (one launch; the state would exceed 512 GiB).
  */
 gdn_status gdn_decode_step(const gdn_desc *desc,
                            const void *q, const void *k, const void *v,
@@ -288,6 +289,18 @@ gdn_status gdn_decode_step_slots(const gdn_desc *desc,
  *                              is fp32 [d_v] on the device, shared by all
  *                              heads, or NULL for ones; norm_eps is finite
  *                              and > 0.  The state update is not affected.
+ *   GDN_STREAM_STATE           a cache policy, not an operation: the state is
+ *                              read and written with nontemporal accesses,
+ *                              which do not keep it in the GPU's caches.
+ *                              Results are bit-identical either way.  Set it
+ *                              when other work runs through the caches before
+ *                              this state is stepped again, as a model's
+ *                              layers each step their own state (section
+ *                              "Decode: minimise bytes moved per token"):
+ *                              there the step runs ~8% faster.  Leave it off
+ *                              when the same states are stepped back to back
+ *                              and fit in the 256 MiB last-level cache, which
+ *                              then serves part of each step.
  *
  * Without flags this is gdn_decode_step (bit-identical results); norm_weight
  * and norm_eps are read only with GDN_FUSE_OUTPUT_NORM.  The state is still
@@ -296,7 +309,7 @@ gdn_status gdn_decode_step_slots(const gdn_desc *desc,
  * norm_eps that is not finite and positive, or a norm_weight that overlaps
  * another buffer.
  */
-typedef enum { GDN_FUSE_GATE_ACTIVATIONS = 1, GDN_FUSE_OUTPUT_NORM = 2 } gdn_fuse_flag;
+typedef enum { GDN_FUSE_GATE_ACTIVATIONS = 1, GDN_FUSE_OUTPUT_NORM = 2, GDN_STREAM_STATE = 4 } gdn_fuse_flag;
 
 gdn_status gdn_decode_step_ex(const gdn_desc *desc,
                               const void *q, const void *k, const void *v,
@@ -391,8 +404,9 @@ gdn_status gdn_prefill_direct(const gdn_desc *desc,
  * folded in, token by token: raw gate inputs (GDN_FUSE_GATE_ACTIVATIONS) and
  * each (token, v-head) output normalised over d_v (GDN_FUSE_OUTPUT_NORM, with
  * norm_weight and norm_eps as there), for multi-token decode and verify steps.
- * Without flags this is gdn_prefill_direct.  Errors: those of
- * gdn_prefill_direct and the flag, eps and weight checks of gdn_decode_step_ex.
+ * Without flags this is gdn_prefill_direct.  GDN_STREAM_STATE is a decode-step
+ * flag only and is rejected here.  Errors: those of gdn_prefill_direct and the
+ * flag, eps and weight checks of gdn_decode_step_ex.
  */
 gdn_status gdn_prefill_direct_ex(const gdn_desc *desc,
                                  const void *q, const void *k, const void *v,

@@ -17,7 +17,7 @@ namespace gdn {
 hipError_t launch_decode(int d, bool in_bf16, bool out_bf16, const void* q, const void* k,
                          const void* v, const float* g, const float* beta, float* state, const int32_t* slots,
                          int num_slots, void* out, int units, int h_k, int h_v, int l2norm, float scale,
-                         int fuse, const float* norm_w, float norm_eps, int grid, hipStream_t stream);
+                         int fuse, const float* norm_w, float norm_eps, hipStream_t stream);
 size_t prefill_record_bytes(int d, bool in_bf16);
 size_t prefill_key_record_bytes(int d, bool in_bf16);
 hipError_t launch_segment_info(void* info, int P, int sb, int T, hipStream_t stream);
@@ -160,22 +160,6 @@ gdn_status check_overlaps(const Span* s, int count, const void* allow_a, const v
                 return fail(GDN_ERR_INVALID_ARGUMENT, "buffers %s and %s overlap", s[i].name, s[j].name);
         }
     return GDN_OK;
-}
-
-int cu_count() {
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
-    }
-    return cus;
-}
-
-// Decode workgroups: two per compute unit, each walking several (sequence,
-// v-head) units so that one unit's loads overlap the previous unit's work.
-int decode_grid(int units) {
-    const int grid = cu_count() * 2;
-    return grid < units ? grid : units;
 }
 
 // Workspace of gdn_prefill_noalloc: a file-scope device array (each GPU the
@@ -446,6 +430,10 @@ gdn_status decode_call(const gdn_desc* desc, const void* q, const void* k, const
                        const float* beta, float* state, int32_t num_slots, const int32_t* slots, void* out,
                        void* stream, int fuse = 0, const float* norm_w = nullptr, float norm_eps = 0.f) {
     const int N = desc->num_seqs, hk = desc->h_k, hv = desc->h_v, d = desc->d_k;
+    // one workgroup of 2 d threads per (sequence, v-head): the grid stays below 2^32 work-items
+    if ((int64_t)N * hv * 2 * d >= ((int64_t)1 << 32))
+        return fail(GDN_ERR_UNSUPPORTED, "num_seqs * h_v = %lld units exceed one decode launch",
+                    (long long)N * hv);
     const size_t io = dtype_size(desc->io_dtype), os = dtype_size(desc->out_dtype);
     const Span spans[] = {
         {(const char*)q, (size_t)N * hk * d * io, "q"},
@@ -464,7 +452,7 @@ gdn_status decode_call(const gdn_desc* desc, const void* q, const void* k, const
     if (st != GDN_OK) return st;
     hipError_t e = gdn::launch_decode(d, desc->io_dtype == GDN_BF16, desc->out_dtype == GDN_BF16, q, k, v, g,
                                       beta, state, slots, num_slots, out, N * hv, hk, hv, desc->qk_l2norm,
-                                      desc->scale, fuse, norm_w, norm_eps, decode_grid(N * hv),
+                                      desc->scale, fuse, norm_w, norm_eps,
                                       reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
     return GDN_OK;
@@ -672,7 +660,7 @@ gdn_status gdn_decode_step_ex(const gdn_desc* desc, const void* q, const void* k
     if (st != GDN_OK) return st;
     if (!q || !k || !v || !g || !beta || !state || !out)
         return fail(GDN_ERR_INVALID_ARGUMENT, "q, k, v, g, beta, state and out must be non-NULL");
-    if (fuse & ~(GDN_FUSE_GATE_ACTIVATIONS | GDN_FUSE_OUTPUT_NORM))
+    if (fuse & ~(GDN_FUSE_GATE_ACTIVATIONS | GDN_FUSE_OUTPUT_NORM | GDN_STREAM_STATE))
         return fail(GDN_ERR_INVALID_ARGUMENT, "unknown fuse flags 0x%x", (unsigned)fuse);
     const bool norm = (fuse & GDN_FUSE_OUTPUT_NORM) != 0;
     if (norm && !(std::isfinite(norm_eps) && norm_eps > 0.f))

@@ -20,23 +20,55 @@
 // and beta = 1 / (1 + exp(-x_beta)) from raw inputs, and the normalisation of
 // each head's output, o / sqrt(mean(o^2) + eps) * w over d_v.  The latter needs
 // the head's d outputs, which are spread over the workgroup's waves: each wave
-// sums its 32 rows, and one LDS exchange behind a barrier (per unit, on every
-// path) combines them.
+// sums its 32 rows, and one LDS exchange combines them.  The barrier the
+// exchange needs comes after the state update and the state stores, so that
+// waiting for the other waves overlaps them.
 //
 // Layout: a workgroup has d/32 waves, and each wave owns 32 state rows.  A
 // lane holds 4 consecutive entries (16 bytes) of one row, so d/4 lanes cover a
 // row, and each wave-wide load reads 1 KiB of contiguous state.  The row sums
 // are a reduce-scatter across the d/4 lanes of a row (DPP inside 16-lane rows,
 // v_permlane16_swap between them).  After it, lane c of a row group holds
-// either S k^ or S q^ of one row.  A grid of a few workgroups
-// per compute unit walks the (sequence, v-head) units.  The next unit's state
-// and token inputs are loaded while the current unit computes and stores.
+// either S k^ or S q^ of one row.  Each workgroup takes one (sequence,
+// v-head) unit: it loads the unit's state and token inputs, computes, stores
+// and exits, and the dispatcher starts the next unit's workgroup in its place,
+// two at a time per compute unit at d = 128 (see kDecodeResidencyLds).
+// Measured cache-cold on MI355X, this moves the state ~9% faster than a few
+// workgroups per compute unit that walk several units each with the next
+// unit's loads in flight, and it needs fewer registers.
+//
+// Cache policy (fuse bit 2, GDN_STREAM_STATE): the state is loaded and stored
+// either as ordinary accesses, which leave it in the last-level cache for a
+// step that comes back to it while it is still there, or as nontemporal ones
+// (the `nt` bit), which do not.  A model steps every layer's state in turn,
+// far more than the cache holds, and there the nontemporal form moves the
+// state ~8% faster from HBM.
 #include "gdn_device.h"
 
 namespace gdn {
 
-// Everything one unit needs, loaded together so the next unit's loads can be
-// in flight while the current unit computes.
+// One lane's 16 bytes of state; NT: the nontemporal cache policy.
+template <bool NT>
+__device__ __forceinline__ float4 state_ld(const float* p) {
+    if constexpr (NT) {
+        const f4_t t = __builtin_nontemporal_load(reinterpret_cast<const f4_t*>(p));
+        return make_float4(t[0], t[1], t[2], t[3]);
+    } else {
+        return *reinterpret_cast<const float4*>(p);
+    }
+}
+
+template <bool NT>
+__device__ __forceinline__ void state_st(float* p, float4 x) {
+    if constexpr (NT) {
+        const f4_t t = {x.x, x.y, x.z, x.w};
+        __builtin_nontemporal_store(t, reinterpret_cast<f4_t*>(p));
+    } else {
+        *reinterpret_cast<float4*>(p) = x;
+    }
+}
+
+// Everything one unit needs, loaded together before any of it is used.
 template <int D>
 struct DecodeIn {
     float4 s[D / 8];  // this lane's state slices (D/8 = LPR/2 rows)
@@ -48,7 +80,7 @@ struct DecodeIn {
 
 // Sequence n's state is slot slots[n] of the state array (slot n when slots is
 // NULL); a slot outside [0, num_slots) skips the unit.
-template <int D, bool IN_BF16>
+template <int D, bool IN_BF16, bool NT>
 __device__ __forceinline__ void decode_load(DecodeIn<D>& in, const float* __restrict__ state,
                                             const int32_t* __restrict__ slots, int num_slots, const void* q,
                                             const void* k, const void* v, const float* g, const float* beta,
@@ -64,8 +96,7 @@ __device__ __forceinline__ void decode_load(DecodeIn<D>& in, const float* __rest
 #pragma unroll
     for (int m = 0; m < NL; ++m) {
         const int row = wave * 32 + m * RPI + sub;
-        in.s[m] = in.slot >= 0 ? *reinterpret_cast<const float4*>(S + (size_t)row * D + 4 * c)
-                               : make_float4(0.f, 0.f, 0.f, 0.f);
+        in.s[m] = in.slot >= 0 ? state_ld<NT>(S + (size_t)row * D + 4 * c) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     load4<IN_BF16>(k, ((size_t)n * h_k + hk) * D + 4 * c, in.kx);
     load4<IN_BF16>(q, ((size_t)n * h_k + hk) * D + 4 * c, in.qx);
@@ -94,14 +125,16 @@ __device__ __forceinline__ void token_gates(float g, float b, bool raw_gates, fl
 // token's output o = S q^ at `orow` (the output row of this unit and token).
 // `ub` is this wave's 32-float LDS area, through which u is broadcast to the
 // lanes of its row group.  Cross-lane sums run on DPP and v_permlane16_swap.
-// With NORM the output is normalised over the head's d rows first: wrow is
-// the weight of this lane's row and nb the unit's D/32-float LDS exchange
-// area; every wave of the workgroup must call it.
+// With NORM the output is normalised over the head's d rows, which needs
+// every wave's part of the sum of squares: this wave's part goes to nb[wave]
+// (nb: the unit's D/32-float LDS exchange area), the update runs, and the
+// output is returned unwritten (lanes c >= d/8) for norm_output, which every
+// wave of the workgroup must then call.  The wait for the other waves thus
+// comes after the update (and whatever the caller puts in between).
 template <int D, bool OUT_BF16, bool NORM = false>
-__device__ __forceinline__ void decode_token(float4 (&sr)[D / 8], const float (&kin)[4], const float (&qin)[4],
-                                             float vin, float alpha, float bin, void* out, size_t orow, int l2norm,
-                                             float scale, float* ub, int wave, int lane, float wrow = 1.f,
-                                             float eps = 0.f, float* nb = nullptr) {
+__device__ __forceinline__ float decode_token(float4 (&sr)[D / 8], const float (&kin)[4], const float (&qin)[4],
+                                              float vin, float alpha, float bin, void* out, size_t orow, int l2norm,
+                                              float scale, float* ub, int wave, int lane, float* nb = nullptr) {
     constexpr int LPR = D / 4, RPI = WAVE / LPR, NL = LPR / 2;
     const int c = lane % LPR, sub = lane / LPR;
     // Every multiply-add below is an explicit fmaf: the rounding then does not
@@ -145,12 +178,6 @@ __device__ __forceinline__ void decode_token(float4 (&sr)[D / 8], const float (&
         const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(o2), 0)) +
                          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(o2), 32));
         if (lane == 0) nb[wave] = ws;
-        lds_barrier();
-        float tot = 0.f;
-#pragma unroll
-        for (int w = 0; w < D / 32; ++w) tot += nb[w];
-        const float r = 1.0f / sqrtf(tot * (1.0f / D) + eps);
-        if (c >= NL) store1<OUT_BF16>(out, orow * D + row, ov * r * wrow);
     } else {
         if (c >= NL) store1<OUT_BF16>(out, orow * D + row, ov);
     }
@@ -173,79 +200,76 @@ __device__ __forceinline__ void decode_token(float4 (&sr)[D / 8], const float (&
         sm.w = fmaf(um[m], kx[3], alpha * sm.w);
         sr[m] = sm;
     }
+    return ov;
+}
+
+// Writes the output that decode_token<..., NORM = true> returned for row group
+// `wave`: waits for every wave's sum of squares in nb, then stores
+// o / sqrt(mean(o^2) + eps) * wrow (wrow: the weight of this lane's row).
+template <int D, bool OUT_BF16>
+__device__ __forceinline__ void norm_output(float ov, void* out, size_t orow, int wave, int lane, float wrow,
+                                            float eps, const float* nb) {
+    constexpr int LPR = D / 4, RPI = WAVE / LPR, NL = LPR / 2;
+    const int c = lane % LPR, sub = lane / LPR;
+    lds_barrier();
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < D / 32; ++w) tot += nb[w];
+    const float r = 1.0f / sqrtf(tot * (1.0f / D) + eps);
+    if (c >= NL) store1<OUT_BF16>(out, orow * D + wave * 32 + (c - NL) * RPI + sub, ov * r * wrow);
 }
 
 // This lane's state slices of one (sequence, v-head) unit, in or out.
-template <int D>
+template <int D, bool NT = false>
 __device__ __forceinline__ void state_store(const float4 (&sr)[D / 8], float* __restrict__ S, int wave, int lane) {
     constexpr int LPR = D / 4, RPI = WAVE / LPR, NL = LPR / 2;
     const int c = lane % LPR, sub = lane / LPR;
 #pragma unroll
-    for (int m = 0; m < NL; ++m)
-        *reinterpret_cast<float4*>(S + (size_t)(wave * 32 + m * RPI + sub) * D + 4 * c) = sr[m];
+    for (int m = 0; m < NL; ++m) state_st<NT>(S + (size_t)(wave * 32 + m * RPI + sub) * D + 4 * c, sr[m]);
 }
 
 // raw_gates: in.g and in.b are the raw gate inputs (see the header).
-template <int D, bool OUT_BF16, bool NORM>
+template <int D, bool OUT_BF16, bool NORM, bool NT>
 __device__ __forceinline__ void decode_compute(DecodeIn<D>& in, float* __restrict__ state, void* out, int unit,
                                                int h_v, int l2norm, float scale, float* ub, int wave, int lane,
                                                bool raw_gates, float eps, float* nb) {
-    if (in.slot < 0) {  // skipped: zero outputs, state untouched
+    if (in.slot < 0) {  // skipped (every wave of the unit's workgroup): zero outputs, state untouched
         constexpr int LPR = D / 4, RPI = WAVE / LPR, NL = LPR / 2;
         const int c = lane % LPR, sub = lane / LPR;
         if (c >= NL) store1<OUT_BF16>(out, (size_t)unit * D + wave * 32 + (c - NL) * RPI + sub, 0.f);
-        if constexpr (NORM) lds_barrier();  // one barrier per unit on every path
         return;
     }
     const int h = unit % h_v;
     float alpha, bta;
     token_gates(in.g, in.b, raw_gates, alpha, bta);
-    decode_token<D, OUT_BF16, NORM>(in.s, in.kx, in.qx, in.v, alpha, bta, out, (size_t)unit, l2norm, scale, ub,
-                                    wave, lane, in.w, eps, nb);
-    state_store<D>(in.s, state + ((size_t)in.slot * h_v + h) * D * D, wave, lane);
+    const float ov = decode_token<D, OUT_BF16, NORM>(in.s, in.kx, in.qx, in.v, alpha, bta, out, (size_t)unit,
+                                                     l2norm, scale, ub, wave, lane, nb);
+    state_store<D, NT>(in.s, state + ((size_t)in.slot * h_v + h) * D * D, wave, lane);
+    if constexpr (NORM) norm_output<D, OUT_BF16>(ov, out, (size_t)unit, wave, lane, in.w, eps, nb);
 }
 
-// Each workgroup walks units blockIdx.x, blockIdx.x + gridDim.x, ... with the
-// next unit's state and token inputs loaded while the current unit computes.
-// Every iteration issues the same loads (past the end it re-reads the last
-// unit, unused), so each wait covers exactly one unit's data.  Units alternate
-// between two LDS exchange areas for the output norm: a wave writes the area
-// of unit i + 2 only after the barrier of unit i + 1, which every wave reaches
-// after its reads of unit i.
-template <int D, bool IN_BF16, bool OUT_BF16, bool NORM>
-__device__ __forceinline__ void decode_units(const void* __restrict__ q, const void* __restrict__ k,
-                                             const void* __restrict__ v, const float* __restrict__ g,
-                                             const float* __restrict__ beta, float* __restrict__ state,
-                                             const int32_t* __restrict__ slots, int num_slots, void* __restrict__ out,
-                                             int units, int h_k, int h_v, int l2norm, float scale, bool raw_gates,
-                                             const float* __restrict__ norm_w, float eps, float* ub, float* nsum,
-                                             int wave, int u, int stride) {
+template <int D, bool IN_BF16, bool OUT_BF16, bool NORM, bool NT>
+__device__ __forceinline__ void decode_unit(const void* __restrict__ q, const void* __restrict__ k,
+                                            const void* __restrict__ v, const float* __restrict__ g,
+                                            const float* __restrict__ beta, float* __restrict__ state,
+                                            const int32_t* __restrict__ slots, int num_slots, void* __restrict__ out,
+                                            int h_k, int h_v, int l2norm, float scale, bool raw_gates,
+                                            const float* __restrict__ norm_w, float eps, float* ub, float* nsum,
+                                            int wave, int u) {
     const int lane = threadIdx.x % WAVE;
-    const int last = units - 1;
-    if (u > last) return;
-    DecodeIn<D> A, B;
-    decode_load<D, IN_BF16>(A, state, slots, num_slots, q, k, v, g, beta, norm_w, u, h_k, h_v, wave, lane);
-    for (;;) {
-        decode_load<D, IN_BF16>(B, state, slots, num_slots, q, k, v, g, beta, norm_w, min(u + stride, last), h_k,
-                                h_v, wave, lane);
-        decode_compute<D, OUT_BF16, NORM>(A, state, out, u, h_v, l2norm, scale, ub, wave, lane, raw_gates, eps, nsum);
-        u += stride;
-        if (u > last) break;
-        decode_load<D, IN_BF16>(A, state, slots, num_slots, q, k, v, g, beta, norm_w, min(u + stride, last), h_k,
-                                h_v, wave, lane);
-        decode_compute<D, OUT_BF16, NORM>(B, state, out, u, h_v, l2norm, scale, ub, wave, lane, raw_gates, eps,
-                                          nsum + D / 32);
-        u += stride;
-        if (u > last) break;
-    }
+    DecodeIn<D> in;
+    decode_load<D, IN_BF16, NT>(in, state, slots, num_slots, q, k, v, g, beta, norm_w, u, h_k, h_v, wave, lane);
+    decode_compute<D, OUT_BF16, NORM, NT>(in, state, out, u, h_v, l2norm, scale, ub, wave, lane, raw_gates, eps,
+                                          nsum);
 }
 
-// fuse: bit 0 raw gate inputs, bit 1 output norm (weights norm_w, NULL for ones).
-// A workgroup of D/32 waves owns whole units (wave w: rows 32w..32w+31).  With
+// fuse: bit 0 raw gate inputs, bit 1 output norm (weights norm_w, NULL for ones),
+// bit 2 the nontemporal state accesses.  The grid has one workgroup per unit:
+// a workgroup of D/32 waves owns unit blockIdx.x (wave w: rows 32w..32w+31).  With
 // one-wave workgroups (no output norm: the rows of a unit are independent) the
 // D/32 row groups of a unit are D/32 workgroups, so a few units still spread
-// over many compute units: workgroup b takes row group b % (D/32) of units
-// b / (D/32), b / (D/32) + gridDim.x / (D/32), ...
+// over many compute units: workgroup b takes row group b % (D/32) of unit
+// b / (D/32) (gridDim.x is a multiple of D/32).
 template <int D, bool IN_BF16, bool OUT_BF16>
 __global__ __launch_bounds__(2 * D) void decode_step_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
@@ -253,21 +277,26 @@ __global__ __launch_bounds__(2 * D) void decode_step_kernel(
     const int32_t* __restrict__ slots, int num_slots, void* __restrict__ out, int units, int h_k, int h_v,
     int l2norm, float scale, int fuse, const float* __restrict__ norm_w, float norm_eps) {
     __shared__ __align__(16) float ubuf[(D / 32) * 32];
-    __shared__ __align__(16) float nsum[2 * (D / 32)];
+    __shared__ __align__(16) float nsum[D / 32];
     constexpr int NW = D / 32;
     const bool split = blockDim.x == WAVE;  // one-wave workgroups (launched only without the norm)
     const int wave = split ? (int)(blockIdx.x % NW) : (int)(threadIdx.x / WAVE);
-    const int u0 = split ? (int)(blockIdx.x / NW) : (int)blockIdx.x;
-    const int stride = split ? (int)(gridDim.x / NW) : (int)gridDim.x;
+    const int u = split ? (int)(blockIdx.x / NW) : (int)blockIdx.x;
+    if (u >= units) return;  // the whole workgroup
     float* ub = ubuf + wave * 32;
     const bool raw_gates = (fuse & 1) != 0;
-    if (fuse & 2)
-        decode_units<D, IN_BF16, OUT_BF16, true>(q, k, v, g, beta, state, slots, num_slots, out, units, h_k, h_v,
-                                                 l2norm, scale, raw_gates, norm_w, norm_eps, ub, nsum, wave, u0,
-                                                 stride);
-    else
-        decode_units<D, IN_BF16, OUT_BF16, false>(q, k, v, g, beta, state, slots, num_slots, out, units, h_k, h_v,
-                                                  l2norm, scale, raw_gates, nullptr, 0.f, ub, nsum, wave, u0, stride);
+#define GDN_UNIT(NORM, NT)                                                                                      \
+    decode_unit<D, IN_BF16, OUT_BF16, NORM, NT>(q, k, v, g, beta, state, slots, num_slots, out, h_k, h_v, l2norm, \
+                                                scale, raw_gates, NORM ? norm_w : nullptr, NORM ? norm_eps : 0.f,  \
+                                                ub, nsum, wave, u)
+    if (fuse & 2) {
+        if (fuse & 4) GDN_UNIT(true, true);
+        else GDN_UNIT(true, false);
+    } else {
+        if (fuse & 4) GDN_UNIT(false, true);
+        else GDN_UNIT(false, false);
+    }
+#undef GDN_UNIT
 }
 
 // ---- direct scan: the token recurrence with the state in registers ---------------------
@@ -345,9 +374,11 @@ __device__ __forceinline__ void direct_unit(const void* __restrict__ q, const vo
                                            hk, h_k, h_v, wave, lane);
                     float alpha, bta;
                     token_gates(cur.g, cur.b, raw_gates, alpha, bta);
-                    decode_token<D, OUT_BF16, NORM>(sr, cur.kx, cur.qx, cur.v, alpha, bta, out,
-                                                    (size_t)(t + i) * h_v + h, l2norm, scale, ub, wave, lane, wrow,
-                                                    eps, nsum + ((t + i - b0) & 1) * (D / 32));
+                    float* nb = nsum + ((t + i - b0) & 1) * (D / 32);
+                    const size_t orow = (size_t)(t + i) * h_v + h;
+                    const float ov = decode_token<D, OUT_BF16, NORM>(sr, cur.kx, cur.qx, cur.v, alpha, bta, out,
+                                                                     orow, l2norm, scale, ub, wave, lane, nb);
+                    if constexpr (NORM) norm_output<D, OUT_BF16>(ov, out, orow, wave, lane, wrow, eps, nb);
                 }
             }
         }
@@ -401,11 +432,24 @@ hipError_t launch_direct(int d, bool in_bf16, bool out_bf16, const void* q, cons
     return hipErrorInvalidValue;
 }
 
+// Most units one launch takes, one workgroup of 2 d threads each: the grid
+// stays below 2^32 work-items.  The state of that many units (512 GiB at
+// d = 64) exceeds the 288 GB of device memory.
+template <int D>
+constexpr int decode_max_units() { return (int)((1LL << 31) / D) - 1; }
+// Dynamic LDS, unused, that the d = 128 whole-unit launch reserves so that two
+// workgroups share a compute unit (the registers would allow four).  Measured
+// on MI355X with states beyond the last-level cache, two move the state 3-7%
+// faster than four, with either cache policy (256 and 1024 sequences x 32
+// heads); a state that stays in the cache steps ~1% slower.  At d = 64, whose
+// workgroups have two waves, the same cap measured slower at small batches.
+constexpr size_t kDecodeResidencyLds = 60 * 1024;
+
 template <int D, bool IB, bool OB>
 static hipError_t launch_decode_t(const void* q, const void* k, const void* v, const float* g,
                                   const float* beta, float* state, const int32_t* slots, int num_slots,
                                   void* out, int units, int h_k, int h_v, int l2norm, float scale, int fuse,
-                                  const float* norm_w, float norm_eps, int grid, hipStream_t stream) {
+                                  const float* norm_w, float norm_eps, hipStream_t stream) {
     // Too few units to fill the chip (and no output norm): one-wave workgroups, one per
     // row group of a unit, so each unit's rows spread over D/32 compute units.
     const bool split = !(fuse & 2) && (long long)units * (D / 32) <= 2LL * compute_units();
@@ -415,7 +459,9 @@ static hipError_t launch_decode_t(const void* q, const void* k, const void* v, c
                            norm_eps);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((decode_step_kernel<D, IB, OB>), dim3(grid), dim3(2 * D), 0, stream, q, k, v,
+    if (units > decode_max_units<D>()) return hipErrorInvalidValue;
+    const size_t lds = D == 128 ? kDecodeResidencyLds : 0;
+    hipLaunchKernelGGL((decode_step_kernel<D, IB, OB>), dim3(units), dim3(2 * D), lds, stream, q, k, v,
                        g, beta, state, slots, num_slots, out, units, h_k, h_v, l2norm, scale, fuse, norm_w,
                        norm_eps);
     return hipGetLastError();
@@ -424,12 +470,11 @@ static hipError_t launch_decode_t(const void* q, const void* k, const void* v, c
 hipError_t launch_decode(int d, bool in_bf16, bool out_bf16, const void* q, const void* k,
                          const void* v, const float* g, const float* beta, float* state, const int32_t* slots,
                          int num_slots, void* out, int units, int h_k, int h_v, int l2norm, float scale,
-                         int fuse, const float* norm_w, float norm_eps, int grid, hipStream_t stream) {
-    if (grid < 1 || grid > units) grid = units;
+                         int fuse, const float* norm_w, float norm_eps, hipStream_t stream) {
 #define GDN_DEC(D, IB, OB)                                                                        \
     if (d == D && in_bf16 == IB && out_bf16 == OB)                                                \
         return launch_decode_t<D, IB, OB>(q, k, v, g, beta, state, slots, num_slots, out, units, h_k, h_v, \
-                                          l2norm, scale, fuse, norm_w, norm_eps, grid, stream);
+                                          l2norm, scale, fuse, norm_w, norm_eps, stream);
     GDN_DEC(128, true, true) GDN_DEC(128, true, false) GDN_DEC(128, false, true)
     GDN_DEC(128, false, false) GDN_DEC(64, true, true) GDN_DEC(64, true, false)
     GDN_DEC(64, false, true) GDN_DEC(64, false, false)

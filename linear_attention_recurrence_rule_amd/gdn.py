@@ -254,6 +254,7 @@ def gdn_decode_step(desc, q, k, v, g, beta, state, out, stream=None):
 
 GDN_FUSE_GATE_ACTIVATIONS = 1
 GDN_FUSE_OUTPUT_NORM = 2
+GDN_STREAM_STATE = 4
 
 
 def gdn_prefill_direct_ex(desc, q, k, v, g, beta, state_in, out, state_out, cu_seqlens, fuse, norm_weight,
@@ -424,9 +425,10 @@ def prefill_direct(q, k, v, g, beta, *, state_in=None, state_out=None, cu_seqlen
 
 
 def decode_step(q, k, v, g, beta, state, *, out=None, out_dtype=None, qk_l2norm=True, scale=1.0,
-                stream=None):
+                stream_state=False, stream=None):
     """One token per sequence: q, k [N, h_k, d]; v [N, h_v, d]; g, beta [N, h_v];
-    state [N, h_v, d, d] fp32, updated in place.  Returns out [N, h_v, d]."""
+    state [N, h_v, d, d] fp32, updated in place.  Returns out [N, h_v, d].
+    stream_state: nontemporal state accesses (GDN_STREAM_STATE), same results."""
     dev = q.device
     io = _io_dtype(q)
     N, h_k, d = q.shape
@@ -441,17 +443,22 @@ def decode_step(q, k, v, g, beta, state, *, out=None, out_dtype=None, qk_l2norm=
                      qk_l2norm=qk_l2norm, scale=scale)
     if out is None:
         out = torch.empty((N, h_v, d), dtype=_TORCH_DT[od], device=dev)
-    gdn_decode_step(desc, q, k, v, g, beta, state, out, stream)
+    if stream_state:
+        gdn_decode_step_ex(desc, q, k, v, g, beta, state, out, GDN_STREAM_STATE, None, 0.0, stream)
+    else:
+        gdn_decode_step(desc, q, k, v, g, beta, state, out, stream)
     return out
 
 
 def decode_step_fused(q, k, v, g, beta, state, *, raw_gates=True, output_norm=True, norm_weight=None,
-                      norm_eps=1e-6, out=None, out_dtype=None, qk_l2norm=True, scale=1.0, stream=None):
+                      norm_eps=1e-6, out=None, out_dtype=None, qk_l2norm=True, scale=1.0, stream_state=False,
+                      stream=None):
     """decode_step with the per-token operations beside it folded in: with
     raw_gates, g and beta are the raw inputs x_g, x_beta (alpha = 1 / (1 + e^x_g),
     beta = 1 / (1 + e^-x_beta)); with output_norm, each head's output is divided by
     its root-mean-square over d (plus norm_eps inside the root) and multiplied by
-    norm_weight ([d] fp32, None for ones).  state is updated in place."""
+    norm_weight ([d] fp32, None for ones).  state is updated in place; stream_state as in
+    decode_step."""
     dev = q.device
     io = _io_dtype(q)
     N, h_k, d = q.shape
@@ -470,7 +477,8 @@ def decode_step_fused(q, k, v, g, beta, state, *, raw_gates=True, output_norm=Tr
                      qk_l2norm=qk_l2norm, scale=scale)
     if out is None:
         out = torch.empty((N, h_v, d), dtype=_TORCH_DT[od], device=dev)
-    fuse = (GDN_FUSE_GATE_ACTIVATIONS if raw_gates else 0) | (GDN_FUSE_OUTPUT_NORM if output_norm else 0)
+    fuse = ((GDN_FUSE_GATE_ACTIVATIONS if raw_gates else 0) | (GDN_FUSE_OUTPUT_NORM if output_norm else 0)
+            | (GDN_STREAM_STATE if stream_state else 0))
     gdn_decode_step_ex(desc, q, k, v, g, beta, state, out, fuse, norm_weight, norm_eps, stream)
     return out
 

@@ -223,8 +223,11 @@ def test_decode_ex_rejects_bad_arguments(L):
     assert call(desc(num_seqs=8, h_v=30)) == gdn.GDN_ERR_INVALID_ARGUMENT
     assert call(desc(num_seqs=8, d=32)) == gdn.GDN_ERR_UNSUPPORTED
     assert call(desc(num_seqs=8), s=None) == gdn.GDN_ERR_INVALID_ARGUMENT
-    assert call(desc(num_seqs=8), f=4) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call(desc(num_seqs=8), f=8) == gdn.GDN_ERR_INVALID_ARGUMENT
     assert "flags" in gdn.last_error()
+    # one workgroup of 2 d threads per unit: 2^19 x 32 units x 256 reaches 2^32 work-items
+    assert call(desc(num_seqs=1 << 19), f=gdn.GDN_STREAM_STATE) == gdn.GDN_ERR_UNSUPPORTED
+    assert "units" in gdn.last_error()
     for eps in (0.0, -1e-6, float("nan"), float("inf")):
         assert call(desc(num_seqs=8), e=eps) == gdn.GDN_ERR_INVALID_ARGUMENT
         assert "norm_eps" in gdn.last_error()
@@ -245,6 +248,7 @@ def test_direct_ex_rejects_bad_arguments(L):
     assert call(desc(total_tokens=16, h_v=30)) == gdn.GDN_ERR_INVALID_ARGUMENT
     assert call(desc(total_tokens=16), f=8) == gdn.GDN_ERR_INVALID_ARGUMENT
     assert "flags" in gdn.last_error()
+    assert call(desc(total_tokens=16), f=gdn.GDN_STREAM_STATE) == gdn.GDN_ERR_INVALID_ARGUMENT  # decode only
     assert call(desc(total_tokens=16), e=0.0) == gdn.GDN_ERR_INVALID_ARGUMENT
     assert call(desc(total_tokens=16), e=float("nan")) == gdn.GDN_ERR_INVALID_ARGUMENT
     assert call(desc(total_tokens=16), w=(FAKE + 6 << 32) + 64) == gdn.GDN_ERR_INVALID_ARGUMENT  # weight in out

@@ -223,7 +223,8 @@ def _fused_step(x, t, state, fuse, w, out_dt, eps=1e-6):
                                 dev(x["x_g"][t] if fuse & 1 else x["g"][t]),
                                 dev(x["x_beta"][t] if fuse & 1 else x["beta"][t]), state,
                                 raw_gates=bool(fuse & 1), output_norm=bool(fuse & 2),
-                                norm_weight=None if w is None else dev(w), norm_eps=eps, out_dtype=out_dt)
+                                norm_weight=None if w is None else dev(w), norm_eps=eps, out_dtype=out_dt,
+                                stream_state=bool(fuse & 4))
     return out
 
 
@@ -235,12 +236,12 @@ def _fused_ref(x, t, ref_state, fuse, w, eps=1e-6):
                                  output_norm=bool(fuse & 2), norm_weight=w, norm_eps=eps)
 
 
-@pytest.mark.parametrize("fuse", [1, 2, 3])
+@pytest.mark.parametrize("fuse", [1, 2, 3, 7])
 @pytest.mark.parametrize("d,io,out_dt", [(128, inputs.BF16, inputs.BF16), (128, inputs.BF16, inputs.F32),
                                          (64, inputs.F32, inputs.F32), (64, inputs.BF16, inputs.BF16)])
 def test_decode_fused_matches_oracle(fuse, d, io, out_dt):
     """Three steps in place with raw gates (x_g, x_beta ~ N(0, 1)), the output norm
-    (random channel weights, eps 1e-6), or both."""
+    (random channel weights, eps 1e-6), or both; 7 adds the nontemporal state accesses."""
     N, h_k, h_v, steps = 5, 2, 4, 3
     x = inputs.decode_inputs(seed=61 + d + io + 4 * fuse, num_seqs=N, steps=steps, h_k=h_k, h_v=h_v, d=d,
                              io_dtype=io, state_std=0.3)
@@ -278,6 +279,24 @@ def test_decode_fused_flags_off_and_norm_leave_the_state_bitwise():
     assert torch.equal(states[2], states[0]) and torch.equal(states[3], states[1])
 
 
+@pytest.mark.parametrize("fuse", [0, 1, 2, 3])
+@pytest.mark.parametrize("N,h_k,h_v,d", [(6, 2, 8, 128), (16, 16, 32, 128), (40, 2, 4, 64)])
+def test_decode_stream_state_is_bitwise_the_same(fuse, N, h_k, h_v, d):
+    """GDN_STREAM_STATE changes only the cache policy of the state accesses: outputs and
+    state equal those without it bit for bit, with every combination of the other flags.
+    Without the norm, 6 x 8 units run as one-wave workgroups (one per 32-row group) and the
+    other shapes as one workgroup per unit; two steps in place."""
+    x = inputs.decode_inputs(seed=83 + N + d, num_seqs=N, steps=2, h_k=h_k, h_v=h_v, d=d, io_dtype=inputs.BF16,
+                             state_std=0.3)
+    w = (1.0 + 0.5 * np.random.default_rng(9).standard_normal(d)).astype(np.float32)
+    s_plain, s_stream = dev(x["state"]), dev(x["state"])
+    for t in range(2):
+        o_plain = _fused_step(x, t, s_plain, fuse, w, inputs.F32)
+        o_stream = _fused_step(x, t, s_stream, fuse | 4, w, inputs.F32)
+        assert torch.equal(o_plain, o_stream)
+        assert torch.equal(s_plain, s_stream)
+
+
 def test_decode_fused_extreme_raw_gates():
     """Raw gate inputs at +-100 and 0: alpha and beta reach 0 and 1 without overflow."""
     N, h_k, h_v, d = 4, 1, 6, 64
@@ -295,8 +314,8 @@ def test_decode_fused_extreme_raw_gates():
 
 def test_decode_fused_full_workload():
     """The 64-sequence x 32-v-head, d = 128 decode workload with both folds, raw gates
-    from the workload's own N(0, 1) draws: four units per persistent workgroup, so the
-    output norm's two alternating LDS exchange areas are both reused; two steps in place."""
+    from the workload's own N(0, 1) draws (2048 workgroups, one per unit, each with its
+    own output-norm exchange); two steps in place."""
     w_ = inputs.WORKLOADS["decode_n64_hv32_hk16_d128_512steps"]
     x = inputs.workload_inputs(w_, steps=2)
     w = (1.0 + 0.25 * np.random.default_rng(5).standard_normal(w_.d)).astype(np.float32)
