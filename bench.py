@@ -535,11 +535,11 @@ def main():
                          "16 packed sequences) with tok/s and roofline fractions (one JSON line each)")
     ap.add_argument("--decode-sweep", action="store_true",
                     help="instead of the benchmark line: the decode step by batch size, 1 to 1024 sequences "
-                         "of 32 v-heads, plain and fused (one JSON line per size)")
+                         "of 32 v-heads, plain, fused and with GDN_STREAM_STATE (one JSON line per size)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on exactly one GPU; --gpus %d is not supported "
-              "(the multi-GPU sharding is described in DESIGN.md, not built)." % args.gpus, file=sys.stderr)
+        print("bench.py: the library and this benchmark run on one GPU; --gpus %d is not supported "
+              "(sharding heads and sequences over GPUs is not implemented)." % args.gpus, file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
