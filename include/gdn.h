@@ -435,7 +435,7 @@ gdn_status gdn_prefill_direct_ex(const gdn_desc *desc,
  * results and errors are those of gdn_prefill, whose result this is bit for
  * bit.
  */
-#define GDN_PREFILL_NOALLOC_WORKSPACE_BYTES (32u << 20)
+#define GDN_PREFILL_NOALLOC_WORKSPACE_BYTES (64u << 20)
 
 gdn_status gdn_prefill_noalloc(const gdn_desc *desc,
                                const void *q, const void *k, const void *v,

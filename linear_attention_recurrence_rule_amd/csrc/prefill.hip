@@ -1015,11 +1015,13 @@ __global__ __launch_bounds__(SCAN_THREADS) void chunk_scan_kernel(
 
 // ---- host launchers ----------------------------------------------------------------------
 size_t tp_record_bytes();
+size_t key16_record_bytes(int d);
 hipError_t launch_prep_bf16(int d, const void* q, const void* k, const float* g, const float* beta,
                             const void* info, const int32_t* slot_seq, int slots, int T, int h_k, int h_v,
-                            int l2norm, float scale, void* recs, unsigned* clear_status, hipStream_t stream);
+                            int l2norm, float scale, void* recs, void* krecs, unsigned* clear_status,
+                            hipStream_t stream);
 hipError_t launch_scan_bf16(int d, bool out_bf16, int rows, int mode, const void* q, const void* k, const void* v,
-                            const void* recs, const void* info, const float* s_in, float* s_out, void* out, void* sink,
+                            const void* recs, const void* krecs, const void* info, const float* s_in, float* s_out, void* out, void* sink,
                             int units, int T, int h_k, int h_v, unsigned* status, hipStream_t stream);
 
 // Workspace record sizes: bf16 inputs use one record per (block slot, v-head)
@@ -1031,7 +1033,7 @@ size_t prefill_record_bytes(int d, bool in_bf16) {
 }
 
 size_t prefill_key_record_bytes(int d, bool in_bf16) {
-    if (in_bf16) return 0;
+    if (in_bf16) return key16_record_bytes(d);
     return d == 128 ? KeyRec<128, float>::BYTES : KeyRec<64, float>::BYTES;
 }
 
@@ -1089,7 +1091,7 @@ hipError_t launch_prep(int d, bool in_bf16, const void* q, const void* k, const 
                        int slots, int T, int h_k, int h_v, int l2norm, float scale, void* recs,
                        void* krecs, unsigned* clear_status, hipStream_t stream) {
     if (in_bf16)
-        return launch_prep_bf16(d, q, k, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, recs,
+        return launch_prep_bf16(d, q, k, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, recs, krecs,
                                 clear_status, stream);
     if (d == 64)
         return launch_prep_t<64, float, false>(q, k, v, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale,
@@ -1129,7 +1131,7 @@ hipError_t launch_scan(int d, bool in_bf16, bool out_bf16, int rows, const void*
                        hipStream_t stream) {
     const int rs = scan_rows_per_workgroup(d, in_bf16, units, rows);
     if (in_bf16)
-        return launch_scan_bf16(d, out_bf16, rs, 0, q, k, v, recs, info, s_in, s_out, out, sink, units, T, h_k, h_v,
+        return launch_scan_bf16(d, out_bf16, rs, 0, q, k, v, recs, krecs, info, s_in, s_out, out, sink, units, T, h_k, h_v,
                                 status, stream);
 #define GDN_SCAN(D, OP, IB, OB)                                                                                \
     if (d == D && in_bf16 == IB && out_bf16 == OB)                                                             \
@@ -1228,7 +1230,7 @@ hipError_t launch_scan_transition(int d, bool in_bf16, int rows, const void* q, 
                                   int units, int T, int h_k, int h_v, hipStream_t stream) {
     const int rs = scan_rows_per_workgroup(d, in_bf16, units, rows);
     if (in_bf16)
-        return launch_scan_bf16(d, false, rs, 1, q, k, v, recs, info, nullptr, s_out, nullptr, sink, units, T, h_k,
+        return launch_scan_bf16(d, false, rs, 1, q, k, v, recs, krecs, info, nullptr, s_out, nullptr, sink, units, T, h_k,
                                 h_v, nullptr, stream);
     if (d == 64)
         return rs == 16 ? launch_scan_t<64, float, false, 16, 1>(recs, krecs, info, nullptr, s_out, nullptr, sink,

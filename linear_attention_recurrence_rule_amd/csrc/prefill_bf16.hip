@@ -48,6 +48,25 @@ struct TpRec {
 };
 __device__ __forceinline__ int tri_frag(int mb, int kb) { return mb < 2 ? mb : 2 * mb - 2 + kb; }
 
+// ---- key record of one (block slot, k-head) -----------------------------------------------
+// The block's keys and queries as fp16, each token's row scaled by 2^-E with E
+// the exponent of the row's largest magnitude (so every element is below 1 and
+// the conversion from bf16 is exact down to 2^-14 of that magnitude), then the
+// factors 2^E per token (keys, then queries).  The keys keep the swizzled row
+// layout of the raw tiles (raw_unit): the scan reads them as rows and as
+// columns from LDS.  The queries are stored as the A fragments of their 16-token
+// blocks (fragment tb * (D / 32) + kb, 64 lanes x 16 bytes, the order of
+// raw_rowfrag), which the scan loads straight into registers.  Both v-heads of
+// a k-head read the same record.
+template <int D>
+struct KeyRec16 {
+    static constexpr size_t K = 0;
+    static constexpr size_t Q = (size_t)CHUNK * D * 2;
+    static constexpr size_t E = 2 * (size_t)CHUNK * D * 2;
+    static constexpr size_t BYTES = E + 1024;
+    static constexpr int EK = 0, EQ = 64;  // float offsets in E
+};
+
 // Byte offset of the 16-byte unit u of row r in a swizzled raw tile of D bf16 per row:
 // the units of row r are permuted by XOR with (r mod units per row), so that a
 // column read or a read of 16 rows at one column spreads over the LDS banks.
@@ -97,6 +116,18 @@ __device__ __forceinline__ bf8_t raw_colfrag(const uint16_t* M, int cb, int kb, 
 
 __device__ __forceinline__ void mma_bf16(f4_t& acc, const bf8_t& a, const bf8_t& b) {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma_f16(f4_t& acc, const h8_t& a, const h8_t& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+}
+// The row and column fragments above, of a tile of fp16 elements in the same layout.
+template <int D>
+__device__ __forceinline__ h8_t h16_rowfrag(const _Float16* M, int rb, int kb, int lane) {
+    return __builtin_bit_cast(h8_t, raw_rowfrag<D>(reinterpret_cast<const uint16_t*>(M), rb, kb, lane));
+}
+template <int D>
+__device__ __forceinline__ h8_t h16_colfrag(const _Float16* M, int cb, int kb, int lane) {
+    return __builtin_bit_cast(h8_t, raw_colfrag<D>(reinterpret_cast<const uint16_t*>(M), cb, kb, lane));
 }
 
 __device__ __forceinline__ float bf16_lo_bits(uint32_t w) { return __uint_as_float(w << 16); }
@@ -159,8 +190,8 @@ template <int D, int NH>
 __global__ __launch_bounds__(PAIR_THREADS, 1) void chunk_prep_pair_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const float* __restrict__ g,
     const float* __restrict__ beta, const SeqInfo* __restrict__ info, const int32_t* __restrict__ slot_seq,
-    int T, int h_k, int h_v, int l2norm, float scale, char* __restrict__ recs, int slots, int items_per_wg,
-    unsigned* __restrict__ clear_status) {
+    int T, int h_k, int h_v, int l2norm, float scale, char* __restrict__ recs, char* __restrict__ krecs, int slots,
+    int items_per_wg, unsigned* __restrict__ clear_status) {
     using OP = _Float16;
     using LT = PairLds<D, NH>;
     if (clear_status && blockIdx.x == 0 && threadIdx.x == 0) *clear_status = 0u;  // a new call's status word
@@ -363,6 +394,52 @@ __global__ __launch_bounds__(PAIR_THREADS, 1) void chunk_prep_pair_kernel(
                         const bf8_t x = raw_row8<D>(L.kraw, b, kb, lane);
                         mma_bf16(acc[b], x, x);
                     }
+                }
+            }
+        }
+        if (live && pr == 0) {
+            // The key record of (block slot, k-head), written once per k-head: every
+            // compute wave takes 8 rows of the key and the query tile.  A row's UPR
+            // 16-byte units sit in UPR consecutive lanes, which find the row's largest
+            // magnitude together; the row is scaled by 2^-E and rounded to fp16.
+            constexpr int UPR = D / 8, RPR = WAVE / UPR, ROUNDS = 8 / RPR;
+            const int u = lane % UPR;
+            char* kr = krecs + ((size_t)slot * h_k + hk) * KeyRec16<D>::BYTES;
+#pragma unroll
+            for (int op = 0; op < 2; ++op) {
+                const uint16_t* tile = op ? L.qraw : L.kraw;
+#pragma unroll
+                for (int rr = 0; rr < ROUNDS; ++rr) {
+                    const int r = 8 * wave + RPR * rr + lane / UPR;
+                    const uint4 w4 = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(tile) + raw_unit<D>(r, u));
+                    const uint32_t wd[4] = {w4.x, w4.y, w4.z, w4.w};
+                    float x[8], m = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        x[2 * e] = bf16_lo_bits(wd[e]);
+                        x[2 * e + 1] = bf16_hi_bits(wd[e]);
+                        m = fmaxf(m, fmaxf(fabsf(x[2 * e]), fabsf(x[2 * e + 1])));
+                    }
+                    m = group_max<UPR>(m);
+                    const int E = min(__builtin_amdgcn_frexp_expf(m), 127);
+                    h8_t hx;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) hx[e] = (_Float16)__builtin_amdgcn_ldexpf(x[e], -E);
+                    if (op == 0) {
+                        *reinterpret_cast<h8_t*>(kr + KeyRec16<D>::K + raw_unit<D>(r, u)) = hx;
+                    } else {
+                        // queries in A-fragment order: columns 32 kb + o .. + 7 (o = 8 (u mod 4)) of row
+                        // 16 tb + i are elements 4 h .. 4 h + 3 (h = o / 16) of lanes i + 16 qq and
+                        // i + 16 (qq + 1), qq = (o mod 16) / 4, in fragment tb * (D / 32) + kb
+                        const int o = 8 * (u & 3), hh = o >> 4, qq = (o & 15) >> 2;
+                        char* fb = kr + KeyRec16<D>::Q + (size_t)(((r >> 4) * (D / 32) + (u >> 2)) * WAVE) * 16 + 8 * hh;
+                        const uint4 bits = __builtin_bit_cast(uint4, hx);
+                        *reinterpret_cast<uint2*>(fb + ((r & 15) + 16 * qq) * 16) = uint2{bits.x, bits.y};
+                        *reinterpret_cast<uint2*>(fb + ((r & 15) + 16 * (qq + 1)) * 16) = uint2{bits.z, bits.w};
+                    }
+                    if (u == 0)
+                        reinterpret_cast<float*>(kr + KeyRec16<D>::E)[(op ? KeyRec16<D>::EQ : KeyRec16<D>::EK) + r] =
+                            __builtin_amdgcn_ldexpf(1.f, E);
                 }
             }
         }
@@ -1003,24 +1080,32 @@ __global__ __launch_bounds__(TPS_MAX_THREADS) void chunk_scan_tp_kernel(
 // ============================================================================================
 // chunk_scan_tpf: the scan for 16-row slices, two waves per token block
 // ============================================================================================
-// The inputs and the arithmetic of chunk_scan_tp (MODE 0, one 16-row slice per
-// workgroup), with the roles arranged so that no partial product crosses waves.
-// Every wave that contracts with S^T reads its bf16 high / low parts from LDS
-// (a Y-wave all but its own share), and per-wave LDS reads are the scarce
-// resource, so the work of token block tb is split over two waves:
-//   Y-wave tb (w = tb):     Y and R, U = T R and the parts of diag(s c) U, and
-//                           the update of the fp32 S^T tiles 16 TPW tb .. + 16 TPW - 1
-//                           of the keys (TPW = D / 64 tiles), which it holds;
-//   Z-wave tb (w = 4 + tb): Z = Q^raw S^T and O = diag(gamma c_q) Z + P U, and
+// The arithmetic of chunk_scan_tp (MODE 0, one 16-row slice per workgroup) on
+// fp16 matrix cores with power-of-two scaling instead of bf16 high / low parts:
+//   * keys and queries come from the key records, each token's row scaled by
+//     2^-E and rounded to fp16; the factors 2^E join gamma c, s c and gamma c_q;
+//   * S^T is published as one fp16 fragment per 32-wide key block kb, each of
+//     its 16 columns (rows of S) scaled by 2^-F(kb, column), F the exponent of
+//     that column's largest magnitude in the block, so every element is below 1
+//     and the fp32 range of S is kept.  A product with S^T keeps one
+//     accumulator per kb and sums them with the factors 2^F;
+//   * diag(s c 2^E) U, the operand of the update, is one fp16 fragment like U.
+// The roles are arranged so that no partial product crosses waves; per-wave LDS
+// reads are the scarce resource, so the work of token block tb is split over
+// two waves:
+//   Y-wave tb (w = tb):     Y and R, U = T R and diag(s c 2^E) U; the Y-waves
+//                           w < D / 32 also hold the fp32 S^T tiles of key block
+//                           w and update and publish them;
+//   Z-wave tb (w = 4 + tb): Z = Q S^T and O = diag(gamma c_q 2^E) Z + P U, and
 //                           the output stores;
 //   copier waves (w = 8..11) stream the inputs as in chunk_scan_tp.
 // Three barriers per block:
 //   B1  block c in its slot, S^T published  -> Y-waves: Y, R;  Z-waves: Z
-//   BR  R in LDS                            -> Y-waves: U, its parts;  Z-waves: block c - 1's outputs to HBM
-//   BU  U and its parts in LDS              -> Y-waves: S^T update, published;  Z-waves: O, to LDS
+//   BR  R in LDS                            -> Y-waves: U, diag(s c 2^E) U;  Z-waves: block c - 1's outputs to HBM
+//   BU  U and diag(s c 2^E) U in LDS        -> Y-waves: S^T update, published;  Z-waves: O, to LDS
 // Reads that phase B1 does not need (T, P and their factors) wait until after BR:
 // phase B1 is the one bound by the workgroup's LDS read bandwidth, and for the same
-// reason a Y-wave takes its own share of S^T from registers.
+// reason a Y-wave takes its own key block of S^T from registers.
 // The Y- and Z-waves issue no global loads inside the block loop, so the
 // Z-waves' stores never hold up a load wait.
 
@@ -1028,39 +1113,47 @@ constexpr int TPF_YW = 4, TPF_ZW = 4, TPF_LOAD = 4;
 constexpr int TPF_COMPUTE = TPF_YW + TPF_ZW;
 constexpr int TPF_THREADS = (TPF_COMPUTE + TPF_LOAD) * WAVE;
 
+template <int D>
+struct TpfSlot {
+    _Float16 k[CHUNK * D];                  // scaled fp16 keys (swizzled rows), from the key record
+    uint16_t vs[CHUNK * 16];                // the slice's raw values [token][16]
+    _Float16 tp[2][TpRec::NF * WAVE * 8];   // T and P fragments, as in the record
+    float fac[256];                         // gck, gcq, sck, gamma_n
+    float es[256];                          // 2^E of the keys and of the queries
+};
+
 template <int D, bool OUT_BF16>
 constexpr size_t tpf_scan_lds_bytes() {
-    return 3 * sizeof(TpSlot<D, 1>)           // ring
-           + 2 * (size_t)CHUNK * D * 2        // q ring
-           + 2 * (D / 32) * WAVE * 8 * 2      // S^T high / low
-           + 4 * 2 * WAVE * 8 * 2             // R, U, the high / low parts of diag(s c) U
+    return 3 * sizeof(TpfSlot<D>)             // ring
+           + (D / 32) * WAVE * 8 * 2          // S^T fragments
+           + 16 * 4 * 4                       // their column factors
+           + 3 * 2 * WAVE * 8 * 2             // R, U, diag(s c 2^E) U
            + (size_t)CHUNK * 16 * (OUT_BF16 ? 2 : 4);  // outputs
 }
 
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(TPF_THREADS) void chunk_scan_tpf_kernel(
-    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
-    const char* __restrict__ recs, const SeqInfo* __restrict__ info, const float* __restrict__ state_in,
-    float* __restrict__ state_out, void* __restrict__ out, char* __restrict__ sink, int units, int T, int h_k,
-    int h_v, unsigned* __restrict__ status) {
-    using Slot = TpSlot<D, 1>;
-    constexpr int RS = 16, SLICES = D / RS, NKB = D / 32, TPW = D / 64, RING = 3;
-    constexpr int NK = CHUNK * D * 2 / 1024;   // 1 KiB loads of a raw q or k tile
+    const void* __restrict__ v, const char* __restrict__ recs, const char* __restrict__ krecs,
+    const SeqInfo* __restrict__ info, const float* __restrict__ state_in, float* __restrict__ state_out,
+    void* __restrict__ out, char* __restrict__ sink, int units, int T, int h_k, int h_v,
+    unsigned* __restrict__ status) {
+    using Slot = TpfSlot<D>;
+    using KR = KeyRec16<D>;
+    constexpr int RS = 16, SLICES = D / RS, NKB = D / 32, RING = 3;
+    constexpr int NK = CHUNK * D * 2 / 1024;   // 1 KiB loads of a key or query tile
     constexpr int NV = CHUNK * RS * 2 / 1024;  // 1 KiB loads of the v slice
-    constexpr int KL = NK / TPF_LOAD;          // k (or q) loads per copier wave
+    constexpr int KL = NK / TPF_LOAD;          // key (or query) loads per copier wave
     constexpr int TPL = 2 * TpRec::NF / TPF_LOAD;  // T and P loads per copier wave
-    static_assert(NK % TPF_LOAD == 0 && (2 * TpRec::NF) % TPF_LOAD == 0 && NV + 1 <= TPF_LOAD,
+    static_assert(NK % TPF_LOAD == 0 && (2 * TpRec::NF) % TPF_LOAD == 0 && NV + 2 == TPF_LOAD,
                   "copy split over the copier waves");
-    static_assert(TPW >= 1 && TPW <= 2, "one or two key tiles per compute wave");
+    static_assert(NKB <= TPF_YW && NKB <= 4, "one key block of S^T per holding Y-wave");
     constexpr int OB = OUT_BF16 ? 2 : 4;  // bytes per output element
     __shared__ __align__(16) Slot ring[RING];
-    __shared__ __align__(16) uint16_t sQ[2][CHUNK * D];           // raw q ring (swizzled rows)
-    __shared__ __align__(16) uint16_t sShi[NKB * WAVE * 8];       // S^T high / low B fragments (kb)
-    __shared__ __align__(16) uint16_t sSlo[NKB * WAVE * 8];
+    __shared__ __align__(16) _Float16 sS[NKB * WAVE * 8];         // S^T fragments (kb), scaled
+    __shared__ __align__(16) float sScl[16 * 4];                  // 2^F of column j, key block kb at [4 j + kb]
     __shared__ __align__(16) _Float16 sR[2 * WAVE * 8];           // R, fp16 B fragments (32-token block)
     __shared__ __align__(16) _Float16 sU[2 * WAVE * 8];           // U
-    __shared__ __align__(16) uint16_t sUh[2 * WAVE * 8];          // diag(s c) U, bf16 high / low parts
-    __shared__ __align__(16) uint16_t sUl[2 * WAVE * 8];
+    __shared__ __align__(16) _Float16 sUs[2 * WAVE * 8];          // diag(s c 2^E) U
     __shared__ __align__(16) char sO[CHUNK * RS * OB];            // one block's 64 x 16 outputs, row-major
     // XCD placement as in chunk_scan_tp: a unit's SLICES workgroups share an XCD.
     const int xcd = blockIdx.x % 8, m = blockIdx.x / 8;
@@ -1084,28 +1177,24 @@ __global__ __launch_bounds__(TPF_THREADS) void chunk_scan_tpf_kernel(
 
     if (w >= TPF_COMPUTE) {
         // ------------------------------ copier waves ------------------------------
-        // Block c + 2 is copied during block c: k after B1 (the slot of block c - 1 is
-        // free), q after BR (block c's q has been read), T, P, the v slice and the
-        // factors after BU.  Every load moves 16 bytes a lane; copiers 0 .. NV - 1 also
-        // take a 1 KiB piece of the v slice, copier NV the factors.  Before B1 of block
-        // c + 1 a copier waits until only block c + 2's loads are in flight.
+        // Block c + 2 is copied during block c: its keys after B1 (the slot of block
+        // c - 1 is free), T, P, the v slice and the factors after BU.  Every load moves
+        // 16 bytes a lane; copiers 0 .. NV - 1 also take a 1 KiB piece of the v slice,
+        // copier NV the record's factors and copier NV + 1 the key record's.  Before B1
+        // of block c + 1 a copier waits until only block c + 2's loads are in flight.
         typedef __attribute__((address_space(3))) void* lds_ptr;
         const int lw = w - TPF_COMPUTE;
-        constexpr int RPI = 1024 / (2 * D), UPR = D / 8;  // rows per 1 KiB load, 16-byte units per row
-        auto tile_load = [&](const void* base, int tok0, uint16_t* dst, int i) __attribute__((always_inline)) {
-            const int r = i * RPI + lane / UPR, p = lane % UPR;
-            const int u = p ^ (r & (UPR - 1));  // the global unit this lane's LDS slot holds (raw_unit)
-            const size_t tt = (size_t)min(tok0 + r, T - 1);
-            const uint16_t* src = reinterpret_cast<const uint16_t*>(base) + (tt * h_k + hk) * D + 8 * u;
-            __builtin_amdgcn_global_load_lds(src, (lds_ptr)(dst + i * 512), 16, 0, 0);
+        auto krec = [&](int c) __attribute__((always_inline)) {
+            return krecs + ((size_t)(slot0 + c) * h_k + hk) * KR::BYTES;
         };
         auto copy_k = [&](int c) __attribute__((always_inline)) {
+            const char* src = krec(c) + KR::K;
+            char* dst = reinterpret_cast<char*>(ring[c % RING].k);
 #pragma unroll
-            for (int mm = 0; mm < KL; ++mm) tile_load(k, begin + c * CHUNK, ring[c % RING].k, TPF_LOAD * mm + lw);
-        };
-        auto copy_q = [&](int c) __attribute__((always_inline)) {
-#pragma unroll
-            for (int mm = 0; mm < KL; ++mm) tile_load(q, begin + c * CHUNK, sQ[c & 1], TPF_LOAD * mm + lw);
+            for (int mm = 0; mm < KL; ++mm) {
+                const int j = TPF_LOAD * mm + lw;
+                __builtin_amdgcn_global_load_lds(src + j * 1024 + lane * 16, (lds_ptr)(dst + j * 1024), 16, 0, 0);
+            }
         };
         auto copy_rest = [&](int c) __attribute__((always_inline)) {
             Slot* sl = &ring[c % RING];
@@ -1123,18 +1212,16 @@ __global__ __launch_bounds__(TPF_THREADS) void chunk_scan_tpf_kernel(
                 __builtin_amdgcn_global_load_lds(src, (lds_ptr)(sl->vs + lw * 512), 16, 0, 0);
             } else if (lw == NV) {
                 __builtin_amdgcn_global_load_lds(rec + TpRec::F + lane * 16, (lds_ptr)(sl->fac), 16, 0, 0);
+            } else {
+                const char* src = krec(c) + KR::E + lane * 16;
+                __builtin_amdgcn_global_load_lds(src, (lds_ptr)(sl->es), 16, 0, 0);
             }
         };
-        // loads per block of this copier: k, q, T and P, and one v or factor load for copiers 0 .. NV
-        constexpr int LB = 2 * KL + TPL;
-        auto wait_all_but_block = [&]() __attribute__((always_inline)) {  // all but one block's loads landed
-            if (lw <= NV) wait_vmcnt<LB + 1>();
-            else wait_vmcnt<LB>();
-        };
-        if (nchunks > 0) { copy_k(0); copy_q(0); copy_rest(0); }
+        constexpr int LB = KL + TPL + 1;  // loads per block of every copier
+        if (nchunks > 0) { copy_k(0); copy_rest(0); }
         if (nchunks > 1) {
-            copy_k(1); copy_q(1); copy_rest(1);
-            wait_all_but_block();
+            copy_k(1); copy_rest(1);
+            wait_vmcnt<LB>();
         } else {
             wait_vmcnt<0>();
         }
@@ -1142,11 +1229,10 @@ __global__ __launch_bounds__(TPF_THREADS) void chunk_scan_tpf_kernel(
             lds_barrier();  // B1
             if (c + 2 < nchunks) copy_k(c + 2);
             lds_barrier();  // BR
-            if (c + 2 < nchunks) copy_q(c + 2);
             lds_barrier();  // BU
             if (c + 2 < nchunks) copy_rest(c + 2);
             if (c + 1 < nchunks) {
-                if (c + 2 < nchunks) wait_all_but_block();
+                if (c + 2 < nchunks) wait_vmcnt<LB>();
                 else wait_vmcnt<0>();
             }
         }
@@ -1156,45 +1242,75 @@ __global__ __launch_bounds__(TPF_THREADS) void chunk_scan_tpf_kernel(
 
     bool bad = false;  // a non-finite output or final state in this lane
     typedef __attribute__((address_space(3))) s4v_t* lds_s4;
+    const f4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+    // Sum over the key blocks of a product with S^T: acc[i] (key block (i + rot) mod
+    // NKB) times 2^F of that block and column j16.  The accumulators are indexed by
+    // loop position only (a runtime index into a register array would compile to
+    // indexed register moves); the rotation goes into the LDS address.
+    auto combine = [&](const f4_t (&acc)[NKB], int rot) __attribute__((always_inline)) {
+        f4_t s = acc[0] * sScl[4 * j16 + rot];
+#pragma unroll
+        for (int i = 1; i < NKB; ++i) {
+            const float f = sScl[4 * j16 + ((i + rot) & (NKB - 1))];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s[e] = fmaf(acc[i][e], f, s[e]);
+        }
+        return s;
+    };
+    constexpr int LPR = RS * OB / 16;  // 16-byte pieces per output row
+    constexpr int PIECES = CHUNK * LPR;
+    // Block c's outputs, sO to HBM, by the Y-waves (they issue no loads, so no load
+    // wait ever covers these stores).
+    auto store_out = [&](int c, int yw) __attribute__((always_inline)) {
+        const int nt = min(CHUNK, len - c * CHUNK), t = yw * WAVE + lane;
+        for (int p = t; p < PIECES; p += TPF_YW * WAVE) {
+            const int row = p / LPR, col16 = p % LPR;
+            const uint4 val = *reinterpret_cast<const uint4*>(sO + row * RS * OB + col16 * 16);
+            char* dst = row < nt ? reinterpret_cast<char*>(out) +
+                                       (((size_t)(begin + c * CHUNK + row) * h_v + h) * D + r0) * OB + col16 * 16
+                                 : sink + (t % WAVE) * 16;
+            *reinterpret_cast<uint4*>(dst) = val;
+        }
+    };
     if (w >= TPF_YW) {
         // ------------------------------ Z-waves ------------------------------
+        // The query fragments of token block tb go straight from the key record into
+        // registers, two blocks ahead: block c + 2's after BR of block c, into the set
+        // block c has just used.  The loop is unrolled by two so that the sets are
+        // fixed registers.  These waves issue no stores, so each wait covers loads only.
         const int tb = w - TPF_YW, kbt = tb >> 1;
-        constexpr int LPR = RS * OB / 16;  // 16-byte pieces per output row
-        constexpr int PIECES = CHUNK * LPR;
-        auto store_out = [&](int c) __attribute__((always_inline)) {  // block c's outputs, sO to HBM
-            const int nt = min(CHUNK, len - c * CHUNK), t = tb * WAVE + lane;
-            for (int p = t; p < PIECES; p += TPF_ZW * WAVE) {
-                const int row = p / LPR, col16 = p % LPR;
-                const uint4 val = *reinterpret_cast<const uint4*>(sO + row * RS * OB + col16 * 16);
-                char* dst = row < nt ? reinterpret_cast<char*>(out) +
-                                           (((size_t)(begin + c * CHUNK + row) * h_v + h) * D + r0) * OB + col16 * 16
-                                     : sink + (t % WAVE) * 16;
-                *reinterpret_cast<uint4*>(dst) = val;
-            }
+        auto load_q = [&](h8_t (&qs)[NKB], int c) __attribute__((always_inline)) {
+            const char* src = krecs + ((size_t)(slot0 + c) * h_k + hk) * KR::BYTES + KR::Q;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+                qs[kb] = *reinterpret_cast<const h8_t*>(src + ((size_t)(tb * NKB + kb) * WAVE + lane) * 16);
         };
-        for (int c = 0; c < nchunks; ++c) {
+        auto block = [&](int c, h8_t (&qs)[NKB]) __attribute__((always_inline)) {
             const Slot& B = ring[c % RING];
-            lds_barrier();  // B1: block c in its slot, S^T published, block c - 1's outputs in sO
-            // ---- Z = Q^raw S^T for token block tb (high and low parts in two accumulators) ----
-            f4_t z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
+            lds_barrier();  // B1: block c in its slot, S^T published
+            // ---- Z = Q S^T for token block tb, one accumulator per key block ----
+            f4_t za[NKB];
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
-                const bf8_t qa = raw_rowfrag<D>(sQ[c & 1], tb, kb, lane);
-                mma_bf16(z0, qa, bfrag(sShi, kb, lane));
-                mma_bf16(z1, qa, bfrag(sSlo, kb, lane));
+                za[kb] = zero4;
+                mma_f16(za[kb], qs[kb], *reinterpret_cast<const h8_t*>(&sS[(kb * WAVE + lane) * 8]));
             }
+            f4_t z = combine(za, 0);
             // Z is complete in this phase: keeps the compiler from sinking its products
             // into phase BU, where they would contend with the Y-wave's update on this SIMD.
-            asm volatile("" : "+v"(z0), "+v"(z1));
+            asm volatile("" : "+v"(z));
             lds_barrier();  // BR
-            const f4_t gcq = *reinterpret_cast<const f4_t*>(&B.fac[TpRec::GCQ + 16 * tb + 4 * q4]);
+            // (the last two blocks reload the last block: an unconditional load keeps the
+            // compiler's wait for a set at "all but the other set's four loads")
+            load_q(qs, min(c + 2, nchunks - 1));
+            const f4_t gcq = *reinterpret_cast<const f4_t*>(&B.fac[TpRec::GCQ + 16 * tb + 4 * q4]) *
+                             *reinterpret_cast<const f4_t*>(&B.es[KR::EQ + 16 * tb + 4 * q4]);
             Frag<_Float16> pf[2];  // (for tb < 2 the second fragment repeats the first and goes unused)
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) pf[kb] = frag_stored<_Float16>(B.tp[1], tri_frag(tb, kb), lane);
-            if (c >= 1) store_out(c - 1);
             lds_barrier();  // BU: U in LDS; sO is no longer read
-            {   // ---- O = diag(gamma c_q) Z + P U ----
-                f4_t o = gcq * (z0 + z1);
+            {   // ---- O = diag(gamma c_q 2^E) Z + P U ----
+                f4_t o = gcq * z;
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
                     if (kb <= kbt) mma(o, pf[kb], frag_stored<_Float16>(sU, kb, lane));
@@ -1206,119 +1322,142 @@ __global__ __launch_bounds__(TPF_THREADS) void chunk_scan_tpf_kernel(
                     else reinterpret_cast<float*>(sO)[e] = o[r];
                 }
             }
+        };
+        if (nchunks > 0) {
+            h8_t qa[NKB], qb[NKB];
+            load_q(qa, 0);
+            load_q(qb, min(1, nchunks - 1));
+            // whole pairs, so that no path skips a set's loads (the compiler's waits then
+            // hold a set's loads only)
+            int c = 0;
+            for (; c + 1 < nchunks; c += 2) {
+                block(c, qa);
+                block(c + 1, qb);
+            }
+            if (c < nchunks) block(c, qa);
         }
-        lds_barrier();  // B1 after the last block: its outputs are in sO
-        if (nchunks > 0) store_out(nchunks - 1);
+        lds_barrier();  // B1 after the last block
         report_status(status, bad, GDN_PREFILL_STATUS_NONFINITE);
         return;
     }
 
     // ------------------------------ Y-waves ------------------------------
     const int tb = w, kbt = tb >> 1, part = tb & 1;  // token block, its 32-token block and half
-    f4_t St[TPW];  // S^T tiles 16 (TPW w + i) .. + 15 of the keys x this slice's 16 rows
+    const bool holder = w < NKB;  // holds S^T tiles 32 w .. 32 w + 31 of the keys
+    f4_t St[2];  // the two 16-key accumulator tiles of key block w x this slice's 16 rows
     const size_t sbase = (size_t)unit * D * D;
     const int srow = r0 + j16;
+    if (holder) {
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-        const int col = 16 * (TPW * w + i) + 4 * q4;
-        if (state_in) {
-            const float4 x = *reinterpret_cast<const float4*>(state_in + sbase + (size_t)srow * D + col);
-            St[i] = f4_t{x.x, x.y, x.z, x.w};
-        } else {
-            St[i] = f4_t{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < 2; ++i) {
+            const int col = 32 * w + 16 * i + 4 * q4;
+            if (state_in) {
+                const float4 x = *reinterpret_cast<const float4*>(state_in + sbase + (size_t)srow * D + col);
+                St[i] = f4_t{x.x, x.y, x.z, x.w};
+            } else {
+                St[i] = zero4;
+            }
         }
     }
-    bf8_t own_hi, own_lo;  // this wave's share of the high / low S^T fragments (TPW == 2)
-    auto publish = [&]() __attribute__((always_inline)) {  // this wave's tiles as high / low B fragment parts
-        if constexpr (TPW == 2) {
-            bf8_t hi, lo;
-            split_from_acc(St[0], St[1], hi, lo);
-            own_hi = hi;
-            own_lo = lo;
-            bfrag_store(sShi, w, lane, hi);
-            bfrag_store(sSlo, w, lane, lo);
-        } else {
-            store_split(sShi, sSlo, w >> 1, w & 1, lane, St[0]);
+    h8_t own;  // this holder's published fragment
+    auto publish = [&]() __attribute__((always_inline)) {
+        // the column's largest magnitude over key block w: each lane holds 8 of its 32
+        // entries, the lanes j16 + 16 q of the four rows of lanes the rest
+        float mx = 0.f;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fabsf(St[i][e]));
+        F2 t = permlane16_swap(mx, mx);
+        mx = fmaxf(t.x, t.y);
+        t = permlane32_swap(mx, mx);
+        mx = fmaxf(t.x, t.y);
+        const int F = __builtin_amdgcn_frexp_expf(mx);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            own[e] = (_Float16)__builtin_amdgcn_ldexpf(St[0][e], -F);
+            own[e + 4] = (_Float16)__builtin_amdgcn_ldexpf(St[1][e], -F);
         }
+        *reinterpret_cast<h8_t*>(&sS[(w * WAVE + lane) * 8]) = own;
+        if (q4 == 0) sScl[4 * j16 + w] = __builtin_amdgcn_ldexpf(1.f, F);
     };
-    publish();
+    if (holder) publish();
     for (int c = 0; c < nchunks; ++c) {
         const Slot& B = ring[c % RING];
         lds_barrier();  // B1: block c in its slot, S^T published
-        // ---- Y = K^raw S^T and R = V - diag(gamma c) Y for token block tb ----
+        // ---- Y = K S^T and R = V - diag(gamma c 2^E) Y for token block tb ----
         const s4v_t vv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(  // v[token 16tb + 4q + e][row j]
             (lds_s4)(B.vs + (16 * tb + 4 * q4 + (j16 >> 2)) * RS + 4 * (j16 & 3)));
-        const f4_t gck = *reinterpret_cast<const f4_t*>(&B.fac[TpRec::GCK + 16 * tb + 4 * q4]);
-        f4_t y0 = {0.f, 0.f, 0.f, 0.f}, y1 = {0.f, 0.f, 0.f, 0.f};
+        const f4_t gck = *reinterpret_cast<const f4_t*>(&B.fac[TpRec::GCK + 16 * tb + 4 * q4]) *
+                         *reinterpret_cast<const f4_t*>(&B.es[KR::EK + 16 * tb + 4 * q4]);
+        f4_t ya[NKB];
+        const int rot = holder ? w : 0;
 #pragma unroll
-        for (int kr = 0; kr < NKB; ++kr) {  // from this wave's own key block on (its fragments in registers)
-            const int kb = TPW == 2 ? (kr + w) % NKB : kr;
-            const bf8_t ka = raw_rowfrag<D>(B.k, tb, kb, lane);
-            if (TPW == 2 && kr == 0) {
-                mma_bf16(y0, ka, own_hi);
-                mma_bf16(y1, ka, own_lo);
-            } else {
-                mma_bf16(y0, ka, bfrag(sShi, kb, lane));
-                mma_bf16(y1, ka, bfrag(sSlo, kb, lane));
-            }
+        for (int kr = 0; kr < NKB; ++kr) {  // from this wave's own key block on (its fragment in registers)
+            const int kb = (kr + rot) & (NKB - 1);
+            ya[kr] = zero4;
+            const h8_t ka = h16_rowfrag<D>(B.k, tb, kb, lane);
+            if (holder && kr == 0) mma_f16(ya[kr], ka, own);
+            else mma_f16(ya[kr], ka, *reinterpret_cast<const h8_t*>(&sS[(kb * WAVE + lane) * 8]));
         }
         {
-            const f4_t yy = y0 + y1;
+            const f4_t yy = combine(ya, rot);
             f4_t r;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) r[e] = __uint_as_float((uint32_t)(uint16_t)vv[e] << 16) - gck[e] * yy[e];
+            for (int e = 0; e < 4; ++e) r[e] = fmaf(-gck[e], yy[e], __uint_as_float((uint32_t)(uint16_t)vv[e] << 16));
             store_part<_Float16>(sR, kbt, part, lane, r);
         }
         lds_barrier();  // BR: R in LDS; S^T is no longer read
-        const f4_t sc = *reinterpret_cast<const f4_t*>(&B.fac[TpRec::SCK + 16 * tb + 4 * q4]);
+        if (c >= 1) store_out(c - 1, w);
+        const f4_t sc = *reinterpret_cast<const f4_t*>(&B.fac[TpRec::SCK + 16 * tb + 4 * q4]) *
+                        *reinterpret_cast<const f4_t*>(&B.es[KR::EK + 16 * tb + 4 * q4]);
         Frag<_Float16> tf[2];  // (for tb < 2 the second fragment repeats the first and goes unused)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) tf[kb] = frag_stored<_Float16>(B.tp[0], tri_frag(tb, kb), lane);
-        // ---- U = T R and the parts of diag(s c) U ----
+        // ---- U = T R and diag(s c 2^E) U ----
         {
-            f4_t u = {0.f, 0.f, 0.f, 0.f};
+            f4_t u = zero4;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
                 if (kb <= kbt) mma(u, tf[kb], frag_stored<_Float16>(sR, kb, lane));
             store_part<_Float16>(sU, kbt, part, lane, u);
-            store_split(sUh, sUl, kbt, part, lane, u * sc);
+            store_part<_Float16>(sUs, kbt, part, lane, u * sc);
         }
-        bf8_t kt[TPW][2];  // K^raw^T column fragments of this wave's key tiles
+        h8_t kt[2][2];  // K^T column fragments of this holder's key tiles
+        if (holder) {
 #pragma unroll
-        for (int i = 0; i < TPW; ++i)
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) kt[i][kk] = raw_colfrag<D>(B.k, TPW * w + i, kk, lane);
-        lds_barrier();  // BU: U and its parts in LDS
-        // ---- S^T <- gamma_n S^T + K^raw^T diag(s c) U on this wave's tiles ----
-        {
+                for (int kk = 0; kk < 2; ++kk) kt[i][kk] = h16_colfrag<D>(B.k, 2 * w + i, kk, lane);
+        }
+        lds_barrier();  // BU: U and diag(s c 2^E) U in LDS
+        // ---- S^T <- gamma_n S^T + K^T diag(s c 2^E) U on this holder's tiles ----
+        if (holder) {
             const float gn = B.fac[TpRec::GN];
-            bf8_t uh[2], ul[2];
+            h8_t us[2];
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                uh[kk] = bfrag(sUh, kk, lane);
-                ul[kk] = bfrag(sUl, kk, lane);
-            }
+            for (int kk = 0; kk < 2; ++kk) us[kk] = *reinterpret_cast<const h8_t*>(&sUs[(kk * WAVE + lane) * 8]);
 #pragma unroll
-            for (int i = 0; i < TPW; ++i) {
+            for (int i = 0; i < 2; ++i) {
                 St[i] *= gn;
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    mma_bf16(St[i], kt[i][kk], uh[kk]);
-                    mma_bf16(St[i], kt[i][kk], ul[kk]);
-                }
+                for (int kk = 0; kk < 2; ++kk) mma_f16(St[i], kt[i][kk], us[kk]);
             }
             publish();
         }
     }
-    lds_barrier();  // B1 after the last block
-    if (state_out) {
+    lds_barrier();  // B1 after the last block: its outputs are in sO
+    if (nchunks > 0) store_out(nchunks - 1, w);
+    if (holder) {
+        if (state_out) {
 #pragma unroll
-        for (int i = 0; i < TPW; ++i)
-            *reinterpret_cast<float4*>(state_out + sbase + (size_t)srow * D + 16 * (TPW * w + i) + 4 * q4) =
-                make_float4(St[i][0], St[i][1], St[i][2], St[i][3]);
+            for (int i = 0; i < 2; ++i)
+                *reinterpret_cast<float4*>(state_out + sbase + (size_t)srow * D + 32 * w + 16 * i + 4 * q4) =
+                    make_float4(St[i][0], St[i][1], St[i][2], St[i][3]);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) bad |= any_nonfinite(St[i]);
     }
-#pragma unroll
-    for (int i = 0; i < TPW; ++i) bad |= any_nonfinite(St[i]);
     report_status(status, bad, GDN_PREFILL_STATUS_NONFINITE);
 }
 
@@ -1328,11 +1467,12 @@ __global__ __launch_bounds__(TPF_THREADS) void chunk_scan_tpf_kernel(
 int compute_units();
 
 size_t tp_record_bytes() { return TpRec::BYTES; }
+size_t key16_record_bytes(int d) { return d == 128 ? KeyRec16<128>::BYTES : KeyRec16<64>::BYTES; }
 
 template <int D, int NH>
 static hipError_t launch_prep_pair_t(const void* q, const void* k, const float* g, const float* beta,
                                      const void* info, const int32_t* slot_seq, int slots, int T, int h_k, int h_v,
-                                     int l2norm, float scale, char* recs, unsigned* clear_status,
+                                     int l2norm, float scale, char* recs, char* krecs, unsigned* clear_status,
                                      hipStream_t stream) {
     constexpr size_t lds = pair_lds_bytes<D, NH>();
     static_assert(lds <= 160 * 1024, "chunk_prep_pair LDS budget");
@@ -1347,23 +1487,24 @@ static hipError_t launch_prep_pair_t(const void* q, const void* k, const float* 
     const int per = (items + resident - 1) / resident;
     const int grid = (items + per - 1) / per;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(PAIR_THREADS), lds, stream, q, k, g, beta,
-                       reinterpret_cast<const SeqInfo*>(info), slot_seq, T, h_k, h_v, l2norm, scale, recs, slots, per,
-                       clear_status);
+                       reinterpret_cast<const SeqInfo*>(info), slot_seq, T, h_k, h_v, l2norm, scale, recs, krecs, slots,
+                       per, clear_status);
     return hipGetLastError();
 }
 
 hipError_t launch_prep_bf16(int d, const void* q, const void* k, const float* g, const float* beta,
                             const void* info, const int32_t* slot_seq, int slots, int T, int h_k, int h_v,
-                            int l2norm, float scale, void* recs, unsigned* clear_status, hipStream_t stream) {
+                            int l2norm, float scale, void* recs, void* krecs, unsigned* clear_status,
+                            hipStream_t stream) {
     char* r = reinterpret_cast<char*>(recs);
+    char* kr = reinterpret_cast<char*>(krecs);
     unsigned* cs = clear_status;
     const bool pair = (h_v / h_k) % 2 == 0;
-    if (d == 128)
-        return pair ? launch_prep_pair_t<128, 2>(q, k, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, cs, stream)
-                    : launch_prep_pair_t<128, 1>(q, k, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, cs, stream);
-    if (d == 64)
-        return pair ? launch_prep_pair_t<64, 2>(q, k, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, cs, stream)
-                    : launch_prep_pair_t<64, 1>(q, k, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, cs, stream);
+#define GDN_PREP(D, NH) \
+    launch_prep_pair_t<D, NH>(q, k, g, beta, info, slot_seq, slots, T, h_k, h_v, l2norm, scale, r, kr, cs, stream)
+    if (d == 128) return pair ? GDN_PREP(128, 2) : GDN_PREP(128, 1);
+    if (d == 64) return pair ? GDN_PREP(64, 2) : GDN_PREP(64, 1);
+#undef GDN_PREP
     return hipErrorInvalidValue;
 }
 
@@ -1380,25 +1521,27 @@ static hipError_t launch_scan_tp_t(const void* q, const void* k, const void* v, 
 }
 
 template <int D, bool OB>
-static hipError_t launch_scan_tpf_t(const void* q, const void* k, const void* v, const void* recs, const void* info,
+static hipError_t launch_scan_tpf_t(const void* v, const void* recs, const void* krecs, const void* info,
                                     const float* s_in, float* s_out, void* out, void* sink, int units, int T, int h_k,
                                     int h_v, unsigned* status, hipStream_t stream) {
     static_assert(tpf_scan_lds_bytes<D, OB>() <= 160 * 1024, "chunk_scan_tpf LDS budget");
     const int groups = (units + 7) / 8;  // see the XCD placement in chunk_scan_tp_kernel
-    hipLaunchKernelGGL((chunk_scan_tpf_kernel<D, OB>), dim3(groups * 8 * (D / 16)), dim3(TPF_THREADS), 0, stream, q, k,
-                       v, reinterpret_cast<const char*>(recs), reinterpret_cast<const SeqInfo*>(info), s_in, s_out, out,
-                       reinterpret_cast<char*>(sink), units, T, h_k, h_v, status);
+    hipLaunchKernelGGL((chunk_scan_tpf_kernel<D, OB>), dim3(groups * 8 * (D / 16)), dim3(TPF_THREADS), 0, stream, v,
+                       reinterpret_cast<const char*>(recs), reinterpret_cast<const char*>(krecs),
+                       reinterpret_cast<const SeqInfo*>(info), s_in, s_out, out, reinterpret_cast<char*>(sink), units,
+                       T, h_k, h_v, status);
     return hipGetLastError();
 }
 
 hipError_t launch_scan_bf16(int d, bool out_bf16, int rows, int mode, const void* q, const void* k, const void* v,
-                            const void* recs, const void* info, const float* s_in, float* s_out, void* out, void* sink,
+                            const void* recs, const void* krecs, const void* info, const float* s_in, float* s_out, void* out, void* sink,
                             int units, int T, int h_k, int h_v, unsigned* status, hipStream_t stream) {
     // The scan proper on 16-row slices runs on chunk_scan_tpf; chunk_scan_tp takes
     // 32-row slices and the segment maps (MODE 1).
 #define GDN_TPF(D, OB)                                                                                         \
     if (d == D && out_bf16 == OB && rows == 16 && mode == 0)                                                  \
-        return launch_scan_tpf_t<D, OB>(q, k, v, recs, info, s_in, s_out, out, sink, units, T, h_k, h_v, status, stream);
+        return launch_scan_tpf_t<D, OB>(v, recs, krecs, info, s_in, s_out, out, sink, units, T, h_k, h_v, status, \
+                                        stream);
     GDN_TPF(128, true) GDN_TPF(128, false) GDN_TPF(64, true) GDN_TPF(64, false)
 #undef GDN_TPF
 #define GDN_TPS(D, OB, NB, MODE)                                                                              \

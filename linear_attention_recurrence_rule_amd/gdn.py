@@ -175,7 +175,7 @@ def gdn_prefill_ex(desc, q, k, v, g, beta, state_in, out, state_out, cu_seqlens,
                                 _ptr(workspace), int(workspace_bytes), _stream(stream)))
 
 
-GDN_PREFILL_NOALLOC_WORKSPACE_BYTES = 32 << 20
+GDN_PREFILL_NOALLOC_WORKSPACE_BYTES = 64 << 20
 
 
 def gdn_prefill_noalloc(desc, q, k, v, g, beta, state_in, out, state_out, cu_seqlens, chunk, stream=None):

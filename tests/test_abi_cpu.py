@@ -68,15 +68,17 @@ def desc(**kw):
 
 def test_workspace_bytes(L):
     # bf16 inputs, per (block, v-head): the six non-zero 1 KiB fragments of T and
-    # of P (fp16) and 1 KiB of per-token factors; no key records.
-    # 64 blocks x 32 v-heads.
+    # of P (fp16) and 1 KiB of per-token factors; per (block, k-head) a key record:
+    # the scaled fp16 key and query tiles (64 x 128 each) and 1 KiB of factors.
+    # 64 blocks x 32 v-heads / 16 k-heads.
     rec = 2 * 6 * 1024 + 1024
+    key = 2 * 64 * 128 * 2 + 1024
     plan = (1280 + 1 * 16 + 64 * 4 + 255) // 256 * 256  # 1 KiB sink, 256 B status word, then the plan
-    assert gdn.gdn_prefill_workspace_bytes(desc()) == plan + 64 * 32 * rec
+    assert gdn.gdn_prefill_workspace_bytes(desc()) == plan + 64 * (32 * rec + 16 * key)
     # packed sequences: at most T/64 + N blocks in total
     n = gdn.gdn_prefill_workspace_bytes(desc(num_seqs=16, total_tokens=1000))
     slots = (1000 + 16 * 63) // 64
-    assert n == (1280 + 16 * 16 + slots * 4 + 255) // 256 * 256 + slots * 32 * rec
+    assert n == (1280 + 16 * 16 + slots * 4 + 255) // 256 * 256 + slots * (32 * rec + 16 * key)
     # fp32 inputs keep fp32 operands
     rec64f = 4 * 64 * 64 * 4 + 512
     key64f = 64 * 64 * 4
@@ -262,7 +264,8 @@ def test_two_level_workspace_bytes(L):
     # 64 blocks in 8 segments of 8: single-sequence records, a 256-byte segment table, then
     # R and B for 7 segments and start and end states for 8 (32 v-heads, d = 128, fp32)
     rec = 2 * 6 * 1024 + 1024
-    base = 1280 + 64 * 32 * rec
+    key = 2 * 64 * 128 * 2 + 1024
+    base = 1280 + 64 * (32 * rec + 16 * key)
     st = 32 * 128 * 128 * 4
     assert gdn.gdn_prefill_two_level_workspace_bytes(desc(total_tokens=4096), 8) == base + 256 + (7 + 7 + 8 + 8) * st
     # more segments than blocks: one segment per block
