@@ -55,8 +55,8 @@ __device__ __forceinline__ int tri_frag(int mb, int kb) { return mb < 2 ? mb : 2
 // factors 2^E per token (keys, then queries).  The keys keep the swizzled row
 // layout of the raw tiles (raw_unit): the scan reads them as rows and as
 // columns from LDS.  The queries are stored as the A fragments of their 16-token
-// blocks (fragment tb * (D / 32) + kb, 64 lanes x 16 bytes, the order of
-// raw_rowfrag), which the scan loads straight into registers.  Both v-heads of
+// blocks (fragment tb * (D / 32) + kb, 64 lanes x 16 bytes, the permuted key order
+// of h16_row8), which the scan loads straight into registers.  Both v-heads of
 // a k-head read the same record.
 template <int D>
 struct KeyRec16 {
@@ -120,14 +120,32 @@ __device__ __forceinline__ void mma_bf16(f4_t& acc, const bf8_t& a, const bf8_t&
 __device__ __forceinline__ void mma_f16(f4_t& acc, const h8_t& a, const h8_t& b) {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
 }
-// The row and column fragments above, of a tile of fp16 elements in the same layout.
+// Fragments of an fp16 tile in the swizzled row layout, for products with S^T
+// fragments built from accumulator tiles.  Key index x of such a product (x the
+// position in the accumulator order: 32 kb + 4 q + e for e < 4, 32 kb + 16 + 4 q + e - 4
+// for e >= 4) stands for the key 32 kb + 8 q + e, a permutation inside each block of
+// 32 keys.  The state's tiles hold the keys in that order, so a row fragment is 16
+// contiguous bytes (raw_row8), and a column fragment of tile m holds, for lane i, the
+// column 32 (m / 2) + 8 (i / 4) + 4 (m mod 2) + (i mod 4).
 template <int D>
-__device__ __forceinline__ h8_t h16_rowfrag(const _Float16* M, int rb, int kb, int lane) {
-    return __builtin_bit_cast(h8_t, raw_rowfrag<D>(reinterpret_cast<const uint16_t*>(M), rb, kb, lane));
+__device__ __forceinline__ h8_t h16_row8(const _Float16* M, int rb, int kb, int lane) {
+    return __builtin_bit_cast(h8_t, raw_row8<D>(reinterpret_cast<const uint16_t*>(M), rb, kb, lane));
 }
+// Column fragment (A of the update: rows = the keys of tile m, contraction = the tokens
+// of the 32-token block kb): two transposing reads (ds_read_b64_tr_b16) of the swizzled
+// rows.  Lane s of group q addresses token row 32 kb + 4 q + (s >> 2) at the four
+// columns of column group s & 3; lane i then receives its column's four rows.
 template <int D>
-__device__ __forceinline__ h8_t h16_colfrag(const _Float16* M, int cb, int kb, int lane) {
-    return __builtin_bit_cast(h8_t, raw_colfrag<D>(reinterpret_cast<const uint16_t*>(M), cb, kb, lane));
+__device__ __forceinline__ h8_t h16_colfrag_p(const _Float16* M, int m, int kb, int lane) {
+    typedef __attribute__((address_space(3))) s4v_t* lds_s4;
+    const int s = lane & 15, q = lane >> 4;
+    const int r = 32 * kb + 4 * q + (s >> 2), col = 32 * (m >> 1) + 8 * (s & 3) + 4 * (m & 1);
+    const char* base = reinterpret_cast<const char*>(M);
+    const int o0 = raw_unit<D>(r, col >> 3) + ((col & 7) << 1);
+    const int o1 = raw_unit<D>(r + 16, col >> 3) + ((col & 7) << 1);
+    const s4v_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(base + o0));
+    const s4v_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(base + o1));
+    return __builtin_bit_cast(h8_t, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 __device__ __forceinline__ float bf16_lo_bits(uint32_t w) { return __uint_as_float(w << 16); }
@@ -428,14 +446,11 @@ __global__ __launch_bounds__(PAIR_THREADS, 1) void chunk_prep_pair_kernel(
                     if (op == 0) {
                         *reinterpret_cast<h8_t*>(kr + KeyRec16<D>::K + raw_unit<D>(r, u)) = hx;
                     } else {
-                        // queries in A-fragment order: columns 32 kb + o .. + 7 (o = 8 (u mod 4)) of row
-                        // 16 tb + i are elements 4 h .. 4 h + 3 (h = o / 16) of lanes i + 16 qq and
-                        // i + 16 (qq + 1), qq = (o mod 16) / 4, in fragment tb * (D / 32) + kb
-                        const int o = 8 * (u & 3), hh = o >> 4, qq = (o & 15) >> 2;
-                        char* fb = kr + KeyRec16<D>::Q + (size_t)(((r >> 4) * (D / 32) + (u >> 2)) * WAVE) * 16 + 8 * hh;
-                        const uint4 bits = __builtin_bit_cast(uint4, hx);
-                        *reinterpret_cast<uint2*>(fb + ((r & 15) + 16 * qq) * 16) = uint2{bits.x, bits.y};
-                        *reinterpret_cast<uint2*>(fb + ((r & 15) + 16 * (qq + 1)) * 16) = uint2{bits.z, bits.w};
+                        // queries as A fragments in the permuted key order (h16_row8): unit u of
+                        // row 16 tb + i is lane i + 16 (u mod 4) of fragment tb * (D / 32) + u / 4
+                        *reinterpret_cast<h8_t*>(kr + KeyRec16<D>::Q +
+                                                 ((size_t)(((r >> 4) * (D / 32) + (u >> 2)) * WAVE) + (r & 15) +
+                                                  16 * (u & 3)) * 16) = hx;
                     }
                     if (u == 0)
                         reinterpret_cast<float*>(kr + KeyRec16<D>::E)[(op ? KeyRec16<D>::EQ : KeyRec16<D>::EK) + r] =
@@ -1243,20 +1258,21 @@ __global__ __launch_bounds__(TPF_THREADS) void chunk_scan_tpf_kernel(
     bool bad = false;  // a non-finite output or final state in this lane
     typedef __attribute__((address_space(3))) s4v_t* lds_s4;
     const f4_t zero4 = {0.f, 0.f, 0.f, 0.f};
-    // Sum over the key blocks of a product with S^T: acc[i] (key block (i + rot) mod
-    // NKB) times 2^F of that block and column j16.  The accumulators are indexed by
-    // loop position only (a runtime index into a register array would compile to
-    // indexed register moves); the rotation goes into the LDS address.
-    auto combine = [&](const f4_t (&acc)[NKB], int rot) __attribute__((always_inline)) {
-        f4_t s = acc[0] * sScl[4 * j16 + rot];
+    // Sum over the key blocks of a product with S^T: acc[i] times scl[i], the factor
+    // 2^F of acc[i]'s key block and column j16.  Arrays are indexed by loop position
+    // only (a runtime index into a register array would compile to indexed register
+    // moves); a rotation of the key blocks goes into the LDS addresses of the reads.
+    auto combine = [&](const f4_t (&acc)[NKB], const float (&scl)[NKB]) __attribute__((always_inline)) {
+        f4_t s = acc[0] * scl[0];
 #pragma unroll
-        for (int i = 1; i < NKB; ++i) {
-            const float f = sScl[4 * j16 + ((i + rot) & (NKB - 1))];
+        for (int i = 1; i < NKB; ++i)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) s[e] = fmaf(acc[i][e], f, s[e]);
-        }
+            for (int e = 0; e < 4; ++e) s[e] = fmaf(acc[i][e], scl[i], s[e]);
         return s;
     };
+    // Each phase first issues the LDS reads that its products need, then a scheduling
+    // barrier: left alone the compiler puts every read just before its use and waits
+    // for it there, one read latency per product.
     constexpr int LPR = RS * OB / 16;  // 16-byte pieces per output row
     constexpr int PIECES = CHUNK * LPR;
     // Block c's outputs, sO to HBM, by the Y-waves (they issue no loads, so no load
@@ -1289,13 +1305,21 @@ __global__ __launch_bounds__(TPF_THREADS) void chunk_scan_tpf_kernel(
             const Slot& B = ring[c % RING];
             lds_barrier();  // B1: block c in its slot, S^T published
             // ---- Z = Q S^T for token block tb, one accumulator per key block ----
+            h8_t sf[NKB];
+            float scl[NKB];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                sf[kb] = *reinterpret_cast<const h8_t*>(&sS[(kb * WAVE + lane) * 8]);
+                scl[kb] = sScl[4 * j16 + kb];
+            }
+            __builtin_amdgcn_sched_barrier(0);
             f4_t za[NKB];
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
                 za[kb] = zero4;
-                mma_f16(za[kb], qs[kb], *reinterpret_cast<const h8_t*>(&sS[(kb * WAVE + lane) * 8]));
+                mma_f16(za[kb], qs[kb], sf[kb]);
             }
-            f4_t z = combine(za, 0);
+            f4_t z = combine(za, scl);
             // Z is complete in this phase: keeps the compiler from sinking its products
             // into phase BU, where they would contend with the Y-wave's update on this SIMD.
             asm volatile("" : "+v"(z));
@@ -1350,7 +1374,7 @@ __global__ __launch_bounds__(TPF_THREADS) void chunk_scan_tpf_kernel(
     if (holder) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const int col = 32 * w + 16 * i + 4 * q4;
+            const int col = 32 * w + 8 * q4 + 4 * i;  // the permuted key order (h16_row8)
             if (state_in) {
                 const float4 x = *reinterpret_cast<const float4*>(state_in + sbase + (size_t)srow * D + col);
                 St[i] = f4_t{x.x, x.y, x.z, x.w};
@@ -1390,46 +1414,58 @@ __global__ __launch_bounds__(TPF_THREADS) void chunk_scan_tpf_kernel(
             (lds_s4)(B.vs + (16 * tb + 4 * q4 + (j16 >> 2)) * RS + 4 * (j16 & 3)));
         const f4_t gck = *reinterpret_cast<const f4_t*>(&B.fac[TpRec::GCK + 16 * tb + 4 * q4]) *
                          *reinterpret_cast<const f4_t*>(&B.es[KR::EK + 16 * tb + 4 * q4]);
-        f4_t ya[NKB];
+        // key blocks from this wave's own on (its fragment is in registers)
         const int rot = holder ? w : 0;
+        h8_t ka[NKB], sf[NKB];
+        float scl[NKB];
 #pragma unroll
-        for (int kr = 0; kr < NKB; ++kr) {  // from this wave's own key block on (its fragment in registers)
+        for (int kr = 0; kr < NKB; ++kr) {
             const int kb = (kr + rot) & (NKB - 1);
+            ka[kr] = h16_row8<D>(B.k, tb, kb, lane);
+            sf[kr] = (holder && kr == 0) ? own : *reinterpret_cast<const h8_t*>(&sS[(kb * WAVE + lane) * 8]);
+            scl[kr] = sScl[4 * j16 + kb];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        f4_t ya[NKB];
+#pragma unroll
+        for (int kr = 0; kr < NKB; ++kr) {
             ya[kr] = zero4;
-            const h8_t ka = h16_rowfrag<D>(B.k, tb, kb, lane);
-            if (holder && kr == 0) mma_f16(ya[kr], ka, own);
-            else mma_f16(ya[kr], ka, *reinterpret_cast<const h8_t*>(&sS[(kb * WAVE + lane) * 8]));
+            mma_f16(ya[kr], ka[kr], sf[kr]);
         }
         {
-            const f4_t yy = combine(ya, rot);
+            const f4_t yy = combine(ya, scl);
             f4_t r;
 #pragma unroll
             for (int e = 0; e < 4; ++e) r[e] = fmaf(-gck[e], yy[e], __uint_as_float((uint32_t)(uint16_t)vv[e] << 16));
             store_part<_Float16>(sR, kbt, part, lane, r);
         }
         lds_barrier();  // BR: R in LDS; S^T is no longer read
-        if (c >= 1) store_out(c - 1, w);
         const f4_t sc = *reinterpret_cast<const f4_t*>(&B.fac[TpRec::SCK + 16 * tb + 4 * q4]) *
                         *reinterpret_cast<const f4_t*>(&B.es[KR::EK + 16 * tb + 4 * q4]);
-        Frag<_Float16> tf[2];  // (for tb < 2 the second fragment repeats the first and goes unused)
+        Frag<_Float16> tf[2], rr[2];  // (for tb < 2 the second fragments go unused)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) tf[kb] = frag_stored<_Float16>(B.tp[0], tri_frag(tb, kb), lane);
-        // ---- U = T R and diag(s c 2^E) U ----
-        {
-            f4_t u = zero4;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-                if (kb <= kbt) mma(u, tf[kb], frag_stored<_Float16>(sR, kb, lane));
-            store_part<_Float16>(sU, kbt, part, lane, u);
-            store_part<_Float16>(sUs, kbt, part, lane, u * sc);
+        for (int kb = 0; kb < 2; ++kb) {
+            tf[kb] = frag_stored<_Float16>(B.tp[0], tri_frag(tb, kb), lane);
+            rr[kb] = frag_stored<_Float16>(sR, kb, lane);
         }
         h8_t kt[2][2];  // K^T column fragments of this holder's key tiles
         if (holder) {
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk) kt[i][kk] = h16_colfrag<D>(B.k, 2 * w + i, kk, lane);
+                for (int kk = 0; kk < 2; ++kk) kt[i][kk] = h16_colfrag_p<D>(B.k, 2 * w + i, kk, lane);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        // ---- U = T R and diag(s c 2^E) U ----
+        {
+            f4_t u = zero4;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                if (kb <= kbt) mma(u, tf[kb], rr[kb]);
+            store_part<_Float16>(sU, kbt, part, lane, u);
+            store_part<_Float16>(sUs, kbt, part, lane, u * sc);
+        }
+        if (c >= 1) store_out(c - 1, w);
         lds_barrier();  // BU: U and diag(s c 2^E) U in LDS
         // ---- S^T <- gamma_n S^T + K^T diag(s c 2^E) U on this holder's tiles ----
         if (holder) {
@@ -1452,7 +1488,7 @@ __global__ __launch_bounds__(TPF_THREADS) void chunk_scan_tpf_kernel(
         if (state_out) {
 #pragma unroll
             for (int i = 0; i < 2; ++i)
-                *reinterpret_cast<float4*>(state_out + sbase + (size_t)srow * D + 32 * w + 16 * i + 4 * q4) =
+                *reinterpret_cast<float4*>(state_out + sbase + (size_t)srow * D + 32 * w + 8 * q4 + 4 * i) =
                     make_float4(St[i][0], St[i][1], St[i][2], St[i][3]);
         }
 #pragma unroll
