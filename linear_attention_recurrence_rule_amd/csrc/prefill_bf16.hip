@@ -52,12 +52,12 @@ __device__ __forceinline__ int tri_frag(int mb, int kb) { return mb < 2 ? mb : 2
 // The block's keys and queries as fp16, each token's row scaled by 2^-E with E
 // the exponent of the row's largest magnitude (so every element is below 1 and
 // the conversion from bf16 is exact down to 2^-14 of that magnitude), then the
-// factors 2^E per token (keys, then queries).  The keys keep the swizzled row
-// layout of the raw tiles (raw_unit): the scan reads them as rows and as
-// columns from LDS.  The queries are stored as the A fragments of their 16-token
-// blocks (fragment tb * (D / 32) + kb, 64 lanes x 16 bytes, the permuted key order
-// of h16_row8), which the scan loads straight into registers.  Both v-heads of
-// a k-head read the same record.
+// factors 2^E per token (keys, then queries).  The keys are rows in a swizzled
+// layout (key_unit): the scan reads them as rows and as columns from LDS.  The
+// queries are stored as the A fragments of their 16-token blocks (fragment
+// tb * (D / 32) + kb, 64 lanes x 16 bytes, the permuted key order of h16_row8),
+// which the scan loads straight into registers.  Both v-heads of a k-head read
+// the same record.
 template <int D>
 struct KeyRec16 {
     static constexpr size_t K = 0;
@@ -127,9 +127,21 @@ __device__ __forceinline__ void mma_f16(f4_t& acc, const h8_t& a, const h8_t& b)
 // 32 keys.  The state's tiles hold the keys in that order, so a row fragment is 16
 // contiguous bytes (raw_row8), and a column fragment of tile m holds, for lane i, the
 // column 32 (m / 2) + 8 (i / 4) + 4 (m mod 2) + (i mod 4).
+//
+// The key tile of the key record (and of the scan's LDS) has a swizzle of its own:
+// the 16-byte units of row r are XOR-permuted by ((r mod 4) << 2) | ((r / 4) mod 4).
+// A row fragment reads one unit of 16 consecutive rows and a column fragment four
+// units of 4 consecutive rows; both land on 16 distinct units (with the row-only
+// permutation of raw_unit the column reads met only 4).
+template <int D>
+__device__ __forceinline__ int key_unit(int r, int u) {
+    constexpr int UPR = D / 8;
+    return r * (D * 2) + ((u ^ ((((r & 3) << 2) | ((r >> 2) & 3)) & (UPR - 1))) << 4);
+}
 template <int D>
 __device__ __forceinline__ h8_t h16_row8(const _Float16* M, int rb, int kb, int lane) {
-    return __builtin_bit_cast(h8_t, raw_row8<D>(reinterpret_cast<const uint16_t*>(M), rb, kb, lane));
+    const int r = 16 * rb + (lane & 15), u = 4 * kb + (lane >> 4);
+    return *reinterpret_cast<const h8_t*>(reinterpret_cast<const char*>(M) + key_unit<D>(r, u));
 }
 // Column fragment (A of the update: rows = the keys of tile m, contraction = the tokens
 // of the 32-token block kb): two transposing reads (ds_read_b64_tr_b16) of the swizzled
@@ -141,8 +153,8 @@ __device__ __forceinline__ h8_t h16_colfrag_p(const _Float16* M, int m, int kb, 
     const int s = lane & 15, q = lane >> 4;
     const int r = 32 * kb + 4 * q + (s >> 2), col = 32 * (m >> 1) + 8 * (s & 3) + 4 * (m & 1);
     const char* base = reinterpret_cast<const char*>(M);
-    const int o0 = raw_unit<D>(r, col >> 3) + ((col & 7) << 1);
-    const int o1 = raw_unit<D>(r + 16, col >> 3) + ((col & 7) << 1);
+    const int o0 = key_unit<D>(r, col >> 3) + ((col & 7) << 1);
+    const int o1 = key_unit<D>(r + 16, col >> 3) + ((col & 7) << 1);
     const s4v_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(base + o0));
     const s4v_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(base + o1));
     return __builtin_bit_cast(h8_t, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -444,7 +456,7 @@ __global__ __launch_bounds__(PAIR_THREADS, 1) void chunk_prep_pair_kernel(
 #pragma unroll
                     for (int e = 0; e < 8; ++e) hx[e] = (_Float16)__builtin_amdgcn_ldexpf(x[e], -E);
                     if (op == 0) {
-                        *reinterpret_cast<h8_t*>(kr + KeyRec16<D>::K + raw_unit<D>(r, u)) = hx;
+                        *reinterpret_cast<h8_t*>(kr + KeyRec16<D>::K + key_unit<D>(r, u)) = hx;
                     } else {
                         // queries as A fragments in the permuted key order (h16_row8): unit u of
                         // row 16 tb + i is lane i + 16 (u mod 4) of fragment tb * (D / 32) + u / 4
