@@ -421,13 +421,13 @@ gdn_status gdn_prefill_direct_ex(const gdn_desc *desc,
  * gdn_prefill for callers that cannot allocate device memory: code under HIP
  * graph capture, tight serving loops, and harnesses that forbid hipMalloc.
  * The workspace is the library's own: a static device array of
- * GDN_PREFILL_NOALLOC_WORKSPACE_BYTES (32 MiB) on each GPU it runs on, held
+ * GDN_PREFILL_NOALLOC_WORKSPACE_BYTES (64 MiB) on each GPU it runs on, held
  * until the process ends.  The call allocates nothing.  Its first call on a
  * device looks up that device's copy of the array (no allocation either).
  *
  * Problems whose gdn_prefill_workspace_bytes() exceeds the array are
  * rejected with GDN_ERR_WORKSPACE before anything is enqueued (at 32 v-heads
- * and d = 128 the array holds about 4900 tokens).  All calls on one GPU share
+ * and d = 128 the array holds about 4400 tokens).  All calls on one GPU share
  * the array, so calls that overlap on one GPU (on different streams, or
  * from different host threads without ordering) race; serialise them.  The
  * contents left by an earlier call do not matter.  The status word of the
