@@ -113,6 +113,36 @@ def test_extreme_qk_magnitudes(qk_scale):
     assert eo <= 2e-3 and es <= 2e-3
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_scaled_fp16_operands_over_wide_ranges(d):
+    """The bf16 path rounds its matrix-core operands to fp16 after scaling by powers of
+    two: keys and queries per token, the state per 32-key block and state row.  Here
+    every token's k and q carry their own factor 2^c, c in [-30, 30] (exact in bf16), and
+    the initial state's rows and 32-key blocks their own factors 2^a * 2^b, a in
+    [-24, 8], b in [-24, 0], with slow gates so that the initial state persists.  Each
+    state row is compared with the oracle relative to that row's largest magnitude,
+    and each output column (state row) relative to its own largest magnitude."""
+    T = 320
+    x = inputs.prefill_inputs(seed=41 + d, lengths=[T - 97, 97], h_k=2, h_v=4, d=d, io_dtype=inputs.BF16,
+                              state_std=1.0, gate_mean=-7.0)
+    rng = np.random.default_rng(42)
+    for n in ("q", "k"):
+        f = (2.0 ** rng.integers(-30, 31, size=(T, 2, 1))).astype(np.float32)
+        x[n] = inputs.f32_to_bf16_bits(inputs.bf16_bits_to_f32(x[n]) * f)
+    N = 2
+    rows = 2.0 ** rng.integers(-24, 9, size=(N, 4, d, 1))
+    blocks = np.repeat(2.0 ** rng.integers(-24, 1, size=(N, 4, 1, d // 32)), 32, axis=3)
+    x["state_in"] = (x["state_in"] * rows * blocks).astype(np.float32)
+    out, st = run_gpu(x, inputs.F32)
+    ro, rs = run_oracle(x)
+    o, s = host(out), host(st)
+    assert np.isfinite(o).all() and np.isfinite(s).all()
+    err_rows = np.abs(s - rs).max(axis=3) / np.abs(rs).max(axis=3)       # [N, h_v, d_v]
+    err_cols = np.abs(o - ro).max(axis=0) / np.abs(ro).max(axis=0)       # [h_v, d_v]
+    print("wide ranges d=%d: worst state row %.3g, worst output column %.3g" % (d, err_rows.max(), err_cols.max()))
+    assert err_rows.max() <= 2e-3 and err_cols.max() <= 2e-3
+
+
 @pytest.mark.parametrize("d,h_k,h_v", [(128, 2, 2), (64, 2, 2), (128, 1, 3), (64, 3, 3)])
 def test_odd_head_ratios_bf16(d, h_k, h_v):
     """v-heads per k-head of 1 and 3: the bf16 prepare kernel then takes one v-head per
