@@ -1404,10 +1404,13 @@ __global__ __launch_bounds__(TPF_THREADS) void chunk_scan_tpf_kernel(
         for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fabsf(St[i][e]));
+        // (magnitudes: their bit patterns order as unsigned integers, and an integer
+        // maximum needs no canonicalising of its inputs)
+        auto umax = [](float a, float b) { return __uint_as_float(max(__float_as_uint(a), __float_as_uint(b))); };
         F2 t = permlane16_swap(mx, mx);
-        mx = fmaxf(t.x, t.y);
+        mx = umax(t.x, t.y);
         t = permlane32_swap(mx, mx);
-        mx = fmaxf(t.x, t.y);
+        mx = umax(t.x, t.y);
         const int F = __builtin_amdgcn_frexp_expf(mx);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
