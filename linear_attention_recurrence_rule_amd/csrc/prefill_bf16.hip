@@ -336,8 +336,10 @@ __global__ __launch_bounds__(PAIR_THREADS, 1) void chunk_prep_pair_kernel(
 
         // ---- P2a ------------------------------------------------------------------------------
         // The 16 off-diagonal tiles u (u < 6 the K K^T block of slot u, u >= 6 the Q K^T tile
-        // u - 6) go to waves 0..5: two each to waves 0..3, four each to waves 4, 5.
-        const int u0 = wave < 4 ? 2 * wave : 8 + 4 * (wave - 4), nt = wave < 4 ? 2 : wave < 6 ? 4 : 0;
+        // u - 6) go to waves 0..5: three each to waves 0, 1, 4 and 5, two each to waves 2, 3
+        // (waves 4 and 5, whose tiles' P halves go to the records in P2b, bound that phase).
+        const int u0 = wave < 2 ? 3 * wave : wave < 4 ? 6 + 2 * (wave - 2) : 10 + 3 * (wave - 4);
+        const int nt = wave < 2 ? 3 : wave < 4 ? 2 : wave < 6 ? 3 : 0;
         f4_t acc[4];
         if (live) {
             if (wave < 4) {
