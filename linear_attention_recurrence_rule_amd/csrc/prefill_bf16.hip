@@ -1122,21 +1122,23 @@ __global__ __launch_bounds__(TPS_MAX_THREADS) void chunk_scan_tp_kernel(
 // The roles are arranged so that no partial product crosses waves; per-wave LDS
 // reads are the scarce resource, so the work of token block tb is split over
 // two waves:
-//   Y-wave tb (w = tb):     Y and R, U = T R and diag(s c 2^E) U; the Y-waves
-//                           w < D / 32 also hold the fp32 S^T tiles of key block
-//                           w and update and publish them;
-//   Z-wave tb (w = 4 + tb): Z = Q S^T and O = diag(gamma c_q 2^E) Z + P U, and
-//                           the output stores;
-//   copier waves (w = 8..11) stream the inputs as in chunk_scan_tp.
+//   Y-wave tb (w = tb):     Y and R, U = T R and diag(s c 2^E) U, and the output
+//                           stores; the Y-waves w < D / 32 also hold the fp32 S^T
+//                           tiles of key block w and update and publish them;
+//   Z-wave tb (w = 4 + tb): Z = Q S^T (the query fragments loaded straight into
+//                           registers) and O = diag(gamma c_q 2^E) Z + P U;
+//   copier waves (w = 8..11) stream the keys, v, T, P and the factors into LDS.
 // Three barriers per block:
 //   B1  block c in its slot, S^T published  -> Y-waves: Y, R;  Z-waves: Z
-//   BR  R in LDS                            -> Y-waves: U, diag(s c 2^E) U;  Z-waves: block c - 1's outputs to HBM
+//   BR  R in LDS                            -> Y-waves: U, diag(s c 2^E) U, block c - 1's outputs to HBM;
+//                                              Z-waves: the queries of block c + 2
 //   BU  U and diag(s c 2^E) U in LDS        -> Y-waves: S^T update, published;  Z-waves: O, to LDS
 // Reads that phase B1 does not need (T, P and their factors) wait until after BR:
 // phase B1 is the one bound by the workgroup's LDS read bandwidth, and for the same
 // reason a Y-wave takes its own key block of S^T from registers.
-// The Y- and Z-waves issue no global loads inside the block loop, so the
-// Z-waves' stores never hold up a load wait.
+// Inside the block loop the Y-waves store but never load and the Z-waves load but
+// never store: a wave's memory counter covers both, so a Z-wave's wait for its
+// queries never waits for output stores.
 
 constexpr int TPF_YW = 4, TPF_ZW = 4, TPF_LOAD = 4;
 constexpr int TPF_COMPUTE = TPF_YW + TPF_ZW;
