@@ -14,16 +14,22 @@
 //   U = T (V - diag(gamma c) K^raw S^T),  gamma = exp(G),
 //   O = diag(gamma c^q) Q^raw S^T + P U,
 //   S' = exp(G_n) S + U^T diag(exp(G_n - G) c) K^raw.
-// Two kernels:
+// Kernels:
 //   chunk_prep_pair (parallel over blocks x k-heads): T, P and the per-token
-//     factors of each (block, v-head), about 13 KiB per record;
-//   chunk_scan_tp (sequential over the blocks of a sequence, parallel over
-//     sequences x v-heads x row slices of S): reads each block's raw q, k, v
-//     tiles and its record, keeps S in registers and writes it once.
-// The state-side products (K^raw S^T, Q^raw S^T and the update) run on bf16
-// matrix cores with the exact bf16 inputs and S (and diag(s) U) split into a
-// bf16 high and low part, about 16 significant bits.  T, P, V - ..., U enter
-// the two token-contractions U = T R and P U as fp16.
+//     factors of each (block, v-head), about 13 KiB per record, and a key
+//     record per (block, k-head): the keys and queries as fp16, each token's
+//     row scaled by a power of two;
+//   chunk_scan_tpf (sequential over the blocks of a sequence, parallel over
+//     sequences x v-heads x 16-row slices of S): reads each block's key
+//     record, v slice and record, keeps S in registers in fp32 and writes it
+//     once.  Its state-side products (K S^T, Q S^T and the update) run on
+//     fp16 matrix cores, S^T's operand copy scaled per key block and row by a
+//     power of two;
+//   chunk_scan_tp (32-row slices, and the segment maps of the two-level scan):
+//     the same recurrence from the raw bf16 q and k tiles, with S (and
+//     diag(s) U) split into a bf16 high and low part, about 16 significant bits.
+// In both scans T, P, R = V - ... and U enter the token contractions U = T R
+// and P U as fp16.
 #include "prefill_shared.h"
 
 namespace gdn {
