@@ -683,12 +683,6 @@ struct TpShape {
     static constexpr int L = N / TpsRoles<D, NB>::LOAD;    // per copier wave
     static_assert(N % TpsRoles<D, NB>::LOAD == 0, "copy split");
     static constexpr int NKB = D / 32;                     // 32-wide key blocks
-    // With one row block the raw q tile also goes through LDS (a ring of two),
-    // copied like k in whole rows; with two there is no room, and the token
-    // waves load their q rows straight into registers.
-    static constexpr bool QDMA = NB == 1;
-    static constexpr int LQ = QDMA ? NK / TpsRoles<D, NB>::LOAD : 0;  // q loads per copier wave
-    static_assert(NK % TpsRoles<D, NB>::LOAD == 0, "q copy split");
 };
 
 // B fragment from two accumulator tiles stacked along the contraction (as
@@ -739,8 +733,7 @@ constexpr size_t tp_scan_lds_bytes(bool out_bf16) {
            + 2 * (D / 32) * NB * WAVE * 8 * 2            // S^T high / low
            + TpsXchg<D, NB>::BYTES                       // partial Y, or U and its parts
            + NB * 2 * WAVE * 8 * 2                       // R
-           + (size_t)CHUNK * 16 * NB * (out_bf16 ? 2 : 4)   // outputs
-           + (TpShape<D, NB>::QDMA ? 2 * CHUNK * D * 2 : 0);  // q ring
+           + (size_t)CHUNK * 16 * NB * (out_bf16 ? 2 : 4);  // outputs
 }
 
 // MODE 0: the scan.  MODE 1: both parts of a segment's state map, no outputs:
@@ -768,7 +761,6 @@ __global__ __launch_bounds__(TPS_MAX_THREADS) void chunk_scan_tp_kernel(
     uint16_t* sUl = sUh + NB * 2 * WAVE * 8;
     __shared__ __align__(16) _Float16 sR[NB * 2 * WAVE * 8];     // R as fp16 B fragments (kb, row block)
     __shared__ __align__(16) char sO[CHUNK * RS * OB];           // one block's 64 x RS outputs, row-major
-    __shared__ __align__(16) uint16_t sQ[Sh::QDMA ? 2 : 1][Sh::QDMA ? CHUNK * D : 8];  // raw q ring (swizzled rows)
     // Workgroups are dispatched round-robin over the 8 XCDs (blockIdx % 8).
     // The SLICES workgroups of one (sequence, v-head) unit are placed on the
     // same XCD, so they share each block's inputs through that XCD's L2.
@@ -817,10 +809,6 @@ __global__ __launch_bounds__(TPS_MAX_THREADS) void chunk_scan_tp_kernel(
             const uint16_t* src = reinterpret_cast<const uint16_t*>(base) + (tt * h_k + hk) * D + 8 * u;
             __builtin_amdgcn_global_load_lds(src, (lds_ptr)(dst + i * 512), 16, 0, 0);
         };
-        auto copy_q = [&](int c) __attribute__((always_inline)) {
-#pragma unroll
-            for (int mm = 0; mm < Sh::LQ; ++mm) tile_load(q, begin + c * CHUNK, sQ[c & 1], Ro::LOAD * mm + lw);
-        };
         auto load = [&](int c, int mm) __attribute__((always_inline)) {
             Slot* sl = &ring[c % RING];
             const int tok0 = begin + c * CHUNK;
@@ -848,16 +836,10 @@ __global__ __launch_bounds__(TPS_MAX_THREADS) void chunk_scan_tp_kernel(
 #pragma unroll
             for (int mm = 0; mm < Sh::L; ++mm) load(c, mm);
         };
-        constexpr int LB = Sh::L + Sh::LQ;  // loads per copier wave and block
-        if (nchunks > 0) {
-            copy(0);
-            if (MODE == 0) copy_q(0);
-        }
+        if (nchunks > 0) copy(0);
         if (nchunks > 1) {
             copy(1);
-            if (MODE == 0) copy_q(1);
-            if (MODE == 0) wait_vmcnt<LB>();
-            else wait_vmcnt<Sh::L>();
+            wait_vmcnt<Sh::L>();
         } else {
             wait_vmcnt<0>();
         }
@@ -873,8 +855,7 @@ __global__ __launch_bounds__(TPS_MAX_THREADS) void chunk_scan_tp_kernel(
                 else wait_vmcnt<0>();
             }
             lds_barrier();  // BR: block c + 1 has landed
-            lds_barrier();  // BU: block c's q is no longer read
-            if (MODE == 0 && c + 2 < nchunks) copy_q(c + 2);
+            lds_barrier();  // BU
         }
         lds_barrier();  // B1 after the last block
         lds_barrier();  // BF
@@ -939,10 +920,6 @@ __global__ __launch_bounds__(TPS_MAX_THREADS) void chunk_scan_tp_kernel(
                 if (MODE == 0) pf[kb] = frag_stored<_Float16>(B.tp[1], tri_frag(tb, kb), lane);
             }
             if (MODE == 0) {
-                if constexpr (Sh::QDMA) {
-#pragma unroll
-                    for (int kb = 0; kb < NKB; ++kb) cur[kb] = raw_rowfrag<D>(sQ[c & 1], tb, kb, lane);
-                }
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {  // Z = Q^raw S^T, high and low parts into one accumulator
                     f4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -997,11 +974,11 @@ __global__ __launch_bounds__(TPS_MAX_THREADS) void chunk_scan_tp_kernel(
                         else reinterpret_cast<float*>(sO)[e] = o[r];
                     }
                 }
-                if (!Sh::QDMA && c + 2 < nchunks) load_q(c + 2, cur);
+                if (c + 2 < nchunks) load_q(c + 2, cur);
             }
         };
-        if (!Sh::QDMA && MODE == 0 && nchunks > 0) load_q(0, qa[0]);
-        if (!Sh::QDMA && MODE == 0 && nchunks > 1) load_q(1, qa[1]);
+        if (MODE == 0 && nchunks > 0) load_q(0, qa[0]);
+        if (MODE == 0 && nchunks > 1) load_q(1, qa[1]);
         for (int c = 0; c < nchunks; c += 2) {
             step(c, qa[0]);
             if (c + 1 < nchunks) step(c + 1, qa[1]);
