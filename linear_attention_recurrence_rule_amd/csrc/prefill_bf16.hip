@@ -250,8 +250,11 @@ __global__ __launch_bounds__(PAIR_THREADS, 1) void chunk_prep_pair_kernel(
 
     if (wave >= PAIR_COMPUTE_WAVES) {
         // ------------------------------ loader waves ------------------------------
-        // Item i + 1's copies go out after B2 of item i (q, k, g and beta are read in P2a
-        // only) and must have landed by the next B1.
+        // Item i + 1's copies go out while item i is in P2b and P4 (q, k, g and beta are
+        // read in P2a only) and must have landed by the next B1: the raw k tile after
+        // B2, the raw q tile, g and beta after B3.  Issued all after B2, the loads queue
+        // behind the compute waves' record stores long enough to make the loaders the
+        // last waves at B3.
         typedef __attribute__((address_space(3))) void* lds_ptr;
         const int lw = wave - PAIR_COMPUTE_WAVES, lane = tid % WAVE;
         constexpr int RPI = 1024 / (2 * D);  // rows per direct load
@@ -277,13 +280,14 @@ __global__ __launch_bounds__(PAIR_THREADS, 1) void chunk_prep_pair_kernel(
             return m;
         };
         // token indices clamped into [0, T); rows past the block end are masked on use
-        auto issue = [&](int item, int tok0) {
+        auto issue = [&](int item, int tok0, int part) __attribute__((always_inline)) {
             int hk, pr;
             const int h0 = heads_of(item, hk, pr);
             static_assert((2 * NL) % PAIR_LOADER_WAVES == 0 && (2 * NH) % PAIR_LOADER_WAVES == 0,
                           "loads in multiples of the loader count");
 #pragma unroll
             for (int mm = 0; mm < 2 * NL / PAIR_LOADER_WAVES; ++mm) {
+                if ((mm < NL / PAIR_LOADER_WAVES) != (part == 0)) continue;  // part 0: k, part 1: q
                 const int i = mm * PAIR_LOADER_WAVES + lw;
                 const int m4 = i % NL;
                 const int r = m4 * RPI + lane / UPR, p = lane % UPR;
@@ -295,6 +299,7 @@ __global__ __launch_bounds__(PAIR_THREADS, 1) void chunk_prep_pair_kernel(
             }
 #pragma unroll
             for (int mm = 0; mm < 2 * NH / PAIR_LOADER_WAVES; ++mm) {  // g and beta, one fp32 per lane
+                if (part == 0) break;
                 const int i = mm * PAIR_LOADER_WAVES + lw;
                 const int j = i >> 1;
                 const size_t tg = (size_t)min(tok0 + lane, T - 1) * h_v + h0 + j;
@@ -306,18 +311,21 @@ __global__ __launch_bounds__(PAIR_THREADS, 1) void chunk_prep_pair_kernel(
         {
             const PairMeta m = meta_of(i0);
             if (lw == 0 && lane == 0) L.meta[0] = m;
-            issue(i0, m.live ? m.tok0 : 0);
+            issue(i0, m.live ? m.tok0 : 0, 0);
+            issue(i0, m.live ? m.tok0 : 0, 1);
             wait_vmcnt<0>();
         }
         for (int item = i0; item < i1; ++item, par ^= 1) {
             lds_barrier();  // B1
             lds_barrier();  // B2: q, k, g and beta are no longer read
+            PairMeta mn{0, 0, 0, 0};
             if (item + 1 < i1) {
-                const PairMeta m = meta_of(item + 1);
-                if (lw == 0 && lane == 0) L.meta[par ^ 1] = m;
-                issue(item + 1, m.live ? m.tok0 : 0);
+                mn = meta_of(item + 1);
+                if (lw == 0 && lane == 0) L.meta[par ^ 1] = mn;
+                issue(item + 1, mn.live ? mn.tok0 : 0, 0);
             }
             lds_barrier();  // B3
+            if (item + 1 < i1) issue(item + 1, mn.live ? mn.tok0 : 0, 1);
             wait_vmcnt<0>();
         }
         return;
