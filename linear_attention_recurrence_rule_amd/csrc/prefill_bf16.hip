@@ -251,10 +251,10 @@ __global__ __launch_bounds__(PAIR_THREADS, 1) void chunk_prep_pair_kernel(
     if (wave >= PAIR_COMPUTE_WAVES) {
         // ------------------------------ loader waves ------------------------------
         // Item i + 1's copies go out while item i is in P2b and P4 (q, k, g and beta are
-        // read in P2a only) and must have landed by the next B1: the raw k tile after
-        // B2, the raw q tile, g and beta after B3.  Issued all after B2, the loads queue
-        // behind the compute waves' record stores long enough to make the loaders the
-        // last waves at B3.
+        // read in P2a only) and must have landed by the next B1: the raw k tile and half
+        // the q tile after B2 (part 0), the rest of q, g and beta after B3 (part 1).
+        // Issued all after B2, the loads queue behind the compute waves' record stores
+        // long enough to make the loaders the last waves at B3.
         typedef __attribute__((address_space(3))) void* lds_ptr;
         const int lw = wave - PAIR_COMPUTE_WAVES, lane = tid % WAVE;
         constexpr int RPI = 1024 / (2 * D);  // rows per direct load
@@ -280,6 +280,7 @@ __global__ __launch_bounds__(PAIR_THREADS, 1) void chunk_prep_pair_kernel(
             return m;
         };
         // token indices clamped into [0, T); rows past the block end are masked on use
+        constexpr int EARLY = (3 * NL / 2) / PAIR_LOADER_WAVES;  // part 0's tile loads per loader
         auto issue = [&](int item, int tok0, int part) __attribute__((always_inline)) {
             int hk, pr;
             const int h0 = heads_of(item, hk, pr);
@@ -287,7 +288,7 @@ __global__ __launch_bounds__(PAIR_THREADS, 1) void chunk_prep_pair_kernel(
                           "loads in multiples of the loader count");
 #pragma unroll
             for (int mm = 0; mm < 2 * NL / PAIR_LOADER_WAVES; ++mm) {
-                if ((mm < NL / PAIR_LOADER_WAVES) != (part == 0)) continue;  // part 0: k, part 1: q
+                if ((mm < EARLY) != (part == 0)) continue;
                 const int i = mm * PAIR_LOADER_WAVES + lw;
                 const int m4 = i % NL;
                 const int r = m4 * RPI + lane / UPR, p = lane % UPR;
