@@ -561,11 +561,25 @@ __global__ __launch_bounds__(PAIR_THREADS, 1) void chunk_prep_pair_kernel(
                 float x[16];
 #pragma unroll
                 for (int i = 0; i < 16; ++i) x[i] = (i == j) ? 1.f : 0.f;
+                // Each step's row of N^T is read one step ahead (left to the compiler,
+                // every step waited for its own reads; further ahead the registers
+                // would no longer allow two workgroups per CU).
+                f4_t nr[15][4];
+                constexpr int AHEAD = 1;
+                auto fetch = [&](int m) __attribute__((always_inline)) {
+#pragma unroll
+                    for (int i4 = ((m + 1) / 4) * 4; i4 < 16; i4 += 4)
+                        nr[m][i4 / 4] = *reinterpret_cast<const f4_t*>(&Nt[m * XS + i4]);
+                };
+#pragma unroll
+                for (int m = 0; m < AHEAD; ++m) fetch(m);
 #pragma unroll
                 for (int m = 0; m < 15; ++m) {
+                    if (m + AHEAD < 15) fetch(m + AHEAD);
+                    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int i4 = ((m + 1) / 4) * 4; i4 < 16; i4 += 4) {
-                        const f4_t nc = *reinterpret_cast<const f4_t*>(&Nt[m * XS + i4]);
+                        const f4_t nc = nr[m][i4 / 4];
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
                             if (i4 + e > m) x[i4 + e] = fmaf(-nc[e], x[m], x[i4 + e]);
